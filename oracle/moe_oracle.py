@@ -1,0 +1,370 @@
+"""Plain fp64 CPU oracle of the TQP routed-expert layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: it exists so that tests, the package smoke check and the benchmark's
+CPU baseline can compare the HIP library against an obviously correct
+definition.  It imports nothing from the HIP library or its binding and shares
+no helper with them; the only thing both sides see is the input tensors.
+
+What is computed (cited by page title and section):
+  * "Reversible Sparse MoE Single Node" (skill card), Principle 3 "TQP
+    Optimizer Strategy" and Implementation Considerations "TQP Quantization":
+    expert base weights are quantized and fixed, low-rank adapters are full
+    precision and trained, the router is full precision.  So every expert
+    matrix is W_eff = dequant(q, s) + lam * A @ B, the base receives no
+    gradient and the adapters do.
+  * Same card, Architecture Details, and the abstract of "Reversible
+    Foundations: Training a 120B Sparse MoE through State-Preserving Scaling":
+    routed experts with top-k routing (460 experts, top-12 at the largest
+    stage).
+  * Same card, Implementation Considerations "Reversibility": routing is a
+    stateless function of the layer input.
+  * Same card, Related Methods: LoRA, i.e. the adapter product x @ A @ B.
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository): symmetric int4 with bf16 group scales; top-k
+over the logits with ties to the lower expert index; gates = softmax over the
+selected logits (= softmax over all experts renormalised over the selected);
+dropless routing; SwiGLU experts without biases, silu(z) = z / (1 + e^-z);
+LoRA on gate, up and down; loss L = sum_t <dY_t, y_t>; the top-k choice is
+held constant in the backward and the router receives no weight gradient but
+does pass gradient to x through the gates.
+
+Everything is evaluated in float64 from the exact stored inputs: bf16 bit
+patterns and float32 values convert to float64 exactly, int4 nibbles become
+integers and bf16 scales become float64.  Parity pins for every function are
+in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------- storage --
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact float64 value of a stored tensor: uint16 arrays are bf16 bit
+    patterns, float32 arrays are float32 values."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported storage dtype {a.dtype}")
+
+
+def unpack_int4(q_packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/2] -> int64 [..., K] signed values.
+
+    Word layout: every aligned 32-bit little-endian word covers an 8-wide
+    block of K; nibble slot j (bits 4j..4j+3) holds element 2j for j < 4 and
+    element 2(j-4)+1 for j >= 4; nibbles are two's complement."""
+    q_packed = np.ascontiguousarray(q_packed, dtype=np.uint8)
+    lead = q_packed.shape[:-1]
+    words = q_packed.reshape(lead + (q_packed.shape[-1] // 4, 4)).astype(np.int64)
+    word = words[..., 0] | (words[..., 1] << 8) | (words[..., 2] << 16) | (words[..., 3] << 24)
+    out = np.empty(lead + (word.shape[-1], 8), dtype=np.int64)
+    for slot in range(8):
+        nib = (word >> (4 * slot)) & 0xF
+        val = np.where(nib >= 8, nib - 16, nib)
+        elem = 2 * slot if slot < 4 else 2 * (slot - 4) + 1
+        out[..., elem] = val
+    return out.reshape(lead + (word.shape[-1] * 8,))
+
+
+def dequantize(q_packed: np.ndarray, scale_bits: np.ndarray, group: int) -> np.ndarray:
+    """W_hat[n, c] = s[n, c // group] * q[n, c]  (float64, exact)."""
+    q = unpack_int4(q_packed)
+    s = to_f64(scale_bits)
+    return q * np.repeat(s, group, axis=-1)
+
+
+# --------------------------------------------------------------- routing --
+
+
+def router_logits(x, w_router, b_router=None) -> np.ndarray:
+    """l[t, e] = sum_c x[t, c] W_r[c, e] + b[e]  (full-precision router)."""
+    l = to_f64(x) @ to_f64(w_router)
+    if b_router is not None:
+        l = l + to_f64(b_router)[None, :]
+    return l
+
+
+def topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """First k experts of each row under the order (logit descending, expert
+    index ascending); returned in that order, int32 [T, k]."""
+    T, E = logits.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    experts = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((experts, -logits[t]))
+        idx[t] = order[:k]
+    return idx
+
+
+def gates(logits: np.ndarray, topk_idx: np.ndarray) -> np.ndarray:
+    """gamma[t, j] = exp(l[t, S_j]) / sum_i exp(l[t, S_i]) over the selected
+    experts S (computed relative to the largest selected logit)."""
+    sel = np.take_along_axis(logits, topk_idx.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def near_ties(logits: np.ndarray, k: int, thr: float = 1e-5):
+    """(boundary, order) boolean masks per token.  boundary: the k-th and
+    (k+1)-th largest logits differ by less than thr, so the selected set can
+    legitimately differ between precisions.  order: two adjacent selected
+    logits differ by less than thr, so their slot order can differ."""
+    srt = -np.sort(-logits, axis=1)
+    T, E = logits.shape
+    boundary = np.zeros(T, bool)
+    if k < E:
+        boundary = (srt[:, k - 1] - srt[:, k]) < thr
+    order = np.zeros(T, bool)
+    if k > 1:
+        order = (np.diff(-srt[:, :k], axis=1) < thr).any(axis=1)
+    return boundary, order
+
+
+# ----------------------------------------------------------- permutation --
+
+
+def permutation(topk_idx: np.ndarray, E: int):
+    """Expert-contiguous placement of the T*k routed slots, stable in token
+    order: counts[e], offsets[e] (exclusive scan, offsets[E] = T*k),
+    perm_src[p] = t*k + j and slot_pos[t*k + j] = p."""
+    T, k = topk_idx.shape
+    flat = topk_idx.reshape(-1).astype(np.int64)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:E].copy()
+    perm_src = np.empty(T * k, dtype=np.int64)
+    slot_pos = np.empty(T * k, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = flat[t * k + j]
+            p = cursor[e]
+            cursor[e] += 1
+            perm_src[p] = t * k + j
+            slot_pos[t * k + j] = p
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm_src.astype(np.int32), slot_pos.astype(np.int32))
+
+
+# ---------------------------------------------------------------- experts --
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+class Expert:
+    """Float64 view of one expert's frozen base and adapters."""
+
+    def __init__(self, inputs: dict, e: int, group: int):
+        self.e = e
+        self.W = {m: dequantize(inputs[f"q_{m}"][e], inputs[f"s_{m}"][e], group)
+                  for m in ("gate", "up", "down")}
+        self.A = {m: to_f64(inputs[f"A_{m}"][e]) for m in ("gate", "up", "down")}
+        self.B = {m: to_f64(inputs[f"B_{m}"][e]) for m in ("gate", "up", "down")}
+
+
+def expert_forward(ex: Expert, X: np.ndarray, lam: float) -> dict:
+    """SwiGLU expert with adapters on every matrix, rows X [M, d]:
+    G = X W_g^T + lam (X A_g) B_g, U likewise, H = silu(G) * U,
+    O = H W_d^T + lam (H A_d) B_d."""
+    Zg = X @ ex.A["gate"]
+    Zu = X @ ex.A["up"]
+    G = X @ ex.W["gate"].T + lam * (Zg @ ex.B["gate"])
+    U = X @ ex.W["up"].T + lam * (Zu @ ex.B["up"])
+    H = silu(G) * U
+    Zd = H @ ex.A["down"]
+    O = H @ ex.W["down"].T + lam * (Zd @ ex.B["down"])
+    return {"G": G, "U": U, "H": H, "O": O, "Zg": Zg, "Zu": Zu, "Zd": Zd}
+
+
+def expert_backward(ex: Expert, X: np.ndarray, fw: dict, dO: np.ndarray, lam: float) -> dict:
+    """Adapter-only backward of expert_forward for upstream dO [M, d]:
+    gradients of A and B of each matrix, and dX [M, d].  The base is frozen,
+    so no gradient of W is formed."""
+    G, U, H = fw["G"], fw["U"], fw["H"]
+    dB_down = lam * fw["Zd"].T @ dO
+    dZd = lam * dO @ ex.B["down"].T
+    dA_down = H.T @ dZd
+    dH = dO @ ex.W["down"] + dZd @ ex.A["down"].T
+    sg = sigmoid(G)
+    dG = dH * U * sg * (1.0 + G * (1.0 - sg))
+    dU = dH * G * sg
+    dB_gate = lam * fw["Zg"].T @ dG
+    dB_up = lam * fw["Zu"].T @ dU
+    dZg = lam * dG @ ex.B["gate"].T
+    dZu = lam * dU @ ex.B["up"].T
+    dA_gate = X.T @ dZg
+    dA_up = X.T @ dZu
+    dX = (dG @ ex.W["gate"] + dU @ ex.W["up"]
+          + dZg @ ex.A["gate"].T + dZu @ ex.A["up"].T)
+    return {"dA_gate": dA_gate, "dB_gate": dB_gate, "dA_up": dA_up, "dB_up": dB_up,
+            "dA_down": dA_down, "dB_down": dB_down, "dX": dX}
+
+
+# ------------------------------------------------------------ whole layer --
+
+
+def route(inputs: dict, k: int, topk_idx: np.ndarray | None = None) -> dict:
+    """Logits, selection, gates and permutation.  A caller may pass the
+    selection to evaluate the layer on a given routing."""
+    l = router_logits(inputs["x"], inputs["w_router"], inputs.get("b_router"))
+    idx = topk(l, k) if topk_idx is None else np.asarray(topk_idx, np.int32)
+    E = l.shape[1]
+    counts, offsets, perm_src, slot_pos = permutation(idx, E)
+    return {"logits": l, "topk_idx": idx, "gates": gates(l, idx), "counts": counts,
+            "offsets": offsets, "perm_src": perm_src, "slot_pos": slot_pos}
+
+
+def forward(inputs: dict, k: int, group: int, lam: float = 1.0,
+            topk_idx: np.ndarray | None = None, keep: bool = False) -> dict:
+    """y[t] = sum_j gamma[t, j] * O_{e(t,j)}(x_t), j ascending."""
+    R = route(inputs, k, topk_idx)
+    x = to_f64(inputs["x"])
+    T, d = x.shape
+    E = R["logits"].shape[1]
+    S = T * k
+    O = np.zeros((S, d))
+    saved = {}
+    for e in range(E):
+        lo, hi = R["offsets"][e], R["offsets"][e + 1]
+        if hi == lo:
+            continue
+        rows = R["perm_src"][lo:hi] // k
+        ex = Expert(inputs, e, group)
+        fw = expert_forward(ex, x[rows], lam)
+        O[lo:hi] = fw["O"]
+        if keep:
+            saved[e] = fw
+    gam = R["gates"]
+    y = np.zeros((T, d))
+    for j in range(k):
+        y += gam[:, j:j + 1] * O[R["slot_pos"].reshape(T, k)[:, j]]
+    out = dict(R)
+    out.update({"e_out": O, "y": y})
+    if keep:
+        out["saved"] = saved
+    return out
+
+
+def backward(inputs: dict, fwd: dict, k: int, group: int, lam: float = 1.0) -> dict:
+    """Gradients of L = sum_t <dY_t, y_t> with the top-k choice held fixed:
+    dX (through the experts and through the gates into the router input) and
+    the six adapter gradients per expert.  The router and base are frozen."""
+    x = to_f64(inputs["x"])
+    dy = to_f64(inputs["dy"])
+    wr = to_f64(inputs["w_router"])
+    T, d = x.shape
+    E = wr.shape[1]
+    idx, gam = fwd["topk_idx"], fwd["gates"]
+    slot = fwd["slot_pos"].reshape(T, k)
+    O = fwd["e_out"]
+    # gate path: dgamma, softmax over the selected logits, router input grad
+    dgam = np.einsum("td,tjd->tj", dy, O[slot])
+    dl = gam * (dgam - (gam * dgam).sum(axis=1, keepdims=True))
+    dx = np.zeros((T, d))
+    for j in range(k):
+        dx += dl[:, j:j + 1] * wr[:, idx[:, j]].T
+    # expert path
+    f = inputs["q_gate"].shape[1]
+    r = inputs["A_gate"].shape[2]
+    grads = {"dA_gate": np.zeros((E, d, r)), "dB_gate": np.zeros((E, r, f)),
+             "dA_up": np.zeros((E, d, r)), "dB_up": np.zeros((E, r, f)),
+             "dA_down": np.zeros((E, f, r)), "dB_down": np.zeros((E, r, d))}
+    dXp = np.zeros((T * k, d))
+    for e in range(E):
+        lo, hi = fwd["offsets"][e], fwd["offsets"][e + 1]
+        if hi == lo:
+            continue
+        src = fwd["perm_src"][lo:hi]
+        rows, js = src // k, src % k
+        ex = Expert(inputs, e, group)
+        fw = fwd["saved"][e] if "saved" in fwd else expert_forward(ex, x[rows], lam)
+        dO = gam[rows, js][:, None] * dy[rows]
+        g = expert_backward(ex, x[rows], fw, dO, lam)
+        for name in grads:
+            grads[name][e] = g[name]
+        dXp[lo:hi] = g["dX"]
+    for j in range(k):
+        dx += dXp[slot[:, j]]
+    out = {"dx": dx, "dx_router": dx - sum(dXp[slot[:, j]] for j in range(k)),
+           "dgates": dgam, "dlogits_sel": dl}
+    out.update(grads)
+    return out
+
+
+# ------------------------------------------------- sampled evaluation --
+# The same definitions evaluated on a subset, for shapes where the whole
+# layer is too slow on the CPU: outputs of chosen tokens and gradients of
+# chosen experts are exact functions of their own rows.
+
+
+def forward_tokens(inputs: dict, tokens, k: int, group: int, lam: float = 1.0,
+                   topk_idx: np.ndarray | None = None, cache: dict | None = None) -> dict:
+    """Routing and y for the listed tokens only (topk_idx, if given, holds the
+    selection of those tokens, one row each)."""
+    tokens = np.asarray(tokens)
+    x = to_f64(inputs["x"][tokens])
+    l = router_logits(inputs["x"][tokens], inputs["w_router"], inputs.get("b_router"))
+    idx = topk(l, k) if topk_idx is None else np.asarray(topk_idx, np.int32)
+    gam = gates(l, idx)
+    cache = {} if cache is None else cache
+    y = np.zeros_like(x)
+    O = np.zeros((len(tokens), k, x.shape[1]))
+    for i in range(len(tokens)):
+        for j in range(k):
+            e = int(idx[i, j])
+            if e not in cache:
+                cache[e] = Expert(inputs, e, group)
+            O[i, j] = expert_forward(cache[e], x[i:i + 1], lam)["O"][0]
+            y[i] += gam[i, j] * O[i, j]
+    return {"logits": l, "topk_idx": idx, "gates": gam, "O": O, "y": y}
+
+
+def backward_tokens(inputs: dict, tokens, k: int, group: int, lam: float = 1.0,
+                    topk_idx: np.ndarray | None = None, cache: dict | None = None) -> np.ndarray:
+    """dX rows of the listed tokens (each is a function of that token alone)."""
+    tokens = np.asarray(tokens)
+    fw = forward_tokens(inputs, tokens, k, group, lam, topk_idx, cache)
+    cache = {} if cache is None else cache
+    x = to_f64(inputs["x"][tokens])
+    dy = to_f64(inputs["dy"][tokens])
+    wr = to_f64(inputs["w_router"])
+    idx, gam, O = fw["topk_idx"], fw["gates"], fw["O"]
+    dgam = np.einsum("id,ijd->ij", dy, O)
+    dl = gam * (dgam - (gam * dgam).sum(axis=1, keepdims=True))
+    dx = np.zeros_like(x)
+    for i in range(len(tokens)):
+        for j in range(k):
+            e = int(idx[i, j])
+            ex = cache.setdefault(e, Expert(inputs, e, group))
+            dx[i] += dl[i, j] * wr[:, e]
+            f1 = expert_forward(ex, x[i:i + 1], lam)
+            g = expert_backward(ex, x[i:i + 1], f1, gam[i, j] * dy[i:i + 1], lam)
+            dx[i] += g["dX"][0]
+    return dx
+
+
+def expert_grads(inputs: dict, R: dict, e: int, k: int, group: int, lam: float = 1.0) -> dict:
+    """The six adapter gradients of expert e given the full routing R (as
+    returned by route())."""
+    lo, hi = R["offsets"][e], R["offsets"][e + 1]
+    src = R["perm_src"][lo:hi]
+    rows, js = src // k, src % k
+    ex = Expert(inputs, e, group)
+    X = to_f64(inputs["x"][rows])
+    fw = expert_forward(ex, X, lam)
+    dO = R["gates"][rows, js][:, None] * to_f64(inputs["dy"][rows])
+    return expert_backward(ex, X, fw, dO, lam)
