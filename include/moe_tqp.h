@@ -1,0 +1,198 @@
+/*
+ * moe_tqp.h -- C ABI of the MI355X (gfx950) routed-expert layer under TQP.
+ *
+ * The layer: a full-precision router picks k of E experts per token, each
+ * expert is a SwiGLU FFN whose base weights are quantized to int4 and frozen,
+ * with trained low-rank adapters on every matrix, and the k expert outputs
+ * are mixed by the routing gates.  The backward produces the gradient of the
+ * input and of the adapters only.
+ *
+ * Sources (page title, section):
+ *   - skill card "Reversible Sparse MoE Single Node", Principle 3 "TQP
+ *     Optimizer Strategy": base expert weights quantized and fixed, low-rank
+ *     adapters carry the optimizer state.
+ *   - same card, Implementation Considerations, "TQP Quantization": int8 or
+ *     int4 base, full-precision trainable adapters, full-precision router.
+ *   - same card, Architecture Details, and the abstract of "Reversible
+ *     Foundations: Training a 120B Sparse MoE through State-Preserving
+ *     Scaling": 460 routed experts under top-12 routing, 8K context.
+ *   - same card, Implementation Considerations, "Reversibility": routing
+ *     decisions are stateless.
+ *   - same card, Related Methods: LoRA (adapter product x A B).
+ * The pages fix no formats, shapes or kernels; every layout below is this
+ * library's own.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream) in stream order.
+ *   - Arguments are validated on the host before any HIP call.  On failure
+ *     the call returns a negative status, enqueues nothing and writes nothing;
+ *     moe_last_error() then describes the failed check (thread-local).
+ *   - Launch failures are reported as MOE_ERR_HIP.
+ *   - Outputs are overwritten, never accumulated into.  Every output element
+ *     is written, including zero gradients of experts that received no token.
+ *   - The library keeps no state between calls; calls are re-entrant.
+ *   - Results are bitwise reproducible for identical inputs: integer
+ *     histograms, scan-ordered placement, fixed-order reductions, no float
+ *     atomics.
+ *   - Row-major storage throughout.  "act" tensors are float32 when
+ *     dims.act == MOE_F32 and bf16 (raw uint16 bit patterns) when
+ *     dims.act == MOE_BF16.  Gates, logits and adapter gradients are float32.
+ *
+ * Shapes: T tokens, d = d_model, E experts, k experts per token, f = d_ff,
+ * r = adapter rank, g = quantization group, S = T*k routed slots.
+ */
+#ifndef MOE_TQP_H
+#define MOE_TQP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,     /* null pointer, bad shape, bad scale          */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, group)    */
+  MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than moe_workspace_size()  */
+  MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed         */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer dimensions.  Limits: T >= 1, 1 <= k <= min(E, 32), E <= 1024,
+ * group in {32, 64, 128}, d % group == 0, f % group == 0, 1 <= r <= 32,
+ * S = T*k <= 2^26, d, f <= 65536. */
+typedef struct {
+  int32_t T, d_model, n_experts, top_k, d_ff, rank, group;
+  int32_t act;        /* moe_dtype */
+  float lora_scale;   /* lambda in W_eff = W_hat + lambda * A B; finite */
+} moe_dims;
+
+/* One expert matrix W[N][K] (out x in) for all E experts, frozen int4 base
+ * plus adapter.  For gate and up N = f, K = d; for down N = d, K = f.
+ *   q     uint8 [E][N][K/2]: symmetric int4, two's-complement nibbles.  Each
+ *         aligned little-endian 32-bit word holds one 8-wide block k0..k7 of
+ *         K; nibble slot j (bits 4j..4j+3) holds k_{2j} for j < 4 and
+ *         k_{2(j-4)+1} for j >= 4.
+ *   scale bf16  [E][N][K/g]: W_hat[n][c] = scale[n][c/g] * q[n][c].
+ *   A     act   [E][K][r]
+ *   B     act   [E][r][N]
+ * Effective matrix: W_eff = W_hat + lambda * (A B)^T, i.e. for a row x,
+ * x W_eff^T = x W_hat^T + lambda (x A) B. */
+typedef struct {
+  const uint8_t *q;
+  const uint16_t *scale;
+  const void *A;
+  const void *B;
+} moe_qlora;
+
+/* Which call a workspace size is asked for. */
+typedef enum {
+  MOE_CALL_ROUTE = 0,
+  MOE_CALL_PERMUTE = 1,
+  MOE_CALL_EXPERT_FWD = 2,
+  MOE_CALL_COMBINE = 3,
+  MOE_CALL_ADAPTER_BWD = 4
+} moe_call;
+
+/* Router, softmax and top-k.  logits[t][e] = sum_c x[t][c] w_router[c][e]
+ * + b_router[e] in float32; the k largest logits are selected under the order
+ * (logit descending, expert index ascending) and written in that order to
+ * topk_idx; gates[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the
+ * selected logits (softmax over all experts renormalised to the selected).
+ *   x          act  [T][d]
+ *   w_router   f32  [d][E]
+ *   b_router   f32  [E] or NULL (no bias)
+ *   topk_idx   i32  [T][k]     (out)
+ *   gates      f32  [T][k]     (out)
+ *   logits     f32  [T][E] or NULL (out, optional)
+ *   ws         workspace of moe_workspace_size(MOE_CALL_ROUTE) bytes */
+moe_status moe_route(const moe_dims *dims, const void *x, const float *w_router,
+                     const float *b_router, int32_t *topk_idx, float *gates,
+                     float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert histogram, scan and stable permutation of the S routed slots into
+ * expert-contiguous order (expert ascending, token ascending within an
+ * expert).  Every topk_idx entry must be in [0, E) and a token's k entries
+ * distinct (as moe_route produces); other input is undefined behaviour.
+ *   counts    i32 [E]     slots per expert (out)
+ *   offsets   i32 [E+1]   exclusive scan of counts, offsets[E] = S (out)
+ *   perm_src  i32 [S]     perm_src[p] = t*k + j of the slot at position p (out)
+ *   slot_pos  i32 [S]     slot_pos[t*k + j] = p (out)
+ *   x_perm    act [S][d] or NULL: x_perm[p] = x[perm_src[p] / k] (out)
+ *   x         act [T][d]  read only when x_perm != NULL (may be NULL otherwise) */
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void *x,
+                       int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                       int32_t *slot_pos, void *x_perm, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Expert FFNs over the permuted rows.  For every position p with expert e
+ * (offsets[e] <= p < offsets[e+1]) and input row X = x[perm_src[p] / k]:
+ *   G = X Wg_hat^T + lambda (X A_g) B_g,   U = X Wu_hat^T + lambda (X A_u) B_u
+ *   H = silu(G) * U,   silu(z) = z / (1 + exp(-z))
+ *   e_out[p] = H Wd_hat^T + lambda (H A_d) B_d
+ * Arithmetic: MOE_F32 computes in float32 throughout; MOE_BF16 feeds bf16
+ * operands to the matrix cores with float32 accumulation and rounds H and
+ * e_out to bf16 (each once, to nearest even).
+ *   x        act [T][d]
+ *   offsets, perm_src as written by moe_permute (device)
+ *   e_out    act [S][d] in permuted order (out)
+ *   save     NULL, or moe_save_size() bytes that moe_adapter_bwd consumes
+ *            (opaque: pre-activations and adapter projections) (out) */
+moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
+                          const int32_t *perm_src, moe_qlora gate, moe_qlora up,
+                          moe_qlora down, void *e_out, void *save, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Gate-weighted combine: y[t] = sum_{j=0..k-1} gates[t][j] e_out[slot_pos[t*k+j]],
+ * float32 accumulation in ascending j, one rounding to act at the end.
+ *   y act [T][d] (out) */
+moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *slot_pos,
+                       const float *gates, void *y, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Adapter-only backward of route -> expert FFNs -> combine for an upstream
+ * gradient dy (loss L = sum_t <dy_t, y_t>).  The selection is held fixed; the
+ * router and every base matrix are frozen (no weight gradient), but the gates
+ * pass gradient to x through the router:
+ *   dgamma[t][j] = <dy_t, e_out[slot_pos[t,j]]>,
+ *   dl[t][j] = gamma[t][j] (dgamma[t][j] - sum_i gamma[t][i] dgamma[t][i]),
+ *   dx[t] = sum_j dl[t][j] w_router[:, e_{t,j}]  +  sum_j dX_expert(t, j)
+ * with, per expert and dO = gamma * dy on its rows:
+ *   dB_d = lambda (H A_d)^T dO, dZ_d = lambda dO B_d^T, dA_d = H^T dZ_d,
+ *   dH = dO Wd_hat + dZ_d A_d^T,  dG = dH U s (1 + G (1 - s)), dU = dH G s,
+ *   s = sigmoid(G); dB_g = lambda (X A_g)^T dG, dZ_g = lambda dG B_g^T,
+ *   dA_g = X^T dZ_g (likewise up), dX = dG Wg_hat + dU Wu_hat + dZ_g A_g^T
+ *   + dZ_u A_u^T.
+ * Inputs are those of the forward calls; save must hold what moe_expert_fwd
+ * wrote for the same inputs.
+ *   dy   act [T][d];  dx act [T][d] (out)
+ *   dA_gate, dA_up f32 [E][d][r]; dB_gate, dB_up f32 [E][r][f];
+ *   dA_down f32 [E][f][r]; dB_down f32 [E][r][d]  (out) */
+moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
+                           const int32_t *topk_idx, const float *gates,
+                           const int32_t *offsets, const int32_t *perm_src,
+                           const int32_t *slot_pos, const float *w_router,
+                           moe_qlora gate, moe_qlora up, moe_qlora down,
+                           const void *e_out, const void *save, void *dx,
+                           float *dA_gate, float *dB_gate, float *dA_up, float *dB_up,
+                           float *dA_down, float *dB_down, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Host-only queries; they validate dims like the calls do. */
+moe_status moe_workspace_size(const moe_dims *dims, int32_t call, size_t *bytes);
+moe_status moe_save_size(const moe_dims *dims, size_t *bytes);
+const char *moe_status_string(int32_t status);
+const char *moe_last_error(void);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_TQP_H */

@@ -1,0 +1,155 @@
+"""ctypes binding of libmoe_tqp.so (see include/moe_tqp.h).
+
+Argument marshalling only: torch tensors are passed by device pointer and the
+current HIP stream; every step of the layer runs in the library's kernels.
+Importing this module loads the library and raises if it was not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_tqp.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+CALL_ROUTE, CALL_PERMUTE, CALL_EXPERT_FWD, CALL_COMBINE, CALL_ADAPTER_BWD = range(5)
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("lora_scale", ctypes.c_float)]
+
+
+class QLora(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise MoeError(f"{LIB_PATH} is missing: build it with "
+                       "`python -m sparse_moe_expert_fp32_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    DP = ctypes.POINTER(Dims)
+    sig = {
+        "moe_route": [DP, P, P, P, P, P, P, P, SZ, P],
+        "moe_permute": [DP, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_expert_fwd": [DP, P, P, P, QLora, QLora, QLora, P, P, P, SZ, P],
+        "moe_combine": [DP, P, P, P, P, P, SZ, P],
+        "moe_adapter_bwd": [DP, P, P, P, P, P, P, P, P, QLora, QLora, QLora, P, P, P,
+                            P, P, P, P, P, P, P, SZ, P],
+        "moe_workspace_size": [DP, I32, ctypes.POINTER(SZ)],
+        "moe_save_size": [DP, ctypes.POINTER(SZ)],
+        "moe_status_string": [I32],
+        "moe_last_error": [],
+        "moe_abi_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = I32
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
+           "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
+           "moe_abi_version")
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        raise MoeError(f"{name}: {LIB.moe_status_string(status).decode()}: "
+                       f"{LIB.moe_last_error().decode()}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dims(T, d, E, k, f, r, group, act, lora_scale=1.0) -> Dims:
+    a = {"f32": MOE_F32, "bf16": MOE_BF16}.get(act, act)
+    return Dims(T, d, E, k, f, r, group, a, lora_scale)
+
+
+def dims_of(cfg, T: int | None = None) -> Dims:
+    return dims(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.r, cfg.group,
+                cfg.act, cfg.lora_scale)
+
+
+def qlora(q, scale, A, B) -> QLora:
+    return QLora(_p(q), _p(scale), _p(A), _p(B))
+
+
+def moe_workspace_size(dm: Dims, call: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(LIB.moe_workspace_size(ctypes.byref(dm), call, ctypes.byref(out)), "moe_workspace_size")
+    return out.value
+
+
+def moe_save_size(dm: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(LIB.moe_save_size(ctypes.byref(dm), ctypes.byref(out)), "moe_save_size")
+    return out.value
+
+
+def moe_abi_version() -> int:
+    return LIB.moe_abi_version()
+
+
+def moe_route(dm, x, w_router, b_router, topk_idx, gates, logits, ws, stream=None):
+    _check(LIB.moe_route(ctypes.byref(dm), _p(x), _p(w_router), _p(b_router), _p(topk_idx),
+                         _p(gates), _p(logits), _p(ws), ws.numel() if ws is not None else 0,
+                         _stream(stream)), "moe_route")
+
+
+def moe_permute(dm, topk_idx, x, counts, offsets, perm_src, slot_pos, x_perm, ws, stream=None):
+    _check(LIB.moe_permute(ctypes.byref(dm), _p(topk_idx), _p(x), _p(counts), _p(offsets),
+                           _p(perm_src), _p(slot_pos), _p(x_perm), _p(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
+
+
+def moe_expert_fwd(dm, x, offsets, perm_src, gate, up, down, e_out, save, ws, stream=None):
+    _check(LIB.moe_expert_fwd(ctypes.byref(dm), _p(x), _p(offsets), _p(perm_src), gate, up, down,
+                              _p(e_out), _p(save), _p(ws), ws.numel() if ws is not None else 0,
+                              _stream(stream)), "moe_expert_fwd")
+
+
+def moe_combine(dm, e_out, slot_pos, gates, y, ws=None, stream=None):
+    _check(LIB.moe_combine(ctypes.byref(dm), _p(e_out), _p(slot_pos), _p(gates), _p(y), _p(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)), "moe_combine")
+
+
+def moe_adapter_bwd(dm, dy, x, topk_idx, gates, offsets, perm_src, slot_pos, w_router, gate, up,
+                    down, e_out, save, dx, dA_gate, dB_gate, dA_up, dB_up, dA_down, dB_down, ws,
+                    stream=None):
+    _check(LIB.moe_adapter_bwd(ctypes.byref(dm), _p(dy), _p(x), _p(topk_idx), _p(gates),
+                               _p(offsets), _p(perm_src), _p(slot_pos), _p(w_router), gate, up,
+                               down, _p(e_out), _p(save), _p(dx), _p(dA_gate), _p(dB_gate),
+                               _p(dA_up), _p(dB_up), _p(dA_down), _p(dB_down), _p(ws),
+                               ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_adapter_bwd")

@@ -1,0 +1,382 @@
+// C ABI of the TQP routed-expert layer: host-side validation, workspace
+// carving and the kernel sequence of every call.  See include/moe_tqp.h.
+#include "moe_tqp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define REQUIRE(cond, msg) \
+  do {                     \
+    if (!(cond)) return fail(MOE_ERR_INVALID, msg); \
+  } while (0)
+
+moe_status check_dims(const moe_dims *d) {
+  if (!d) return fail(MOE_ERR_INVALID, "dims is NULL");
+  REQUIRE(d->T >= 1, "T must be >= 1");
+  REQUIRE(d->n_experts >= 1 && d->n_experts <= 1024, "n_experts must be in [1, 1024]");
+  REQUIRE(d->top_k >= 1 && d->top_k <= 32 && d->top_k <= d->n_experts,
+          "top_k must be in [1, min(n_experts, 32)]");
+  REQUIRE(d->d_model >= 1 && d->d_model <= 65536, "d_model must be in [1, 65536]");
+  REQUIRE(d->d_ff >= 1 && d->d_ff <= 65536, "d_ff must be in [1, 65536]");
+  REQUIRE(d->rank >= 1 && d->rank <= 32, "rank must be in [1, 32]");
+  REQUIRE((int64_t)d->T * d->top_k <= (int64_t(1) << 26), "T * top_k must be <= 2^26");
+  REQUIRE(std::isfinite(d->lora_scale), "lora_scale must be finite");
+  if (d->act != MOE_F32 && d->act != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "act must be MOE_F32 or MOE_BF16");
+  if (d->group != 32 && d->group != 64 && d->group != 128)
+    return fail(MOE_ERR_UNSUPPORTED, "group must be 32, 64 or 128");
+  REQUIRE(d->d_model % d->group == 0, "d_model must be a multiple of group");
+  REQUIRE(d->d_ff % d->group == 0, "d_ff must be a multiple of group");
+  return MOE_OK;
+}
+
+moe_status check_qlora(const moe_qlora &m, const char *name) {
+  if (!m.q || !m.scale || !m.A || !m.B)
+    return fail(MOE_ERR_INVALID, std::string(name) + ": q, scale, A and B must be non-NULL");
+  return MOE_OK;
+}
+
+moe_status hip_status(const char *where) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+  return MOE_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  }
+};
+
+size_t act_bytes(const moe_dims *d) { return d->act == MOE_BF16 ? 2 : 4; }
+
+// ---- save buffer: Z [S][3r] f32 | G [S][f] act | U [S][f] act | H [S][f] act
+struct SaveLayout {
+  size_t Z, G, U, H, total;
+  explicit SaveLayout(const moe_dims *d) {
+    size_t S = (size_t)d->T * d->top_k, f = d->d_ff, ab = act_bytes(d);
+    Carve c;
+    Z = c.take(S * 3 * d->rank * 4);
+    G = c.take(S * f * ab);
+    U = c.take(S * f * ab);
+    H = c.take(S * f * ab);
+    total = c.off;
+  }
+};
+
+size_t max_tiles(const moe_dims *d, int BM) {
+  return ((size_t)d->T * d->top_k + BM - 1) / BM + d->n_experts;
+}
+
+// ---- expert forward workspace
+struct FwdLayout {
+  size_t tiles, ntiles, save, G32, U32, total;
+  explicit FwdLayout(const moe_dims *d) {
+    size_t S = (size_t)d->T * d->top_k, f = d->d_ff;
+    Carve c;
+    tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
+    ntiles = c.take(sizeof(int));
+    save = c.take(SaveLayout(d).total);  // used when the caller passes no save buffer
+    G32 = c.take(S * f * 4);
+    U32 = c.take(S * f * 4);
+    total = c.off;
+  }
+};
+
+// ---- adapter backward workspace
+struct BwdLayout {
+  size_t tiles, ntiles, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
+  explicit BwdLayout(const moe_dims *d) {
+    size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
+    Carve c;
+    tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
+    ntiles = c.take(sizeof(int));
+    wr_t = c.take((size_t)d->n_experts * dm * 4);
+    dx_r = c.take((size_t)d->T * dm * 4);
+    dO = c.take(S * dm * ab);
+    dZ = c.take(S * 3 * d->rank * 4);
+    dH32 = c.take(S * f * 4);
+    dG = c.take(S * f * ab);
+    dU = c.take(S * f * ab);
+    dXp = c.take(S * dm * 4);
+    total = c.off;
+  }
+};
+
+size_t ws_bytes_for(const moe_dims *d, int call) {
+  switch (call) {
+    case MOE_CALL_ROUTE: return moe::route_ws_bytes(d->T, d->d_model, d->n_experts);
+    case MOE_CALL_PERMUTE: return moe::permute_ws_bytes(d->T, d->n_experts, d->top_k);
+    case MOE_CALL_EXPERT_FWD: return FwdLayout(d).total;
+    case MOE_CALL_COMBINE: return 0;
+    case MOE_CALL_ADAPTER_BWD: return BwdLayout(d).total;
+    default: return (size_t)-1;
+  }
+}
+
+moe_status check_ws(const moe_dims *d, int call, const void *ws, size_t ws_bytes) {
+  size_t need = ws_bytes_for(d, call);
+  if (need && !ws) return fail(MOE_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                       " bytes, got " + std::to_string(ws_bytes));
+  return MOE_OK;
+}
+
+template <typename T> T *at(void *base, size_t off) { return (T *)((char *)base + off); }
+
+}  // namespace
+
+#define TRY(expr)                  \
+  do {                             \
+    moe_status _s = (expr);        \
+    if (_s != MOE_OK) return _s;   \
+  } while (0)
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_workspace_size(const moe_dims *dims, int32_t call, size_t *bytes) {
+  TRY(check_dims(dims));
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  if (call < MOE_CALL_ROUTE || call > MOE_CALL_ADAPTER_BWD)
+    return fail(MOE_ERR_INVALID, "unknown call id");
+  *bytes = ws_bytes_for(dims, call);
+  return MOE_OK;
+}
+
+moe_status moe_save_size(const moe_dims *dims, size_t *bytes) {
+  TRY(check_dims(dims));
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  *bytes = SaveLayout(dims).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_dims *dims, const void *x, const float *w_router,
+                     const float *b_router, int32_t *topk_idx, float *gates, float *logits,
+                     void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_dims(dims));
+  REQUIRE(x && w_router && topk_idx && gates, "moe_route: x, w_router, topk_idx, gates required");
+  TRY(check_ws(dims, MOE_CALL_ROUTE, ws, ws_bytes));
+  moe::launch_route(dims->act == MOE_BF16, x, w_router, b_router, dims->T, dims->d_model,
+                    dims->n_experts, dims->top_k, topk_idx, gates, logits, ws,
+                    (hipStream_t)stream);
+  return hip_status("moe_route");
+}
+
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void *x,
+                       int32_t *counts, int32_t *offsets, int32_t *perm_src, int32_t *slot_pos,
+                       void *x_perm, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_dims(dims));
+  REQUIRE(topk_idx && counts && offsets && perm_src && slot_pos,
+          "moe_permute: topk_idx, counts, offsets, perm_src, slot_pos required");
+  REQUIRE(!x_perm || x, "moe_permute: x required when x_perm is requested");
+  TRY(check_ws(dims, MOE_CALL_PERMUTE, ws, ws_bytes));
+  moe::launch_permute(topk_idx, dims->T, dims->n_experts, dims->top_k, counts, offsets, perm_src,
+                      slot_pos, x, x_perm, (int)(dims->d_model * act_bytes(dims)), ws,
+                      (hipStream_t)stream);
+  return hip_status("moe_permute");
+}
+
+moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *slot_pos,
+                       const float *gates, void *y, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  TRY(check_dims(dims));
+  REQUIRE(e_out && slot_pos && gates && y, "moe_combine: e_out, slot_pos, gates, y required");
+  moe::launch_combine(dims->act == MOE_BF16, e_out, slot_pos, gates, dims->T, dims->d_model,
+                      dims->top_k, y, (hipStream_t)stream);
+  return hip_status("moe_combine");
+}
+
+moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
+                          const int32_t *perm_src, moe_qlora gate, moe_qlora up, moe_qlora down,
+                          void *e_out, void *save, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_dims(dims));
+  REQUIRE(x && offsets && perm_src && e_out, "moe_expert_fwd: x, offsets, perm_src, e_out required");
+  TRY(check_qlora(gate, "gate"));
+  TRY(check_qlora(up, "up"));
+  TRY(check_qlora(down, "down"));
+  TRY(check_ws(dims, MOE_CALL_EXPERT_FWD, ws, ws_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = dims->act == MOE_BF16;
+  const int T = dims->T, d = dims->d_model, E = dims->n_experts, k = dims->top_k, f = dims->d_ff,
+            r = dims->rank, g = dims->group;
+  const size_t S = (size_t)T * k;
+  const float lam = dims->lora_scale;
+  FwdLayout L(dims);
+  void *sv = save ? save : at<char>(ws, L.save);
+  SaveLayout SL(dims);
+  float *Z = at<float>(sv, SL.Z);
+  void *Gs = at<char>(sv, SL.G), *Us = at<char>(sv, SL.U), *H = at<char>(sv, SL.H);
+  int2 *tiles = at<int2>(ws, L.tiles);
+  int *ntiles = at<int>(ws, L.ntiles);
+  const int BM = moe::simple_tile_rows();
+  const int mt = (int)max_tiles(dims, BM);
+  moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
+
+  // Z_g = X A_g, Z_u = X A_u (rows gathered from x)
+  moe::ProjArgs P{};
+  P.a = x; P.lda = d; P.gather = true; P.perm_src = perm_src; P.kk = k;
+  P.tiles = tiles; P.ntiles = ntiles; P.max_tiles = mt; P.offsets = offsets;
+  P.m_es = (size_t)d * r; P.m_cs = r; P.m_js = 1; P.K = d; P.r = r; P.s = 1.f; P.ldz = 3 * r;
+  P.m = gate.A; P.Z = Z;
+  moe::launch_proj_simple(bf, P, st);
+  P.m = up.A; P.Z = Z + r;
+  moe::launch_proj_simple(bf, P, st);
+
+  // G, U in float32, then SwiGLU
+  float *G32 = at<float>(ws, L.G32), *U32 = at<float>(ws, L.U32);
+  moe::LinArgs A{};
+  A.a = x; A.lda = d; A.gather = true; A.perm_src = perm_src; A.kk = k;
+  A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
+  A.N = f; A.K = d; A.g = g; A.trans = false; A.ldz = 3 * r;
+  A.l_es = (size_t)r * f; A.l_js = f; A.l_ns = 1; A.r = r; A.lam = lam; A.ldo = f;
+  A.acc_out = false;
+  A.q = gate.q; A.scale = gate.scale; A.Z = Z; A.lmat = gate.B; A.out = G32;
+  moe::launch_lin_simple(bf, true, A, st);
+  A.q = up.q; A.scale = up.scale; A.Z = Z + r; A.lmat = up.B; A.out = U32;
+  moe::launch_lin_simple(bf, true, A, st);
+  moe::launch_swiglu_fwd(bf, G32, U32, S * f, H, Gs, Us, st);
+
+  // Z_d = H A_d, then O = H W_d^T + lam Z_d B_d
+  P.a = H; P.lda = f; P.gather = false; P.m = down.A; P.m_es = (size_t)f * r; P.m_cs = r;
+  P.K = f; P.Z = Z + 2 * r;
+  moe::launch_proj_simple(bf, P, st);
+  A.a = H; A.lda = f; A.gather = false; A.N = d; A.K = f; A.q = down.q; A.scale = down.scale;
+  A.Z = Z + 2 * r; A.lmat = down.B; A.l_es = (size_t)r * d; A.l_js = d; A.out = e_out; A.ldo = d;
+  moe::launch_lin_simple(bf, false, A, st);
+  return hip_status("moe_expert_fwd");
+}
+
+moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
+                           const int32_t *topk_idx, const float *gates, const int32_t *offsets,
+                           const int32_t *perm_src, const int32_t *slot_pos,
+                           const float *w_router, moe_qlora gate, moe_qlora up, moe_qlora down,
+                           const void *e_out, const void *save, void *dx, float *dA_gate,
+                           float *dB_gate, float *dA_up, float *dB_up, float *dA_down,
+                           float *dB_down, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_dims(dims));
+  REQUIRE(dy && x && topk_idx && gates && offsets && perm_src && slot_pos && w_router && e_out &&
+              save && dx,
+          "moe_adapter_bwd: every tensor argument is required");
+  REQUIRE(dA_gate && dB_gate && dA_up && dB_up && dA_down && dB_down,
+          "moe_adapter_bwd: all six adapter-gradient outputs are required");
+  TRY(check_qlora(gate, "gate"));
+  TRY(check_qlora(up, "up"));
+  TRY(check_qlora(down, "down"));
+  TRY(check_ws(dims, MOE_CALL_ADAPTER_BWD, ws, ws_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = dims->act == MOE_BF16;
+  const int T = dims->T, d = dims->d_model, E = dims->n_experts, k = dims->top_k, f = dims->d_ff,
+            r = dims->rank, g = dims->group;
+  const size_t S = (size_t)T * k;
+  const float lam = dims->lora_scale;
+  BwdLayout L(dims);
+  SaveLayout SL(dims);
+  const float *Z = at<const float>((void *)save, SL.Z);
+  const void *Gs = at<const char>((void *)save, SL.G), *Us = at<const char>((void *)save, SL.U),
+             *H = at<const char>((void *)save, SL.H);
+  int2 *tiles = at<int2>(ws, L.tiles);
+  int *ntiles = at<int>(ws, L.ntiles);
+  float *wr_t = at<float>(ws, L.wr_t), *dx_r = at<float>(ws, L.dx_r);
+  void *dO = at<char>(ws, L.dO);
+  float *dZ = at<float>(ws, L.dZ), *dH32 = at<float>(ws, L.dH32), *dXp = at<float>(ws, L.dXp);
+  void *dG = at<char>(ws, L.dG), *dU = at<char>(ws, L.dU);
+  const int BM = moe::simple_tile_rows();
+  const int mt = (int)max_tiles(dims, BM);
+  moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
+
+  // gate path and dO = gamma * dy in permuted order
+  moe::launch_transpose_f32(w_router, d, E, wr_t, st);
+  moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r, dO, st);
+
+  // down: dZ_d = lam dO B_d^T; dB_d = lam Z_d^T dO; dH = dO W_d + dZ_d A_d^T
+  moe::ProjArgs P{};
+  P.a = dO; P.lda = d; P.gather = false; P.perm_src = perm_src; P.kk = k;
+  P.tiles = tiles; P.ntiles = ntiles; P.max_tiles = mt; P.offsets = offsets;
+  P.m = down.B; P.m_es = (size_t)r * d; P.m_cs = 1; P.m_js = d; P.K = d; P.r = r; P.s = lam;
+  P.Z = dZ + 2 * r; P.ldz = 3 * r;
+  moe::launch_proj_simple(bf, P, st);
+  moe::WgradArgs W{};
+  W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E;
+  W.l = Z + 2 * r; W.ldl = 3 * r; W.l_f32 = true; W.gather = false;
+  W.r = dO; W.ldr = d; W.Aw = r; W.Bw = d; W.s = lam; W.out = dB_down;
+  moe::launch_wgrad_simple(bf, W, st);
+  moe::LinArgs A{};
+  A.a = dO; A.lda = d; A.gather = false; A.perm_src = perm_src; A.kk = k;
+  A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
+  A.q = down.q; A.scale = down.scale; A.N = f; A.K = d; A.g = g; A.trans = true;
+  A.Z = dZ + 2 * r; A.ldz = 3 * r; A.lmat = down.A; A.l_es = (size_t)f * r; A.l_js = 1;
+  A.l_ns = r; A.r = r; A.lam = 1.f; A.out = dH32; A.ldo = f; A.acc_out = false;
+  moe::launch_lin_simple(bf, true, A, st);
+  // SwiGLU backward; dA_d = H^T dZ_d
+  moe::launch_swiglu_bwd(bf, dH32, Gs, Us, S * f, dG, dU, st);
+  W.l = H; W.ldl = f; W.l_f32 = false; W.r = dZ + 2 * r; W.ldr = 3 * r; W.Aw = f; W.Bw = r;
+  W.s = 1.f; W.out = dA_down;
+  moe::launch_wgrad_simple(bf, W, st);
+
+  // gate / up: dZ = lam dG B^T; dB = lam Z^T dG; dA = X^T dZ
+  P.m_es = (size_t)r * f; P.m_cs = 1; P.m_js = f; P.K = f; P.lda = f;
+  P.a = dG; P.m = gate.B; P.Z = dZ;
+  moe::launch_proj_simple(bf, P, st);
+  P.a = dU; P.m = up.B; P.Z = dZ + r;
+  moe::launch_proj_simple(bf, P, st);
+  W.l = Z; W.ldl = 3 * r; W.l_f32 = true; W.r = dG; W.ldr = f; W.Aw = r; W.Bw = f; W.s = lam;
+  W.out = dB_gate;
+  moe::launch_wgrad_simple(bf, W, st);
+  W.l = Z + r; W.r = dU; W.out = dB_up;
+  moe::launch_wgrad_simple(bf, W, st);
+  W.l = x; W.ldl = d; W.l_f32 = false; W.gather = true; W.r = dZ; W.ldr = 3 * r; W.Aw = d;
+  W.Bw = r; W.s = 1.f; W.out = dA_gate;
+  moe::launch_wgrad_simple(bf, W, st);
+  W.r = dZ + r; W.out = dA_up;
+  moe::launch_wgrad_simple(bf, W, st);
+
+  // dX_perm = dG W_g + dZ_g A_g^T + dU W_u + dZ_u A_u^T   (float32)
+  A.a = dG; A.lda = f; A.q = gate.q; A.scale = gate.scale; A.N = d; A.K = f;
+  A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)d * r; A.l_js = 1; A.l_ns = r;
+  A.out = dXp; A.ldo = d; A.acc_out = false;
+  moe::launch_lin_simple(bf, true, A, st);
+  A.a = dU; A.q = up.q; A.scale = up.scale; A.Z = dZ + r; A.lmat = up.A; A.acc_out = true;
+  moe::launch_lin_simple(bf, true, A, st);
+
+  moe::launch_unpermute_sum(bf, true, dx_r, dXp, slot_pos, T, d, k, dx, st);
+  return hip_status("moe_adapter_bwd");
+}
+
+}  // extern "C"

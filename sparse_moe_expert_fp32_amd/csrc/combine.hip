@@ -1,0 +1,238 @@
+// Per-token kernels: gate-weighted combine, the gate/router part of the
+// backward, and the final gather of the expert input-gradients.
+//
+// Each token gathers its own k rows in ascending slot order with a float32
+// accumulator, so no float atomics are needed and results are reproducible
+// bit for bit.  The mixing of the selected experts' outputs by the routing
+// weights is the routed-expert layer of the skill card "Reversible Sparse
+// MoE Single Node" (Architecture Details, top-k routing); the gradient
+// through the gates into the router input follows from the full-precision
+// router of the same card (Implementation Considerations, TQP Quantization),
+// whose own weights are not trained here.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Vector of VEC elements of T loaded as 16 bytes.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  static DEV void ld(const float *p, float *v) {
+    float4 a = *reinterpret_cast<const float4 *>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+  static DEV void st(float *p, const float *v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  static DEV void ld(const bf16_t *p, float *v) {
+    uint4 a = *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static DEV void st(bf16_t *p, const float *v) {
+    uint4 a;
+    a.x = pack2bf(v[0], v[1]); a.y = pack2bf(v[2], v[3]);
+    a.z = pack2bf(v[4], v[5]); a.w = pack2bf(v[6], v[7]);
+    *reinterpret_cast<uint4 *>(p) = a;
+  }
+};
+
+// y[t] = sum_j gates[t][j] * e_out[slot_pos[t*k+j]]
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ e_out,
+                                                      const int32_t *__restrict__ slot_pos,
+                                                      const float *__restrict__ gates, int d,
+                                                      int k, T *__restrict__ y) {
+  constexpr int V = Vec16<T>::N;
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * V; c < d; c += 256 * V) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float g = gates[(size_t)t * k + j];
+      int p = slot_pos[(size_t)t * k + j];
+      float v[V];
+      Vec16<T>::ld(e_out + (size_t)p * d + c, v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    Vec16<T>::st(y + (size_t)t * d + c, acc);
+  }
+}
+
+// out[e][c] = in[c][e]   (W_r [d][E] -> [E][d] so that a token's router
+// columns are read with unit stride)
+__global__ void transpose_f32_kernel(const float *__restrict__ in, int rows, int cols,
+                                     float *__restrict__ out) {
+  __shared__ float tile[32][33];
+  int bx = blockIdx.x * 32, by = blockIdx.y * 32;
+  int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
+  for (int i = ty; i < 32; i += 8) {
+    int r = by + i, c = bx + tx;
+    tile[i][tx] = (r < rows && c < cols) ? in[(size_t)r * cols + c] : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    int r = bx + i, c = by + tx;  // out row = input column
+    if (r < cols && c < rows) out[(size_t)r * rows + c] = tile[tx][i];
+  }
+}
+
+// Block-wide sum of KMAX-wide partial vectors in a fixed tree order.
+template <int KMAX>
+DEV void block_sum(float (&v)[KMAX], int k, float *red /*[4][KMAX]*/) {
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      float s = v[j];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) red[wave * KMAX + j] = s;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k) v[j] = (red[j] + red[KMAX + j]) + (red[2 * KMAX + j] + red[3 * KMAX + j]);
+  __syncthreads();
+}
+
+// Per token t (one block):
+//   dgamma_j = <dy_t, e_out[p_j]>,  dl_j = gamma_j (dgamma_j - sum_i gamma_i dgamma_i)
+//   dx_r[t]  = sum_j dl_j * W_r[:, e_j]      (float32)
+//   dO[p_j]  = gamma_j * dy_t                (act dtype, permuted order)
+template <typename T>
+__global__ __launch_bounds__(256) void gate_grad_kernel(
+    const T *__restrict__ dy, const T *__restrict__ e_out, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ gates, const int32_t *__restrict__ slot_pos,
+    const float *__restrict__ wr_t, int d, int k, float *__restrict__ dx_r, T *__restrict__ dO) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ float red[4 * 32];
+  __shared__ int sp[32], se[32];
+  __shared__ float sg[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    sp[threadIdx.x] = slot_pos[(size_t)t * k + threadIdx.x];
+    se[threadIdx.x] = topk_idx[(size_t)t * k + threadIdx.x];
+    sg[threadIdx.x] = gates[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  float part[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) part[j] = 0.f;
+  for (int c = threadIdx.x * V; c < d; c += 256 * V) {
+    float g[V];
+    Vec16<T>::ld(dy + (size_t)t * d + c, g);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j < k) {
+        float o[V];
+        Vec16<T>::ld(e_out + (size_t)sp[j] * d + c, o);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) s = fmaf(g[i], o[i], s);
+        part[j] += s;
+      }
+    }
+  }
+  block_sum<32>(part, k, red);
+  float mean = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    if (j < k) mean = fmaf(sg[j], part[j], mean);
+  for (int c = threadIdx.x * V; c < d; c += 256 * V) {
+    float g[V], acc[V];
+    Vec16<T>::ld(dy + (size_t)t * d + c, g);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j >= k) break;
+      float dl = sg[j] * (part[j] - mean);
+      const float *w = wr_t + (size_t)se[j] * d + c;
+      float o[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) { acc[i] = fmaf(dl, w[i], acc[i]); o[i] = sg[j] * g[i]; }
+      Vec16<T>::st(dO + (size_t)sp[j] * d + c, o);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) dx_r[(size_t)t * d + c + i] = acc[i];
+  }
+}
+
+// dx[t] = dx_r[t] + sum_j dxp[slot_pos[t*k+j]]   (j ascending)
+template <typename T, typename TP>
+__global__ __launch_bounds__(256) void unpermute_sum_kernel(const float *__restrict__ dx_r,
+                                                            const TP *__restrict__ dxp,
+                                                            const int32_t *__restrict__ slot_pos,
+                                                            int d, int k, T *__restrict__ dx) {
+  constexpr int V = Vec16<T>::N;
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * V; c < d; c += 256 * V) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = dx_r[(size_t)t * d + c + i];
+    for (int j = 0; j < k; ++j) {
+      int p = slot_pos[(size_t)t * k + j];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += Elem<TP>::ld(dxp, (size_t)p * d + c + i);
+    }
+    Vec16<T>::st(dx + (size_t)t * d + c, acc);
+  }
+}
+
+void launch_combine(bool bf16, const void *e_out, const int32_t *slot_pos, const float *gates,
+                    int Tn, int d, int k, void *y, hipStream_t st) {
+  if (bf16)
+    combine_kernel<bf16_t><<<Tn, 256, 0, st>>>((const bf16_t *)e_out, slot_pos, gates, d, k,
+                                               (bf16_t *)y);
+  else
+    combine_kernel<float><<<Tn, 256, 0, st>>>((const float *)e_out, slot_pos, gates, d, k,
+                                              (float *)y);
+}
+
+void launch_transpose_f32(const float *in, int rows, int cols, float *out, hipStream_t st) {
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32);
+  transpose_f32_kernel<<<grid, 256, 0, st>>>(in, rows, cols, out);
+}
+
+void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_t *topk_idx,
+                      const float *gates, const int32_t *slot_pos, const float *wr_t, int Tn,
+                      int d, int k, float *dx_r, void *dO, hipStream_t st) {
+  if (bf16)
+    gate_grad_kernel<bf16_t><<<Tn, 256, 0, st>>>((const bf16_t *)dy, (const bf16_t *)e_out,
+                                                 topk_idx, gates, slot_pos, wr_t, d, k, dx_r,
+                                                 (bf16_t *)dO);
+  else
+    gate_grad_kernel<float><<<Tn, 256, 0, st>>>((const float *)dy, (const float *)e_out,
+                                                topk_idx, gates, slot_pos, wr_t, d, k, dx_r,
+                                                (float *)dO);
+}
+
+void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void *dxp,
+                          const int32_t *slot_pos, int Tn, int d, int k, void *dx,
+                          hipStream_t st) {
+  if (bf16) {
+    if (dxp_f32)
+      unpermute_sum_kernel<bf16_t, float><<<Tn, 256, 0, st>>>(dx_r, (const float *)dxp, slot_pos,
+                                                              d, k, (bf16_t *)dx);
+    else
+      unpermute_sum_kernel<bf16_t, bf16_t><<<Tn, 256, 0, st>>>(dx_r, (const bf16_t *)dxp,
+                                                               slot_pos, d, k, (bf16_t *)dx);
+  } else {
+    unpermute_sum_kernel<float, float><<<Tn, 256, 0, st>>>(dx_r, (const float *)dxp, slot_pos, d,
+                                                           k, (float *)dx);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,64 @@
+// Host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (route.hip)
+size_t route_ws_bytes(int T, int d, int E);
+void launch_route(bool bf16, const void *x, const float *wr, const float *bias, int T, int d,
+                  int E, int k, int32_t *topk_idx, float *gates, float *logits, void *ws,
+                  hipStream_t st);
+
+// ---- permutation (permute.hip)
+size_t permute_ws_bytes(int T, int E, int k);
+void launch_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
+                    int32_t *perm_src, int32_t *slot_pos, const void *x, void *x_perm,
+                    int row_bytes, void *ws, hipStream_t st);
+
+// ---- per-token kernels (combine.hip)
+void launch_combine(bool bf16, const void *e_out, const int32_t *slot_pos, const float *gates,
+                    int T, int d, int k, void *y, hipStream_t st);
+void launch_transpose_f32(const float *in, int rows, int cols, float *out, hipStream_t st);
+void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_t *topk_idx,
+                      const float *gates, const int32_t *slot_pos, const float *wr_t, int T,
+                      int d, int k, float *dx_r, void *dO, hipStream_t st);
+void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void *dxp,
+                          const int32_t *slot_pos, int T, int d, int k, void *dx,
+                          hipStream_t st);
+
+// ---- float32 expert kernels (expert_simple.hip)
+void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles,
+                        hipStream_t st);
+int simple_tile_rows();
+
+struct LinArgs {
+  const void *a; int lda; bool gather; const int32_t *perm_src; int kk;
+  const int2 *tiles; const int *ntiles; int max_tiles; const int32_t *offsets;
+  const uint8_t *q; const uint16_t *scale; int N, K, g; bool trans;
+  const float *Z; int ldz; const void *lmat; size_t l_es; int l_js, l_ns, r; float lam;
+  void *out; int ldo; bool acc_out;
+};
+void launch_lin_simple(bool act_bf16, bool out_f32, const LinArgs &L, hipStream_t st);
+
+struct ProjArgs {
+  const void *a; int lda; bool gather; const int32_t *perm_src; int kk;
+  const int2 *tiles; const int *ntiles; int max_tiles; const int32_t *offsets;
+  const void *m; size_t m_es; int m_cs, m_js; int K, r; float s; float *Z; int ldz;
+};
+void launch_proj_simple(bool act_bf16, const ProjArgs &P, hipStream_t st);
+
+struct WgradArgs {
+  const void *l; int ldl; bool l_f32; bool gather; const int32_t *perm_src; int kk;
+  const void *r; int ldr; const int32_t *offsets; int E, Aw, Bw; float s; float *out;
+};
+void launch_wgrad_simple(bool act_bf16, const WgradArgs &W, hipStream_t st);
+
+void launch_swiglu_fwd(bool act_bf16, const float *G, const float *U, size_t n, void *H,
+                       void *Gs, void *Us, hipStream_t st);
+void launch_swiglu_bwd(bool act_bf16, const float *dH, const void *Gs, const void *Us, size_t n,
+                       void *dG, void *dU, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,110 @@
+"""Device buffers for one layer and the call sequence of the five entry points.
+
+This is plumbing around the C ABI: it uploads the (numpy) inputs once,
+allocates outputs and workspaces with torch, and calls the library in the
+order route -> permute -> expert_fwd -> combine [-> adapter_bwd].  No
+arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+MATS = ("gate", "up", "down")
+
+
+def to_device(a, device):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_numpy(t):
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class DeviceLayer:
+    def __init__(self, cfg, inputs: dict, device: str = "cuda", want_logits: bool = False,
+                 want_x_perm: bool = False, with_backward: bool | None = None):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        self.dm = B.dims_of(cfg)
+        T, d, E, k, f, r = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.r
+        S = T * k
+        act = torch.float32 if cfg.act == "f32" else torch.bfloat16
+        self.t = {key: to_device(v, self.dev) for key, v in inputs.items()}
+        self.w = {m: B.qlora(self.t[f"q_{m}"], self.t[f"s_{m}"], self.t[f"A_{m}"],
+                             self.t[f"B_{m}"]) for m in MATS}
+        z = lambda *shape, dtype=act: torch.empty(shape, dtype=dtype, device=self.dev)
+        i32, f32 = torch.int32, torch.float32
+        self.topk_idx, self.gates = z(T, k, dtype=i32), z(T, k, dtype=f32)
+        self.logits = z(T, E, dtype=f32) if want_logits else None
+        self.counts, self.offsets = z(E, dtype=i32), z(E + 1, dtype=i32)
+        self.perm_src, self.slot_pos = z(S, dtype=i32), z(S, dtype=i32)
+        self.x_perm = z(S, d) if want_x_perm else None
+        self.e_out, self.y = z(S, d), z(T, d)
+        bwd = cfg.train if with_backward is None else with_backward
+        self.save = (torch.empty(B.moe_save_size(self.dm), dtype=torch.uint8, device=self.dev)
+                     if bwd else None)
+        calls = (B.CALL_ROUTE, B.CALL_PERMUTE, B.CALL_EXPERT_FWD, B.CALL_COMBINE) + \
+            ((B.CALL_ADAPTER_BWD,) if bwd else ())
+        self.ws = {c: torch.empty(max(1, B.moe_workspace_size(self.dm, c)), dtype=torch.uint8,
+                                  device=self.dev) for c in calls}
+        if bwd:
+            self.dx = z(T, d)
+            self.grads = {"dA_gate": z(E, d, r, dtype=f32), "dB_gate": z(E, r, f, dtype=f32),
+                          "dA_up": z(E, d, r, dtype=f32), "dB_up": z(E, r, f, dtype=f32),
+                          "dA_down": z(E, f, r, dtype=f32), "dB_down": z(E, r, d, dtype=f32)}
+
+    # ---- the five calls
+    def route(self, stream=None):
+        t = self.t
+        B.moe_route(self.dm, t["x"], t["w_router"], t.get("b_router"), self.topk_idx, self.gates,
+                    self.logits, self.ws[B.CALL_ROUTE], stream)
+
+    def permute(self, stream=None):
+        B.moe_permute(self.dm, self.topk_idx, self.t["x"], self.counts, self.offsets,
+                      self.perm_src, self.slot_pos, self.x_perm, self.ws[B.CALL_PERMUTE], stream)
+
+    def expert_fwd(self, stream=None):
+        B.moe_expert_fwd(self.dm, self.t["x"], self.offsets, self.perm_src, self.w["gate"],
+                         self.w["up"], self.w["down"], self.e_out, self.save,
+                         self.ws[B.CALL_EXPERT_FWD], stream)
+
+    def combine(self, stream=None):
+        B.moe_combine(self.dm, self.e_out, self.slot_pos, self.gates, self.y, None, stream)
+
+    def adapter_bwd(self, stream=None):
+        t, g = self.t, self.grads
+        B.moe_adapter_bwd(self.dm, t["dy"], t["x"], self.topk_idx, self.gates, self.offsets,
+                          self.perm_src, self.slot_pos, t["w_router"], self.w["gate"],
+                          self.w["up"], self.w["down"], self.e_out, self.save, self.dx,
+                          g["dA_gate"], g["dB_gate"], g["dA_up"], g["dB_up"], g["dA_down"],
+                          g["dB_down"], self.ws[B.CALL_ADAPTER_BWD], stream)
+
+    def forward(self, stream=None):
+        self.route(stream)
+        self.permute(stream)
+        self.expert_fwd(stream)
+        self.combine(stream)
+
+    def train_step(self, stream=None):
+        self.forward(stream)
+        self.adapter_bwd(stream)
+
+    # ---- results on the host
+    def routing(self) -> dict:
+        out = {n: to_numpy(getattr(self, n)) for n in
+               ("topk_idx", "gates", "counts", "offsets", "perm_src", "slot_pos")}
+        if self.logits is not None:
+            out["logits"] = to_numpy(self.logits)
+        return out

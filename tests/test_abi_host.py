@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, and rejects bad arguments with the
+documented status before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_tqp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*|int32_t)\s*(moe_\w+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from sparse_moe_expert_fp32_amd import binding
+    return binding
+
+
+def test_header_declares_the_five_calls():
+    fns = declared_functions()
+    for name in ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(B.EXPORTS)
+    assert B.moe_abi_version() == 1
+
+
+def good(B, **kw):
+    base = dict(T=64, d=128, E=8, k=2, f=256, r=4, group=32, act="f32")
+    base.update(kw)
+    return B.dims(**base)
+
+
+def test_workspace_and_save_sizes(B):
+    dm = good(B)
+    for c in range(5):
+        assert B.moe_workspace_size(dm, c) >= 0
+    assert B.moe_save_size(dm) > 0
+    big = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16")
+    assert B.moe_save_size(big) >= 8192 * 12 * 768 * 2 * 3
+
+
+BAD = [
+    (dict(T=0), -1), (dict(E=0), -1), (dict(E=1025), -1), (dict(k=0), -1), (dict(k=9), -1),
+    (dict(E=64, k=33), -1), (dict(r=0), -1), (dict(r=33), -1), (dict(group=16), -2),
+    (dict(group=48), -2), (dict(act=7), -2), (dict(d=80), -1), (dict(f=200), -1),
+    (dict(T=1 << 24, k=8, E=16), -1), (dict(d=0), -1),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_invalid_dims_rejected(B, kw, code):
+    dm = good(B, **kw)
+    out = ctypes.c_size_t(12345)
+    st = B.LIB.moe_workspace_size(ctypes.byref(dm), 0, ctypes.byref(out))
+    assert st == code
+    assert out.value == 12345                       # nothing written
+    assert B.LIB.moe_last_error().decode()
+
+
+def test_nonfinite_scale_rejected(B):
+    dm = good(B, lora_scale=float("nan"))
+    assert B.LIB.moe_save_size(ctypes.byref(dm), ctypes.byref(ctypes.c_size_t())) == -1
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any HIP call
+
+
+def test_null_pointers_rejected_before_launch(B):
+    dm = good(B)
+    L = B.LIB
+    P = FAKE
+    q = B.QLora(P, P, P, P)
+    qnull = B.QLora(P, None, P, P)
+    assert L.moe_route(ctypes.byref(dm), None, P, None, P, P, None, P, 1 << 30, None) == -1
+    assert L.moe_permute(ctypes.byref(dm), P, None, P, P, None, P, None, P, 1 << 30, None) == -1
+    assert L.moe_permute(ctypes.byref(dm), P, None, P, P, P, P, P, P, 1 << 30, None) == -1
+    assert L.moe_expert_fwd(ctypes.byref(dm), P, P, P, q, qnull, q, P, None, P, 1 << 30,
+                            None) == -1
+    assert "up" in L.moe_last_error().decode()
+    assert L.moe_combine(ctypes.byref(dm), P, None, P, P, None, 0, None) == -1
+    assert L.moe_adapter_bwd(ctypes.byref(dm), P, P, P, P, P, P, P, P, q, q, q, P, None, P,
+                             P, P, P, P, P, P, P, 1 << 30, None) == -1
+    assert L.moe_route(None, P, P, None, P, P, None, P, 1 << 30, None) == -1
+
+
+def test_small_workspace_rejected(B):
+    dm = good(B)
+    L = B.LIB
+    P = FAKE
+    need = B.moe_workspace_size(dm, B.CALL_ROUTE)
+    assert need > 0
+    assert L.moe_route(ctypes.byref(dm), P, P, None, P, P, None, P, need - 1, None) == -3
+    assert L.moe_route(ctypes.byref(dm), P, P, None, P, P, None, None, need, None) == -3
+    q = B.QLora(P, P, P, P)
+    need = B.moe_workspace_size(dm, B.CALL_EXPERT_FWD)
+    assert L.moe_expert_fwd(ctypes.byref(dm), P, P, P, q, q, q, P, None, P, need - 1, None) == -3
+    assert "workspace" in L.moe_last_error().decode()
+
+
+def test_status_strings(B):
+    assert B.LIB.moe_status_string(0) == b"MOE_OK"
+    assert B.LIB.moe_status_string(-3) == b"MOE_ERR_WORKSPACE"
+    assert B.LIB.moe_status_string(-99) == b"MOE_ERR_UNKNOWN"

@@ -1,0 +1,141 @@
+"""GPU parity of the HIP library against the fp64 oracle, through the C ABI.
+
+Shapes the oracle finishes in seconds, spanning several tiles with ragged
+tails, plus the edge cases of the layer.  The full-size shapes are in
+test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity import ADAPTERS, check_routing, full_parity, rel_l2, run_gpu
+from sparse_moe_expert_fp32_amd import configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def cfg_of(**kw):
+    base = dict(name="t", cfg_id=200, T=300, d=256, E=16, k=4, f=384, r=16, group=128,
+                act="bf16", router_bias_var=0.3, train=True)
+    base.update(kw)
+    return configs.LayerConfig(**base)
+
+
+def show(name, rep):
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.2e}" if isinstance(v, float) else f"{k}={v}"
+                                          for k, v in rep.items()), flush=True)
+
+
+def test_tiny_f32_forward_backward(cuda_ok):
+    cfg = configs.C1
+    inp = inputs.generate(cfg, 0)
+    rep, _ = full_parity(cfg, inp)
+    show("C1", rep)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_small_bf16_forward_backward(cuda_ok, group):
+    cfg = cfg_of(group=group, cfg_id=210 + group)
+    rep, _ = full_parity(cfg, inputs.generate(cfg, 0))
+    show(f"bf16 g{group}", rep)
+
+
+def test_small_f32_ragged(cuda_ok):
+    cfg = cfg_of(act="f32", T=77, d=192, E=12, k=3, f=160, r=5, group=32, cfg_id=220)
+    rep, _ = full_parity(cfg, inputs.generate(cfg, 1))
+    show("f32 ragged", rep)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=1, cfg_id=230),                               # one token
+    dict(T=37, k=1, cfg_id=231),                         # k = 1, ragged T
+    dict(E=8, k=8, T=50, cfg_id=232),                    # k = E
+    dict(E=70, k=5, T=129, cfg_id=233),                  # E not a multiple of 64
+    dict(E=130, k=12, T=64, cfg_id=234, router_bias_var=0.0),  # many empty experts
+])
+def test_edge_shapes(cuda_ok, kw):
+    cfg = cfg_of(**kw)
+    rep, gpu = full_parity(cfg, inputs.generate(cfg, 0))
+    show(f"edge {kw}", rep)
+
+
+def test_routing_collapse_to_one_expert(cuda_ok):
+    cfg = cfg_of(T=200, E=10, k=1, cfg_id=240)
+    inp = inputs.generate(cfg, 0)
+    b = np.zeros(cfg.E, np.float32)
+    b[3] = 1e4
+    inp["b_router"] = b
+    rep, gpu = full_parity(cfg, inp)
+    assert gpu["counts"][3] == cfg.T and gpu["counts"].sum() == cfg.T
+    for n in ADAPTERS:
+        assert np.all(np.delete(gpu[n], 3, axis=0) == 0.0)
+    show("collapse", rep)
+
+
+def test_router_dyadic_bit_exact(cuda_ok):
+    """x in {i/16}, W_r in {j/64}: every fp32 partial sum is exact, so the GPU
+    logits equal the oracle's bit for bit and routing needs no tie exemption."""
+    for act in ("f32", "bf16"):
+        cfg = cfg_of(act=act, T=256, d=512, E=100, k=12, cfg_id=250, router_bias_var=0.0)
+        inp = inputs.generate(cfg, 0)
+        rng = np.random.default_rng(7)
+        xi = rng.integers(-64, 65, (cfg.T, cfg.d)).astype(np.float32) / 16
+        inp["x"] = xi if act == "f32" else inputs.bf16_bits(xi)
+        inp["w_router"] = rng.integers(-64, 65, (cfg.d, cfg.E)).astype(np.float32) / 64
+        gpu, _ = run_gpu(cfg, inp, backward=False)
+        l64 = oracle.router_logits(inp["x"], inp["w_router"])
+        assert np.array_equal(gpu["logits"].astype(np.float64), l64)
+        assert np.array_equal(gpu["topk_idx"], oracle.topk(l64, cfg.k))
+
+
+def test_router_exact_ties_lower_index(cuda_ok):
+    cfg = cfg_of(T=128, E=20, k=5, cfg_id=251, router_bias_var=0.0)
+    inp = inputs.generate(cfg, 0)
+    w = inp["w_router"]
+    w[:, 9] = w[:, 2]
+    w[:, 15] = w[:, 2]
+    gpu, _ = run_gpu(cfg, inp, backward=False)
+    assert np.array_equal(gpu["logits"][:, 2], gpu["logits"][:, 9])
+    l64 = oracle.router_logits(inp["x"], w)
+    ref = oracle.topk(l64, cfg.k)
+    for t in range(cfg.T):
+        row = gpu["topk_idx"][t].tolist()
+        for a, b in ((2, 9), (2, 15), (9, 15)):
+            if a in row and b in row:
+                assert row.index(a) < row.index(b)
+            if b in row:
+                assert a in row
+    check_routing(cfg, gpu, l64)
+    assert (gpu["topk_idx"] == ref).all(axis=1).mean() > 0.99
+
+
+def test_permute_on_oracle_indices(cuda_ok):
+    """moe_permute alone, fed the oracle's selection: exact, no exemption."""
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
+    cfg = cfg_of(T=1000, E=460, k=12, d=128, f=128, cfg_id=252)
+    inp = inputs.generate(cfg, 0)
+    idx = oracle.route(inp, cfg.k)["topk_idx"]
+    L = DeviceLayer(cfg, inp, want_x_perm=True, with_backward=False)
+    L.topk_idx.copy_(torch.from_numpy(idx))
+    L.permute()
+    torch.cuda.synchronize()
+    ref = oracle.permutation(idx, cfg.E)
+    for name, r in zip(("counts", "offsets", "perm_src", "slot_pos"), ref):
+        assert np.array_equal(to_numpy(getattr(L, name)), r), name
+    xp = to_numpy(L.x_perm)
+    assert np.array_equal(xp, inp["x"][ref[2] // cfg.k])
+
+
+def test_bitwise_deterministic(cuda_ok):
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import to_numpy
+    cfg = cfg_of(T=500, E=40, k=6, cfg_id=260)
+    inp = inputs.generate(cfg, 0)
+    a, L = run_gpu(cfg, inp)
+    L.train_step()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy(L.y), a["y"])
+    assert np.array_equal(to_numpy(L.dx), a["dx"])
+    for n in ADAPTERS:
+        assert np.array_equal(to_numpy(L.grads[n]), a[n]), n
