@@ -81,10 +81,10 @@ typedef struct {
  *         K; nibble slot j (bits 4j..4j+3) holds k_{2j} for j < 4 and
  *         k_{2(j-4)+1} for j >= 4.
  *   scale bf16  [E][N][K/g]: W_hat[n][c] = scale[n][c/g] * q[n][c].
- *   A     act   [E][K][r]
- *   B     act   [E][r][N]
- * Effective matrix: W_eff = W_hat + lambda * (A B)^T, i.e. for a row x,
- * x W_eff^T = x W_hat^T + lambda (x A) B. */
+ *   A     act   [E][r][K]   (out x in, like the base)
+ *   B     act   [E][N][r]
+ * Effective matrix: W_eff = W_hat + lambda * B A, i.e. for a row x,
+ * x W_eff^T = x W_hat^T + lambda (x A^T) B^T. */
 typedef struct {
   const uint8_t *q;
   const uint16_t *scale;
@@ -134,9 +134,9 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
 
 /* Expert FFNs over the permuted rows.  For every position p with expert e
  * (offsets[e] <= p < offsets[e+1]) and input row X = x[perm_src[p] / k]:
- *   G = X Wg_hat^T + lambda (X A_g) B_g,   U = X Wu_hat^T + lambda (X A_u) B_u
+ *   G = X Wg_hat^T + lambda (X A_g^T) B_g^T,  U likewise with the up matrix,
  *   H = silu(G) * U,   silu(z) = z / (1 + exp(-z))
- *   e_out[p] = H Wd_hat^T + lambda (H A_d) B_d
+ *   e_out[p] = H Wd_hat^T + lambda (H A_d^T) B_d^T
  * Arithmetic: MOE_F32 computes in float32 throughout; MOE_BF16 feeds bf16
  * operands to the matrix cores with float32 accumulation and rounds H and
  * e_out to bf16 (each once, to nearest even).
@@ -164,17 +164,17 @@ moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *s
  *   dgamma[t][j] = <dy_t, e_out[slot_pos[t,j]]>,
  *   dl[t][j] = gamma[t][j] (dgamma[t][j] - sum_i gamma[t][i] dgamma[t][i]),
  *   dx[t] = sum_j dl[t][j] w_router[:, e_{t,j}]  +  sum_j dX_expert(t, j)
- * with, per expert and dO = gamma * dy on its rows:
- *   dB_d = lambda (H A_d)^T dO, dZ_d = lambda dO B_d^T, dA_d = H^T dZ_d,
- *   dH = dO Wd_hat + dZ_d A_d^T,  dG = dH U s (1 + G (1 - s)), dU = dH G s,
- *   s = sigmoid(G); dB_g = lambda (X A_g)^T dG, dZ_g = lambda dG B_g^T,
- *   dA_g = X^T dZ_g (likewise up), dX = dG Wg_hat + dU Wu_hat + dZ_g A_g^T
- *   + dZ_u A_u^T.
+ * with, per expert, Z = X A^T of each matrix and dO = gamma * dy on its rows:
+ *   dB_d = lambda dO^T Z_d, dZ_d = lambda dO B_d, dA_d = dZ_d^T H,
+ *   dH = dO Wd_hat + dZ_d A_d,  dG = dH U s (1 + G (1 - s)), dU = dH G s,
+ *   s = sigmoid(G); dB_g = lambda dG^T Z_g, dZ_g = lambda dG B_g,
+ *   dA_g = dZ_g^T X (likewise up), dX = dG Wg_hat + dU Wu_hat + dZ_g A_g
+ *   + dZ_u A_u.
  * Inputs are those of the forward calls; save must hold what moe_expert_fwd
  * wrote for the same inputs.
  *   dy   act [T][d];  dx act [T][d] (out)
- *   dA_gate, dA_up f32 [E][d][r]; dB_gate, dB_up f32 [E][r][f];
- *   dA_down f32 [E][f][r]; dB_down f32 [E][r][d]  (out) */
+ *   dA_gate, dA_up f32 [E][r][d]; dB_gate, dB_up f32 [E][f][r];
+ *   dA_down f32 [E][r][f]; dB_down f32 [E][d][r]  (out, layouts of A and B) */
 moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
                            const int32_t *topk_idx, const float *gates,
                            const int32_t *offsets, const int32_t *perm_src,
@@ -184,6 +184,28 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
                            float *dA_gate, float *dB_gate, float *dA_up, float *dB_up,
                            float *dA_down, float *dB_down, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* Instrumentation, not part of the method: time every launch of one internal
+ * kernel with a pair of HIP events recorded on the launch stream around it.
+ * moe_timer_start arms the calling thread for `tag` (one of moe_kernel_tag;
+ * at most 4096 launches are recorded); moe_timer_stop waits for the recorded
+ * events, returns the summed milliseconds and the number of launches, and
+ * disarms.  Events are created on the first use and reused; the state is
+ * thread-local. */
+typedef enum {
+  MOE_KT_ROUTER_LOGITS = 0, /* router GEMM (vector ALU)                    */
+  MOE_KT_ROUTER_TOPK = 1,   /* partial sum, top-k, softmax                  */
+  MOE_KT_PERMUTE = 2,       /* scatter of the permutation                   */
+  MOE_KT_GATEUP = 3,        /* gate/up expert GEMM with SwiGLU epilogue     */
+  MOE_KT_DOWN = 4,          /* down expert GEMM                             */
+  MOE_KT_COMBINE = 5,       /* gate-weighted combine                        */
+  MOE_KT_GATE_GRAD = 6,     /* gate / router-input gradient, dO             */
+  MOE_KT_BWD_DOWN = 7,      /* dH = dO W_d + dZ_d A_d^T (and SwiGLU bwd)    */
+  MOE_KT_BWD_GATEUP = 8,    /* dX_perm = dG W_g + dU W_u + ...              */
+  MOE_KT_COUNT = 9
+} moe_kernel_tag;
+moe_status moe_timer_start(int32_t tag);
+moe_status moe_timer_stop(float *total_ms, int32_t *launches);
 
 /* Host-only queries; they validate dims like the calls do. */
 moe_status moe_workspace_size(const moe_dims *dims, int32_t call, size_t *bytes);

@@ -11,7 +11,7 @@ What is computed (cited by page title and section):
     Optimizer Strategy" and Implementation Considerations "TQP Quantization":
     expert base weights are quantized and fixed, low-rank adapters are full
     precision and trained, the router is full precision.  So every expert
-    matrix is W_eff = dequant(q, s) + lam * A @ B, the base receives no
+    matrix is W_eff = dequant(q, s) + lam * B @ A, the base receives no
     gradient and the adapters do.
   * Same card, Architecture Details, and the abstract of "Reversible
     Foundations: Training a 120B Sparse MoE through State-Preserving Scaling":
@@ -19,7 +19,8 @@ What is computed (cited by page title and section):
     stage).
   * Same card, Implementation Considerations "Reversibility": routing is a
     stateless function of the layer input.
-  * Same card, Related Methods: LoRA, i.e. the adapter product x @ A @ B.
+  * Same card, Related Methods: LoRA, i.e. the adapter product of a row with
+    two low-rank factors; stored out x in here (A [r, K], B [N, r]).
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository): symmetric int4 with bf16 group scales; top-k
 over the logits with ties to the lower expert index; gates = softmax over the
@@ -177,16 +178,19 @@ class Expert:
 
 
 def expert_forward(ex: Expert, X: np.ndarray, lam: float) -> dict:
-    """SwiGLU expert with adapters on every matrix, rows X [M, d]:
-    G = X W_g^T + lam (X A_g) B_g, U likewise, H = silu(G) * U,
-    O = H W_d^T + lam (H A_d) B_d."""
-    Zg = X @ ex.A["gate"]
-    Zu = X @ ex.A["up"]
-    G = X @ ex.W["gate"].T + lam * (Zg @ ex.B["gate"])
-    U = X @ ex.W["up"].T + lam * (Zu @ ex.B["up"])
+    """SwiGLU expert with adapters on every matrix, rows X [M, d].  Adapters
+    are stored out x in like the base (A [r, K], B [N, r]), so the adapted
+    matrix is W_hat + lam * B A and its product with a row is
+    x W_hat^T + lam (x A^T) B^T:
+    G = X W_g^T + lam (X A_g^T) B_g^T, U likewise, H = silu(G) * U,
+    O = H W_d^T + lam (H A_d^T) B_d^T."""
+    Zg = X @ ex.A["gate"].T
+    Zu = X @ ex.A["up"].T
+    G = X @ ex.W["gate"].T + lam * (Zg @ ex.B["gate"].T)
+    U = X @ ex.W["up"].T + lam * (Zu @ ex.B["up"].T)
     H = silu(G) * U
-    Zd = H @ ex.A["down"]
-    O = H @ ex.W["down"].T + lam * (Zd @ ex.B["down"])
+    Zd = H @ ex.A["down"].T
+    O = H @ ex.W["down"].T + lam * (Zd @ ex.B["down"].T)
     return {"G": G, "U": U, "H": H, "O": O, "Zg": Zg, "Zu": Zu, "Zd": Zd}
 
 
@@ -195,21 +199,21 @@ def expert_backward(ex: Expert, X: np.ndarray, fw: dict, dO: np.ndarray, lam: fl
     gradients of A and B of each matrix, and dX [M, d].  The base is frozen,
     so no gradient of W is formed."""
     G, U, H = fw["G"], fw["U"], fw["H"]
-    dB_down = lam * fw["Zd"].T @ dO
-    dZd = lam * dO @ ex.B["down"].T
-    dA_down = H.T @ dZd
-    dH = dO @ ex.W["down"] + dZd @ ex.A["down"].T
+    dB_down = lam * dO.T @ fw["Zd"]
+    dZd = lam * dO @ ex.B["down"]
+    dA_down = dZd.T @ H
+    dH = dO @ ex.W["down"] + dZd @ ex.A["down"]
     sg = sigmoid(G)
     dG = dH * U * sg * (1.0 + G * (1.0 - sg))
     dU = dH * G * sg
-    dB_gate = lam * fw["Zg"].T @ dG
-    dB_up = lam * fw["Zu"].T @ dU
-    dZg = lam * dG @ ex.B["gate"].T
-    dZu = lam * dU @ ex.B["up"].T
-    dA_gate = X.T @ dZg
-    dA_up = X.T @ dZu
+    dB_gate = lam * dG.T @ fw["Zg"]
+    dB_up = lam * dU.T @ fw["Zu"]
+    dZg = lam * dG @ ex.B["gate"]
+    dZu = lam * dU @ ex.B["up"]
+    dA_gate = dZg.T @ X
+    dA_up = dZu.T @ X
     dX = (dG @ ex.W["gate"] + dU @ ex.W["up"]
-          + dZg @ ex.A["gate"].T + dZu @ ex.A["up"].T)
+          + dZg @ ex.A["gate"] + dZu @ ex.A["up"])
     return {"dA_gate": dA_gate, "dB_gate": dB_gate, "dA_up": dA_up, "dB_up": dB_up,
             "dA_down": dA_down, "dB_down": dB_down, "dX": dX}
 
@@ -279,10 +283,10 @@ def backward(inputs: dict, fwd: dict, k: int, group: int, lam: float = 1.0) -> d
         dx += dl[:, j:j + 1] * wr[:, idx[:, j]].T
     # expert path
     f = inputs["q_gate"].shape[1]
-    r = inputs["A_gate"].shape[2]
-    grads = {"dA_gate": np.zeros((E, d, r)), "dB_gate": np.zeros((E, r, f)),
-             "dA_up": np.zeros((E, d, r)), "dB_up": np.zeros((E, r, f)),
-             "dA_down": np.zeros((E, f, r)), "dB_down": np.zeros((E, r, d))}
+    r = inputs["A_gate"].shape[1]
+    grads = {"dA_gate": np.zeros((E, r, d)), "dB_gate": np.zeros((E, f, r)),
+             "dA_up": np.zeros((E, r, d)), "dB_up": np.zeros((E, f, r)),
+             "dA_down": np.zeros((E, r, f)), "dB_down": np.zeros((E, d, r))}
     dXp = np.zeros((T * k, d))
     for e in range(E):
         lo, hi = fwd["offsets"][e], fwd["offsets"][e + 1]

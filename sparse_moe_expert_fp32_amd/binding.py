@@ -53,6 +53,8 @@ def _load():
         "moe_status_string": [I32],
         "moe_last_error": [],
         "moe_abi_version": [],
+        "moe_timer_start": [I32],
+        "moe_timer_stop": [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -66,7 +68,11 @@ def _load():
 LIB = _load()
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
-           "moe_abi_version")
+           "moe_abi_version", "moe_timer_start", "moe_timer_stop")
+
+# kernel tags of moe_timer_start (moe_kernel_tag)
+KT = {"router_logits": 0, "router_topk": 1, "permute": 2, "gateup": 3, "down": 4, "combine": 5,
+      "gate_grad": 6, "bwd_down": 7, "bwd_gateup": 8}
 
 
 def _check(status: int, name: str):
@@ -119,6 +125,16 @@ def moe_save_size(dm: Dims) -> int:
 
 def moe_abi_version() -> int:
     return LIB.moe_abi_version()
+
+
+def moe_timer_start(tag) -> None:
+    _check(LIB.moe_timer_start(KT.get(tag, tag)), "moe_timer_start")
+
+
+def moe_timer_stop():
+    ms, n = ctypes.c_float(0), ctypes.c_int32(0)
+    _check(LIB.moe_timer_stop(ctypes.byref(ms), ctypes.byref(n)), "moe_timer_stop")
+    return ms.value, n.value
 
 
 def moe_route(dm, x, w_router, b_router, topk_idx, gates, logits, ws, stream=None):

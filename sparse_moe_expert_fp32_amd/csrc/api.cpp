@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 
@@ -145,7 +146,47 @@ moe_status check_ws(const moe_dims *d, int call, const void *ws, size_t ws_bytes
 
 template <typename T> T *at(void *base, size_t off) { return (T *)((char *)base + off); }
 
+// ---- kernel timer (instrumentation)
+struct KernelTimer {
+  int tag = -1;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // pairs: start, stop
+  ~KernelTimer() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+thread_local KernelTimer g_timer;
+constexpr int kTimerCap = 4096;
+
+void timer_mark(int tag, hipStream_t st, int which) {
+  KernelTimer &T = g_timer;
+  if (T.tag != tag) return;
+  if (which == 0 && T.used >= kTimerCap) return;
+  int slot = which == 0 ? T.used : T.used - 1;
+  if (which == 0) {
+    if ((int)T.ev.size() < 2 * (slot + 1)) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      T.ev.push_back(a);
+      T.ev.push_back(b);
+    }
+    (void)hipEventRecord(T.ev[2 * slot], st);
+    T.used++;
+  } else if (slot >= 0) {
+    (void)hipEventRecord(T.ev[2 * slot + 1], st);
+  }
+}
+
 }  // namespace
+
+// Bracket one kernel launch with the armed timer's events.
+#define TIMED(tag, st, ...)      \
+  do {                           \
+    timer_mark(tag, st, 0);      \
+    __VA_ARGS__;                 \
+    timer_mark(tag, st, 1);      \
+  } while (0)
 
 #define TRY(expr)                  \
   do {                             \
@@ -170,6 +211,32 @@ const char *moe_status_string(int32_t s) {
 
 const char *moe_last_error(void) { return g_last_error.c_str(); }
 
+moe_status moe_timer_start(int32_t tag) {
+  if (tag < 0 || tag >= MOE_KT_COUNT) return fail(MOE_ERR_INVALID, "unknown kernel tag");
+  g_timer.tag = tag;
+  g_timer.used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_timer_stop(float *total_ms, int32_t *launches) {
+  if (!total_ms || !launches) return fail(MOE_ERR_INVALID, "total_ms and launches are required");
+  KernelTimer &T = g_timer;
+  double sum = 0.0;
+  for (int i = 0; i < T.used; ++i) {
+    if (hipEventSynchronize(T.ev[2 * i + 1]) != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, T.ev[2 * i], T.ev[2 * i + 1]) != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipEventElapsedTime failed");
+    sum += ms;
+  }
+  *total_ms = (float)sum;
+  *launches = T.used;
+  T.tag = -1;
+  T.used = 0;
+  return MOE_OK;
+}
+
 moe_status moe_workspace_size(const moe_dims *dims, int32_t call, size_t *bytes) {
   TRY(check_dims(dims));
   if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
@@ -192,9 +259,14 @@ moe_status moe_route(const moe_dims *dims, const void *x, const float *w_router,
   TRY(check_dims(dims));
   REQUIRE(x && w_router && topk_idx && gates, "moe_route: x, w_router, topk_idx, gates required");
   TRY(check_ws(dims, MOE_CALL_ROUTE, ws, ws_bytes));
-  moe::launch_route(dims->act == MOE_BF16, x, w_router, b_router, dims->T, dims->d_model,
-                    dims->n_experts, dims->top_k, topk_idx, gates, logits, ws,
-                    (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  int splits = 1;
+  TIMED(MOE_KT_ROUTER_LOGITS, st,
+        moe::launch_router_logits(dims->act == MOE_BF16, x, w_router, dims->T, dims->d_model,
+                                  dims->n_experts, ws, &splits, st));
+  TIMED(MOE_KT_ROUTER_TOPK, st,
+        moe::launch_router_topk(ws, splits, b_router, dims->T, dims->n_experts, dims->top_k,
+                                topk_idx, gates, logits, st));
   return hip_status("moe_route");
 }
 
@@ -218,8 +290,9 @@ moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *s
   (void)ws_bytes;
   TRY(check_dims(dims));
   REQUIRE(e_out && slot_pos && gates && y, "moe_combine: e_out, slot_pos, gates, y required");
-  moe::launch_combine(dims->act == MOE_BF16, e_out, slot_pos, gates, dims->T, dims->d_model,
-                      dims->top_k, y, (hipStream_t)stream);
+  TIMED(MOE_KT_COMBINE, (hipStream_t)stream,
+        moe::launch_combine(dims->act == MOE_BF16, e_out, slot_pos, gates, dims->T,
+                            dims->d_model, dims->top_k, y, (hipStream_t)stream));
   return hip_status("moe_combine");
 }
 
@@ -253,7 +326,7 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   moe::ProjArgs P{};
   P.a = x; P.lda = d; P.gather = true; P.perm_src = perm_src; P.kk = k;
   P.tiles = tiles; P.ntiles = ntiles; P.max_tiles = mt; P.offsets = offsets;
-  P.m_es = (size_t)d * r; P.m_cs = r; P.m_js = 1; P.K = d; P.r = r; P.s = 1.f; P.ldz = 3 * r;
+  P.m_es = (size_t)r * d; P.m_cs = 1; P.m_js = d; P.K = d; P.r = r; P.s = 1.f; P.ldz = 3 * r;
   P.m = gate.A; P.Z = Z;
   moe::launch_proj_simple(bf, P, st);
   P.m = up.A; P.Z = Z + r;
@@ -265,21 +338,22 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   A.a = x; A.lda = d; A.gather = true; A.perm_src = perm_src; A.kk = k;
   A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
   A.N = f; A.K = d; A.g = g; A.trans = false; A.ldz = 3 * r;
-  A.l_es = (size_t)r * f; A.l_js = f; A.l_ns = 1; A.r = r; A.lam = lam; A.ldo = f;
+  A.l_es = (size_t)f * r; A.l_js = 1; A.l_ns = r; A.r = r; A.lam = lam; A.ldo = f;
   A.acc_out = false;
   A.q = gate.q; A.scale = gate.scale; A.Z = Z; A.lmat = gate.B; A.out = G32;
-  moe::launch_lin_simple(bf, true, A, st);
+  TIMED(MOE_KT_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
   A.q = up.q; A.scale = up.scale; A.Z = Z + r; A.lmat = up.B; A.out = U32;
-  moe::launch_lin_simple(bf, true, A, st);
+  TIMED(MOE_KT_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
   moe::launch_swiglu_fwd(bf, G32, U32, S * f, H, Gs, Us, st);
 
   // Z_d = H A_d, then O = H W_d^T + lam Z_d B_d
-  P.a = H; P.lda = f; P.gather = false; P.m = down.A; P.m_es = (size_t)f * r; P.m_cs = r;
-  P.K = f; P.Z = Z + 2 * r;
+  P.a = H; P.lda = f; P.gather = false; P.m = down.A; P.m_es = (size_t)r * f; P.m_cs = 1;
+  P.m_js = f; P.K = f; P.Z = Z + 2 * r;
   moe::launch_proj_simple(bf, P, st);
   A.a = H; A.lda = f; A.gather = false; A.N = d; A.K = f; A.q = down.q; A.scale = down.scale;
-  A.Z = Z + 2 * r; A.lmat = down.B; A.l_es = (size_t)r * d; A.l_js = d; A.out = e_out; A.ldo = d;
-  moe::launch_lin_simple(bf, false, A, st);
+  A.Z = Z + 2 * r; A.lmat = down.B; A.l_es = (size_t)d * r; A.l_js = 1; A.l_ns = r;
+  A.out = e_out; A.ldo = d;
+  TIMED(MOE_KT_DOWN, st, moe::launch_lin_simple(bf, false, A, st));
   return hip_status("moe_expert_fwd");
 }
 
@@ -323,57 +397,63 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
 
   // gate path and dO = gamma * dy in permuted order
   moe::launch_transpose_f32(w_router, d, E, wr_t, st);
-  moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r, dO, st);
+  TIMED(MOE_KT_GATE_GRAD, st,
+        moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r, dO,
+                              st));
 
   // down: dZ_d = lam dO B_d^T; dB_d = lam Z_d^T dO; dH = dO W_d + dZ_d A_d^T
   moe::ProjArgs P{};
   P.a = dO; P.lda = d; P.gather = false; P.perm_src = perm_src; P.kk = k;
   P.tiles = tiles; P.ntiles = ntiles; P.max_tiles = mt; P.offsets = offsets;
-  P.m = down.B; P.m_es = (size_t)r * d; P.m_cs = 1; P.m_js = d; P.K = d; P.r = r; P.s = lam;
+  P.m = down.B; P.m_es = (size_t)d * r; P.m_cs = r; P.m_js = 1; P.K = d; P.r = r; P.s = lam;
   P.Z = dZ + 2 * r; P.ldz = 3 * r;
   moe::launch_proj_simple(bf, P, st);
   moe::WgradArgs W{};
   W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E;
-  W.l = Z + 2 * r; W.ldl = 3 * r; W.l_f32 = true; W.gather = false;
-  W.r = dO; W.ldr = d; W.Aw = r; W.Bw = d; W.s = lam; W.out = dB_down;
+  // dB_d [d][r] = lam * sum_p dO[p][n] Z_d[p][j]
+  W.l = dO; W.ldl = d; W.l_f32 = false; W.gather = false;
+  W.r = Z + 2 * r; W.ldr = 3 * r; W.Aw = d; W.Bw = r; W.s = lam; W.out = dB_down;
   moe::launch_wgrad_simple(bf, W, st);
   moe::LinArgs A{};
   A.a = dO; A.lda = d; A.gather = false; A.perm_src = perm_src; A.kk = k;
   A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
   A.q = down.q; A.scale = down.scale; A.N = f; A.K = d; A.g = g; A.trans = true;
-  A.Z = dZ + 2 * r; A.ldz = 3 * r; A.lmat = down.A; A.l_es = (size_t)f * r; A.l_js = 1;
-  A.l_ns = r; A.r = r; A.lam = 1.f; A.out = dH32; A.ldo = f; A.acc_out = false;
-  moe::launch_lin_simple(bf, true, A, st);
+  A.Z = dZ + 2 * r; A.ldz = 3 * r; A.lmat = down.A; A.l_es = (size_t)r * f; A.l_js = f;
+  A.l_ns = 1; A.r = r; A.lam = 1.f; A.out = dH32; A.ldo = f; A.acc_out = false;
+  TIMED(MOE_KT_BWD_DOWN, st, moe::launch_lin_simple(bf, true, A, st));
   // SwiGLU backward; dA_d = H^T dZ_d
   moe::launch_swiglu_bwd(bf, dH32, Gs, Us, S * f, dG, dU, st);
-  W.l = H; W.ldl = f; W.l_f32 = false; W.r = dZ + 2 * r; W.ldr = 3 * r; W.Aw = f; W.Bw = r;
+  // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
+  W.l = dZ + 2 * r; W.ldl = 3 * r; W.l_f32 = true; W.r = H; W.ldr = f; W.Aw = r; W.Bw = f;
   W.s = 1.f; W.out = dA_down;
   moe::launch_wgrad_simple(bf, W, st);
 
   // gate / up: dZ = lam dG B^T; dB = lam Z^T dG; dA = X^T dZ
-  P.m_es = (size_t)r * f; P.m_cs = 1; P.m_js = f; P.K = f; P.lda = f;
+  P.m_es = (size_t)f * r; P.m_cs = r; P.m_js = 1; P.K = f; P.lda = f;
   P.a = dG; P.m = gate.B; P.Z = dZ;
   moe::launch_proj_simple(bf, P, st);
   P.a = dU; P.m = up.B; P.Z = dZ + r;
   moe::launch_proj_simple(bf, P, st);
-  W.l = Z; W.ldl = 3 * r; W.l_f32 = true; W.r = dG; W.ldr = f; W.Aw = r; W.Bw = f; W.s = lam;
+  // dB [f][r] = lam * sum_p dG[p][n] Z[p][j]
+  W.l = dG; W.ldl = f; W.l_f32 = false; W.r = Z; W.ldr = 3 * r; W.Aw = f; W.Bw = r; W.s = lam;
   W.out = dB_gate;
   moe::launch_wgrad_simple(bf, W, st);
-  W.l = Z + r; W.r = dU; W.out = dB_up;
+  W.l = dU; W.r = Z + r; W.out = dB_up;
   moe::launch_wgrad_simple(bf, W, st);
-  W.l = x; W.ldl = d; W.l_f32 = false; W.gather = true; W.r = dZ; W.ldr = 3 * r; W.Aw = d;
-  W.Bw = r; W.s = 1.f; W.out = dA_gate;
+  // dA [r][d] = sum_p dZ[p][j] X[token(p)][c]
+  W.l = dZ; W.ldl = 3 * r; W.l_f32 = true; W.gather = true; W.r = x; W.ldr = d; W.Aw = r;
+  W.Bw = d; W.s = 1.f; W.out = dA_gate;
   moe::launch_wgrad_simple(bf, W, st);
-  W.r = dZ + r; W.out = dA_up;
+  W.l = dZ + r; W.out = dA_up;
   moe::launch_wgrad_simple(bf, W, st);
 
   // dX_perm = dG W_g + dZ_g A_g^T + dU W_u + dZ_u A_u^T   (float32)
   A.a = dG; A.lda = f; A.q = gate.q; A.scale = gate.scale; A.N = d; A.K = f;
-  A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)d * r; A.l_js = 1; A.l_ns = r;
+  A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)r * d; A.l_js = d; A.l_ns = 1;
   A.out = dXp; A.ldo = d; A.acc_out = false;
-  moe::launch_lin_simple(bf, true, A, st);
+  TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
   A.a = dU; A.q = up.q; A.scale = up.scale; A.Z = dZ + r; A.lmat = up.A; A.acc_out = true;
-  moe::launch_lin_simple(bf, true, A, st);
+  TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
 
   moe::launch_unpermute_sum(bf, true, dx_r, dXp, slot_pos, T, d, k, dx, st);
   return hip_status("moe_adapter_bwd");

@@ -6,7 +6,7 @@
 // The computation is TQP's expert under "Reversible Sparse MoE Single Node"
 // (skill card), Principle 3 and Implementation Considerations "TQP
 // Quantization": a frozen quantized base plus a trained low-rank adapter on
-// every matrix (LoRA, Related Methods), so W_eff = W_hat + lam * (A B)^T, the
+// every matrix (LoRA, Related Methods), so W_eff = W_hat + lam * B A, the
 // base gets no gradient.  The SwiGLU form of the expert is this library's
 // reading; the pages do not name the FFN.
 #include "common.h"
@@ -170,8 +170,9 @@ __global__ __launch_bounds__(256) void proj_simple_kernel(
 
 // ----------------------------------------------------- adapter gradients --
 // out[e][a][b] = s * sum_{p in expert e} L(p, a) R(p, b), rows in ascending p.
-// L(p, a) = l[(GATHER ? perm_src[p]/kk : p) * ldl + a];  R(p, b) = rr[p * ldr + b].
-template <typename TL, typename TR, bool GATHER>
+// L(p, a) = l[row_L(p) * ldl + a],  R(p, b) = rr[row_R(p) * ldr + b], where a
+// side marked "gather" reads row perm_src[p] / kk (a token row) instead of p.
+template <typename TL, typename TR, bool GL, bool GR>
 __global__ __launch_bounds__(256) void wgrad_simple_kernel(
     const TL *__restrict__ l, int ldl, const int32_t *__restrict__ perm_src, int kk,
     const TR *__restrict__ rr, int ldr, const int32_t *__restrict__ offsets, int Aw, int Bw,
@@ -185,9 +186,11 @@ __global__ __launch_bounds__(256) void wgrad_simple_kernel(
   for (int p0 = lo; p0 < hi; p0 += 16) {
     {
       int i = tid >> 4, j = tid & 15, p = p0 + i;
-      int row = p < hi ? (GATHER ? perm_src[p] / kk : p) : -1;
-      Ls[i][j] = (row >= 0 && a0 + j < Aw) ? Elem<TL>::ld(l, (size_t)row * ldl + a0 + j) : 0.f;
-      Rs[i][j] = (p < hi && b0 + j < Bw) ? Elem<TR>::ld(rr, (size_t)p * ldr + b0 + j) : 0.f;
+      int src = p < hi ? perm_src[p] / kk : -1;
+      int rowl = p < hi ? (GL ? src : p) : -1;
+      int rowr = p < hi ? (GR ? src : p) : -1;
+      Ls[i][j] = (rowl >= 0 && a0 + j < Aw) ? Elem<TL>::ld(l, (size_t)rowl * ldl + a0 + j) : 0.f;
+      Rs[i][j] = (rowr >= 0 && b0 + j < Bw) ? Elem<TR>::ld(rr, (size_t)rowr * ldr + b0 + j) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -273,16 +276,19 @@ void launch_proj_simple(bool act_bf16, const ProjArgs &P, hipStream_t st) {
 
 void launch_wgrad_simple(bool act_bf16, const WgradArgs &W, hipStream_t st) {
   dim3 grid((W.Bw + 15) / 16, (W.Aw + 15) / 16, W.E);
-#define WG_CALL(TL, TR, G)                                                                     \
-  wgrad_simple_kernel<TL, TR, G><<<grid, 256, 0, st>>>((const TL *)W.l, W.ldl, W.perm_src,    \
-                                                       W.kk, (const TR *)W.r, W.ldr,           \
-                                                       W.offsets, W.Aw, W.Bw, W.s, W.out)
+#define WG_CALL(TL, TR, GL, GR)                                                                \
+  wgrad_simple_kernel<TL, TR, GL, GR><<<grid, 256, 0, st>>>(                                   \
+      (const TL *)W.l, W.ldl, W.perm_src, W.kk, (const TR *)W.r, W.ldr, W.offsets, W.Aw, W.Bw, \
+      W.s, W.out)
+  // one side is float32 (a low-rank projection), the other the act dtype
   if (act_bf16) {
-    if (W.l_f32) WG_CALL(float, bf16_t, false);
-    else if (W.gather) WG_CALL(bf16_t, float, true);
-    else WG_CALL(bf16_t, float, false);
+    if (W.l_f32) {
+      if (W.gather) WG_CALL(float, bf16_t, false, true); else WG_CALL(float, bf16_t, false, false);
+    } else {
+      WG_CALL(bf16_t, float, false, false);
+    }
   } else {
-    if (W.gather) WG_CALL(float, float, true); else WG_CALL(float, float, false);
+    if (W.gather) WG_CALL(float, float, false, true); else WG_CALL(float, float, false, false);
   }
 #undef WG_CALL
 }

@@ -8,9 +8,10 @@ namespace moe {
 
 // ---- router (route.hip)
 size_t route_ws_bytes(int T, int d, int E);
-void launch_route(bool bf16, const void *x, const float *wr, const float *bias, int T, int d,
-                  int E, int k, int32_t *topk_idx, float *gates, float *logits, void *ws,
-                  hipStream_t st);
+void launch_router_logits(bool bf16, const void *x, const float *wr, int T, int d, int E,
+                          void *ws, int *splits_out, hipStream_t st);
+void launch_router_topk(const void *ws, int splits, const float *bias, int T, int E, int k,
+                        int32_t *topk_idx, float *gates, float *logits, hipStream_t st);
 
 // ---- permutation (permute.hip)
 size_t permute_ws_bytes(int T, int E, int k);
@@ -50,6 +51,8 @@ struct ProjArgs {
 };
 void launch_proj_simple(bool act_bf16, const ProjArgs &P, hipStream_t st);
 
+// out[e][a][b] = s * sum_p L(p,a) R(p,b); exactly one of L, R is float32 (l_f32
+// says which); `gather` makes the act-dtype side R read token rows of x.
 struct WgradArgs {
   const void *l; int ldl; bool l_f32; bool gather; const int32_t *perm_src; int kk;
   const void *r; int ldr; const int32_t *offsets; int E, Aw, Bw; float s; float *out;

@@ -171,9 +171,8 @@ static void launch_logits_ne(int NE, const void *x, const float *wr, int Tn, int
   else launch_logits<T, 16>(x, wr, Tn, d, E, splits, split_len, partial, st);
 }
 
-void launch_route(bool bf16, const void *x, const float *wr, const float *bias, int Tn, int d,
-                  int E, int k, int32_t *topk_idx, float *gates, float *logits, void *ws,
-                  hipStream_t st) {
+void launch_router_logits(bool bf16, const void *x, const float *wr, int Tn, int d, int E,
+                          void *ws, int *splits_out, hipStream_t st) {
   int splits = route_splits(Tn, d);
   int chunks = (d + RT_KC - 1) / RT_KC;
   int split_len = ((chunks + splits - 1) / splits) * RT_KC;
@@ -182,8 +181,13 @@ void launch_route(bool bf16, const void *x, const float *wr, const float *bias, 
   int NE = (E + 63) / 64;
   if (bf16) launch_logits_ne<bf16_t>(NE, x, wr, Tn, d, E, splits, split_len, partial, st);
   else launch_logits_ne<float>(NE, x, wr, Tn, d, E, splits, split_len, partial, st);
-  router_topk_kernel<<<(Tn + 3) / 4, 256, 0, st>>>(partial, splits, bias, Tn, E, k, topk_idx,
-                                                   gates, logits);
+  *splits_out = splits;
+}
+
+void launch_router_topk(const void *ws, int splits, const float *bias, int Tn, int E, int k,
+                        int32_t *topk_idx, float *gates, float *logits, hipStream_t st) {
+  router_topk_kernel<<<(Tn + 3) / 4, 256, 0, st>>>((const float *)ws, splits, bias, Tn, E, k,
+                                                   topk_idx, gates, logits);
 }
 
 }  // namespace moe

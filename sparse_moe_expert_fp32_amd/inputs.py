@@ -18,6 +18,8 @@ the order W_gate, W_up, W_down, A_gate, B_gate, A_up, B_up, A_down, B_down.
 Draws are PCG64 float32 standard normals scaled by the standard deviation.
 
 Storage formats (these are the library's input formats):
+  * adapters are stored out x in like the base: A [r][K], B [N][r], so the
+    adapter term of a row x is (x A^T) B^T.
   * bf16 tensors are carried as uint16 bit patterns, rounded to nearest even.
   * int4 base matrix W[N, K] (out x in) -> q: uint8 [N, K/2] and
     scale: bf16 [N, K/group].  Symmetric per-group quantisation along K:
@@ -120,12 +122,12 @@ def _expert(cfg: LayerConfig, ss: np.random.SeedSequence):
     out = {}
     for name, w in (("gate", wg), ("up", wu), ("down", wd)):
         out[name] = quantize_int4(w, g)
-    out["A_gate"] = to_storage(_normal(s[3], (d, r), 1.0 / d), cfg.act)
-    out["B_gate"] = to_storage(_normal(s[4], (r, f), 0.02), cfg.act)
-    out["A_up"] = to_storage(_normal(s[5], (d, r), 1.0 / d), cfg.act)
-    out["B_up"] = to_storage(_normal(s[6], (r, f), 0.02), cfg.act)
-    out["A_down"] = to_storage(_normal(s[7], (f, r), 1.0 / f), cfg.act)
-    out["B_down"] = to_storage(_normal(s[8], (r, d), 0.02), cfg.act)
+    out["A_gate"] = to_storage(_normal(s[3], (r, d), 1.0 / d), cfg.act)
+    out["B_gate"] = to_storage(_normal(s[4], (f, r), 0.02), cfg.act)
+    out["A_up"] = to_storage(_normal(s[5], (r, d), 1.0 / d), cfg.act)
+    out["B_up"] = to_storage(_normal(s[6], (f, r), 0.02), cfg.act)
+    out["A_down"] = to_storage(_normal(s[7], (r, f), 1.0 / f), cfg.act)
+    out["B_down"] = to_storage(_normal(s[8], (d, r), 0.02), cfg.act)
     return out
 
 
@@ -142,8 +144,8 @@ def generate(cfg: LayerConfig, seed: int = 0, threads: int | None = None) -> dic
 
     Keys: x [T,d], dy [T,d] (act storage); w_router [d,E] f32; b_router [E]
     f32 or None; for m in gate/up/down: q_m [E,N,K/2] u8, s_m [E,N,K/g] u16,
-    A_m [E,K,r], B_m [E,r,N] (act storage).  N,K = (f,d) for gate/up and
-    (d,f) for down.
+    A_m [E,r,K], B_m [E,N,r] (act storage; out x in like the base).
+    N,K = (f,d) for gate/up and (d,f) for down.
     """
     root = np.random.SeedSequence([seed, cfg.cfg_id])
     s_x, s_wr, s_b, s_dy, *s_exp = root.spawn(4 + cfg.E)
@@ -160,8 +162,8 @@ def generate(cfg: LayerConfig, seed: int = 0, threads: int | None = None) -> dic
     for m, (N, K) in shapes.items():
         out[f"q_{m}"] = np.empty((E, N, K // 2), np.uint8)
         out[f"s_{m}"] = np.empty((E, N, K // g), np.uint16)
-        out[f"A_{m}"] = np.empty((E, K, r), adt)
-        out[f"B_{m}"] = np.empty((E, r, N), adt)
+        out[f"A_{m}"] = np.empty((E, r, K), adt)
+        out[f"B_{m}"] = np.empty((E, N, r), adt)
 
     def fill(e):
         ex = _expert(cfg, s_exp[e])

@@ -61,9 +61,9 @@ class DeviceLayer:
                                   device=self.dev) for c in calls}
         if bwd:
             self.dx = z(T, d)
-            self.grads = {"dA_gate": z(E, d, r, dtype=f32), "dB_gate": z(E, r, f, dtype=f32),
-                          "dA_up": z(E, d, r, dtype=f32), "dB_up": z(E, r, f, dtype=f32),
-                          "dA_down": z(E, f, r, dtype=f32), "dB_down": z(E, r, d, dtype=f32)}
+            self.grads = {"dA_gate": z(E, r, d, dtype=f32), "dB_gate": z(E, f, r, dtype=f32),
+                          "dA_up": z(E, r, d, dtype=f32), "dB_up": z(E, f, r, dtype=f32),
+                          "dA_down": z(E, r, f, dtype=f32), "dB_down": z(E, d, r, dtype=f32)}
 
     # ---- the five calls
     def route(self, stream=None):

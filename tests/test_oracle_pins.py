@@ -258,7 +258,7 @@ def test_zero_base_isolates_low_rank_path():
     inp = _layer(cfg, mutate=zero_q)
     lam = 0.5
     out = oracle.forward(inp, 1, cfg.group, lam)
-    M = {m: lam * torch.from_numpy(oracle.to_f64(inp[f"A_{m}"][0]) @ oracle.to_f64(inp[f"B_{m}"][0])).T
+    M = {m: lam * torch.from_numpy(oracle.to_f64(inp[f"B_{m}"][0]) @ oracle.to_f64(inp[f"A_{m}"][0]))
          for m in ("gate", "up", "down")}
     x = torch.from_numpy(oracle.to_f64(inp["x"]))
     y = F.linear(F.silu(F.linear(x, M["gate"])) * F.linear(x, M["up"]), M["down"])
@@ -364,7 +364,8 @@ def test_backward_matches_torch_autograd_dense():
         for t in range(cfg.T):
             for j in range(cfg.k):
                 e = int(idx[t, j])
-                lin = lambda v, m: F.linear(v, W[m][e]) + lam * (v @ P[f"A_{m}"][e]) @ P[f"B_{m}"][e]
+                lin = lambda v, m: (F.linear(v, W[m][e])
+                                    + lam * F.linear(F.linear(v, P[f"A_{m}"][e]), P[f"B_{m}"][e]))
                 h = F.silu(lin(x[t], "gate")) * lin(x[t], "up")
                 y[t] = y[t] + gam[t, j] * lin(h, "down")
         (y * torch.from_numpy(oracle.to_f64(inp["dy"]))).sum().backward()
