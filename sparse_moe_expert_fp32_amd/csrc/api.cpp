@@ -89,20 +89,44 @@ size_t max_tiles(const moe_dims *d, int BM) {
   return ((size_t)d->T * d->top_k + BM - 1) / BM + d->n_experts;
 }
 
+// The matrix-core path: bf16 activations, quantization group 128, d and f
+// multiples of 128.  Everything else runs the float32 kernels.
+bool use_mfma(const moe_dims *d) {
+  return d->act == MOE_BF16 && d->group == 128 && d->d_model % 128 == 0 && d->d_ff % 128 == 0;
+}
+
 // ---- expert forward workspace
 struct FwdLayout {
-  size_t tiles, ntiles, save, G32, U32, total;
+  size_t tiles, ntiles, save, G32, U32, tiles_m, ntiles_m, rs_x, rs_h, total;
   explicit FwdLayout(const moe_dims *d) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff;
     Carve c;
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
     save = c.take(SaveLayout(d).total);  // used when the caller passes no save buffer
-    G32 = c.take(S * f * 4);
-    U32 = c.take(S * f * 4);
+    if (use_mfma(d)) {
+      G32 = U32 = 0;
+      tiles_m = c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2));
+      ntiles_m = c.take(sizeof(int));
+      rs_x = c.take((size_t)d->T * (d->d_model / 128) * 4);
+      rs_h = c.take(S * (f / 128) * 4);
+    } else {
+      G32 = c.take(S * f * 4);
+      U32 = c.take(S * f * 4);
+      tiles_m = ntiles_m = rs_x = rs_h = 0;
+    }
     total = c.off;
   }
 };
+
+int persistent_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    cus = 256;
+  return cus & ~7;
+}
 
 // ---- adapter backward workspace
 struct BwdLayout {
@@ -331,6 +355,40 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   moe::launch_proj_simple(bf, P, st);
   P.m = up.A; P.Z = Z + r;
   moe::launch_proj_simple(bf, P, st);
+
+  if (use_mfma(dims)) {
+    int2 *tiles_m = at<int2>(ws, L.tiles_m);
+    int *ntiles_m = at<int>(ws, L.ntiles_m);
+    float *rs_x = at<float>(ws, L.rs_x), *rs_h = at<float>(ws, L.rs_h);
+    moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st);
+    moe::launch_group_rowsum(x, T, d, 128, rs_x, st);
+    const int grid = persistent_grid();
+    moe::MfmaGemmArgs M{};
+    M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
+    M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
+    M.K = d; M.N = f; M.NT = (f + 127) / 128;
+    M.q0 = gate.q; M.s0 = gate.scale; M.B0 = (const uint16_t *)gate.B;
+    M.q1 = up.q; M.s1 = up.scale; M.B1 = (const uint16_t *)up.B;
+    M.Z0 = Z; M.Z1 = Z + r; M.ldz = 3 * r; M.r = r; M.lam = lam;
+    M.out = (uint16_t *)H; M.ldo = f;
+    M.saveG = save ? (uint16_t *)Gs : nullptr;
+    M.saveU = save ? (uint16_t *)Us : nullptr;
+    M.rsum_out = rs_h; M.ld_rsum_out = f / 128;
+    TIMED(MOE_KT_GATEUP, st, moe::launch_grouped_gemm(0, M, grid, st));
+    // Z_d = H A_d^T
+    P.a = H; P.lda = f; P.gather = false; P.m = down.A; P.m_es = (size_t)r * f; P.m_cs = 1;
+    P.m_js = f; P.K = f; P.Z = Z + 2 * r;
+    moe::launch_proj_simple(bf, P, st);
+    moe::MfmaGemmArgs D{};
+    D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128;
+    D.tiles = tiles_m; D.ntiles = ntiles_m; D.offsets = offsets;
+    D.K = f; D.N = d; D.NT = (d + 255) / 256;
+    D.q0 = down.q; D.s0 = down.scale; D.B0 = (const uint16_t *)down.B;
+    D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
+    D.out = (uint16_t *)e_out; D.ldo = d;
+    TIMED(MOE_KT_DOWN, st, moe::launch_grouped_gemm(1, D, grid, st));
+    return hip_status("moe_expert_fwd");
+  }
 
   // G, U in float32, then SwiGLU
   float *G32 = at<float>(ws, L.G32), *U32 = at<float>(ws, L.U32);

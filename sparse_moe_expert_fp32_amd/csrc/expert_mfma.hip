@@ -1,0 +1,324 @@
+// Grouped int4 x bf16 expert GEMMs on the CDNA4 matrix cores (gfx950).
+//
+// TQP keeps each expert's base matrix quantized and frozen and adds a trained
+// low-rank adapter ("Reversible Sparse MoE Single Node" skill card,
+// Principle 3 and Implementation Considerations "TQP Quantization"; LoRA under
+// Related Methods).  Per expert segment of the expert-contiguous rows:
+//   gate/up:  G = X W_g^T + lam (X A_g^T) B_g^T, U likewise, H = silu(G) * U
+//   down:     O = H W_d^T + lam (H A_d^T) B_d^T
+// The SwiGLU form is this library's reading; the pages do not name the FFN.
+//
+// Design (one 256-thread block = 4 waves, 128 rows x N-tile per work item):
+//  * Work items (M-tile, N-tile) are processed by a persistent grid.  Each of
+//    the 8 XCDs takes a contiguous eighth of the item list, so the rows and
+//    weights of neighbouring tiles stay in that XCD's L2.
+//  * The A rows (x gathered by token, or H) stream through LDS one
+//    quantization group (128 of K) at a time, double buffered, loaded with
+//    global_load_lds_dwordx4 straight into LDS in an XOR-swizzled layout
+//    (16-byte chunk c of row r lives at chunk c ^ (r & 15)) so the MFMA
+//    operand reads are bank-conflict free.
+//  * Each wave owns 64 output columns for all 128 rows.  Its int4 weights are
+//    read straight from global memory (16 bytes per lane per group and 16
+//    columns) and unpacked in registers: a nibble u (offset by 8) becomes the
+//    bf16 bit pattern 0x4300 | u, i.e. the exact value 136 + q.  The offset is
+//    removed exactly by starting every group's accumulation at
+//    -136 * (sum of that group's A row), a per-row value precomputed in
+//    float32; then the group's partial product is scaled by the bf16 group
+//    scale into the float32 accumulator.  The weights therefore enter the
+//    matrix cores exactly (no rounding of s*q).
+//  * MFMA v_mfma_f32_16x16x32_bf16: within a group, lane group lg = lane/16
+//    covers K offsets [32 lg, 32 lg + 32), k-step s the 8 values 32 lg + 8 s.
+//    A and B use the same mapping, so the products pair up correctly.
+//  * Epilogue: the adapter term (lam Z) B^T is one more MFMA (K = rank) into
+//    the same accumulator; gate/up applies SwiGLU in registers (a lane holds
+//    the matching gate and up columns), writes H (bf16) and, for the down
+//    product's offset correction, the row sums of H per group.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int GM_BM = 128;   // rows per tile
+constexpr int GM_KG = 128;   // K per staged chunk = quantization group
+
+// 8 int4 values (one word of the storage layout) -> bf16 (136 + q), in k order.
+DEV uint4 unpack_offset8(uint32_t w) {
+  const uint32_t t = w ^ 0x88888888u;
+  uint4 r;
+  r.x = (t & 0x000F000Fu) | 0x43004300u;
+  r.y = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((t >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((t >> 12) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+DEV f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+DEV f32x4_t mfma16(short4_t a, short4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------- row sums --
+// out[row][g] = sum of a[row][g*G .. g*G+G) (bf16 values, float32 sum in k order)
+__global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int K, int G,
+                                    float *__restrict__ out) {
+  const int ng = K / G;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * ng) return;
+  size_t row = i / ng;
+  int g = (int)(i % ng);
+  const uint4 *p = reinterpret_cast<const uint4 *>(a + row * K + (size_t)g * G);
+  float s = 0.f;
+  for (int v = 0; v < G / 8; ++v) {
+    uint4 u = p[v];
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s += __uint_as_float(w[j] << 16);
+      s += __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  out[i] = s;
+}
+
+// ------------------------------------------------------------ grouped GEMM --
+// MODE 0: gate/up with SwiGLU epilogue (A = x rows gathered by token)
+// MODE 1: down (A = H rows in permuted order)
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const MfmaGemmArgs A) {
+  __shared__ __attribute__((aligned(16))) bf16_t a_lds[2][GM_BM * GM_KG];
+  __shared__ __attribute__((aligned(16))) float corr_lds[2][GM_BM];
+  __shared__ int tok_lds[GM_BM];
+  __shared__ float red_lds[4][GM_BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = A.K, N = A.N, NG = K / GM_KG;
+  const int total = A.ntiles[0] * A.NT;
+  const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int wbeg = (int)(((long long)total * xcd) >> 3);
+  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
+
+  for (int wi = wbeg + bi; wi < wend; wi += nper) {
+    const int ti = wi / A.NT, nt = wi - ti * A.NT;
+    const int2 tile = A.tiles[ti];
+    const int e = tile.x, p0 = tile.y;
+    const int rows = min(GM_BM, A.offsets[e + 1] - p0);
+    __syncthreads();  // LDS of the previous item is free
+    if (tid < GM_BM) {
+      const int p = p0 + min(tid, rows - 1);
+      tok_lds[tid] = MODE == 0 ? A.perm_src[p] / A.kk : p;
+    }
+    __syncthreads();
+
+    // ---- staging addresses: 8 x 16-byte chunks per thread per group
+    const char *src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * (w * 8 + j) + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      src[j] = reinterpret_cast<const char *>(A.a) + (size_t)tok_lds[r] * A.lda * 2 + c * 16;
+    }
+    // group sums of this thread's A row (threads < 128), one group ahead
+    const float *rs_row = A.rsum + (size_t)tok_lds[tid & (GM_BM - 1)] * A.ld_rsum;
+    float rs_pref = tid < GM_BM ? rs_row[0] : 0.f;
+
+    // ---- this wave's columns: 4 fragments of 16
+    int col[4];
+    const uint8_t *qp[4];
+    const uint16_t *sp[4];
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      const int c = MODE == 0 ? nt * 128 + w * 32 + (nf & 1) * 16 + lr
+                              : nt * 256 + w * 64 + nf * 16 + lr;
+      col[nf] = c;
+      const int cc = min(c, N - 1);
+      const uint8_t *q = MODE == 0 && nf >= 2 ? A.q1 : A.q0;
+      const uint16_t *s = MODE == 0 && nf >= 2 ? A.s1 : A.s0;
+      qp[nf] = q + ((size_t)e * N + cc) * (K / 2) + lg * 16;
+      sp[nf] = s + ((size_t)e * N + cc) * NG;
+    }
+
+    auto stage = [&](int g, int buf) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds(src[j] + (size_t)g * GM_KG * 2,
+                                         (lds_void *)&a_lds[buf][(w * 8 + j) * 512], 16, 0, 0);
+      if (tid < GM_BM) {
+        corr_lds[buf][tid] = -136.f * rs_pref;
+        if (g + 1 < NG) rs_pref = rs_row[g + 1];
+      }
+    };
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 bq[4];
+    float sc[4];
+    stage(0, 0);
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      bq[nf] = *reinterpret_cast<const uint4 *>(qp[nf]);
+      sc[nf] = bf2f(sp[nf][0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int g = 0; g < NG; ++g) {
+      const int cur = g & 1;
+      uint4 bq_n[4];
+      float sc_n[4];
+      if (g + 1 < NG) {
+        stage(g + 1, cur ^ 1);
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          bq_n[nf] = *reinterpret_cast<const uint4 *>(qp[nf] + (size_t)(g + 1) * (GM_KG / 2));
+          sc_n[nf] = bf2f(sp[nf][g + 1]);
+        }
+      }
+      uint4 bu[4][4];
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        bu[0][nf] = unpack_offset8(bq[nf].x);
+        bu[1][nf] = unpack_offset8(bq[nf].y);
+        bu[2][nf] = unpack_offset8(bq[nf].z);
+        bu[3][nf] = unpack_offset8(bq[nf].w);
+      }
+      const bf16_t *al = a_lds[cur];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const f32x4_t ci = *reinterpret_cast<const f32x4_t *>(&corr_lds[cur][16 * m + 4 * lg]);
+        f32x4_t P[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint4 av = *reinterpret_cast<const uint4 *>(
+              al + (16 * m + lr) * GM_KG + (((lg * 4 + s) ^ lr) << 3));
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf) P[nf] = mfma32(av, bu[s][nf], s == 0 ? ci : P[nf]);
+        }
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) acc[m][nf] += sc[nf] * P[nf];
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (g + 1 < NG) {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) { bq[nf] = bq_n[nf]; sc[nf] = sc_n[nf]; }
+      }
+    }
+
+    // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16
+    for (int j0 = 0; j0 < A.r; j0 += 16) {
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const bf16_t *Bm = MODE == 0 && nf >= 2 ? A.B1 : A.B0;
+        const int cc = min(col[nf], N - 1);
+        short4_t bv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * lg + i;
+          bv[i] = j < A.r ? (short)Bm[((size_t)e * N + cc) * A.r + j] : (short)0;
+        }
+        const float *Zp = MODE == 0 && nf >= 2 ? A.Z1 : A.Z0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int p = p0 + min(16 * m + lr, rows - 1);
+          short4_t av;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = j0 + 4 * lg + i;
+            av[i] = j < A.r ? (short)f2bf(A.lam * Zp[(size_t)p * A.ldz + j]) : (short)0;
+          }
+          acc[m][nf] = mfma16(av, bv, acc[m][nf]);
+        }
+      }
+    }
+
+    // ---- epilogue
+    if (MODE == 0) {
+      float rsum_part[8][4];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rsum_part[m][i] = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 16 * m + 4 * lg + i;
+          const bool rv = rr < rows;
+          const size_t p = (size_t)(p0 + rr);
+#pragma unroll
+          for (int nf = 0; nf < 2; ++nf) {
+            const float gv = acc[m][nf][i], uv = acc[m][nf + 2][i];
+            const uint16_t hb = f2bf(silu_f(gv) * uv);
+            const int c = col[nf];
+            if (rv && c < N) {
+              A.out[p * A.ldo + c] = hb;
+              if (A.saveG) {
+                A.saveG[p * A.ldo + c] = f2bf(gv);
+                A.saveU[p * A.ldo + c] = f2bf(uv);
+              }
+              rsum_part[m][i] += bf2f(hb);
+            }
+          }
+        }
+      }
+      // row sums of H over this block's 128 columns (= one quantization group)
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = rsum_part[m][i];
+          v += __shfl_xor(v, 1);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 8);
+          if (lr == 0) red_lds[w][16 * m + 4 * lg + i] = v;
+        }
+      __syncthreads();
+      if (tid < rows && A.rsum_out)
+        A.rsum_out[(size_t)(p0 + tid) * A.ld_rsum_out + nt] =
+            (red_lds[0][tid] + red_lds[1][tid]) + (red_lds[2][tid] + red_lds[3][tid]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 16 * m + 4 * lg + i;
+          if (rr >= rows) continue;
+          const size_t p = (size_t)(p0 + rr);
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf)
+            if (col[nf] < N) A.out[p * A.ldo + col[nf]] = f2bf(acc[m][nf][i]);
+        }
+    }
+  }
+}
+
+int mfma_tile_rows() { return GM_BM; }
+
+void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st) {
+  size_t n = (size_t)rows * (K / G);
+  group_rowsum_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((const bf16_t *)a, rows, K, G,
+                                                                   out);
+}
+
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t st) {
+  if (mode == 0) grouped_gemm_kernel<0><<<grid, 256, 0, st>>>(A);
+  else grouped_gemm_kernel<1><<<grid, 256, 0, st>>>(A);
+}
+
+}  // namespace moe

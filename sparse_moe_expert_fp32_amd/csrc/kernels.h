@@ -64,4 +64,22 @@ void launch_swiglu_fwd(bool act_bf16, const float *G, const float *U, size_t n, 
 void launch_swiglu_bwd(bool act_bf16, const float *dH, const void *Gs, const void *Us, size_t n,
                        void *dG, void *dU, hipStream_t st);
 
+// ---- matrix-core grouped GEMMs (expert_mfma.hip), bf16 activations, group 128
+struct MfmaGemmArgs {
+  const void *a; int lda;                 // A rows: x [T][d] (mode 0) or H [S][f] (mode 1)
+  const int32_t *perm_src; int kk;        // mode 0: token of a permuted row
+  const float *rsum; int ld_rsum;         // per A row, per group of 128: sum of the row
+  const int2 *tiles; const int *ntiles; const int32_t *offsets;
+  int K, N, NT;                           // reduction, columns per matrix, N-tiles per M-tile
+  const uint8_t *q0; const uint16_t *s0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
+  const uint8_t *q1; const uint16_t *s1; const uint16_t *B1;   // up (mode 0)
+  const float *Z0, *Z1; int ldz; int r; float lam;             // X A^T projections (float32)
+  uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
+  uint16_t *saveG, *saveU;                // mode 0, optional
+  float *rsum_out; int ld_rsum_out;       // mode 0: group sums of H rows
+};
+int mfma_tile_rows();
+void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st);
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t st);
+
 }  // namespace moe
