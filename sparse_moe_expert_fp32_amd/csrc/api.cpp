@@ -130,20 +130,23 @@ int persistent_grid() {
 
 // ---- adapter backward workspace
 struct BwdLayout {
-  size_t tiles, ntiles, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
+  size_t tiles, ntiles, tiles_m, ntiles_m, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
   explicit BwdLayout(const moe_dims *d) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
+    const bool mf = use_mfma(d);
     Carve c;
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
+    tiles_m = mf ? c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2)) : 0;
+    ntiles_m = mf ? c.take(sizeof(int)) : 0;
     wr_t = c.take((size_t)d->n_experts * dm * 4);
     dx_r = c.take((size_t)d->T * dm * 4);
     dO = c.take(S * dm * ab);
     dZ = c.take(S * 3 * d->rank * 4);
-    dH32 = c.take(S * f * 4);
+    dH32 = mf ? 0 : c.take(S * f * 4);
     dG = c.take(S * f * ab);
     dU = c.take(S * f * ab);
-    dXp = c.take(S * dm * 4);
+    dXp = c.take(S * dm * (mf ? ab : 4));   // bf16 on the matrix-core path
     total = c.off;
   }
 };
@@ -447,7 +450,8 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   int *ntiles = at<int>(ws, L.ntiles);
   float *wr_t = at<float>(ws, L.wr_t), *dx_r = at<float>(ws, L.dx_r);
   void *dO = at<char>(ws, L.dO);
-  float *dZ = at<float>(ws, L.dZ), *dH32 = at<float>(ws, L.dH32), *dXp = at<float>(ws, L.dXp);
+  float *dZ = at<float>(ws, L.dZ), *dH32 = at<float>(ws, L.dH32);
+  void *dXp = at<char>(ws, L.dXp);
   void *dG = at<char>(ws, L.dG), *dU = at<char>(ws, L.dU);
   const int BM = moe::simple_tile_rows();
   const int mt = (int)max_tiles(dims, BM);
@@ -472,15 +476,30 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   W.l = dO; W.ldl = d; W.l_f32 = false; W.gather = false;
   W.r = Z + 2 * r; W.ldr = 3 * r; W.Aw = d; W.Bw = r; W.s = lam; W.out = dB_down;
   moe::launch_wgrad_simple(bf, W, st);
+  const bool mf = use_mfma(dims);
+  int2 *tiles_m = mf ? at<int2>(ws, L.tiles_m) : nullptr;
+  int *ntiles_m = mf ? at<int>(ws, L.ntiles_m) : nullptr;
+  const int grid = mf ? persistent_grid() : 0;
+  if (mf) moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st);
   moe::LinArgs A{};
   A.a = dO; A.lda = d; A.gather = false; A.perm_src = perm_src; A.kk = k;
   A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
   A.q = down.q; A.scale = down.scale; A.N = f; A.K = d; A.g = g; A.trans = true;
   A.Z = dZ + 2 * r; A.ldz = 3 * r; A.lmat = down.A; A.l_es = (size_t)r * f; A.l_js = f;
   A.l_ns = 1; A.r = r; A.lam = 1.f; A.out = dH32; A.ldo = f; A.acc_out = false;
-  TIMED(MOE_KT_BWD_DOWN, st, moe::launch_lin_simple(bf, true, A, st));
-  // SwiGLU backward; dA_d = H^T dZ_d
-  moe::launch_swiglu_bwd(bf, dH32, Gs, Us, S * f, dG, dU, st);
+  if (mf) {
+    // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
+    moe::MfmaGemmTArgs M{};
+    M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
+    M.K = d; M.N = f; M.NT = f / 128; M.q0 = down.q; M.s0 = down.scale;
+    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
+    M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
+    M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
+    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, grid, st));
+  } else {
+    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_lin_simple(bf, true, A, st));
+    moe::launch_swiglu_bwd(bf, dH32, Gs, Us, S * f, dG, dU, st);
+  }
   // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
   W.l = dZ + 2 * r; W.ldl = 3 * r; W.l_f32 = true; W.r = H; W.ldr = f; W.Aw = r; W.Bw = f;
   W.s = 1.f; W.out = dA_down;
@@ -505,15 +524,26 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   W.l = dZ + r; W.out = dA_up;
   moe::launch_wgrad_simple(bf, W, st);
 
-  // dX_perm = dG W_g + dZ_g A_g^T + dU W_u + dZ_u A_u^T   (float32)
-  A.a = dG; A.lda = f; A.q = gate.q; A.scale = gate.scale; A.N = d; A.K = f;
-  A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)r * d; A.l_js = d; A.l_ns = 1;
-  A.out = dXp; A.ldo = d; A.acc_out = false;
-  TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
-  A.a = dU; A.q = up.q; A.scale = up.scale; A.Z = dZ + r; A.lmat = up.A; A.acc_out = true;
-  TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
-
-  moe::launch_unpermute_sum(bf, true, dx_r, dXp, slot_pos, T, d, k, dx, st);
+  // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
+  if (mf) {
+    moe::MfmaGemmTArgs M{};
+    M.a0 = dG; M.a1 = dU; M.lda = f; M.tiles = tiles_m; M.ntiles = ntiles_m;
+    M.offsets = offsets; M.K = f; M.N = d; M.NT = d / 128;
+    M.q0 = gate.q; M.s0 = gate.scale; M.q1 = up.q; M.s1 = up.scale;
+    M.Z0 = dZ; M.Z1 = dZ + r; M.ldz = 3 * r; M.r = r;
+    M.L0 = (const uint16_t *)gate.A; M.L1 = (const uint16_t *)up.A;
+    M.out = (uint16_t *)dXp; M.ldo = d;
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, M, grid, st));
+    moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
+  } else {
+    A.a = dG; A.lda = f; A.q = gate.q; A.scale = gate.scale; A.N = d; A.K = f;
+    A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)r * d; A.l_js = d; A.l_ns = 1;
+    A.out = dXp; A.ldo = d; A.acc_out = false;
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
+    A.a = dU; A.q = up.q; A.scale = up.scale; A.Z = dZ + r; A.lmat = up.A; A.acc_out = true;
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
+    moe::launch_unpermute_sum(bf, true, dx_r, dXp, slot_pos, T, d, k, dx, st);
+  }
   return hip_status("moe_adapter_bwd");
 }
 

@@ -35,37 +35,12 @@
 //    product's offset correction, the row sums of H per group.
 #include "common.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int GM_BM = 128;   // rows per tile
 constexpr int GM_KG = 128;   // K per staged chunk = quantization group
-
-// 8 int4 values (one word of the storage layout) -> bf16 (136 + q), in k order.
-DEV uint4 unpack_offset8(uint32_t w) {
-  const uint32_t t = w ^ 0x88888888u;
-  uint4 r;
-  r.x = (t & 0x000F000Fu) | 0x43004300u;
-  r.y = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((t >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((t >> 12) & 0x000F000Fu) | 0x43004300u;
-  return r;
-}
-
-DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-DEV f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
-DEV f32x4_t mfma16(short4_t a, short4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // ---------------------------------------------------------------- row sums --
 // out[row][g] = sum of a[row][g*G .. g*G+G) (bf16 values, float32 sum in k order)
@@ -151,8 +126,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(const MfmaGemmArgs
     auto stage = [&](int g, int buf) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds(src[j] + (size_t)g * GM_KG * 2,
-                                         (lds_void *)&a_lds[buf][(w * 8 + j) * 512], 16, 0, 0);
+        load_lds16(src[j] + (size_t)g * GM_KG * 2, &a_lds[buf][(w * 8 + j) * 512]);
       if (tid < GM_BM) {
         corr_lds[buf][tid] = -136.f * rs_pref;
         if (g + 1 < NG) rs_pref = rs_row[g + 1];

@@ -82,4 +82,18 @@ int mfma_tile_rows();
 void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st);
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t st);
 
+// transposed-base products of the backward (expert_mfma_bwd.hip)
+struct MfmaGemmTArgs {
+  const void *a0, *a1; int lda;           // A rows: dO (mode 0) or dG, dU (mode 1), [S][lda]
+  const int2 *tiles; const int *ntiles; const int32_t *offsets;
+  int K, N, NT;                           // reduction per source, output columns, N / 128
+  const uint8_t *q0; const uint16_t *s0;  // stored [E][K][N/2], scales [E][K][N/128]
+  const uint8_t *q1; const uint16_t *s1;  // mode 1: second source (up)
+  const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
+  const uint16_t *L0, *L1;                // adapter A of the matrix, [E][r][N]
+  const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: SwiGLU backward, [S][N]
+  uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
+};
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st);
+
 }  // namespace moe

@@ -1,0 +1,59 @@
+// Matrix-core helpers for gfx950 (CDNA4): operand types, MFMA wrappers,
+// int4 unpacking and direct global->LDS loads.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 8 int4 values (one word of the storage layout) -> bf16 (136 + q), in k order:
+// nibble u ^ 8 (= q + 8) placed in the mantissa of 128.0 (0x4300) is exactly
+// 136 + q.
+DEV uint4 unpack_offset8(uint32_t w) {
+  const uint32_t t = w ^ 0x88888888u;
+  uint4 r;
+  r.x = (t & 0x000F000Fu) | 0x43004300u;
+  r.y = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((t >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((t >> 12) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+// Signed int4 of element j (0..7) of a storage word.
+DEV int int4_of_word(uint32_t w, int j) {
+  const int slot = (j >> 1) + ((j & 1) << 2);
+  return __builtin_amdgcn_sbfe(w, 4 * slot, 4);
+}
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+DEV uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// D = A(16x32) B(32x16) + C.  Lane l holds A row l%16 / B column l%16 with 8
+// consecutive K values of lane group l/16; D lane l holds column l%16, rows
+// 4*(l/16) .. 4*(l/16)+3.
+DEV f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// Same with K = 16 (4 values per lane).
+DEV f32x4_t mfma16(short4_t a, short4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds_wave_base + 16 i.
+DEV void load_lds16(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+}  // namespace moe
