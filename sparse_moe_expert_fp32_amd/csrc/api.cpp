@@ -130,15 +130,20 @@ int persistent_grid() {
 
 // ---- adapter backward workspace
 struct BwdLayout {
-  size_t tiles, ntiles, tiles_m, ntiles_m, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
+  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, bt, wr_t, dx_r, dO, dZ, dH32, dG,
+      dU, dXp, total;
   explicit BwdLayout(const moe_dims *d) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
     const bool mf = use_mfma(d);
     Carve c;
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
-    tiles_m = mf ? c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2)) : 0;
+    tiles_m = mf ? c.take(max_tiles(d, moe::mfma_t_tile_rows()) * sizeof(int2)) : 0;
     ntiles_m = mf ? c.take(sizeof(int)) : 0;
+    tiles_p = mf ? c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2)) : 0;
+    ntiles_p = mf ? c.take(sizeof(int)) : 0;
+    // B of down, gate, up transposed to [E][r][N] (bf16)
+    bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
     wr_t = c.take((size_t)d->n_experts * dm * 4);
     dx_r = c.take((size_t)d->T * dm * 4);
     dO = c.take(S * dm * ab);
@@ -349,22 +354,25 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   const int mt = (int)max_tiles(dims, BM);
   moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
 
-  // Z_g = X A_g, Z_u = X A_u (rows gathered from x)
   moe::ProjArgs P{};
   P.a = x; P.lda = d; P.gather = true; P.perm_src = perm_src; P.kk = k;
   P.tiles = tiles; P.ntiles = ntiles; P.max_tiles = mt; P.offsets = offsets;
   P.m_es = (size_t)r * d; P.m_cs = 1; P.m_js = d; P.K = d; P.r = r; P.s = 1.f; P.ldz = 3 * r;
-  P.m = gate.A; P.Z = Z;
-  moe::launch_proj_simple(bf, P, st);
-  P.m = up.A; P.Z = Z + r;
-  moe::launch_proj_simple(bf, P, st);
 
   if (use_mfma(dims)) {
     int2 *tiles_m = at<int2>(ws, L.tiles_m);
+    const int mtl = (int)max_tiles(dims, moe::mfma_tile_rows());
     int *ntiles_m = at<int>(ws, L.ntiles_m);
     float *rs_x = at<float>(ws, L.rs_x), *rs_h = at<float>(ws, L.rs_h);
     moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st);
     moe::launch_group_rowsum(x, T, d, 128, rs_x, st);
+    // Z_g = X A_g^T, Z_u = X A_u^T (rows gathered from x)
+    moe::ProjMArgs Q{};
+    Q.a = (const uint16_t *)x; Q.lda = d; Q.perm_src = perm_src; Q.kk = k;
+    Q.tiles = tiles_m; Q.ntiles = ntiles_m; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 2;
+    Q.m0 = (const uint16_t *)gate.A; Q.m1 = (const uint16_t *)up.A; Q.scale = 1.f;
+    Q.Z0 = Z; Q.Z1 = Z + r; Q.ldz = 3 * r;
+    moe::launch_proj_mfma(Q, mtl, true, st);
     const int grid = persistent_grid();
     moe::MfmaGemmArgs M{};
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
@@ -379,9 +387,9 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128;
     TIMED(MOE_KT_GATEUP, st, moe::launch_grouped_gemm(0, M, grid, st));
     // Z_d = H A_d^T
-    P.a = H; P.lda = f; P.gather = false; P.m = down.A; P.m_es = (size_t)r * f; P.m_cs = 1;
-    P.m_js = f; P.K = f; P.Z = Z + 2 * r;
-    moe::launch_proj_simple(bf, P, st);
+    Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
+    Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
+    moe::launch_proj_mfma(Q, mtl, false, st);
     moe::MfmaGemmArgs D{};
     D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128;
     D.tiles = tiles_m; D.ntiles = ntiles_m; D.offsets = offsets;
@@ -392,6 +400,12 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     TIMED(MOE_KT_DOWN, st, moe::launch_grouped_gemm(1, D, grid, st));
     return hip_status("moe_expert_fwd");
   }
+
+  // Z_g = X A_g^T, Z_u = X A_u^T (rows gathered from x)
+  P.m = gate.A; P.Z = Z;
+  moe::launch_proj_simple(bf, P, st);
+  P.m = up.A; P.Z = Z + r;
+  moe::launch_proj_simple(bf, P, st);
 
   // G, U in float32, then SwiGLU
   float *G32 = at<float>(ws, L.G32), *U32 = at<float>(ws, L.U32);
@@ -450,12 +464,9 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   int *ntiles = at<int>(ws, L.ntiles);
   float *wr_t = at<float>(ws, L.wr_t), *dx_r = at<float>(ws, L.dx_r);
   void *dO = at<char>(ws, L.dO);
-  float *dZ = at<float>(ws, L.dZ), *dH32 = at<float>(ws, L.dH32);
+  float *dZ = at<float>(ws, L.dZ);
   void *dXp = at<char>(ws, L.dXp);
   void *dG = at<char>(ws, L.dG), *dU = at<char>(ws, L.dU);
-  const int BM = moe::simple_tile_rows();
-  const int mt = (int)max_tiles(dims, BM);
-  moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
 
   // gate path and dO = gamma * dy in permuted order
   moe::launch_transpose_f32(w_router, d, E, wr_t, st);
@@ -463,7 +474,80 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
         moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r, dO,
                               st));
 
-  // down: dZ_d = lam dO B_d^T; dB_d = lam Z_d^T dO; dH = dO W_d + dZ_d A_d^T
+  if (use_mfma(dims)) {
+    int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
+    int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
+    const int grid = persistent_grid();
+    const int mtp = (int)max_tiles(dims, moe::mfma_tile_rows());
+    moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st);
+    moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_p, ntiles_p, st);
+    uint16_t *bt_d = at<uint16_t>(ws, L.bt);
+    uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
+    moe::launch_transpose_nr(down.B, E, d, r, bt_d, st);
+    moe::launch_transpose_nr(gate.B, E, f, r, bt_g, st);
+    moe::launch_transpose_nr(up.B, E, f, r, bt_u, st);
+    const uint16_t *H16 = (const uint16_t *)H;
+
+    // dZ_d = lam dO B_d
+    moe::ProjMArgs Q{};
+    Q.a = (const uint16_t *)dO; Q.lda = d; Q.perm_src = perm_src; Q.kk = k;
+    Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 1;
+    Q.m0 = bt_d; Q.scale = lam; Q.Z0 = dZ + 2 * r; Q.ldz = 3 * r;
+    moe::launch_proj_mfma(Q, mtp, false, st);
+    // dB_d [d][r] = lam sum_p dO[p][n] Z_d[p][j]
+    moe::WgradMArgs W{};
+    W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r;
+    W.w = (const uint16_t *)dO; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
+    W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
+    moe::launch_wgrad_mfma(W, false, st);
+    // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
+    moe::MfmaGemmTArgs M{};
+    M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
+    M.K = d; M.N = f; M.NT = f / 128; M.q0 = down.q; M.s0 = down.scale;
+    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
+    M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
+    M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
+    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, grid, st));
+    // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
+    W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
+    W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
+    moe::launch_wgrad_mfma(W, false, st);
+    // dZ_g = lam dG B_g, dZ_u = lam dU B_u
+    Q.a = (const uint16_t *)dG; Q.lda = f; Q.K = f; Q.m0 = bt_g; Q.Z0 = dZ;
+    moe::launch_proj_mfma(Q, mtp, false, st);
+    Q.a = (const uint16_t *)dU; Q.m0 = bt_u; Q.Z0 = dZ + r;
+    moe::launch_proj_mfma(Q, mtp, false, st);
+    // dB [f][r] = lam sum_p dG[p][n] Z[p][j]
+    W.w = (const uint16_t *)dG; W.ldw = f; W.rr = Z; W.wide = f; W.scale = lam; W.out = dB_gate;
+    W.oe = (size_t)f * r; W.oa = r; W.ob = 1;
+    moe::launch_wgrad_mfma(W, false, st);
+    W.w = (const uint16_t *)dU; W.rr = Z + r; W.out = dB_up;
+    moe::launch_wgrad_mfma(W, false, st);
+    // dA [r][d] = sum_p dZ[p][j] X[token(p)][c]
+    W.w = (const uint16_t *)x; W.ldw = d; W.rr = dZ; W.wide = d; W.scale = 1.f; W.out = dA_gate;
+    W.oe = (size_t)r * d; W.oa = 1; W.ob = d;
+    moe::launch_wgrad_mfma(W, true, st);
+    W.rr = dZ + r; W.out = dA_up;
+    moe::launch_wgrad_mfma(W, true, st);
+    // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
+    moe::MfmaGemmTArgs X{};
+    X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m; X.ntiles = ntiles_m;
+    X.offsets = offsets; X.K = f; X.N = d; X.NT = d / 128;
+    X.q0 = gate.q; X.s0 = gate.scale; X.q1 = up.q; X.s1 = up.scale;
+    X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
+    X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A;
+    X.out = (uint16_t *)dXp; X.ldo = d;
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, grid, st));
+    moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
+    return hip_status("moe_adapter_bwd");
+  }
+
+  // ---- float32 kernels
+  float *dH32 = at<float>(ws, L.dH32);
+  const int BM = moe::simple_tile_rows();
+  const int mt = (int)max_tiles(dims, BM);
+  moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
+  // down: dZ_d = lam dO B_d; dB_d = lam dO^T Z_d; dH = dO W_d + dZ_d A_d
   moe::ProjArgs P{};
   P.a = dO; P.lda = d; P.gather = false; P.perm_src = perm_src; P.kk = k;
   P.tiles = tiles; P.ntiles = ntiles; P.max_tiles = mt; P.offsets = offsets;
@@ -476,36 +560,19 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   W.l = dO; W.ldl = d; W.l_f32 = false; W.gather = false;
   W.r = Z + 2 * r; W.ldr = 3 * r; W.Aw = d; W.Bw = r; W.s = lam; W.out = dB_down;
   moe::launch_wgrad_simple(bf, W, st);
-  const bool mf = use_mfma(dims);
-  int2 *tiles_m = mf ? at<int2>(ws, L.tiles_m) : nullptr;
-  int *ntiles_m = mf ? at<int>(ws, L.ntiles_m) : nullptr;
-  const int grid = mf ? persistent_grid() : 0;
-  if (mf) moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st);
   moe::LinArgs A{};
   A.a = dO; A.lda = d; A.gather = false; A.perm_src = perm_src; A.kk = k;
   A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
   A.q = down.q; A.scale = down.scale; A.N = f; A.K = d; A.g = g; A.trans = true;
   A.Z = dZ + 2 * r; A.ldz = 3 * r; A.lmat = down.A; A.l_es = (size_t)r * f; A.l_js = f;
   A.l_ns = 1; A.r = r; A.lam = 1.f; A.out = dH32; A.ldo = f; A.acc_out = false;
-  if (mf) {
-    // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
-    moe::MfmaGemmTArgs M{};
-    M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
-    M.K = d; M.N = f; M.NT = f / 128; M.q0 = down.q; M.s0 = down.scale;
-    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
-    M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
-    M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
-    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, grid, st));
-  } else {
-    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_lin_simple(bf, true, A, st));
-    moe::launch_swiglu_bwd(bf, dH32, Gs, Us, S * f, dG, dU, st);
-  }
+  TIMED(MOE_KT_BWD_DOWN, st, moe::launch_lin_simple(bf, true, A, st));
+  moe::launch_swiglu_bwd(bf, dH32, Gs, Us, S * f, dG, dU, st);
   // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
   W.l = dZ + 2 * r; W.ldl = 3 * r; W.l_f32 = true; W.r = H; W.ldr = f; W.Aw = r; W.Bw = f;
   W.s = 1.f; W.out = dA_down;
   moe::launch_wgrad_simple(bf, W, st);
-
-  // gate / up: dZ = lam dG B^T; dB = lam Z^T dG; dA = X^T dZ
+  // gate / up: dZ = lam dG B; dB = lam dG^T Z; dA = dZ^T X
   P.m_es = (size_t)f * r; P.m_cs = r; P.m_js = 1; P.K = f; P.lda = f;
   P.a = dG; P.m = gate.B; P.Z = dZ;
   moe::launch_proj_simple(bf, P, st);
@@ -523,27 +590,14 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   moe::launch_wgrad_simple(bf, W, st);
   W.l = dZ + r; W.out = dA_up;
   moe::launch_wgrad_simple(bf, W, st);
-
-  // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
-  if (mf) {
-    moe::MfmaGemmTArgs M{};
-    M.a0 = dG; M.a1 = dU; M.lda = f; M.tiles = tiles_m; M.ntiles = ntiles_m;
-    M.offsets = offsets; M.K = f; M.N = d; M.NT = d / 128;
-    M.q0 = gate.q; M.s0 = gate.scale; M.q1 = up.q; M.s1 = up.scale;
-    M.Z0 = dZ; M.Z1 = dZ + r; M.ldz = 3 * r; M.r = r;
-    M.L0 = (const uint16_t *)gate.A; M.L1 = (const uint16_t *)up.A;
-    M.out = (uint16_t *)dXp; M.ldo = d;
-    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, M, grid, st));
-    moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
-  } else {
-    A.a = dG; A.lda = f; A.q = gate.q; A.scale = gate.scale; A.N = d; A.K = f;
-    A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)r * d; A.l_js = d; A.l_ns = 1;
-    A.out = dXp; A.ldo = d; A.acc_out = false;
-    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
-    A.a = dU; A.q = up.q; A.scale = up.scale; A.Z = dZ + r; A.lmat = up.A; A.acc_out = true;
-    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
-    moe::launch_unpermute_sum(bf, true, dx_r, dXp, slot_pos, T, d, k, dx, st);
-  }
+  // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u   (float32)
+  A.a = dG; A.lda = f; A.q = gate.q; A.scale = gate.scale; A.N = d; A.K = f;
+  A.Z = dZ; A.lmat = gate.A; A.l_es = (size_t)r * d; A.l_js = d; A.l_ns = 1;
+  A.out = dXp; A.ldo = d; A.acc_out = false;
+  TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
+  A.a = dU; A.q = up.q; A.scale = up.scale; A.Z = dZ + r; A.lmat = up.A; A.acc_out = true;
+  TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_lin_simple(bf, true, A, st));
+  moe::launch_unpermute_sum(bf, true, dx_r, dXp, slot_pos, T, d, k, dx, st);
   return hip_status("moe_adapter_bwd");
 }
 

@@ -195,6 +195,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
   }
 }
 
+int mfma_t_tile_rows() { return GT_BM; }
+
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st) {
   if (mode == 0) grouped_gemm_t_kernel<0><<<grid, 256, 0, st>>>(A);
   else grouped_gemm_t_kernel<1><<<grid, 256, 0, st>>>(A);

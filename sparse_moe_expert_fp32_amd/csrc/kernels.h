@@ -94,6 +94,25 @@ struct MfmaGemmTArgs {
   const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: SwiGLU backward, [S][N]
   uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
 };
+int mfma_t_tile_rows();
+
+// ---- rank-r adapter products on the matrix cores (lowrank.hip)
+struct ProjMArgs {                        // Z_s = scale * A M_s^T over each expert's rows
+  const uint16_t *a; int lda; const int32_t *perm_src; int kk;
+  const int2 *tiles; const int *ntiles; const int32_t *offsets;   // 64-row tiles
+  int K, r, nsrc;
+  const uint16_t *m0, *m1;                // [E][r][K]
+  float scale; float *Z0, *Z1; int ldz;
+};
+void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st);
+struct WgradMArgs {                       // out[e][a][b] = scale * sum_p W[p][a] R[p][b]
+  const uint16_t *w; int ldw; const int32_t *perm_src; int kk;
+  const float *rr; int ldr;
+  const int32_t *offsets; int E, wide, r; float scale;
+  float *out; size_t oe; int oa, ob;
+};
+void launch_wgrad_mfma(const WgradMArgs &G, bool gather, hipStream_t st);
+void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st);
 
 }  // namespace moe

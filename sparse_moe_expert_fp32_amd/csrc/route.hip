@@ -9,10 +9,10 @@
 // state neither.
 //
 // Two kernels:
-//   router_logits  fp32 FMA on the vector ALUs (no matrix cores), a 32-token
-//                  x (64*NE)-expert register tile per 256-thread block, d
-//                  optionally split across blocks so that small token counts
-//                  still fill the chip; each split writes its own partial.
+//   router_logits  fp32 FMA on the vector ALUs (no matrix cores), a 128-token
+//                  x 128-expert tile per 256-thread block, d optionally split
+//                  across blocks so that small token counts still fill the
+//                  chip; each split writes its own partial.
 //   router_topk    one wave per token: sums the partials in split order, adds
 //                  the bias, then k rounds of a wave-wide argmax on the key
 //                  (logit desc, index asc) and the softmax of the k winners.
@@ -21,63 +21,82 @@
 
 namespace moe {
 
-constexpr int RT_TM = 32;   // tokens per block (8 per wave)
-constexpr int RT_KC = 16;   // d-chunk staged in LDS
+constexpr int RT_TM = 128;  // tokens per block
+constexpr int RT_TE = 128;  // experts per block
+constexpr int RT_KC = 16;   // d-chunk staged in LDS per step
 
-// The d-chunk staged per step: 16 rows of W_r, 8 when E > 512 (LDS budget).
-template <typename T, int NE>
+// Block tile 128 tokens x 128 experts, 256 threads, each an 8 x 8 register
+// tile; x is staged transposed ([k][token]) and W_r as is ([k][expert]) so
+// that every thread reads its 8 + 8 operands with four 16-byte LDS loads per
+// k and issues 64 FMAs.  blockIdx.z splits d; each split writes a partial.
+template <typename T>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const T *__restrict__ x, const float *__restrict__ wr, int Tn, int d, int E,
     int split_len, float *__restrict__ partial) {
-  constexpr int KC = NE <= 8 ? RT_KC : RT_KC / 2;
-  __shared__ float xs[RT_TM][KC + 1];
-  __shared__ float ws[KC][NE * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT_TM;
-  const int c_begin = blockIdx.y * split_len;
+  __shared__ __attribute__((aligned(16))) float xs[2][RT_KC][RT_TM];
+  __shared__ __attribute__((aligned(16))) float ws[2][RT_KC][RT_TE];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int t0 = blockIdx.x * RT_TM, e0 = blockIdx.y * RT_TE;
+  const int c_begin = blockIdx.z * split_len;
   const int c_end = min(d, c_begin + split_len);
-  float acc[8][NE];
+  // staging roles: x: token tid/2, 8 consecutive k; W: row tid/16, 8 experts
+  const int xt = tid >> 1, xk = (tid & 1) * 8;
+  const int wk = tid >> 4, we = (tid & 15) * 8;
+  float acc[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int n = 0; n < NE; ++n) acc[i][n] = 0.f;
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
 
-  for (int c0 = c_begin; c0 < c_end; c0 += KC) {
-    // stage x[t0:t0+32, c0:c0+KC] and W_r[c0:c0+KC, :]
-    for (int i = tid; i < RT_TM * KC; i += 256) {
-      int tt = i / KC, cc = i % KC;
-      int t = t0 + tt, c = c0 + cc;
-      xs[tt][cc] = (t < Tn && c < c_end) ? Elem<T>::ld(x, (size_t)t * d + c) : 0.f;
-    }
-    for (int i = tid; i < KC * NE * 64; i += 256) {
-      int cc = i / (NE * 64), e = i % (NE * 64);
-      int c = c0 + cc;
-      ws[cc][e] = (c < c_end && e < E) ? wr[(size_t)c * E + e] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int cc = 0; cc < KC; ++cc) {
-      float wv[NE];
-#pragma unroll
-      for (int n = 0; n < NE; ++n) wv[n] = ws[cc][lane + 64 * n];
+  auto stage = [&](int c0, int buf) {
+    {
+      const int t = t0 + xt;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float xv = xs[wave * 8 + i][cc];
-#pragma unroll
-        for (int n = 0; n < NE; ++n) acc[i][n] = fmaf(xv, wv[n], acc[i][n]);
+        const int c = c0 + xk + i;
+        xs[buf][xk + i][xt] = (t < Tn && c < c_end) ? Elem<T>::ld(x, (size_t)t * d + c) : 0.f;
       }
     }
+    {
+      const int c = c0 + wk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = e0 + we + i;
+        ws[buf][wk][we + i] = (c < c_end && e < E) ? wr[(size_t)c * E + e] : 0.f;
+      }
+    }
+  };
+
+  int buf = 0;
+  stage(c_begin, 0);
+  __syncthreads();
+  for (int c0 = c_begin; c0 < c_end; c0 += RT_KC) {
+    if (c0 + RT_KC < c_end) stage(c0 + RT_KC, buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < RT_KC; ++kk) {
+      const float4 xa = *reinterpret_cast<const float4 *>(&xs[buf][kk][ty * 8]);
+      const float4 xb = *reinterpret_cast<const float4 *>(&xs[buf][kk][ty * 8 + 4]);
+      const float4 wa = *reinterpret_cast<const float4 *>(&ws[buf][kk][tx * 8]);
+      const float4 wb = *reinterpret_cast<const float4 *>(&ws[buf][kk][tx * 8 + 4]);
+      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+    }
     __syncthreads();
+    buf ^= 1;
   }
-  float *out = partial + (size_t)blockIdx.y * Tn * E;
+  float *out = partial + (size_t)blockIdx.z * Tn * E;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int t = t0 + wave * 8 + i;
+    const int t = t0 + ty * 8 + i;
     if (t >= Tn) continue;
 #pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      int e = lane + 64 * n;
-      if (e < E) out[(size_t)t * E + e] = acc[i][n];
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + tx * 8 + j;
+      if (e < E) out[(size_t)t * E + e] = acc[i][j];
     }
   }
 }
@@ -140,47 +159,33 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
 }
 
-int route_splits(int T, int d) {
-  int nbx = (T + RT_TM - 1) / RT_TM;
-  int max_splits = (d + RT_KC - 1) / RT_KC;
-  int s = (256 + nbx - 1) / nbx;
+int route_splits(int T, int d, int E) {
+  const int blocks = ((T + RT_TM - 1) / RT_TM) * ((E + RT_TE - 1) / RT_TE);
+  const int max_splits = (d + RT_KC - 1) / RT_KC;
+  int s = (512 + blocks - 1) / blocks;
   if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;
   return s;
 }
 
 size_t route_ws_bytes(int T, int d, int E) {
-  return (size_t)route_splits(T, d) * T * E * sizeof(float);
-}
-
-template <typename T, int NE>
-static void launch_logits(const void *x, const float *wr, int Tn, int d, int E, int splits,
-                          int split_len, float *partial, hipStream_t st) {
-  dim3 grid((Tn + RT_TM - 1) / RT_TM, splits);
-  router_logits_kernel<T, NE><<<grid, 256, 0, st>>>((const T *)x, wr, Tn, d, E, split_len,
-                                                    partial);
-}
-
-template <typename T>
-static void launch_logits_ne(int NE, const void *x, const float *wr, int Tn, int d, int E,
-                             int splits, int split_len, float *partial, hipStream_t st) {
-  if (NE <= 1) launch_logits<T, 1>(x, wr, Tn, d, E, splits, split_len, partial, st);
-  else if (NE <= 2) launch_logits<T, 2>(x, wr, Tn, d, E, splits, split_len, partial, st);
-  else if (NE <= 4) launch_logits<T, 4>(x, wr, Tn, d, E, splits, split_len, partial, st);
-  else if (NE <= 8) launch_logits<T, 8>(x, wr, Tn, d, E, splits, split_len, partial, st);
-  else launch_logits<T, 16>(x, wr, Tn, d, E, splits, split_len, partial, st);
+  return (size_t)route_splits(T, d, E) * T * E * sizeof(float);
 }
 
 void launch_router_logits(bool bf16, const void *x, const float *wr, int Tn, int d, int E,
                           void *ws, int *splits_out, hipStream_t st) {
-  int splits = route_splits(Tn, d);
-  int chunks = (d + RT_KC - 1) / RT_KC;
-  int split_len = ((chunks + splits - 1) / splits) * RT_KC;
+  int splits = route_splits(Tn, d, E);
+  const int chunks = (d + RT_KC - 1) / RT_KC;
+  const int split_len = ((chunks + splits - 1) / splits) * RT_KC;
   splits = (d + split_len - 1) / split_len;
   float *partial = (float *)ws;
-  int NE = (E + 63) / 64;
-  if (bf16) launch_logits_ne<bf16_t>(NE, x, wr, Tn, d, E, splits, split_len, partial, st);
-  else launch_logits_ne<float>(NE, x, wr, Tn, d, E, splits, split_len, partial, st);
+  dim3 grid((Tn + RT_TM - 1) / RT_TM, (E + RT_TE - 1) / RT_TE, splits);
+  if (bf16)
+    router_logits_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t *)x, wr, Tn, d, E, split_len,
+                                                       partial);
+  else
+    router_logits_kernel<float><<<grid, 256, 0, st>>>((const float *)x, wr, Tn, d, E, split_len,
+                                                      partial);
   *splits_out = splits;
 }
 
