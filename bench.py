@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a kernel of "
+                         "known traffic that calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is "
@@ -198,6 +201,15 @@ def main():
         "load": {"max": int(counts.max()), "mean": float(counts.mean()),
                  "empty_experts": int((counts == 0).sum())},
     }
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_probe_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -119,13 +119,15 @@ struct FwdLayout {
   }
 };
 
-int persistent_grid() {
+// Persistent grids: blocks_per_cu resident blocks on every compute unit
+// (rounded to a multiple of the 8 XCDs).
+int persistent_grid(int blocks_per_cu = 1) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 8)
     cus = 256;
-  return cus & ~7;
+  return (cus * blocks_per_cu) & ~7;
 }
 
 // ---- adapter backward workspace
@@ -373,7 +375,7 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     Q.m0 = (const uint16_t *)gate.A; Q.m1 = (const uint16_t *)up.A; Q.scale = 1.f;
     Q.Z0 = Z; Q.Z1 = Z + r; Q.ldz = 3 * r;
     moe::launch_proj_mfma(Q, mtl, true, st);
-    const int grid = persistent_grid();
+    const int grid = persistent_grid(2);
     moe::MfmaGemmArgs M{};
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
     M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;

@@ -56,4 +56,21 @@ DEV void load_lds16(const void *gsrc, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
 }
 
+// 4 bytes per lane straight into LDS: lane i writes lds_wave_base + 4 i
+// (only the active lanes write).
+DEV void load_lds4(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would make the compiler drain every outstanding load, including LDS-DMA
+// that is deliberately left in flight.  Callers wait (s_waitcnt) for the
+// data they need before calling it; the empty asm statements keep the
+// compiler from moving memory operations across it.
+DEV void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace moe
