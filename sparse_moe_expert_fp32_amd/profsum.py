@@ -33,23 +33,25 @@ def trace(stats_csv: str, out_md: str, cmd: str, top: int = 25):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def _per_dispatch(path: str, counter: str):
+def _dispatches(path: str, counter: str):
     acc = defaultdict(lambda: defaultdict(float))
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
         acc[r["Kernel_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
-    return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+    return {k: list(v.values()) for k, v in acc.items()}
 
 
 def traffic(fetch_csv, write_csv, out_json, kernel, copy_bytes, flops_per_launch, cmd,
             sources_hash):
-    f = _per_dispatch(fetch_csv, "FETCH_SIZE")
-    w = _per_dispatch(write_csv, "WRITE_SIZE")
+    f = _dispatches(fetch_csv, "FETCH_SIZE")
+    w = _dispatches(write_csv, "WRITE_SIZE")
     pick = lambda d, rx: next(v for k, v in d.items() if re.search(rx, k))
-    copy_rx = r"copyBuffer|copy|Copy"
-    kf, kw = pick(f, kernel), pick(w, kernel)
-    cf, cw = pick(f, copy_rx), pick(w, copy_rx)
+    copy_rx = r"copyBuffer"
+    mean = lambda v: sum(v) / len(v)
+    kf, kw = mean(pick(f, kernel)), mean(pick(w, kernel))
+    # the probe is the largest copy dispatch (the others are small uploads)
+    cf, cw = max(pick(f, copy_rx)), max(pick(w, copy_rx))
     f_scale = copy_bytes / (cf * 1024.0)
     w_scale = copy_bytes / (cw * 1024.0)
     rec = {
