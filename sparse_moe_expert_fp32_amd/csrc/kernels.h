@@ -86,15 +86,18 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t 
 struct MfmaGemmTArgs {
   const void *a0, *a1; int lda;           // A rows: dO (mode 0) or dG, dU (mode 1), [S][lda]
   const int2 *tiles; const int *ntiles; const int32_t *offsets;
-  int K, N, NT;                           // reduction per source, output columns, N / 128
-  const uint8_t *q0; const uint16_t *s0;  // stored [E][K][N/2], scales [E][K][N/128]
-  const uint8_t *q1; const uint16_t *s1;  // mode 1: second source (up)
+  int K, N, NT;                           // reduction per source, output columns, ceil(N / 256)
+  const uint16_t *w0, *w1;                // dequantised base, [E][N][K] bf16 (w1: mode 1, up)
   const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
   const uint16_t *L0, *L1;                // adapter A of the matrix, [E][r][N]
   const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: SwiGLU backward, [S][N]
   uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
 };
 int mfma_t_tile_rows();
+int mfma_t_tile_cols();
+// out[e][c][n] = bf16(s[e][n][c/128] q[e][n][c]) for experts with rows; R, C multiples of 64
+void launch_dequant_t(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
+                      int C, uint16_t *out, hipStream_t st);
 
 // ---- rank-r adapter products on the matrix cores (lowrank.hip)
 struct ProjMArgs {                        // Z_s = scale * A M_s^T over each expert's rows
