@@ -130,6 +130,12 @@ int persistent_grid(int blocks_per_cu = 1) {
   return (cus * blocks_per_cu) & ~7;
 }
 
+// one transposed int4 matrix with its f32 scales (d x f or f x d: the same size)
+size_t qt_slot_bytes(const moe_dims *d) {
+  const size_t e = d->n_experts, df = (size_t)d->d_model * d->d_ff;
+  return e * df / 2 + e * df / 128 * 4;
+}
+
 // ---- adapter backward workspace
 struct BwdLayout {
   size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, bt, wt, wr_t, dx_r, dO, dZ, dH32,
@@ -146,8 +152,8 @@ struct BwdLayout {
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // B of down, gate, up transposed to [E][r][N] (bf16)
     bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
-    // dequantised base, two [E][..][..] bf16 slots: down, then gate and up
-    wt = mf ? c.take((size_t)d->n_experts * dm * f * 2 * 2) : 0;
+    // transposed int4 base + scales, two slots: down, then gate and up
+    wt = mf ? c.take(2 * qt_slot_bytes(d)) : 0;
     wr_t = c.take((size_t)d->n_experts * dm * 4);
     dx_r = c.take((size_t)d->T * dm * 4);
     dO = c.take(S * dm * ab);
@@ -481,7 +487,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   if (use_mfma(dims)) {
     int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
-    const int grid = persistent_grid(2);
+    const int grid = persistent_grid();
     const int mtp = (int)max_tiles(dims, moe::mfma_tile_rows());
     moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st);
     moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_p, ntiles_p, st);
@@ -490,7 +496,9 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::launch_transpose_nr(down.B, E, d, r, bt_d, st);
     moe::launch_transpose_nr(gate.B, E, f, r, bt_g, st);
     moe::launch_transpose_nr(up.B, E, f, r, bt_u, st);
-    uint16_t *wt0 = at<uint16_t>(ws, L.wt), *wt1 = wt0 + (size_t)E * d * f;
+    const size_t qsz = (size_t)E * d * f / 2, slot = qt_slot_bytes(dims);
+    uint8_t *qt0 = at<uint8_t>(ws, L.wt), *qt1 = qt0 + slot;
+    float *st0 = reinterpret_cast<float *>(qt0 + qsz), *st1 = reinterpret_cast<float *>(qt1 + qsz);
     const uint16_t *H16 = (const uint16_t *)H;
 
     // dZ_d = lam dO B_d
@@ -508,11 +516,11 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
     moe::MfmaGemmTArgs M{};
     M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
-    M.K = d; M.N = f; M.NT = (f + 255) / 256; M.w0 = wt0;
+    M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qt0; M.st0 = st0;
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
-    moe::launch_dequant_t(down.q, down.scale, offsets, E, d, f, wt0, st);
+    moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
     TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
@@ -538,12 +546,13 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
     moe::MfmaGemmTArgs X{};
     X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m; X.ntiles = ntiles_m;
-    X.offsets = offsets; X.K = f; X.N = d; X.NT = (d + 255) / 256; X.w0 = wt0; X.w1 = wt1;
+    X.offsets = offsets; X.K = f; X.N = d; X.NT = (d + 255) / 256;
+    X.qt0 = qt0; X.st0 = st0; X.qt1 = qt1; X.st1 = st1;
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A;
     X.out = (uint16_t *)dXp; X.ldo = d;
-    moe::launch_dequant_t(gate.q, gate.scale, offsets, E, f, d, wt0, st);
-    moe::launch_dequant_t(up.q, up.scale, offsets, E, f, d, wt1, st);
+    moe::launch_transpose_q(gate.q, gate.scale, offsets, E, f, d, qt0, st0, st);
+    moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
     TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, grid, st));
     moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
     return hip_status("moe_adapter_bwd");

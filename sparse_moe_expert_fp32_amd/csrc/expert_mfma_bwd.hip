@@ -2,270 +2,341 @@
 //
 // Under TQP the base is frozen ("Reversible Sparse MoE Single Node" skill card,
 // Principle 3), so the backward only needs the input gradients through each
-// expert matrix, i.e. products with the base itself (not its transpose):
+// expert matrix, i.e. products with the base itself (the forward uses its
+// transpose):
 //   mode 0:  dH = dO W_d + dZ_d A_d, then the SwiGLU backward
 //            dG = dH U s (1 + G (1 - s)), dU = dH G s, s = sigmoid(G)
 //   mode 1:  dX_perm = dG W_g + dU W_u + dZ_g A_g + dZ_u A_u
 // (dZ = lam dOut B of the same matrix, computed beforehand).
 //
-// Here the reduction runs over the storage rows of the int4 base and the
-// group scale changes with every reduction step, so the exact per-group
-// scaling of the forward does not apply.  A pre-pass dequantises the frozen
-// base of every expert that received rows into bf16(s * q) (one rounding per
-// weight) laid out [E][N_out][K] with the reduction contiguous; the product
-// then runs like the forward kernel: A rows through LDS (LDS-DMA, XOR
-// swizzle), B straight from global memory into registers one group ahead,
+// The reduction runs over the storage rows n of the int4 base, and the group
+// scale s[n][c/128] changes with every reduction step but is constant over
+// 128 output columns.  So the scale moves onto the other operand:
+//   sum_n A[p][n] s[n][g] q[n][c] = sum_n A'_g[p][n] q[n][c],
+//   A'_g[p][n] = bf16(A[p][n] s[n][g]),   g = c / 128,
+// and the int4 operand stays int4 all the way to the matrix cores, unpacked
+// exactly as 136 + q (nibble in the mantissa of 128.0).  The offset is taken
+// out by one more MFMA per row fragment against a constant 136 operand, which
+// accumulates 136 sum_n A'_g[p][n] from exactly the values the main products
+// used.
+//
+// A pre-pass transposes the int4 nibbles so that each output column holds its
+// reduction run as packed words (the same 8-per-word order as the forward
+// operand) and lays the scales out per column group.  The GEMM: 128 x 256
+// output tile per block, four waves as 2 x 2, 64 x 128 per wave (one column
+// group per wave); A rows double-buffered through LDS (LDS-DMA, XOR swizzle),
+// scales through LDS, int4 words straight into registers one step ahead,
 // v_mfma_f32_16x16x32_bf16 into float32 accumulators, persistent
-// XCD-partitioned work list, two blocks per CU.
+// XCD-partitioned work list, one block per CU.
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
 
 namespace moe {
 
-constexpr int GT_BM = 64, GT_KG = 128, GT_BN = 256;
+constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 128;
 
-// ------------------------------------------------------------ dequantise --
-// out[e][c][n] = bf16(s[e][n][c/128] * q[e][n][c]) for experts with rows.
-// q: [E][R][C/2] (storage rows R = reduction of the backward), s: [E][R][C/128].
-// Block: 64 storage rows x 64 columns; LDS transpose; 16-byte stores along n.
-__global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t *__restrict__ q,
-                                                        const uint16_t *__restrict__ s,
-                                                        const int32_t *__restrict__ offsets,
-                                                        int R, int C, uint16_t *__restrict__ out) {
-  __shared__ uint16_t t[64][72];   // [c][n], padded rows
+// ------------------------------------------------------------ transpose --
+// q: [E][R][C/2] (packed along C), s: [E][R][C/128] bf16  ->
+// qt: [E][C][R/2] (packed along R, same in-word order), st: [E][C/128][R] f32.
+// Experts without rows are skipped.  Block: 64 storage rows x 64 columns.
+__global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restrict__ q,
+                                                          const uint16_t *__restrict__ s,
+                                                          const int32_t *__restrict__ offsets,
+                                                          int R, int C, uint8_t *__restrict__ qt,
+                                                          float *__restrict__ st) {
+  __shared__ uint8_t t[64][68];   // [c][n] raw nibbles 0..15
   const int e = blockIdx.z;
-  if (offsets[e + 1] == offsets[e]) return;   // no rows routed to this expert
+  if (offsets[e + 1] == offsets[e]) return;
   const int n0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tid = threadIdx.x;
-  // read: 64 rows x 8 words; each thread 2 words (row tid/4, words (tid%4)*2 +{0,1})
   {
     const int rr = tid >> 2, wq = (tid & 3) * 2;
     const size_t row = (size_t)e * R + n0 + rr;
     const uint32_t *qw = reinterpret_cast<const uint32_t *>(q + row * (C / 2)) + (c0 >> 3);
-    const float sc = bf2f(s[row * (C / 128) + (c0 >> 7)]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t wv = qw[wq + h];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int c = (wq + h) * 8 + j;
-        t[c][rr] = f2bf((float)int4_of_word(wv, j) * sc);
+        const int slot = (j >> 1) + ((j & 1) << 2);   // nibble slot of element j
+        t[(wq + h) * 8 + j][rr] = (uint8_t)((wv >> (4 * slot)) & 15u);
       }
     }
   }
+  if ((c0 & 127) == 0 && tid < 64) {
+    const int G = C / 128, g = c0 >> 7;
+    st[((size_t)e * G + g) * R + n0 + tid] = bf2f(s[((size_t)e * R + n0 + tid) * G + g]);
+  }
   __syncthreads();
-  // write: 64 columns x 8 chunks of 8 n; each thread 2 chunks
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int idx = tid * 2 + h, c = idx >> 3, ch = idx & 7;
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(&t[c][ch * 8]);
-    uint4 v;
-    v.x = src[0]; v.y = src[1]; v.z = src[2]; v.w = src[3];
-    *reinterpret_cast<uint4 *>(out + ((size_t)e * C + c0 + c) * R + n0 + ch * 8) = v;
+    const int idx = tid * 2 + h, c = idx >> 3, j = idx & 7;   // word j of column c
+    const uint8_t *v = &t[c][8 * j];
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = (i >> 1) + ((i & 1) << 2);
+      w |= (uint32_t)v[i] << (4 * slot);
+    }
+    reinterpret_cast<uint32_t *>(qt + ((size_t)e * C + c0 + c) * (R / 2) + n0 / 2)[j] = w;
   }
 }
 
-// ------------------------------------------------------------ bf16 GEMM --
+// ------------------------------------------------------------------ GEMM --
+// A bf16x8 fragment times 8 per-k scales, rounded back to bf16.
+DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
+  uint4 r;
+  r.x = cvt_pk_bf16(__uint_as_float(a.x << 16) * sc[0], __uint_as_float(a.x & 0xffff0000u) * sc[1]);
+  r.y = cvt_pk_bf16(__uint_as_float(a.y << 16) * sc[2], __uint_as_float(a.y & 0xffff0000u) * sc[3]);
+  r.z = cvt_pk_bf16(__uint_as_float(a.z << 16) * sc[4], __uint_as_float(a.z & 0xffff0000u) * sc[5]);
+  r.w = cvt_pk_bf16(__uint_as_float(a.w << 16) * sc[6], __uint_as_float(a.w & 0xffff0000u) * sc[7]);
+  return r;
+}
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 0): wait
+// for every outstanding vector memory (incl. LDS-DMA) and LDS operation
+constexpr int kWaitAll = 0x0070;
+
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
-  // two distinct arrays, so that reads of one are not ordered behind the
+__global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
+  // two distinct slots, so that reads of one are not ordered behind the
   // LDS-DMA writes into the other
-  __shared__ __attribute__((aligned(16))) bf16_t lds0[GT_BM * GT_KG];
-  __shared__ __attribute__((aligned(16))) bf16_t lds1[GT_BM * GT_KG];
-  const int Kh = A.K, N = A.N;
-  const int NGh = Kh / GT_KG;
-  const int NG = MODE == 1 ? 2 * NGh : NGh;   // mode 1 reduces over [dG | dU]
+  __shared__ __attribute__((aligned(16))) bf16_t al0[GT_BM * GT_KS];
+  __shared__ __attribute__((aligned(16))) bf16_t al1[GT_BM * GT_KS];
+  __shared__ __attribute__((aligned(16))) float sl0[2 * GT_KS];
+  __shared__ __attribute__((aligned(16))) float sl1[2 * GT_KS];
+
+  const int Kh = A.K, N = A.N, G = N / 128;
+  const int NKh = Kh / GT_KS;
+  const int NK = MODE == 1 ? 2 * NKh : NKh;   // mode 1 reduces over [dG | dU]
   const int total = A.ntiles[0] * A.NT;
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int wbeg = (int)(((long long)total * xcd) >> 3);
   const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
+  const uint4 c136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136
+  // int4 unpack: each bf16 pair of 136 + q is one shift and one three-input
+  // logic op, ((w >> 4i) & 0x000F000F) ^ 0x43084308 (constants in registers)
+  const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  uint32_t kMagic;
+  asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(kMagic));
 
   for (int wi = wbeg + bi; wi < wend; wi += nper) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));   // keep tid-only arithmetic inside the loop
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
+    const int wm = w & 1, wn = w >> 1;
     const int ti = wi / A.NT, nt = wi - ti * A.NT;
     const int2 tile = A.tiles[ti];
     const int e = tile.x, p0 = tile.y;
     const int rows = min(GT_BM, A.offsets[e + 1] - p0);
     const int c0 = nt * GT_BN;
-    __syncthreads();  // LDS of the previous item is free
 
-    // A staging: 64 rows x 16 chunks, 4 per thread per group (rows p0 + r)
-    uint32_t aoff[4];
+    // A staging: wave w, instruction i covers rows 4 (8w + i) .. +3
+    uint32_t aoff[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * (w * 4 + j) + (lane >> 4);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * (w * 8 + i) + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
-      aoff[j] = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.lda * 2) + c * 16;
+      aoff[i] = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.lda * 2) + c * 16;
     }
-    auto stage = [&](int g, bf16_t *buf) {
-      const bool second = MODE == 1 && g >= NGh;
+    // scale staging: wave w: column group (w >> 1), k 64 (w & 1) + lane
+    const int sg = min(c0 / 128 + (w >> 1), G - 1);
+    const int sk = 64 * (w & 1) + lane;
+    // int4 words: this wave's 128 columns, words 4 lg .. 4 lg + 3 of each step
+    const int cb = c0 + 128 * wn + lr;
+    auto stage = [&](int jr, bf16_t *abuf, float *sbuf) {
+      const int j = min(jr, NK - 1);
+      const bool second = MODE == 1 && j >= NKh;
+      const int kj = second ? j - NKh : j;
       const char *base = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
-      const size_t koff = (size_t)(second ? g - NGh : g) * GT_KG * 2;
+      const uint32_t koff = (uint32_t)kj * GT_KS * 2;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_lds16(base + aoff[j] + koff, buf + (w * 4 + j) * 512);
+      for (int i = 0; i < 8; ++i) load_lds16(base + aoff[i] + koff, abuf + (w * 8 + i) * 512);
+      const float *sp = second ? A.st1 : A.st0;
+      if (jr < NK) load_lds4(sp + ((size_t)e * G + sg) * Kh + kj * GT_KS + sk, sbuf + w * 64);
+      else sbuf[w * 64 + lane] = 0.f;
     };
-    // B: this wave's 64 columns, 16 bytes (8 k) per lane per k-step and fragment
-    const int cw = min(c0 + w * 64 + lr, N - 1);
-    uint4 b0[4][4], b1[4][4];
-    auto load_b = [&](int g, uint4 (&b)[4][4]) {
-      const bool second = MODE == 1 && g >= NGh;
-      const uint16_t *wt = second ? A.w1 : A.w0;
-      const int kg = second ? g - NGh : g;
+    auto load_b = [&](int jr, uint4 (&b)[8]) {
+      const int j = min(jr, NK - 1);
+      const bool second = MODE == 1 && j >= NKh;
+      const int kj = second ? j - NKh : j;
+      const uint8_t *qp = second ? A.qt1 : A.qt0;
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int c = min(cw + nf * 16, N - 1);
-        const uint16_t *col = wt + ((size_t)e * N + c) * Kh + kg * GT_KG + 32 * lg;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) b[s][nf] = *reinterpret_cast<const uint4 *>(col + 8 * s);
+      for (int nf = 0; nf < 8; ++nf) {
+        const int c = min(cb + 16 * nf, N - 1);
+        b[nf] = *reinterpret_cast<const uint4 *>(qp + ((size_t)e * N + c) * (Kh / 2) +
+                                                 kj * (GT_KS / 2) + 16 * lg);
       }
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][8], corr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      corr[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nf = 0; nf < 8; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // one 128-deep step: 4 k-substeps x 4 row fragments x (8 + 1) MFMAs.
+    // Lane group lg takes k = 32 lg + 8 s .. + 7 in substep s (A chunk
+    // 4 lg + s, int4 word 4 lg + s), the same permutation on both operands.
+    auto compute = [&](const bf16_t *abuf, const float *sbuf, const uint4 (&b)[8]) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float sc[8];
+        {
+          const float4 s0 = *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 32 * lg + 8 * s);
+          const float4 s1 =
+              *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 32 * lg + 8 * s + 4);
+          sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+          sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+        }
+        uint4 av[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = 64 * wm + 16 * m + lr;
+          const uint4 araw = *reinterpret_cast<const uint4 *>(
+              abuf + r * GT_KS + (((4 * lg + s) ^ (r & 15)) << 3));
+          av[m] = scale_frag(araw, sc);
+          corr[m] = mfma32(av[m], c136, corr[m]);
+        }
+#pragma unroll
+        for (int nf = 0; nf < 8; ++nf) {
+          const uint32_t x = s == 0 ? b[nf].x : s == 1 ? b[nf].y : s == 2 ? b[nf].z : b[nf].w;
+          uint4 bu;
+          bu.x = __builtin_amdgcn_bitop3_b32(x, kMask, kMagic, 0x6A);
+          bu.y = __builtin_amdgcn_bitop3_b32(x >> 4, kMask, kMagic, 0x6A);
+          bu.z = __builtin_amdgcn_bitop3_b32(x >> 8, kMask, kMagic, 0x6A);
+          bu.w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[m][nf] = mfma32(av[m], bu, acc[m][nf]);
+        }
+      }
+    };
+
+    // double buffer: even steps in (al0, sl0, b0), odd steps in (al1, sl1, b1)
+    uint4 b0[8], b1[8];
+    __syncthreads();  // LDS of the previous item is free
+    load_b(0, b0);
+    stage(0, al0, sl0);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    block_barrier();
+    // (the scheduling barriers keep the next step's loads ahead of the MFMAs,
+    // which the scheduler would otherwise sink next to their wait)
+    // An odd step count gets one phantom step at the end: valid (clamped)
+    // operands with zero scales, so it adds exactly nothing.
+    for (int j = 0; j < NK; j += 2) {
+      load_b(j + 1, b1);
+      stage(j + 1, al1, sl1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(al0, sl0, b0);
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      block_barrier();
+      if (j + 2 < NK) {
+        load_b(j + 2, b0);
+        stage(j + 2, al0, sl0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(al1, sl1, b1);
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      block_barrier();
+    }
+
+    // remove the 136 offset of the int4 operand
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nf = 0; nf < 8; ++nf) acc[m][nf] -= corr[m];
 
-    // one k-group: 4 m-fragments x 4 k-steps x 4 column fragments
-    auto compute = [&](const bf16_t *al, const uint4 (&b)[4][4]) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 av = *reinterpret_cast<const uint4 *>(
-              al + (16 * m + lr) * GT_KG + (((lg * 4 + s) ^ lr) << 3));
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf) acc[m][nf] = mfma32(av, b[s][nf], acc[m][nf]);
-        }
-    };
-
-    // double buffer: even groups in (lds0, b0), odd groups in (lds1, b1)
-    stage(0, lds0);
-    load_b(0, b0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int g = 0; g < NG; g += 2) {
-      if (g + 1 < NG) {
-        stage(g + 1, lds1);
-        load_b(g + 1, b1);
-      }
-      compute(lds0, b0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (g + 1 >= NG) break;
-      if (g + 2 < NG) {
-        stage(g + 2, lds0);
-        load_b(g + 2, b0);
-      }
-      compute(lds1, b1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-
-    // adapter term: acc += dZ L with L = A of the matrix ([r][N]), K = rank
+    // adapter term: acc += dZ L with L = A of the matrix ([r][N]), K = rank.
+    // Loads are unconditional (clamped indices) so that they issue together;
+    // rank columns beyond r are zeroed afterwards.
     const int nsrc = MODE == 1 ? 2 : 1;
     for (int src = 0; src < nsrc; ++src) {
       const float *Zp = src ? A.Z1 : A.Z0;
       const uint16_t *Lm = src ? A.L1 : A.L0;
       for (int j0 = 0; j0 < A.r; j0 += 16) {
+        float zv[4][4];
+        uint16_t lv[8][4];
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const int c = min(cw + nf * 16, N - 1);
+        for (int m = 0; m < 4; ++m) {
+          const int p = p0 + min(64 * wm + 16 * m + lr, rows - 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            zv[m][i] = Zp[(size_t)p * A.ldz + min(j0 + 4 * lg + i, A.r - 1)];
+        }
+#pragma unroll
+        for (int nf = 0; nf < 8; ++nf) {
+          const int c = min(cb + 16 * nf, N - 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lv[nf][i] = Lm[((size_t)e * A.r + min(j0 + 4 * lg + i, A.r - 1)) * N + c];
+        }
+        short4_t av[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            av[m][i] = j0 + 4 * lg + i < A.r ? (short)f2bf(zv[m][i]) : (short)0;
+#pragma unroll
+        for (int nf = 0; nf < 8; ++nf) {
           short4_t bv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 4 * lg + i;
-            bv[i] = j < A.r ? (short)Lm[((size_t)e * A.r + j) * N + c] : (short)0;
-          }
+          for (int i = 0; i < 4; ++i) bv[i] = j0 + 4 * lg + i < A.r ? (short)lv[nf][i] : (short)0;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int p = p0 + min(16 * m + lr, rows - 1);
-            short4_t av;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = j0 + 4 * lg + i;
-              av[i] = j < A.r ? (short)f2bf(Zp[(size_t)p * A.ldz + j]) : (short)0;
-            }
-            acc[m][nf] = mfma16(av, bv, acc[m][nf]);
-          }
+          for (int m = 0; m < 4; ++m) acc[m][nf] = mfma16(av[m], bv, acc[m][nf]);
         }
       }
     }
 
-    // epilogue: results to LDS (two 64 x 128 tiles), then 16-byte stores
-    __syncthreads();
-    bf16_t *t0 = lds0, *t1 = lds1;
-    auto tidx = [](int r, int c) { return r * 128 + ((((c >> 3) ^ (r & 15))) << 3) + (c & 7); };
-    bf16_t *tw = w < 2 ? t0 : t1;
-    if (MODE == 0) {
-      // dG -> tiles, dU kept in registers for a second round
+    // epilogue: per 16-row fragment, through a wave-private 16 x 128 LDS tile
+    // (slot 0 is free: every wave passed the loop's last barrier)
+    bf16_t *tw = al0 + w * (16 * 128);
+    const bool cols_ok = c0 + 128 * wn < N;   // N is a multiple of 128
+    auto tidx = [](int r, int c) { return r * 128 + (((c >> 3) ^ r) << 3) + (c & 7); };
+    auto flush = [&](int m, uint16_t *dst, int ldo) {
+      // 16 rows x 16 chunks of 8 columns: 4 chunks per lane
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int it = 0; it < 4; ++it) {
+        const int idx = it * 64 + lane, r = idx >> 4, ch = idx & 15;
+        const int rr = 64 * wm + 16 * m + r;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&tw[r * 128 + ((ch ^ r) << 3)]);
+        if (cols_ok && rr < rows)
+          *reinterpret_cast<uint4 *>(&dst[(size_t)(p0 + rr) * ldo + c0 + 128 * wn + ch * 8]) = v;
+      }
+    };
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (MODE == 0) {
+        float du[8][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * m + 4 * lg + i;
-          const size_t p = (size_t)(p0 + min(r, rows - 1));
+          const int rr = 64 * wm + 16 * m + 4 * lg + i;
+          const size_t p = (size_t)(p0 + min(rr, rows - 1));
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) {
-            const int c = min(cw + nf * 16, N - 1);
-            const size_t o = p * N + c;
+          for (int nf = 0; nf < 8; ++nf) {
+            const size_t o = p * N + min(cb + 16 * nf, N - 1);
             const float dh = acc[m][nf][i];
             const float gv = bf2f(A.G[o]), uv = bf2f(A.U[o]);
-            const float sg = sigmoid_f(gv);
-            tw[tidx(r, (w & 1) * 64 + nf * 16 + lr)] = f2bf(dh * uv * sg * (1.f + gv * (1.f - sg)));
-            acc[m][nf][i] = dh * gv * sg;   // dU
+            const float sgm = sigmoid_f(gv);
+            tw[tidx(4 * lg + i, 16 * nf + lr)] = f2bf(dh * uv * sgm * (1.f + gv * (1.f - sgm)));
+            du[nf][i] = dh * gv * sgm;
           }
-          asm volatile("" ::: "memory");   // bound the number of G/U loads in flight
         }
-    } else {
+        flush(m, A.dG, N);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * m + 4 * lg + i;
+          for (int nf = 0; nf < 8; ++nf) tw[tidx(4 * lg + i, 16 * nf + lr)] = f2bf(du[nf][i]);
+        flush(m, A.dU, N);
+      } else {
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-            tw[tidx(r, (w & 1) * 64 + nf * 16 + lr)] = f2bf(acc[m][nf][i]);
-        }
-    }
-    __syncthreads();
-    uint16_t *dst = MODE == 0 ? A.dG : A.out;
-    const int ldo = MODE == 0 ? N : A.ldo;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31;
-      const int c = c0 + ch * 8;
-      const bf16_t *tr = ch < 16 ? t0 : t1;
-      const int chl = ch & 15;
-      if (r < rows && c < N)
-        *reinterpret_cast<uint4 *>(&dst[(size_t)(p0 + r) * ldo + c]) =
-            *reinterpret_cast<const uint4 *>(&tr[r * 128 + ((chl ^ (r & 15)) << 3)]);
-    }
-    if (MODE == 0) {
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * m + 4 * lg + i;
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-            tw[tidx(r, (w & 1) * 64 + nf * 16 + lr)] = f2bf(acc[m][nf][i]);
-        }
-      __syncthreads();
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31;
-        const int c = c0 + ch * 8;
-        const bf16_t *tr = ch < 16 ? t0 : t1;
-        const int chl = ch & 15;
-        if (r < rows && c < N)
-          *reinterpret_cast<uint4 *>(&A.dU[(size_t)(p0 + r) * N + c]) =
-              *reinterpret_cast<const uint4 *>(&tr[r * 128 + ((chl ^ (r & 15)) << 3)]);
+          for (int nf = 0; nf < 8; ++nf) tw[tidx(4 * lg + i, 16 * nf + lr)] = f2bf(acc[m][nf][i]);
+        flush(m, A.out, A.ldo);
       }
     }
   }
@@ -274,10 +345,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_t_kernel(const MfmaGemmTA
 int mfma_t_tile_rows() { return GT_BM; }
 int mfma_t_tile_cols() { return GT_BN; }
 
-void launch_dequant_t(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
-                      int C, uint16_t *out, hipStream_t st) {
+void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
+                        int C, uint8_t *qt, float *st, hipStream_t stream) {
   dim3 grid(C / 64, R / 64, E);
-  dequant_t_kernel<<<grid, 256, 0, st>>>(q, s, offsets, R, C, out);
+  transpose_q_kernel<<<grid, 256, 0, stream>>>(q, s, offsets, R, C, qt, st);
 }
 
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st) {

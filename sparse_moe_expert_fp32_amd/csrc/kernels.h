@@ -87,7 +87,8 @@ struct MfmaGemmTArgs {
   const void *a0, *a1; int lda;           // A rows: dO (mode 0) or dG, dU (mode 1), [S][lda]
   const int2 *tiles; const int *ntiles; const int32_t *offsets;
   int K, N, NT;                           // reduction per source, output columns, ceil(N / 256)
-  const uint16_t *w0, *w1;                // dequantised base, [E][N][K] bf16 (w1: mode 1, up)
+  const uint8_t *qt0, *qt1;               // int4 base transposed, [E][N][K/2] (qt1: mode 1, up)
+  const float *st0, *st1;                 // its scales per column group, [E][N/128][K]
   const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
   const uint16_t *L0, *L1;                // adapter A of the matrix, [E][r][N]
   const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: SwiGLU backward, [S][N]
@@ -95,9 +96,10 @@ struct MfmaGemmTArgs {
 };
 int mfma_t_tile_rows();
 int mfma_t_tile_cols();
-// out[e][c][n] = bf16(s[e][n][c/128] q[e][n][c]) for experts with rows; R, C multiples of 64
-void launch_dequant_t(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
-                      int C, uint16_t *out, hipStream_t st);
+// int4 [E][R][C/2] + scales [E][R][C/128] -> transposed int4 [E][C][R/2] + scales
+// [E][C/128][R] (f32), for experts with rows; R, C multiples of 64
+void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
+                        int C, uint8_t *qt, float *st, hipStream_t stream);
 
 // ---- rank-r adapter products on the matrix cores (lowrank.hip)
 struct ProjMArgs {                        // Z_s = scale * A M_s^T over each expert's rows
