@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -138,8 +139,8 @@ size_t qt_slot_bytes(const moe_dims *d) {
 
 // ---- adapter backward workspace
 struct BwdLayout {
-  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, bt, wt, wr_t, dx_r, dO, dZ, dH32,
-      dG, dU, dXp, total;
+  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, bt, wt,
+      wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
   explicit BwdLayout(const moe_dims *d) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
     const bool mf = use_mfma(d);
@@ -150,6 +151,11 @@ struct BwdLayout {
     ntiles_m = mf ? c.take(sizeof(int)) : 0;
     tiles_p = mf ? c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2)) : 0;
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
+    // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
+    tiles_w = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * sizeof(int2)) : 0;
+    ntiles_w = mf ? c.take(sizeof(int)) : 0;
+    part = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * 2 * std::max(dm, f) * d->rank * 4)
+              : 0;
     // B of down, gate, up transposed to [E][r][N] (bf16)
     bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
     // transposed int4 base + scales, two slots: down, then gate and up
@@ -508,11 +514,16 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     Q.m0 = bt_d; Q.scale = lam; Q.Z0 = dZ + 2 * r; Q.ldz = 3 * r;
     moe::launch_proj_mfma(Q, mtp, false, st);
     // dB_d [d][r] = lam sum_p dO[p][n] Z_d[p][j]
+    int2 *tiles_w = at<int2>(ws, L.tiles_w);
+    int *ntiles_w = at<int>(ws, L.ntiles_w);
+    const int mtw = (int)max_tiles(dims, moe::wgrad_tile_rows());
+    moe::launch_build_tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, st);
     moe::WgradMArgs W{};
-    W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r;
+    W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r; W.nsrc = 1;
+    W.tiles = tiles_w; W.ntiles = ntiles_w; W.part = at<float>(ws, L.part);
     W.w = (const uint16_t *)dO; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
     W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
-    moe::launch_wgrad_mfma(W, false, st);
+    moe::launch_wgrad_mfma(W, mtw, false, st);
     // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
     moe::MfmaGemmTArgs M{};
     M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
@@ -525,7 +536,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
-    moe::launch_wgrad_mfma(W, false, st);
+    moe::launch_wgrad_mfma(W, mtw, false, st);
     // dZ_g = lam dG B_g, dZ_u = lam dU B_u
     Q.a = (const uint16_t *)dG; Q.lda = f; Q.K = f; Q.m0 = bt_g; Q.Z0 = dZ;
     moe::launch_proj_mfma(Q, mtp, false, st);
@@ -534,15 +545,14 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // dB [f][r] = lam sum_p dG[p][n] Z[p][j]
     W.w = (const uint16_t *)dG; W.ldw = f; W.rr = Z; W.wide = f; W.scale = lam; W.out = dB_gate;
     W.oe = (size_t)f * r; W.oa = r; W.ob = 1;
-    moe::launch_wgrad_mfma(W, false, st);
+    moe::launch_wgrad_mfma(W, mtw, false, st);
     W.w = (const uint16_t *)dU; W.rr = Z + r; W.out = dB_up;
-    moe::launch_wgrad_mfma(W, false, st);
-    // dA [r][d] = sum_p dZ[p][j] X[token(p)][c]
+    moe::launch_wgrad_mfma(W, mtw, false, st);
+    // dA [r][d] = sum_p dZ[p][j] X[token(p)][c], gate and up in one pass over X
     W.w = (const uint16_t *)x; W.ldw = d; W.rr = dZ; W.wide = d; W.scale = 1.f; W.out = dA_gate;
     W.oe = (size_t)r * d; W.oa = 1; W.ob = d;
-    moe::launch_wgrad_mfma(W, true, st);
-    W.rr = dZ + r; W.out = dA_up;
-    moe::launch_wgrad_mfma(W, true, st);
+    W.nsrc = 2; W.rr1 = dZ + r; W.out1 = dA_up;
+    moe::launch_wgrad_mfma(W, mtw, true, st);
     // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
     moe::MfmaGemmTArgs X{};
     X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m; X.ntiles = ntiles_m;

@@ -24,8 +24,8 @@
 // reduction run as packed words (the same 8-per-word order as the forward
 // operand) and lays the scales out per column group.  The GEMM: 128 x 256
 // output tile per block, four waves as 2 x 2, 64 x 128 per wave (one column
-// group per wave); A rows double-buffered through LDS (LDS-DMA, XOR swizzle),
-// scales through LDS, int4 words straight into registers one step ahead,
+// group per wave); A rows through a 3-deep LDS ring (LDS-DMA, XOR swizzle),
+// scales through LDS, int4 words straight into registers two steps ahead,
 // v_mfma_f32_16x16x32_bf16 into float32 accumulators, persistent
 // XCD-partitioned work list, one block per CU.
 #include "common.h"
@@ -39,47 +39,45 @@ constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 128;
 // ------------------------------------------------------------ transpose --
 // q: [E][R][C/2] (packed along C), s: [E][R][C/128] bf16  ->
 // qt: [E][C][R/2] (packed along R, same in-word order), st: [E][C/128][R] f32.
-// Experts without rows are skipped.  Block: 64 storage rows x 64 columns.
+// Experts without rows are skipped.  Block: 128 storage rows x 128 columns;
+// each thread transposes one 8 x 8 nibble block in registers (8 words read
+// from 8 rows -> 8 words of 8 columns), then the words are re-laid out
+// through LDS so that every column is written as 64 contiguous bytes.
+DEV int nib_slot(int j) { return (j >> 1) + ((j & 1) << 2); }   // slot of element j
+
 __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restrict__ q,
                                                           const uint16_t *__restrict__ s,
                                                           const int32_t *__restrict__ offsets,
                                                           int R, int C, uint8_t *__restrict__ qt,
                                                           float *__restrict__ st) {
-  __shared__ uint8_t t[64][68];   // [c][n] raw nibbles 0..15
+  __shared__ uint32_t lw[128][17];   // [column][row block of 8], padded
   const int e = blockIdx.z;
   if (offsets[e + 1] == offsets[e]) return;
-  const int n0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tid = threadIdx.x;
-  {
-    const int rr = tid >> 2, wq = (tid & 3) * 2;
-    const size_t row = (size_t)e * R + n0 + rr;
-    const uint32_t *qw = reinterpret_cast<const uint32_t *>(q + row * (C / 2)) + (c0 >> 3);
+  const int n0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const int tid = threadIdx.x, wq = tid & 15, a = tid >> 4;
+  uint32_t in[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t wv = qw[wq + h];
+  for (int i = 0; i < 8; ++i)
+    in[i] = reinterpret_cast<const uint32_t *>(q + ((size_t)e * R + n0 + 8 * a + i) * (C / 2) +
+                                               c0 / 2)[wq];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int slot = (j >> 1) + ((j & 1) << 2);   // nibble slot of element j
-        t[(wq + h) * 8 + j][rr] = (uint8_t)((wv >> (4 * slot)) & 15u);
-      }
-    }
+  for (int j = 0; j < 8; ++j) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o |= ((in[i] >> (4 * nib_slot(j))) & 15u) << (4 * nib_slot(i));
+    lw[8 * wq + j][a] = o;
   }
-  if ((c0 & 127) == 0 && tid < 64) {
+  if (tid < 128) {
     const int G = C / 128, g = c0 >> 7;
     st[((size_t)e * G + g) * R + n0 + tid] = bf2f(s[((size_t)e * R + n0 + tid) * G + g]);
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int idx = tid * 2 + h, c = idx >> 3, j = idx & 7;   // word j of column c
-    const uint8_t *v = &t[c][8 * j];
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int slot = (i >> 1) + ((i & 1) << 2);
-      w |= (uint32_t)v[i] << (4 * slot);
-    }
-    reinterpret_cast<uint32_t *>(qt + ((size_t)e * C + c0 + c) * (R / 2) + n0 / 2)[j] = w;
+    const int idx = tid * 2 + h, c = idx >> 2, q4 = idx & 3;
+    uint4 v;
+    v.x = lw[c][4 * q4]; v.y = lw[c][4 * q4 + 1]; v.z = lw[c][4 * q4 + 2]; v.w = lw[c][4 * q4 + 3];
+    *reinterpret_cast<uint4 *>(qt + ((size_t)e * C + c0 + c) * (R / 2) + n0 / 2 + 16 * q4) = v;
   }
 }
 
@@ -94,18 +92,23 @@ DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
   return r;
 }
 
-// s_waitcnt immediate (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 0): wait
-// for every outstanding vector memory (incl. LDS-DMA) and LDS operation
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).  vmcnt_imm(n): at most n vector memory operations
+// (loads, LDS-DMA, stores) of this wave outstanding; kWaitAll: none, and no
+// LDS operation either.
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kWaitAll = 0x0070;
 
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
-  // two distinct slots, so that reads of one are not ordered behind the
-  // LDS-DMA writes into the other
+  // three distinct ring slots, so that reads of one are not ordered behind
+  // the LDS-DMA writes into the others
   __shared__ __attribute__((aligned(16))) bf16_t al0[GT_BM * GT_KS];
   __shared__ __attribute__((aligned(16))) bf16_t al1[GT_BM * GT_KS];
+  __shared__ __attribute__((aligned(16))) bf16_t al2[GT_BM * GT_KS];
   __shared__ __attribute__((aligned(16))) float sl0[2 * GT_KS];
   __shared__ __attribute__((aligned(16))) float sl1[2 * GT_KS];
+  __shared__ __attribute__((aligned(16))) float sl2[2 * GT_KS];
 
   const int Kh = A.K, N = A.N, G = N / 128;
   const int NKh = Kh / GT_KS;
@@ -155,8 +158,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
 #pragma unroll
       for (int i = 0; i < 8; ++i) load_lds16(base + aoff[i] + koff, abuf + (w * 8 + i) * 512);
       const float *sp = second ? A.st1 : A.st0;
-      if (jr < NK) load_lds4(sp + ((size_t)e * G + sg) * Kh + kj * GT_KS + sk, sbuf + w * 64);
-      else sbuf[w * 64 + lane] = 0.f;
+      load_lds4(sp + ((size_t)e * G + sg) * Kh + kj * GT_KS + sk, sbuf + w * 64);
     };
     auto load_b = [&](int jr, uint4 (&b)[8]) {
       const int j = min(jr, NK - 1);
@@ -216,33 +218,43 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
       }
     };
 
-    // double buffer: even steps in (al0, sl0, b0), odd steps in (al1, sl1, b1)
-    uint4 b0[8], b1[8];
+    // 3-deep pipeline: step j computes from ring slot j % 3 while the loads
+    // of step j + 2 are in flight.  Per thread and step: 8 word loads, 8 + 1
+    // LDS-DMA (the same count in every wave), so "step j + 1 has landed" is
+    // vmcnt(17).  The loop runs in groups of three steps; steps past the end
+    // compute nothing (uniform branch) but still issue their loads, clamped to
+    // the last real step (cache hits into a slot nobody reads), so that every
+    // wait is the same and the compiler's own wait tracking stays exact.  The
+    // scheduling barriers keep each step's loads ahead of the MFMAs, where
+    // the scheduler would otherwise sink them next to their wait.
+    constexpr int kOps = 17;
+    uint4 b0[8], b1[8], b2[8];
     __syncthreads();  // LDS of the previous item is free
     load_b(0, b0);
     stage(0, al0, sl0);
+    load_b(1, b1);
+    stage(1, al1, sl1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
+    block_barrier();
+    for (int j = 0; j < NK; j += 3) {
+#define MOE_T_STEP(JJ, CUR_A, CUR_S, CUR_B, NXT_A, NXT_S, NXT_B) \
+  {                                                              \
+    const int jj = (JJ);                                         \
+    load_b(jj + 2, NXT_B);                                       \
+    stage(jj + 2, NXT_A, NXT_S);                                 \
+    __builtin_amdgcn_sched_barrier(0);                           \
+    if (jj < NK) compute(CUR_A, CUR_S, CUR_B);                   \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));                 \
+    block_barrier();                                             \
+  }
+      MOE_T_STEP(j, al0, sl0, b0, al2, sl2, b2)
+      MOE_T_STEP(j + 1, al1, sl1, b1, al0, sl0, b0)
+      MOE_T_STEP(j + 2, al2, sl2, b2, al1, sl1, b1)
+#undef MOE_T_STEP
+    }
+    // drain the trailing (clamped) loads before the ring is reused below
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     block_barrier();
-    // (the scheduling barriers keep the next step's loads ahead of the MFMAs,
-    // which the scheduler would otherwise sink next to their wait)
-    // An odd step count gets one phantom step at the end: valid (clamped)
-    // operands with zero scales, so it adds exactly nothing.
-    for (int j = 0; j < NK; j += 2) {
-      load_b(j + 1, b1);
-      stage(j + 1, al1, sl1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(al0, sl0, b0);
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      block_barrier();
-      if (j + 2 < NK) {
-        load_b(j + 2, b0);
-        stage(j + 2, al0, sl0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      compute(al1, sl1, b1);
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      block_barrier();
-    }
 
     // remove the 136 offset of the int4 operand
 #pragma unroll
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
     }
 
     // epilogue: per 16-row fragment, through a wave-private 16 x 128 LDS tile
-    // (slot 0 is free: every wave passed the loop's last barrier)
+    // (slot 0 of the ring is free: every wave passed the loop's last barrier)
     bf16_t *tw = al0 + w * (16 * 128);
     const bool cols_ok = c0 + 128 * wn < N;   // N is a multiple of 128
     auto tidx = [](int r, int c) { return r * 128 + (((c >> 3) ^ r) << 3) + (c & 7); };
@@ -347,7 +359,7 @@ int mfma_t_tile_cols() { return GT_BN; }
 
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream) {
-  dim3 grid(C / 64, R / 64, E);
+  dim3 grid(C / 128, R / 128, E);
   transpose_q_kernel<<<grid, 256, 0, stream>>>(q, s, offsets, R, C, qt, st);
 }
 

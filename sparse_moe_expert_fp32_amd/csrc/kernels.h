@@ -97,7 +97,7 @@ struct MfmaGemmTArgs {
 int mfma_t_tile_rows();
 int mfma_t_tile_cols();
 // int4 [E][R][C/2] + scales [E][R][C/128] -> transposed int4 [E][C][R/2] + scales
-// [E][C/128][R] (f32), for experts with rows; R, C multiples of 64
+// [E][C/128][R] (f32), for experts with rows; R, C multiples of 128
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream);
 
@@ -110,13 +110,18 @@ struct ProjMArgs {                        // Z_s = scale * A M_s^T over each exp
   float scale; float *Z0, *Z1; int ldz;
 };
 void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st);
-struct WgradMArgs {                       // out[e][a][b] = scale * sum_p W[p][a] R[p][b]
+struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p][a] R_s[p][b]
   const uint16_t *w; int ldw; const int32_t *perm_src; int kk;
-  const float *rr; int ldr;
+  const float *rr; int ldr;               // R of source 0
+  const float *rr1; float *out1;          // second source (nsrc = 2): same W, strides, scale
+  int nsrc;
   const int32_t *offsets; int E, wide, r; float scale;
   float *out; size_t oe; int oa, ob;
+  const int2 *tiles; const int *ntiles;   // wgrad_tile_rows()-row tiles
+  float *part;                            // partials: [tiles][nsrc][wide][r]
 };
-void launch_wgrad_mfma(const WgradMArgs &G, bool gather, hipStream_t st);
+int wgrad_tile_rows();
+void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st);
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st);
 
