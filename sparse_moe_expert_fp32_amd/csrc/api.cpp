@@ -389,7 +389,7 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     Q.m0 = (const uint16_t *)gate.A; Q.m1 = (const uint16_t *)up.A; Q.scale = 1.f;
     Q.Z0 = Z; Q.Z1 = Z + r; Q.ldz = 3 * r;
     moe::launch_proj_mfma(Q, mtl, true, st);
-    const int grid = persistent_grid(2);
+    const int grid = persistent_grid(moe::mfma_blocks_per_cu());
     moe::MfmaGemmArgs M{};
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
     M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
@@ -493,7 +493,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   if (use_mfma(dims)) {
     int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
-    const int grid = persistent_grid();
+    const int grid = persistent_grid(moe::mfma_t_blocks_per_cu());
     const int mtp = (int)max_tiles(dims, moe::mfma_tile_rows());
     moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st);
     moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_p, ntiles_p, st);

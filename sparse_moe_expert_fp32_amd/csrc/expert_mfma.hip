@@ -40,6 +40,7 @@
 namespace moe {
 
 constexpr int GM_BM = 64;    // rows per tile
+constexpr int GM_BPC = 2;    // resident blocks per CU
 constexpr int GM_KG = 128;   // K per staged chunk = quantization group
 
 // ---------------------------------------------------------------- row sums --
@@ -73,7 +74,7 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 // + the same 32 up columns, MODE 1: 64 columns).  Two blocks share a CU so
 // that one block's memory waits overlap the other's matrix work.
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const MfmaGemmArgs A) {
+__global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGemmArgs A) {
   __shared__ __attribute__((aligned(16))) bf16_t a_lds[2][GM_BM * GM_KG];
   __shared__ __attribute__((aligned(16))) float corr_lds[2][GM_BM];
   __shared__ int tok_lds[GM_BM];
@@ -329,6 +330,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const MfmaGemmArgs
 }
 
 int mfma_tile_rows() { return GM_BM; }
+int mfma_blocks_per_cu() { return GM_BPC; }
 
 void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st) {
   size_t n = (size_t)rows * (K / G);

@@ -22,27 +22,30 @@
 //
 // A pre-pass transposes the int4 nibbles so that each output column holds its
 // reduction run as packed words (the same 8-per-word order as the forward
-// operand) and lays the scales out per column group.  The GEMM: 128 x 256
-// output tile per block, four waves as 2 x 2, 64 x 128 per wave (one column
-// group per wave); A rows through a 3-deep LDS ring (LDS-DMA, XOR swizzle),
-// scales through LDS, int4 words straight into registers two steps ahead,
-// v_mfma_f32_16x16x32_bf16 into float32 accumulators, persistent
-// XCD-partitioned work list, one block per CU.
+// operand), blocked by 64 reduction steps, and lays the scales out per column
+// group.  The GEMM: 128 x 256 output tile per block, four waves as 2 x 2,
+// 64 x 128 per wave (one column group per wave); A rows, int4 words and
+// scales stream through a 3-deep LDS ring (LDS-DMA, A XOR-swizzled) in steps
+// of 64; v_mfma_f32_16x16x32_bf16 into float32 accumulators; persistent
+// XCD-partitioned work list; two blocks per CU, so that one block's VALU work
+// (scaling, unpacking) overlaps the other's matrix work.
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
 
 namespace moe {
 
-constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 128;
+constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 64, GT_BPC = 2;   // GT_BPC: blocks per CU
 
 // ------------------------------------------------------------ transpose --
 // q: [E][R][C/2] (packed along C), s: [E][R][C/128] bf16  ->
-// qt: [E][C][R/2] (packed along R, same in-word order), st: [E][C/128][R] f32.
+// qt: [E][R/64][C][32 bytes] (each column's run of 64 storage rows as 8 words,
+//     same in-word order as the forward operand), st: [E][C/128][R] f32.
 // Experts without rows are skipped.  Block: 128 storage rows x 128 columns;
 // each thread transposes one 8 x 8 nibble block in registers (8 words read
 // from 8 rows -> 8 words of 8 columns), then the words are re-laid out
-// through LDS so that every column is written as 64 contiguous bytes.
+// through LDS so that each 64-row block of a column tile is one contiguous
+// 4 KB run.
 DEV int nib_slot(int j) { return (j >> 1) + ((j & 1) << 2); }   // slot of element j
 
 __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restrict__ q,
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restr
     const int idx = tid * 2 + h, c = idx >> 2, q4 = idx & 3;
     uint4 v;
     v.x = lw[c][4 * q4]; v.y = lw[c][4 * q4 + 1]; v.z = lw[c][4 * q4 + 2]; v.w = lw[c][4 * q4 + 3];
-    *reinterpret_cast<uint4 *>(qt + ((size_t)e * C + c0 + c) * (R / 2) + n0 / 2 + 16 * q4) = v;
+    const size_t blk = (size_t)e * (R / 64) + n0 / 64 + (q4 >> 1);
+    *reinterpret_cast<uint4 *>(qt + (blk * C + c0 + c) * 32 + 16 * (q4 & 1)) = v;
   }
 }
 
@@ -100,12 +104,16 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kWaitAll = 0x0070;
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
-  // three distinct ring slots, so that reads of one are not ordered behind
-  // the LDS-DMA writes into the others
+__global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
+  // a 3-deep ring of stages, each with its A rows, int4 words and scales;
+  // distinct arrays, so that reads of one stage are not ordered behind the
+  // LDS-DMA writes into the others
   __shared__ __attribute__((aligned(16))) bf16_t al0[GT_BM * GT_KS];
   __shared__ __attribute__((aligned(16))) bf16_t al1[GT_BM * GT_KS];
   __shared__ __attribute__((aligned(16))) bf16_t al2[GT_BM * GT_KS];
+  __shared__ __attribute__((aligned(16))) uint8_t bl0[GT_BN * GT_KS / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t bl1[GT_BN * GT_KS / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t bl2[GT_BN * GT_KS / 2];
   __shared__ __attribute__((aligned(16))) float sl0[2 * GT_KS];
   __shared__ __attribute__((aligned(16))) float sl1[2 * GT_KS];
   __shared__ __attribute__((aligned(16))) float sl2[2 * GT_KS];
@@ -136,41 +144,39 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
     const int rows = min(GT_BM, A.offsets[e + 1] - p0);
     const int c0 = nt * GT_BN;
 
-    // A staging: wave w, instruction i covers rows 4 (8w + i) .. +3
-    uint32_t aoff[8];
+    // A staging: wave w, op i covers rows 8 (4w + i) .. +7 (8 chunks of 16 B each)
+    uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * (w * 8 + i) + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * (w * 4 + i) + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
       aoff[i] = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.lda * 2) + c * 16;
     }
-    // scale staging: wave w: column group (w >> 1), k 64 (w & 1) + lane
+    // int4 staging: wave w, op i covers columns 32 (2w + i) .. +31, 32 bytes each
+    uint32_t boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int col = min(c0 + 32 * (2 * w + i) + (lane >> 1), N - 1);
+      boff[i] = (uint32_t)col * 32 + 16 * (lane & 1);
+    }
+    // scale staging: wave w, lanes < 32: column group (w >> 1), k 32 (w & 1) + lane
     const int sg = min(c0 / 128 + (w >> 1), G - 1);
-    const int sk = 64 * (w & 1) + lane;
-    // int4 words: this wave's 128 columns, words 4 lg .. 4 lg + 3 of each step
-    const int cb = c0 + 128 * wn + lr;
-    auto stage = [&](int jr, bf16_t *abuf, float *sbuf) {
-      const int j = min(jr, NK - 1);
+    const int sk = 32 * (w & 1) + lane;
+    auto stage = [&](int jr, bf16_t *abuf, uint8_t *bbuf, float *sbuf) {
+      const int j = min(jr, NK - 1);   // past the end: a harmless copy of the last step
       const bool second = MODE == 1 && j >= NKh;
       const int kj = second ? j - NKh : j;
-      const char *base = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
+      const char *abase = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
       const uint32_t koff = (uint32_t)kj * GT_KS * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) load_lds16(base + aoff[i] + koff, abuf + (w * 8 + i) * 512);
-      const float *sp = second ? A.st1 : A.st0;
-      load_lds4(sp + ((size_t)e * G + sg) * Kh + kj * GT_KS + sk, sbuf + w * 64);
-    };
-    auto load_b = [&](int jr, uint4 (&b)[8]) {
-      const int j = min(jr, NK - 1);
-      const bool second = MODE == 1 && j >= NKh;
-      const int kj = second ? j - NKh : j;
-      const uint8_t *qp = second ? A.qt1 : A.qt0;
+      for (int i = 0; i < 4; ++i) load_lds16(abase + aoff[i] + koff, abuf + (w * 4 + i) * 512);
+      const uint8_t *qb = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
 #pragma unroll
-      for (int nf = 0; nf < 8; ++nf) {
-        const int c = min(cb + 16 * nf, N - 1);
-        b[nf] = *reinterpret_cast<const uint4 *>(qp + ((size_t)e * N + c) * (Kh / 2) +
-                                                 kj * (GT_KS / 2) + 16 * lg);
-      }
+      for (int i = 0; i < 2; ++i) load_lds16(qb + boff[i], bbuf + (2 * w + i) * 1024);
+      const float *sp = second ? A.st1 : A.st0;
+      if (lane < 32)
+        load_lds4(sp + ((size_t)e * G + sg) * Kh + kj * GT_KS + sk,
+                  sbuf + (w >> 1) * GT_KS + 32 * (w & 1));
     };
 
     f32x4_t acc[4][8], corr[4];
@@ -181,17 +187,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
       for (int nf = 0; nf < 8; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // one 128-deep step: 4 k-substeps x 4 row fragments x (8 + 1) MFMAs.
-    // Lane group lg takes k = 32 lg + 8 s .. + 7 in substep s (A chunk
-    // 4 lg + s, int4 word 4 lg + s), the same permutation on both operands.
-    auto compute = [&](const bf16_t *abuf, const float *sbuf, const uint4 (&b)[8]) {
+    // one 64-deep step: 2 k-substeps x 4 row fragments x (8 + 1) MFMAs.
+    // Lane group lg takes k = 16 lg + 8 s .. + 7 in substep s (A chunk
+    // 2 lg + s, int4 word 2 lg + s), the same permutation on both operands.
+    auto compute = [&](const bf16_t *abuf, const uint8_t *bbuf, const float *sbuf) {
+      __builtin_amdgcn_sched_barrier(0);
+      uint2 bw[8];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int nf = 0; nf < 8; ++nf)
+        bw[nf] = *reinterpret_cast<const uint2 *>(bbuf + (128 * wn + 16 * nf + lr) * 32 + 8 * lg);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
         float sc[8];
         {
-          const float4 s0 = *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 32 * lg + 8 * s);
+          const float4 s0 = *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 16 * lg + 8 * s);
           const float4 s1 =
-              *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 32 * lg + 8 * s + 4);
+              *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 16 * lg + 8 * s + 4);
           sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
           sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
         }
@@ -200,13 +211,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
         for (int m = 0; m < 4; ++m) {
           const int r = 64 * wm + 16 * m + lr;
           const uint4 araw = *reinterpret_cast<const uint4 *>(
-              abuf + r * GT_KS + (((4 * lg + s) ^ (r & 15)) << 3));
+              abuf + r * GT_KS + (((2 * lg + s) ^ (r & 7)) << 3));
           av[m] = scale_frag(araw, sc);
           corr[m] = mfma32(av[m], c136, corr[m]);
         }
 #pragma unroll
         for (int nf = 0; nf < 8; ++nf) {
-          const uint32_t x = s == 0 ? b[nf].x : s == 1 ? b[nf].y : s == 2 ? b[nf].z : b[nf].w;
+          const uint32_t x = s ? bw[nf].y : bw[nf].x;
           uint4 bu;
           bu.x = __builtin_amdgcn_bitop3_b32(x, kMask, kMagic, 0x6A);
           bu.y = __builtin_amdgcn_bitop3_b32(x >> 4, kMask, kMagic, 0x6A);
@@ -216,45 +227,41 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
           for (int m = 0; m < 4; ++m) acc[m][nf] = mfma32(av[m], bu, acc[m][nf]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     // 3-deep pipeline: step j computes from ring slot j % 3 while the loads
-    // of step j + 2 are in flight.  Per thread and step: 8 word loads, 8 + 1
+    // of steps j + 1 and j + 2 are in flight.  Per thread and step: 4 + 2 + 1
     // LDS-DMA (the same count in every wave), so "step j + 1 has landed" is
-    // vmcnt(17).  The loop runs in groups of three steps; steps past the end
+    // vmcnt(7).  The loop runs in groups of three steps; steps past the end
     // compute nothing (uniform branch) but still issue their loads, clamped to
     // the last real step (cache hits into a slot nobody reads), so that every
-    // wait is the same and the compiler's own wait tracking stays exact.  The
-    // scheduling barriers keep each step's loads ahead of the MFMAs, where
-    // the scheduler would otherwise sink them next to their wait.
-    constexpr int kOps = 17;
-    uint4 b0[8], b1[8], b2[8];
+    // wait is the same and the compiler's own wait tracking stays exact.
+    constexpr int kOps = 7;
     __syncthreads();  // LDS of the previous item is free
-    load_b(0, b0);
-    stage(0, al0, sl0);
-    load_b(1, b1);
-    stage(1, al1, sl1);
+    stage(0, al0, bl0, sl0);
+    stage(1, al1, bl1, sl1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
     block_barrier();
     for (int j = 0; j < NK; j += 3) {
-#define MOE_T_STEP(JJ, CUR_A, CUR_S, CUR_B, NXT_A, NXT_S, NXT_B) \
-  {                                                              \
-    const int jj = (JJ);                                         \
-    load_b(jj + 2, NXT_B);                                       \
-    stage(jj + 2, NXT_A, NXT_S);                                 \
-    __builtin_amdgcn_sched_barrier(0);                           \
-    if (jj < NK) compute(CUR_A, CUR_S, CUR_B);                   \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));                 \
-    block_barrier();                                             \
+#define MOE_T_STEP(JJ, CA, CB, CS, NA, NB, NS)              \
+  {                                                         \
+    const int jj = (JJ);                                    \
+    stage(jj + 2, NA, NB, NS);                              \
+    if (jj < NK) compute(CA, CB, CS);                       \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));            \
+    block_barrier();                                        \
   }
-      MOE_T_STEP(j, al0, sl0, b0, al2, sl2, b2)
-      MOE_T_STEP(j + 1, al1, sl1, b1, al0, sl0, b0)
-      MOE_T_STEP(j + 2, al2, sl2, b2, al1, sl1, b1)
+      MOE_T_STEP(j, al0, bl0, sl0, al2, bl2, sl2)
+      MOE_T_STEP(j + 1, al1, bl1, sl1, al0, bl0, sl0)
+      MOE_T_STEP(j + 2, al2, bl2, sl2, al1, bl1, sl1)
 #undef MOE_T_STEP
     }
     // drain the trailing (clamped) loads before the ring is reused below
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     block_barrier();
+
+    const int cb = c0 + 128 * wn + lr;   // this lane's first output column
 
     // remove the 136 offset of the int4 operand
 #pragma unroll
@@ -356,6 +363,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_t_kernel(const MfmaGemmTA
 
 int mfma_t_tile_rows() { return GT_BM; }
 int mfma_t_tile_cols() { return GT_BN; }
+int mfma_t_blocks_per_cu() { return GT_BPC; }
 
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream) {

@@ -79,6 +79,7 @@ struct MfmaGemmArgs {
   float *rsum_out; int ld_rsum_out;       // mode 0: group sums of H rows
 };
 int mfma_tile_rows();
+int mfma_blocks_per_cu();      // resident blocks per CU the kernel is built for
 void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st);
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t st);
 
@@ -96,6 +97,7 @@ struct MfmaGemmTArgs {
 };
 int mfma_t_tile_rows();
 int mfma_t_tile_cols();
+int mfma_t_blocks_per_cu();   // resident blocks per CU the kernel is built for
 // int4 [E][R][C/2] + scales [E][R][C/128] -> transposed int4 [E][C][R/2] + scales
 // [E][C/128][R] (f32), for experts with rows; R, C multiples of 128
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
