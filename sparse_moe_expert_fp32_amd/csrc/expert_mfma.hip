@@ -41,7 +41,34 @@ namespace moe {
 
 constexpr int GM_BM = 64;    // rows per tile
 constexpr int GM_BPC = 2;    // resident blocks per CU
-constexpr int GM_KG = 128;   // K per staged chunk = quantization group
+constexpr int GM_KG = 128;   // quantization group
+constexpr int GM_KS = 64;    // K per pipeline stage (half a group)
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).  vmcnt_imm(n): at most n vector memory operations
+// (loads, LDS-DMA, stores) of this wave outstanding; kWaitAll: none, and no
+// LDS operation either.
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitAll = 0x0070;
+
+// One pipeline stage in LDS, as a single array (one object per stage keeps
+// the compiler's LDS-DMA wait tracking exact): A rows (64 x 64 bf16, 16-byte
+// chunks XOR-swizzled by row), int4 words (32 bytes per block column), the
+// A row sums of the stage's group, the group scale per block column (bf16 in
+// the low half of a 4-byte slot).
+constexpr int FS_A = 0, FS_B = FS_A + GM_BM * GM_KS * 2, FS_C = FS_B + 256 * GM_KS / 2,
+              FS_S = FS_C + GM_BM * 4, FS_BYTES = FS_S + 256 * 4;
+struct FwdStage {
+  uint4 raw[FS_BYTES / 16];
+  DEV bf16_t *a() { return reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(raw) + FS_A); }
+  DEV uint8_t *b() { return reinterpret_cast<uint8_t *>(raw) + FS_B; }
+  DEV float *c() { return reinterpret_cast<float *>(reinterpret_cast<char *>(raw) + FS_C); }
+  DEV uint32_t *s() { return reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(raw) + FS_S); }
+  DEV const bf16_t *a() const { return reinterpret_cast<const bf16_t *>(reinterpret_cast<const char *>(raw) + FS_A); }
+  DEV const uint8_t *b() const { return reinterpret_cast<const uint8_t *>(raw) + FS_B; }
+  DEV const float *c() const { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(raw) + FS_C); }
+  DEV const uint32_t *s() const { return reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(raw) + FS_S); }
+};
 
 // ---------------------------------------------------------------- row sums --
 // out[row][g] = sum of a[row][g*G .. g*G+G) (bf16 values, float32 sum in k order)
@@ -75,11 +102,15 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 // that one block's memory waits overlap the other's matrix work.
 template <int MODE>
 __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGemmArgs A) {
-  __shared__ __attribute__((aligned(16))) bf16_t a_lds[2][GM_BM * GM_KG];
-  __shared__ __attribute__((aligned(16))) float corr_lds[2][GM_BM];
+  // a 3-deep ring of half-group stages: A rows, int4 words, the A row sums
+  // and the scales of the group.  One object per stage, so that reads of one
+  // stage are not ordered behind the LDS-DMA writes into the others.  After
+  // the K loop the four 8 KB regions r0.a, r1.a, r2.a, r0.b hold the
+  // epilogue tile.
+  __shared__ FwdStage r0, r1, r2;
   __shared__ int tok_lds[GM_BM];
 
-  const int K = A.K, N = A.N, NG = K / GM_KG;
+  const int K = A.K, N = A.N, NG = K / GM_KG, NS = 2 * NG;   // NS: half-group stages
   const int BNO = MODE == 0 ? 128 : 256;   // output columns per item (per matrix)
   const int total = A.ntiles[0] * A.NT;
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
@@ -111,139 +142,205 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     }
     __syncthreads();
 
-    // ---- staging: 64 rows x 16 chunks = 1024 chunks, 4 per thread per group
-    uint32_t src_off[4];
+    // ---- A staging: 64 rows x 8 chunks of 16 B per stage; wave w, op i
+    // covers rows 8 (2w + i) .. +7; chunk c of row r lives at c ^ (r & 7)
+    uint32_t src_off[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * (w * 4 + j) + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
-      src_off[j] = (uint32_t)tok_lds[r] * (uint32_t)(A.lda * 2) + c * 16;
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * (w * 2 + i) + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      src_off[i] = (uint32_t)tok_lds[r] * (uint32_t)(A.lda * 2) + c * 16;
     }
     const char *abase = reinterpret_cast<const char *>(A.a);
-    const float *rs_row = A.rsum + (size_t)tok_lds[tid & (GM_BM - 1)] * A.ld_rsum;
-    float rs_pref = tid < GM_BM ? rs_row[0] : 0.f;
+    // row sums of the group: wave w, lanes < 16 load rows 16 w + lane
+    const float *rs_row = A.rsum + (size_t)tok_lds[16 * w + (lane & 15)] * A.ld_rsum;
 
-    // ---- this wave's columns: 4 fragments of 16
-    int col[4];
-    uint32_t qoff[4], soff[4];
+    // ---- this wave's columns: 4 fragments of 16.  Block column slots: mode 0
+    // gate 0..127 then up 128..255, mode 1 0..255.
+    int col[4], slot[4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      const int c = MODE == 0 ? c0 + w * 32 + (nf & 1) * 16 + lr : c0 + w * 64 + nf * 16 + lr;
-      col[nf] = c;
-      const uint32_t row = (uint32_t)e * N + min(c, N - 1);
-      qoff[nf] = row * (uint32_t)(K / 2) + lg * 16;
-      soff[nf] = row * (uint32_t)NG;
+      col[nf] = MODE == 0 ? c0 + w * 32 + (nf & 1) * 16 + lr : c0 + w * 64 + nf * 16 + lr;
+      slot[nf] = MODE == 0 ? (nf >> 1) * 128 + w * 32 + (nf & 1) * 16 + lr : w * 64 + nf * 16 + lr;
     }
-    const uint8_t *qb0 = A.q0, *qb1 = MODE == 0 ? A.q1 : A.q0;
     const uint16_t *sb0 = A.s0, *sb1 = MODE == 0 ? A.s1 : A.s0;
-
-    auto stage = [&](int g, int buf) {
+    // int4 staging: wave w, op i covers block columns 32 (2w + i) .. +31, 32 B each
+    const uint8_t *qsrc[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        load_lds16(abase + src_off[j] + (size_t)g * GM_KG * 2, &a_lds[buf][(w * 4 + j) * 512]);
-      if (tid < GM_BM) {
-        corr_lds[buf][tid] = -136.f * rs_pref;
-        if (g + 1 < NG) rs_pref = rs_row[g + 1];
-      }
-    };
-    auto load_b = [&](int g, uint4 (&bq)[4], float (&sc)[4]) {
+    for (int i = 0; i < 2; ++i) {
+      const int bc = 32 * (2 * w + i) + (lane >> 1);
+      const bool up = MODE == 0 && bc >= 128;
+      const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
+      qsrc[i] = (up ? A.q1 : A.q0) + ((size_t)e * N + c) * (K / 2) + 16 * (lane & 1);
+    }
+    // scale staging: wave w, lane l -> block column 64 w + l (mode 0: gate
+    // columns first, then up), one bf16 per lane into a 4-byte LDS slot
+    const uint16_t *sptr;
+    {
+      const int bc = 64 * w + lane;
+      const bool up = MODE == 0 && bc >= 128;
+      const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
+      sptr = (up ? sb1 : sb0) + ((size_t)e * N + c) * NG;
+    }
+    // one stage = half a quantization group (64 of K); stages past the end
+    // load a harmless copy of the last one
+    auto stage = [&](int jr, FwdStage &S) {
+      const int j = min(jr, NS - 1), g = j >> 1;
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const uint8_t *qb = nf >= 2 ? qb1 : qb0;
-        const uint16_t *sb = nf >= 2 ? sb1 : sb0;
-        bq[nf] = *reinterpret_cast<const uint4 *>(qb + qoff[nf] + (size_t)g * (GM_KG / 2));
-        sc[nf] = bf2f(sb[soff[nf] + g]);
-      }
+      for (int i = 0; i < 2; ++i)
+        dma16(abase + src_off[i] + (size_t)j * GM_KS * 2, S.a() + (w * 2 + i) * 512);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(qsrc[i] + (size_t)j * (GM_KS / 2), S.b() + (2 * w + i) * 1024);
+      if (lane < 16) dma4(rs_row + g, S.c() + 16 * w);
+      dma2(sptr + g, S.s() + 64 * w);
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][4], P[4][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 bq[4];
-    float sc[4];
-    stage(0, 0);
-    load_b(0, bq, sc);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int g = 0; g < NG; ++g) {
-      const int cur = g & 1;
-      if (g + 1 < NG) stage(g + 1, cur ^ 1);
-      uint4 bu[4][4];
+    // one stage: 2 k-substeps x 4 row fragments x 4 column fragments.  Lane
+    // group lg takes k = 16 lg + 8 s .. + 7 of the stage in substep s (A chunk
+    // 2 lg + s, int4 word 2 lg + s).  The group's partial products P start
+    // at -136 * (row sum of the group) in its first stage and are scaled into
+    // the accumulators after its second.
+    auto compute = [&](int j, const FwdStage &S) {
+      const bf16_t *al = S.a();
+      const uint8_t *bb = S.b();
+      const float *cb = S.c();
+      const uint32_t *sb = S.s();
+      __builtin_amdgcn_sched_barrier(0);
+      if ((j & 1) == 0) {
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const uint32_t wd[4] = {bq[nf].x, bq[nf].y, bq[nf].z, bq[nf].w};
+        for (int m = 0; m < 4; ++m) {
+          const f32x4_t rs = *reinterpret_cast<const f32x4_t *>(&cb[16 * m + 4 * lg]);
+          const f32x4_t ci = -136.f * rs;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t x = wd[s];
-          bu[s][nf].x = __builtin_amdgcn_bitop3_b32(x, kMask, kMagic, 0x6A);
-          bu[s][nf].y = __builtin_amdgcn_bitop3_b32(x >> 4, kMask, kMagic, 0x6A);
-          bu[s][nf].z = __builtin_amdgcn_bitop3_b32(x >> 8, kMask, kMagic, 0x6A);
-          bu[s][nf].w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
+          for (int nf = 0; nf < 4; ++nf) P[m][nf] = ci;
         }
       }
-      float scg[4];
+      uint2 bq[4];
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) scg[nf] = sc[nf];
-      if (g + 1 < NG) load_b(g + 1, bq, sc);   // registers of the unpacked words are free
-      const bf16_t *al = a_lds[cur];
+      for (int nf = 0; nf < 4; ++nf)
+        bq[nf] = *reinterpret_cast<const uint2 *>(bb + slot[nf] * 32 + 8 * lg);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4_t ci = *reinterpret_cast<const f32x4_t *>(&corr_lds[cur][16 * m + 4 * lg]);
-        f32x4_t P[4];
+      for (int s = 0; s < 2; ++s) {
+        uint4 bu[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int nf = 0; nf < 4; ++nf) {
+          const uint32_t x = s ? bq[nf].y : bq[nf].x;
+          bu[nf].x = __builtin_amdgcn_bitop3_b32(x, kMask, kMagic, 0x6A);
+          bu[nf].y = __builtin_amdgcn_bitop3_b32(x >> 4, kMask, kMagic, 0x6A);
+          bu[nf].z = __builtin_amdgcn_bitop3_b32(x >> 8, kMask, kMagic, 0x6A);
+          bu[nf].w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = 16 * m + lr;
           const uint4 av = *reinterpret_cast<const uint4 *>(
-              al + (16 * m + lr) * GM_KG + (((lg * 4 + s) ^ lr) << 3));
+              al + r * GM_KS + (((2 * lg + s) ^ (r & 7)) << 3));
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) P[nf] = mfma32(av, bu[s][nf], s == 0 ? ci : P[nf]);
+          for (int nf = 0; nf < 4; ++nf) P[m][nf] = mfma32(av, bu[nf], P[m][nf]);
         }
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) acc[m][nf] += scg[nf] * P[nf];
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      if (j & 1) {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          const float scg = __uint_as_float(sb[slot[nf]] << 16);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[m][nf] += scg * P[m][nf];
+        }
+      }
+    };
+
+    // 3-deep pipeline: stage j computes from ring slot j % 3 while the loads
+    // of stages j + 1 and j + 2 are in flight.  Per thread and stage: 2 + 2 +
+    // 1 + 1 LDS-DMA (the same count in every wave), so "stage j + 1 has
+    // landed" is vmcnt(6).  The loop runs in groups of three stages; stages
+    // past the end compute nothing (uniform branch) but still issue their
+    // (clamped) loads, so every wait is alike.
+    constexpr int kOps = 6;
+    stage(0, r0);
+    stage(1, r1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
+    block_barrier();
+    for (int j = 0; j < NS; j += 3) {
+#define MOE_F_STEP(JJ, CUR, NXT)                 \
+  {                                              \
+    const int jj = (JJ);                         \
+    stage(jj + 2, NXT);                          \
+    if (jj < NS) compute(jj, CUR);               \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps)); \
+    block_barrier();                             \
+  }
+      MOE_F_STEP(j, r0, r2)
+      MOE_F_STEP(j + 1, r1, r0)
+      MOE_F_STEP(j + 2, r2, r1)
+#undef MOE_F_STEP
     }
 
-    // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16
+    // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16.  All
+    // loads are unconditional (clamped indices) so that they issue together;
+    // rank columns beyond r are zeroed afterwards.
+    constexpr int NSRC = MODE == 0 ? 2 : 1;
     for (int j0 = 0; j0 < A.r; j0 += 16) {
+      float zv[NSRC][4][4];
+      uint16_t bl[4][4];
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const uint16_t *Bm = MODE == 0 && nf >= 2 ? A.B1 : A.B0;
-        const int cc = min(col[nf], N - 1);
-        short4_t bv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 4 * lg + i;
-          bv[i] = j < A.r ? (short)Bm[((size_t)e * N + cc) * A.r + j] : (short)0;
-        }
-        const float *Zp = MODE == 0 && nf >= 2 ? A.Z1 : A.Z0;
+      for (int src = 0; src < NSRC; ++src) {
+        const float *Zp = src ? A.Z1 : A.Z0;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int p = p0 + min(16 * m + lr, rows - 1);
-          short4_t av;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 4 * lg + i;
-            av[i] = j < A.r ? (short)f2bf(A.lam * Zp[(size_t)p * A.ldz + j]) : (short)0;
-          }
-          acc[m][nf] = mfma16(av, bv, acc[m][nf]);
+          for (int i = 0; i < 4; ++i) zv[src][m][i] = Zp[(size_t)p * A.ldz + min(j0 + 4 * lg + i, A.r - 1)];
         }
+      }
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const uint16_t *Bm = MODE == 0 && nf >= 2 ? A.B1 : A.B0;
+        const size_t rowb = ((size_t)e * N + min(col[nf], N - 1)) * A.r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bl[nf][i] = Bm[rowb + min(j0 + 4 * lg + i, A.r - 1)];
+      }
+      short4_t av[NSRC][4];
+#pragma unroll
+      for (int src = 0; src < NSRC; ++src)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            av[src][m][i] = j0 + 4 * lg + i < A.r ? (short)f2bf(A.lam * zv[src][m][i]) : (short)0;
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        short4_t bv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[i] = j0 + 4 * lg + i < A.r ? (short)bl[nf][i] : (short)0;
+        const int src = MODE == 0 && nf >= 2 ? 1 : 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m][nf] = mfma16(av[src][m], bv, acc[m][nf]);
       }
     }
 
-    // ---- epilogue through LDS (16-byte chunks XOR-swizzled per row) so that
-    // every global store is a full 16-byte vector
-    __syncthreads();  // all waves are done reading a_lds
-    bf16_t *t0 = a_lds[0], *t1 = a_lds[1];
-    auto tidx = [](int r, int c, int RW) {
-      return r * RW + ((((c >> 3) ^ (r & 15))) << 3) + (c & 7);
+    // ---- epilogue through LDS so that every global store is a full 16-byte
+    // vector.  The tile (64 rows x 256 columns) lives in the ring arrays r0.a,
+    // r1.a, r2.a, r0.b, 64 columns each, 16-byte chunks XOR-swizzled by row.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);   // trailing (clamped) stage loads
+    __syncthreads();                        // every wave is done with the ring
+    auto quad = [&](int q) -> bf16_t * {
+      return q == 0 ? r0.a() : q == 1 ? r1.a() : q == 2 ? r2.a() : reinterpret_cast<bf16_t *>(r0.b());
+    };
+    auto tel = [&](int r, int c) -> bf16_t & {   // element (r, c), c < 256
+      return quad(c >> 6)[r * 64 + ((((c >> 3) & 7) ^ (r & 7)) << 3) + (c & 7)];
+    };
+    auto tch = [&](int r, int ch) -> uint4 & {   // 16-byte chunk ch (8 columns), ch < 32
+      return *reinterpret_cast<uint4 *>(quad(ch >> 3) + r * 64 + (((ch & 7) ^ (r & 7)) << 3));
     };
     if (MODE == 0) {
-      // H -> t0, G -> t1 (64 x 128 each); then U -> t0
+      // H -> columns 0..127, G -> columns 128..255; then U -> columns 0..127
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -253,8 +350,8 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
           for (int nf = 0; nf < 2; ++nf) {
             const int c = w * 32 + nf * 16 + lr;
             const float gv = acc[m][nf][i], uv = acc[m][nf + 2][i];
-            t0[tidx(r, c, 128)] = f2bf(silu_f(gv) * uv);
-            t1[tidx(r, c, 128)] = f2bf(gv);
+            tel(r, c) = f2bf(silu_f(gv) * uv);
+            tel(r, 128 + c) = f2bf(gv);
           }
         }
       __syncthreads();
@@ -262,8 +359,7 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int idx = it * 256 + tid, r = idx >> 4, ch = idx & 15;
-        const int li = r * 128 + ((ch ^ (r & 15)) << 3);
-        const uint4 hv = *reinterpret_cast<const uint4 *>(&t0[li]);
+        const uint4 hv = tch(r, ch);
         const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
         float v = 0.f;
 #pragma unroll
@@ -274,7 +370,7 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
         if (ok) {
           const size_t o = (size_t)(p0 + r) * A.ldo + c;
           *reinterpret_cast<uint4 *>(&A.out[o]) = hv;
-          if (A.saveG) *reinterpret_cast<uint4 *>(&A.saveG[o]) = *reinterpret_cast<const uint4 *>(&t1[li]);
+          if (A.saveG) *reinterpret_cast<uint4 *>(&A.saveG[o]) = tch(r, 16 + ch);
         }
         v = ok ? v : 0.f;
         v += __shfl_xor(v, 1);
@@ -292,8 +388,7 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * m + 4 * lg + i;
 #pragma unroll
-            for (int nf = 0; nf < 2; ++nf)
-              t0[tidx(r, w * 32 + nf * 16 + lr, 128)] = f2bf(acc[m][nf + 2][i]);
+            for (int nf = 0; nf < 2; ++nf) tel(r, w * 32 + nf * 16 + lr) = f2bf(acc[m][nf + 2][i]);
           }
         __syncthreads();
 #pragma unroll
@@ -301,20 +396,17 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
           const int idx = it * 256 + tid, r = idx >> 4, ch = idx & 15;
           const int c = c0 + ch * 8;
           if (r < rows && c < N)
-            *reinterpret_cast<uint4 *>(&A.saveU[(size_t)(p0 + r) * A.ldo + c]) =
-                *reinterpret_cast<const uint4 *>(&t0[r * 128 + ((ch ^ (r & 15)) << 3)]);
+            *reinterpret_cast<uint4 *>(&A.saveU[(size_t)(p0 + r) * A.ldo + c]) = tch(r, ch);
         }
       }
     } else {
-      // 64 x 256 tile over both buffers (contiguous)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * m + 4 * lg + i;
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-            t0[tidx(r, w * 64 + nf * 16 + lr, 256)] = f2bf(acc[m][nf][i]);
+          for (int nf = 0; nf < 4; ++nf) tel(r, w * 64 + nf * 16 + lr) = f2bf(acc[m][nf][i]);
         }
       __syncthreads();
 #pragma unroll
@@ -322,8 +414,7 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
         const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31;
         const int c = c0 + ch * 8;
         if (r < rows && c < N)
-          *reinterpret_cast<uint4 *>(&A.out[(size_t)(p0 + r) * A.ldo + c]) =
-              *reinterpret_cast<const uint4 *>(&t0[r * 256 + ((ch ^ (r & 15)) << 3)]);
+          *reinterpret_cast<uint4 *>(&A.out[(size_t)(p0 + r) * A.ldo + c]) = tch(r, ch);
       }
     }
   }

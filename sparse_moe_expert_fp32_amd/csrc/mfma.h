@@ -62,6 +62,37 @@ DEV void load_lds4(const void *gsrc, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
 }
 
+// 2 bytes per lane straight into LDS, zero-extended into a 4-byte slot: lane i
+// writes lds_wave_base + 4 i (only the active lanes write).
+DEV void load_lds2(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 2, 0, 0);
+}
+
+// The same three transfers issued from inline asm.  The compiler then does
+// not know that they write LDS, so it adds none of its own waits before LDS
+// reads (its tracking of LDS-DMA is conservative across loop back-edges and
+// would drain a deep prefetch); callers wait explicitly (s_waitcnt vmcnt)
+// and synchronise before reading what these wrote.  They read their address
+// operands at issue and write no registers.
+DEV uint32_t lds_addr(void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)p);
+}
+DEV void dma16(const void *gsrc, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc),
+               "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
+}
+DEV void dma4(const void *gsrc, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc),
+               "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
+}
+DEV void dma2(const void *gsrc, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(gsrc),
+               "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would make the compiler drain every outstanding load, including LDS-DMA
 // that is deliberately left in flight.  Callers wait (s_waitcnt) for the
