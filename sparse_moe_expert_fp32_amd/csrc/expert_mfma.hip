@@ -153,7 +153,6 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     }
     const char *abase = reinterpret_cast<const char *>(A.a);
     // row sums of the group: wave w, lanes < 16 load rows 16 w + lane
-    const float *rs_row = A.rsum + (size_t)tok_lds[16 * w + (lane & 15)] * A.ld_rsum;
 
     // ---- this wave's columns: 4 fragments of 16.  Block column slots: mode 0
     // gate 0..127 then up 128..255, mode 1 0..255.
@@ -164,36 +163,41 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
       slot[nf] = MODE == 0 ? (nf >> 1) * 128 + w * 32 + (nf & 1) * 16 + lr : w * 64 + nf * 16 + lr;
     }
     const uint16_t *sb0 = A.s0, *sb1 = MODE == 0 ? A.s1 : A.s0;
-    // int4 staging: wave w, op i covers block columns 32 (2w + i) .. +31, 32 B each
-    const uint8_t *qsrc[2];
+    // int4 staging: wave w, op i covers block columns 32 (2w + i) .. +31, 32 B
+    // each (all gate or all up within one op)
+    const uint8_t *qbase[2];
+    uint32_t qoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int bc = 32 * (2 * w + i) + (lane >> 1);
       const bool up = MODE == 0 && bc >= 128;
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      qsrc[i] = (up ? A.q1 : A.q0) + ((size_t)e * N + c) * (K / 2) + 16 * (lane & 1);
+      qbase[i] = (up ? A.q1 : A.q0) + (size_t)e * N * (K / 2);
+      qoff[i] = (uint32_t)c * (uint32_t)(K / 2) + 16 * (lane & 1);
     }
     // scale staging: wave w, lane l -> block column 64 w + l (mode 0: gate
     // columns first, then up), one bf16 per lane into a 4-byte LDS slot
-    const uint16_t *sptr;
+    const uint16_t *sbase;
+    uint32_t soff;
     {
       const int bc = 64 * w + lane;
       const bool up = MODE == 0 && bc >= 128;
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      sptr = (up ? sb1 : sb0) + ((size_t)e * N + c) * NG;
+      sbase = (up ? sb1 : sb0) + (size_t)e * N * NG;
+      soff = (uint32_t)c * (uint32_t)NG * 2u;
     }
+    const uint32_t rsoff = (uint32_t)tok_lds[16 * w + (lane & 15)] * (uint32_t)A.ld_rsum * 4u;
     // one stage = half a quantization group (64 of K); stages past the end
     // load a harmless copy of the last one
     auto stage = [&](int jr, FwdStage &S) {
       const int j = min(jr, NS - 1), g = j >> 1;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        dma16(abase + src_off[i] + (size_t)j * GM_KS * 2, S.a() + (w * 2 + i) * 512);
+        dma16(abase + (size_t)j * GM_KS * 2, src_off[i], S.a() + (w * 2 + i) * 512);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma16(qsrc[i] + (size_t)j * (GM_KS / 2), S.b() + (2 * w + i) * 1024);
-      if (lane < 16) dma4(rs_row + g, S.c() + 16 * w);
-      dma2(sptr + g, S.s() + 64 * w);
+      for (int i = 0; i < 2; ++i) dma16(qbase[i] + (size_t)j * (GM_KS / 2), qoff[i], S.b() + (2 * w + i) * 1024);
+      if (lane < 16) dma4(A.rsum + g, rsoff, S.c() + 16 * w);
+      dma2(sbase + g, soff, S.s() + 64 * w);
     };
 
     f32x4_t acc[4][4], P[4][4];

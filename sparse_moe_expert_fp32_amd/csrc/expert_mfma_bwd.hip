@@ -105,9 +105,8 @@ constexpr int kWaitAll = 0x0070;
 
 template <int MODE>
 __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
-  // a 3-deep ring of stages, each with its A rows, int4 words and scales;
-  // distinct arrays, so that reads of one stage are not ordered behind the
-  // LDS-DMA writes into the others
+  // a 3-deep ring of stages, each with its A rows, int4 words and scales
+  // (filled by LDS-DMA issued from inline asm, with explicit waits)
   __shared__ __attribute__((aligned(16))) bf16_t al0[GT_BM * GT_KS];
   __shared__ __attribute__((aligned(16))) bf16_t al1[GT_BM * GT_KS];
   __shared__ __attribute__((aligned(16))) bf16_t al2[GT_BM * GT_KS];
@@ -169,14 +168,13 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
       const char *abase = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
       const uint32_t koff = (uint32_t)kj * GT_KS * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load_lds16(abase + aoff[i] + koff, abuf + (w * 4 + i) * 512);
+      for (int i = 0; i < 4; ++i) dma16(abase + koff, aoff[i], abuf + (w * 4 + i) * 512);
       const uint8_t *qb = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) load_lds16(qb + boff[i], bbuf + (2 * w + i) * 1024);
-      const float *sp = second ? A.st1 : A.st0;
+      for (int i = 0; i < 2; ++i) dma16(qb, boff[i], bbuf + (2 * w + i) * 1024);
+      const float *sp = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
       if (lane < 32)
-        load_lds4(sp + ((size_t)e * G + sg) * Kh + kj * GT_KS + sk,
-                  sbuf + (w >> 1) * GT_KS + 32 * (w & 1));
+        dma4(sp, (uint32_t)(sg * Kh + sk) * 4u, sbuf + (w >> 1) * GT_KS + 32 * (w & 1));
     };
 
     f32x4_t acc[4][8], corr[4];

@@ -68,29 +68,37 @@ DEV void load_lds2(const void *gsrc, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 2, 0, 0);
 }
 
-// The same three transfers issued from inline asm.  The compiler then does
-// not know that they write LDS, so it adds none of its own waits before LDS
-// reads (its tracking of LDS-DMA is conservative across loop back-edges and
-// would drain a deep prefetch); callers wait explicitly (s_waitcnt vmcnt)
-// and synchronise before reading what these wrote.  They read their address
-// operands at issue and write no registers.
+// The same transfers issued from inline asm, addressed as a wave-uniform
+// 64-bit base (SGPRs) plus a 32-bit per-lane byte offset.  The compiler then
+// does not know that they write LDS, so it adds none of its own waits before
+// LDS reads (its tracking of LDS-DMA is conservative across loop back-edges
+// and would drain a deep prefetch); callers wait explicitly (s_waitcnt
+// vmcnt) and synchronise before reading what these wrote.  They read their
+// operands at issue and write no registers.  The base must be the same in
+// every lane of the wave (it is made so with readfirstlane).
 DEV uint32_t lds_addr(void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)p);
 }
-DEV void dma16(const void *gsrc, void *lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc),
-               "s"(lds_addr(lds_wave_base))
-               : "memory", "m0");
+DEV const void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-DEV void dma4(const void *gsrc, void *lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc),
-               "s"(lds_addr(lds_wave_base))
-               : "memory", "m0");
+DEV void dma16(const void *sbase, uint32_t voff, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(uniform_ptr(sbase)), "s"(lds_addr(lds_wave_base))
+               : "memory");
 }
-DEV void dma2(const void *gsrc, void *lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(gsrc),
-               "s"(lds_addr(lds_wave_base))
-               : "memory", "m0");
+DEV void dma4(const void *sbase, uint32_t voff, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
+               "s"(uniform_ptr(sbase)), "s"(lds_addr(lds_wave_base))
+               : "memory");
+}
+DEV void dma2(const void *sbase, uint32_t voff, void *lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff),
+               "s"(uniform_ptr(sbase)), "s"(lds_addr(lds_wave_base))
+               : "memory");
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
