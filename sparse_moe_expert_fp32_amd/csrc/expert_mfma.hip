@@ -33,6 +33,8 @@
 //    the same accumulator; gate/up applies SwiGLU in registers (a lane holds
 //    the matching gate and up columns), writes H (bf16) and, for the down
 //    product's offset correction, the row sums of H per group.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
       const int bc = 32 * (2 * w + i) + (lane >> 1);
       const bool up = MODE == 0 && bc >= 128;
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      qbase[i] = (up ? A.q1 : A.q0) + (size_t)e * N * (K / 2);
+      qbase[i] = (const uint8_t *)uniform_ptr((up ? A.q1 : A.q0) + (size_t)e * N * (K / 2));
       qoff[i] = (uint32_t)c * (uint32_t)(K / 2) + 16 * (lane & 1);
     }
     // scale staging: wave w, lane l -> block column 64 w + l (mode 0: gate
@@ -183,21 +185,26 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
       const int bc = 64 * w + lane;
       const bool up = MODE == 0 && bc >= 128;
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      sbase = (up ? sb1 : sb0) + (size_t)e * N * NG;
+      sbase = (const uint16_t *)uniform_ptr((up ? sb1 : sb0) + (size_t)e * N * NG);
       soff = (uint32_t)c * (uint32_t)NG * 2u;
     }
     const uint32_t rsoff = (uint32_t)tok_lds[16 * w + (lane & 15)] * (uint32_t)A.ld_rsum * 4u;
     // one stage = half a quantization group (64 of K); stages past the end
     // load a harmless copy of the last one
+    // this wave's LDS destinations within a stage (wave-uniform byte offsets)
+    const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t la = FS_A + wu * 2 * 1024, lb = FS_B + wu * 2 * 1024, lc = FS_C + wu * 64,
+                   ls = FS_S + wu * 256;
     auto stage = [&](int jr, FwdStage &S) {
       const int j = min(jr, NS - 1), g = j >> 1;
+      const uint32_t base = lds_addr(S.raw);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(abase + (size_t)j * GM_KS * 2, src_off[i], base + la + i * 1024);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        dma16(abase + (size_t)j * GM_KS * 2, src_off[i], S.a() + (w * 2 + i) * 512);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(qbase[i] + (size_t)j * (GM_KS / 2), qoff[i], S.b() + (2 * w + i) * 1024);
-      if (lane < 16) dma4(A.rsum + g, rsoff, S.c() + 16 * w);
-      dma2(sbase + g, soff, S.s() + 64 * w);
+        dma16(qbase[i] + (size_t)j * (GM_KS / 2), qoff[i], base + lb + i * 1024);
+      if (lane < 16) dma4(A.rsum + g, rsoff, base + lc);
+      dma2(sbase + g, soff, base + ls);
     };
 
     f32x4_t acc[4][4], P[4][4];
@@ -211,21 +218,17 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     // 2 lg + s, int4 word 2 lg + s).  The group's partial products P start
     // at -136 * (row sum of the group) in its first stage and are scaled into
     // the accumulators after its second.
-    auto compute = [&](int j, const FwdStage &S) {
+    auto compute = [&](auto odd, const FwdStage &S) {   // odd: compile-time stage parity
       const bf16_t *al = S.a();
       const uint8_t *bb = S.b();
       const float *cb = S.c();
       const uint32_t *sb = S.s();
       __builtin_amdgcn_sched_barrier(0);
-      if ((j & 1) == 0) {
+      // first stage of a group: its partial products start at -136 * (row sum)
+      f32x4_t ci[4];
+      constexpr bool first = !decltype(odd)::value;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4_t rs = *reinterpret_cast<const f32x4_t *>(&cb[16 * m + 4 * lg]);
-          const f32x4_t ci = -136.f * rs;
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf) P[m][nf] = ci;
-        }
-      }
+      for (int m = 0; m < 4; ++m) ci[m] = -136.f * *reinterpret_cast<const f32x4_t *>(&cb[16 * m + 4 * lg]);
       uint2 bq[4];
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
@@ -247,10 +250,11 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
           const uint4 av = *reinterpret_cast<const uint4 *>(
               al + r * GM_KS + (((2 * lg + s) ^ (r & 7)) << 3));
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) P[m][nf] = mfma32(av, bu[nf], P[m][nf]);
+          for (int nf = 0; nf < 4; ++nf)
+            P[m][nf] = mfma32(av, bu[nf], (s == 0 && first) ? ci[m] : P[m][nf]);
         }
       }
-      if (j & 1) {
+      if (decltype(odd)::value) {
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) {
           const float scg = __uint_as_float(sb[slot[nf]] << 16);
@@ -263,26 +267,31 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     // 3-deep pipeline: stage j computes from ring slot j % 3 while the loads
     // of stages j + 1 and j + 2 are in flight.  Per thread and stage: 2 + 2 +
     // 1 + 1 LDS-DMA (the same count in every wave), so "stage j + 1 has
-    // landed" is vmcnt(6).  The loop runs in groups of three stages; stages
-    // past the end compute nothing (uniform branch) but still issue their
-    // (clamped) loads, so every wait is alike.
+    // landed" is vmcnt(6).  The loop runs in groups of six stages (three ring
+    // slots, two parities); stages past the end compute nothing (uniform
+    // branch) but still issue their (clamped) loads, so every wait is alike.
     constexpr int kOps = 6;
+    using even_t = std::integral_constant<bool, false>;
+    using odd_t = std::integral_constant<bool, true>;
     stage(0, r0);
     stage(1, r1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
     block_barrier();
-    for (int j = 0; j < NS; j += 3) {
-#define MOE_F_STEP(JJ, CUR, NXT)                 \
+    for (int j = 0; j < NS; j += 6) {
+#define MOE_F_STEP(JJ, PAR, CUR, NXT)            \
   {                                              \
     const int jj = (JJ);                         \
     stage(jj + 2, NXT);                          \
-    if (jj < NS) compute(jj, CUR);               \
+    if (jj < NS) compute(PAR(), CUR);            \
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps)); \
     block_barrier();                             \
   }
-      MOE_F_STEP(j, r0, r2)
-      MOE_F_STEP(j + 1, r1, r0)
-      MOE_F_STEP(j + 2, r2, r1)
+      MOE_F_STEP(j, even_t, r0, r2)
+      MOE_F_STEP(j + 1, odd_t, r1, r0)
+      MOE_F_STEP(j + 2, even_t, r2, r1)
+      MOE_F_STEP(j + 3, odd_t, r0, r2)
+      MOE_F_STEP(j + 4, even_t, r1, r0)
+      MOE_F_STEP(j + 5, odd_t, r2, r1)
 #undef MOE_F_STEP
     }
 

@@ -161,6 +161,11 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
     // scale staging: wave w, lanes < 32: column group (w >> 1), k 32 (w & 1) + lane
     const int sg = min(c0 / 128 + (w >> 1), G - 1);
     const int sk = 32 * (w & 1) + lane;
+    // this wave's LDS destinations within a stage (wave-uniform byte offsets)
+    const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t la = wu * 4 * 1024, lb = wu * 2 * 1024,
+                   ls = ((wu >> 1) * GT_KS + 32 * (wu & 1)) * 4;
+    const uint32_t soff = (uint32_t)(sg * Kh + sk) * 4u;
     auto stage = [&](int jr, bf16_t *abuf, uint8_t *bbuf, float *sbuf) {
       const int j = min(jr, NK - 1);   // past the end: a harmless copy of the last step
       const bool second = MODE == 1 && j >= NKh;
@@ -168,13 +173,12 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
       const char *abase = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
       const uint32_t koff = (uint32_t)kj * GT_KS * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(abase + koff, aoff[i], abuf + (w * 4 + i) * 512);
+      for (int i = 0; i < 4; ++i) dma16(abase + koff, aoff[i], lds_addr(abuf) + la + i * 1024);
       const uint8_t *qb = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(qb, boff[i], bbuf + (2 * w + i) * 1024);
+      for (int i = 0; i < 2; ++i) dma16(qb, boff[i], lds_addr(bbuf) + lb + i * 1024);
       const float *sp = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
-      if (lane < 32)
-        dma4(sp, (uint32_t)(sg * Kh + sk) * 4u, sbuf + (w >> 1) * GT_KS + 32 * (w & 1));
+      if (lane < 32) dma4(sp, soff, lds_addr(sbuf) + ls);
     };
 
     f32x4_t acc[4][8], corr[4];

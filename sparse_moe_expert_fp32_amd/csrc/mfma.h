@@ -75,9 +75,10 @@ DEV void load_lds2(const void *gsrc, void *lds_wave_base) {
 // and would drain a deep prefetch); callers wait explicitly (s_waitcnt
 // vmcnt) and synchronise before reading what these wrote.  They read their
 // operands at issue and write no registers.  The base must be the same in
-// every lane of the wave (it is made so with readfirstlane).
-DEV uint32_t lds_addr(void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)p);
+// every lane of the wave: values derived from lane-dependent ones go through
+// uniform_ptr (readfirstlane) first.
+DEV uint32_t lds_addr(const void *p) {   // 32-bit LDS byte address of a __shared__ pointer
+  return (uint32_t)(uintptr_t)(const lds_void *)p;
 }
 DEV const void *uniform_ptr(const void *p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
@@ -85,19 +86,17 @@ DEV const void *uniform_ptr(const void *p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-DEV void dma16(const void *sbase, uint32_t voff, void *lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(uniform_ptr(sbase)), "s"(lds_addr(lds_wave_base))
+// lds: wave-uniform LDS byte address where lane i's data lands (+ size * i)
+DEV void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory");
 }
-DEV void dma4(const void *sbase, uint32_t voff, void *lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
-               "s"(uniform_ptr(sbase)), "s"(lds_addr(lds_wave_base))
+DEV void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory");
 }
-DEV void dma2(const void *sbase, uint32_t voff, void *lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff),
-               "s"(uniform_ptr(sbase)), "s"(lds_addr(lds_wave_base))
+DEV void dma2(const void *sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory");
 }
 
