@@ -41,11 +41,10 @@ constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 64, GT_BPC = 2;   // GT_BPC: blo
 // q: [E][R][C/2] (packed along C), s: [E][R][C/128] bf16  ->
 // qt: [E][R/64][C][32 bytes] (each column's run of 64 storage rows as 8 words,
 //     same in-word order as the forward operand), st: [E][C/128][R] f32.
-// Experts without rows are skipped.  Block: 128 storage rows x 128 columns;
-// each thread transposes one 8 x 8 nibble block in registers (8 words read
-// from 8 rows -> 8 words of 8 columns), then the words are re-laid out
-// through LDS so that each 64-row block of a column tile is one contiguous
-// 4 KB run.
+// Experts without rows are skipped.  Block: 64 storage rows x 256 columns, so
+// every row is read as one 128-byte run and every output block is one 8 KB
+// run; each thread transposes one 8 x 8 nibble block in registers (8 words
+// read from 8 rows -> 8 words of 8 columns), re-laid out through LDS.
 DEV int nib_slot(int j) { return (j >> 1) + ((j & 1) << 2); }   // slot of element j
 
 __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restrict__ q,
@@ -53,35 +52,40 @@ __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restr
                                                           const int32_t *__restrict__ offsets,
                                                           int R, int C, uint8_t *__restrict__ qt,
                                                           float *__restrict__ st) {
-  __shared__ uint32_t lw[128][17];   // [column][row block of 8], padded
+  __shared__ uint32_t lw[256][9];   // [column][row octet], padded
   const int e = blockIdx.z;
   if (offsets[e + 1] == offsets[e]) return;
-  const int n0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
-  const int tid = threadIdx.x, wq = tid & 15, a = tid >> 4;
-  uint32_t in[8];
+  const int n0 = blockIdx.y * 64, c0 = blockIdx.x * 256;
+  const int tid = threadIdx.x, cg = tid & 31, a = tid >> 5;   // 8-column group, row octet
+  const bool ok = c0 + 8 * cg < C;                           // C is a multiple of 128
+  if (ok) {
+    uint32_t in[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    in[i] = reinterpret_cast<const uint32_t *>(q + ((size_t)e * R + n0 + 8 * a + i) * (C / 2) +
-                                               c0 / 2)[wq];
+    for (int i = 0; i < 8; ++i)
+      in[i] = reinterpret_cast<const uint32_t *>(q + ((size_t)e * R + n0 + 8 * a + i) * (C / 2) +
+                                                 c0 / 2)[cg];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t o = 0;
+    for (int j = 0; j < 8; ++j) {
+      uint32_t o = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o |= ((in[i] >> (4 * nib_slot(j))) & 15u) << (4 * nib_slot(i));
-    lw[8 * wq + j][a] = o;
+      for (int i = 0; i < 8; ++i) o |= ((in[i] >> (4 * nib_slot(j))) & 15u) << (4 * nib_slot(i));
+      lw[8 * cg + j][a] = o;
+    }
   }
   if (tid < 128) {
-    const int G = C / 128, g = c0 >> 7;
-    st[((size_t)e * G + g) * R + n0 + tid] = bf2f(s[((size_t)e * R + n0 + tid) * G + g]);
+    const int G = C / 128, g = (c0 >> 7) + (tid >> 6), n = n0 + (tid & 63);
+    if (g < G) st[((size_t)e * G + g) * R + n] = bf2f(s[((size_t)e * R + n) * G + g]);
   }
   __syncthreads();
+  // 256 columns x 32 bytes, contiguous in the output block: 2 x 16 bytes per thread
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int idx = tid * 2 + h, c = idx >> 2, q4 = idx & 3;
+    const int idx = tid * 2 + h, c = idx >> 1, q2 = idx & 1;
+    if (c0 + c >= C) continue;
     uint4 v;
-    v.x = lw[c][4 * q4]; v.y = lw[c][4 * q4 + 1]; v.z = lw[c][4 * q4 + 2]; v.w = lw[c][4 * q4 + 3];
-    const size_t blk = (size_t)e * (R / 64) + n0 / 64 + (q4 >> 1);
-    *reinterpret_cast<uint4 *>(qt + (blk * C + c0 + c) * 32 + 16 * (q4 & 1)) = v;
+    v.x = lw[c][4 * q2]; v.y = lw[c][4 * q2 + 1]; v.z = lw[c][4 * q2 + 2]; v.w = lw[c][4 * q2 + 3];
+    const size_t blk = (size_t)e * (R / 64) + n0 / 64;
+    *reinterpret_cast<uint4 *>(qt + (blk * C + c0 + c) * 32 + 16 * q2) = v;
   }
 }
 
@@ -369,7 +373,7 @@ int mfma_t_blocks_per_cu() { return GT_BPC; }
 
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream) {
-  dim3 grid(C / 128, R / 128, E);
+  dim3 grid((C + 255) / 256, R / 64, E);
   transpose_q_kernel<<<grid, 256, 0, stream>>>(q, s, offsets, R, C, qt, st);
 }
 

@@ -239,42 +239,44 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const WgradMArgs G) {
 }
 
 // Experts spread over several tiles: sum their partials in tile order.
-// Experts without rows (no tiles at all) get zeros here.
+// Experts without rows (no tiles at all) get zeros here.  Each thread handles
+// WR_PER consecutive outputs, so the grid stays small.
+constexpr int WR_PER = 1;
+
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const WgradMArgs G) {
   __shared__ int red[256];
   const int e = blockIdx.y, tid = threadIdx.x;
   const int count = G.offsets[e + 1] - G.offsets[e];
-  if (count == 0) {
-    const size_t per = (size_t)G.wide * G.r;
-    const size_t idx = (size_t)blockIdx.x * 256 + tid;
+  if (count > 0 && count <= WG_TILE) return;   // written directly by its single tile
+  const size_t per = (size_t)G.wide * G.r;
+  const size_t i0 = ((size_t)blockIdx.x * 256 + tid) * WR_PER;
+  int t0 = 0, nt = 0;
+  if (count > 0) {
+    // index of the expert's first tile: tiles are listed expert by expert
+    int c = 0;
+    for (int x = tid; x < e; x += 256)
+      c += (G.offsets[x + 1] - G.offsets[x] + WG_TILE - 1) / WG_TILE;
+    red[tid] = c;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    t0 = red[0];
+    nt = (count + WG_TILE - 1) / WG_TILE;
+  }
+#pragma unroll
+  for (int u = 0; u < WR_PER; ++u) {
+    const size_t idx = i0 + u;
     if (idx >= per * G.nsrc) return;
     const int src = (int)(idx / per);
     const size_t ab = idx - (size_t)src * per;
     const int a = (int)(ab / G.r), b = (int)(ab - (size_t)a * G.r);
-    (src ? G.out1 : G.out)[(size_t)e * G.oe + (size_t)a * G.oa + (size_t)b * G.ob] = 0.f;
-    return;
+    float sum = 0.f;
+    for (int t = 0; t < nt; ++t) sum += G.part[((size_t)(t0 + t) * G.nsrc + src) * per + ab];
+    float *out = src ? G.out1 : G.out;
+    out[(size_t)e * G.oe + (size_t)a * G.oa + (size_t)b * G.ob] = G.scale * sum;
   }
-  if (count <= WG_TILE) return;
-  // index of the expert's first tile: tiles are listed expert by expert
-  int c = 0;
-  for (int x = tid; x < e; x += 256) c += (G.offsets[x + 1] - G.offsets[x] + WG_TILE - 1) / WG_TILE;
-  red[tid] = c;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const int t0 = red[0], nt = (count + WG_TILE - 1) / WG_TILE;
-  const size_t per = (size_t)G.wide * G.r;
-  const size_t idx = (size_t)blockIdx.x * 256 + tid;
-  if (idx >= per * G.nsrc) return;
-  const int src = (int)(idx / per);
-  const size_t ab = idx - (size_t)src * per;
-  const int a = (int)(ab / G.r), b = (int)(ab - (size_t)a * G.r);
-  float sum = 0.f;
-  for (int t = 0; t < nt; ++t) sum += G.part[((size_t)(t0 + t) * G.nsrc + src) * per + ab];
-  float *out = src ? G.out1 : G.out;
-  out[(size_t)e * G.oe + (size_t)a * G.oa + (size_t)b * G.ob] = G.scale * sum;
 }
 
 // out[e][j][n] = in[e][n][j] for bf16 [E][N][r] -> [E][r][N]
@@ -295,7 +297,7 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
   dim3 grid((G.wide + WG_COLS - 1) / WG_COLS, max_tiles);
   if (gather) wgrad_mfma_kernel<true><<<grid, 256, 0, st>>>(G);
   else wgrad_mfma_kernel<false><<<grid, 256, 0, st>>>(G);
-  dim3 rgrid((unsigned)(((size_t)G.wide * G.r * G.nsrc + 255) / 256), G.E);
+  dim3 rgrid((unsigned)(((size_t)G.wide * G.r * G.nsrc + 256 * WR_PER - 1) / (256 * WR_PER)), G.E);
   wgrad_reduce_kernel<<<rgrid, 256, 0, st>>>(G);
 }
 
