@@ -46,12 +46,6 @@ constexpr int GM_BPC = 2;    // resident blocks per CU
 constexpr int GM_KG = 128;   // quantization group
 constexpr int GM_KS = 64;    // K per pipeline stage (half a group)
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8).  vmcnt_imm(n): at most n vector memory operations
-// (loads, LDS-DMA, stores) of this wave outstanding; kWaitAll: none, and no
-// LDS operation either.
-constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
-constexpr int kWaitAll = 0x0070;
 
 // One pipeline stage in LDS, as a single array (one object per stage keeps
 // the compiler's LDS-DMA wait tracking exact): A rows (64 x 64 bf16, 16-byte

@@ -100,12 +100,6 @@ DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
   return r;
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8).  vmcnt_imm(n): at most n vector memory operations
-// (loads, LDS-DMA, stores) of this wave outstanding; kWaitAll: none, and no
-// LDS operation either.
-constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
-constexpr int kWaitAll = 0x0070;
 
 template <int MODE>
 __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {

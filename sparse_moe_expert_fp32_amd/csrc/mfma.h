@@ -100,6 +100,13 @@ DEV void dma2(const void *sbase, uint32_t voff, uint32_t lds) {
                : "memory");
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).  vmcnt_imm(n): at most n vector memory operations
+// (loads, LDS-DMA, stores) of this wave outstanding; kWaitAll: none, and no
+// LDS operation either.
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitAll = 0x0070;
+
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would make the compiler drain every outstanding load, including LDS-DMA
 // that is deliberately left in flight.  Callers wait (s_waitcnt) for the

@@ -9,96 +9,152 @@
 // state neither.
 //
 // Two kernels:
-//   router_logits  fp32 FMA on the vector ALUs (no matrix cores), a 128-token
-//                  x 128-expert tile per 256-thread block, d optionally split
-//                  across blocks so that small token counts still fill the
-//                  chip; each split writes its own partial.
+//   router_logits  float32 matrix cores (v_mfma_f32_16x16x4_f32: float32
+//                  operands, products and sums), a 128-token x 128-expert
+//                  tile per 256-thread block fed by an LDS-DMA ring, d
+//                  optionally split across blocks so that small token counts
+//                  still fill the chip; each split writes its own partial.
 //   router_topk    one wave per token: sums the partials in split order, adds
 //                  the bias, then k rounds of a wave-wide argmax on the key
 //                  (logit desc, index asc) and the softmax of the k winners.
 #include "common.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace moe {
 
 constexpr int RT_TM = 128;  // tokens per block
 constexpr int RT_TE = 128;  // experts per block
-constexpr int RT_KC = 16;   // d-chunk staged in LDS per step
 
-// Block tile 128 tokens x 128 experts, 256 threads, each an 8 x 8 register
-// tile; x is staged transposed ([k][token]) and W_r as is ([k][expert]) so
-// that every thread reads its 8 + 8 operands with four 16-byte LDS loads per
-// k and issues 64 FMAs.  blockIdx.z splits d; each split writes a partial.
+// Block tile 128 tokens x 128 experts, 256 threads = 4 waves as 2 x 2, each
+// wave 64 tokens x 64 experts in 4 x 4 v_mfma_f32_16x16x4_f32 tiles (float32
+// operands, float32 products and sums: the router stays full precision).
+// d runs in 32-deep chunks through a 3-deep LDS ring filled by LDS-DMA:
+// x rows as stored ([token][k], bf16 or f32, 16 bytes per lane) and W_r rows
+// ([k][expert], one float per lane, so any E works).  Lane group lg takes
+// k = 8 lg .. 8 lg + 7 of a chunk, one per MFMA k-step, on both operands.
+// Rows past T and experts past E are clamped to valid memory and never
+// stored.  blockIdx.z splits d; each split writes its own partial.
+typedef float f32x4r_t __attribute__((ext_vector_type(4)));
+constexpr int RT_KS = 32;   // d per pipeline stage
+
+DEV float2 ld2f(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+
 template <typename T>
-__global__ __launch_bounds__(256) void router_logits_kernel(
+__global__ __launch_bounds__(256, 2) void router_logits_kernel(
     const T *__restrict__ x, const float *__restrict__ wr, int Tn, int d, int E,
     int split_len, float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) float xs[2][RT_KC][RT_TM];
-  __shared__ __attribute__((aligned(16))) float ws[2][RT_KC][RT_TE];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  constexpr int XB = RT_TM * RT_KS * (int)sizeof(T);   // x bytes per stage
+  constexpr int WB = RT_KS * RT_TE * 4;                // W bytes per stage
+  __shared__ __attribute__((aligned(16))) uint8_t st0[XB + WB];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[XB + WB];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[XB + WB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4, wm = w & 1, wn = w >> 1;
   const int t0 = blockIdx.x * RT_TM, e0 = blockIdx.y * RT_TE;
   const int c_begin = blockIdx.z * split_len;
   const int c_end = min(d, c_begin + split_len);
-  // staging roles: x: token tid/2, 8 consecutive k; W: row tid/16, 8 experts
-  const int xt = tid >> 1, xk = (tid & 1) * 8;
-  const int wk = tid >> 4, we = (tid & 15) * 8;
-  float acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  const int NC = (c_end - c_begin) / RT_KS;   // d and split_len are multiples of RT_KS
 
-  auto stage = [&](int c0, int buf) {
-    {
-      const int t = t0 + xt;
+  // x staging: a row of a stage is RT_KS * sizeof(T) bytes = 16-byte pieces;
+  // piece p of the block (p < XB / 16) is row p / PR, piece p % PR
+  constexpr int PR = RT_KS * (int)sizeof(T) / 16;
+  constexpr int XOPS = XB / 16 / 256;                 // 16-byte DMA per thread
+  uint32_t xoff[XOPS];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = c0 + xk + i;
-        xs[buf][xk + i][xt] = (t < Tn && c < c_end) ? Elem<T>::ld(x, (size_t)t * d + c) : 0.f;
-      }
-    }
-    {
-      const int c = c0 + wk;
+  for (int i = 0; i < XOPS; ++i) {
+    const int pc = (w * XOPS + i) * 64 + lane, row = pc / PR, piece = pc % PR;
+    xoff[i] = (uint32_t)min(t0 + row, Tn - 1) * (uint32_t)(d * sizeof(T)) + piece * 16;
+  }
+  // W staging: RT_KS rows of 128 experts, one float per lane: 2 ops per row
+  // pair of waves; wave w takes rows w, w + 4, ...
+  constexpr int WOPS = RT_KS * 2 / 4;
+  const uint32_t woff = (uint32_t)min(e0 + (lane & 63), E - 1) * 4u;
+  const uint32_t woff2 = (uint32_t)min(e0 + 64 + (lane & 63), E - 1) * 4u;
+  const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
+  auto stage = [&](int jr, uint8_t *S) {
+    const int j = min(jr, NC - 1);
+    const int c0 = c_begin + j * RT_KS;
+    const uint32_t base = lds_addr(S);
+    const char *xb = reinterpret_cast<const char *>(x) + (size_t)c0 * sizeof(T);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = e0 + we + i;
-        ws[buf][wk][we + i] = (c < c_end && e < E) ? wr[(size_t)c * E + e] : 0.f;
-      }
+    for (int i = 0; i < XOPS; ++i) dma16(xb, xoff[i], base + (wu * XOPS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < WOPS / 2; ++i) {
+      const int row = (int)wu + 4 * i;
+      const float *wrow = wr + (size_t)(c0 + row) * E;
+      dma4(wrow, woff, base + XB + (row * RT_TE) * 4);
+      dma4(wrow, woff2, base + XB + (row * RT_TE + 64) * 4);
     }
   };
 
-  int buf = 0;
-  stage(c_begin, 0);
-  __syncthreads();
-  for (int c0 = c_begin; c0 < c_end; c0 += RT_KC) {
-    if (c0 + RT_KC < c_end) stage(c0 + RT_KC, buf ^ 1);
+  f32x4r_t acc[4][4];
 #pragma unroll
-    for (int kk = 0; kk < RT_KC; ++kk) {
-      const float4 xa = *reinterpret_cast<const float4 *>(&xs[buf][kk][ty * 8]);
-      const float4 xb = *reinterpret_cast<const float4 *>(&xs[buf][kk][ty * 8 + 4]);
-      const float4 wa = *reinterpret_cast<const float4 *>(&ws[buf][kk][tx * 8]);
-      const float4 wb = *reinterpret_cast<const float4 *>(&ws[buf][kk][tx * 8 + 4]);
-      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-      const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4r_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t *S) {
+    const T *xs = reinterpret_cast<const T *>(S);
+    const float *ws = reinterpret_cast<const float *>(S + XB);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+    for (int h = 0; h < 2; ++h) {   // k = 8 lg + 4 h .. + 3
+      float av[4][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const T *xr = xs + (64 * wm + 16 * m + lr) * RT_KS + 8 * lg + 4 * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) av[m][q] = Elem<T>::ld(xr, q);
+      }
+      float bv[4][4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bv[n][q] = ws[(8 * lg + 4 * h + q) * RT_TE + 64 * wn + 16 * n + lr];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][q], bv[n][q], acc[m][n], 0, 0, 0);
     }
-    __syncthreads();
-    buf ^= 1;
+  };
+
+  // 3-deep pipeline (see the expert GEMMs): XOPS + WOPS DMA per thread and stage
+  constexpr int kOps = XOPS + WOPS;
+  stage(0, st0);
+  stage(1, st1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
+  block_barrier();
+  for (int j = 0; j < NC; j += 3) {
+#define MOE_R_STEP(JJ, CUR, NXT)                 \
+  {                                              \
+    const int jj = (JJ);                         \
+    stage(jj + 2, NXT);                          \
+    if (jj < NC) compute(CUR);                   \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps)); \
+    block_barrier();                             \
   }
+    MOE_R_STEP(j, st0, st2)
+    MOE_R_STEP(j + 1, st1, st0)
+    MOE_R_STEP(j + 2, st2, st1)
+#undef MOE_R_STEP
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+
   float *out = partial + (size_t)blockIdx.z * Tn * E;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + ty * 8 + i;
-    if (t >= Tn) continue;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = e0 + tx * 8 + j;
-      if (e < E) out[(size_t)t * E + e] = acc[i][j];
+    for (int n = 0; n < 4; ++n) {
+      const int e = e0 + 64 * wn + 16 * n + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 64 * wm + 16 * m + 4 * lg + i;
+        if (t < Tn && e < E) out[(size_t)t * E + e] = acc[m][n][i];
+      }
     }
-  }
 }
 
 // (v, e) beats (v2, e2): larger logit, or equal logit and lower index.
@@ -161,7 +217,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 
 int route_splits(int T, int d, int E) {
   const int blocks = ((T + RT_TM - 1) / RT_TM) * ((E + RT_TE - 1) / RT_TE);
-  const int max_splits = (d + RT_KC - 1) / RT_KC;
+  const int max_splits = d / RT_KS;   // d is a multiple of the quantization group (>= 32)
   int s = (512 + blocks - 1) / blocks;
   if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;
@@ -175,8 +231,8 @@ size_t route_ws_bytes(int T, int d, int E) {
 void launch_router_logits(bool bf16, const void *x, const float *wr, int Tn, int d, int E,
                           void *ws, int *splits_out, hipStream_t st) {
   int splits = route_splits(Tn, d, E);
-  const int chunks = (d + RT_KC - 1) / RT_KC;
-  const int split_len = ((chunks + splits - 1) / splits) * RT_KC;
+  const int chunks = d / RT_KS;
+  const int split_len = ((chunks + splits - 1) / splits) * RT_KS;
   splits = (d + split_len - 1) / split_len;
   float *partial = (float *)ws;
   dim3 grid((Tn + RT_TM - 1) / RT_TM, (E + RT_TE - 1) / RT_TE, splits);
