@@ -47,24 +47,12 @@ constexpr int GM_KG = 128;   // quantization group
 constexpr int GM_KS = 64;    // K per pipeline stage (half a group)
 
 
-// One pipeline stage in LDS, as a single array (one object per stage keeps
-// the compiler's LDS-DMA wait tracking exact): A rows (64 x 64 bf16, 16-byte
-// chunks XOR-swizzled by row), int4 words (32 bytes per block column), the
-// A row sums of the stage's group, the group scale per block column (bf16 in
-// the low half of a 4-byte slot).
+// One pipeline stage in LDS (byte offsets within the stage): A rows (64 x 64
+// bf16, 16-byte chunks XOR-swizzled by row), int4 words (32 bytes per block
+// column), the A row sums of the stage's group, the group scale per block
+// column (bf16 in the low half of a 4-byte slot).
 constexpr int FS_A = 0, FS_B = FS_A + GM_BM * GM_KS * 2, FS_C = FS_B + 256 * GM_KS / 2,
               FS_S = FS_C + GM_BM * 4, FS_BYTES = FS_S + 256 * 4;
-struct FwdStage {
-  uint4 raw[FS_BYTES / 16];
-  DEV bf16_t *a() { return reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(raw) + FS_A); }
-  DEV uint8_t *b() { return reinterpret_cast<uint8_t *>(raw) + FS_B; }
-  DEV float *c() { return reinterpret_cast<float *>(reinterpret_cast<char *>(raw) + FS_C); }
-  DEV uint32_t *s() { return reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(raw) + FS_S); }
-  DEV const bf16_t *a() const { return reinterpret_cast<const bf16_t *>(reinterpret_cast<const char *>(raw) + FS_A); }
-  DEV const uint8_t *b() const { return reinterpret_cast<const uint8_t *>(raw) + FS_B; }
-  DEV const float *c() const { return reinterpret_cast<const float *>(reinterpret_cast<const char *>(raw) + FS_C); }
-  DEV const uint32_t *s() const { return reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(raw) + FS_S); }
-};
 
 // ---------------------------------------------------------------- row sums --
 // out[row][g] = sum of a[row][g*G .. g*G+G) (bf16 values, float32 sum in k order)
@@ -96,14 +84,18 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 // 4 waves, each with all 64 rows and a quarter of the columns (MODE 0: 32 gate
 // + the same 32 up columns, MODE 1: 64 columns).  Two blocks share a CU so
 // that one block's memory waits overlap the other's matrix work.
+//
+// The products are formed transposed, D^T = W X^T: the unpacked weights are
+// the first MFMA operand and the A rows the second, so a lane's accumulator
+// holds one row and four consecutive output columns.  The epilogue then packs
+// four bf16 results into one 8-byte store and the per-row group sums (the
+// -136 start value) are one broadcast value per lane.
 template <int MODE>
 __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGemmArgs A) {
-  // a 3-deep ring of half-group stages: A rows, int4 words, the A row sums
-  // and the scales of the group.  One object per stage, so that reads of one
-  // stage are not ordered behind the LDS-DMA writes into the others.  After
-  // the K loop the four 8 KB regions r0.a, r1.a, r2.a, r0.b hold the
-  // epilogue tile.
-  __shared__ FwdStage r0, r1, r2;
+  // a 3-deep ring of half-group stages (A rows, int4 words, A row sums and
+  // scales of the group) in one LDS array; after the K loop its first 1 KB
+  // holds the cross-wave row sums of H.
+  __shared__ uint4 ring[3 * FS_BYTES / 16];
   __shared__ int tok_lds[GM_BM];
 
   const int K = A.K, N = A.N, NG = K / GM_KG, NS = 2 * NG;   // NS: half-group stages
@@ -117,6 +109,7 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
   const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t kMagic;
   asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(kMagic));
+  const uint32_t ring_lds = lds_addr(ring);
 
   for (int wi = wbeg + bi; wi < wend; wi += nper) {
     // thread indices are re-derived per item through an opaque copy so that
@@ -148,15 +141,18 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
       src_off[i] = (uint32_t)tok_lds[r] * (uint32_t)(A.lda * 2) + c * 16;
     }
     const char *abase = reinterpret_cast<const char *>(A.a);
-    // row sums of the group: wave w, lanes < 16 load rows 16 w + lane
 
     // ---- this wave's columns: 4 fragments of 16.  Block column slots: mode 0
-    // gate 0..127 then up 128..255, mode 1 0..255.
-    int col[4], slot[4];
+    // gate 0..127 then up 128..255, mode 1 0..255.  bslot / col: the column
+    // whose int4 word lane (lr) feeds into the first MFMA operand; oslot: the
+    // first of the four consecutive output columns the lane accumulates.
+    int col[4], bslot[4], oslot[4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      col[nf] = MODE == 0 ? c0 + w * 32 + (nf & 1) * 16 + lr : c0 + w * 64 + nf * 16 + lr;
-      slot[nf] = MODE == 0 ? (nf >> 1) * 128 + w * 32 + (nf & 1) * 16 + lr : w * 64 + nf * 16 + lr;
+      const int base = MODE == 0 ? (nf >> 1) * 128 + w * 32 + (nf & 1) * 16 : w * 64 + nf * 16;
+      bslot[nf] = base + lr;
+      oslot[nf] = base + 4 * lg;
+      col[nf] = c0 + (MODE == 0 ? (base & 127) : base) + lr;
     }
     const uint16_t *sb0 = A.s0, *sb1 = MODE == 0 ? A.s1 : A.s0;
     // int4 staging: wave w, op i covers block columns 32 (2w + i) .. +31, 32 B
@@ -184,14 +180,14 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     }
     const uint32_t rsoff = (uint32_t)tok_lds[16 * w + (lane & 15)] * (uint32_t)A.ld_rsum * 4u;
     // one stage = half a quantization group (64 of K); stages past the end
-    // load a harmless copy of the last one
-    // this wave's LDS destinations within a stage (wave-uniform byte offsets)
+    // load a harmless copy of the last one.  This wave's LDS destinations
+    // within a stage are wave-uniform byte offsets.
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
     const uint32_t la = FS_A + wu * 2 * 1024, lb = FS_B + wu * 2 * 1024, lc = FS_C + wu * 64,
                    ls = FS_S + wu * 256;
-    auto stage = [&](int jr, FwdStage &S) {
+    auto stage = [&](int jr, int slot) {
       const int j = min(jr, NS - 1), g = j >> 1;
-      const uint32_t base = lds_addr(S.raw);
+      const uint32_t base = ring_lds + slot * FS_BYTES;
 #pragma unroll
       for (int i = 0; i < 2; ++i) dma16(abase + (size_t)j * GM_KS * 2, src_off[i], base + la + i * 1024);
 #pragma unroll
@@ -212,21 +208,26 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     // 2 lg + s, int4 word 2 lg + s).  The group's partial products P start
     // at -136 * (row sum of the group) in its first stage and are scaled into
     // the accumulators after its second.
-    auto compute = [&](auto odd, const FwdStage &S) {   // odd: compile-time stage parity
-      const bf16_t *al = S.a();
-      const uint8_t *bb = S.b();
-      const float *cb = S.c();
-      const uint32_t *sb = S.s();
+    auto compute = [&](auto odd, int slot) {   // odd: compile-time stage parity
+      const char *sp = reinterpret_cast<const char *>(ring) + slot * FS_BYTES;
+      const bf16_t *al = reinterpret_cast<const bf16_t *>(sp + FS_A);
+      const uint8_t *bb = reinterpret_cast<const uint8_t *>(sp + FS_B);
+      const float *cb = reinterpret_cast<const float *>(sp + FS_C);
+      const uint32_t *sb = reinterpret_cast<const uint32_t *>(sp + FS_S);
       __builtin_amdgcn_sched_barrier(0);
-      // first stage of a group: its partial products start at -136 * (row sum)
-      f32x4_t ci[4];
       constexpr bool first = !decltype(odd)::value;
+      f32x4_t ci[4];
+      if (first) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ci[m] = -136.f * *reinterpret_cast<const f32x4_t *>(&cb[16 * m + 4 * lg]);
+        for (int m = 0; m < 4; ++m) {
+          const float v = -136.f * cb[16 * m + lr];
+          ci[m] = f32x4_t{v, v, v, v};
+        }
+      }
       uint2 bq[4];
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
-        bq[nf] = *reinterpret_cast<const uint2 *>(bb + slot[nf] * 32 + 8 * lg);
+        bq[nf] = *reinterpret_cast<const uint2 *>(bb + bslot[nf] * 32 + 8 * lg);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         uint4 bu[4];
@@ -245,15 +246,19 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
               al + r * GM_KS + (((2 * lg + s) ^ (r & 7)) << 3));
 #pragma unroll
           for (int nf = 0; nf < 4; ++nf)
-            P[m][nf] = mfma32(av, bu[nf], (s == 0 && first) ? ci[m] : P[m][nf]);
+            P[m][nf] = mfma32(bu[nf], av, (s == 0 && first) ? ci[m] : P[m][nf]);
         }
       }
-      if (decltype(odd)::value) {
+      if (!first) {
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) {
-          const float scg = __uint_as_float(sb[slot[nf]] << 16);
+          const uint4 sv = *reinterpret_cast<const uint4 *>(sb + oslot[nf]);
+          const float sc[4] = {__uint_as_float(sv.x << 16), __uint_as_float(sv.y << 16),
+                               __uint_as_float(sv.z << 16), __uint_as_float(sv.w << 16)};
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[m][nf] += scg * P[m][nf];
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][nf][i] += sc[i] * P[m][nf][i];
         }
       }
     };
@@ -267,8 +272,8 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     constexpr int kOps = 6;
     using even_t = std::integral_constant<bool, false>;
     using odd_t = std::integral_constant<bool, true>;
-    stage(0, r0);
-    stage(1, r1);
+    stage(0, 0);
+    stage(1, 1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
     block_barrier();
     for (int j = 0; j < NS; j += 6) {
@@ -280,18 +285,18 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps)); \
     block_barrier();                             \
   }
-      MOE_F_STEP(j, even_t, r0, r2)
-      MOE_F_STEP(j + 1, odd_t, r1, r0)
-      MOE_F_STEP(j + 2, even_t, r2, r1)
-      MOE_F_STEP(j + 3, odd_t, r0, r2)
-      MOE_F_STEP(j + 4, even_t, r1, r0)
-      MOE_F_STEP(j + 5, odd_t, r2, r1)
+      MOE_F_STEP(j, even_t, 0, 2)
+      MOE_F_STEP(j + 1, odd_t, 1, 0)
+      MOE_F_STEP(j + 2, even_t, 2, 1)
+      MOE_F_STEP(j + 3, odd_t, 0, 2)
+      MOE_F_STEP(j + 4, even_t, 1, 0)
+      MOE_F_STEP(j + 5, odd_t, 2, 1)
 #undef MOE_F_STEP
     }
 
     // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16.  All
     // loads are unconditional (clamped indices) so that they issue together;
-    // rank columns beyond r are zeroed afterwards.
+    // rank positions beyond r are zeroed on the B side with a bit mask.
     constexpr int NSRC = MODE == 0 ? 2 : 1;
     for (int j0 = 0; j0 < A.r; j0 += 16) {
       float zv[NSRC][4][4];
@@ -319,109 +324,77 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            av[src][m][i] = j0 + 4 * lg + i < A.r ? (short)f2bf(A.lam * zv[src][m][i]) : (short)0;
+          for (int i = 0; i < 4; ++i) av[src][m][i] = (short)f2bf(A.lam * zv[src][m][i]);
+      uint32_t kmask[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg + i < A.r ? 0xFFFFu : 0u;
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) {
         short4_t bv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = j0 + 4 * lg + i < A.r ? (short)bl[nf][i] : (short)0;
+        for (int i = 0; i < 4; ++i) bv[i] = (short)(bl[nf][i] & kmask[i]);
         const int src = MODE == 0 && nf >= 2 ? 1 : 0;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m][nf] = mfma16(av[src][m], bv, acc[m][nf]);
+        for (int m = 0; m < 4; ++m) acc[m][nf] = mfma16(bv, av[src][m], acc[m][nf]);
       }
     }
 
-    // ---- epilogue through LDS so that every global store is a full 16-byte
-    // vector.  The tile (64 rows x 256 columns) lives in the ring arrays r0.a,
-    // r1.a, r2.a, r0.b, 64 columns each, 16-byte chunks XOR-swizzled by row.
+    // ---- epilogue: lane (lr, lg) holds, for row 16 m + lr, the four
+    // consecutive columns oslot[nf] .. + 3; each becomes one 8-byte store.
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // trailing (clamped) stage loads
-    __syncthreads();                        // every wave is done with the ring
-    auto quad = [&](int q) -> bf16_t * {
-      return q == 0 ? r0.a() : q == 1 ? r1.a() : q == 2 ? r2.a() : reinterpret_cast<bf16_t *>(r0.b());
-    };
-    auto tel = [&](int r, int c) -> bf16_t & {   // element (r, c), c < 256
-      return quad(c >> 6)[r * 64 + ((((c >> 3) & 7) ^ (r & 7)) << 3) + (c & 7)];
-    };
-    auto tch = [&](int r, int ch) -> uint4 & {   // 16-byte chunk ch (8 columns), ch < 32
-      return *reinterpret_cast<uint4 *>(quad(ch >> 3) + r * 64 + (((ch & 7) ^ (r & 7)) << 3));
-    };
     if (MODE == 0) {
-      // H -> columns 0..127, G -> columns 128..255; then U -> columns 0..127
+      // H = silu(G) U (and G, U when saved); the row sums of H over this
+      // item's 128 columns (one quantization group of the down product) are
+      // reduced over lane groups by shuffles and over waves through LDS.
+      __syncthreads();                        // every wave is done with the ring
+      float *red = reinterpret_cast<float *>(ring);   // [4 waves][64 rows]
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m) {
+        const int r = 16 * m + lr;
+        const bool ok = r < rows;
+        const size_t ro = (size_t)(p0 + min(r, rows - 1)) * A.ldo;
+        float hs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * m + 4 * lg + i;
-#pragma unroll
-          for (int nf = 0; nf < 2; ++nf) {
-            const int c = w * 32 + nf * 16 + lr;
-            const float gv = acc[m][nf][i], uv = acc[m][nf + 2][i];
-            tel(r, c) = f2bf(silu_f(gv) * uv);
-            tel(r, 128 + c) = f2bf(gv);
+        for (int nf = 0; nf < 2; ++nf) {
+          const f32x4_t g = acc[m][nf], u = acc[m][nf + 2];
+          uint2 h;
+          h.x = cvt_pk_bf16(silu_rcp(g[0]) * u[0], silu_rcp(g[1]) * u[1]);
+          h.y = cvt_pk_bf16(silu_rcp(g[2]) * u[2], silu_rcp(g[3]) * u[3]);
+          hs += (__uint_as_float(h.x << 16) + __uint_as_float(h.x & 0xFFFF0000u)) +
+                (__uint_as_float(h.y << 16) + __uint_as_float(h.y & 0xFFFF0000u));
+          const size_t o = ro + c0 + oslot[nf];
+          if (ok) {
+            *reinterpret_cast<uint2 *>(&A.out[o]) = h;
+            if (A.saveG)
+              *reinterpret_cast<uint2 *>(&A.saveG[o]) =
+                  uint2{cvt_pk_bf16(g[0], g[1]), cvt_pk_bf16(g[2], g[3])};
+            if (A.saveU)
+              *reinterpret_cast<uint2 *>(&A.saveU[o]) =
+                  uint2{cvt_pk_bf16(u[0], u[1]), cvt_pk_bf16(u[2], u[3])};
           }
         }
+        hs += __shfl_xor(hs, 16);
+        hs += __shfl_xor(hs, 32);
+        if (lg == 0) red[w * 64 + r] = hs;
+      }
       __syncthreads();
-      // 64 rows x 16 chunks: thread -> (row, chunk); row sums of H on the way
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int idx = it * 256 + tid, r = idx >> 4, ch = idx & 15;
-        const uint4 hv = tch(r, ch);
-        const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-        float v = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v += __uint_as_float(hw[q] << 16) + __uint_as_float(hw[q] & 0xFFFF0000u);
-        const int c = c0 + ch * 8;
-        const bool ok = r < rows && c < N;
-        if (ok) {
-          const size_t o = (size_t)(p0 + r) * A.ldo + c;
-          *reinterpret_cast<uint4 *>(&A.out[o]) = hv;
-          if (A.saveG) *reinterpret_cast<uint4 *>(&A.saveG[o]) = tch(r, 16 + ch);
-        }
-        v = ok ? v : 0.f;
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        if ((lane & 15) == 0 && r < rows && A.rsum_out)
-          A.rsum_out[(size_t)(p0 + r) * A.ld_rsum_out + nt] = v;
-      }
-      if (A.saveU) {
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * m + 4 * lg + i;
-#pragma unroll
-            for (int nf = 0; nf < 2; ++nf) tel(r, w * 32 + nf * 16 + lr) = f2bf(acc[m][nf + 2][i]);
-          }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int idx = it * 256 + tid, r = idx >> 4, ch = idx & 15;
-          const int c = c0 + ch * 8;
-          if (r < rows && c < N)
-            *reinterpret_cast<uint4 *>(&A.saveU[(size_t)(p0 + r) * A.ldo + c]) = tch(r, ch);
-        }
-      }
+      if (tid < rows && A.rsum_out)
+        A.rsum_out[(size_t)(p0 + tid) * A.ld_rsum_out + nt] =
+            (red[tid] + red[64 + tid]) + (red[128 + tid] + red[192 + tid]);
     } else {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m) {
+        const int r = 16 * m + lr;
+        if (r < rows) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * m + 4 * lg + i;
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf) tel(r, w * 64 + nf * 16 + lr) = f2bf(acc[m][nf][i]);
+          for (int nf = 0; nf < 4; ++nf) {
+            const int c = c0 + oslot[nf];
+            if (c < N)
+              *reinterpret_cast<uint2 *>(&A.out[(size_t)(p0 + r) * A.ldo + c]) =
+                  uint2{cvt_pk_bf16(acc[m][nf][0], acc[m][nf][1]),
+                        cvt_pk_bf16(acc[m][nf][2], acc[m][nf][3])};
+          }
         }
-      __syncthreads();
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int idx = it * 256 + tid, r = idx >> 5, ch = idx & 31;
-        const int c = c0 + ch * 8;
-        if (r < rows && c < N)
-          *reinterpret_cast<uint4 *>(&A.out[(size_t)(p0 + r) * A.ldo + c]) = tch(r, ch);
       }
     }
   }

@@ -37,6 +37,11 @@ DEV uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// silu(z) = z / (1 + e^-z) with the hardware reciprocal (about 1 ulp): +-inf
+// limits come out as 0 and z.
+DEV float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+DEV float sigmoid_rcp(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // D = A(16x32) B(32x16) + C.  Lane l holds A row l%16 / B column l%16 with 8
