@@ -98,9 +98,10 @@ bool use_mfma(const moe_dims *d) {
 
 // ---- expert forward workspace
 struct FwdLayout {
-  size_t tiles, ntiles, save, G32, U32, tiles_m, ntiles_m, rs_x, rs_h, total;
+  size_t tiles, ntiles, save, G32, U32, tiles_m, ntiles_m, tiles_p, ntiles_p, rs_x, rs_h, rt_g,
+      rt_u, rt_d, total;
   explicit FwdLayout(const moe_dims *d) {
-    size_t S = (size_t)d->T * d->top_k, f = d->d_ff;
+    size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, E = d->n_experts;
     Carve c;
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
@@ -108,13 +109,19 @@ struct FwdLayout {
     if (use_mfma(d)) {
       G32 = U32 = 0;
       tiles_m = c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2));
-      ntiles_m = c.take(sizeof(int));
-      rs_x = c.take((size_t)d->T * (d->d_model / 128) * 4);
+      ntiles_m = c.take(8 * sizeof(int));
+      tiles_p = c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2));
+      ntiles_p = c.take(sizeof(int));
+      rs_x = c.take((size_t)d->T * (dm / 128) * 4);
       rs_h = c.take(S * (f / 128) * 4);
+      // scale ratios of the three base matrices, [E][N][K/128] f32
+      rt_g = c.take(E * f * (dm / 128) * 4);
+      rt_u = c.take(E * f * (dm / 128) * 4);
+      rt_d = c.take(E * dm * (f / 128) * 4);
     } else {
       G32 = c.take(S * f * 4);
       U32 = c.take(S * f * 4);
-      tiles_m = ntiles_m = rs_x = rs_h = 0;
+      tiles_m = ntiles_m = tiles_p = ntiles_p = rs_x = rs_h = rt_g = rt_u = rt_d = 0;
     }
     total = c.off;
   }
@@ -149,7 +156,7 @@ struct BwdLayout {
     ntiles = c.take(sizeof(int));
     tiles_m = mf ? c.take(max_tiles(d, moe::mfma_t_tile_rows()) * sizeof(int2)) : 0;
     ntiles_m = mf ? c.take(sizeof(int)) : 0;
-    tiles_p = mf ? c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2)) : 0;
+    tiles_p = mf ? c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2)) : 0;
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
     tiles_w = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * sizeof(int2)) : 0;
@@ -376,44 +383,50 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   P.m_es = (size_t)r * d; P.m_cs = 1; P.m_js = d; P.K = d; P.r = r; P.s = 1.f; P.ldz = 3 * r;
 
   if (use_mfma(dims)) {
-    int2 *tiles_m = at<int2>(ws, L.tiles_m);
-    const int mtl = (int)max_tiles(dims, moe::mfma_tile_rows());
-    int *ntiles_m = at<int>(ws, L.ntiles_m);
+    int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
+    const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
+    int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     float *rs_x = at<float>(ws, L.rs_x), *rs_h = at<float>(ws, L.rs_h);
-    moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st);
-    moe::launch_group_rowsum(x, T, d, 128, rs_x, st);
+    float *rt_g = at<float>(ws, L.rt_g), *rt_u = at<float>(ws, L.rt_u), *rt_d = at<float>(ws, L.rt_d);
+    moe::launch_class_tiles(offsets, E, tiles_m, ntiles_m, st);
+    moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
+    // per-row start values -136 * (row sum per group) and per-column scale ratios
+    moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st);
+    moe::launch_scale_ratio(gate.scale, (size_t)E * f, d / 128, rt_g, st);
+    moe::launch_scale_ratio(up.scale, (size_t)E * f, d / 128, rt_u, st);
+    moe::launch_scale_ratio(down.scale, (size_t)E * d, f / 128, rt_d, st);
     // Z_g = X A_g^T, Z_u = X A_u^T (rows gathered from x)
     moe::ProjMArgs Q{};
     Q.a = (const uint16_t *)x; Q.lda = d; Q.perm_src = perm_src; Q.kk = k;
-    Q.tiles = tiles_m; Q.ntiles = ntiles_m; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 2;
+    Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 2;
     Q.m0 = (const uint16_t *)gate.A; Q.m1 = (const uint16_t *)up.A; Q.scale = 1.f;
     Q.Z0 = Z; Q.Z1 = Z + r; Q.ldz = 3 * r;
-    moe::launch_proj_mfma(Q, mtl, true, st);
+    moe::launch_proj_mfma(Q, mtp, true, st);
     const int grid = persistent_grid(moe::mfma_blocks_per_cu());
     moe::MfmaGemmArgs M{};
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
-    M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
+    M.tiles = tiles_m; M.offsets = offsets;
     M.K = d; M.N = f; M.NT = (f + 127) / 128;
-    M.q0 = gate.q; M.s0 = gate.scale; M.B0 = (const uint16_t *)gate.B;
-    M.q1 = up.q; M.s1 = up.scale; M.B1 = (const uint16_t *)up.B;
+    M.q0 = gate.q; M.rt0 = rt_g; M.B0 = (const uint16_t *)gate.B;
+    M.q1 = up.q; M.rt1 = rt_u; M.B1 = (const uint16_t *)up.B;
     M.Z0 = Z; M.Z1 = Z + r; M.ldz = 3 * r; M.r = r; M.lam = lam;
     M.out = (uint16_t *)H; M.ldo = f;
     M.saveG = save ? (uint16_t *)Gs : nullptr;
     M.saveU = save ? (uint16_t *)Us : nullptr;
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128;
-    TIMED(MOE_KT_GATEUP, st, moe::launch_grouped_gemm(0, M, grid, st));
+    TIMED(MOE_KT_GATEUP, st, moe::launch_grouped_gemm(0, M, ntiles_m, grid, st));
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
     Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
-    moe::launch_proj_mfma(Q, mtl, false, st);
+    moe::launch_proj_mfma(Q, mtp, false, st);
     moe::MfmaGemmArgs D{};
     D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128;
-    D.tiles = tiles_m; D.ntiles = ntiles_m; D.offsets = offsets;
+    D.tiles = tiles_m; D.offsets = offsets;
     D.K = f; D.N = d; D.NT = (d + 255) / 256;
-    D.q0 = down.q; D.s0 = down.scale; D.B0 = (const uint16_t *)down.B;
+    D.q0 = down.q; D.rt0 = rt_d; D.B0 = (const uint16_t *)down.B;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
-    TIMED(MOE_KT_DOWN, st, moe::launch_grouped_gemm(1, D, grid, st));
+    TIMED(MOE_KT_DOWN, st, moe::launch_grouped_gemm(1, D, ntiles_m, grid, st));
     return hip_status("moe_expert_fwd");
   }
 
@@ -494,9 +507,9 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     const int grid = persistent_grid(moe::mfma_t_blocks_per_cu());
-    const int mtp = (int)max_tiles(dims, moe::mfma_tile_rows());
+    const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
     moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st);
-    moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_p, ntiles_p, st);
+    moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     uint16_t *bt_d = at<uint16_t>(ws, L.bt);
     uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
     moe::launch_transpose_nr(down.B, E, d, r, bt_d, st);

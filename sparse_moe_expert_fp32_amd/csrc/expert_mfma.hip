@@ -8,31 +8,32 @@
 //   down:     O = H W_d^T + lam (H A_d^T) B_d^T
 // The SwiGLU form is this library's reading; the pages do not name the FFN.
 //
-// Design (one 256-thread block = 4 waves, 128 rows x N-tile per work item):
+// Design (one 256-thread block = 4 waves, 128 rows x 256 columns per item):
 //  * Work items (M-tile, N-tile) are processed by a persistent grid.  Each of
 //    the 8 XCDs takes a contiguous eighth of the item list, so the rows and
 //    weights of neighbouring tiles stay in that XCD's L2.
-//  * The A rows (x gathered by token, or H) stream through LDS one
-//    quantization group (128 of K) at a time, double buffered, loaded with
-//    global_load_lds_dwordx4 straight into LDS in an XOR-swizzled layout
-//    (16-byte chunk c of row r lives at chunk c ^ (r & 15)) so the MFMA
-//    operand reads are bank-conflict free.
-//  * Each wave owns 64 output columns for all 128 rows.  Its int4 weights are
-//    read straight from global memory (16 bytes per lane per group and 16
-//    columns) and unpacked in registers: a nibble u (offset by 8) becomes the
-//    bf16 bit pattern 0x4300 | u, i.e. the exact value 136 + q.  The offset is
-//    removed exactly by starting every group's accumulation at
-//    -136 * (sum of that group's A row), a per-row value precomputed in
-//    float32; then the group's partial product is scaled by the bf16 group
-//    scale into the float32 accumulator.  The weights therefore enter the
-//    matrix cores exactly (no rounding of s*q).
-//  * MFMA v_mfma_f32_16x16x32_bf16: within a group, lane group lg = lane/16
-//    covers K offsets [32 lg, 32 lg + 32), k-step s the 8 values 32 lg + 8 s.
-//    A and B use the same mapping, so the products pair up correctly.
+//  * K streams through a 3-deep LDS ring in half-group stages (64 of K): the
+//    A rows (x gathered by token, or H), the int4 words of the block's 256
+//    columns and, per group, the per-row start values and per-column scale
+//    ratios, all by LDS-DMA (global_load_lds_*).
+//  * Each wave owns 64 output columns for all 128 rows, so every unpacked
+//    weight fragment feeds eight matrix instructions.  A nibble u (offset by
+//    8) becomes the bf16 bit pattern 0x4300 | u, the exact value 136 + q; the
+//    weights enter the matrix cores exactly (no rounding of s*q).
+//  * Group scales without a second accumulator: with s_g the scale of group
+//    g of a column, the accumulator holds Q_g = (sum over groups g' <= g of
+//    s_g' P_g') / s_g, advanced per group as Q <- Q * (s_{g-1} / s_g) + P_g.
+//    The ratios are precomputed per call (scale_ratio_kernel), and the final
+//    multiplication by the last scale happens in the epilogue.  P_g itself
+//    starts at -136 * (the row's sum over the group), which removes the 136
+//    offset; the per-row start values are precomputed too.
+//  * MFMA v_mfma_f32_16x16x32_bf16 with the weights as the first operand
+//    (D^T = W X^T): a lane's accumulator holds one row and four consecutive
+//    columns, so the epilogue writes 8-byte packed bf16 stores.
 //  * Epilogue: the adapter term (lam Z) B^T is one more MFMA (K = rank) into
 //    the same accumulator; gate/up applies SwiGLU in registers (a lane holds
 //    the matching gate and up columns), writes H (bf16) and, for the down
-//    product's offset correction, the row sums of H per group.
+//    product, the start values -136 * (row sum of H) per group.
 #include <type_traits>
 
 #include "common.h"
@@ -41,23 +42,24 @@
 
 namespace moe {
 
-constexpr int GM_BM = 64;    // rows per tile
+constexpr int GM_BM = 128;   // rows per tile
 constexpr int GM_BPC = 2;    // resident blocks per CU
 constexpr int GM_KG = 128;   // quantization group
 constexpr int GM_KS = 64;    // K per pipeline stage (half a group)
 
-
-// One pipeline stage in LDS (byte offsets within the stage): A rows (64 x 64
-// bf16, 16-byte chunks XOR-swizzled by row), int4 words (32 bytes per block
-// column), the A row sums of the stage's group, the group scale per block
-// column (bf16 in the low half of a 4-byte slot).
-constexpr int FS_A = 0, FS_B = FS_A + GM_BM * GM_KS * 2, FS_C = FS_B + 256 * GM_KS / 2,
-              FS_S = FS_C + GM_BM * 4, FS_BYTES = FS_S + 256 * 4;
+// One pipeline stage in LDS, one array per kind (each read is a per-lane base
+// register plus a compile-time offset below 64 KB): A rows (128 x 64 bf16,
+// 16-byte chunks XOR-swizzled by row), int4 words (32 bytes per block column),
+// and the group data: the scale ratio per block column (256 floats), the
+// per-row start values (128 floats) and a copy of those (128 floats, so that
+// every wave issues the same number of loads).
+constexpr int ST_A = GM_BM * GM_KS * 2, ST_B = 256 * GM_KS / 2, ST_X = 512 * 4;
 
 // ---------------------------------------------------------------- row sums --
-// out[row][g] = sum of a[row][g*G .. g*G+G) (bf16 values, float32 sum in k order)
+// out[row][g] = scale * (sum of a[row][g*G .. g*G+G), bf16 values, float32 sum
+// in k order)
 __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int K, int G,
-                                    float *__restrict__ out) {
+                                    float scale, float *__restrict__ out) {
   const int ng = K / G;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)rows * ng) return;
@@ -74,33 +76,63 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
       s += __uint_as_float(w[j] & 0xFFFF0000u);
     }
   }
-  out[i] = s;
+  out[i] = scale * s;
+}
+
+// ------------------------------------------------------------ scale ratios --
+// Per column c of a quantized matrix with ng groups: rt[c][g] = s'[g-1] / s'[g]
+// for g >= 1 and rt[c][0] = s'[ng-1] (the final multiplier), where s' is the
+// bf16 scale with magnitudes below 2^-100 raised to 2^-100 (so a zero scale
+// leaves a contribution of at most 2^-100 times its partial sum).  One thread
+// per element, so that reads and writes are contiguous across the wave.
+__global__ void scale_ratio_kernel(const uint16_t *__restrict__ s, size_t n, int ng,
+                                   float *__restrict__ rt) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  auto guard = [](float v) { return fabsf(v) < 0x1p-100f ? 0x1p-100f : v; };
+  const int g = (int)(i % (size_t)ng);
+  const float cur = guard(bf2f(s[i]));
+  rt[i] = g == 0 ? guard(bf2f(s[i + ng - 1])) : guard(bf2f(s[i - 1])) / cur;
 }
 
 // ------------------------------------------------------------ grouped GEMM --
 // MODE 0: gate/up with SwiGLU epilogue (A = x rows gathered by token); a work
-//         item covers 64 rows x 128 columns of both gate and up.
-// MODE 1: down (A = H rows in permuted order); 64 rows x 256 columns.
-// 4 waves, each with all 64 rows and a quarter of the columns (MODE 0: 32 gate
-// + the same 32 up columns, MODE 1: 64 columns).  Two blocks share a CU so
-// that one block's memory waits overlap the other's matrix work.
-//
-// The products are formed transposed, D^T = W X^T: the unpacked weights are
-// the first MFMA operand and the A rows the second, so a lane's accumulator
-// holds one row and four consecutive output columns.  The epilogue then packs
-// four bf16 results into one 8-byte store and the per-row group sums (the
-// -136 start value) are one broadcast value per lane.
-template <int MODE>
-__global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGemmArgs A) {
-  // a 3-deep ring of half-group stages (A rows, int4 words, A row sums and
-  // scales of the group) in one LDS array; after the K loop its first 1 KB
-  // holds the cross-wave row sums of H.
-  __shared__ uint4 ring[3 * FS_BYTES / 16];
+//         item covers up to 128 rows x 128 columns of both gate and up.
+// MODE 1: down (A = H rows in permuted order); up to 128 rows x 256 columns.
+// WAVES waves per block, each with all rows of the item and NF column
+// fragments of 16 (mode 0: half gate, half up, so SwiGLU pairs up in a lane).
+// Gate/up runs 8 waves x 2 fragments (four waves per SIMD, 128 VGPRs);
+// down runs 4 waves x 4 fragments (two waves per SIMD: each A fragment read
+// from LDS feeds four matrix instructions).  NM (2, 4, 6, 8) is the number of
+// 16-row fragments of the item's tile class: each class of tiles (32, 64, 96,
+// 128 rows) is its own launch, so a short tail tile costs only its rows.
+template <int MODE, int WAVES, int NM>
+__global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
+    const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
+  // (hip-clang passes the second launch bound through as the minimum number
+  // of waves per SIMD: two blocks per CU are WAVES / 2 waves per SIMD, i.e.
+  // at most 256 (4 waves) or 128 (8 waves) VGPRs.)
+  constexpr int NF = 16 / WAVES;                 // column fragments per wave
+  constexpr int BOPS = 8 / WAVES;                // int4-word loads per wave and stage
+  constexpr int NT_ = 64 * WAVES;                // threads
+  constexpr int WCOLS = (MODE == 0 ? 128 : 256) / WAVES;   // block column slots per wave (per matrix in mode 0)
+  constexpr int AOPS = (2 * NM + WAVES - 1) / WAVES;       // 8-row A loads per wave and stage
+  constexpr int XOPS = 8 / WAVES;                // group-data loads per wave (even stages)
+  // first block column slot of fragment nf relative to the wave's columns:
+  // mode 0 gate slots 0..127 then up 128..255, mode 1 0..255
+  constexpr auto nfc = [](int nf) {
+    return MODE == 0 ? (nf / (NF / 2)) * 128 + (nf % (NF / 2)) * 16 : nf * 16;
+  };
+  // a 3-deep ring of half-group stages; after the K loop the first 4 KB of
+  // the A ring hold the cross-wave row sums of H.
+  __shared__ uint4 ringA[3][ST_A / 16];
+  __shared__ uint4 ringB[3][ST_B / 16];
+  __shared__ float ringX[3][ST_X / 4];
   __shared__ int tok_lds[GM_BM];
 
   const int K = A.K, N = A.N, NG = K / GM_KG, NS = 2 * NG;   // NS: half-group stages
   const int BNO = MODE == 0 ? 128 : 256;   // output columns per item (per matrix)
-  const int total = A.ntiles[0] * A.NT;
+  const int total = cls_count[0] * A.NT, tbase = cls_start[0];
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int wbeg = (int)(((long long)total * xcd) >> 3);
   const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
@@ -109,130 +141,143 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
   const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t kMagic;
   asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(kMagic));
-  const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t ldsA = lds_addr(ringA), ldsB = lds_addr(ringB), ldsX = lds_addr(ringX);
 
   for (int wi = wbeg + bi; wi < wend; wi += nper) {
     // thread indices are re-derived per item through an opaque copy so that
-    // the compiler does not keep tid-only address arithmetic live (and
-    // spilled) across the whole persistent loop
+    // the compiler does not keep tid-only address arithmetic live across the
+    // whole persistent loop
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int ti = wi / A.NT, nt = wi - ti * A.NT;
-    const int2 tile = A.tiles[ti];
+    const int2 tile = A.tiles[tbase + ti];
     const int e = tile.x, p0 = tile.y;
-    const int rows = min(GM_BM, A.offsets[e + 1] - p0);
+    const int rows = min(16 * NM, A.offsets[e + 1] - p0);
     const int c0 = nt * BNO;
     __syncthreads();  // LDS of the previous item is free
-    if (tid < GM_BM) {
-      const int p = p0 + min(tid, rows - 1);
-      tok_lds[tid] = MODE == 0 ? A.perm_src[p] / A.kk : p;
+    for (int t = tid; t < GM_BM; t += NT_) {
+      const int p = p0 + min(t, rows - 1);
+      tok_lds[t] = MODE == 0 ? A.perm_src[p] / A.kk : p;
     }
     __syncthreads();
 
-    // ---- A staging: 64 rows x 8 chunks of 16 B per stage; wave w, op i
-    // covers rows 8 (2w + i) .. +7; chunk c of row r lives at c ^ (r & 7)
-    uint32_t src_off[2];
+    // ---- LDS-DMA sources.  A: 8 rows x 8 chunks of 16 B per wave load; wave
+    // w, load i covers rows 8 (AOPS w + i) .. +7 (rows past the tile repeat
+    // its last row); chunk c of row r lives at c ^ (r & 7).
+    uint32_t src_off[AOPS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * (w * 2 + i) + (lane >> 3);
+    for (int i = 0; i < AOPS; ++i) {
+      const int r = min(8 * (AOPS * w + i) + (lane >> 3), GM_BM - 1);
       const int c = (lane & 7) ^ (r & 7);
       src_off[i] = (uint32_t)tok_lds[r] * (uint32_t)(A.lda * 2) + c * 16;
     }
     const char *abase = reinterpret_cast<const char *>(A.a);
-
-    // ---- this wave's columns: 4 fragments of 16.  Block column slots: mode 0
-    // gate 0..127 then up 128..255, mode 1 0..255.  bslot / col: the column
-    // whose int4 word lane (lr) feeds into the first MFMA operand; oslot: the
-    // first of the four consecutive output columns the lane accumulates.
-    int col[4], bslot[4], oslot[4];
+    // int4 words: 8 loads of 32 block columns x 32 B; wave w takes loads
+    // BOPS w .. BOPS w + BOPS - 1 (each all gate or all up)
+    const uint8_t *qbase[BOPS];
+    uint32_t qoff[BOPS];
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const int base = MODE == 0 ? (nf >> 1) * 128 + w * 32 + (nf & 1) * 16 : w * 64 + nf * 16;
-      bslot[nf] = base + lr;
-      oslot[nf] = base + 4 * lg;
-      col[nf] = c0 + (MODE == 0 ? (base & 127) : base) + lr;
-    }
-    const uint16_t *sb0 = A.s0, *sb1 = MODE == 0 ? A.s1 : A.s0;
-    // int4 staging: wave w, op i covers block columns 32 (2w + i) .. +31, 32 B
-    // each (all gate or all up within one op)
-    const uint8_t *qbase[2];
-    uint32_t qoff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int bc = 32 * (2 * w + i) + (lane >> 1);
+    for (int i = 0; i < BOPS; ++i) {
+      const int bc = 32 * (BOPS * w + i) + (lane >> 1);
       const bool up = MODE == 0 && bc >= 128;
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
       qbase[i] = (const uint8_t *)uniform_ptr((up ? A.q1 : A.q0) + (size_t)e * N * (K / 2));
       qoff[i] = (uint32_t)c * (uint32_t)(K / 2) + 16 * (lane & 1);
     }
-    // scale staging: wave w, lane l -> block column 64 w + l (mode 0: gate
-    // columns first, then up), one bf16 per lane into a 4-byte LDS slot
-    const uint16_t *sbase;
-    uint32_t soff;
-    {
-      const int bc = 64 * w + lane;
-      const bool up = MODE == 0 && bc >= 128;
-      const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      sbase = (const uint16_t *)uniform_ptr((up ? sb1 : sb0) + (size_t)e * N * NG);
-      soff = (uint32_t)c * (uint32_t)NG * 2u;
+    // group data, 8 loads of 64 floats: loads 0-3 the ratios of block
+    // columns 64 q + lane, loads 4-5 the start values of rows 64 (q - 4) +
+    // lane, loads 6-7 the same start values again (into the spare quarter);
+    // wave w takes loads XOPS w .. XOPS w + XOPS - 1
+    const float *xbase[XOPS];
+    uint32_t xoff[XOPS];
+#pragma unroll
+    for (int i = 0; i < XOPS; ++i) {
+      const int q = XOPS * w + i;
+      const float *b;
+      if (q < 4) {
+        const int bc = 64 * q + lane;
+        const bool up = MODE == 0 && bc >= 128;
+        const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
+        b = (up ? A.rt1 : A.rt0) + (size_t)e * N * NG;
+        xoff[i] = (uint32_t)c * (uint32_t)NG * 4u;
+      } else {
+        b = A.rsum;
+        xoff[i] = (uint32_t)tok_lds[64 * (q & 1) + lane] * (uint32_t)A.ld_rsum * 4u;
+      }
+      xbase[i] = (const float *)uniform_ptr(b);
     }
-    const uint32_t rsoff = (uint32_t)tok_lds[16 * w + (lane & 15)] * (uint32_t)A.ld_rsum * 4u;
-    // one stage = half a quantization group (64 of K); stages past the end
-    // load a harmless copy of the last one.  This wave's LDS destinations
-    // within a stage are wave-uniform byte offsets.
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
-    const uint32_t la = FS_A + wu * 2 * 1024, lb = FS_B + wu * 2 * 1024, lc = FS_C + wu * 64,
-                   ls = FS_S + wu * 256;
-    auto stage = [&](int jr, int slot) {
+    const uint32_t la = ldsA + wu * AOPS * 1024, lb = ldsB + wu * BOPS * 1024,
+                   lx = ldsX + wu * XOPS * 256;
+    // per-lane LDS read bases (bytes); the rest of every read address is a
+    // compile-time constant.  The int4 word lane lr feeds into the first MFMA
+    // operand is block column slot w * WCOLS + nfc + lr; the lane's
+    // accumulator holds the four output columns from slot w * WCOLS + nfc + 4 lg.
+    const uint32_t offA0 = opaque(ldsA + lr * 128 + (((2 * lg) ^ (lr & 7)) << 4)),
+                   offB = opaque(ldsB + (w * WCOLS + lr) * 32 + 8 * lg),
+                   offR = opaque(ldsX + (w * WCOLS + 4 * lg) * 4),
+                   offC = opaque(ldsX + 1024 + lr * 4);
+
+    // one stage = half a quantization group (64 of K); a group's first stage
+    // also brings the ratios and start values.  Stages past the end load a
+    // harmless copy of the last one.
+    auto stage = [&](auto evenc, int jr, int slot) {
       const int j = min(jr, NS - 1), g = j >> 1;
-      const uint32_t base = ring_lds + slot * FS_BYTES;
+      // destinations re-derived per stage (scalar adds) rather than held
+      uint32_t sa = la, sb = lb;
+      asm volatile("" : "+s"(sa), "+s"(sb));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(abase + (size_t)j * GM_KS * 2, src_off[i], base + la + i * 1024);
+      for (int i = 0; i < AOPS; ++i)
+        dma16(abase + (size_t)j * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma16(qbase[i] + (size_t)j * (GM_KS / 2), qoff[i], base + lb + i * 1024);
-      if (lane < 16) dma4(A.rsum + g, rsoff, base + lc);
-      dma2(sbase + g, soff, base + ls);
+      for (int i = 0; i < BOPS; ++i)
+        dma16(qbase[i] + (size_t)j * (GM_KS / 2), qoff[i], sb + slot * ST_B + i * 1024);
+      if (decltype(evenc)::value) {
+        uint32_t sx = lx;
+        asm volatile("" : "+s"(sx));
+#pragma unroll
+        for (int i = 0; i < XOPS; ++i) dma4(xbase[i] + g, xoff[i], sx + slot * ST_X + i * 256);
+      }
     };
+    constexpr int kOpsOdd = AOPS + BOPS, kOpsEven = kOpsOdd + XOPS;
 
-    f32x4_t acc[4][4], P[4][4];
+    f32x4_t acc[NM][NF];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nf = 0; nf < NF; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // one stage: 2 k-substeps x 4 row fragments x 4 column fragments.  Lane
+    // one stage: 2 k-substeps x NM row fragments x NF column fragments.  Lane
     // group lg takes k = 16 lg + 8 s .. + 7 of the stage in substep s (A chunk
-    // 2 lg + s, int4 word 2 lg + s).  The group's partial products P start
-    // at -136 * (row sum of the group) in its first stage and are scaled into
-    // the accumulators after its second.
+    // 2 lg + s, int4 word 2 lg + s).  A group's first stage advances the
+    // accumulators: Q <- Q * ratio + (-136 * row sum).
     auto compute = [&](auto odd, int slot) {   // odd: compile-time stage parity
-      const char *sp = reinterpret_cast<const char *>(ring) + slot * FS_BYTES;
-      const bf16_t *al = reinterpret_cast<const bf16_t *>(sp + FS_A);
-      const uint8_t *bb = reinterpret_cast<const uint8_t *>(sp + FS_B);
-      const float *cb = reinterpret_cast<const float *>(sp + FS_C);
-      const uint32_t *sb = reinterpret_cast<const uint32_t *>(sp + FS_S);
       __builtin_amdgcn_sched_barrier(0);
-      constexpr bool first = !decltype(odd)::value;
-      f32x4_t ci[4];
-      if (first) {
+      u32x2_t bq[NF];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float v = -136.f * cb[16 * m + lr];
-          ci[m] = f32x4_t{v, v, v, v};
+      for (int nf = 0; nf < NF; ++nf) bq[nf] = lds_ld<u32x2_t>(offB + slot * ST_B + nfc(nf) * 32);
+      if (!decltype(odd)::value) {
+        f32x4_t rv[NF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) rv[nf] = lds_ld<f32x4_t>(offR + slot * ST_X + nfc(nf) * 4);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const float nv = lds_ld<float>(offC + slot * ST_X + m * 64);
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][nf][i] = __builtin_fmaf(acc[m][nf][i], rv[nf][i], nv);
         }
       }
-      uint2 bq[4];
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf)
-        bq[nf] = *reinterpret_cast<const uint2 *>(bb + bslot[nf] * 32 + 8 * lg);
+      // substep 1 reads chunk 2 lg + 1, i.e. the neighbouring swizzled chunk
+      const uint32_t offA1 = offA0 ^ 16u;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        uint4 bu[4];
+        uint4 bu[NF];
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
+        for (int nf = 0; nf < NF; ++nf) {
           const uint32_t x = s ? bq[nf].y : bq[nf].x;
           bu[nf].x = __builtin_amdgcn_bitop3_b32(x, kMask, kMagic, 0x6A);
           bu[nf].y = __builtin_amdgcn_bitop3_b32(x >> 4, kMask, kMagic, 0x6A);
@@ -240,162 +285,241 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
           bu[nf].w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = 16 * m + lr;
-          const uint4 av = *reinterpret_cast<const uint4 *>(
-              al + r * GM_KS + (((2 * lg + s) ^ (r & 7)) << 3));
+        for (int m = 0; m < NM; ++m) {
+          const u32x4_t a4 = lds_ld<u32x4_t>((s ? offA1 : offA0) + slot * ST_A + m * 2048);
+          const uint4 av = make_uint4(a4.x, a4.y, a4.z, a4.w);
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-            P[m][nf] = mfma32(bu[nf], av, (s == 0 && first) ? ci[m] : P[m][nf]);
-        }
-      }
-      if (!first) {
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const uint4 sv = *reinterpret_cast<const uint4 *>(sb + oslot[nf]);
-          const float sc[4] = {__uint_as_float(sv.x << 16), __uint_as_float(sv.y << 16),
-                               __uint_as_float(sv.z << 16), __uint_as_float(sv.w << 16)};
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][nf][i] += sc[i] * P[m][nf][i];
+          for (int nf = 0; nf < NF; ++nf) acc[m][nf] = mfma32(bu[nf], av, acc[m][nf]);
         }
       }
     };
 
     // 3-deep pipeline: stage j computes from ring slot j % 3 while the loads
-    // of stages j + 1 and j + 2 are in flight.  Per thread and stage: 2 + 2 +
-    // 1 + 1 LDS-DMA (the same count in every wave), so "stage j + 1 has
-    // landed" is vmcnt(6).  The loop runs in groups of six stages (three ring
-    // slots, two parities); stages past the end compute nothing (uniform
-    // branch) but still issue their (clamped) loads, so every wait is alike.
-    constexpr int kOps = 6;
+    // of stages j + 1 and j + 2 are in flight.  Every wave issues the same
+    // number of LDS-DMA per stage (kOpsEven for a group's first stage,
+    // kOpsOdd for its second), so "stage j + 1 has landed" is a vmcnt of the
+    // count of stage j + 2, which has the parity of j.  The loop runs in
+    // groups of six stages (three ring slots, two parities); stages past the
+    // end compute nothing (uniform branch) but still issue their (clamped)
+    // loads, so every wait is alike.
     using even_t = std::integral_constant<bool, false>;
     using odd_t = std::integral_constant<bool, true>;
-    stage(0, 0);
-    stage(1, 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
+    using ev_t = std::integral_constant<bool, true>;
+    using od_t = std::integral_constant<bool, false>;
+    stage(ev_t(), 0, 0);
+    stage(od_t(), 1, 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOpsOdd));
     block_barrier();
     for (int j = 0; j < NS; j += 6) {
-#define MOE_F_STEP(JJ, PAR, CUR, NXT)            \
-  {                                              \
-    const int jj = (JJ);                         \
-    stage(jj + 2, NXT);                          \
-    if (jj < NS) compute(PAR(), CUR);            \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps)); \
-    block_barrier();                             \
+#define MOE_F_STEP(JJ, PAR, LD, OPS, CUR, NXT)  \
+  {                                             \
+    const int jj = (JJ);                        \
+    stage(LD(), jj + 2, NXT);                   \
+    if (jj < NS) compute(PAR(), CUR);           \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS)); \
+    block_barrier();                            \
   }
-      MOE_F_STEP(j, even_t, 0, 2)
-      MOE_F_STEP(j + 1, odd_t, 1, 0)
-      MOE_F_STEP(j + 2, even_t, 2, 1)
-      MOE_F_STEP(j + 3, odd_t, 0, 2)
-      MOE_F_STEP(j + 4, even_t, 1, 0)
-      MOE_F_STEP(j + 5, odd_t, 2, 1)
+      MOE_F_STEP(j, even_t, ev_t, kOpsEven, 0, 2)
+      MOE_F_STEP(j + 1, odd_t, od_t, kOpsOdd, 1, 0)
+      MOE_F_STEP(j + 2, even_t, ev_t, kOpsEven, 2, 1)
+      MOE_F_STEP(j + 3, odd_t, od_t, kOpsOdd, 0, 2)
+      MOE_F_STEP(j + 4, even_t, ev_t, kOpsEven, 1, 0)
+      MOE_F_STEP(j + 5, odd_t, od_t, kOpsOdd, 2, 1)
 #undef MOE_F_STEP
     }
 
-    // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16.  All
-    // loads are unconditional (clamped indices) so that they issue together;
-    // rank positions beyond r are zeroed on the B side with a bit mask.
+    // ---- epilogue columns (in the matrix's own column space), re-derived
+    // from an opaque copy of the thread index: col = the B-operand column of
+    // lane lr, ocol = the first of the lane's four output columns
+    int tid2 = threadIdx.x;
+    asm volatile("" : "+v"(tid2));
+    const int lr2 = tid2 & 15, lg2 = (tid2 >> 4) & 3, w2 = tid2 >> 6;
+    int col[NF], ocol[NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+      const int mc = c0 + w2 * WCOLS + (MODE == 0 ? nfc(nf) & 127 : nfc(nf));
+      col[nf] = mc + lr2;
+      ocol[nf] = mc + 4 * lg2;
+    }
+    // mode 0: fragment nf belongs to the up matrix when nf >= NF / 2
+    auto is_up = [](int nf) { return MODE == 0 && nf >= NF / 2; };
+
+    // ---- the last group's scale: rt[column][0]
+    {
+      float sl[NF][4];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const float *rt = is_up(nf) ? A.rt1 : A.rt0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sl[nf][i] = rt[((size_t)e * N + min(ocol[nf] + i, N - 1)) * NG];
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][nf][i] *= sl[nf][i];
+    }
+
+    // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16.  B
+    // positions beyond r are zeroed with a bit mask; Z is read four floats at
+    // a time (one 16-byte load when r and the row stride allow it), two row
+    // fragments at a time to bound the registers in flight.  Mode 0: gate
+    // fragments take Z_g and B_g, up fragments Z_u and B_u.
     constexpr int NSRC = MODE == 0 ? 2 : 1;
+    const bool zvec = ((A.r | A.ldz) & 3) == 0;
     for (int j0 = 0; j0 < A.r; j0 += 16) {
-      float zv[NSRC][4][4];
-      uint16_t bl[4][4];
+      uint32_t kmask[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg2 + i < A.r ? 0xFFFFu : 0u;
+      short4_t bv[NF];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const uint16_t *Bm = is_up(nf) ? A.B1 : A.B0;
+        const size_t rowb = ((size_t)e * N + min(col[nf], N - 1)) * A.r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bv[nf][i] = (short)(Bm[rowb + min(j0 + 4 * lg2 + i, A.r - 1)] & kmask[i]);
+      }
+      const int jz = min(j0 + 4 * lg2, A.r - 1);
 #pragma unroll
       for (int src = 0; src < NSRC; ++src) {
         const float *Zp = src ? A.Z1 : A.Z0;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int p = p0 + min(16 * m + lr, rows - 1);
+        for (int m = 0; m < NM; ++m) {
+          const float *zr = Zp + (size_t)(p0 + min(16 * m + lr2, rows - 1)) * A.ldz;
+          f32x4_t z;
+          if (zvec) {
+            z = *reinterpret_cast<const f32x4_t *>(zr + jz);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) zv[src][m][i] = Zp[(size_t)p * A.ldz + min(j0 + 4 * lg + i, A.r - 1)];
+            for (int i = 0; i < 4; ++i) z[i] = zr[min(j0 + 4 * lg2 + i, A.r - 1)];
+          }
+          short4_t av;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[i] = (short)f2bf(A.lam * z[i]);
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            if ((is_up(nf) ? 1 : 0) != src) continue;
+            acc[m][nf] = mfma16(bv[nf], av, acc[m][nf]);
+          }
+          if (m & 1) __builtin_amdgcn_sched_barrier(0);
         }
-      }
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const uint16_t *Bm = MODE == 0 && nf >= 2 ? A.B1 : A.B0;
-        const size_t rowb = ((size_t)e * N + min(col[nf], N - 1)) * A.r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bl[nf][i] = Bm[rowb + min(j0 + 4 * lg + i, A.r - 1)];
-      }
-      short4_t av[NSRC][4];
-#pragma unroll
-      for (int src = 0; src < NSRC; ++src)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) av[src][m][i] = (short)f2bf(A.lam * zv[src][m][i]);
-      uint32_t kmask[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg + i < A.r ? 0xFFFFu : 0u;
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        short4_t bv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = (short)(bl[nf][i] & kmask[i]);
-        const int src = MODE == 0 && nf >= 2 ? 1 : 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m][nf] = mfma16(bv, av[src][m], acc[m][nf]);
       }
     }
 
     // ---- epilogue: lane (lr, lg) holds, for row 16 m + lr, the four
-    // consecutive columns oslot[nf] .. + 3; each becomes one 8-byte store.
+    // consecutive columns ocol[nf] .. + 3; each becomes one 8-byte store.
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // trailing (clamped) stage loads
     if (MODE == 0) {
       // H = silu(G) U (and G, U when saved); the row sums of H over this
       // item's 128 columns (one quantization group of the down product) are
-      // reduced over lane groups by shuffles and over waves through LDS.
-      __syncthreads();                        // every wave is done with the ring
-      float *red = reinterpret_cast<float *>(ring);   // [4 waves][64 rows]
+      // reduced over lane groups by shuffles and over the waves through LDS,
+      // and stored as the down product's start values -136 * sum.
+      __syncthreads();                          // every wave is done with the ring
+      float *red = reinterpret_cast<float *>(ringA);   // [WAVES][128 rows]
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = 16 * m + lr;
-        const bool ok = r < rows;
-        const size_t ro = (size_t)(p0 + min(r, rows - 1)) * A.ldo;
+      for (int m = 0; m < NM; ++m) {
+        const int r = 16 * m + lr2;
         float hs = 0.f;
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-          const f32x4_t g = acc[m][nf], u = acc[m][nf + 2];
-          uint2 h;
+        for (int nf = 0; nf < NF / 2; ++nf) {
+          const f32x4_t g = acc[m][nf], u = acc[m][nf + NF / 2];
+          u32x2_t h;
           h.x = cvt_pk_bf16(silu_rcp(g[0]) * u[0], silu_rcp(g[1]) * u[1]);
           h.y = cvt_pk_bf16(silu_rcp(g[2]) * u[2], silu_rcp(g[3]) * u[3]);
           hs += (__uint_as_float(h.x << 16) + __uint_as_float(h.x & 0xFFFF0000u)) +
                 (__uint_as_float(h.y << 16) + __uint_as_float(h.y & 0xFFFF0000u));
-          const size_t o = ro + c0 + oslot[nf];
-          if (ok) {
-            *reinterpret_cast<uint2 *>(&A.out[o]) = h;
+          if (r < rows) {
+            const size_t o = (size_t)(p0 + r) * A.ldo + ocol[nf];
+            *reinterpret_cast<u32x2_t *>(&A.out[o]) = h;
             if (A.saveG)
-              *reinterpret_cast<uint2 *>(&A.saveG[o]) =
-                  uint2{cvt_pk_bf16(g[0], g[1]), cvt_pk_bf16(g[2], g[3])};
+              *reinterpret_cast<u32x2_t *>(&A.saveG[o]) =
+                  u32x2_t{cvt_pk_bf16(g[0], g[1]), cvt_pk_bf16(g[2], g[3])};
             if (A.saveU)
-              *reinterpret_cast<uint2 *>(&A.saveU[o]) =
-                  uint2{cvt_pk_bf16(u[0], u[1]), cvt_pk_bf16(u[2], u[3])};
+              *reinterpret_cast<u32x2_t *>(&A.saveU[o]) =
+                  u32x2_t{cvt_pk_bf16(u[0], u[1]), cvt_pk_bf16(u[2], u[3])};
           }
         }
         hs += __shfl_xor(hs, 16);
         hs += __shfl_xor(hs, 32);
-        if (lg == 0) red[w * 64 + r] = hs;
+        if (lg2 == 0) red[w2 * GM_BM + r] = hs;
       }
       __syncthreads();
-      if (tid < rows && A.rsum_out)
-        A.rsum_out[(size_t)(p0 + tid) * A.ld_rsum_out + nt] =
-            (red[tid] + red[64 + tid]) + (red[128 + tid] + red[192 + tid]);
+      if (tid2 < rows && A.rsum_out) {
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < WAVES; ++q) v += red[q * GM_BM + tid2];
+        A.rsum_out[(size_t)(p0 + tid2) * A.ld_rsum_out + nt] = -136.f * v;
+      }
     } else {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = 16 * m + lr;
+      for (int m = 0; m < NM; ++m) {
+        const int r = 16 * m + lr2;
         if (r < rows) {
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) {
-            const int c = c0 + oslot[nf];
-            if (c < N)
-              *reinterpret_cast<uint2 *>(&A.out[(size_t)(p0 + r) * A.ldo + c]) =
-                  uint2{cvt_pk_bf16(acc[m][nf][0], acc[m][nf][1]),
-                        cvt_pk_bf16(acc[m][nf][2], acc[m][nf][3])};
+          for (int nf = 0; nf < NF; ++nf) {
+            if (ocol[nf] < N)
+              *reinterpret_cast<u32x2_t *>(&A.out[(size_t)(p0 + r) * A.ldo + ocol[nf]]) =
+                  u32x2_t{cvt_pk_bf16(acc[m][nf][0], acc[m][nf][1]),
+                          cvt_pk_bf16(acc[m][nf][2], acc[m][nf][3])};
           }
         }
       }
+    }
+  }
+}
+
+// ------------------------------------------------------------ tile classes --
+// The work list of the grouped GEMMs: each expert's rows in tiles of 128,
+// the last (partial) one rounded up to 32, 64, 96 or 128 rows.  tiles holds
+// the 128-row class first, then 96, 64, 32 (each in expert order); cnt[c] and
+// cnt[4 + c] are the count and first index of class c (c = 0: 128 rows ..
+// c = 3: 32 rows).  One 1024-thread block (E <= 1024).
+__global__ __launch_bounds__(1024) void build_class_tiles_kernel(const int32_t *__restrict__ offsets,
+                                                                 int E, int2 *__restrict__ tiles,
+                                                                 int *__restrict__ cnt) {
+  __shared__ int sc[4][1024];
+  const int e = threadIdx.x;
+  int lo = 0, n = 0;
+  if (e < E) {
+    lo = offsets[e];
+    n = offsets[e + 1] - lo;
+  }
+  const int nfull = n >> 7, tail = n & 127;
+  const int tcls = tail == 0 ? -1 : 3 - ((tail - 1) >> 5);   // 97..127 -> 0, 1..32 -> 3
+  int c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = (k == 0 ? nfull : 0) + (tcls == k ? 1 : 0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sc[k][e] = c[k];
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = e >= off ? sc[k][e - off] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sc[k][e] += v[k];
+    __syncthreads();
+  }
+  int start[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    start[k] = s;
+    s += sc[k][1023];
+  }
+  // class 0: the full tiles, then a 97..127-row tail
+  int pos = start[0] + sc[0][e] - c[0];
+  for (int i = 0; i < c[0]; ++i) tiles[pos + i] = make_int2(e, lo + 128 * i);
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (c[k]) tiles[start[k] + sc[k][e] - 1] = make_int2(e, lo + 128 * nfull);
+  if (e == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cnt[k] = sc[k][1023];
+      cnt[4 + k] = start[k];
     }
   }
 }
@@ -403,15 +527,37 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
 int mfma_tile_rows() { return GM_BM; }
 int mfma_blocks_per_cu() { return GM_BPC; }
 
-void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st) {
+void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, float *out,
+                         hipStream_t st) {
   size_t n = (size_t)rows * (K / G);
   group_rowsum_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((const bf16_t *)a, rows, K, G,
-                                                                   out);
+                                                                   scale, out);
 }
 
-void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t st) {
-  if (mode == 0) grouped_gemm_kernel<0><<<grid, 256, 0, st>>>(A);
-  else grouped_gemm_kernel<1><<<grid, 256, 0, st>>>(A);
+void launch_scale_ratio(const uint16_t *s, size_t cols, int ng, float *rt, hipStream_t st) {
+  const size_t n = cols * (size_t)ng;
+  scale_ratio_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, n, ng, rt);
+}
+
+void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st) {
+  build_class_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, tiles, cnt);
+}
+
+// One launch per tile class (128, 96, 64, 32 rows); cnt as written by
+// launch_class_tiles.
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int grid,
+                         hipStream_t st) {
+  if (mode == 0) {
+    grouped_gemm_kernel<0, 4, 8><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
+    grouped_gemm_kernel<0, 4, 6><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
+    grouped_gemm_kernel<0, 4, 4><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
+    grouped_gemm_kernel<0, 4, 2><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+  } else {
+    grouped_gemm_kernel<1, 4, 8><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
+    grouped_gemm_kernel<1, 4, 6><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
+    grouped_gemm_kernel<1, 4, 4><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
+    grouped_gemm_kernel<1, 4, 2><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+  }
 }
 
 }  // namespace moe

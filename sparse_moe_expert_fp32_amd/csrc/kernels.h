@@ -68,20 +68,29 @@ void launch_swiglu_bwd(bool act_bf16, const float *dH, const void *Gs, const voi
 struct MfmaGemmArgs {
   const void *a; int lda;                 // A rows: x [T][d] (mode 0) or H [S][f] (mode 1)
   const int32_t *perm_src; int kk;        // mode 0: token of a permuted row
-  const float *rsum; int ld_rsum;         // per A row, per group of 128: sum of the row
-  const int2 *tiles; const int *ntiles; const int32_t *offsets;
+  const float *rsum; int ld_rsum;         // per A row, per group of 128: -136 * sum of the row
+  const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
   int K, N, NT;                           // reduction, columns per matrix, N-tiles per M-tile
-  const uint8_t *q0; const uint16_t *s0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
-  const uint8_t *q1; const uint16_t *s1; const uint16_t *B1;   // up (mode 0)
+  const uint8_t *q0; const float *rt0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
+  const uint8_t *q1; const float *rt1; const uint16_t *B1;   // up (mode 0)
   const float *Z0, *Z1; int ldz; int r; float lam;             // X A^T projections (float32)
   uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
   uint16_t *saveG, *saveU;                // mode 0, optional
-  float *rsum_out; int ld_rsum_out;       // mode 0: group sums of H rows
+  float *rsum_out; int ld_rsum_out;       // mode 0: -136 * group sums of H rows
 };
 int mfma_tile_rows();
 int mfma_blocks_per_cu();      // resident blocks per CU the kernel is built for
-void launch_group_rowsum(const void *a, int rows, int K, int G, float *out, hipStream_t st);
-void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, int grid, hipStream_t st);
+void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, float *out,
+                         hipStream_t st);
+// scale ratios of a quantized matrix ([cols][ng] bf16 -> [cols][ng] f32):
+// rt[c][g] = s[c][g-1] / s[c][g] for g >= 1, rt[c][0] = s[c][ng-1]
+void launch_scale_ratio(const uint16_t *s, size_t cols, int ng, float *rt, hipStream_t st);
+// expert tiles of 128 rows, the partial last one of each expert rounded up to
+// 32, 64, 96 or 128 rows, grouped by that class; cnt[8]: count and first
+// index of each class (128-row class first)
+void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st);
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int grid,
+                         hipStream_t st);
 
 // transposed-base products of the backward (expert_mfma_bwd.hip)
 struct MfmaGemmTArgs {
@@ -112,6 +121,7 @@ struct ProjMArgs {                        // Z_s = scale * A M_s^T over each exp
   float scale; float *Z0, *Z1; int ldz;
 };
 void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st);
+int proj_tile_rows();
 struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p][a] R_s[p][b]
   const uint16_t *w; int ldw; const int32_t *perm_src; int kk;
   const float *rr; int ldr;               // R of source 0

@@ -288,6 +288,8 @@ __global__ void transpose_nr_kernel(const uint16_t *__restrict__ in, int E, int 
   for (int j = 0; j < r; ++j) out[(e * r + j) * N + n] = in[i * r + j];
 }
 
+int proj_tile_rows() { return 64; }
+
 void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st) {
   if (gather) proj_mfma_kernel<true><<<max_tiles, 256, 0, st>>>(P);
   else proj_mfma_kernel<false><<<max_tiles, 256, 0, st>>>(P);

@@ -10,6 +10,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // 8 int4 values (one word of the storage layout) -> bf16 (136 + q), in k order:
@@ -84,6 +86,21 @@ DEV void load_lds2(const void *gsrc, void *lds_wave_base) {
 // uniform_ptr (readfirstlane) first.
 DEV uint32_t lds_addr(const void *p) {   // 32-bit LDS byte address of a __shared__ pointer
   return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+// Load a T from LDS byte address `addr`.  With `addr` = an opaque per-lane
+// base + a compile-time constant, the constant becomes the instruction's
+// 16-bit offset (the base should then already include the array's address).
+// T should be a scalar or an ext_vector type: those carry their natural
+// alignment, so 8- and 16-byte reads stay single instructions.
+template <typename T> DEV T lds_ld(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) T *)(uintptr_t)addr;
+}
+template <typename T> DEV void lds_st(uint32_t addr, T v) {
+  *(__attribute__((address_space(3))) T *)(uintptr_t)addr = v;
+}
+DEV uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 DEV const void *uniform_ptr(const void *p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
