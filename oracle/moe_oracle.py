@@ -372,3 +372,29 @@ def expert_grads(inputs: dict, R: dict, e: int, k: int, group: int, lam: float =
     fw = expert_forward(ex, X, lam)
     dO = R["gates"][rows, js][:, None] * to_f64(inputs["dy"][rows])
     return expert_backward(ex, X, fw, dO, lam)
+
+
+# --------------------------------------------------- adapter optimizer step --
+# "Reversible Sparse MoE Single Node" (skill card), Principle 3 "TQP Optimizer
+# Strategy" and Pattern 3: the optimizer state lives on the low-rank adapters
+# only (the quantized base is fixed).  The pages do not name the optimizer;
+# the reading taken here is AdamW as published ("Decoupled Weight Decay
+# Regularization", Loshchilov and Hutter, over Adam of Kingma and Ba): float32
+# master parameters with two float32 moments, bias-corrected moments, and
+# weight decay applied to the parameter directly (not through the gradient).
+
+def adamw_step(p, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float, step: int):
+    """One AdamW step at step number t = `step` (t >= 1), in float64:
+        m' = beta1 m + (1 - beta1) g
+        v' = beta2 v + (1 - beta2) g^2
+        p' = p - lr (  (m' / (1 - beta1^t)) / (sqrt(v' / (1 - beta2^t)) + eps)
+                     + weight_decay p )
+    Returns (p', m', v') as float64 arrays."""
+    p, g, m, v = (np.asarray(a, dtype=np.float64) for a in (p, g, m, v))
+    m1 = beta1 * m + (1.0 - beta1) * g
+    v1 = beta2 * v + (1.0 - beta2) * g * g
+    mhat = m1 / (1.0 - beta1 ** step)
+    vhat = v1 / (1.0 - beta2 ** step)
+    p1 = p - lr * (mhat / (np.sqrt(vhat) + eps) + weight_decay * p)
+    return p1, m1, v1

@@ -421,3 +421,71 @@ def test_generator_is_deterministic():
     assert inputs.checksums(a) == inputs.checksums(b)
     c = inputs.generate(configs.C1, 1, threads=1)
     assert inputs.checksums(a)["x"] != inputs.checksums(c)["x"]
+
+
+# ----------------------------------------------- adapter optimizer (AdamW) --
+# The pages put the optimizer state on the adapters only (skill card,
+# Principle 3 "TQP Optimizer Strategy"); the optimizer itself is read as
+# AdamW (decoupled weight decay, bias-corrected moments).
+
+ADAMW_HP = dict(lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.05)
+
+
+def test_adamw_first_step_is_sign_step():
+    # from zero moments at t = 1 the bias corrections cancel exactly:
+    # m_hat = g, v_hat = g^2, so the step is lr * g / (|g| + eps) + decay
+    rng = np.random.default_rng(7)
+    p, g = rng.standard_normal(1000), rng.standard_normal(1000)
+    z = np.zeros(1000)
+    p1, m1, v1 = oracle.adamw_step(p, g, z, z, step=1, **ADAMW_HP)
+    hp = ADAMW_HP
+    np.testing.assert_allclose(m1, (1 - hp["beta1"]) * g, rtol=1e-15)
+    np.testing.assert_allclose(v1, (1 - hp["beta2"]) * g * g, rtol=1e-15)
+    want = p - hp["lr"] * (np.sign(g) * np.abs(g) / (np.abs(g) + hp["eps"]) + hp["weight_decay"] * p)
+    np.testing.assert_allclose(p1, want, rtol=1e-13, atol=1e-15)
+
+
+def test_adamw_constant_gradient_closed_form():
+    # with a constant gradient, m_t = (1 - beta1^t) g and v_t = (1 - beta2^t)
+    # g^2, so every bias-corrected step is the same: p_t = p_0 - t lr g/(|g|+eps)
+    # (no weight decay); a wrong power of beta or step index breaks this
+    rng = np.random.default_rng(8)
+    p0, g = rng.standard_normal(64), rng.standard_normal(64)
+    p, m, v = p0.copy(), np.zeros(64), np.zeros(64)
+    hp = dict(ADAMW_HP, weight_decay=0.0)
+    for t in range(1, 41):
+        p, m, v = oracle.adamw_step(p, g, m, v, step=t, **hp)
+        np.testing.assert_allclose(m, (1 - hp["beta1"] ** t) * g, rtol=1e-12)
+        np.testing.assert_allclose(v, (1 - hp["beta2"] ** t) * g * g, rtol=1e-12)
+    np.testing.assert_allclose(p, p0 - 40 * hp["lr"] * g / (np.abs(g) + hp["eps"]), rtol=1e-11,
+                               atol=1e-13)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    p = np.linspace(-2, 2, 17)
+    z = np.zeros(17)
+    p1, m1, v1 = oracle.adamw_step(p, z, z, z, step=3, **ADAMW_HP)
+    assert np.all(m1 == 0) and np.all(v1 == 0)
+    np.testing.assert_allclose(p1, p * (1 - ADAMW_HP["lr"] * ADAMW_HP["weight_decay"]), rtol=1e-15)
+
+
+def test_adamw_matches_torch_adamw_float64():
+    # the library routine torch.optim.AdamW (decoupled weight decay, on the
+    # CPU in float64) over several steps of random gradients
+    import torch
+    rng = np.random.default_rng(9)
+    p0 = rng.standard_normal((5, 7))
+    grads = [rng.standard_normal((5, 7)) for _ in range(6)]
+    hp = ADAMW_HP
+    tp = torch.nn.Parameter(torch.tensor(p0, dtype=torch.float64))
+    opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"], foreach=False)
+    p, m, v = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    for t, g in enumerate(grads, start=1):
+        tp.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        p, m, v = oracle.adamw_step(p, g, m, v, step=t, **hp)
+    st = opt.state[tp]
+    np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-15)
