@@ -9,8 +9,8 @@ State-Preserving Scaling", abstract; hidden sizes are this library's).
 
 Prints one JSON line.  `value` is tokens/s of the timed steps with every input
 already resident in device memory.  `roofline` reports the gate/up expert GEMM
-(the dominant kernel) against the bf16 matrix-core peak, timed with HIP events
-on its own launch stream; `cpu_baseline` times the fp64 oracle on a bounded
+(the dominant kernel; one launch per tile class, timed together) against the
+bf16 matrix-core peak, timed with HIP events on its own launch stream; `cpu_baseline` times the fp64 oracle on a bounded
 sample of the same workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -165,6 +165,26 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # adapter optimizer step (AdamW over the six adapters through
+    # moe_adamw_step), timed on its own after the layer steps
+    adamw = None
+    if cfg.train:
+        L.init_optimizer()
+        for _ in range(2):
+            L.optimizer_step()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            L.optimizer_step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        opt_ms = ev0.elapsed_time(ev1) / args.steps
+        n_par = sum(t[0].numel() for t in L.opt.values())
+        nbytes = n_par * (16 + 12 + 2)   # read p, g, m, v; write p, m, v and the bf16 copy
+        adamw = {"ms": opt_ms, "params": n_par, "bytes": nbytes,
+                 "GB_s": nbytes / (opt_ms / 1e3) / 1e9, "frac_hbm": nbytes / (opt_ms / 1e3) / PEAK_HBM}
+        log(f"adamw {opt_ms:.3f} ms for {n_par} adapter parameters")
+
     per_launch_ms = k_ms / max(1, k_launches)
     launches_per_step = k_launches / args.steps
     flops_launch = gateup_flops(cfg) / launches_per_step
@@ -191,12 +211,14 @@ def main():
                    "router_bias_var": cfg.router_bias_var},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
-                     "traffic": traffic, "kernel": "gate/up expert GEMM",
+                     "traffic": traffic,
+                     "kernel": "gate/up expert GEMM (one launch per tile class: 128/96/64/32 rows)",
                      "kernel_ms": per_launch_ms, "launches_per_step": launches_per_step,
                      "flops_per_launch": flops_launch},
         "layer_tflops": layer_flops(cfg, cfg.train) / (ms / 1e3) / 1e12,
         "layer_frac_of_bf16_peak": layer_flops(cfg, cfg.train) / (ms / 1e3) / PEAK_BF16,
         "forward_ms": fwd_ms,
+        "adamw": adamw,
         "forward_tokens_per_s": cfg.T / (fwd_ms / 1e3),
         "load": {"max": int(counts.max()), "mean": float(counts.mean()),
                  "empty_experts": int((counts == 0).sum())},

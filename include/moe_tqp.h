@@ -185,6 +185,36 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
                            float *dA_down, float *dB_down, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* Adapter optimizer step: AdamW on one float32 tensor of n elements (call it
+ * once per adapter tensor: A and B of gate, up and down).  The optimizer
+ * state lives on the adapters only, the quantized base being fixed (skill
+ * card "Reversible Sparse MoE Single Node", Principle 3 "TQP Optimizer
+ * Strategy" and Pattern 3).  The pages name no optimizer; this library reads
+ * it as AdamW ("Decoupled Weight Decay Regularization", Loshchilov and
+ * Hutter): with t = step,
+ *   m <- beta1 m + (1 - beta1) g,   v <- beta2 v + (1 - beta2) g^2,
+ *   master <- master - lr ( (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *                           + weight_decay master )
+ * in float32 (the bias corrections 1 - beta^t are formed in double on the
+ * host).  Elementwise; master, m, v are updated in place.
+ *   master  f32 [n]  float32 master copy of the adapter (in/out)
+ *   grad    f32 [n]  its gradient, e.g. dA_gate of moe_adapter_bwd (layouts
+ *                    of A and B, so any flat order works)
+ *   m, v    f32 [n]  first and second moments (in/out; zero before step 1)
+ *   param   NULL, or [n] in param_dtype (MOE_F32 or MOE_BF16, rounded to
+ *           nearest even): a copy of the new master, e.g. the act-dtype
+ *           adapter that moe_expert_fwd reads (out)
+ * The four float32 buffers must be distinct (param may not alias them).
+ * Validation: step >= 1, beta1, beta2 in [0, 1), eps finite and > 0, lr and
+ * weight_decay finite, n >= 0 (n = 0 enqueues nothing). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t step;
+} moe_adamw_hparams;
+moe_status moe_adamw_step(const moe_adamw_hparams *h, int64_t n, float *master,
+                          const float *grad, float *m, float *v, void *param,
+                          int32_t param_dtype, void *stream);
+
 /* Instrumentation, not part of the method: time every launch of one internal
  * kernel with a pair of HIP events recorded on the launch stream around it.
  * moe_timer_start arms the calling thread for `tag` (one of moe_kernel_tag;
@@ -193,7 +223,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
  * disarms.  Events are created on the first use and reused; the state is
  * thread-local. */
 typedef enum {
-  MOE_KT_ROUTER_LOGITS = 0, /* router GEMM (vector ALU)                    */
+  MOE_KT_ROUTER_LOGITS = 0, /* router GEMM (float32 matrix cores)          */
   MOE_KT_ROUTER_TOPK = 1,   /* partial sum, top-k, softmax                  */
   MOE_KT_PERMUTE = 2,       /* scatter of the permutation                   */
   MOE_KT_GATEUP = 3,        /* gate/up expert GEMM with SwiGLU epilogue     */

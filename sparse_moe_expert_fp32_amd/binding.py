@@ -34,6 +34,12 @@ class QLora(ctypes.Structure):
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
 
 
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise MoeError(f"{LIB_PATH} is missing: build it with "
@@ -55,6 +61,7 @@ def _load():
         "moe_abi_version": [],
         "moe_timer_start": [I32],
         "moe_timer_stop": [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)],
+        "moe_adamw_step": [ctypes.POINTER(AdamWHparams), ctypes.c_int64, P, P, P, P, P, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -68,7 +75,7 @@ def _load():
 LIB = _load()
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
-           "moe_abi_version", "moe_timer_start", "moe_timer_stop")
+           "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step")
 
 # kernel tags of moe_timer_start (moe_kernel_tag)
 KT = {"router_logits": 0, "router_topk": 1, "permute": 2, "gateup": 3, "down": 4, "combine": 5,
@@ -169,3 +176,17 @@ def moe_adapter_bwd(dm, dy, x, topk_idx, gates, offsets, perm_src, slot_pos, w_r
                                _p(dA_up), _p(dB_up), _p(dA_down), _p(dB_down), _p(ws),
                                ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_adapter_bwd")
+
+
+def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step) -> AdamWHparams:
+    return AdamWHparams(lr, beta1, beta2, eps, weight_decay, step)
+
+
+def moe_adamw_step(h: AdamWHparams, master, grad, m, v, param=None, stream=None):
+    if param is None:
+        pdt = MOE_F32
+    else:
+        pdt = MOE_BF16 if param.dtype == torch.bfloat16 else MOE_F32
+    n = master.numel()
+    _check(LIB.moe_adamw_step(ctypes.byref(h), n, _p(master), _p(grad), _p(m), _p(v), _p(param),
+                              pdt, _stream(stream)), "moe_adamw_step")

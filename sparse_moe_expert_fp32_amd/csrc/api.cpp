@@ -339,6 +339,37 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
   return hip_status("moe_permute");
 }
 
+moe_status moe_adamw_step(const moe_adamw_hparams *h, int64_t n, float *master,
+                          const float *grad, float *m, float *v, void *param, int32_t param_dtype,
+                          void *stream) {
+  REQUIRE(h, "moe_adamw_step: hparams is NULL");
+  REQUIRE(n >= 0, "moe_adamw_step: n must be >= 0");
+  REQUIRE(h->step >= 1, "moe_adamw_step: step must be >= 1");
+  REQUIRE(std::isfinite(h->lr) && std::isfinite(h->weight_decay),
+          "moe_adamw_step: lr and weight_decay must be finite");
+  REQUIRE(h->beta1 >= 0.f && h->beta1 < 1.f && h->beta2 >= 0.f && h->beta2 < 1.f,
+          "moe_adamw_step: beta1 and beta2 must be in [0, 1)");
+  REQUIRE(std::isfinite(h->eps) && h->eps > 0.f, "moe_adamw_step: eps must be finite and > 0");
+  if (param && param_dtype != MOE_F32 && param_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_adamw_step: param_dtype must be MOE_F32 or MOE_BF16");
+  if (n == 0) return MOE_OK;
+  REQUIRE(master && grad && m && v, "moe_adamw_step: master, grad, m and v are required");
+  REQUIRE((const void *)grad != master && (const void *)grad != m && (const void *)grad != v &&
+              master != m && master != v && m != v,
+          "moe_adamw_step: master, grad, m and v must be distinct buffers");
+  moe::AdamWArgs a{};
+  a.n = (size_t)n;
+  a.p = master; a.g = grad; a.m = m; a.v = v; a.out = param;
+  a.lr = h->lr; a.beta1 = h->beta1; a.beta2 = h->beta2; a.eps = h->eps;
+  a.weight_decay = h->weight_decay;
+  // bias corrections in double, once per call
+  a.bc1 = (float)(1.0 - std::pow((double)h->beta1, (double)h->step));
+  a.bc2 = (float)(1.0 - std::pow((double)h->beta2, (double)h->step));
+  REQUIRE(a.bc1 > 0.f && a.bc2 > 0.f, "moe_adamw_step: 1 - beta^step underflows to 0");
+  moe::launch_adamw(a, !param ? 0 : param_dtype == MOE_F32 ? 1 : 2, (hipStream_t)stream);
+  return hip_status("moe_adamw_step");
+}
+
 moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *slot_pos,
                        const float *gates, void *y, void *ws, size_t ws_bytes, void *stream) {
   (void)ws;

@@ -137,4 +137,15 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st);
 
+// ---- adapter optimizer step (adamw.hip)
+struct AdamWArgs {
+  size_t n;
+  float *p; const float *g; float *m, *v;   // master parameter, gradient, moments
+  void *out;                                 // copy of the new parameter, or null
+  float lr, beta1, beta2, eps, weight_decay;
+  float bc1, bc2;                            // 1 - beta1^t, 1 - beta2^t
+};
+// out_kind: 0 none, 1 float32 copy, 2 bf16 copy
+void launch_adamw(const AdamWArgs &h, int out_kind, hipStream_t st);
+
 }  // namespace moe

@@ -101,6 +101,28 @@ class DeviceLayer:
         self.forward(stream)
         self.adapter_bwd(stream)
 
+    # ---- adapter optimizer (AdamW through moe_adamw_step)
+    ADAPTERS = (("dA_gate", "A_gate"), ("dB_gate", "B_gate"), ("dA_up", "A_up"),
+                ("dB_up", "B_up"), ("dA_down", "A_down"), ("dB_down", "B_down"))
+
+    def init_optimizer(self):
+        """float32 master copies of the six adapters and zero moments."""
+        self.opt = {}
+        for gname, pname in self.ADAPTERS:
+            master = self.t[pname].float().contiguous()
+            self.opt[pname] = (master, torch.zeros_like(master), torch.zeros_like(master))
+        self.opt_step = 0
+
+    def optimizer_step(self, lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0,
+                       stream=None):
+        """One AdamW step on every adapter; the act-dtype adapters that the
+        forward reads are rewritten from the updated masters."""
+        self.opt_step += 1
+        h = B.adamw_hparams(lr, beta1, beta2, eps, weight_decay, self.opt_step)
+        for gname, pname in self.ADAPTERS:
+            master, m, v = self.opt[pname]
+            B.moe_adamw_step(h, master, self.grads[gname], m, v, self.t[pname], stream)
+
     # ---- results on the host
     def routing(self) -> dict:
         out = {n: to_numpy(getattr(self, n)) for n in

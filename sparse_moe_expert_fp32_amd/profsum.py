@@ -6,7 +6,8 @@
 
 `trace` turns a --kernel-trace --stats kernel_stats.csv into a markdown table.
 `traffic` takes two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
-averages them per dispatch of the kernel, and scales each by the ratio between
+averages them per dispatch of each kernel the pattern matches, sums those (the
+launches of one stage), and scales each by the ratio between
 the known size of a device-to-device copy and what the same counter read for
 that copy (the copy kernel reads and writes exactly copy-bytes).
 """
@@ -19,7 +20,13 @@ import re
 from collections import defaultdict
 
 
-def trace(stats_csv: str, out_md: str, cmd: str, top: int = 25):
+# kernels launched together as one stage of the layer (one launch per tile
+# class); the trace summary adds a line with their summed average per stage
+STAGES = {"gate/up expert GEMM (grouped_gemm_kernel<0, ...>, all tile classes)": r"grouped_gemm_kernel<0,",
+          "down expert GEMM (grouped_gemm_kernel<1, ...>, all tile classes)": r"grouped_gemm_kernel<1,"}
+
+
+def trace(stats_csv: str, out_md: str, cmd: str, top: int = 30):
     rows = list(csv.DictReader(open(stats_csv)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     lines = [f"# Kernel trace summary", "", f"Command: `{cmd}`", "",
@@ -30,6 +37,12 @@ def trace(stats_csv: str, out_md: str, cmd: str, top: int = 25):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / total * 100:.1f}% |")
+    lines += ["", "Per-stage sums (average of each launch in the stage, added):", ""]
+    for label, rx in STAGES.items():
+        sel = [r for r in rows if re.search(rx, r["Name"])]
+        if sel:
+            us = sum(float(r["AverageNs"]) for r in sel) / 1e3
+            lines.append(f"- {label}: {us:.1f} us ({len(sel)} launches)")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -49,7 +62,11 @@ def traffic(fetch_csv, write_csv, out_json, kernel, copy_bytes, flops_per_launch
     pick = lambda d, rx: next(v for k, v in d.items() if re.search(rx, k))
     copy_rx = r"copyBuffer"
     mean = lambda v: sum(v) / len(v)
-    kf, kw = mean(pick(f, kernel)), mean(pick(w, kernel))
+    # every kernel name the pattern matches is one launch of the stage (one
+    # per tile class): per-dispatch means, summed over the launches
+    allm = lambda d, rx: [v for k, v in d.items() if re.search(rx, k)]
+    kf = sum(mean(v) for v in allm(f, kernel))
+    kw = sum(mean(v) for v in allm(w, kernel))
     # the probe is the largest copy dispatch (the others are small uploads)
     cf, cw = max(pick(f, copy_rx)), max(pick(w, copy_rx))
     f_scale = copy_bytes / (cf * 1024.0)

@@ -114,3 +114,30 @@ def test_status_strings(B):
     assert B.LIB.moe_status_string(0) == b"MOE_OK"
     assert B.LIB.moe_status_string(-3) == b"MOE_ERR_WORKSPACE"
     assert B.LIB.moe_status_string(-99) == b"MOE_ERR_UNKNOWN"
+
+
+# ---- adapter optimizer step: host-side validation (nothing reaches the GPU)
+
+def adamw_call(B, n=16, ptrs=(0x1000, 0x2000, 0x3000, 0x4000), param=None, pdt=0, **kw):
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+    hp.update(kw)
+    h = B.adamw_hparams(**hp)
+    return B.LIB.moe_adamw_step(ctypes.byref(h), n, *ptrs, param, pdt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(step=0), -1), (dict(beta1=1.0), -1), (dict(beta2=-0.1), -1), (dict(eps=0.0), -1),
+    (dict(eps=float("nan")), -1), (dict(lr=float("inf")), -1),
+    (dict(weight_decay=float("nan")), -1), (dict(n=-1), -1),
+    (dict(ptrs=(None, 0x2000, 0x3000, 0x4000)), -1),
+    (dict(ptrs=(0x1000, 0x1000, 0x3000, 0x4000)), -1),
+    (dict(ptrs=(0x1000, 0x2000, 0x3000, 0x3000)), -1),
+    (dict(param=0x5000, pdt=7), -2),
+])
+def test_adamw_rejects_bad_arguments(B, kw, status):
+    assert adamw_call(B, **kw) == status
+    assert B.LIB.moe_last_error().decode().startswith("moe_adamw_step")
+
+
+def test_adamw_empty_tensor_is_a_no_op(B):
+    assert adamw_call(B, n=0, ptrs=(None, None, None, None)) == 0
