@@ -155,7 +155,7 @@ struct BwdLayout {
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
     tiles_m = mf ? c.take(max_tiles(d, moe::mfma_t_tile_rows()) * sizeof(int2)) : 0;
-    ntiles_m = mf ? c.take(sizeof(int)) : 0;
+    ntiles_m = mf ? c.take(8 * sizeof(int)) : 0;
     tiles_p = mf ? c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2)) : 0;
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
@@ -539,7 +539,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     const int grid = persistent_grid(moe::mfma_t_blocks_per_cu());
     const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
-    moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st);
+    moe::launch_class_tiles(offsets, E, tiles_m, ntiles_m, st);
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     uint16_t *bt_d = at<uint16_t>(ws, L.bt);
     uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
@@ -570,13 +570,13 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::launch_wgrad_mfma(W, mtw, false, st);
     // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
     moe::MfmaGemmTArgs M{};
-    M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.ntiles = ntiles_m; M.offsets = offsets;
+    M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.offsets = offsets;
     M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qt0; M.st0 = st0;
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
     moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
-    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, grid, st));
+    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
@@ -599,7 +599,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::launch_wgrad_mfma(W, mtw, true, st);
     // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
     moe::MfmaGemmTArgs X{};
-    X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m; X.ntiles = ntiles_m;
+    X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m;
     X.offsets = offsets; X.K = f; X.N = d; X.NT = (d + 255) / 256;
     X.qt0 = qt0; X.st0 = st0; X.qt1 = qt1; X.st1 = st1;
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
@@ -607,7 +607,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.out = (uint16_t *)dXp; X.ldo = d;
     moe::launch_transpose_q(gate.q, gate.scale, offsets, E, f, d, qt0, st0, st);
     moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
-    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, grid, st));
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, ntiles_m, grid, st));
     moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
     return hip_status("moe_adapter_bwd");
   }

@@ -125,7 +125,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
   };
   // a 3-deep ring of half-group stages; after the K loop the first 4 KB of
   // the A ring hold the cross-wave row sums of H.
-  __shared__ uint4 ringA[3][ST_A / 16];
+  // (ringA 32-byte aligned: the second substep's chunk is the first's
+  // address with bit 4 flipped)
+  __shared__ __attribute__((aligned(32))) uint4 ringA[3][ST_A / 16];
   __shared__ uint4 ringB[3][ST_B / 16];
   __shared__ float ringX[3][ST_X / 4];
   __shared__ int tok_lds[GM_BM];
@@ -241,7 +243,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
         for (int i = 0; i < XOPS; ++i) dma4(xbase[i] + g, xoff[i], sx + slot * ST_X + i * 256);
       }
     };
-    constexpr int kOpsOdd = AOPS + BOPS, kOpsEven = kOpsOdd + XOPS;
 
     f32x4_t acc[NM][NF];
 #pragma unroll
@@ -294,37 +295,36 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
       }
     };
 
-    // 3-deep pipeline: stage j computes from ring slot j % 3 while the loads
-    // of stages j + 1 and j + 2 are in flight.  Every wave issues the same
-    // number of LDS-DMA per stage (kOpsEven for a group's first stage,
-    // kOpsOdd for its second), so "stage j + 1 has landed" is a vmcnt of the
-    // count of stage j + 2, which has the parity of j.  The loop runs in
-    // groups of six stages (three ring slots, two parities); stages past the
-    // end compute nothing (uniform branch) but still issue their (clamped)
-    // loads, so every wait is alike.
+    // 3-deep ring: step j computes from slot j % 3 while the loads of stage
+    // j + 2 (issued at the start of the step) are in flight; at the end of
+    // the step every wave waits for all of its loads and the block syncs, so
+    // stage j + 1 is in LDS when step j + 1 starts and slot j % 3 is free for
+    // stage j + 3.  The loop runs in groups of six stages (three ring slots,
+    // two parities); stages past the end compute nothing (uniform branch)
+    // but still issue their (clamped) loads.
     using even_t = std::integral_constant<bool, false>;
     using odd_t = std::integral_constant<bool, true>;
     using ev_t = std::integral_constant<bool, true>;
     using od_t = std::integral_constant<bool, false>;
     stage(ev_t(), 0, 0);
     stage(od_t(), 1, 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOpsOdd));
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
     block_barrier();
     for (int j = 0; j < NS; j += 6) {
-#define MOE_F_STEP(JJ, PAR, LD, OPS, CUR, NXT)  \
+#define MOE_F_STEP(JJ, PAR, LD, CUR, NXT)       \
   {                                             \
     const int jj = (JJ);                        \
     stage(LD(), jj + 2, NXT);                   \
     if (jj < NS) compute(PAR(), CUR);           \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS)); \
+    __builtin_amdgcn_s_waitcnt(kWaitVm); \
     block_barrier();                            \
   }
-      MOE_F_STEP(j, even_t, ev_t, kOpsEven, 0, 2)
-      MOE_F_STEP(j + 1, odd_t, od_t, kOpsOdd, 1, 0)
-      MOE_F_STEP(j + 2, even_t, ev_t, kOpsEven, 2, 1)
-      MOE_F_STEP(j + 3, odd_t, od_t, kOpsOdd, 0, 2)
-      MOE_F_STEP(j + 4, even_t, ev_t, kOpsEven, 1, 0)
-      MOE_F_STEP(j + 5, odd_t, od_t, kOpsOdd, 2, 1)
+      MOE_F_STEP(j, even_t, ev_t, 0, 2)
+      MOE_F_STEP(j + 1, odd_t, od_t, 1, 0)
+      MOE_F_STEP(j + 2, even_t, ev_t, 2, 1)
+      MOE_F_STEP(j + 3, odd_t, od_t, 0, 2)
+      MOE_F_STEP(j + 4, even_t, ev_t, 1, 0)
+      MOE_F_STEP(j + 5, odd_t, od_t, 2, 1)
 #undef MOE_F_STEP
     }
 

@@ -37,6 +37,7 @@ namespace moe {
 
 constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 64, GT_BPC = 2;   // GT_BPC: blocks per CU
 
+
 // ------------------------------------------------------------ transpose --
 // q: [E][R][C/2] (packed along C), s: [E][R][C/128] bf16  ->
 // qt: [E][R/64][C][32 bytes] (each column's run of 64 storage rows as 8 words,
@@ -89,6 +90,12 @@ __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restr
   }
 }
 
+// One pipeline stage in LDS, one array per kind (each read is a per-lane base
+// register plus a compile-time offset): A rows (128 x 64 bf16, 16-byte chunks
+// XOR-swizzled by row), int4 words (256 columns x 32 bytes), the scales of the
+// stage's 64 reduction steps for the block's two column groups.
+constexpr int TS_A = GT_BM * GT_KS * 2, TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;
+
 // ------------------------------------------------------------------ GEMM --
 // A bf16x8 fragment times 8 per-k scales, rounded back to bf16.
 DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
@@ -100,25 +107,28 @@ DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
   return r;
 }
 
-
-template <int MODE>
-__global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaGemmTArgs A) {
-  // a 3-deep ring of stages, each with its A rows, int4 words and scales
-  // (filled by LDS-DMA issued from inline asm, with explicit waits)
-  __shared__ __attribute__((aligned(16))) bf16_t al0[GT_BM * GT_KS];
-  __shared__ __attribute__((aligned(16))) bf16_t al1[GT_BM * GT_KS];
-  __shared__ __attribute__((aligned(16))) bf16_t al2[GT_BM * GT_KS];
-  __shared__ __attribute__((aligned(16))) uint8_t bl0[GT_BN * GT_KS / 2];
-  __shared__ __attribute__((aligned(16))) uint8_t bl1[GT_BN * GT_KS / 2];
-  __shared__ __attribute__((aligned(16))) uint8_t bl2[GT_BN * GT_KS / 2];
-  __shared__ __attribute__((aligned(16))) float sl0[2 * GT_KS];
-  __shared__ __attribute__((aligned(16))) float sl1[2 * GT_KS];
-  __shared__ __attribute__((aligned(16))) float sl2[2 * GT_KS];
+// NMH: row fragments of 16 per wave; the item's tile class has 32 NMH rows
+// (128, 96, 64, 32), each class its own launch.  Waves 2 x 2: wave (wm, wn)
+// takes rows 16 NMH wm .. + 16 NMH and the 128 columns of column group wn.
+// Products are formed transposed (D^T = W^T A^T: the unpacked weights are the
+// first MFMA operand) so a lane holds one row and four consecutive columns and
+// the epilogue reads G, U and writes its results 8 bytes at a time.
+template <int MODE, int NMH>
+__global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
+    const MfmaGemmTArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
+  // a 3-deep ring of stages (filled by LDS-DMA issued from inline asm, with
+  // explicit waits)
+  // (ringA 32-byte aligned: the second substep's chunk is the first's
+  // address with bit 4 flipped)
+  __shared__ __attribute__((aligned(32))) uint4 ringA[3][TS_A / 16];
+  __shared__ uint4 ringB[3][TS_B / 16];
+  __shared__ float ringS[3][TS_S / 4];
+  constexpr int AOPS = NMH;   // 8-row A loads per wave and stage
 
   const int Kh = A.K, N = A.N, G = N / 128;
   const int NKh = Kh / GT_KS;
   const int NK = MODE == 1 ? 2 * NKh : NKh;   // mode 1 reduces over [dG | dU]
-  const int total = A.ntiles[0] * A.NT;
+  const int total = cls_count[0] * A.NT, tbase = cls_start[0];
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int wbeg = (int)(((long long)total * xcd) >> 3);
   const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
@@ -128,6 +138,7 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
   const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t kMagic;
   asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(kMagic));
+  const uint32_t ldsA = lds_addr(ringA), ldsB = lds_addr(ringB), ldsS = lds_addr(ringS);
 
   for (int wi = wbeg + bi; wi < wend; wi += nper) {
     int tid = threadIdx.x;
@@ -136,20 +147,21 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
     const int lr = lane & 15, lg = lane >> 4;
     const int wm = w & 1, wn = w >> 1;
     const int ti = wi / A.NT, nt = wi - ti * A.NT;
-    const int2 tile = A.tiles[ti];
+    const int2 tile = A.tiles[tbase + ti];
     const int e = tile.x, p0 = tile.y;
-    const int rows = min(GT_BM, A.offsets[e + 1] - p0);
+    const int rows = min(32 * NMH, A.offsets[e + 1] - p0);
     const int c0 = nt * GT_BN;
 
-    // A staging: wave w, op i covers rows 8 (4w + i) .. +7 (8 chunks of 16 B each)
-    uint32_t aoff[4];
+    // A staging: wave w, load i covers rows 8 (AOPS w + i) .. +7 (8 chunks of
+    // 16 B each); chunk c of row r lives at c ^ (r & 7)
+    uint32_t aoff[AOPS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * (w * 4 + i) + (lane >> 3);
+    for (int i = 0; i < AOPS; ++i) {
+      const int r = 8 * (w * AOPS + i) + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);
       aoff[i] = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.lda * 2) + c * 16;
     }
-    // int4 staging: wave w, op i covers columns 32 (2w + i) .. +31, 32 bytes each
+    // int4 staging: wave w, load i covers columns 32 (2w + i) .. +31, 32 bytes each
     uint32_t boff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -159,61 +171,68 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
     // scale staging: wave w, lanes < 32: column group (w >> 1), k 32 (w & 1) + lane
     const int sg = min(c0 / 128 + (w >> 1), G - 1);
     const int sk = 32 * (w & 1) + lane;
-    // this wave's LDS destinations within a stage (wave-uniform byte offsets)
-    const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
-    const uint32_t la = wu * 4 * 1024, lb = wu * 2 * 1024,
-                   ls = ((wu >> 1) * GT_KS + 32 * (wu & 1)) * 4;
     const uint32_t soff = (uint32_t)(sg * Kh + sk) * 4u;
-    auto stage = [&](int jr, bf16_t *abuf, uint8_t *bbuf, float *sbuf) {
+    // this wave's LDS-DMA destinations within a stage (wave-uniform)
+    const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t la = ldsA + wu * AOPS * 1024, lb = ldsB + wu * 2 * 1024,
+                   ls = ldsS + ((wu >> 1) * GT_KS + 32 * (wu & 1)) * 4;
+    // per-lane LDS read bases (bytes); the rest of every read address is a
+    // compile-time constant
+    const uint32_t offA0 = opaque(ldsA + (16 * NMH * wm + lr) * 128 + (((2 * lg) ^ (lr & 7)) << 4)),
+                   offB = opaque(ldsB + (128 * wn + lr) * 32 + 8 * lg),
+                   offS = opaque(ldsS + (wn * GT_KS + 16 * lg) * 4);
+
+    auto stage = [&](int jr, int slot) {
       const int j = min(jr, NK - 1);   // past the end: a harmless copy of the last step
       const bool second = MODE == 1 && j >= NKh;
       const int kj = second ? j - NKh : j;
       const char *abase = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
       const uint32_t koff = (uint32_t)kj * GT_KS * 2;
+      // destinations re-derived per stage (scalar adds) rather than held
+      uint32_t sa = la, sb = lb, ss = ls;
+      asm volatile("" : "+s"(sa), "+s"(sb), "+s"(ss));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(abase + koff, aoff[i], lds_addr(abuf) + la + i * 1024);
+      for (int i = 0; i < AOPS; ++i) dma16(abase + koff, aoff[i], sa + slot * TS_A + i * 1024);
       const uint8_t *qb = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(qb, boff[i], lds_addr(bbuf) + lb + i * 1024);
+      for (int i = 0; i < 2; ++i) dma16(qb, boff[i], sb + slot * TS_B + i * 1024);
       const float *sp = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
-      if (lane < 32) dma4(sp, soff, lds_addr(sbuf) + ls);
+      if (lane < 32) dma4(sp, soff, ss + slot * TS_S);
     };
 
-    f32x4_t acc[4][8], corr[4];
+    f32x4_t acc[NMH][8], corr[NMH];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < NMH; ++m) {
       corr[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nf = 0; nf < 8; ++nf) acc[m][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // one 64-deep step: 2 k-substeps x 4 row fragments x (8 + 1) MFMAs.
+    // one 64-deep step: 2 k-substeps x NMH row fragments x (8 + 1) MFMAs.
     // Lane group lg takes k = 16 lg + 8 s .. + 7 in substep s (A chunk
     // 2 lg + s, int4 word 2 lg + s), the same permutation on both operands.
-    auto compute = [&](const bf16_t *abuf, const uint8_t *bbuf, const float *sbuf) {
+    auto compute = [&](int slot) {
       __builtin_amdgcn_sched_barrier(0);
-      uint2 bw[8];
+      u32x2_t bw[8];
 #pragma unroll
-      for (int nf = 0; nf < 8; ++nf)
-        bw[nf] = *reinterpret_cast<const uint2 *>(bbuf + (128 * wn + 16 * nf + lr) * 32 + 8 * lg);
+      for (int nf = 0; nf < 8; ++nf) bw[nf] = lds_ld<u32x2_t>(offB + slot * TS_B + nf * 16 * 32);
+      // substep 1 reads chunk 2 lg + 1, the neighbouring swizzled chunk
+      const uint32_t offA1 = offA0 ^ 16u;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         float sc[8];
         {
-          const float4 s0 = *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 16 * lg + 8 * s);
-          const float4 s1 =
-              *reinterpret_cast<const float4 *>(sbuf + wn * GT_KS + 16 * lg + 8 * s + 4);
-          sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
-          sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+          const f32x4_t s0 = lds_ld<f32x4_t>(offS + slot * TS_S + 32 * s);
+          const f32x4_t s1 = lds_ld<f32x4_t>(offS + slot * TS_S + 32 * s + 16);
+          sc[0] = s0[0]; sc[1] = s0[1]; sc[2] = s0[2]; sc[3] = s0[3];
+          sc[4] = s1[0]; sc[5] = s1[1]; sc[6] = s1[2]; sc[7] = s1[3];
         }
-        uint4 av[4];
+        uint4 av[NMH];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = 64 * wm + 16 * m + lr;
-          const uint4 araw = *reinterpret_cast<const uint4 *>(
-              abuf + r * GT_KS + (((2 * lg + s) ^ (r & 7)) << 3));
-          av[m] = scale_frag(araw, sc);
-          corr[m] = mfma32(av[m], c136, corr[m]);
+        for (int m = 0; m < NMH; ++m) {
+          const u32x4_t a4 = lds_ld<u32x4_t>((s ? offA1 : offA0) + slot * TS_A + m * 2048);
+          av[m] = scale_frag(make_uint4(a4.x, a4.y, a4.z, a4.w), sc);
+          corr[m] = mfma32(c136, av[m], corr[m]);
         }
 #pragma unroll
         for (int nf = 0; nf < 8; ++nf) {
@@ -224,138 +243,121 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
           bu.z = __builtin_amdgcn_bitop3_b32(x >> 8, kMask, kMagic, 0x6A);
           bu.w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[m][nf] = mfma32(av[m], bu, acc[m][nf]);
+          for (int m = 0; m < NMH; ++m) acc[m][nf] = mfma32(bu, av[m], acc[m][nf]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // 3-deep pipeline: step j computes from ring slot j % 3 while the loads
-    // of steps j + 1 and j + 2 are in flight.  Per thread and step: 4 + 2 + 1
-    // LDS-DMA (the same count in every wave), so "step j + 1 has landed" is
-    // vmcnt(7).  The loop runs in groups of three steps; steps past the end
-    // compute nothing (uniform branch) but still issue their loads, clamped to
-    // the last real step (cache hits into a slot nobody reads), so that every
-    // wait is the same and the compiler's own wait tracking stays exact.
-    constexpr int kOps = 7;
+    // 3-deep ring: step j computes from slot j % 3 while the loads of step
+    // j + 2 (issued at the start of the step) are in flight; at the end of the
+    // step every wave waits for all of its loads and the block syncs.  The
+    // loop runs in groups of three steps; steps past the end compute nothing
+    // (uniform branch) but still issue their loads, clamped to the last real
+    // step.
     __syncthreads();  // LDS of the previous item is free
-    stage(0, al0, bl0, sl0);
-    stage(1, al1, bl1, sl1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
+    stage(0, 0);
+    stage(1, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
     block_barrier();
     for (int j = 0; j < NK; j += 3) {
-#define MOE_T_STEP(JJ, CA, CB, CS, NA, NB, NS)              \
-  {                                                         \
-    const int jj = (JJ);                                    \
-    stage(jj + 2, NA, NB, NS);                              \
-    if (jj < NK) compute(CA, CB, CS);                       \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));            \
-    block_barrier();                                        \
+#define MOE_T_STEP(JJ, CUR, NXT)                 \
+  {                                              \
+    const int jj = (JJ);                         \
+    stage(jj + 2, NXT);                          \
+    if (jj < NK) compute(CUR);                   \
+    __builtin_amdgcn_s_waitcnt(kWaitVm); \
+    block_barrier();                             \
   }
-      MOE_T_STEP(j, al0, bl0, sl0, al2, bl2, sl2)
-      MOE_T_STEP(j + 1, al1, bl1, sl1, al0, bl0, sl0)
-      MOE_T_STEP(j + 2, al2, bl2, sl2, al1, bl1, sl1)
+      MOE_T_STEP(j, 0, 2)
+      MOE_T_STEP(j + 1, 1, 0)
+      MOE_T_STEP(j + 2, 2, 1)
 #undef MOE_T_STEP
     }
-    // drain the trailing (clamped) loads before the ring is reused below
+    // drain the trailing (clamped) loads before the ring is reused
     __builtin_amdgcn_s_waitcnt(kWaitAll);
-    block_barrier();
 
-    const int cb = c0 + 128 * wn + lr;   // this lane's first output column
+    // ---- epilogue indices, re-derived from an opaque copy of the thread
+    // index: the lane's row in fragment m is rbase + 16 m; its output columns
+    // are ocol + 16 nf .. + 3; col is the column of the A-of-the-matrix
+    // operand lane lr feeds into the adapter product
+    int tid2 = threadIdx.x;
+    asm volatile("" : "+v"(tid2));
+    const int lr2 = tid2 & 15, lg2 = (tid2 >> 4) & 3, wm2 = (tid2 >> 6) & 1, wn2 = tid2 >> 7;
+    const int rbase = 16 * NMH * wm2 + lr2;
+    const int ocol = c0 + 128 * wn2 + 4 * lg2, lcol = c0 + 128 * wn2 + lr2;
 
     // remove the 136 offset of the int4 operand
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < NMH; ++m)
 #pragma unroll
       for (int nf = 0; nf < 8; ++nf) acc[m][nf] -= corr[m];
 
     // adapter term: acc += dZ L with L = A of the matrix ([r][N]), K = rank.
-    // Loads are unconditional (clamped indices) so that they issue together;
-    // rank columns beyond r are zeroed afterwards.
+    // Loads use clamped indices so that they issue together; rank positions
+    // beyond r are zeroed on the L side.
     const int nsrc = MODE == 1 ? 2 : 1;
     for (int src = 0; src < nsrc; ++src) {
       const float *Zp = src ? A.Z1 : A.Z0;
       const uint16_t *Lm = src ? A.L1 : A.L0;
       for (int j0 = 0; j0 < A.r; j0 += 16) {
-        float zv[4][4];
-        uint16_t lv[8][4];
+        uint32_t kmask[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int p = p0 + min(64 * wm + 16 * m + lr, rows - 1);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            zv[m][i] = Zp[(size_t)p * A.ldz + min(j0 + 4 * lg + i, A.r - 1)];
-        }
+        for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg2 + i < A.r ? 0xFFFFu : 0u;
+        short4_t lv[8];
 #pragma unroll
         for (int nf = 0; nf < 8; ++nf) {
-          const int c = min(cb + 16 * nf, N - 1);
+          const int c = min(lcol + 16 * nf, N - 1);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            lv[nf][i] = Lm[((size_t)e * A.r + min(j0 + 4 * lg + i, A.r - 1)) * N + c];
+            lv[nf][i] = (short)(Lm[((size_t)e * A.r + min(j0 + 4 * lg2 + i, A.r - 1)) * N + c] &
+                                kmask[i]);
         }
-        short4_t av[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < NMH; ++m) {
+          const size_t p = (size_t)(p0 + min(rbase + 16 * m, rows - 1));
+          short4_t av;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            av[m][i] = j0 + 4 * lg + i < A.r ? (short)f2bf(zv[m][i]) : (short)0;
+            av[i] = (short)f2bf(Zp[p * A.ldz + min(j0 + 4 * lg2 + i, A.r - 1)]);
 #pragma unroll
-        for (int nf = 0; nf < 8; ++nf) {
-          short4_t bv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bv[i] = j0 + 4 * lg + i < A.r ? (short)lv[nf][i] : (short)0;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) acc[m][nf] = mfma16(av[m], bv, acc[m][nf]);
+          for (int nf = 0; nf < 8; ++nf) acc[m][nf] = mfma16(lv[nf], av, acc[m][nf]);
         }
       }
     }
 
-    // epilogue: per 16-row fragment, through a wave-private 16 x 128 LDS tile
-    // (slot 0 of the ring is free: every wave passed the loop's last barrier)
-    bf16_t *tw = al0 + w * (16 * 128);
-    const bool cols_ok = c0 + 128 * wn < N;   // N is a multiple of 128
-    auto tidx = [](int r, int c) { return r * 128 + (((c >> 3) ^ r) << 3) + (c & 7); };
-    auto flush = [&](int m, uint16_t *dst, int ldo) {
-      // 16 rows x 16 chunks of 8 columns: 4 chunks per lane
+    // epilogue: 8-byte loads of G, U and 8-byte stores of the results
+    const bool cols_ok = c0 + 128 * wn2 < N;   // N is a multiple of 128
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int idx = it * 64 + lane, r = idx >> 4, ch = idx & 15;
-        const int rr = 64 * wm + 16 * m + r;
-        const uint4 v = *reinterpret_cast<const uint4 *>(&tw[r * 128 + ((ch ^ r) << 3)]);
-        if (cols_ok && rr < rows)
-          *reinterpret_cast<uint4 *>(&dst[(size_t)(p0 + rr) * ldo + c0 + 128 * wn + ch * 8]) = v;
-      }
-    };
+    for (int m = 0; m < NMH; ++m) {
+      const int r = rbase + 16 * m;
+      if (!cols_ok || r >= rows) continue;
+      const size_t p = (size_t)(p0 + r);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (MODE == 0) {
-        float du[8][4];
+      for (int nf = 0; nf < 8; ++nf) {
+        const int c = ocol + 16 * nf;
+        const f32x4_t a = acc[m][nf];
+        if (MODE == 0) {
+          const size_t o = p * N + c;
+          const u32x2_t gw = *reinterpret_cast<const u32x2_t *>(&A.G[o]);
+          const u32x2_t uw = *reinterpret_cast<const u32x2_t *>(&A.U[o]);
+          const float gv[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
+                               __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xffff0000u)};
+          const float uv[4] = {__uint_as_float(uw.x << 16), __uint_as_float(uw.x & 0xffff0000u),
+                               __uint_as_float(uw.y << 16), __uint_as_float(uw.y & 0xffff0000u)};
+          float dg[4], du[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 64 * wm + 16 * m + 4 * lg + i;
-          const size_t p = (size_t)(p0 + min(rr, rows - 1));
-#pragma unroll
-          for (int nf = 0; nf < 8; ++nf) {
-            const size_t o = p * N + min(cb + 16 * nf, N - 1);
-            const float dh = acc[m][nf][i];
-            const float gv = bf2f(A.G[o]), uv = bf2f(A.U[o]);
-            const float sgm = sigmoid_f(gv);
-            tw[tidx(4 * lg + i, 16 * nf + lr)] = f2bf(dh * uv * sgm * (1.f + gv * (1.f - sgm)));
-            du[nf][i] = dh * gv * sgm;
+          for (int i = 0; i < 4; ++i) {
+            const float sgm = sigmoid_rcp(gv[i]);
+            dg[i] = a[i] * uv[i] * sgm * (1.f + gv[i] * (1.f - sgm));
+            du[i] = a[i] * gv[i] * sgm;
           }
+          *reinterpret_cast<u32x2_t *>(&A.dG[o]) = u32x2_t{cvt_pk_bf16(dg[0], dg[1]), cvt_pk_bf16(dg[2], dg[3])};
+          *reinterpret_cast<u32x2_t *>(&A.dU[o]) = u32x2_t{cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
+        } else {
+          *reinterpret_cast<u32x2_t *>(&A.out[p * A.ldo + c]) =
+              u32x2_t{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3])};
         }
-        flush(m, A.dG, N);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int nf = 0; nf < 8; ++nf) tw[tidx(4 * lg + i, 16 * nf + lr)] = f2bf(du[nf][i]);
-        flush(m, A.dU, N);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int nf = 0; nf < 8; ++nf) tw[tidx(4 * lg + i, 16 * nf + lr)] = f2bf(acc[m][nf][i]);
-        flush(m, A.out, A.ldo);
       }
     }
   }
@@ -365,15 +367,28 @@ int mfma_t_tile_rows() { return GT_BM; }
 int mfma_t_tile_cols() { return GT_BN; }
 int mfma_t_blocks_per_cu() { return GT_BPC; }
 
+// One launch per tile class (128, 96, 64, 32 rows); cnt as written by
+// launch_class_tiles.
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int grid,
+                           hipStream_t st) {
+  if (mode == 0) {
+    grouped_gemm_t_kernel<0, 4><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
+    grouped_gemm_t_kernel<0, 3><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
+    grouped_gemm_t_kernel<0, 2><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
+    grouped_gemm_t_kernel<0, 1><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+  } else {
+    grouped_gemm_t_kernel<1, 4><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
+    grouped_gemm_t_kernel<1, 3><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
+    grouped_gemm_t_kernel<1, 2><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
+    grouped_gemm_t_kernel<1, 1><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+  }
+}
+
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream) {
   dim3 grid((C + 255) / 256, R / 64, E);
   transpose_q_kernel<<<grid, 256, 0, stream>>>(q, s, offsets, R, C, qt, st);
 }
 
-void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st) {
-  if (mode == 0) grouped_gemm_t_kernel<0><<<grid, 256, 0, st>>>(A);
-  else grouped_gemm_t_kernel<1><<<grid, 256, 0, st>>>(A);
-}
 
 }  // namespace moe

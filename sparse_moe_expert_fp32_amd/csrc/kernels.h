@@ -95,7 +95,7 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int gr
 // transposed-base products of the backward (expert_mfma_bwd.hip)
 struct MfmaGemmTArgs {
   const void *a0, *a1; int lda;           // A rows: dO (mode 0) or dG, dU (mode 1), [S][lda]
-  const int2 *tiles; const int *ntiles; const int32_t *offsets;
+  const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
   int K, N, NT;                           // reduction per source, output columns, ceil(N / 256)
   const uint8_t *qt0, *qt1;               // int4 base transposed, [E][N][K/2] (qt1: mode 1, up)
   const float *st0, *st1;                 // its scales per column group, [E][N/128][K]
@@ -135,7 +135,9 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
 int wgrad_tile_rows();
 void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st);
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
-void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, int grid, hipStream_t st);
+// one launch per tile class of launch_class_tiles (cnt: its counts and starts)
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int grid,
+                           hipStream_t st);
 
 // ---- adapter optimizer step (adamw.hip)
 struct AdamWArgs {

@@ -128,6 +128,12 @@ DEV void dma2(const void *sbase, uint32_t voff, uint32_t lds) {
 // LDS operation either.
 constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kWaitAll = 0x0070;
+// every vector memory operation of this wave done (LDS untouched).  The
+// LDS-DMA pipelines wait with this rather than with a count of the newest
+// loads: LDS-DMA loads of one wave were observed to complete out of issue
+// order (a count-based wait let a stage be read before all of it had
+// landed), and waiting for all of them costs nothing measurable here.
+constexpr int kWaitVm = vmcnt_imm(0);
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would make the compiler drain every outstanding load, including LDS-DMA

@@ -121,11 +121,12 @@ __global__ __launch_bounds__(256, 2) void router_logits_kernel(
     }
   };
 
-  // 3-deep pipeline (see the expert GEMMs): XOPS + WOPS DMA per thread and stage
-  constexpr int kOps = XOPS + WOPS;
+  // 3-deep ring: step j computes from slot j % 3 while the loads of step
+  // j + 2 are in flight; each step ends with a wait for all of the wave's
+  // loads and a block barrier
   stage(0, st0);
   stage(1, st1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps));
+  __builtin_amdgcn_s_waitcnt(kWaitVm);
   block_barrier();
   for (int j = 0; j < NC; j += 3) {
 #define MOE_R_STEP(JJ, CUR, NXT)                 \
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void router_logits_kernel(
     const int jj = (JJ);                         \
     stage(jj + 2, NXT);                          \
     if (jj < NC) compute(CUR);                   \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOps)); \
+    __builtin_amdgcn_s_waitcnt(kWaitVm);         \
     block_barrier();                             \
   }
     MOE_R_STEP(j, st0, st2)

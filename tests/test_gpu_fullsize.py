@@ -104,9 +104,12 @@ def test_e460_t8192_bitwise_repeatable(cuda_ok, big):
     import torch
     from sparse_moe_expert_fp32_amd.layer import to_numpy
     cfg, inp, gpu, L, R, _ = big
-    L.train_step()
-    torch.cuda.synchronize()
-    assert np.array_equal(to_numpy(L.y), gpu["y"])
-    assert np.array_equal(to_numpy(L.dx), gpu["dx"])
-    for n in ADAPTERS:
-        assert np.array_equal(to_numpy(L.grads[n]), gpu[n]), n
+    # several repeats: a pipeline that reads a stage before all of it has
+    # landed shows up as run-to-run differences in a few rows
+    for rep in range(3):
+        L.train_step()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_numpy(L.y), gpu["y"]), rep
+        assert np.array_equal(to_numpy(L.dx), gpu["dx"]), rep
+        for n in ADAPTERS:
+            assert np.array_equal(to_numpy(L.grads[n]), gpu[n]), (rep, n)
