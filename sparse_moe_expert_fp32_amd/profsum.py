@@ -23,7 +23,9 @@ from collections import defaultdict
 # kernels launched together as one stage of the layer (one launch per tile
 # class); the trace summary adds a line with their summed average per stage
 STAGES = {"gate/up expert GEMM (grouped_gemm_kernel<0, ...>, all tile classes)": r"grouped_gemm_kernel<0,",
-          "down expert GEMM (grouped_gemm_kernel<1, ...>, all tile classes)": r"grouped_gemm_kernel<1,"}
+          "down expert GEMM (grouped_gemm_kernel<1, ...>, all tile classes)": r"grouped_gemm_kernel<1,",
+          "backward dH + SwiGLU (grouped_gemm_t_kernel<0, ...>, all tile classes)": r"grouped_gemm_t_kernel<0,",
+          "backward dX_perm (grouped_gemm_t_kernel<1, ...>, all tile classes)": r"grouped_gemm_t_kernel<1,"}
 
 
 def trace(stats_csv: str, out_md: str, cmd: str, top: int = 30):
