@@ -445,7 +445,7 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     M.saveG = save ? (uint16_t *)Gs : nullptr;
     M.saveU = save ? (uint16_t *)Us : nullptr;
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128;
-    TIMED(MOE_KT_GATEUP, st, moe::launch_grouped_gemm(0, M, ntiles_m, grid, st));
+    TIMED(MOE_KT_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(0, M, ntiles_m, c, grid, st));
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
     Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
@@ -457,7 +457,7 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     D.q0 = down.q; D.rt0 = rt_d; D.B0 = (const uint16_t *)down.B;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
-    TIMED(MOE_KT_DOWN, st, moe::launch_grouped_gemm(1, D, ntiles_m, grid, st));
+    TIMED(MOE_KT_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));
     return hip_status("moe_expert_fwd");
   }
 
@@ -576,7 +576,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
     moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
-    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, grid, st));
+    TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
@@ -607,7 +607,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.out = (uint16_t *)dXp; X.ldo = d;
     moe::launch_transpose_q(gate.q, gate.scale, offsets, E, f, d, qt0, st0, st);
     moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
-    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, ntiles_m, grid, st));
+    TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
     moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
     return hip_status("moe_adapter_bwd");
   }

@@ -543,21 +543,19 @@ void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hi
   build_class_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, tiles, cnt);
 }
 
-// One launch per tile class (128, 96, 64, 32 rows); cnt as written by
-// launch_class_tiles.
-void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int grid,
+// The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32); cnt as
+// written by launch_class_tiles.
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
                          hipStream_t st) {
+  const int *c = cnt + cls, *s = cnt + 4 + cls;
+#define MOE_GG(MODE, NM)                                                   \
+  grouped_gemm_kernel<MODE, 4, NM><<<grid, 256, 0, st>>>(A, c, s)
   if (mode == 0) {
-    grouped_gemm_kernel<0, 4, 8><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
-    grouped_gemm_kernel<0, 4, 6><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
-    grouped_gemm_kernel<0, 4, 4><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
-    grouped_gemm_kernel<0, 4, 2><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+    if (cls == 0) MOE_GG(0, 8); else if (cls == 1) MOE_GG(0, 6); else if (cls == 2) MOE_GG(0, 4); else MOE_GG(0, 2);
   } else {
-    grouped_gemm_kernel<1, 4, 8><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
-    grouped_gemm_kernel<1, 4, 6><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
-    grouped_gemm_kernel<1, 4, 4><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
-    grouped_gemm_kernel<1, 4, 2><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+    if (cls == 0) MOE_GG(1, 8); else if (cls == 1) MOE_GG(1, 6); else if (cls == 2) MOE_GG(1, 4); else MOE_GG(1, 2);
   }
+#undef MOE_GG
 }
 
 }  // namespace moe

@@ -367,21 +367,18 @@ int mfma_t_tile_rows() { return GT_BM; }
 int mfma_t_tile_cols() { return GT_BN; }
 int mfma_t_blocks_per_cu() { return GT_BPC; }
 
-// One launch per tile class (128, 96, 64, 32 rows); cnt as written by
-// launch_class_tiles.
-void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int grid,
+// The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32); cnt as
+// written by launch_class_tiles.
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
                            hipStream_t st) {
+  const int *c = cnt + cls, *s = cnt + 4 + cls;
+#define MOE_GT(MODE, NMH) grouped_gemm_t_kernel<MODE, NMH><<<grid, 256, 0, st>>>(A, c, s)
   if (mode == 0) {
-    grouped_gemm_t_kernel<0, 4><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
-    grouped_gemm_t_kernel<0, 3><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
-    grouped_gemm_t_kernel<0, 2><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
-    grouped_gemm_t_kernel<0, 1><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+    if (cls == 0) MOE_GT(0, 4); else if (cls == 1) MOE_GT(0, 3); else if (cls == 2) MOE_GT(0, 2); else MOE_GT(0, 1);
   } else {
-    grouped_gemm_t_kernel<1, 4><<<grid, 256, 0, st>>>(A, cnt + 0, cnt + 4);
-    grouped_gemm_t_kernel<1, 3><<<grid, 256, 0, st>>>(A, cnt + 1, cnt + 5);
-    grouped_gemm_t_kernel<1, 2><<<grid, 256, 0, st>>>(A, cnt + 2, cnt + 6);
-    grouped_gemm_t_kernel<1, 1><<<grid, 256, 0, st>>>(A, cnt + 3, cnt + 7);
+    if (cls == 0) MOE_GT(1, 4); else if (cls == 1) MOE_GT(1, 3); else if (cls == 2) MOE_GT(1, 2); else MOE_GT(1, 1);
   }
+#undef MOE_GT
 }
 
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,

@@ -89,7 +89,8 @@ void launch_scale_ratio(const uint16_t *s, size_t cols, int ng, float *rt, hipSt
 // 32, 64, 96 or 128 rows, grouped by that class; cnt[8]: count and first
 // index of each class (128-row class first)
 void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st);
-void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int grid,
+// the launch of tile class cls (0: 128-row tiles .. 3: 32-row tiles)
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
                          hipStream_t st);
 
 // transposed-base products of the backward (expert_mfma_bwd.hip)
@@ -135,8 +136,8 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
 int wgrad_tile_rows();
 void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st);
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
-// one launch per tile class of launch_class_tiles (cnt: its counts and starts)
-void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int grid,
+// the launch of tile class cls of launch_class_tiles (cnt: counts and starts)
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
                            hipStream_t st);
 
 // ---- adapter optimizer step (adamw.hip)
