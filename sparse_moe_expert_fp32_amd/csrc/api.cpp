@@ -160,7 +160,7 @@ struct BwdLayout {
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
     tiles_w = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * sizeof(int2)) : 0;
-    ntiles_w = mf ? c.take(sizeof(int)) : 0;
+    ntiles_w = mf ? c.take((1 + (size_t)d->n_experts) * sizeof(int)) : 0;   // count, first tile per expert
     part = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * 2 * std::max(dm, f) * d->rank * 4)
               : 0;
     // B of down, gate, up transposed to [E][r][N] (bf16)
@@ -561,10 +561,10 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     int2 *tiles_w = at<int2>(ws, L.tiles_w);
     int *ntiles_w = at<int>(ws, L.ntiles_w);
     const int mtw = (int)max_tiles(dims, moe::wgrad_tile_rows());
-    moe::launch_build_tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, st);
+    moe::launch_build_tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, st, ntiles_w + 1);
     moe::WgradMArgs W{};
     W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r; W.nsrc = 1;
-    W.tiles = tiles_w; W.ntiles = ntiles_w; W.part = at<float>(ws, L.part);
+    W.tiles = tiles_w; W.ntiles = ntiles_w; W.tfirst = ntiles_w + 1; W.part = at<float>(ws, L.part);
     W.w = (const uint16_t *)dO; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
     W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
     moe::launch_wgrad_mfma(W, mtw, false, st);

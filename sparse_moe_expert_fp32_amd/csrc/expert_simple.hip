@@ -16,10 +16,12 @@ namespace moe {
 
 // ------------------------------------------------------------ tile list --
 // One entry per (expert, BM-row block); entries ordered by expert.  tiles[i]
-// = (e, first row); ntiles[0] = count.  Launched with one 1024-thread block.
+// = (e, first row); ntiles[0] = count; first (when given) [e] = index of the
+// expert's first entry.  Launched with one 1024-thread block.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ offsets,
                                                            int E, int BM, int2 *__restrict__ tiles,
-                                                           int *__restrict__ ntiles) {
+                                                           int *__restrict__ ntiles,
+                                                           int *__restrict__ first_out) {
   __shared__ int sc[1024];
   const int e = threadIdx.x;
   int c = 0, lo = 0;
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   }
   int first = sc[e] - c;
   for (int i = 0; i < c; ++i) tiles[first + i] = make_int2(e, lo + i * BM);
+  if (first_out && e < E) first_out[e] = first;
   if (e == 1023) ntiles[0] = sc[e];
 }
 
@@ -230,8 +233,8 @@ __global__ void swiglu_bwd_kernel(const float *__restrict__ dH, const T *__restr
 // ------------------------------------------------------------- launchers --
 
 void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles,
-                        hipStream_t st) {
-  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, BM, tiles, ntiles);
+                        hipStream_t st, int *first) {
+  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, BM, tiles, ntiles, first);
 }
 
 int simple_tile_rows() { return SB_M; }

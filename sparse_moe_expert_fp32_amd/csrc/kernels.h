@@ -31,8 +31,9 @@ void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void
                           hipStream_t st);
 
 // ---- float32 expert kernels (expert_simple.hip)
+// first (optional, E ints): index of each expert's first tile
 void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles,
-                        hipStream_t st);
+                        hipStream_t st, int *first = nullptr);
 int simple_tile_rows();
 
 struct LinArgs {
@@ -131,6 +132,7 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
   const int32_t *offsets; int E, wide, r; float scale;
   float *out; size_t oe; int oa, ob;
   const int2 *tiles; const int *ntiles;   // wgrad_tile_rows()-row tiles
+  const int *tfirst;                      // [E] index of each expert's first tile
   float *part;                            // partials: [tiles][nsrc][wide][r]
 };
 int wgrad_tile_rows();
