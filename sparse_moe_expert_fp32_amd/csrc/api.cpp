@@ -169,7 +169,7 @@ struct BwdLayout {
     wt = mf ? c.take(2 * qt_slot_bytes(d)) : 0;
     wr_t = c.take((size_t)d->n_experts * dm * 4);
     dx_r = c.take((size_t)d->T * dm * 4);
-    dO = c.take(S * dm * ab);
+    dO = mf ? 0 : c.take(S * dm * ab);   // the matrix-core path reads dy by token instead
     dZ = c.take(S * 3 * d->rank * 4);
     dH32 = mf ? 0 : c.take(S * f * 4);
     dG = c.take(S * f * ab);
@@ -523,12 +523,14 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   int2 *tiles = at<int2>(ws, L.tiles);
   int *ntiles = at<int>(ws, L.ntiles);
   float *wr_t = at<float>(ws, L.wr_t), *dx_r = at<float>(ws, L.dx_r);
-  void *dO = at<char>(ws, L.dO);
+  // dO = gamma * dy in permuted order: materialised only for the float32
+  // kernels (the matrix-core path reads dy by token and applies the gates)
+  void *dO = use_mfma(dims) ? nullptr : at<char>(ws, L.dO);
   float *dZ = at<float>(ws, L.dZ);
   void *dXp = at<char>(ws, L.dXp);
   void *dG = at<char>(ws, L.dG), *dU = at<char>(ws, L.dU);
 
-  // gate path and dO = gamma * dy in permuted order
+  // gate path (and dO)
   moe::launch_transpose_f32(w_router, d, E, wr_t, st);
   TIMED(MOE_KT_GATE_GRAD, st,
         moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r, dO,
@@ -551,12 +553,13 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     float *st0 = reinterpret_cast<float *>(qt0 + qsz), *st1 = reinterpret_cast<float *>(qt1 + qsz);
     const uint16_t *H16 = (const uint16_t *)H;
 
-    // dZ_d = lam dO B_d
+    // dZ_d = lam dO B_d = lam g_p (dy[t(p)] B_d)
     moe::ProjMArgs Q{};
-    Q.a = (const uint16_t *)dO; Q.lda = d; Q.perm_src = perm_src; Q.kk = k;
+    Q.a = (const uint16_t *)dy; Q.lda = d; Q.perm_src = perm_src; Q.kk = k; Q.gsc = gates;
     Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 1;
     Q.m0 = bt_d; Q.scale = lam; Q.Z0 = dZ + 2 * r; Q.ldz = 3 * r;
-    moe::launch_proj_mfma(Q, mtp, false, st);
+    moe::launch_proj_mfma(Q, mtp, true, st);
+    Q.gsc = nullptr;
     // dB_d [d][r] = lam sum_p dO[p][n] Z_d[p][j]
     int2 *tiles_w = at<int2>(ws, L.tiles_w);
     int *ntiles_w = at<int>(ws, L.ntiles_w);
@@ -565,12 +568,16 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::WgradMArgs W{};
     W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r; W.nsrc = 1;
     W.tiles = tiles_w; W.ntiles = ntiles_w; W.tfirst = ntiles_w + 1; W.part = at<float>(ws, L.part);
-    W.w = (const uint16_t *)dO; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
+    // (= lam sum_p dy[t(p)][n] g_p Z_d[p][j])
+    W.w = (const uint16_t *)dy; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
+    W.gsc = gates;
     W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
-    moe::launch_wgrad_mfma(W, mtw, false, st);
+    moe::launch_wgrad_mfma(W, mtw, true, st);
+    W.gsc = nullptr;
     // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
     moe::MfmaGemmTArgs M{};
-    M.a0 = dO; M.lda = d; M.tiles = tiles_m; M.offsets = offsets;
+    M.a0 = dy; M.lda = d; M.perm_src = perm_src; M.kk = k; M.gsc = gates;
+    M.tiles = tiles_m; M.offsets = offsets;
     M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qt0; M.st0 = st0;
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;

@@ -110,7 +110,8 @@ DEV void block_sum(float (&v)[KMAX], int k, float *red /*[4][KMAX]*/) {
 // Per token t (one block):
 //   dgamma_j = <dy_t, e_out[p_j]>,  dl_j = gamma_j (dgamma_j - sum_i gamma_i dgamma_i)
 //   dx_r[t]  = sum_j dl_j * W_r[:, e_j]      (float32)
-//   dO[p_j]  = gamma_j * dy_t                (act dtype, permuted order)
+//   dO[p_j]  = gamma_j * dy_t                (act dtype, permuted order; skipped
+//                                            when dO is null)
 template <typename T>
 __global__ __launch_bounds__(256) void gate_grad_kernel(
     const T *__restrict__ dy, const T *__restrict__ e_out, const int32_t *__restrict__ topk_idx,
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(
       float o[V];
 #pragma unroll
       for (int i = 0; i < V; ++i) { acc[i] = fmaf(dl, w[i], acc[i]); o[i] = sg[j] * g[i]; }
-      Vec16<T>::st(dO + (size_t)sp[j] * d + c, o);
+      if (dO) Vec16<T>::st(dO + (size_t)sp[j] * d + c, o);
     }
 #pragma unroll
     for (int i = 0; i < V; ++i) dx_r[(size_t)t * d + c + i] = acc[i];

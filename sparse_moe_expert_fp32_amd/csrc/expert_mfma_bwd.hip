@@ -7,7 +7,11 @@
 //   mode 0:  dH = dO W_d + dZ_d A_d, then the SwiGLU backward
 //            dG = dH U s (1 + G (1 - s)), dU = dH G s, s = sigmoid(G)
 //   mode 1:  dX_perm = dG W_g + dU W_u + dZ_g A_g + dZ_u A_u
-// (dZ = lam dOut B of the same matrix, computed beforehand).
+// (dZ = lam dOut B of the same matrix, computed beforehand).  The output
+// gradient of a permuted row p is its gate times the upstream gradient of its
+// token, dO[p] = g_p dy[t(p)], so mode 0 reads the rows of dy by token and
+// multiplies the product's row by g_p (dZ_d already carries it): dO is never
+// materialised.
 //
 // The reduction runs over the storage rows n of the int4 base, and the group
 // scale s[n][c/128] changes with every reduction step but is constant over
@@ -154,12 +158,16 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
 
     // A staging: wave w, load i covers rows 8 (AOPS w + i) .. +7 (8 chunks of
     // 16 B each); chunk c of row r lives at c ^ (r & 7)
+    // (mode 0 with gate scaling: the rows of dy by token)
+    const bool tokrows = MODE == 0 && A.gsc != nullptr;
     uint32_t aoff[AOPS];
 #pragma unroll
     for (int i = 0; i < AOPS; ++i) {
       const int r = 8 * (w * AOPS + i) + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);
-      aoff[i] = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.lda * 2) + c * 16;
+      const int p = p0 + min(r, rows - 1);
+      const int arow = tokrows ? A.perm_src[p] / A.kk : p;
+      aoff[i] = (uint32_t)arow * (uint32_t)(A.lda * 2) + c * 16;
     }
     // int4 staging: wave w, load i covers columns 32 (2w + i) .. +31, 32 bytes each
     uint32_t boff[2];
@@ -287,11 +295,15 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
     const int rbase = 16 * NMH * wm2 + lr2;
     const int ocol = c0 + 128 * wn2 + 4 * lg2, lcol = c0 + 128 * wn2 + lr2;
 
-    // remove the 136 offset of the int4 operand
+    // remove the 136 offset of the int4 operand (and apply the row's gate
+    // when the rows are dy by token)
 #pragma unroll
-    for (int m = 0; m < NMH; ++m)
+    for (int m = 0; m < NMH; ++m) {
+      float gm = 1.f;
+      if (MODE == 0 && A.gsc) gm = A.gsc[A.perm_src[p0 + min(rbase + 16 * m, rows - 1)]];
 #pragma unroll
-      for (int nf = 0; nf < 8; ++nf) acc[m][nf] -= corr[m];
+      for (int nf = 0; nf < 8; ++nf) acc[m][nf] = (acc[m][nf] - corr[m]) * gm;
+    }
 
     // adapter term: acc += dZ L with L = A of the matrix ([r][N]), K = rank.
     // Loads use clamped indices so that they issue together; rank positions

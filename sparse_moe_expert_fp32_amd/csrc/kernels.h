@@ -97,6 +97,9 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cl
 // transposed-base products of the backward (expert_mfma_bwd.hip)
 struct MfmaGemmTArgs {
   const void *a0, *a1; int lda;           // A rows: dO (mode 0) or dG, dU (mode 1), [S][lda]
+  // mode 0 with gsc set: A row p is a0[perm_src[p] / kk] (dy by token) and the
+  // product row is scaled by gsc[perm_src[p]] (the gate) before the adapter term
+  const int32_t *perm_src; int kk; const float *gsc;
   const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
   int K, N, NT;                           // reduction per source, output columns, ceil(N / 256)
   const uint8_t *qt0, *qt1;               // int4 base transposed, [E][N][K/2] (qt1: mode 1, up)
@@ -121,12 +124,14 @@ struct ProjMArgs {                        // Z_s = scale * A M_s^T over each exp
   int K, r, nsrc;
   const uint16_t *m0, *m1;                // [E][r][K]
   float scale; float *Z0, *Z1; int ldz;
+  const float *gsc;                       // GATHER: row p also scaled by gsc[perm_src[p]] (or null)
 };
 void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st);
 int proj_tile_rows();
 struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p][a] R_s[p][b]
   const uint16_t *w; int ldw; const int32_t *perm_src; int kk;
   const float *rr; int ldr;               // R of source 0
+  const float *gsc;                       // GATHER: R row p scaled by gsc[perm_src[p]] (or null)
   const float *rr1; float *out1;          // second source (nsrc = 2): same W, strides, scale
   int nsrc;
   const int32_t *offsets; int E, wide, r; float scale;

@@ -17,8 +17,9 @@
 namespace moe {
 
 // ------------------------------------------------------------ projections --
-// Z_s[p][j] = scale * sum_k A(p, k) M_s[e][j][k] for sources s < nsrc, j < r.
-// A(p, k) = a[(GATHER ? perm_src[p] / kk : p) * lda + k]; M_s is [E][r][K].
+// Z_s[p][j] = scale * g_p * sum_k A(p, k) M_s[e][j][k] for sources s < nsrc,
+// j < r.  A(p, k) = a[(GATHER ? perm_src[p] / kk : p) * lda + k]; M_s is
+// [E][r][K]; g_p = gsc[perm_src[p]] when gsc is given (GATHER), else 1.
 // NF = nsrc * ceil(r / 16) 16-column fragments.  One block per 64-row tile;
 // the tiles are spread so that each XCD takes a contiguous run of the list
 // (the tiles of one expert share that XCD's L2 copy of M).  The reduction is
@@ -116,6 +117,14 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
   }
   __syncthreads();
   if (w > 0) return;
+  float gs[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = min(p0 + 16 * m + 4 * lg + i, p_end - 1);
+      gs[m][i] = GATHER && P.gsc ? P.scale * P.gsc[P.perm_src[p]] : P.scale;
+    }
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int src = f / nj, j = 16 * (f - src * nj) + lr;
@@ -127,15 +136,17 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
         const int o = ((m * NF + f) * 4 + i) * 64 + lane;
         const float v = ((acc[m][f][i] + red[0][o]) + red[1][o]) + red[2][o];
         const int p = p0 + 16 * m + 4 * lg + i;
-        if (j < P.r && p < p_end) Z[(size_t)p * P.ldz + j] = P.scale * v;
+        if (j < P.r && p < p_end) Z[(size_t)p * P.ldz + j] = gs[m][i] * v;
       }
   }
 }
 
 // ------------------------------------------------------ adapter gradients --
-// out_s[e*oe + a*oa + b*ob] = scale * sum_{p in expert e} W(p, a) R_s[p][b],
+// out_s[e*oe + a*oa + b*ob] = scale * sum_{p in expert e} W(p, a) g_p R_s[p][b],
 // a < wide, b < r, for one or two R sources sharing W (NM = nsrc *
-// ceil(r / 16) fragments of 16 R columns).
+// ceil(r / 16) fragments of 16 R columns); W(p, a) = w[(GATHER ? perm_src[p]
+// / kk : p) * ldw + a], g_p = gsc[perm_src[p]] when gsc is given (GATHER),
+// else 1.
 //
 // Work items are (512-row tile of an expert, 256 wide columns), so a heavily
 // loaded expert is spread over many blocks.  An expert that fits one tile
@@ -167,6 +178,7 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
   __shared__ uint4 wl[WG_ROWS / 8][WG_COLS];                          // 32 KB
   __shared__ __attribute__((aligned(16))) uint16_t rl[16 * NM][WG_ROWS + 8];
   __shared__ int srow[WG_TILE];                                       // source row per tile row
+  __shared__ float sgam[WG_TILE];                                     // its R scale
   const int ti = blockIdx.y;
   if (ti >= G.ntiles[0]) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -180,7 +192,11 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
   constexpr int RC = 16 * NM;       // staged R columns (all sources)
   constexpr int RPER = RC / 4;      // R values per thread and chunk
   if (GATHER) {
-    for (int t = tid; t < hi - p0; t += 256) srow[t] = G.perm_src[p0 + t] / G.kk;
+    for (int t = tid; t < hi - p0; t += 256) {
+      const int ps = G.perm_src[p0 + t];
+      srow[t] = ps / G.kk;
+      sgam[t] = G.gsc ? G.gsc[ps] : 1.f;
+    }
     __syncthreads();
   }
   f32x4_t acc[NM][4];
@@ -208,7 +224,9 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
       const int idx = tid + 256 * u, pp = idx / RC, cc = idx - pp * RC;
       const int src = cc / (nj * 16), b = cc - src * nj * 16;
       const float *R = src ? G.rr1 : G.rr;
-      rv[u] = R[(size_t)min(pc + pp, hi - 1) * G.ldr + min(b, G.r - 1)];
+      const int p = min(pc + pp, hi - 1);
+      rv[u] = R[(size_t)p * G.ldr + min(b, G.r - 1)];
+      if (GATHER) rv[u] *= sgam[p - p0];
     }
   };
   load(p0);
