@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -83,6 +83,14 @@ typedef struct {
  *   scale bf16  [E][N][K/g]: W_hat[n][c] = scale[n][c/g] * q[n][c].
  *   A     act   [E][r][K]   (out x in, like the base)
  *   B     act   [E][N][r]
+ *   qt    optional (may be NULL): the base re-laid out for the input-gradient
+ *         products of moe_adapter_bwd, as written by moe_pack_base_t from
+ *         this q and scale.  The base is frozen under TQP, so a caller can
+ *         pack it once and pass it to every backward call; with NULL the
+ *         backward re-lays out the base of every expert with rows in its own
+ *         workspace on each call.  Results are the same either way.  Read
+ *         only by the matrix-core path (bf16, group 128, d and f multiples
+ *         of 128); ignored otherwise.  16-byte aligned.
  * Effective matrix: W_eff = W_hat + lambda * B A, i.e. for a row x,
  * x W_eff^T = x W_hat^T + lambda (x A^T) B^T. */
 typedef struct {
@@ -90,6 +98,7 @@ typedef struct {
   const uint16_t *scale;
   const void *A;
   const void *B;
+  const void *qt;
 } moe_qlora;
 
 /* Which call a workspace size is asked for. */
@@ -183,6 +192,26 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
                            const void *e_out, const void *save, void *dx,
                            float *dA_gate, float *dB_gate, float *dA_up, float *dB_up,
                            float *dA_down, float *dB_down, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Transposed packing of one frozen base matrix for the backward (the qt
+ * field of moe_qlora).  The input-gradient products reduce over the storage
+ * rows N of the base, so their int4 operand must be packed along N: for
+ * every expert e, block of 64 storage rows n0 and column c, 32 bytes hold
+ * q[e][n0 .. n0+63][c] in the word order of the forward layout, and the
+ * scales follow as float32 [E][K/128][N] (K of the matrix).  The backward
+ * products are those of moe_adapter_bwd (skill card "Reversible Sparse MoE
+ * Single Node", Principle 3: the base is frozen, only the adapters train).
+ *   matrix  MOE_MAT_GATE_UP (q [E][f][d/2], scale [E][f][d/128]) or
+ *           MOE_MAT_DOWN (q [E][d][f/2], scale [E][d][f/128])
+ *   packed  device buffer of moe_pack_base_t_size() bytes, 16-byte aligned
+ *           (out; caller-owned)
+ * Only the matrix-core path has this layout: other dims give
+ * MOE_ERR_UNSUPPORTED.  Asynchronous on `stream`. */
+typedef enum { MOE_MAT_GATE_UP = 0, MOE_MAT_DOWN = 1 } moe_matrix;
+moe_status moe_pack_base_t_size(const moe_dims *dims, size_t *bytes);
+moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *q,
+                           const uint16_t *scale, void *packed, size_t packed_bytes,
                            void *stream);
 
 /* Adapter optimizer step: AdamW on one float32 tensor of n elements (call it

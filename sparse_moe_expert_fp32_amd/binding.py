@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_tqp.
 
 MOE_F32, MOE_BF16 = 0, 1
 CALL_ROUTE, CALL_PERMUTE, CALL_EXPERT_FWD, CALL_COMBINE, CALL_ADAPTER_BWD = range(5)
+MAT_GATE_UP, MAT_DOWN = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -31,7 +32,7 @@ class Dims(ctypes.Structure):
 
 class QLora(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("qt", ctypes.c_void_p)]
 
 
 class AdamWHparams(ctypes.Structure):
@@ -62,6 +63,8 @@ def _load():
         "moe_timer_start": [I32],
         "moe_timer_stop": [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)],
         "moe_adamw_step": [ctypes.POINTER(AdamWHparams), ctypes.c_int64, P, P, P, P, P, I32, P],
+        "moe_pack_base_t_size": [DP, ctypes.POINTER(SZ)],
+        "moe_pack_base_t": [DP, I32, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -75,7 +78,8 @@ def _load():
 LIB = _load()
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
-           "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step")
+           "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step",
+           "moe_pack_base_t_size", "moe_pack_base_t")
 
 # kernel tags of moe_timer_start (moe_kernel_tag)
 KT = {"router_logits": 0, "router_topk": 1, "permute": 2, "gateup": 3, "down": 4, "combine": 5,
@@ -114,8 +118,8 @@ def dims_of(cfg, T: int | None = None) -> Dims:
                 cfg.act, cfg.lora_scale)
 
 
-def qlora(q, scale, A, B) -> QLora:
-    return QLora(_p(q), _p(scale), _p(A), _p(B))
+def qlora(q, scale, A, B, qt=None) -> QLora:
+    return QLora(_p(q), _p(scale), _p(A), _p(B), _p(qt))
 
 
 def moe_workspace_size(dm: Dims, call: int) -> int:
@@ -176,6 +180,24 @@ def moe_adapter_bwd(dm, dy, x, topk_idx, gates, offsets, perm_src, slot_pos, w_r
                                _p(dA_up), _p(dB_up), _p(dA_down), _p(dB_down), _p(ws),
                                ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_adapter_bwd")
+
+
+def pack_base_supported(dm: Dims) -> bool:
+    """Whether these dims have a packed transposed base (the matrix-core path)."""
+    out = ctypes.c_size_t(0)
+    return LIB.moe_pack_base_t_size(ctypes.byref(dm), ctypes.byref(out)) == 0
+
+
+def moe_pack_base_t_size(dm: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(LIB.moe_pack_base_t_size(ctypes.byref(dm), ctypes.byref(out)), "moe_pack_base_t_size")
+    return out.value
+
+
+def moe_pack_base_t(dm: Dims, matrix: int, q, scale, packed, stream=None):
+    _check(LIB.moe_pack_base_t(ctypes.byref(dm), matrix, _p(q), _p(scale), _p(packed),
+                               packed.numel() if packed is not None else 0, _stream(stream)),
+           "moe_pack_base_t")
 
 
 def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step) -> AdamWHparams:

@@ -49,6 +49,8 @@ moe_status check_dims(const moe_dims *d) {
 moe_status check_qlora(const moe_qlora &m, const char *name) {
   if (!m.q || !m.scale || !m.A || !m.B)
     return fail(MOE_ERR_INVALID, std::string(name) + ": q, scale, A and B must be non-NULL");
+  if (((uintptr_t)m.qt & 15) != 0)
+    return fail(MOE_ERR_INVALID, std::string(name) + ": qt must be 16-byte aligned");
   return MOE_OK;
 }
 
@@ -339,6 +341,38 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
   return hip_status("moe_permute");
 }
 
+moe_status moe_pack_base_t_size(const moe_dims *dims, size_t *bytes) {
+  TRY(check_dims(dims));
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  if (!use_mfma(dims))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_pack_base_t: only the matrix-core path (bf16, group 128, d and f "
+                "multiples of 128) has a packed transposed base");
+  *bytes = qt_slot_bytes(dims);
+  return MOE_OK;
+}
+
+moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *q,
+                           const uint16_t *scale, void *packed, size_t packed_bytes,
+                           void *stream) {
+  size_t need = 0;
+  TRY(moe_pack_base_t_size(dims, &need));
+  if (matrix != MOE_MAT_GATE_UP && matrix != MOE_MAT_DOWN)
+    return fail(MOE_ERR_INVALID, "moe_pack_base_t: matrix must be MOE_MAT_GATE_UP or MOE_MAT_DOWN");
+  REQUIRE(q && scale && packed, "moe_pack_base_t: q, scale and packed must be non-NULL");
+  REQUIRE(((uintptr_t)packed & 15) == 0, "moe_pack_base_t: packed must be 16-byte aligned");
+  if (packed_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_pack_base_t: packed buffer too small: need " +
+                                       std::to_string(need) + " bytes, got " +
+                                       std::to_string(packed_bytes));
+  const int E = dims->n_experts, d = dims->d_model, f = dims->d_ff;
+  const int R = matrix == MOE_MAT_GATE_UP ? f : d, C = matrix == MOE_MAT_GATE_UP ? d : f;
+  uint8_t *qt = (uint8_t *)packed;
+  float *st = reinterpret_cast<float *>(qt + (size_t)E * d * f / 2);
+  moe::launch_transpose_q(q, scale, nullptr, E, R, C, qt, st, (hipStream_t)stream);
+  return hip_status("moe_pack_base_t");
+}
+
 moe_status moe_adamw_step(const moe_adamw_hparams *h, int64_t n, float *master,
                           const float *grad, float *m, float *v, void *param, int32_t param_dtype,
                           void *stream) {
@@ -578,11 +612,19 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::MfmaGemmTArgs M{};
     M.a0 = dy; M.lda = d; M.perm_src = perm_src; M.kk = k; M.gsc = gates;
     M.tiles = tiles_m; M.offsets = offsets;
-    M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qt0; M.st0 = st0;
+    // the transposed base: the caller's packing, else this call's own
+    const uint8_t *qd = qt0;
+    const float *sd = st0;
+    if (down.qt) {
+      qd = (const uint8_t *)down.qt;
+      sd = reinterpret_cast<const float *>(qd + qsz);
+    } else {
+      moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
+    }
+    M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qd; M.st0 = sd;
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
-    moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
     TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
@@ -609,11 +651,21 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m;
     X.offsets = offsets; X.K = f; X.N = d; X.NT = (d + 255) / 256;
     X.qt0 = qt0; X.st0 = st0; X.qt1 = qt1; X.st1 = st1;
+    if (gate.qt) {
+      X.qt0 = (const uint8_t *)gate.qt;
+      X.st0 = reinterpret_cast<const float *>(X.qt0 + qsz);
+    } else {
+      moe::launch_transpose_q(gate.q, gate.scale, offsets, E, f, d, qt0, st0, st);
+    }
+    if (up.qt) {
+      X.qt1 = (const uint8_t *)up.qt;
+      X.st1 = reinterpret_cast<const float *>(X.qt1 + qsz);
+    } else {
+      moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
+    }
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A;
     X.out = (uint16_t *)dXp; X.ldo = d;
-    moe::launch_transpose_q(gate.q, gate.scale, offsets, E, f, d, qt0, st0, st);
-    moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
     TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
     moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
     return hip_status("moe_adapter_bwd");

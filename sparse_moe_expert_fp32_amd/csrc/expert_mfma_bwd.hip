@@ -46,7 +46,7 @@ constexpr int GT_BM = 128, GT_BN = 256, GT_KS = 64, GT_BPC = 2;   // GT_BPC: blo
 // q: [E][R][C/2] (packed along C), s: [E][R][C/128] bf16  ->
 // qt: [E][R/64][C][32 bytes] (each column's run of 64 storage rows as 8 words,
 //     same in-word order as the forward operand), st: [E][C/128][R] f32.
-// Experts without rows are skipped.  Block: 64 storage rows x 256 columns, so
+// Experts without rows are skipped (all are transposed when offsets is null).  Block: 64 storage rows x 256 columns, so
 // every row is read as one 128-byte run and every output block is one 8 KB
 // run; each thread transposes one 8 x 8 nibble block in registers (8 words
 // read from 8 rows -> 8 words of 8 columns), re-laid out through LDS.
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restr
                                                           float *__restrict__ st) {
   __shared__ uint32_t lw[256][9];   // [column][row octet], padded
   const int e = blockIdx.z;
-  if (offsets[e + 1] == offsets[e]) return;
+  if (offsets && offsets[e + 1] == offsets[e]) return;
   const int n0 = blockIdx.y * 64, c0 = blockIdx.x * 256;
   const int tid = threadIdx.x, cg = tid & 31, a = tid >> 5;   // 8-column group, row octet
   const bool ok = c0 + 8 * cg < C;                           // C is a multiple of 128

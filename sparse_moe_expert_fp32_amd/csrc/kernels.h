@@ -113,7 +113,8 @@ int mfma_t_tile_rows();
 int mfma_t_tile_cols();
 int mfma_t_blocks_per_cu();   // resident blocks per CU the kernel is built for
 // int4 [E][R][C/2] + scales [E][R][C/128] -> transposed int4 [E][C][R/2] + scales
-// [E][C/128][R] (f32), for experts with rows; R, C multiples of 128
+// [E][C/128][R] (f32), for experts with rows (every expert when offsets is
+// null); R, C multiples of 128
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream);
 

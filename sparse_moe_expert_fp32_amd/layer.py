@@ -34,7 +34,8 @@ def to_numpy(t):
 
 class DeviceLayer:
     def __init__(self, cfg, inputs: dict, device: str = "cuda", want_logits: bool = False,
-                 want_x_perm: bool = False, with_backward: bool | None = None):
+                 want_x_perm: bool = False, with_backward: bool | None = None,
+                 pack_base: bool = True):
         self.cfg = cfg
         self.dev = torch.device(device)
         self.dm = B.dims_of(cfg)
@@ -59,6 +60,17 @@ class DeviceLayer:
             ((B.CALL_ADAPTER_BWD,) if bwd else ())
         self.ws = {c: torch.empty(max(1, B.moe_workspace_size(self.dm, c)), dtype=torch.uint8,
                                   device=self.dev) for c in calls}
+        # the frozen base re-laid out once for the backward (matrix-core path)
+        self.packed = {}
+        if bwd and pack_base and B.pack_base_supported(self.dm):
+            nb = B.moe_pack_base_t_size(self.dm)
+            for m in MATS:
+                buf = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+                B.moe_pack_base_t(self.dm, B.MAT_DOWN if m == "down" else B.MAT_GATE_UP,
+                                  self.t[f"q_{m}"], self.t[f"s_{m}"], buf)
+                self.packed[m] = buf
+            self.w = {m: B.qlora(self.t[f"q_{m}"], self.t[f"s_{m}"], self.t[f"A_{m}"],
+                                 self.t[f"B_{m}"], self.packed[m]) for m in MATS}
         if bwd:
             self.dx = z(T, d)
             self.grads = {"dA_gate": z(E, r, d, dtype=f32), "dB_gate": z(E, f, r, dtype=f32),

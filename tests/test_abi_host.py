@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(B):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(declared_functions()) == set(B.EXPORTS)
-    assert B.moe_abi_version() == 1
+    assert B.moe_abi_version() == 2
 
 
 def good(B, **kw):
@@ -141,3 +141,39 @@ def test_adamw_rejects_bad_arguments(B, kw, status):
 
 def test_adamw_empty_tensor_is_a_no_op(B):
     assert adamw_call(B, n=0, ptrs=(None, None, None, None)) == 0
+
+
+# ---- packed transposed base: host-side validation
+
+def test_pack_size_and_support(B):
+    big = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16")
+    E, d, f = 460, 2048, 768
+    assert B.moe_pack_base_t_size(big) == E * d * f // 2 + E * d * f // 128 * 4
+    assert B.pack_base_supported(big)
+    for dm in (good(B), good(B, act="bf16"), B.dims(64, 192, 8, 2, 256, 4, 64, "bf16")):
+        out = ctypes.c_size_t(7)
+        assert B.LIB.moe_pack_base_t_size(ctypes.byref(dm), ctypes.byref(out)) == -2
+        assert out.value == 7
+        assert not B.pack_base_supported(dm)
+
+
+@pytest.mark.parametrize("matrix,q,s,packed,nbytes,status", [
+    (2, FAKE, FAKE, FAKE, 1 << 40, -1),          # no such matrix
+    (0, None, FAKE, FAKE, 1 << 40, -1),          # null q
+    (1, FAKE, FAKE, None, 1 << 40, -1),          # null output
+    (0, FAKE, FAKE, FAKE + 8, 1 << 40, -1),      # misaligned output
+    (0, FAKE, FAKE, FAKE, 1024, -3),             # output too small
+])
+def test_pack_rejects_bad_arguments(B, matrix, q, s, packed, nbytes, status):
+    dm = B.dims(256, 256, 8, 2, 128, 16, 128, "bf16")
+    assert B.LIB.moe_pack_base_t(ctypes.byref(dm), matrix, q, s, packed, nbytes, None) == status
+    assert B.LIB.moe_last_error().decode()
+
+
+def test_misaligned_packed_base_rejected(B):
+    dm = B.dims(256, 256, 8, 2, 128, 16, 128, "bf16")
+    P = FAKE
+    q, qbad = B.QLora(P, P, P, P, P), B.QLora(P, P, P, P, P + 4)
+    assert B.LIB.moe_adapter_bwd(ctypes.byref(dm), P, P, P, P, P, P, P, P, q, qbad, q, P, P, P,
+                                 P, P, P, P, P, P, P, 1 << 40, None) == -1
+    assert "qt" in B.LIB.moe_last_error().decode()

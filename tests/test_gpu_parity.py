@@ -139,3 +139,24 @@ def test_bitwise_deterministic(cuda_ok):
     assert np.array_equal(to_numpy(L.dx), a["dx"])
     for n in ADAPTERS:
         assert np.array_equal(to_numpy(L.grads[n]), a[n]), n
+
+
+def test_packed_base_matches_per_call_transpose(cuda_ok):
+    """The backward with the base packed once (moe_pack_base_t) gives the same
+    bits as the backward that re-lays out the base in its workspace, also with
+    experts that receive no rows (the packing covers every expert)."""
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
+    cfg = cfg_of(T=60, E=64, k=2, cfg_id=270)   # 120 rows over 64 experts: some get none
+    inp = inputs.generate(cfg, 0)
+    out = []
+    for pack in (False, True):
+        L = DeviceLayer(cfg, inp, device="cuda:0", pack_base=pack)
+        assert bool(L.packed) == pack
+        L.train_step()
+        torch.cuda.synchronize()
+        out.append({"dx": to_numpy(L.dx), **{n: to_numpy(L.grads[n]) for n in ADAPTERS}})
+        counts = to_numpy(L.counts)
+    assert (counts == 0).any()
+    for n in out[0]:
+        assert np.array_equal(out[0][n], out[1][n]), n
