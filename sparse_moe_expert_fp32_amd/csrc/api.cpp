@@ -457,9 +457,9 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     // per-row start values -136 * (row sum per group) and per-column scale ratios
     moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st);
-    moe::launch_scale_ratio(gate.scale, (size_t)E * f, d / 128, rt_g, st);
-    moe::launch_scale_ratio(up.scale, (size_t)E * f, d / 128, rt_u, st);
-    moe::launch_scale_ratio(down.scale, (size_t)E * d, f / 128, rt_d, st);
+    moe::launch_scale_ratio(gate.scale, E, f, d / 128, rt_g, st);
+    moe::launch_scale_ratio(up.scale, E, f, d / 128, rt_u, st);
+    moe::launch_scale_ratio(down.scale, E, d, f / 128, rt_d, st);
     // Z_g = X A_g^T, Z_u = X A_u^T (rows gathered from x)
     moe::ProjMArgs Q{};
     Q.a = (const uint16_t *)x; Q.lda = d; Q.perm_src = perm_src; Q.kk = k;

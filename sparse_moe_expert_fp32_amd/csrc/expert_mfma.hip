@@ -15,7 +15,9 @@
 //  * K streams through a 3-deep LDS ring in half-group stages (64 of K): the
 //    A rows (x gathered by token, or H), the int4 words of the block's 256
 //    columns and, per group, the per-row start values and per-column scale
-//    ratios, all by LDS-DMA (global_load_lds_*).
+//    ratios, all by LDS-DMA (global_load_lds_*).  The stage after the last
+//    one brings the epilogue's operands the same way (adapter projections
+//    Z, adapter B rows, last scales), so the epilogue reads only LDS.
 //  * Each wave owns 64 output columns for all 128 rows, so every unpacked
 //    weight fragment feeds eight matrix instructions.  A nibble u (offset by
 //    8) becomes the bf16 bit pattern 0x4300 | u, the exact value 136 + q; the
@@ -30,11 +32,15 @@
 //  * MFMA v_mfma_f32_16x16x32_bf16 with the weights as the first operand
 //    (D^T = W X^T): a lane's accumulator holds one row and four consecutive
 //    columns, so the epilogue writes 8-byte packed bf16 stores.
+//  * Within a stage the LDS reads of the A fragments run a few fragments
+//    ahead of the matrix instructions and the VALU work (unpacking, group
+//    update) sits between them, pinned by scheduling-group barriers.
 //  * Epilogue: the adapter term (lam Z) B^T is one more MFMA (K = rank) into
 //    the same accumulator; gate/up applies SwiGLU in registers (a lane holds
 //    the matching gate and up columns), writes H (bf16) and, for the down
 //    product, the start values -136 * (row sum of H) per group.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -49,10 +55,10 @@ constexpr int GM_KS = 64;    // K per pipeline stage (half a group)
 
 // One pipeline stage in LDS, one array per kind (each read is a per-lane base
 // register plus a compile-time offset below 64 KB): A rows (128 x 64 bf16,
-// 16-byte chunks XOR-swizzled by row), int4 words (32 bytes per block column),
-// and the group data: the scale ratio per block column (256 floats), the
-// per-row start values (128 floats) and a copy of those (128 floats, so that
-// every wave issues the same number of loads).
+// 16-byte chunks XOR-swizzled by row_swz), int4 words (32 bytes per block
+// column), and the group data: the scale ratio per block column (256
+// floats), the per-row start values (128 floats) and a copy of those (128
+// floats, so that every wave issues the same number of loads).
 constexpr int ST_A = GM_BM * GM_KS * 2, ST_B = 256 * GM_KS / 2, ST_X = 512 * 4;
 
 // ---------------------------------------------------------------- row sums --
@@ -80,19 +86,45 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 }
 
 // ------------------------------------------------------------ scale ratios --
-// Per column c of a quantized matrix with ng groups: rt[c][g] = s'[g-1] / s'[g]
-// for g >= 1 and rt[c][0] = s'[ng-1] (the final multiplier), where s' is the
-// bf16 scale with magnitudes below 2^-100 raised to 2^-100 (so a zero scale
-// leaves a contribution of at most 2^-100 times its partial sum).  One thread
-// per element, so that reads and writes are contiguous across the wave.
-__global__ void scale_ratio_kernel(const uint16_t *__restrict__ s, size_t n, int ng,
+// Per column c of a quantized matrix [E][N] with ng groups, group-major:
+// rt[e][g][c] = s'[g-1] / s'[g] for g >= 1 and rt[e][0][c] = s'[ng-1] (the
+// final multiplier), where s' is the bf16 scale with magnitudes below 2^-100
+// raised to 2^-100 (so a zero scale leaves a contribution of at most 2^-100
+// times its partial sum).  One thread per output element (the writes are
+// contiguous; a group's ratios of consecutive columns are contiguous too, so
+// the GEMM stages them as one run).
+__global__ void scale_ratio_kernel(const uint16_t *__restrict__ s, int N, int ng, size_t n,
                                    float *__restrict__ rt) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  const size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= n) return;
   auto guard = [](float v) { return fabsf(v) < 0x1p-100f ? 0x1p-100f : v; };
-  const int g = (int)(i % (size_t)ng);
+  const int c = (int)(o % (size_t)N);
+  const size_t eg = o / (size_t)N;
+  const int g = (int)(eg % (size_t)ng);
+  const size_t i = ((eg / (size_t)ng) * N + c) * ng + g;   // s[e][c][g]
   const float cur = guard(bf2f(s[i]));
-  rt[i] = g == 0 ? guard(bf2f(s[i + ng - 1])) : guard(bf2f(s[i - 1])) / cur;
+  rt[o] = g == 0 ? guard(bf2f(s[i + ng - 1])) : guard(bf2f(s[i - 1])) / cur;
+}
+
+// ------------------------------------------------------- stage schedule --
+// Scheduling groups of one forward pipeline stage (see compute() in
+// grouped_gemm_kernel): DS reads (mask 0x100), VALU (0x2), matrix
+// instructions (0x8), in the order the stage is written.
+template <int NM, int NF, bool EVEN, int PD, int I>
+DEV void fwd_frag_sched() {
+  constexpr int sub = I / NM, m = I % NM;
+  if constexpr (I + PD < 2 * NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+  constexpr int nvalu = ((EVEN && sub == 0 && m + 1 < NM) ? 4 * NF : 0) + (I == NM / 2 ? 7 * NF : 0);
+  if constexpr (nvalu > 0) __builtin_amdgcn_sched_group_barrier(0x002, nvalu, 0);
+}
+template <int NM, int NF, bool EVEN, int PD, int... I>
+DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
+  // prologue: B words (+ ratios and start values), the first PD A reads;
+  // unpacking of substep 0 (+ the update of row fragment 0)
+  __builtin_amdgcn_sched_group_barrier(0x100, NF + (EVEN ? NF + (NM > 4 ? 2 : 1) : 0) + PD, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 7 * NF + (EVEN ? 4 * NF : 0), 0);
+  (fwd_frag_sched<NM, NF, EVEN, PD, I>(), ...);
 }
 
 // ------------------------------------------------------------ grouped GEMM --
@@ -106,7 +138,7 @@ __global__ void scale_ratio_kernel(const uint16_t *__restrict__ s, size_t n, int
 // from LDS feeds four matrix instructions).  NM (2, 4, 6, 8) is the number of
 // 16-row fragments of the item's tile class: each class of tiles (32, 64, 96,
 // 128 rows) is its own launch, so a short tail tile costs only its rows.
-template <int MODE, int WAVES, int NM>
+template <int MODE, int WAVES, int NM, bool EPL>
 __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
     const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
   // (hip-clang passes the second launch bound through as the minimum number
@@ -167,48 +199,52 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
 
     // ---- LDS-DMA sources.  A: 8 rows x 8 chunks of 16 B per wave load; wave
     // w, load i covers rows 8 (AOPS w + i) .. +7 (rows past the tile repeat
-    // its last row); chunk c of row r lives at c ^ (r & 7).
+    // its last row); chunk c of row r lives at c ^ row_swz(r).
     uint32_t src_off[AOPS];
 #pragma unroll
     for (int i = 0; i < AOPS; ++i) {
       const int r = min(8 * (AOPS * w + i) + (lane >> 3), GM_BM - 1);
-      const int c = (lane & 7) ^ (r & 7);
+      const int c = (lane & 7) ^ row_swz(r);
       src_off[i] = (uint32_t)tok_lds[r] * (uint32_t)(A.lda * 2) + c * 16;
     }
     const char *abase = reinterpret_cast<const char *>(A.a);
     // int4 words: 8 loads of 32 block columns x 32 B; wave w takes loads
     // BOPS w .. BOPS w + BOPS - 1 (each all gate or all up)
-    const uint8_t *qbase[BOPS];
+    // (all of a wave's word loads are of one matrix: gate for waves 0-1,
+    // up for waves 2-3 in mode 0)
+    const uint8_t *qbase =
+        (const uint8_t *)uniform_ptr((MODE == 0 && w >= 2 ? A.q1 : A.q0) + (size_t)e * N * (K / 2));
     uint32_t qoff[BOPS];
 #pragma unroll
     for (int i = 0; i < BOPS; ++i) {
       const int bc = 32 * (BOPS * w + i) + (lane >> 1);
-      const bool up = MODE == 0 && bc >= 128;
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      qbase[i] = (const uint8_t *)uniform_ptr((up ? A.q1 : A.q0) + (size_t)e * N * (K / 2));
       qoff[i] = (uint32_t)c * (uint32_t)(K / 2) + 16 * (lane & 1);
     }
     // group data, 8 loads of 64 floats: loads 0-3 the ratios of block
-    // columns 64 q + lane, loads 4-5 the start values of rows 64 (q - 4) +
-    // lane, loads 6-7 the same start values again (into the spare quarter);
-    // wave w takes loads XOPS w .. XOPS w + XOPS - 1
-    const float *xbase[XOPS];
+    // columns 64 q + lane (group g at + g N), loads 4-5 the start values of
+    // the 128 rows (group g at + g), row 16 m + l at position 8 l + m (a
+    // lane's values are adjacent), loads 6-7 the same start values again
+    // (into the spare quarter); wave w takes loads XOPS w .. XOPS w + XOPS - 1
+    // (a wave's group-data loads share one base: waves 0-1 the ratios of
+    // gate (mode 1: all) columns, wave 1 in mode 0 those of up, waves 2-3 the
+    // start values)
+    const bool xr = w < 2;   // this wave loads ratios
+    const float *xbase = (const float *)uniform_ptr(
+        xr ? ((MODE == 0 && w == 1 ? A.rt1 : A.rt0) + (size_t)e * NG * N) : A.rsum);
+    const int xstr = __builtin_amdgcn_readfirstlane(xr ? N : 1);
     uint32_t xoff[XOPS];
 #pragma unroll
     for (int i = 0; i < XOPS; ++i) {
       const int q = XOPS * w + i;
-      const float *b;
       if (q < 4) {
         const int bc = 64 * q + lane;
-        const bool up = MODE == 0 && bc >= 128;
         const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-        b = (up ? A.rt1 : A.rt0) + (size_t)e * N * NG;
-        xoff[i] = (uint32_t)c * (uint32_t)NG * 4u;
+        xoff[i] = (uint32_t)c * 4u;
       } else {
-        b = A.rsum;
-        xoff[i] = (uint32_t)tok_lds[64 * (q & 1) + lane] * (uint32_t)A.ld_rsum * 4u;
+        const int pos = 64 * (q & 1) + lane;
+        xoff[i] = (uint32_t)tok_lds[16 * (pos & 7) + (pos >> 3)] * (uint32_t)A.ld_rsum * 4u;
       }
-      xbase[i] = (const float *)uniform_ptr(b);
     }
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
     const uint32_t la = ldsA + wu * AOPS * 1024, lb = ldsB + wu * BOPS * 1024,
@@ -217,16 +253,50 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
     // compile-time constant.  The int4 word lane lr feeds into the first MFMA
     // operand is block column slot w * WCOLS + nfc + lr; the lane's
     // accumulator holds the four output columns from slot w * WCOLS + nfc + 4 lg.
-    const uint32_t offA0 = opaque(ldsA + lr * 128 + (((2 * lg) ^ (lr & 7)) << 4)),
+    const uint32_t offA0 = opaque(ldsA + lr * 128 + (((2 * lg) ^ row_swz(lr)) << 4)),
                    offB = opaque(ldsB + (w * WCOLS + lr) * 32 + 8 * lg),
                    offR = opaque(ldsX + (w * WCOLS + 4 * lg) * 4),
-                   offC = opaque(ldsX + 1024 + lr * 4);
+                   offC = opaque(ldsX + 1024 + lr * 32);
 
+    // The epilogue's operands go through the ring too, as the stage after
+    // the last one (rank 16): the adapter projections Z of the item's rows
+    // in the A array (row r: Z_g then Z_u, or Z_d; 64 floats at most, with
+    // the A swizzle), the adapter B rows of its block columns in the word
+    // array (32 bytes each), and group 0's ratios, i.e. the last scales, in
+    // the group-data array.
+    // (EPL: rank 16 and Z rows 16-byte aligned, checked by the launcher)
+    constexpr bool ep_lds = EPL;
+    auto stage_ep = [&](int slot) {
+      uint32_t sa = la, sb = lb, sx = lx;
+      asm volatile("" : "+s"(sa), "+s"(sb), "+s"(sx));
+      const char *zb = reinterpret_cast<const char *>(uniform_ptr(A.Z0));
+#pragma unroll
+      for (int i = 0; i < AOPS; ++i) {
+        const int r = min(8 * (AOPS * w + i) + (lane >> 3), GM_BM - 1);
+        const int c = ((lane & 7) ^ row_swz(r)) & (MODE == 0 ? 7 : 3);   // Z_d: 4 chunks
+        const uint32_t zo = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.ldz * 4) + c * 16;
+        dma16(zb, zo, sa + slot * ST_A + i * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < BOPS; ++i) {
+        const int bc = 32 * (BOPS * w + i) + (lane >> 1);
+        const bool up = MODE == 0 && bc >= 128;
+        const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
+        const char *bb = reinterpret_cast<const char *>(uniform_ptr((up ? A.B1 : A.B0) + (size_t)e * N * 16));
+        dma16(bb, (uint32_t)c * 32u + 16 * (lane & 1), sb + slot * ST_B + i * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < XOPS; ++i) dma4(xbase, xoff[i], sx + slot * ST_X + i * 256);
+    };
     // one stage = half a quantization group (64 of K); a group's first stage
-    // also brings the ratios and start values.  Stages past the end load a
-    // harmless copy of the last one.
+    // also brings the ratios and start values.  The stage after the last is
+    // the epilogue's (rank 16); later ones load nothing.
     auto stage = [&](auto evenc, int jr, int slot) {
-      const int j = min(jr, NS - 1), g = j >> 1;
+      if (jr >= NS) {
+        if (ep_lds && jr == NS) stage_ep(slot);
+        return;
+      }
+      const int j = jr, g = j >> 1;
       // destinations re-derived per stage (scalar adds) rather than held
       uint32_t sa = la, sb = lb;
       asm volatile("" : "+s"(sa), "+s"(sb));
@@ -235,12 +305,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
         dma16(abase + (size_t)j * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
 #pragma unroll
       for (int i = 0; i < BOPS; ++i)
-        dma16(qbase[i] + (size_t)j * (GM_KS / 2), qoff[i], sb + slot * ST_B + i * 1024);
+        dma16(qbase + (size_t)j * (GM_KS / 2), qoff[i], sb + slot * ST_B + i * 1024);
       if (decltype(evenc)::value) {
         uint32_t sx = lx;
         asm volatile("" : "+s"(sx));
 #pragma unroll
-        for (int i = 0; i < XOPS; ++i) dma4(xbase[i] + g, xoff[i], sx + slot * ST_X + i * 256);
+        for (int i = 0; i < XOPS; ++i) dma4(xbase + (size_t)g * xstr, xoff[i], sx + slot * ST_X + i * 256);
       }
     };
 
@@ -254,45 +324,70 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
     // group lg takes k = 16 lg + 8 s .. + 7 of the stage in substep s (A chunk
     // 2 lg + s, int4 word 2 lg + s).  A group's first stage advances the
     // accumulators: Q <- Q * ratio + (-136 * row sum).
+    //
+    // The stage is written as one software pipeline over its 2 NM A
+    // fragments (substep-major): the LDS read of fragment i + PD is issued
+    // before the NF matrix instructions of fragment i, and the VALU work (the
+    // second substep's unpacking, and in a group's first stage the update of
+    // row fragment m + 1) sits between them, so it runs in the shadow of the
+    // matrix instructions.  The scheduling-group barriers at the end pin that
+    // order (the scheduler would otherwise cluster every read right before
+    // its use to save registers, exposing the LDS latency).
+    constexpr int PD = NM >= 8 ? 2 : 3;   // A read distance, in fragments
     auto compute = [&](auto odd, int slot) {   // odd: compile-time stage parity
+      constexpr bool EVEN = !decltype(odd)::value;
       __builtin_amdgcn_sched_barrier(0);
       u32x2_t bq[NF];
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) bq[nf] = lds_ld<u32x2_t>(offB + slot * ST_B + nfc(nf) * 32);
-      if (!decltype(odd)::value) {
-        f32x4_t rv[NF];
+      f32x4_t rv[NF], nv4[2];
+      if (EVEN) {
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) rv[nf] = lds_ld<f32x4_t>(offR + slot * ST_X + nfc(nf) * 4);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const float nv = lds_ld<float>(offC + slot * ST_X + m * 64);
-#pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][nf][i] = __builtin_fmaf(acc[m][nf][i], rv[nf][i], nv);
-        }
+        nv4[0] = lds_ld<f32x4_t>(offC + slot * ST_X);
+        if (NM > 4) nv4[1] = lds_ld<f32x4_t>(offC + slot * ST_X + 16);
       }
       // substep 1 reads chunk 2 lg + 1, i.e. the neighbouring swizzled chunk
       const uint32_t offA1 = offA0 ^ 16u;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint4 bu[NF];
+      auto lda = [&](int i) {
+        const int sub = i / NM, m = i % NM;
+        const u32x4_t a4 = lds_ld<u32x4_t>((sub ? offA1 : offA0) + slot * ST_A + m * 2048);
+        return make_uint4(a4.x, a4.y, a4.z, a4.w);
+      };
+      auto unpack = [&](int sub, uint4 (&bu)[NF]) {
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
-          const uint32_t x = s ? bq[nf].y : bq[nf].x;
+          const uint32_t x = sub ? bq[nf].y : bq[nf].x;
           bu[nf].x = __builtin_amdgcn_bitop3_b32(x, kMask, kMagic, 0x6A);
           bu[nf].y = __builtin_amdgcn_bitop3_b32(x >> 4, kMask, kMagic, 0x6A);
           bu[nf].z = __builtin_amdgcn_bitop3_b32(x >> 8, kMask, kMagic, 0x6A);
           bu[nf].w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
         }
+      };
+      auto advance = [&](int m) {   // a group's first stage: Q <- Q * ratio + start
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const u32x4_t a4 = lds_ld<u32x4_t>((s ? offA1 : offA0) + slot * ST_A + m * 2048);
-          const uint4 av = make_uint4(a4.x, a4.y, a4.z, a4.w);
+        for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf) acc[m][nf] = mfma32(bu[nf], av, acc[m][nf]);
-        }
+          for (int i = 0; i < 4; ++i)
+            acc[m][nf][i] = __builtin_fmaf(acc[m][nf][i], rv[nf][i], nv4[m >> 2][m & 3]);
+      };
+      uint4 a[2 * NM], bu0[NF], bu1[NF];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) a[i] = lda(i);
+      unpack(0, bu0);
+      if (EVEN) advance(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NM; ++i) {
+        const int sub = i / NM, m = i % NM;
+        if (i + PD < 2 * NM) a[i + PD] = lda(i + PD);
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) acc[m][nf] = mfma32(sub ? bu1[nf] : bu0[nf], a[i], acc[m][nf]);
+        if (EVEN && sub == 0 && m + 1 < NM) advance(m + 1);
+        if (i == NM / 2) unpack(1, bu1);
       }
+      // the order above, as scheduling groups
+      fwd_stage_sched<NM, NF, EVEN, PD>(std::make_integer_sequence<int, 2 * NM>());
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     // 3-deep ring: step j computes from slot j % 3 while the loads of stage
@@ -344,66 +439,92 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
     // mode 0: fragment nf belongs to the up matrix when nf >= NF / 2
     auto is_up = [](int nf) { return MODE == 0 && nf >= NF / 2; };
 
-    // ---- the last group's scale: rt[column][0]
-    {
-      float sl[NF][4];
-#pragma unroll
-      for (int nf = 0; nf < NF; ++nf) {
-        const float *rt = is_up(nf) ? A.rt1 : A.rt0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sl[nf][i] = rt[((size_t)e * N + min(ocol[nf] + i, N - 1)) * NG];
-      }
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][nf][i] *= sl[nf][i];
-    }
-
-    // ---- adapter term: acc += (lam Z) B^T, K = rank in steps of 16.  B
-    // positions beyond r are zeroed with a bit mask; Z is read four floats at
-    // a time (one 16-byte load when r and the row stride allow it), two row
-    // fragments at a time to bound the registers in flight.  Mode 0: gate
-    // fragments take Z_g and B_g, up fragments Z_u and B_u.
+    // ---- the last group's scale (group 0's ratio) and the adapter term
+    // acc += (lam Z) B^T, K = rank in steps of 16 (mode 0: gate fragments
+    // take Z_g and B_g, up fragments Z_u and B_u).  Rank 16: all operands
+    // from the epilogue stage in ring slot NS % 3, one row fragment at a
+    // time; otherwise from global memory.
     constexpr int NSRC = MODE == 0 ? 2 : 1;
-    const bool zvec = ((A.r | A.ldz) & 3) == 0;
-    for (int j0 = 0; j0 < A.r; j0 += 16) {
-      uint32_t kmask[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg2 + i < A.r ? 0xFFFFu : 0u;
+    auto zbf = [&](f32x4_t z) {   // lam z rounded to bf16 (nearest even)
+      const uint32_t lo = cvt_pk_bf16(A.lam * z[0], A.lam * z[1]);
+      const uint32_t hi = cvt_pk_bf16(A.lam * z[2], A.lam * z[3]);
+      return __builtin_bit_cast(short4_t, u32x2_t{lo, hi});
+    };
+    if constexpr (ep_lds) {
+      const int es = NS % 3;
+      const int wc = w2 * WCOLS;   // the wave's first block column slot
       short4_t bv[NF];
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
-        const uint16_t *Bm = is_up(nf) ? A.B1 : A.B0;
-        const size_t rowb = ((size_t)e * N + min(col[nf], N - 1)) * A.r;
+        const f32x4_t sl = lds_ld<f32x4_t>(ldsX + es * ST_X + (wc + nfc(nf) + 4 * lg2) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          bv[nf][i] = (short)(Bm[rowb + min(j0 + 4 * lg2 + i, A.r - 1)] & kmask[i]);
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][nf][i] *= sl[i];
+        bv[nf] = lds_ld<short4_t>(ldsB + es * ST_B + (wc + nfc(nf) + lr2) * 32 + 8 * lg2);
       }
-      const int jz = min(j0 + 4 * lg2, A.r - 1);
 #pragma unroll
-      for (int src = 0; src < NSRC; ++src) {
-        const float *Zp = src ? A.Z1 : A.Z0;
+      for (int m = 0; m < NM; ++m) {
+        if (m & 1) __builtin_amdgcn_sched_barrier(0);
+        const int r = 16 * m + lr2;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const float *zr = Zp + (size_t)(p0 + min(16 * m + lr2, rows - 1)) * A.ldz;
-          f32x4_t z;
-          if (zvec) {
-            z = *reinterpret_cast<const f32x4_t *>(zr + jz);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = zr[min(j0 + 4 * lg2 + i, A.r - 1)];
-          }
-          short4_t av;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) av[i] = (short)f2bf(A.lam * z[i]);
+        for (int src = 0; src < NSRC; ++src) {
+          const f32x4_t z = lds_ld<f32x4_t>(ldsA + es * ST_A + r * 128 + (((4 * src + lg2) ^ row_swz(r)) << 4));
+          const short4_t av = zbf(z);
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
             if ((is_up(nf) ? 1 : 0) != src) continue;
             acc[m][nf] = mfma16(bv[nf], av, acc[m][nf]);
           }
-          if (m & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const float *rt = is_up(nf) ? A.rt1 : A.rt0;
+        const f32x4_t sl = *reinterpret_cast<const f32x4_t *>(rt + (size_t)e * NG * N + min(ocol[nf], N - 4));
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][nf][i] *= sl[i];
+      }
+      const bool zvec = ((A.r | A.ldz) & 3) == 0;
+      for (int j0 = 0; j0 < A.r; j0 += 16) {
+        uint32_t kmask[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg2 + i < A.r ? 0xFFFFu : 0u;
+        short4_t bv[NF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+          const uint16_t *Bm = is_up(nf) ? A.B1 : A.B0;
+          const size_t rowb = ((size_t)e * N + min(col[nf], N - 1)) * A.r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            bv[nf][i] = (short)(Bm[rowb + min(j0 + 4 * lg2 + i, A.r - 1)] & kmask[i]);
+        }
+        const int jz = min(j0 + 4 * lg2, A.r - 1);
+#pragma unroll
+        for (int src = 0; src < NSRC; ++src) {
+          const float *Zp = src ? A.Z1 : A.Z0;
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const float *zr = Zp + (size_t)(p0 + min(16 * m + lr2, rows - 1)) * A.ldz;
+            f32x4_t z;
+            if (zvec) {
+              z = *reinterpret_cast<const f32x4_t *>(zr + jz);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) z[i] = zr[min(j0 + 4 * lg2 + i, A.r - 1)];
+            }
+            const short4_t av = zbf(z);
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+              if ((is_up(nf) ? 1 : 0) != src) continue;
+              acc[m][nf] = mfma16(bv[nf], av, acc[m][nf]);
+            }
+            if (m & 1) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
@@ -534,9 +655,10 @@ void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, flo
                                                                    scale, out);
 }
 
-void launch_scale_ratio(const uint16_t *s, size_t cols, int ng, float *rt, hipStream_t st) {
+void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st) {
+  const size_t cols = (size_t)E * N;
   const size_t n = cols * (size_t)ng;
-  scale_ratio_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, n, ng, rt);
+  scale_ratio_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, N, ng, n, rt);
 }
 
 void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st) {
@@ -548,8 +670,11 @@ void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hi
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
                          hipStream_t st) {
   const int *c = cnt + cls, *s = cnt + 4 + cls;
-#define MOE_GG(MODE, NM)                                                   \
-  grouped_gemm_kernel<MODE, 4, NM><<<grid, 256, 0, st>>>(A, c, s)
+  // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
+  const bool epl = A.r == 16 && (A.ldz & 3) == 0;
+#define MOE_GG(MODE, NM)                                                        \
+  if (epl) grouped_gemm_kernel<MODE, 4, NM, true><<<grid, 256, 0, st>>>(A, c, s); \
+  else grouped_gemm_kernel<MODE, 4, NM, false><<<grid, 256, 0, st>>>(A, c, s)
   if (mode == 0) {
     if (cls == 0) MOE_GG(0, 8); else if (cls == 1) MOE_GG(0, 6); else if (cls == 2) MOE_GG(0, 4); else MOE_GG(0, 2);
   } else {

@@ -157,14 +157,14 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
     const int c0 = nt * GT_BN;
 
     // A staging: wave w, load i covers rows 8 (AOPS w + i) .. +7 (8 chunks of
-    // 16 B each); chunk c of row r lives at c ^ (r & 7)
+    // 16 B each); chunk c of row r lives at c ^ row_swz(r)
     // (mode 0 with gate scaling: the rows of dy by token)
     const bool tokrows = MODE == 0 && A.gsc != nullptr;
     uint32_t aoff[AOPS];
 #pragma unroll
     for (int i = 0; i < AOPS; ++i) {
       const int r = 8 * (w * AOPS + i) + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
+      const int c = (lane & 7) ^ row_swz(r);
       const int p = p0 + min(r, rows - 1);
       const int arow = tokrows ? A.perm_src[p] / A.kk : p;
       aoff[i] = (uint32_t)arow * (uint32_t)(A.lda * 2) + c * 16;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
                    ls = ldsS + ((wu >> 1) * GT_KS + 32 * (wu & 1)) * 4;
     // per-lane LDS read bases (bytes); the rest of every read address is a
     // compile-time constant
-    const uint32_t offA0 = opaque(ldsA + (16 * NMH * wm + lr) * 128 + (((2 * lg) ^ (lr & 7)) << 4)),
+    const uint32_t offA0 = opaque(ldsA + (16 * NMH * wm + lr) * 128 + (((2 * lg) ^ row_swz(lr)) << 4)),
                    offB = opaque(ldsB + (128 * wn + lr) * 32 + 8 * lg),
                    offS = opaque(ldsS + (wn * GT_KS + 16 * lg) * 4);
 

@@ -72,6 +72,7 @@ struct MfmaGemmArgs {
   const float *rsum; int ld_rsum;         // per A row, per group of 128: -136 * sum of the row
   const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
   int K, N, NT;                           // reduction, columns per matrix, N-tiles per M-tile
+  // rt: scale ratios [E][K/128][N] of launch_scale_ratio
   const uint8_t *q0; const float *rt0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
   const uint8_t *q1; const float *rt1; const uint16_t *B1;   // up (mode 0)
   const float *Z0, *Z1; int ldz; int r; float lam;             // X A^T projections (float32)
@@ -83,9 +84,9 @@ int mfma_tile_rows();
 int mfma_blocks_per_cu();      // resident blocks per CU the kernel is built for
 void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, float *out,
                          hipStream_t st);
-// scale ratios of a quantized matrix ([cols][ng] bf16 -> [cols][ng] f32):
-// rt[c][g] = s[c][g-1] / s[c][g] for g >= 1, rt[c][0] = s[c][ng-1]
-void launch_scale_ratio(const uint16_t *s, size_t cols, int ng, float *rt, hipStream_t st);
+// scale ratios of a quantized matrix ([E][N][ng] bf16 -> [E][ng][N] f32):
+// rt[e][g][c] = s[e][c][g-1] / s[e][c][g] for g >= 1, rt[e][0][c] = s[e][c][ng-1]
+void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st);
 // expert tiles of 128 rows, the partial last one of each expert rounded up to
 // 32, 64, 96 or 128 rows, grouped by that class; cnt[8]: count and first
 // index of each class (128-row class first)

@@ -46,6 +46,12 @@ DEV float sigmoid_rcp(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z))
 
 DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// XOR swizzle of the 16-byte chunks of 128-byte LDS rows: chunk c of row r
+// is stored at position c ^ row_swz(r).  A 16-byte read by 16 lanes of rows
+// r0 .. r0+15 (one chunk index each) then touches every 16-byte bank group
+// of 256 bytes once: rows r and r + 8 share a bank group under r & 7 alone.
+DEV int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // D = A(16x32) B(32x16) + C.  Lane l holds A row l%16 / B column l%16 with 8
 // consecutive K values of lane group l/16; D lane l holds column l%16, rows
 // 4*(l/16) .. 4*(l/16)+3.
@@ -56,7 +62,6 @@ DEV f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
 DEV f32x4_t mfma16(short4_t a, short4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
 // writes lds_wave_base + 16 i.
 DEV void load_lds16(const void *gsrc, void *lds_wave_base) {
