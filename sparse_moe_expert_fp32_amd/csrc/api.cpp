@@ -148,7 +148,7 @@ size_t qt_slot_bytes(const moe_dims *d) {
 
 // ---- adapter backward workspace
 struct BwdLayout {
-  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, bt, wt,
+  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, bt, lt, wt,
       wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
   explicit BwdLayout(const moe_dims *d) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
@@ -167,6 +167,8 @@ struct BwdLayout {
               : 0;
     // B of down, gate, up transposed to [E][r][N] (bf16)
     bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
+    // A of down, gate, up transposed to [E][N][r] (bf16), for rank 16
+    lt = mf && d->rank == 16 ? c.take((size_t)d->n_experts * d->rank * (f + 2 * dm) * 2) : 0;
     // transposed int4 base + scales, two slots: down, then gate and up
     wt = mf ? c.take(2 * qt_slot_bytes(d)) : 0;
     wr_t = c.take((size_t)d->n_experts * dm * 4);
@@ -582,6 +584,17 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::launch_transpose_nr(down.B, E, d, r, bt_d, st);
     moe::launch_transpose_nr(gate.B, E, f, r, bt_g, st);
     moe::launch_transpose_nr(up.B, E, f, r, bt_u, st);
+    // A of each matrix as [E][N][r] for the epilogue stages of the
+    // input-gradient products (rank 16)
+    uint16_t *lt_d = nullptr, *lt_g = nullptr, *lt_u = nullptr;
+    if (r == 16) {
+      lt_d = at<uint16_t>(ws, L.lt);
+      lt_g = lt_d + (size_t)E * r * f;
+      lt_u = lt_g + (size_t)E * r * d;
+      moe::launch_transpose_rn(down.A, E, r, f, lt_d, st);
+      moe::launch_transpose_rn(gate.A, E, r, d, lt_g, st);
+      moe::launch_transpose_rn(up.A, E, r, d, lt_u, st);
+    }
     const size_t qsz = (size_t)E * d * f / 2, slot = qt_slot_bytes(dims);
     uint8_t *qt0 = at<uint8_t>(ws, L.wt), *qt1 = qt0 + slot;
     float *st0 = reinterpret_cast<float *>(qt0 + qsz), *st1 = reinterpret_cast<float *>(qt1 + qsz);
@@ -622,7 +635,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
       moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
     }
     M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qd; M.st0 = sd;
-    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
+    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A; M.LT0 = lt_d;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
     TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
@@ -664,7 +677,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
       moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
     }
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
-    X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A;
+    X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
     X.out = (uint16_t *)dXp; X.ldo = d;
     TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
     moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);

@@ -117,7 +117,7 @@ DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
 // Products are formed transposed (D^T = W^T A^T: the unpacked weights are the
 // first MFMA operand) so a lane holds one row and four consecutive columns and
 // the epilogue reads G, U and writes its results 8 bytes at a time.
-template <int MODE, int NMH>
+template <int MODE, int NMH, bool EPL>
 __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
     const MfmaGemmTArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
   // a 3-deep ring of stages (filled by LDS-DMA issued from inline asm, with
@@ -190,7 +190,45 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
                    offB = opaque(ldsB + (128 * wn + lr) * 32 + 8 * lg),
                    offS = opaque(ldsS + (wn * GT_KS + 16 * lg) * 4);
 
+    // the row gates (mode 0, rows of dy by token), fetched now for the epilogue
+    float gm[NMH];
+#pragma unroll
+    for (int m = 0; m < NMH; ++m) {
+      const int r = 16 * NMH * wm + lr + 16 * m;
+      gm[m] = MODE == 0 && A.gsc ? A.gsc[A.perm_src[p0 + min(r, rows - 1)]] : 1.f;
+    }
+
+    // EPL (rank 16): the epilogue's operands come through the ring as the
+    // stages after the last: stage NK brings the rows' dZ (Z_d, or Z_g then
+    // Z_u: 64 floats at most, with the A swizzle) into the A array and the
+    // transposed adapter A of the block columns (32 bytes each) into the
+    // word array; in mode 1 stage NK + 1 brings that of the second matrix.
+    auto stage_ep = [&](int part, int slot) {
+      uint32_t sa = la, sb = lb;
+      asm volatile("" : "+s"(sa), "+s"(sb));
+      if (part == 0) {
+        const char *zb = reinterpret_cast<const char *>(uniform_ptr(A.Z0));
+#pragma unroll
+        for (int i = 0; i < AOPS; ++i) {
+          const int r = 8 * (w * AOPS + i) + (lane >> 3);
+          const int c = ((lane & 7) ^ row_swz(r)) & (MODE == 1 ? 7 : 3);   // Z_d: 4 chunks
+          const uint32_t zo = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.ldz * 4) + c * 16;
+          dma16(zb, zo, sa + slot * TS_A + i * 1024);
+        }
+      }
+      const char *lb16 = reinterpret_cast<const char *>(uniform_ptr((part ? A.LT1 : A.LT0) + (size_t)e * N * 16));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int col = min(c0 + 32 * (2 * w + i) + (lane >> 1), N - 1);
+        dma16(lb16, (uint32_t)col * 32u + 16 * (lane & 1), sb + slot * TS_B + i * 1024);
+      }
+    };
     auto stage = [&](int jr, int slot) {
+      if (EPL && jr >= NK) {
+        if (jr == NK) stage_ep(0, slot);
+        else if (MODE == 1 && jr == NK + 1) stage_ep(1, slot);
+        return;
+      }
       const int j = min(jr, NK - 1);   // past the end: a harmless copy of the last step
       const bool second = MODE == 1 && j >= NKh;
       const int kj = second ? j - NKh : j;
@@ -298,42 +336,60 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
     // remove the 136 offset of the int4 operand (and apply the row's gate
     // when the rows are dy by token)
 #pragma unroll
-    for (int m = 0; m < NMH; ++m) {
-      float gm = 1.f;
-      if (MODE == 0 && A.gsc) gm = A.gsc[A.perm_src[p0 + min(rbase + 16 * m, rows - 1)]];
+    for (int m = 0; m < NMH; ++m)
 #pragma unroll
-      for (int nf = 0; nf < 8; ++nf) acc[m][nf] = (acc[m][nf] - corr[m]) * gm;
-    }
+      for (int nf = 0; nf < 8; ++nf) acc[m][nf] = (acc[m][nf] - corr[m]) * gm[m];
 
     // adapter term: acc += dZ L with L = A of the matrix ([r][N]), K = rank.
-    // Loads use clamped indices so that they issue together; rank positions
-    // beyond r are zeroed on the L side.
     const int nsrc = MODE == 1 ? 2 : 1;
-    for (int src = 0; src < nsrc; ++src) {
-      const float *Zp = src ? A.Z1 : A.Z0;
-      const uint16_t *Lm = src ? A.L1 : A.L0;
-      for (int j0 = 0; j0 < A.r; j0 += 16) {
-        uint32_t kmask[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg2 + i < A.r ? 0xFFFFu : 0u;
+    if constexpr (EPL) {
+      // from the epilogue stages: dZ rows in the A array of ring slot NK % 3,
+      // L^T rows in the word arrays of slots NK % 3 and (mode 1) NK % 3 + 1
+      const int es = NK % 3;
+      for (int src = 0; src < nsrc; ++src) {
+        const int ls = src ? (es == 2 ? 0 : es + 1) : es;
         short4_t lv[8];
 #pragma unroll
-        for (int nf = 0; nf < 8; ++nf) {
-          const int c = min(lcol + 16 * nf, N - 1);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            lv[nf][i] = (short)(Lm[((size_t)e * A.r + min(j0 + 4 * lg2 + i, A.r - 1)) * N + c] &
-                                kmask[i]);
-        }
+        for (int nf = 0; nf < 8; ++nf)
+          lv[nf] = lds_ld<short4_t>(ldsB + ls * TS_B + (128 * wn2 + 16 * nf + lr2) * 32 + 8 * lg2);
 #pragma unroll
         for (int m = 0; m < NMH; ++m) {
-          const size_t p = (size_t)(p0 + min(rbase + 16 * m, rows - 1));
-          short4_t av;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            av[i] = (short)f2bf(Zp[p * A.ldz + min(j0 + 4 * lg2 + i, A.r - 1)]);
+          const int r = rbase + 16 * m;
+          const f32x4_t z = lds_ld<f32x4_t>(ldsA + es * TS_A + r * 128 + (((4 * src + lg2) ^ row_swz(r)) << 4));
+          const short4_t av = __builtin_bit_cast(short4_t, u32x2_t{cvt_pk_bf16(z[0], z[1]), cvt_pk_bf16(z[2], z[3])});
 #pragma unroll
           for (int nf = 0; nf < 8; ++nf) acc[m][nf] = mfma16(lv[nf], av, acc[m][nf]);
+        }
+      }
+    } else {
+      // Loads use clamped indices so that they issue together; rank positions
+      // beyond r are zeroed on the L side.
+      for (int src = 0; src < nsrc; ++src) {
+        const float *Zp = src ? A.Z1 : A.Z0;
+        const uint16_t *Lm = src ? A.L1 : A.L0;
+        for (int j0 = 0; j0 < A.r; j0 += 16) {
+          uint32_t kmask[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kmask[i] = j0 + 4 * lg2 + i < A.r ? 0xFFFFu : 0u;
+          short4_t lv[8];
+#pragma unroll
+          for (int nf = 0; nf < 8; ++nf) {
+            const int c = min(lcol + 16 * nf, N - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              lv[nf][i] = (short)(Lm[((size_t)e * A.r + min(j0 + 4 * lg2 + i, A.r - 1)) * N + c] &
+                                  kmask[i]);
+          }
+#pragma unroll
+          for (int m = 0; m < NMH; ++m) {
+            const size_t p = (size_t)(p0 + min(rbase + 16 * m, rows - 1));
+            short4_t av;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              av[i] = (short)f2bf(Zp[p * A.ldz + min(j0 + 4 * lg2 + i, A.r - 1)]);
+#pragma unroll
+            for (int nf = 0; nf < 8; ++nf) acc[m][nf] = mfma16(lv[nf], av, acc[m][nf]);
+          }
         }
       }
     }
@@ -384,7 +440,12 @@ int mfma_t_blocks_per_cu() { return GT_BPC; }
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
                            hipStream_t st) {
   const int *c = cnt + cls, *s = cnt + 4 + cls;
-#define MOE_GT(MODE, NMH) grouped_gemm_t_kernel<MODE, NMH><<<grid, 256, 0, st>>>(A, c, s)
+  // operands of the epilogue through the LDS ring: rank 16, dZ rows 16-byte
+  // aligned, transposed adapter A given
+  const bool epl = A.r == 16 && (A.ldz & 3) == 0 && A.LT0 && (mode == 0 || A.LT1);
+#define MOE_GT(MODE, NMH)                                                           \
+  if (epl) grouped_gemm_t_kernel<MODE, NMH, true><<<grid, 256, 0, st>>>(A, c, s);   \
+  else grouped_gemm_t_kernel<MODE, NMH, false><<<grid, 256, 0, st>>>(A, c, s)
   if (mode == 0) {
     if (cls == 0) MOE_GT(0, 4); else if (cls == 1) MOE_GT(0, 3); else if (cls == 2) MOE_GT(0, 2); else MOE_GT(0, 1);
   } else {

@@ -107,6 +107,7 @@ struct MfmaGemmTArgs {
   const float *st0, *st1;                 // its scales per column group, [E][N/128][K]
   const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
   const uint16_t *L0, *L1;                // adapter A of the matrix, [E][r][N]
+  const uint16_t *LT0, *LT1;              // the same transposed, [E][N][r] (rank 16; or null)
   const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: SwiGLU backward, [S][N]
   uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
 };
@@ -145,6 +146,8 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
 int wgrad_tile_rows();
 void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st);
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
+// bf16 [E][r][N] -> [E][N][r]
+void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st);
 // the launch of tile class cls of launch_class_tiles (cnt: counts and starts)
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
                            hipStream_t st);

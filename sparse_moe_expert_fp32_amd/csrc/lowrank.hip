@@ -376,9 +376,70 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
 
 int wgrad_tile_rows() { return WG_TILE; }
 
+// out[e][n][j] = in[e][j][n] for bf16 [E][r][N] -> [E][N][r]: one block per
+// (256 values of n, expert), read as r row segments of 512 bytes, written
+// as one contiguous run of 256 r values, through LDS.
+__global__ __launch_bounds__(256) void transpose_rn_kernel(const uint16_t *__restrict__ in, int r,
+                                                           int N, uint16_t *__restrict__ out) {
+  __shared__ uint16_t t[TN_N * 33];   // [n][j], j < r <= 32, padded
+  const int e = blockIdx.y, n0 = blockIdx.x * TN_N, tid = threadIdx.x;
+  const int nn = min(TN_N, N - n0);
+  for (int i = tid; i < nn * r; i += 256) {
+    const int j = i / nn, n = i - j * nn;
+    t[n * 33 + j] = in[((size_t)e * r + j) * N + n0 + n];
+  }
+  __syncthreads();
+  uint16_t *dst = out + ((size_t)e * N + n0) * r;
+  for (int i = tid; i < nn * r; i += 256) {
+    const int n = i / r, j = i - n * r;
+    dst[i] = t[n * 33 + j];
+  }
+}
+
+// Rank 16: one thread per n, 16 values of 2 bytes each way; the column
+// side moves as two 16-byte accesses, the row side as coalesced 2-byte
+// accesses across the wave.
+__global__ __launch_bounds__(256) void transpose_rn16_kernel(const uint16_t *__restrict__ in, int N,
+                                                             uint16_t *__restrict__ out) {
+  const int e = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const uint16_t *src = in + (size_t)e * 16 * N + n;
+  uint32_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (uint32_t)src[(2 * j) * (size_t)N] | ((uint32_t)src[(2 * j + 1) * (size_t)N] << 16);
+  uint4 *dst = reinterpret_cast<uint4 *>(out + ((size_t)e * N + n) * 16);
+  dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
+  dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
+}
+__global__ __launch_bounds__(256) void transpose_nr16_kernel(const uint16_t *__restrict__ in, int N,
+                                                             uint16_t *__restrict__ out) {
+  const int e = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const uint4 *src = reinterpret_cast<const uint4 *>(in + ((size_t)e * N + n) * 16);
+  const uint4 a = src[0], b = src[1];
+  const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint16_t *dst = out + (size_t)e * 16 * N + n;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    dst[(2 * j) * (size_t)N] = (uint16_t)(v[j] & 0xFFFFu);
+    dst[(2 * j + 1) * (size_t)N] = (uint16_t)(v[j] >> 16);
+  }
+}
+
+void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st) {
+  dim3 grid((N + TN_N - 1) / TN_N, E);
+  if (r == 16 && ((uintptr_t)out & 15) == 0)   // (16-byte stores)
+    transpose_rn16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, N, (uint16_t *)out);
+  else
+    transpose_rn_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, r, N, (uint16_t *)out);
+}
+
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st) {
   dim3 grid((N + TN_N - 1) / TN_N, E);
-  transpose_nr_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, N, r, (uint16_t *)out);
+  if (r == 16 && ((uintptr_t)in & 15) == 0)    // (16-byte loads)
+    transpose_nr16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, N, (uint16_t *)out);
+  else
+    transpose_nr_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, N, r, (uint16_t *)out);
 }
 
 }  // namespace moe
