@@ -90,20 +90,22 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 // rt[e][g][c] = s'[g-1] / s'[g] for g >= 1 and rt[e][0][c] = s'[ng-1] (the
 // final multiplier), where s' is the bf16 scale with magnitudes below 2^-100
 // raised to 2^-100 (so a zero scale leaves a contribution of at most 2^-100
-// times its partial sum).  One thread per output element (the writes are
-// contiguous; a group's ratios of consecutive columns are contiguous too, so
-// the GEMM stages them as one run).
-__global__ void scale_ratio_kernel(const uint16_t *__restrict__ s, int N, int ng, size_t n,
-                                   float *__restrict__ rt) {
-  const size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (o >= n) return;
+// times its partial sum).  One thread per column: its ng scales are one
+// contiguous run, and each group's writes are contiguous across the wave.
+__global__ __launch_bounds__(256) void scale_ratio_kernel(const uint16_t *__restrict__ s, int E,
+                                                          int N, int ng, float *__restrict__ rt) {
+  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= N) return;
   auto guard = [](float v) { return fabsf(v) < 0x1p-100f ? 0x1p-100f : v; };
-  const int c = (int)(o % (size_t)N);
-  const size_t eg = o / (size_t)N;
-  const int g = (int)(eg % (size_t)ng);
-  const size_t i = ((eg / (size_t)ng) * N + c) * ng + g;   // s[e][c][g]
-  const float cur = guard(bf2f(s[i]));
-  rt[o] = g == 0 ? guard(bf2f(s[i + ng - 1])) : guard(bf2f(s[i - 1])) / cur;
+  const uint16_t *sc = s + ((size_t)e * N + c) * ng;
+  float *out = rt + (size_t)e * ng * N + c;
+  float prev = guard(bf2f(sc[0]));
+  for (int g = 1; g < ng; ++g) {
+    const float cur = guard(bf2f(sc[g]));
+    out[(size_t)g * N] = prev / cur;
+    prev = cur;
+  }
+  out[0] = prev;   // the last scale
 }
 
 // ------------------------------------------------------- stage schedule --
@@ -656,9 +658,8 @@ void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, flo
 }
 
 void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st) {
-  const size_t cols = (size_t)E * N;
-  const size_t n = cols * (size_t)ng;
-  scale_ratio_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, N, ng, n, rt);
+  dim3 grid((N + 255) / 256, E);
+  scale_ratio_kernel<<<grid, 256, 0, st>>>(s, E, N, ng, rt);
 }
 
 void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st) {
