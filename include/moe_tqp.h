@@ -258,7 +258,8 @@ typedef enum {
   MOE_KT_GATEUP = 3,        /* gate/up expert GEMM with SwiGLU epilogue     */
   MOE_KT_DOWN = 4,          /* down expert GEMM                             */
   MOE_KT_COMBINE = 5,       /* gate-weighted combine                        */
-  MOE_KT_GATE_GRAD = 6,     /* gate / router-input gradient, dO             */
+  MOE_KT_GATE_GRAD = 6,     /* gate / router-input gradient (dO, or on the
+                               matrix-core path the final sum of dX)       */
   MOE_KT_BWD_DOWN = 7,      /* dH = dO W_d + dZ_d A_d^T (and SwiGLU bwd)    */
   MOE_KT_BWD_GATEUP = 8,    /* dX_perm = dG W_g + dU W_u + ...              */
   MOE_KT_COUNT = 9

@@ -566,11 +566,13 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   void *dXp = at<char>(ws, L.dXp);
   void *dG = at<char>(ws, L.dG), *dU = at<char>(ws, L.dU);
 
-  // gate path (and dO)
+  // gate path: W_r^T for the router-input gradient; the float32 kernels also
+  // take dO from this pass, the matrix-core path runs it last (below)
   moe::launch_transpose_f32(w_router, d, E, wr_t, st);
-  TIMED(MOE_KT_GATE_GRAD, st,
-        moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r, dO,
-                              st));
+  if (!use_mfma(dims))
+    TIMED(MOE_KT_GATE_GRAD, st,
+          moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r,
+                                dO, st));
 
   if (use_mfma(dims)) {
     int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
@@ -680,7 +682,15 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
     X.out = (uint16_t *)dXp; X.ldo = d;
     TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
-    moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
+    // gate gradient and the per-token sum of dX_perm, one pass per token
+    TIMED(MOE_KT_GATE_GRAD, st, {
+      if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, dx,
+                                 st)) {
+        moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r,
+                              nullptr, st);
+        moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
+      }
+    });
     return hip_status("moe_adapter_bwd");
   }
 

@@ -171,6 +171,96 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(
   }
 }
 
+// ---- one wave per token (bf16 activations, d a multiple of 8)
+//
+// A wave walks its token's row in chunks of 512 columns (8 per lane, 16-byte
+// accesses); the k slots are taken in KB batches of 4, fully unrolled, so all
+// of a chunk's row loads are independent and in flight together.  Slots past
+// k read slot k-1's row again (in bounds, from cache) and are masked out.
+
+// The backward's per-token tail on the matrix-core path (dO is never formed
+// there), after the expert input-gradients dX_perm:
+//   dgamma_j = <dy_t, e_out[p_j]>,  dl_j = gamma_j (dgamma_j - sum_i gamma_i dgamma_i)
+//   dx[t]    = sum_j dl_j * W_r[:, e_j] + sum_j dX_perm[p_j]   (j ascending, float32)
+// The same sums as gate_grad_kernel followed by unpermute_sum_kernel, without
+// the float32 router-gradient rows between them.
+template <int KB>
+__global__ __launch_bounds__(256) void token_bwd_wave_kernel(
+    const bf16_t *__restrict__ dy, const bf16_t *__restrict__ e_out,
+    const int32_t *__restrict__ topk_idx, const float *__restrict__ gates,
+    const int32_t *__restrict__ slot_pos, const float *__restrict__ wr_t,
+    const bf16_t *__restrict__ dxp, int T, int d, int k, bf16_t *__restrict__ dx) {
+  constexpr int KM = 4 * KB;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  int p[KM], e[KM];
+  float g[KM], part[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int jc = j < k ? j : k - 1;
+    p[j] = slot_pos[(size_t)t * k + jc];
+    e[j] = topk_idx[(size_t)t * k + jc];
+    g[j] = gates[(size_t)t * k + jc];
+    part[j] = 0.f;
+  }
+  for (int c = lane * 8; c < d; c += 512) {
+    float gy[8], v[KM][8];
+    Vec16<bf16_t>::ld(dy + (size_t)t * d + c, gy);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) Vec16<bf16_t>::ld(e_out + (size_t)p[j] * d + c, v[j]);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = fmaf(gy[i], v[j][i], s);
+      part[j] += s;
+    }
+  }
+  float mean = 0.f;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    float s = part[j];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    part[j] = s;
+    if (j < k) mean = fmaf(g[j], s, mean);
+  }
+  float dl[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) dl[j] = g[j] * (part[j] - mean);
+  // 4 columns per lane here (256-column chunks): the float32 W_r rows make
+  // this pass twice as wide in registers as the first
+  for (int c = lane * 4; c < d; c += 256) {
+    float4 w[KM];
+    uint2 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      w[j] = *reinterpret_cast<const float4 *>(wr_t + (size_t)e[j] * d + c);
+      v[j] = *reinterpret_cast<const uint2 *>(dxp + (size_t)p[j] * d + c);
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) {
+        acc[0] = fmaf(dl[j], w[j].x, acc[0]);
+        acc[1] = fmaf(dl[j], w[j].y, acc[1]);
+        acc[2] = fmaf(dl[j], w[j].z, acc[2]);
+        acc[3] = fmaf(dl[j], w[j].w, acc[3]);
+      }
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) {
+        acc[0] += __uint_as_float(v[j].x << 16);
+        acc[1] += __uint_as_float(v[j].x & 0xFFFF0000u);
+        acc[2] += __uint_as_float(v[j].y << 16);
+        acc[3] += __uint_as_float(v[j].y & 0xFFFF0000u);
+      }
+    *reinterpret_cast<uint2 *>(dx + (size_t)t * d + c) =
+        make_uint2(pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3]));
+  }
+}
+
 // dx[t] = dx_r[t] + sum_j dxp[slot_pos[t*k+j]]   (j ascending)
 template <typename T, typename TP>
 __global__ __launch_bounds__(256) void unpermute_sum_kernel(const float *__restrict__ dx_r,
@@ -218,6 +308,24 @@ void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_
     gate_grad_kernel<float><<<Tn, 256, 0, st>>>((const float *)dy, (const float *)e_out,
                                                 topk_idx, gates, slot_pos, wr_t, d, k, dx_r,
                                                 (float *)dO);
+}
+
+bool launch_token_bwd(const void *dy, const void *e_out, const int32_t *topk_idx,
+                      const float *gates, const int32_t *slot_pos, const float *wr_t,
+                      const void *dxp, int Tn, int d, int k, void *dx, hipStream_t st) {
+  if (d % 8 != 0 || k > 16) return false;
+  const int wgrid = (Tn + 3) / 4;
+  const bf16_t *a = (const bf16_t *)dy, *b = (const bf16_t *)e_out, *c = (const bf16_t *)dxp;
+  bf16_t *o = (bf16_t *)dx;
+#define MOE_TB(KB) token_bwd_wave_kernel<KB><<<wgrid, 256, 0, st>>>(a, b, topk_idx, gates, slot_pos, wr_t, c, Tn, d, k, o)
+  switch ((k + 3) / 4) {
+    case 1: MOE_TB(1); break;
+    case 2: MOE_TB(2); break;
+    case 3: MOE_TB(3); break;
+    default: MOE_TB(4); break;
+  }
+#undef MOE_TB
+  return true;
 }
 
 void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void *dxp,

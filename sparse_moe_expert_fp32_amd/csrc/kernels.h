@@ -26,6 +26,12 @@ void launch_transpose_f32(const float *in, int rows, int cols, float *out, hipSt
 void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_t *topk_idx,
                       const float *gates, const int32_t *slot_pos, const float *wr_t, int T,
                       int d, int k, float *dx_r, void *dO, hipStream_t st);
+// matrix-core path (bf16, no dO): the gate gradient and the gather of dX in
+// one pass per token, dx[t] = sum_j dl_j W_r[:, e_j] + sum_j dxp[p_j]; returns
+// false (nothing launched) when the shape is not covered (d % 8, k > 16)
+bool launch_token_bwd(const void *dy, const void *e_out, const int32_t *topk_idx,
+                      const float *gates, const int32_t *slot_pos, const float *wr_t,
+                      const void *dxp, int T, int d, int k, void *dx, hipStream_t st);
 void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void *dxp,
                           const int32_t *slot_pos, int T, int d, int k, void *dx,
                           hipStream_t st);

@@ -52,6 +52,8 @@ def test_small_f32_ragged(cuda_ok):
     dict(E=8, k=8, T=50, cfg_id=232),                    # k = E
     dict(E=70, k=5, T=129, cfg_id=233),                  # E not a multiple of 64
     dict(E=130, k=12, T=64, cfg_id=234, router_bias_var=0.0),  # many empty experts
+    dict(E=40, k=13, T=45, cfg_id=235),                  # k not a multiple of 4
+    dict(E=48, k=20, T=40, cfg_id=236),                  # k > 16: block-per-token kernels
 ])
 def test_edge_shapes(cuda_ok, kw):
     cfg = cfg_of(**kw)
