@@ -59,7 +59,7 @@ constexpr int GM_KS = 64;    // K per pipeline stage (half a group)
 // column), and the group data: the scale ratio per block column (256
 // floats), the per-row start values (128 floats) and a copy of those (128
 // floats, so that every wave issues the same number of loads).
-constexpr int ST_A = GM_BM * GM_KS * 2, ST_B = 256 * GM_KS / 2, ST_X = 512 * 4;
+constexpr int ST_B = 256 * GM_KS / 2, ST_X = 512 * 4;   // (the A stage holds the class's rows)
 
 // ---------------------------------------------------------------- row sums --
 // out[row][g] = scale * (sum of a[row][g*G .. g*G+G), bf16 values, float32 sum
@@ -140,12 +140,16 @@ DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
 // from LDS feeds four matrix instructions).  NM (2, 4, 6, 8) is the number of
 // 16-row fragments of the item's tile class: each class of tiles (32, 64, 96,
 // 128 rows) is its own launch, so a short tail tile costs only its rows.
+// blocks per CU of tile class NM: the 32-row class (A ring of 12 KB, about
+// 130 VGPRs) runs three, the others two
+constexpr int gm_bpc(int NM) { return NM <= 2 ? 3 : GM_BPC; }
+
 template <int MODE, int WAVES, int NM, bool EPL>
-__global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
+__global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_gemm_kernel(
     const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
   // (hip-clang passes the second launch bound through as the minimum number
-  // of waves per SIMD: two blocks per CU are WAVES / 2 waves per SIMD, i.e.
-  // at most 256 (4 waves) or 128 (8 waves) VGPRs.)
+  // of waves per SIMD: b blocks per CU are b WAVES / 4 waves per SIMD, i.e.
+  // at most 256 VGPRs for two blocks of four waves, 168 for three.)
   constexpr int NF = 16 / WAVES;                 // column fragments per wave
   constexpr int BOPS = 8 / WAVES;                // int4-word loads per wave and stage
   constexpr int NT_ = 64 * WAVES;                // threads
@@ -157,10 +161,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void grouped_gemm_kernel(
   constexpr auto nfc = [](int nf) {
     return MODE == 0 ? (nf / (NF / 2)) * 128 + (nf % (NF / 2)) * 16 : nf * 16;
   };
-  // a 3-deep ring of half-group stages; after the K loop the first 4 KB of
+  // a 3-deep ring of half-group stages; after the K loop the first 2 KB of
   // the A ring hold the cross-wave row sums of H.
   // (ringA 32-byte aligned: the second substep's chunk is the first's
   // address with bit 4 flipped)
+  constexpr int ST_A = 16 * NM * GM_KS * 2;     // A stage: the class's rows x 64 K
+  static_assert(3 * ST_A >= WAVES * GM_BM * 4, "the row-sum exchange lives in the A ring");
   __shared__ __attribute__((aligned(32))) uint4 ringA[3][ST_A / 16];
   __shared__ uint4 ringB[3][ST_B / 16];
   __shared__ float ringX[3][ST_X / 4];
@@ -671,6 +677,8 @@ void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hi
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
                          hipStream_t st) {
   const int *c = cnt + cls, *s = cnt + 4 + cls;
+  // grid: GM_BPC blocks per CU; the 32-row class runs gm_bpc(2) per CU
+  if (cls == 3) grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
   // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
 #define MOE_GG(MODE, NM)                                                        \

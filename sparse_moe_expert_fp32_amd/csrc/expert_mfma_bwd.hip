@@ -98,7 +98,10 @@ __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restr
 // register plus a compile-time offset): A rows (128 x 64 bf16, 16-byte chunks
 // XOR-swizzled by row), int4 words (256 columns x 32 bytes), the scales of the
 // stage's 64 reduction steps for the block's two column groups.
-constexpr int TS_A = GT_BM * GT_KS * 2, TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;
+constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage holds the class's rows)
+// blocks per CU of tile class NMH, as LDS (the A ring holds 32 NMH rows) and
+// registers allow: 32-row tiles four, 64-row tiles three, the others two
+constexpr int gt_bpc(int NMH) { return NMH <= 1 ? 4 : NMH == 2 ? 3 : GT_BPC; }
 
 // ------------------------------------------------------------------ GEMM --
 // A bf16x8 fragment times 8 per-k scales, rounded back to bf16.
@@ -118,12 +121,13 @@ DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
 // first MFMA operand) so a lane holds one row and four consecutive columns and
 // the epilogue reads G, U and writes its results 8 bytes at a time.
 template <int MODE, int NMH, bool EPL>
-__global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(
+__global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
     const MfmaGemmTArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
   // a 3-deep ring of stages (filled by LDS-DMA issued from inline asm, with
   // explicit waits)
   // (ringA 32-byte aligned: the second substep's chunk is the first's
   // address with bit 4 flipped)
+  constexpr int TS_A = 32 * NMH * GT_KS * 2;   // A stage: the class's rows x 64 K
   __shared__ __attribute__((aligned(32))) uint4 ringA[3][TS_A / 16];
   __shared__ uint4 ringB[3][TS_B / 16];
   __shared__ float ringS[3][TS_S / 4];
@@ -440,6 +444,8 @@ int mfma_t_blocks_per_cu() { return GT_BPC; }
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
                            hipStream_t st) {
   const int *c = cnt + cls, *s = cnt + 4 + cls;
+  // grid: GT_BPC blocks per CU; the 64- and 32-row classes run more
+  if (cls >= 2) grid = (grid / GT_BPC * gt_bpc(cls == 2 ? 2 : 1)) & ~7;
   // operands of the epilogue through the LDS ring: rank 16, dZ rows 16-byte
   // aligned, transposed adapter A given
   const bool epl = A.r == 16 && (A.ldz & 3) == 0 && A.LT0 && (mode == 0 || A.LT1);
