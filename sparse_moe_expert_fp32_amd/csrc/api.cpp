@@ -162,7 +162,8 @@ struct BwdLayout {
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
     tiles_w = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * sizeof(int2)) : 0;
-    ntiles_w = mf ? c.take((1 + (size_t)d->n_experts) * sizeof(int)) : 0;   // count, first tile per expert
+    // count, first tile per expert, then the list of experts the reduction writes
+    ntiles_w = mf ? c.take((2 + 2 * (size_t)d->n_experts) * sizeof(int)) : 0;
     part = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * 2 * std::max(dm, f) * d->rank * 4)
               : 0;
     // B of down, gate, up transposed to [E][r][N] (bf16)
@@ -616,7 +617,8 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::launch_build_tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, st, ntiles_w + 1);
     moe::WgradMArgs W{};
     W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r; W.nsrc = 1;
-    W.tiles = tiles_w; W.ntiles = ntiles_w; W.tfirst = ntiles_w + 1; W.part = at<float>(ws, L.part);
+    W.tiles = tiles_w; W.ntiles = ntiles_w; W.tfirst = ntiles_w + 1; W.multi = ntiles_w + 1 + E;
+    W.part = at<float>(ws, L.part);
     // (= lam sum_p dy[t(p)][n] g_p Z_d[p][j])
     W.w = (const uint16_t *)dy; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
     W.gsc = gates;

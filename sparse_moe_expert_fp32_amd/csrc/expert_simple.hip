@@ -41,6 +41,21 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   for (int i = 0; i < c; ++i) tiles[first + i] = make_int2(e, lo + i * BM);
   if (first_out && e < E) first_out[e] = first;
   if (e == 1023) ntiles[0] = sc[e];
+  if (!first_out) return;
+  // after the first tiles: the number of experts not covered by exactly one
+  // tile (empty or split), then those experts in ascending order
+  __syncthreads();
+  const int f = e < E && c != 1 ? 1 : 0;
+  sc[e] = f;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int v = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  if (f) first_out[E + sc[e]] = e;   // position 1 + (exclusive prefix)
+  if (e == 1023) first_out[E] = sc[e];
 }
 
 // ------------------------------------------------------ int4 expert GEMM --

@@ -37,7 +37,8 @@ void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void
                           hipStream_t st);
 
 // ---- float32 expert kernels (expert_simple.hip)
-// first (optional, E ints): index of each expert's first tile
+// first (optional, 2E + 1 ints): index of each expert's first tile, then the
+// number of experts with no tile or more than one, then those experts
 void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles,
                         hipStream_t st, int *first = nullptr);
 int simple_tile_rows();
@@ -147,6 +148,7 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
   float *out; size_t oe; int oa, ob;
   const int2 *tiles; const int *ntiles;   // wgrad_tile_rows()-row tiles
   const int *tfirst;                      // [E] index of each expert's first tile
+  const int *multi;                       // count, then the experts not written by one tile
   float *part;                            // partials: [tiles][nsrc][wide][r]
 };
 int wgrad_tile_rows();

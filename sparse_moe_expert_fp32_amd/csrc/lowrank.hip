@@ -10,6 +10,8 @@
 //
 // Both run bf16 operands with float32 accumulation.  The reductions keep a
 // fixed order (no atomics), so results are reproducible bit for bit.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
@@ -293,25 +295,30 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
 // handles WR_PER consecutive outputs.
 constexpr int WR_PER = 4;
 
+// Only the experts on the list (empty ones, which get zeros, and split ones);
+// block row y takes list entries y, y + gridDim.y, ...
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const WgradMArgs G) {
-  const int e = blockIdx.y, tid = threadIdx.x;
-  const int count = G.offsets[e + 1] - G.offsets[e];
-  if (count > 0 && count <= WG_TILE) return;   // written directly by its single tile
+  const int tid = threadIdx.x;
   const size_t per = (size_t)G.wide * G.r;
   const size_t i0 = ((size_t)blockIdx.x * 256 + tid) * WR_PER;
-  const int t0 = count > 0 ? G.tfirst[e] : 0;
-  const int nt = (count + WG_TILE - 1) / WG_TILE;
+  const int nl = G.multi[0];
+  for (int q = blockIdx.y; q < nl; q += gridDim.y) {
+    const int e = G.multi[1 + q];
+    const int count = G.offsets[e + 1] - G.offsets[e];
+    const int t0 = count > 0 ? G.tfirst[e] : 0;
+    const int nt = (count + WG_TILE - 1) / WG_TILE;
 #pragma unroll
-  for (int u = 0; u < WR_PER; ++u) {
-    const size_t idx = i0 + u;
-    if (idx >= per * G.nsrc) return;
-    const int src = (int)(idx / per);
-    const size_t ab = idx - (size_t)src * per;
-    const int a = (int)(ab / G.r), b = (int)(ab - (size_t)a * G.r);
-    float sum = 0.f;
-    for (int t = 0; t < nt; ++t) sum += G.part[((size_t)(t0 + t) * G.nsrc + src) * per + ab];
-    float *out = src ? G.out1 : G.out;
-    out[(size_t)e * G.oe + (size_t)a * G.oa + (size_t)b * G.ob] = G.scale * sum;
+    for (int u = 0; u < WR_PER; ++u) {
+      const size_t idx = i0 + u;
+      if (idx >= per * G.nsrc) break;
+      const int src = (int)(idx / per);
+      const size_t ab = idx - (size_t)src * per;
+      const int a = (int)(ab / G.r), b = (int)(ab - (size_t)a * G.r);
+      float sum = 0.f;
+      for (int t = 0; t < nt; ++t) sum += G.part[((size_t)(t0 + t) * G.nsrc + src) * per + ab];
+      float *out = src ? G.out1 : G.out;
+      out[(size_t)e * G.oe + (size_t)a * G.oa + (size_t)b * G.ob] = G.scale * sum;
+    }
   }
 }
 
@@ -370,7 +377,8 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
     MOE_WG(4)
   }
 #undef MOE_WG
-  dim3 rgrid((unsigned)(((size_t)G.wide * G.r * G.nsrc + 256 * WR_PER - 1) / (256 * WR_PER)), G.E);
+  dim3 rgrid((unsigned)(((size_t)G.wide * G.r * G.nsrc + 256 * WR_PER - 1) / (256 * WR_PER)),
+             (unsigned)std::min(G.E, 64));
   wgrad_reduce_kernel<<<rgrid, 256, 0, st>>>(G);
 }
 
