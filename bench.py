@@ -218,9 +218,10 @@ def main():
         "layer_tflops": layer_flops(cfg, cfg.train) / (ms / 1e3) / 1e12,
         "layer_frac_of_bf16_peak": layer_flops(cfg, cfg.train) / (ms / 1e3) / PEAK_BF16,
         "forward_ms": fwd_ms,
-        # the frozen int4 base is re-laid out for the backward once at setup
-        # (moe_pack_base_t), like its quantisation; the timed steps run every
-        # per-step kernel
+        # the frozen int4 base is re-laid out once at setup (moe_pack_base_f
+        # for the forward, moe_pack_base_t for the backward), like its
+        # quantisation; the timed steps run every per-step kernel
+        "base_packed_for_forward": bool(getattr(L, "packed_f", None)),
         "base_packed_for_backward": bool(getattr(L, "packed", None)),
         "adamw": adamw,
         "forward_tokens_per_s": cfg.T / (fwd_ms / 1e3),

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -91,6 +91,11 @@ typedef struct {
  *         workspace on each call.  Results are the same either way.  Read
  *         only by the matrix-core path (bf16, group 128, d and f multiples
  *         of 128); ignored otherwise.  16-byte aligned.
+ *   qf    optional (may be NULL): the int4 base re-laid out for the
+ *         forward products of moe_expert_fwd, as written by moe_pack_base_f
+ *         from this q; the scales are still read from `scale`.  Same
+ *         contract as qt: pack once, results identical with NULL; read only
+ *         by the matrix-core path; 16-byte aligned.
  * Effective matrix: W_eff = W_hat + lambda * B A, i.e. for a row x,
  * x W_eff^T = x W_hat^T + lambda (x A^T) B^T. */
 typedef struct {
@@ -99,6 +104,7 @@ typedef struct {
   const void *A;
   const void *B;
   const void *qt;
+  const void *qf;
 } moe_qlora;
 
 /* Which call a workspace size is asked for. */
@@ -213,6 +219,23 @@ moe_status moe_pack_base_t_size(const moe_dims *dims, size_t *bytes);
 moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *q,
                            const uint16_t *scale, void *packed, size_t packed_bytes,
                            void *stream);
+
+/* Stage-major packing of one frozen base matrix for the forward (the qf
+ * field of moe_qlora).  The forward products reduce over K in steps of 64,
+ * each step reading 32 bytes of every output column; packed, one step of
+ * one expert is a contiguous run: for every expert e, block of 64 columns of
+ * K k0 and storage row n, 32 bytes hold q[e][n][k0/2 .. k0/2+31] unchanged
+ * (layout [E][K/64][N][32 B], the same byte count as q).  The products are
+ * those of moe_expert_fwd (skill card "Reversible Sparse MoE Single Node",
+ * Principle 3: the quantized base is fixed, so it is packed once).
+ *   matrix  MOE_MAT_GATE_UP (q [E][f][d/2]) or MOE_MAT_DOWN (q [E][d][f/2])
+ *   packed  device buffer of moe_pack_base_f_size() bytes, 16-byte aligned
+ *           (out; caller-owned); must not overlap q
+ * Only the matrix-core path has this layout: other dims give
+ * MOE_ERR_UNSUPPORTED.  Asynchronous on `stream`. */
+moe_status moe_pack_base_f_size(const moe_dims *dims, size_t *bytes);
+moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *q, void *packed,
+                           size_t packed_bytes, void *stream);
 
 /* Adapter optimizer step: AdamW on one float32 tensor of n elements (call it
  * once per adapter tensor: A and B of gate, up and down).  The optimizer

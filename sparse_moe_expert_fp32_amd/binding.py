@@ -32,7 +32,8 @@ class Dims(ctypes.Structure):
 
 class QLora(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("qt", ctypes.c_void_p)]
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("qt", ctypes.c_void_p),
+                ("qf", ctypes.c_void_p)]
 
 
 class AdamWHparams(ctypes.Structure):
@@ -65,6 +66,8 @@ def _load():
         "moe_adamw_step": [ctypes.POINTER(AdamWHparams), ctypes.c_int64, P, P, P, P, P, I32, P],
         "moe_pack_base_t_size": [DP, ctypes.POINTER(SZ)],
         "moe_pack_base_t": [DP, I32, P, P, P, SZ, P],
+        "moe_pack_base_f_size": [DP, ctypes.POINTER(SZ)],
+        "moe_pack_base_f": [DP, I32, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -79,7 +82,7 @@ LIB = _load()
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
            "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step",
-           "moe_pack_base_t_size", "moe_pack_base_t")
+           "moe_pack_base_t_size", "moe_pack_base_t", "moe_pack_base_f_size", "moe_pack_base_f")
 
 # kernel tags of moe_timer_start (moe_kernel_tag)
 KT = {"router_logits": 0, "router_topk": 1, "permute": 2, "gateup": 3, "down": 4, "combine": 5,
@@ -118,8 +121,8 @@ def dims_of(cfg, T: int | None = None) -> Dims:
                 cfg.act, cfg.lora_scale)
 
 
-def qlora(q, scale, A, B, qt=None) -> QLora:
-    return QLora(_p(q), _p(scale), _p(A), _p(B), _p(qt))
+def qlora(q, scale, A, B, qt=None, qf=None) -> QLora:
+    return QLora(_p(q), _p(scale), _p(A), _p(B), _p(qt), _p(qf))
 
 
 def moe_workspace_size(dm: Dims, call: int) -> int:
@@ -198,6 +201,18 @@ def moe_pack_base_t(dm: Dims, matrix: int, q, scale, packed, stream=None):
     _check(LIB.moe_pack_base_t(ctypes.byref(dm), matrix, _p(q), _p(scale), _p(packed),
                                packed.numel() if packed is not None else 0, _stream(stream)),
            "moe_pack_base_t")
+
+
+def moe_pack_base_f_size(dm: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    _check(LIB.moe_pack_base_f_size(ctypes.byref(dm), ctypes.byref(out)), "moe_pack_base_f_size")
+    return out.value
+
+
+def moe_pack_base_f(dm: Dims, matrix: int, q, packed, stream=None):
+    _check(LIB.moe_pack_base_f(ctypes.byref(dm), matrix, _p(q), _p(packed),
+                               packed.numel() if packed is not None else 0, _stream(stream)),
+           "moe_pack_base_f")
 
 
 def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step) -> AdamWHparams:

@@ -51,6 +51,8 @@ moe_status check_qlora(const moe_qlora &m, const char *name) {
     return fail(MOE_ERR_INVALID, std::string(name) + ": q, scale, A and B must be non-NULL");
   if (((uintptr_t)m.qt & 15) != 0)
     return fail(MOE_ERR_INVALID, std::string(name) + ": qt must be 16-byte aligned");
+  if (((uintptr_t)m.qf & 15) != 0)
+    return fail(MOE_ERR_INVALID, std::string(name) + ": qf must be 16-byte aligned");
   return MOE_OK;
 }
 
@@ -376,6 +378,38 @@ moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *
   return hip_status("moe_pack_base_t");
 }
 
+moe_status moe_pack_base_f_size(const moe_dims *dims, size_t *bytes) {
+  TRY(check_dims(dims));
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  if (!use_mfma(dims))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_pack_base_f: only the matrix-core path (bf16, group 128, d and f "
+                "multiples of 128) has a packed forward base");
+  *bytes = (size_t)dims->n_experts * dims->d_model * dims->d_ff / 2;
+  return MOE_OK;
+}
+
+moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *q, void *packed,
+                           size_t packed_bytes, void *stream) {
+  size_t need = 0;
+  TRY(moe_pack_base_f_size(dims, &need));
+  if (matrix != MOE_MAT_GATE_UP && matrix != MOE_MAT_DOWN)
+    return fail(MOE_ERR_INVALID, "moe_pack_base_f: matrix must be MOE_MAT_GATE_UP or MOE_MAT_DOWN");
+  REQUIRE(q && packed, "moe_pack_base_f: q and packed must be non-NULL");
+  REQUIRE(((uintptr_t)q & 15) == 0 && ((uintptr_t)packed & 15) == 0,
+          "moe_pack_base_f: q and packed must be 16-byte aligned");
+  if (packed_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_pack_base_f: packed buffer too small: need " +
+                                       std::to_string(need) + " bytes, got " +
+                                       std::to_string(packed_bytes));
+  const uintptr_t q0 = (uintptr_t)q, p0 = (uintptr_t)packed;
+  REQUIRE(p0 + need <= q0 || q0 + need <= p0, "moe_pack_base_f: packed must not overlap q");
+  const int d = dims->d_model, f = dims->d_ff;
+  const int N = matrix == MOE_MAT_GATE_UP ? f : d, K = matrix == MOE_MAT_GATE_UP ? d : f;
+  moe::launch_pack_fwd(q, dims->n_experts, N, K, (uint8_t *)packed, (hipStream_t)stream);
+  return hip_status("moe_pack_base_f");
+}
+
 moe_status moe_adamw_step(const moe_adamw_hparams *h, int64_t n, float *master,
                           const float *grad, float *m, float *v, void *param, int32_t param_dtype,
                           void *stream) {
@@ -475,8 +509,12 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
     M.tiles = tiles_m; M.offsets = offsets;
     M.K = d; M.N = f; M.NT = (f + 127) / 128;
-    M.q0 = gate.q; M.rt0 = rt_g; M.B0 = (const uint16_t *)gate.B;
-    M.q1 = up.q; M.rt1 = rt_u; M.B1 = (const uint16_t *)up.B;
+    // the stage-major packed base when both matrices have one
+    M.q_packed = gate.qf && up.qf;
+    M.q0 = M.q_packed ? (const uint8_t *)gate.qf : gate.q; M.rt0 = rt_g;
+    M.B0 = (const uint16_t *)gate.B;
+    M.q1 = M.q_packed ? (const uint8_t *)up.qf : up.q; M.rt1 = rt_u;
+    M.B1 = (const uint16_t *)up.B;
     M.Z0 = Z; M.Z1 = Z + r; M.ldz = 3 * r; M.r = r; M.lam = lam;
     M.out = (uint16_t *)H; M.ldo = f;
     M.saveG = save ? (uint16_t *)Gs : nullptr;
@@ -491,7 +529,9 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128;
     D.tiles = tiles_m; D.offsets = offsets;
     D.K = f; D.N = d; D.NT = (d + 255) / 256;
-    D.q0 = down.q; D.rt0 = rt_d; D.B0 = (const uint16_t *)down.B;
+    D.q_packed = down.qf != nullptr;
+    D.q0 = D.q_packed ? (const uint8_t *)down.qf : down.q; D.rt0 = rt_d;
+    D.B0 = (const uint16_t *)down.B;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
     TIMED(MOE_KT_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));

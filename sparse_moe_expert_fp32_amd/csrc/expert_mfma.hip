@@ -144,7 +144,8 @@ DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
 // 130 VGPRs) runs three, the others two
 constexpr int gm_bpc(int NM) { return NM <= 2 ? 3 : GM_BPC; }
 
-template <int MODE, int WAVES, int NM, bool EPL>
+// QP: q0, q1 in the stage-major packed layout (launch_pack_fwd)
+template <int MODE, int WAVES, int NM, bool EPL, bool QP>
 __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_gemm_kernel(
     const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
   // (hip-clang passes the second launch bound through as the minimum number
@@ -227,7 +228,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
     for (int i = 0; i < BOPS; ++i) {
       const int bc = 32 * (BOPS * w + i) + (lane >> 1);
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
-      qoff[i] = (uint32_t)c * (uint32_t)(K / 2) + 16 * (lane & 1);
+      // (packed base: column c of a stage at 32 c; plain: at c K/2)
+      qoff[i] = (uint32_t)c * (QP ? 32u : (uint32_t)(K / 2)) + 16 * (lane & 1);
     }
     // group data, 8 loads of 64 floats: loads 0-3 the ratios of block
     // columns 64 q + lane (group g at + g N), loads 4-5 the start values of
@@ -311,9 +313,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
 #pragma unroll
       for (int i = 0; i < AOPS; ++i)
         dma16(abase + (size_t)j * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
+      // stage step of the int4 words: 32 bytes (plain), a whole stage of
+      // the expert's columns, 32 N bytes (packed)
 #pragma unroll
       for (int i = 0; i < BOPS; ++i)
-        dma16(qbase + (size_t)j * (GM_KS / 2), qoff[i], sb + slot * ST_B + i * 1024);
+        dma16(qbase + (size_t)j * (QP ? (uint32_t)N * 32u : 32u), qoff[i], sb + slot * ST_B + i * 1024);
       if (decltype(evenc)::value) {
         uint32_t sx = lx;
         asm volatile("" : "+s"(sx));
@@ -599,6 +603,28 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
   }
 }
 
+// ------------------------------------------------------ forward packing --
+// q [E][N][K/2] -> [E][K/64][N][32 B]: each 32-byte K block of a storage row
+// moves unchanged to the run of its (expert, 64-wide K step).  One thread per
+// 16 bytes, in output order (the writes are contiguous; a wave's reads are 32
+// rows x 32 bytes).
+__global__ __launch_bounds__(256) void pack_fwd_kernel(const uint4 *__restrict__ q, int N, int K,
+                                                       size_t n16, uint4 *__restrict__ qf) {
+  const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= n16) return;
+  const size_t per_e = (size_t)N * K / 32;   // 16-byte units per expert
+  const size_t e = o / per_e, r = o - e * per_e;
+  const size_t j = r / ((size_t)N * 2), cr = r - j * N * 2;   // cr = 2 c + half
+  const size_t c = cr >> 1, h = cr & 1;
+  qf[o] = q[e * per_e + c * (K / 32) + j * 2 + h];
+}
+
+void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st) {
+  const size_t n16 = (size_t)E * N * K / 32;
+  pack_fwd_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(
+      reinterpret_cast<const uint4 *>(q), N, K, n16, reinterpret_cast<uint4 *>(qf));
+}
+
 // ------------------------------------------------------------ tile classes --
 // The work list of the grouped GEMMs: each expert's rows in tiles of 128,
 // the last (partial) one rounded up to 32, 64, 96 or 128 rows.  tiles holds
@@ -681,15 +707,20 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cl
   if (cls == 3) grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
   // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
-#define MOE_GG(MODE, NM)                                                        \
-  if (epl) grouped_gemm_kernel<MODE, 4, NM, true><<<grid, 256, 0, st>>>(A, c, s); \
-  else grouped_gemm_kernel<MODE, 4, NM, false><<<grid, 256, 0, st>>>(A, c, s)
+#define MOE_GG2(MODE, NM, QP)                                                        \
+  if (epl) grouped_gemm_kernel<MODE, 4, NM, true, QP><<<grid, 256, 0, st>>>(A, c, s);  \
+  else grouped_gemm_kernel<MODE, 4, NM, false, QP><<<grid, 256, 0, st>>>(A, c, s)
+#define MOE_GG(MODE, NM)                                                \
+  do {                                                                  \
+    if (A.q_packed) { MOE_GG2(MODE, NM, true); } else { MOE_GG2(MODE, NM, false); } \
+  } while (0)
   if (mode == 0) {
     if (cls == 0) MOE_GG(0, 8); else if (cls == 1) MOE_GG(0, 6); else if (cls == 2) MOE_GG(0, 4); else MOE_GG(0, 2);
   } else {
     if (cls == 0) MOE_GG(1, 8); else if (cls == 1) MOE_GG(1, 6); else if (cls == 2) MOE_GG(1, 4); else MOE_GG(1, 2);
   }
 #undef MOE_GG
+#undef MOE_GG2
 }
 
 }  // namespace moe

@@ -83,6 +83,7 @@ struct MfmaGemmArgs {
   const uint8_t *q0; const float *rt0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
   const uint8_t *q1; const float *rt1; const uint16_t *B1;   // up (mode 0)
   const float *Z0, *Z1; int ldz; int r; float lam;             // X A^T projections (float32)
+  bool q_packed;                          // q0, q1 in the stage-major layout of launch_pack_fwd
   uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
   uint16_t *saveG, *saveU;                // mode 0, optional
   float *rsum_out; int ld_rsum_out;       // mode 0: -136 * group sums of H rows
@@ -98,6 +99,8 @@ void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipS
 // 32, 64, 96 or 128 rows, grouped by that class; cnt[8]: count and first
 // index of each class (128-row class first)
 void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st);
+// int4 [E][N][K/2] -> stage-major [E][K/64][N][32 B] (K a multiple of 64)
+void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st);
 // the launch of tile class cls (0: 128-row tiles .. 3: 32-row tiles)
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
                          hipStream_t st);

@@ -60,17 +60,23 @@ class DeviceLayer:
             ((B.CALL_ADAPTER_BWD,) if bwd else ())
         self.ws = {c: torch.empty(max(1, B.moe_workspace_size(self.dm, c)), dtype=torch.uint8,
                                   device=self.dev) for c in calls}
-        # the frozen base re-laid out once for the backward (matrix-core path)
-        self.packed = {}
-        if bwd and pack_base and B.pack_base_supported(self.dm):
-            nb = B.moe_pack_base_t_size(self.dm)
+        # the frozen base re-laid out once (matrix-core path): stage-major for
+        # the forward, transposed for the backward
+        self.packed, self.packed_f = {}, {}
+        if pack_base and B.pack_base_supported(self.dm):
+            nbf = B.moe_pack_base_f_size(self.dm)
+            nbt = B.moe_pack_base_t_size(self.dm) if bwd else 0
             for m in MATS:
-                buf = torch.empty(nb, dtype=torch.uint8, device=self.dev)
-                B.moe_pack_base_t(self.dm, B.MAT_DOWN if m == "down" else B.MAT_GATE_UP,
-                                  self.t[f"q_{m}"], self.t[f"s_{m}"], buf)
-                self.packed[m] = buf
+                mat = B.MAT_DOWN if m == "down" else B.MAT_GATE_UP
+                self.packed_f[m] = torch.empty(nbf, dtype=torch.uint8, device=self.dev)
+                B.moe_pack_base_f(self.dm, mat, self.t[f"q_{m}"], self.packed_f[m])
+                if bwd:
+                    self.packed[m] = torch.empty(nbt, dtype=torch.uint8, device=self.dev)
+                    B.moe_pack_base_t(self.dm, mat, self.t[f"q_{m}"], self.t[f"s_{m}"],
+                                      self.packed[m])
             self.w = {m: B.qlora(self.t[f"q_{m}"], self.t[f"s_{m}"], self.t[f"A_{m}"],
-                                 self.t[f"B_{m}"], self.packed[m]) for m in MATS}
+                                 self.t[f"B_{m}"], self.packed.get(m), self.packed_f[m])
+                      for m in MATS}
         if bwd:
             self.dx = z(T, d)
             self.grads = {"dA_gate": z(E, r, d, dtype=f32), "dB_gate": z(E, f, r, dtype=f32),

@@ -143,21 +143,28 @@ def test_bitwise_deterministic(cuda_ok):
         assert np.array_equal(to_numpy(L.grads[n]), a[n]), n
 
 
-def test_packed_base_matches_per_call_transpose(cuda_ok):
-    """The backward with the base packed once (moe_pack_base_t) gives the same
-    bits as the backward that re-lays out the base in its workspace, also with
-    experts that receive no rows (the packing covers every expert)."""
+@pytest.mark.parametrize("kw", [
+    dict(T=60, E=64, k=2, cfg_id=270),                # 120 rows over 64 experts: some get none
+    dict(T=70, E=48, k=2, d=384, f=256, cfg_id=271),  # down output columns 384: a partial tile
+])
+def test_packed_base_matches_plain_layout(cuda_ok, kw):
+    """The layer with the base packed once (moe_pack_base_f for the forward,
+    moe_pack_base_t for the backward) gives the same bits as the layer that
+    reads the plain layout (and re-lays out the base in its workspace for the
+    backward), also with experts that receive no rows (the packing covers
+    every expert) and with a partial last column tile."""
     import torch
     from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
-    cfg = cfg_of(T=60, E=64, k=2, cfg_id=270)   # 120 rows over 64 experts: some get none
+    cfg = cfg_of(**kw)
     inp = inputs.generate(cfg, 0)
     out = []
     for pack in (False, True):
         L = DeviceLayer(cfg, inp, device="cuda:0", pack_base=pack)
-        assert bool(L.packed) == pack
+        assert bool(L.packed) == pack and bool(L.packed_f) == pack
         L.train_step()
         torch.cuda.synchronize()
-        out.append({"dx": to_numpy(L.dx), **{n: to_numpy(L.grads[n]) for n in ADAPTERS}})
+        out.append({"y": to_numpy(L.y), "e_out": to_numpy(L.e_out), "dx": to_numpy(L.dx),
+                    **{n: to_numpy(L.grads[n]) for n in ADAPTERS}})
         counts = to_numpy(L.counts)
     assert (counts == 0).any()
     for n in out[0]:
