@@ -509,12 +509,11 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
     M.tiles = tiles_m; M.offsets = offsets;
     M.K = d; M.N = f; M.NT = (f + 127) / 128;
-    // the stage-major packed base when both matrices have one
-    M.q_packed = gate.qf && up.qf;
-    M.q0 = M.q_packed ? (const uint8_t *)gate.qf : gate.q; M.rt0 = rt_g;
-    M.B0 = (const uint16_t *)gate.B;
-    M.q1 = M.q_packed ? (const uint8_t *)up.qf : up.q; M.rt1 = rt_u;
-    M.B1 = (const uint16_t *)up.B;
+    // the stage-major packed base where both matrices have one
+    M.q0 = gate.q; M.rt0 = rt_g; M.B0 = (const uint16_t *)gate.B;
+    M.q1 = up.q; M.rt1 = rt_u; M.B1 = (const uint16_t *)up.B;
+    M.qp0 = gate.qf && up.qf ? (const uint8_t *)gate.qf : nullptr;
+    M.qp1 = gate.qf && up.qf ? (const uint8_t *)up.qf : nullptr;
     M.Z0 = Z; M.Z1 = Z + r; M.ldz = 3 * r; M.r = r; M.lam = lam;
     M.out = (uint16_t *)H; M.ldo = f;
     M.saveG = save ? (uint16_t *)Gs : nullptr;
@@ -529,9 +528,8 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128;
     D.tiles = tiles_m; D.offsets = offsets;
     D.K = f; D.N = d; D.NT = (d + 255) / 256;
-    D.q_packed = down.qf != nullptr;
-    D.q0 = D.q_packed ? (const uint8_t *)down.qf : down.q; D.rt0 = rt_d;
-    D.B0 = (const uint16_t *)down.B;
+    D.q0 = down.q; D.rt0 = rt_d; D.B0 = (const uint16_t *)down.B;
+    D.qp0 = (const uint8_t *)down.qf;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
     TIMED(MOE_KT_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));

@@ -707,12 +707,17 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cl
   if (cls == 3) grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
   // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
+  // the packed base where given and used (P.q0 null: plain layout)
+  MfmaGemmArgs P = A;
+  const bool use_p = A.qp0 && (mode == 1 || (A.qp1 && cls != 0));
+  P.q0 = use_p ? A.qp0 : nullptr;
+  P.q1 = use_p ? A.qp1 : nullptr;
 #define MOE_GG2(MODE, NM, QP)                                                        \
-  if (epl) grouped_gemm_kernel<MODE, 4, NM, true, QP><<<grid, 256, 0, st>>>(A, c, s);  \
-  else grouped_gemm_kernel<MODE, 4, NM, false, QP><<<grid, 256, 0, st>>>(A, c, s)
+  if (epl) grouped_gemm_kernel<MODE, 4, NM, true, QP><<<grid, 256, 0, st>>>(QP ? P : A, c, s);  \
+  else grouped_gemm_kernel<MODE, 4, NM, false, QP><<<grid, 256, 0, st>>>(QP ? P : A, c, s)
 #define MOE_GG(MODE, NM)                                                \
   do {                                                                  \
-    if (A.q_packed) { MOE_GG2(MODE, NM, true); } else { MOE_GG2(MODE, NM, false); } \
+    if (P.q0) { MOE_GG2(MODE, NM, true); } else { MOE_GG2(MODE, NM, false); } \
   } while (0)
   if (mode == 0) {
     if (cls == 0) MOE_GG(0, 8); else if (cls == 1) MOE_GG(0, 6); else if (cls == 2) MOE_GG(0, 4); else MOE_GG(0, 2);

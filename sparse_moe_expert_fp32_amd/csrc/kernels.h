@@ -83,7 +83,10 @@ struct MfmaGemmArgs {
   const uint8_t *q0; const float *rt0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
   const uint8_t *q1; const float *rt1; const uint16_t *B1;   // up (mode 0)
   const float *Z0, *Z1; int ldz; int r; float lam;             // X A^T projections (float32)
-  bool q_packed;                          // q0, q1 in the stage-major layout of launch_pack_fwd
+  // q0, q1 in the stage-major layout of launch_pack_fwd (or null): used by
+  // the launches the layout speeds up (mode 1, and the short tile classes of
+  // mode 0, whose 128-row kernel needs more registers with it)
+  const uint8_t *qp0, *qp1;
   uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
   uint16_t *saveG, *saveU;                // mode 0, optional
   float *rsum_out; int ld_rsum_out;       // mode 0: -136 * group sums of H rows
