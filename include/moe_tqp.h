@@ -91,11 +91,11 @@ typedef struct {
  *         workspace on each call.  Results are the same either way.  Read
  *         only by the matrix-core path (bf16, group 128, d and f multiples
  *         of 128); ignored otherwise.  16-byte aligned.
- *   qf    optional (may be NULL): the int4 base re-laid out for the
- *         forward products of moe_expert_fwd, as written by moe_pack_base_f
- *         from this q; the scales are still read from `scale`.  Same
- *         contract as qt: pack once, results identical with NULL; read only
- *         by the matrix-core path; 16-byte aligned.
+ *   qf    optional (may be NULL): the base re-laid out for the forward
+ *         products of moe_expert_fwd, as written by moe_pack_base_f from
+ *         this q and scale.  Same contract as qt: pack once, results
+ *         identical with NULL; read only by the matrix-core path; 16-byte
+ *         aligned.
  * Effective matrix: W_eff = W_hat + lambda * B A, i.e. for a row x,
  * x W_eff^T = x W_hat^T + lambda (x A^T) B^T. */
 typedef struct {
@@ -225,17 +225,23 @@ moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *
  * each step reading 32 bytes of every output column; packed, one step of
  * one expert is a contiguous run: for every expert e, block of 64 columns of
  * K k0 and storage row n, 32 bytes hold q[e][n][k0/2 .. k0/2+31] unchanged
- * (layout [E][K/64][N][32 B], the same byte count as q).  The products are
- * those of moe_expert_fwd (skill card "Reversible Sparse MoE Single Node",
- * Principle 3: the quantized base is fixed, so it is packed once).
- *   matrix  MOE_MAT_GATE_UP (q [E][f][d/2]) or MOE_MAT_DOWN (q [E][d][f/2])
+ * (layout [E][K/64][N][32 B], the byte count of q).  The float32 table of
+ * group-scale ratios the forward applies follows, [E][K/128][N]: entry g >= 1
+ * of column n is s'[n][g-1] / s'[n][g] and entry 0 is s'[n][K/128-1], where
+ * s' is the bf16 scale with magnitudes below 2^-100 raised to 2^-100.  The
+ * products are those of moe_expert_fwd (skill card "Reversible Sparse MoE
+ * Single Node", Principle 3: the quantized base is fixed, so it is packed
+ * once).
+ *   matrix  MOE_MAT_GATE_UP (q [E][f][d/2], scale [E][f][d/128]) or
+ *           MOE_MAT_DOWN (q [E][d][f/2], scale [E][d][f/128])
  *   packed  device buffer of moe_pack_base_f_size() bytes, 16-byte aligned
  *           (out; caller-owned); must not overlap q
  * Only the matrix-core path has this layout: other dims give
  * MOE_ERR_UNSUPPORTED.  Asynchronous on `stream`. */
 moe_status moe_pack_base_f_size(const moe_dims *dims, size_t *bytes);
-moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *q, void *packed,
-                           size_t packed_bytes, void *stream);
+moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *q,
+                           const uint16_t *scale, void *packed, size_t packed_bytes,
+                           void *stream);
 
 /* Adapter optimizer step: AdamW on one float32 tensor of n elements (call it
  * once per adapter tensor: A and B of gate, up and down).  The optimizer

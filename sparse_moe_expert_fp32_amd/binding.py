@@ -67,7 +67,7 @@ def _load():
         "moe_pack_base_t_size": [DP, ctypes.POINTER(SZ)],
         "moe_pack_base_t": [DP, I32, P, P, P, SZ, P],
         "moe_pack_base_f_size": [DP, ctypes.POINTER(SZ)],
-        "moe_pack_base_f": [DP, I32, P, P, SZ, P],
+        "moe_pack_base_f": [DP, I32, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -209,8 +209,8 @@ def moe_pack_base_f_size(dm: Dims) -> int:
     return out.value
 
 
-def moe_pack_base_f(dm: Dims, matrix: int, q, packed, stream=None):
-    _check(LIB.moe_pack_base_f(ctypes.byref(dm), matrix, _p(q), _p(packed),
+def moe_pack_base_f(dm: Dims, matrix: int, q, scale, packed, stream=None):
+    _check(LIB.moe_pack_base_f(ctypes.byref(dm), matrix, _p(q), _p(scale), _p(packed),
                                packed.numel() if packed is not None else 0, _stream(stream)),
            "moe_pack_base_f")
 

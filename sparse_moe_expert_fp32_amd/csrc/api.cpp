@@ -378,6 +378,16 @@ moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *
   return hip_status("moe_pack_base_t");
 }
 
+// the forward-packed base: int4 words [E][K/64][N][32 B], then the scale
+// ratios [E][K/128][N] f32 (the same sizes for gate/up and down)
+size_t qf_bytes(const moe_dims *d) {
+  const size_t e = d->n_experts, df = (size_t)d->d_model * d->d_ff;
+  return e * df / 2 + e * df / 128 * 4;
+}
+float *qf_ratios(const moe_dims *d, const void *qf) {
+  return reinterpret_cast<float *>((char *)qf + (size_t)d->n_experts * d->d_model * d->d_ff / 2);
+}
+
 moe_status moe_pack_base_f_size(const moe_dims *dims, size_t *bytes) {
   TRY(check_dims(dims));
   if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
@@ -385,17 +395,18 @@ moe_status moe_pack_base_f_size(const moe_dims *dims, size_t *bytes) {
     return fail(MOE_ERR_UNSUPPORTED,
                 "moe_pack_base_f: only the matrix-core path (bf16, group 128, d and f "
                 "multiples of 128) has a packed forward base");
-  *bytes = (size_t)dims->n_experts * dims->d_model * dims->d_ff / 2;
+  *bytes = qf_bytes(dims);
   return MOE_OK;
 }
 
-moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *q, void *packed,
-                           size_t packed_bytes, void *stream) {
+moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *q,
+                           const uint16_t *scale, void *packed, size_t packed_bytes,
+                           void *stream) {
   size_t need = 0;
   TRY(moe_pack_base_f_size(dims, &need));
   if (matrix != MOE_MAT_GATE_UP && matrix != MOE_MAT_DOWN)
     return fail(MOE_ERR_INVALID, "moe_pack_base_f: matrix must be MOE_MAT_GATE_UP or MOE_MAT_DOWN");
-  REQUIRE(q && packed, "moe_pack_base_f: q and packed must be non-NULL");
+  REQUIRE(q && scale && packed, "moe_pack_base_f: q, scale and packed must be non-NULL");
   REQUIRE(((uintptr_t)q & 15) == 0 && ((uintptr_t)packed & 15) == 0,
           "moe_pack_base_f: q and packed must be 16-byte aligned");
   if (packed_bytes < need)
@@ -403,10 +414,13 @@ moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *
                                        std::to_string(need) + " bytes, got " +
                                        std::to_string(packed_bytes));
   const uintptr_t q0 = (uintptr_t)q, p0 = (uintptr_t)packed;
-  REQUIRE(p0 + need <= q0 || q0 + need <= p0, "moe_pack_base_f: packed must not overlap q");
+  const size_t qsz = (size_t)dims->n_experts * dims->d_model * dims->d_ff / 2;
+  REQUIRE(p0 + need <= q0 || q0 + qsz <= p0, "moe_pack_base_f: packed must not overlap q");
   const int d = dims->d_model, f = dims->d_ff;
   const int N = matrix == MOE_MAT_GATE_UP ? f : d, K = matrix == MOE_MAT_GATE_UP ? d : f;
-  moe::launch_pack_fwd(q, dims->n_experts, N, K, (uint8_t *)packed, (hipStream_t)stream);
+  const int E = dims->n_experts;
+  moe::launch_pack_fwd(q, E, N, K, (uint8_t *)packed, (hipStream_t)stream);
+  moe::launch_scale_ratio(scale, E, N, K / 128, qf_ratios(dims, packed), (hipStream_t)stream);
   return hip_status("moe_pack_base_f");
 }
 
@@ -494,9 +508,19 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     // per-row start values -136 * (row sum per group) and per-column scale ratios
     moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st);
-    moe::launch_scale_ratio(gate.scale, E, f, d / 128, rt_g, st);
-    moe::launch_scale_ratio(up.scale, E, f, d / 128, rt_u, st);
-    moe::launch_scale_ratio(down.scale, E, d, f / 128, rt_d, st);
+    // (the packed bases carry their ratio tables)
+    const bool pk_gu = gate.qf && up.qf;
+    if (pk_gu) {
+      rt_g = qf_ratios(dims, gate.qf);
+      rt_u = qf_ratios(dims, up.qf);
+    } else {
+      moe::launch_scale_ratio(gate.scale, E, f, d / 128, rt_g, st);
+      moe::launch_scale_ratio(up.scale, E, f, d / 128, rt_u, st);
+    }
+    if (down.qf)
+      rt_d = qf_ratios(dims, down.qf);
+    else
+      moe::launch_scale_ratio(down.scale, E, d, f / 128, rt_d, st);
     // Z_g = X A_g^T, Z_u = X A_u^T (rows gathered from x)
     moe::ProjMArgs Q{};
     Q.a = (const uint16_t *)x; Q.lda = d; Q.perm_src = perm_src; Q.kk = k;
@@ -512,8 +536,8 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
     // the stage-major packed base where both matrices have one
     M.q0 = gate.q; M.rt0 = rt_g; M.B0 = (const uint16_t *)gate.B;
     M.q1 = up.q; M.rt1 = rt_u; M.B1 = (const uint16_t *)up.B;
-    M.qp0 = gate.qf && up.qf ? (const uint8_t *)gate.qf : nullptr;
-    M.qp1 = gate.qf && up.qf ? (const uint8_t *)up.qf : nullptr;
+    M.qp0 = pk_gu ? (const uint8_t *)gate.qf : nullptr;
+    M.qp1 = pk_gu ? (const uint8_t *)up.qf : nullptr;
     M.Z0 = Z; M.Z1 = Z + r; M.ldz = 3 * r; M.r = r; M.lam = lam;
     M.out = (uint16_t *)H; M.ldo = f;
     M.saveG = save ? (uint16_t *)Gs : nullptr;

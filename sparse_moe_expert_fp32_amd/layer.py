@@ -69,7 +69,8 @@ class DeviceLayer:
             for m in MATS:
                 mat = B.MAT_DOWN if m == "down" else B.MAT_GATE_UP
                 self.packed_f[m] = torch.empty(nbf, dtype=torch.uint8, device=self.dev)
-                B.moe_pack_base_f(self.dm, mat, self.t[f"q_{m}"], self.packed_f[m])
+                B.moe_pack_base_f(self.dm, mat, self.t[f"q_{m}"], self.t[f"s_{m}"],
+                                  self.packed_f[m])
                 if bwd:
                     self.packed[m] = torch.empty(nbt, dtype=torch.uint8, device=self.dev)
                     B.moe_pack_base_t(self.dm, mat, self.t[f"q_{m}"], self.t[f"s_{m}"],

@@ -183,25 +183,26 @@ def test_misaligned_packed_base_rejected(B):
 
 def test_pack_f_size_and_support(B):
     big = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16")
-    assert B.moe_pack_base_f_size(big) == 460 * 2048 * 768 // 2
+    assert B.moe_pack_base_f_size(big) == 460 * 2048 * 768 // 2 + 460 * 2048 * 768 // 128 * 4
     for dm in (good(B), good(B, act="bf16"), B.dims(64, 192, 8, 2, 256, 4, 64, "bf16")):
         out = ctypes.c_size_t(7)
         assert B.LIB.moe_pack_base_f_size(ctypes.byref(dm), ctypes.byref(out)) == -2
         assert out.value == 7
 
 
-@pytest.mark.parametrize("matrix,q,packed,nbytes,status", [
-    (2, FAKE, 1 << 32, 1 << 40, -1),             # no such matrix
-    (0, None, 1 << 32, 1 << 40, -1),             # null q
-    (1, FAKE, None, 1 << 40, -1),                # null output
-    (0, FAKE, (1 << 32) + 8, 1 << 40, -1),       # misaligned output
-    (0, FAKE + 4, 1 << 32, 1 << 40, -1),         # misaligned q
-    (0, FAKE, FAKE + 64, 1 << 40, -1),           # output overlaps q
-    (0, FAKE, 1 << 32, 1024, -3),                # output too small
+@pytest.mark.parametrize("matrix,q,s,packed,nbytes,status", [
+    (2, FAKE, FAKE, 1 << 32, 1 << 40, -1),          # no such matrix
+    (0, None, FAKE, 1 << 32, 1 << 40, -1),          # null q
+    (0, FAKE, None, 1 << 32, 1 << 40, -1),          # null scale
+    (1, FAKE, FAKE, None, 1 << 40, -1),             # null output
+    (0, FAKE, FAKE, (1 << 32) + 8, 1 << 40, -1),    # misaligned output
+    (0, FAKE + 4, FAKE, 1 << 32, 1 << 40, -1),      # misaligned q
+    (0, FAKE, FAKE, FAKE + 64, 1 << 40, -1),        # output overlaps q
+    (0, FAKE, FAKE, 1 << 32, 1024, -3),             # output too small
 ])
-def test_pack_f_rejects_bad_arguments(B, matrix, q, packed, nbytes, status):
+def test_pack_f_rejects_bad_arguments(B, matrix, q, s, packed, nbytes, status):
     dm = B.dims(256, 256, 8, 2, 128, 16, 128, "bf16")
-    assert B.LIB.moe_pack_base_f(ctypes.byref(dm), matrix, q, packed, nbytes, None) == status
+    assert B.LIB.moe_pack_base_f(ctypes.byref(dm), matrix, q, s, packed, nbytes, None) == status
     assert B.LIB.moe_last_error().decode().startswith("moe_pack_base_f")
 
 
