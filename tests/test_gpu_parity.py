@@ -157,15 +157,22 @@ def test_packed_base_matches_plain_layout(cuda_ok, kw):
     from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
     cfg = cfg_of(**kw)
     inp = inputs.generate(cfg, 0)
+    from sparse_moe_expert_fp32_amd import binding as B
     out = []
-    for pack in (False, True):
-        L = DeviceLayer(cfg, inp, device="cuda:0", pack_base=pack)
-        assert bool(L.packed) == pack and bool(L.packed_f) == pack
+    for pack in (False, True, "mixed"):
+        L = DeviceLayer(cfg, inp, device="cuda:0", pack_base=bool(pack))
+        assert bool(L.packed) == bool(pack) and bool(L.packed_f) == bool(pack)
+        if pack == "mixed":
+            # a forward-packed down and gate but a plain up: gate/up falls back
+            # to the plain layout (both or neither), down stays packed
+            L.w["up"] = B.qlora(L.t["q_up"], L.t["s_up"], L.t["A_up"], L.t["B_up"],
+                                L.packed["up"], None)
         L.train_step()
         torch.cuda.synchronize()
         out.append({"y": to_numpy(L.y), "e_out": to_numpy(L.e_out), "dx": to_numpy(L.dx),
                     **{n: to_numpy(L.grads[n]) for n in ADAPTERS}})
         counts = to_numpy(L.counts)
     assert (counts == 0).any()
-    for n in out[0]:
-        assert np.array_equal(out[0][n], out[1][n]), n
+    for o in out[1:]:
+        for n in out[0]:
+            assert np.array_equal(out[0][n], o[n]), n
