@@ -185,6 +185,28 @@ def main():
                  "GB_s": nbytes / (opt_ms / 1e3) / 1e9, "frac_hbm": nbytes / (opt_ms / 1e3) / PEAK_HBM}
         log(f"adamw {opt_ms:.3f} ms for {n_par} adapter parameters")
 
+    # reversible residual block around the layer: the backward's replay
+    # x2 = y2 - MoE(y1), i.e. the layer forward recomputed from y1 and the
+    # coupling (moe_rev_couple), timed on its own; the reconstruction error
+    # is against the x2 the forward coupling started from
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(7)
+    x2 = torch.randn(cfg.T, cfg.d, generator=gen).to(L.dev).to(act)
+    y2, back = torch.empty_like(x2), torch.empty_like(x2)
+    L.rev_forward(x2, y2)
+    L.rev_inverse(y2, back)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        L.rev_inverse(y2, back)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    rev_ms = ev0.elapsed_time(ev1) / args.steps
+    rerr = (back.float() - x2.float()).abs()
+    reversible = {"replay_ms": rev_ms, "x2_max_abs_err": float(rerr.max()),
+                  "x2_exact_fraction": float((rerr == 0).float().mean())}
+    log(f"reversible replay {rev_ms:.3f} ms, x2 max abs error {float(rerr.max()):.3e}")
+
     per_launch_ms = k_ms / max(1, k_launches)
     launches_per_step = k_launches / args.steps
     flops_launch = gateup_flops(cfg) / launches_per_step
@@ -224,6 +246,7 @@ def main():
         "base_packed_for_forward": bool(getattr(L, "packed_f", None)),
         "base_packed_for_backward": bool(getattr(L, "packed", None)),
         "adamw": adamw,
+        "reversible": reversible,
         "forward_tokens_per_s": cfg.T / (fwd_ms / 1e3),
         "load": {"max": int(counts.max()), "mean": float(counts.mean()),
                  "empty_experts": int((counts == 0).sum())},

@@ -172,6 +172,22 @@ moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *s
                        const float *gates, void *y, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* Additive coupling of a reversible residual block around the layer (skill
+ * card "Reversible Sparse MoE Single Node": Principle 1, reconstruct rather
+ * than store activations; Pattern 1, addition/subtraction as the inverse
+ * operations; Implementation Considerations, reversible residual blocks and
+ * stateless routing).  With m = the layer output y for the block's other
+ * stream y1 (moe_combine):
+ *   sign = +1:  out = x + m   (forward:  y2 = x2 + MoE(y1))
+ *   sign = -1:  out = x - m   (inverse:  x2 = y2 - MoE(y1))
+ * over T * d_model values in the act dtype, float32 arithmetic with one
+ * rounding.  Routing is a pure function of y1, so recomputing m in the
+ * backward reproduces it bit for bit; the reconstruction of x2 is exact up
+ * to the two roundings to the act dtype.  out may alias x (not m).
+ * Asynchronous on `stream`. */
+moe_status moe_rev_couple(const moe_dims *dims, const void *x, const void *m, void *out,
+                          int32_t sign, void *stream);
+
 /* Adapter-only backward of route -> expert FFNs -> combine for an upstream
  * gradient dy (loss L = sum_t <dy_t, y_t>).  The selection is held fixed; the
  * router and every base matrix are frozen (no weight gradient), but the gates

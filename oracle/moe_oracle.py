@@ -398,3 +398,24 @@ def adamw_step(p, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
     vhat = v1 / (1.0 - beta2 ** step)
     p1 = p - lr * (mhat / (np.sqrt(vhat) + eps) + weight_decay * p)
     return p1, m1, v1
+
+
+# ---------------------------------------------- reversible residual block --
+# "Reversible Sparse MoE Single Node" (skill card), Principle 1 "Reversible
+# Recurrence Stack" and Pattern 1 "Reversible Layer Implementation": a block
+# reconstructs its input from its output instead of storing it, through
+# invertible operations such as addition and subtraction; Implementation
+# Considerations: reversible residual blocks, stateless routing.  The layer is
+# the block's function G: with streams (y1, x2),
+#     y2 = x2 + G(y1),        x2 = y2 - G(y1).
+
+def rev_forward(inputs: dict, x2, k: int, group: int, lam: float = 1.0,
+                topk_idx: np.ndarray | None = None) -> np.ndarray:
+    """y2 = x2 + MoE(y1), y1 = inputs["x"], in float64."""
+    return to_f64(x2) + forward(inputs, k, group, lam, topk_idx=topk_idx)["y"]
+
+
+def rev_inverse(inputs: dict, y2, k: int, group: int, lam: float = 1.0,
+                topk_idx: np.ndarray | None = None) -> np.ndarray:
+    """x2 = y2 - MoE(y1), MoE(y1) recomputed from y1, in float64."""
+    return to_f64(y2) - forward(inputs, k, group, lam, topk_idx=topk_idx)["y"]

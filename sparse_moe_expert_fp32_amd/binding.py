@@ -68,6 +68,7 @@ def _load():
         "moe_pack_base_t": [DP, I32, P, P, P, SZ, P],
         "moe_pack_base_f_size": [DP, ctypes.POINTER(SZ)],
         "moe_pack_base_f": [DP, I32, P, P, P, SZ, P],
+        "moe_rev_couple": [DP, P, P, P, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -82,7 +83,8 @@ LIB = _load()
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
            "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step",
-           "moe_pack_base_t_size", "moe_pack_base_t", "moe_pack_base_f_size", "moe_pack_base_f")
+           "moe_pack_base_t_size", "moe_pack_base_t", "moe_pack_base_f_size", "moe_pack_base_f",
+           "moe_rev_couple")
 
 # kernel tags of moe_timer_start (moe_kernel_tag)
 KT = {"router_logits": 0, "router_topk": 1, "permute": 2, "gateup": 3, "down": 4, "combine": 5,
@@ -201,6 +203,11 @@ def moe_pack_base_t(dm: Dims, matrix: int, q, scale, packed, stream=None):
     _check(LIB.moe_pack_base_t(ctypes.byref(dm), matrix, _p(q), _p(scale), _p(packed),
                                packed.numel() if packed is not None else 0, _stream(stream)),
            "moe_pack_base_t")
+
+
+def moe_rev_couple(dm: Dims, x, m, out, sign: int, stream=None):
+    _check(LIB.moe_rev_couple(ctypes.byref(dm), _p(x), _p(m), _p(out), sign, _stream(stream)),
+           "moe_rev_couple")
 
 
 def moe_pack_base_f_size(dm: Dims) -> int:

@@ -467,6 +467,17 @@ moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *s
   return hip_status("moe_combine");
 }
 
+moe_status moe_rev_couple(const moe_dims *dims, const void *x, const void *m, void *out,
+                          int32_t sign, void *stream) {
+  TRY(check_dims(dims));
+  REQUIRE(x && m && out, "moe_rev_couple: x, m and out must be non-NULL");
+  REQUIRE(sign == 1 || sign == -1, "moe_rev_couple: sign must be +1 or -1");
+  REQUIRE(out != m, "moe_rev_couple: out must not alias m");
+  moe::launch_rev_couple(dims->act == MOE_BF16, x, m, out, (size_t)dims->T * dims->d_model,
+                         (float)sign, (hipStream_t)stream);
+  return hip_status("moe_rev_couple");
+}
+
 moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
                           const int32_t *perm_src, moe_qlora gate, moe_qlora up, moe_qlora down,
                           void *e_out, void *save, void *ws, size_t ws_bytes, void *stream) {

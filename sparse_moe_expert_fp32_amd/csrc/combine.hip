@@ -9,6 +9,8 @@
 // through the gates into the router input follows from the full-precision
 // router of the same card (Implementation Considerations, TQP Quantization),
 // whose own weights are not trained here.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -259,6 +261,53 @@ __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
     *reinterpret_cast<uint2 *>(dx + (size_t)t * d + c) =
         make_uint2(pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3]));
   }
+}
+
+// Reversible coupling around the layer: out = x + sign * m elementwise, in
+// float32 with one rounding to T.  With m the layer's output for the other
+// stream y1 this is the additive coupling of a reversible residual block
+// (skill card "Reversible Sparse MoE Single Node", Pattern 1: addition and
+// subtraction as the invertible operations; Implementation Considerations:
+// reversible residual blocks, stateless routing): sign +1 gives
+// y2 = x2 + MoE(y1), sign -1 recovers x2 = y2 - MoE(y1).  VEC: 16-byte
+// accesses (every pointer 16-byte aligned), the grid strides over the data.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void rev_couple_kernel(const T *__restrict__ x,
+                                                         const T *__restrict__ m, T *out,
+                                                         size_t n, float sign) {
+  constexpr int V = Vec16<T>::N;
+  const size_t stride = (size_t)gridDim.x * 256;
+  const size_t t0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (VEC) {
+    for (size_t i = t0; i < n / V; i += stride) {
+      float a[V], b[V];
+      Vec16<T>::ld(x + i * V, a);
+      Vec16<T>::ld(m + i * V, b);
+#pragma unroll
+      for (int u = 0; u < V; ++u) a[u] = fmaf(sign, b[u], a[u]);
+      Vec16<T>::st(out + i * V, a);
+    }
+  }
+  for (size_t i = (VEC ? n / V * V : 0) + t0; i < n; i += stride)
+    Elem<T>::st(out, i, fmaf(sign, Elem<T>::ld(m, i), Elem<T>::ld(x, i)));
+}
+
+void launch_rev_couple(bool bf16, const void *x, const void *m, void *out, size_t n, float sign,
+                       hipStream_t st) {
+  const bool vec = (((uintptr_t)x | (uintptr_t)m | (uintptr_t)out) & 15) == 0;
+  const size_t work = (n + 7) / 8;
+  const unsigned grid = (unsigned)std::max<size_t>(1, std::min<size_t>((work + 255) / 256, 8192));
+#define MOE_RC(TY)                                                                              \
+  if (vec) rev_couple_kernel<TY, true><<<grid, 256, 0, st>>>((const TY *)x, (const TY *)m,      \
+                                                             (TY *)out, n, sign);               \
+  else rev_couple_kernel<TY, false><<<grid, 256, 0, st>>>((const TY *)x, (const TY *)m,         \
+                                                          (TY *)out, n, sign);
+  if (bf16) {
+    MOE_RC(bf16_t)
+  } else {
+    MOE_RC(float)
+  }
+#undef MOE_RC
 }
 
 // dx[t] = dx_r[t] + sum_j dxp[slot_pos[t*k+j]]   (j ascending)

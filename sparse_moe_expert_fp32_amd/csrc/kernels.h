@@ -36,6 +36,10 @@ void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void
                           const int32_t *slot_pos, int T, int d, int k, void *dx,
                           hipStream_t st);
 
+// out = x + sign * m over n act-dtype values (float32 arithmetic, one rounding)
+void launch_rev_couple(bool bf16, const void *x, const void *m, void *out, size_t n, float sign,
+                       hipStream_t st);
+
 // ---- float32 expert kernels (expert_simple.hip)
 // first (optional, 2E + 1 ints): index of each expert's first tile, then the
 // number of experts with no tile or more than one, then those experts

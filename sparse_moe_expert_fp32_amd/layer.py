@@ -120,6 +120,18 @@ class DeviceLayer:
         self.forward(stream)
         self.adapter_bwd(stream)
 
+    # ---- reversible residual block around the layer: the layer input x is
+    # the block's stream y1, m = MoE(y1) is self.y after forward()
+    def rev_forward(self, x2, y2, stream=None):
+        """y2 = x2 + MoE(y1)."""
+        self.forward(stream)
+        B.moe_rev_couple(self.dm, x2, self.y, y2, +1, stream)
+
+    def rev_inverse(self, y2, x2, stream=None):
+        """x2 = y2 - MoE(y1), MoE(y1) recomputed from y1 (stateless routing)."""
+        self.forward(stream)
+        B.moe_rev_couple(self.dm, y2, self.y, x2, -1, stream)
+
     # ---- adapter optimizer (AdamW through moe_adamw_step)
     ADAPTERS = (("dA_gate", "A_gate"), ("dB_gate", "B_gate"), ("dA_up", "A_up"),
                 ("dB_up", "B_up"), ("dA_down", "A_down"), ("dB_down", "B_down"))

@@ -214,3 +214,16 @@ def test_misaligned_forward_packed_base_rejected(B):
     assert B.LIB.moe_expert_fwd(ctypes.byref(dm), P, P, P, q, qbad, q, P, P, P, need,
                                 None) == -1
     assert "qf" in B.LIB.moe_last_error().decode()
+
+
+# ---- reversible coupling: host-side validation
+
+@pytest.mark.parametrize("x,m,out,sign", [
+    (None, FAKE, FAKE + 4096, 1), (FAKE, None, FAKE + 4096, 1), (FAKE, FAKE + 64, None, 1),
+    (FAKE, FAKE + 64, FAKE + 4096, 0), (FAKE, FAKE + 64, FAKE + 4096, 2),
+    (FAKE, FAKE + 64, FAKE + 64, -1),    # out aliases m
+])
+def test_rev_couple_rejects_bad_arguments(B, x, m, out, sign):
+    dm = good(B)
+    assert B.LIB.moe_rev_couple(ctypes.byref(dm), x, m, out, sign, None) == -1
+    assert B.LIB.moe_last_error().decode().startswith("moe_rev_couple")

@@ -176,3 +176,37 @@ def test_packed_base_matches_plain_layout(cuda_ok, kw):
     for o in out[1:]:
         for n in out[0]:
             assert np.array_equal(out[0][n], o[n]), n
+
+
+def test_reversible_block_replay(cuda_ok):
+    """Reversible residual block around the layer: y2 = x2 + MoE(y1) on the
+    GPU agrees with the oracle to the layer tolerance; the backward's replay
+    recomputes MoE(y1) bit for bit (stateless routing) and recovers x2 within
+    the two roundings to bf16 (half an ulp of y2 plus half an ulp of x2)."""
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
+    cfg = cfg_of(T=200, E=16, k=4, cfg_id=280, train=False)
+    inp = inputs.generate(cfg, 0)
+    L = DeviceLayer(cfg, inp, device="cuda:0", with_backward=False)
+    rng = np.random.default_rng(11)
+    x2 = torch.from_numpy(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)).to(
+        "cuda:0").to(torch.bfloat16)
+    y2, back = torch.empty_like(x2), torch.empty_like(x2)
+    L.rev_forward(x2, y2)
+    m1 = to_numpy(L.y)
+    idx = to_numpy(L.topk_idx)
+    L.rev_inverse(y2, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy(L.y), m1)          # replayed bit for bit
+    x2n, y2n, bn = to_numpy(x2), to_numpy(y2), to_numpy(back)
+    R = oracle.route(inp, cfg.k)
+    b, o = oracle.near_ties(R["logits"], cfg.k)
+    assert np.all((idx == R["topk_idx"]).all(axis=1) | b | o)
+    ref = oracle.rev_forward(inp, x2n, cfg.k, cfg.group, cfg.lora_scale, topk_idx=idx)
+    e_y2 = rel_l2(oracle.to_f64(y2n), ref)
+    assert e_y2 <= 1e-2
+    ulp = lambda v: np.spacing(np.abs(oracle.to_f64(v)).astype(np.float32)).astype(np.float64) * 65536
+    err = np.abs(oracle.to_f64(bn) - oracle.to_f64(x2n))
+    assert np.all(err <= 0.5 * (ulp(y2n) + ulp(bn)) * 1.001)
+    show("reversible", {"y2": e_y2, "max_abs_x2_err": float(err.max()),
+                        "exact_fraction": float((err == 0).mean())})

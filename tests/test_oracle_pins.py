@@ -489,3 +489,30 @@ def test_adamw_matches_torch_adamw_float64():
     np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ---- reversible residual block around the layer
+
+def test_reversible_block_inverts_and_reduces():
+    """y2 = x2 + MoE(y1) is undone by x2 = y2 - MoE(y1) up to float64
+    rounding; with x2 = 0 it is the layer itself; with a zero layer (zero base
+    and zero B, so every expert output is 0) it is the identity, exactly."""
+    cfg = tiny()
+    inp = _layer(cfg)
+    rng = np.random.default_rng(5)
+    x2 = rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    y2 = oracle.rev_forward(inp, x2, cfg.k, cfg.group)
+    m = oracle.forward(inp, cfg.k, cfg.group)["y"]
+    assert np.abs(m).max() > 1e-3
+    back = oracle.rev_inverse(inp, y2, cfg.k, cfg.group)
+    bound = 4 * np.finfo(np.float64).eps * (np.abs(x2) + np.abs(m))
+    assert np.all(np.abs(back - x2) <= bound)
+    assert np.array_equal(oracle.rev_forward(inp, np.zeros_like(x2), cfg.k, cfg.group), m)
+
+    def zero_layer(inp):
+        for mat in ("gate", "up", "down"):
+            inp[f"q_{mat}"][:] = 0
+            inp[f"B_{mat}"][:] = 0
+    z = _layer(cfg, mutate=zero_layer)
+    assert np.array_equal(oracle.rev_forward(z, x2, cfg.k, cfg.group), x2.astype(np.float64))
+    assert np.array_equal(oracle.rev_inverse(z, x2, cfg.k, cfg.group), x2.astype(np.float64))
