@@ -126,7 +126,7 @@ def main():
 
     import torch
     from sparse_moe_expert_fp32_amd import binding as B
-    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, grow_inputs, to_numpy
 
     cfg = configs.CONFIGS[args.workload]
     t0 = time.perf_counter()
@@ -207,6 +207,24 @@ def main():
                   "x2_exact_fraction": float((rerr == 0).float().mean())}
     log(f"reversible replay {rev_ms:.3f} ms, x2 max abs error {float(rerr.max()):.3e}")
 
+    # few -> many growth (moe_grow_copy, moe_grow_router): the transform of
+    # this layer to twice the experts, timed, and the grown layer's forward
+    # (twice k, unperturbed router) against the original output
+    ev0.record(stream)
+    cfg2, g2 = grow_inputs(L.t, cfg, 2)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    grow_ms = ev0.elapsed_time(ev1)
+    y_orig = L.y.float().clone()
+    L2 = DeviceLayer(cfg2, g2, device=L.dev, with_backward=False)
+    L2.forward()
+    torch.cuda.synchronize()
+    growth = {"factor": 2, "experts": cfg2.E, "top_k": cfg2.k, "transform_ms": grow_ms,
+              "forward_rel_l2_vs_original": float((L2.y.float() - y_orig).norm() / y_orig.norm())}
+    log(f"growth x2: {grow_ms:.3f} ms, grown forward rel L2 vs original "
+        f"{growth['forward_rel_l2_vs_original']:.2e}")
+    del L2, g2
+
     per_launch_ms = k_ms / max(1, k_launches)
     launches_per_step = k_launches / args.steps
     flops_launch = gateup_flops(cfg) / launches_per_step
@@ -247,6 +265,7 @@ def main():
         "base_packed_for_backward": bool(getattr(L, "packed", None)),
         "adamw": adamw,
         "reversible": reversible,
+        "growth": growth,
         "forward_tokens_per_s": cfg.T / (fwd_ms / 1e3),
         "load": {"max": int(counts.max()), "mean": float(counts.mean()),
                  "empty_experts": int((counts == 0).sum())},

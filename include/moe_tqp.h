@@ -259,6 +259,31 @@ moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *
                            const uint16_t *scale, void *packed, size_t packed_bytes,
                            void *stream);
 
+/* Few -> many expert growth ("Reversible Sparse MoE Single Node" skill
+ * card, Principle 2 "State-Preserving Growth": few to many, duplicate experts
+ * and reinitialise routing).  Grown expert e * factor + c (c = 0 ..
+ * factor-1) is a copy of expert e, so every per-expert tensor of the layer
+ * (q, scale, A, B of each matrix) is grown by moe_grow_copy and the router
+ * by moe_grow_router; the grown layer has n_experts * factor experts and,
+ * to compute the same function, top_k * factor experts per token (then the
+ * factor copies of each selected expert tie, are all selected and share its
+ * gate).  Limits: factor >= 1, n_experts * factor <= 1024.
+ *   moe_grow_copy:   src holds n_experts blocks of block_bytes; dst
+ *                    (n_experts * factor blocks, caller-owned) must not
+ *                    overlap src.
+ *   moe_grow_router: w_router [d][E] f32 -> w_out [d][E factor]; column
+ *                    e factor + c is column e, moved for c >= 1 by
+ *                    noise_scale * noise[i][e factor + c] (noise [d][E factor]
+ *                    f32, caller-drawn; NULL or noise_scale 0 keeps every
+ *                    copy exact), in float32 with one rounding; b_router [E]
+ *                    (or NULL) -> b_out [E factor] copied.
+ * Asynchronous on `stream`. */
+moe_status moe_grow_copy(const void *src, void *dst, int64_t block_bytes, int32_t n_experts,
+                         int32_t factor, void *stream);
+moe_status moe_grow_router(int32_t d, int32_t n_experts, int32_t factor, const float *w_router,
+                           const float *b_router, const float *noise, float noise_scale,
+                           float *w_out, float *b_out, void *stream);
+
 /* Adapter optimizer step: AdamW on one float32 tensor of n elements (call it
  * once per adapter tensor: A and B of gate, up and down).  The optimizer
  * state lives on the adapters only, the quantized base being fixed (skill

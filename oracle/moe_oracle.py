@@ -419,3 +419,40 @@ def rev_inverse(inputs: dict, y2, k: int, group: int, lam: float = 1.0,
                 topk_idx: np.ndarray | None = None) -> np.ndarray:
     """x2 = y2 - MoE(y1), MoE(y1) recomputed from y1, in float64."""
     return to_f64(y2) - forward(inputs, k, group, lam, topk_idx=topk_idx)["y"]
+
+
+# ------------------------------------------------- few -> many growth --
+# "Reversible Sparse MoE Single Node" (skill card), Principle 2
+# "State-Preserving Growth": the few -> many expansion duplicates experts and
+# reinitialises routing; Pattern 2: expansions are initialised from the
+# smaller model and must preserve its state.  Grown expert e F + c
+# (c = 0 .. F-1) is expert e; router column e F + c is column e, moved for
+# c >= 1 by s * z[:, e F + c] in float32 with one rounding.  With s = 0 and
+# F k experts per token the grown layer computes the original function.
+
+PER_EXPERT_PREFIXES = ("q_", "s_", "A_", "B_")
+
+
+def grow(inputs: dict, factor: int, noise=None, noise_scale: float = 0.0) -> dict:
+    """The grown layer's tensors (the dict layout of the inputs)."""
+    out = dict(inputs)
+    for key, v in inputs.items():
+        if v is not None and key.startswith(PER_EXPERT_PREFIXES):
+            out[key] = np.repeat(v, factor, axis=0)
+    w = np.repeat(np.asarray(inputs["w_router"], np.float32), factor, axis=1)
+    if noise is not None and noise_scale != 0.0:
+        moved = (w.astype(np.float64) + np.float64(np.float32(noise_scale))
+                 * np.asarray(noise, np.float64)).astype(np.float32)
+        copies = (np.arange(w.shape[1]) % factor) != 0
+        w[:, copies] = moved[:, copies]
+    out["w_router"] = w
+    if inputs.get("b_router") is not None:
+        out["b_router"] = np.repeat(np.asarray(inputs["b_router"], np.float32), factor)
+    return out
+
+
+def routing_load(topk_idx: np.ndarray, E: int) -> dict:
+    """Routing-collapse statistics of one routing: the most loaded expert's
+    share over the mean load, and the number of experts that get no token."""
+    counts = np.bincount(np.asarray(topk_idx).ravel(), minlength=E)
+    return {"max_over_mean": float(counts.max() / counts.mean()), "empty": int((counts == 0).sum())}

@@ -69,6 +69,8 @@ def _load():
         "moe_pack_base_f_size": [DP, ctypes.POINTER(SZ)],
         "moe_pack_base_f": [DP, I32, P, P, P, SZ, P],
         "moe_rev_couple": [DP, P, P, P, I32, P],
+        "moe_grow_copy": [P, P, ctypes.c_int64, I32, I32, P],
+        "moe_grow_router": [I32, I32, I32, P, P, P, ctypes.c_float, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -84,7 +86,7 @@ EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_ada
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
            "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step",
            "moe_pack_base_t_size", "moe_pack_base_t", "moe_pack_base_f_size", "moe_pack_base_f",
-           "moe_rev_couple")
+           "moe_rev_couple", "moe_grow_copy", "moe_grow_router")
 
 # kernel tags of moe_timer_start (moe_kernel_tag)
 KT = {"router_logits": 0, "router_topk": 1, "permute": 2, "gateup": 3, "down": 4, "combine": 5,
@@ -208,6 +210,17 @@ def moe_pack_base_t(dm: Dims, matrix: int, q, scale, packed, stream=None):
 def moe_rev_couple(dm: Dims, x, m, out, sign: int, stream=None):
     _check(LIB.moe_rev_couple(ctypes.byref(dm), _p(x), _p(m), _p(out), sign, _stream(stream)),
            "moe_rev_couple")
+
+
+def moe_grow_copy(src, dst, block_bytes: int, n_experts: int, factor: int, stream=None):
+    _check(LIB.moe_grow_copy(_p(src), _p(dst), block_bytes, n_experts, factor, _stream(stream)),
+           "moe_grow_copy")
+
+
+def moe_grow_router(d: int, n_experts: int, factor: int, w, b, noise, noise_scale: float,
+                    w_out, b_out, stream=None):
+    _check(LIB.moe_grow_router(d, n_experts, factor, _p(w), _p(b), _p(noise), noise_scale,
+                               _p(w_out), _p(b_out), _stream(stream)), "moe_grow_router")
 
 
 def moe_pack_base_f_size(dm: Dims) -> int:

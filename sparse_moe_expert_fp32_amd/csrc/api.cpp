@@ -467,6 +467,33 @@ moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *s
   return hip_status("moe_combine");
 }
 
+moe_status moe_grow_copy(const void *src, void *dst, int64_t block_bytes, int32_t n_experts,
+                         int32_t factor, void *stream) {
+  REQUIRE(src && dst, "moe_grow_copy: src and dst must be non-NULL");
+  REQUIRE(block_bytes > 0, "moe_grow_copy: block_bytes must be positive");
+  REQUIRE(n_experts >= 1 && factor >= 1 && (int64_t)n_experts * factor <= 1024,
+          "moe_grow_copy: need n_experts >= 1, factor >= 1, n_experts * factor <= 1024");
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  const size_t sb = (size_t)block_bytes * n_experts, db = sb * factor;
+  REQUIRE(d0 + db <= s0 || s0 + sb <= d0, "moe_grow_copy: dst must not overlap src");
+  moe::launch_grow_copy(src, dst, (size_t)block_bytes, n_experts, factor, (hipStream_t)stream);
+  return hip_status("moe_grow_copy");
+}
+
+moe_status moe_grow_router(int32_t d, int32_t n_experts, int32_t factor, const float *w_router,
+                           const float *b_router, const float *noise, float noise_scale,
+                           float *w_out, float *b_out, void *stream) {
+  REQUIRE(w_router && w_out, "moe_grow_router: w_router and w_out must be non-NULL");
+  REQUIRE(!b_router || b_out, "moe_grow_router: b_out is required with b_router");
+  REQUIRE(d >= 1 && d <= 65536, "moe_grow_router: d must be in [1, 65536]");
+  REQUIRE(n_experts >= 1 && factor >= 1 && (int64_t)n_experts * factor <= 1024,
+          "moe_grow_router: need n_experts >= 1, factor >= 1, n_experts * factor <= 1024");
+  REQUIRE(std::isfinite(noise_scale), "moe_grow_router: noise_scale must be finite");
+  moe::launch_grow_router(w_router, b_router, noise, noise_scale, d, n_experts, factor, w_out,
+                          b_out, (hipStream_t)stream);
+  return hip_status("moe_grow_router");
+}
+
 moe_status moe_rev_couple(const moe_dims *dims, const void *x, const void *m, void *out,
                           int32_t sign, void *stream) {
   TRY(check_dims(dims));

@@ -40,6 +40,13 @@ void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void
 void launch_rev_couple(bool bf16, const void *x, const void *m, void *out, size_t n, float sign,
                        hipStream_t st);
 
+// ---- few -> many expert growth (grow.hip)
+// dst block e F + c = src block e (E source blocks of block_bytes)
+void launch_grow_copy(const void *src, void *dst, size_t block_bytes, int E, int F, hipStream_t st);
+// w [d][E] -> w_out [d][E F] (copies c >= 1 moved by s z), b [E] -> b_out [E F]
+void launch_grow_router(const float *w, const float *b, const float *z, float s, int d, int E,
+                        int F, float *w_out, float *b_out, hipStream_t st);
+
 // ---- float32 expert kernels (expert_simple.hip)
 // first (optional, 2E + 1 ints): index of each expert's first tile, then the
 // number of experts with no tile or more than one, then those experts

@@ -18,6 +18,8 @@ MATS = ("gate", "up", "down")
 def to_device(a, device):
     if a is None:
         return None
+    if isinstance(a, torch.Tensor):
+        return a.to(device)
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
@@ -161,3 +163,27 @@ class DeviceLayer:
         if self.logits is not None:
             out["logits"] = to_numpy(self.logits)
         return out
+
+
+def grow_inputs(t: dict, cfg, factor: int, noise=None, noise_scale: float = 0.0):
+    """Few -> many growth of a layer's device tensors through moe_grow_copy /
+    moe_grow_router: returns the grown config (E and k times `factor`) and
+    tensors (expert e * factor + c is a copy of expert e; router copies c >= 1
+    moved by noise_scale * noise, noise [d][E * factor] float32)."""
+    out = {}
+    for key, v in t.items():
+        if v is not None and key.startswith(("q_", "s_", "A_", "B_")):
+            dst = torch.empty((v.shape[0] * factor,) + tuple(v.shape[1:]), dtype=v.dtype,
+                              device=v.device)
+            B.moe_grow_copy(v, dst, v[0].numel() * v.element_size(), v.shape[0], factor)
+            out[key] = dst
+        else:
+            out[key] = v
+    w, b = t["w_router"], t.get("b_router")
+    d, E = w.shape
+    w_out = torch.empty((d, E * factor), dtype=torch.float32, device=w.device)
+    b_out = torch.empty(E * factor, dtype=torch.float32, device=w.device) if b is not None else None
+    z = to_device(noise, w.device) if noise is not None else None
+    B.moe_grow_router(d, E, factor, w, b, z, float(noise_scale), w_out, b_out)
+    out["w_router"], out["b_router"] = w_out, b_out
+    return cfg.with_(E=E * factor, k=cfg.k * factor), out

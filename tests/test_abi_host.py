@@ -227,3 +227,25 @@ def test_rev_couple_rejects_bad_arguments(B, x, m, out, sign):
     dm = good(B)
     assert B.LIB.moe_rev_couple(ctypes.byref(dm), x, m, out, sign, None) == -1
     assert B.LIB.moe_last_error().decode().startswith("moe_rev_couple")
+
+
+# ---- expert growth: host-side validation
+
+@pytest.mark.parametrize("src,dst,nb,E,F", [
+    (None, 1 << 32, 64, 4, 2), (FAKE, None, 64, 4, 2), (FAKE, 1 << 32, 0, 4, 2),
+    (FAKE, 1 << 32, 64, 0, 2), (FAKE, 1 << 32, 64, 4, 0), (FAKE, 1 << 32, 64, 600, 2),
+    (FAKE, FAKE + 64, 64, 4, 2),          # dst overlaps src
+])
+def test_grow_copy_rejects_bad_arguments(B, src, dst, nb, E, F):
+    assert B.LIB.moe_grow_copy(src, dst, nb, E, F, None) == -1
+    assert B.LIB.moe_last_error().decode().startswith("moe_grow_copy")
+
+
+@pytest.mark.parametrize("d,E,F,w,b,wo,bo,s", [
+    (64, 8, 2, None, None, FAKE, None, 0.0), (64, 8, 2, FAKE, None, None, None, 0.0),
+    (64, 8, 2, FAKE, FAKE, FAKE, None, 0.0), (0, 8, 2, FAKE, None, FAKE, None, 0.0),
+    (64, 8, 200, FAKE, None, FAKE, None, 0.0), (64, 8, 2, FAKE, None, FAKE, None, float("nan")),
+])
+def test_grow_router_rejects_bad_arguments(B, d, E, F, w, b, wo, bo, s):
+    assert B.LIB.moe_grow_router(d, E, F, w, b, None, s, wo, bo, None) == -1
+    assert B.LIB.moe_last_error().decode().startswith("moe_grow_router")

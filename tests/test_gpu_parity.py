@@ -210,3 +210,54 @@ def test_reversible_block_replay(cuda_ok):
     assert np.all(err <= 0.5 * (ulp(y2n) + ulp(bn)) * 1.001)
     show("reversible", {"y2": e_y2, "max_abs_x2_err": float(err.max()),
                         "exact_fraction": float((err == 0).mean())})
+
+
+def test_expert_growth(cuda_ok):
+    """Few -> many growth on the GPU (moe_grow_copy, moe_grow_router): the
+    grown tensors equal the oracle's growth bit for bit (router columns moved
+    by noise: within one float32 ulp); unperturbed, the grown layer with
+    twice the experts and twice k routes every token to both copies of its
+    original experts and computes the original function; perturbed, the
+    routing-collapse statistic of the grown router is reported."""
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, grow_inputs, to_device, to_numpy
+    F = 2
+    cfg = cfg_of(T=128, E=12, k=3, cfg_id=290, router_bias_var=0.5, train=False)
+    inp = inputs.generate(cfg, 0)
+    z = np.random.default_rng(9).standard_normal((cfg.d, cfg.E * F)).astype(np.float32)
+    t = {k: to_device(v, "cuda:0") for k, v in inp.items()}
+    for s in (0.0, 0.05):
+        cfg2, g = grow_inputs(t, cfg, F, z, s)
+        torch.cuda.synchronize()
+        ref = oracle.grow(inp, F, z, s)
+        for key, v in ref.items():
+            if v is None or key in ("x", "dy"):
+                continue
+            got = to_numpy(g[key])
+            if key == "w_router":
+                assert np.all(np.abs(got.astype(np.float64) - v) <= np.spacing(np.abs(v))), key
+            else:
+                assert np.array_equal(got, v), key
+    L0 = DeviceLayer(cfg, inp, device="cuda:0", with_backward=False)
+    L0.forward()
+    cfg2, g = grow_inputs(t, cfg, F)
+    L1 = DeviceLayer(cfg2, g, device="cuda:0", with_backward=False)
+    L1.forward()
+    torch.cuda.synchronize()
+    i0, i1 = to_numpy(L0.topk_idx), to_numpy(L1.topk_idx)
+    for t_ in range(cfg.T):
+        assert sorted(i1[t_] // F) == sorted(np.repeat(i0[t_], F))
+    yref = oracle.forward(inp, cfg.k, cfg.group, cfg.lora_scale, topk_idx=i0)["y"]
+    e0 = rel_l2(oracle.to_f64(to_numpy(L0.y)), yref)
+    e1 = rel_l2(oracle.to_f64(to_numpy(L1.y)), yref)
+    assert e0 <= 1e-2 and e1 <= 1e-2
+    cfg3, g3 = grow_inputs(t, cfg, F, z, 0.05)
+    L3 = DeviceLayer(cfg3, g3, device="cuda:0", with_backward=False)
+    L3.forward()
+    torch.cuda.synchronize()
+    st0 = oracle.routing_load(i0, cfg.E)
+    st3 = oracle.routing_load(to_numpy(L3.topk_idx), cfg3.E)
+    e3 = rel_l2(oracle.to_f64(to_numpy(L3.y)), yref)
+    show("growth", {"y_grown": e1, "y_orig": e0, "y_perturbed_vs_orig": e3,
+                    "max_over_mean_before": st0["max_over_mean"],
+                    "max_over_mean_after": st3["max_over_mean"], "empty_after": st3["empty"]})

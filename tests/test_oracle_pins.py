@@ -516,3 +516,39 @@ def test_reversible_block_inverts_and_reduces():
     z = _layer(cfg, mutate=zero_layer)
     assert np.array_equal(oracle.rev_forward(z, x2, cfg.k, cfg.group), x2.astype(np.float64))
     assert np.array_equal(oracle.rev_inverse(z, x2, cfg.k, cfg.group), x2.astype(np.float64))
+
+
+# ---- few -> many expert growth
+
+@pytest.mark.parametrize("factor", [2, 3])
+def test_growth_preserves_the_function(factor):
+    """Unperturbed growth by F with F k experts per token: every original
+    selection becomes its F copies, each with 1/F of the gate, and the layer
+    output is unchanged up to float64 rounding."""
+    cfg = tiny(router_bias_var=0.5)
+    inp = _layer(cfg)
+    g = oracle.grow(inp, factor)
+    assert g["q_gate"].shape[0] == cfg.E * factor
+    y0 = oracle.forward(inp, cfg.k, cfg.group)["y"]
+    R0, R1 = oracle.route(inp, cfg.k), oracle.route(g, cfg.k * factor)
+    for t in range(cfg.T):
+        assert sorted(R1["topk_idx"][t] // factor) == sorted(np.repeat(R0["topk_idx"][t], factor))
+        for e in R0["topk_idx"][t]:
+            sel = R1["topk_idx"][t] // factor == e
+            j = list(R0["topk_idx"][t]).index(e)
+            assert np.allclose(R1["gates"][t][sel], R0["gates"][t][j] / factor, rtol=1e-12)
+    y1 = oracle.forward(g, cfg.k * factor, cfg.group)["y"]
+    assert np.allclose(y1, y0, rtol=1e-11, atol=1e-13)
+
+
+def test_growth_router_noise_moves_only_copies():
+    cfg = tiny()
+    inp = _layer(cfg)
+    z = np.random.default_rng(3).standard_normal((cfg.d, cfg.E * 2)).astype(np.float32)
+    g = oracle.grow(inp, 2, z, 0.25)
+    w0 = inp["w_router"]
+    assert np.array_equal(g["w_router"][:, 0::2], w0)
+    want = (w0.astype(np.float64) + 0.25 * z[:, 1::2].astype(np.float64)).astype(np.float32)
+    assert np.array_equal(g["w_router"][:, 1::2], want)
+    st = oracle.routing_load(oracle.route(g, cfg.k * 2)["topk_idx"], cfg.E * 2)
+    assert st["max_over_mean"] >= 1.0 and 0 <= st["empty"] <= cfg.E * 2
