@@ -13,7 +13,7 @@ already resident in device memory.  `roofline` reports the gate/up expert GEMM
 bf16 matrix-core peak, timed with HIP events on its own launch stream; `cpu_baseline` times the fp64 oracle on a bounded
 sample of the same workload on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-extras]
 """
 from __future__ import annotations
 
@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=configs.C5.name, choices=sorted(configs.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the reversible-replay and growth measurements (kernel "
+                         "profiles of the layer step alone)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -189,41 +192,43 @@ def main():
     # x2 = y2 - MoE(y1), i.e. the layer forward recomputed from y1 and the
     # coupling (moe_rev_couple), timed on its own; the reconstruction error
     # is against the x2 the forward coupling started from
-    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
-    gen = torch.Generator().manual_seed(7)
-    x2 = torch.randn(cfg.T, cfg.d, generator=gen).to(L.dev).to(act)
-    y2, back = torch.empty_like(x2), torch.empty_like(x2)
-    L.rev_forward(x2, y2)
-    L.rev_inverse(y2, back)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    reversible = growth = None
+    if not args.no_extras:
+        act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+        gen = torch.Generator().manual_seed(7)
+        x2 = torch.randn(cfg.T, cfg.d, generator=gen).to(L.dev).to(act)
+        y2, back = torch.empty_like(x2), torch.empty_like(x2)
+        L.rev_forward(x2, y2)
         L.rev_inverse(y2, back)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    rev_ms = ev0.elapsed_time(ev1) / args.steps
-    rerr = (back.float() - x2.float()).abs()
-    reversible = {"replay_ms": rev_ms, "x2_max_abs_err": float(rerr.max()),
-                  "x2_exact_fraction": float((rerr == 0).float().mean())}
-    log(f"reversible replay {rev_ms:.3f} ms, x2 max abs error {float(rerr.max()):.3e}")
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            L.rev_inverse(y2, back)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        rev_ms = ev0.elapsed_time(ev1) / args.steps
+        rerr = (back.float() - x2.float()).abs()
+        reversible = {"replay_ms": rev_ms, "x2_max_abs_err": float(rerr.max()),
+                      "x2_exact_fraction": float((rerr == 0).float().mean())}
+        log(f"reversible replay {rev_ms:.3f} ms, x2 max abs error {float(rerr.max()):.3e}")
 
-    # few -> many growth (moe_grow_copy, moe_grow_router): the transform of
-    # this layer to twice the experts, timed, and the grown layer's forward
-    # (twice k, unperturbed router) against the original output
-    ev0.record(stream)
-    cfg2, g2 = grow_inputs(L.t, cfg, 2)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    grow_ms = ev0.elapsed_time(ev1)
-    y_orig = L.y.float().clone()
-    L2 = DeviceLayer(cfg2, g2, device=L.dev, with_backward=False)
-    L2.forward()
-    torch.cuda.synchronize()
-    growth = {"factor": 2, "experts": cfg2.E, "top_k": cfg2.k, "transform_ms": grow_ms,
-              "forward_rel_l2_vs_original": float((L2.y.float() - y_orig).norm() / y_orig.norm())}
-    log(f"growth x2: {grow_ms:.3f} ms, grown forward rel L2 vs original "
-        f"{growth['forward_rel_l2_vs_original']:.2e}")
-    del L2, g2
+        # few -> many growth (moe_grow_copy, moe_grow_router): the transform of
+        # this layer to twice the experts, timed, and the grown layer's forward
+        # (twice k, unperturbed router) against the original output
+        ev0.record(stream)
+        cfg2, g2 = grow_inputs(L.t, cfg, 2)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        grow_ms = ev0.elapsed_time(ev1)
+        y_orig = L.y.float().clone()
+        L2 = DeviceLayer(cfg2, g2, device=L.dev, with_backward=False)
+        L2.forward()
+        torch.cuda.synchronize()
+        growth = {"factor": 2, "experts": cfg2.E, "top_k": cfg2.k, "transform_ms": grow_ms,
+                  "forward_rel_l2_vs_original": float((L2.y.float() - y_orig).norm() / y_orig.norm())}
+        log(f"growth x2: {grow_ms:.3f} ms, grown forward rel L2 vs original "
+            f"{growth['forward_rel_l2_vs_original']:.2e}")
+        del L2, g2
 
     per_launch_ms = k_ms / max(1, k_launches)
     launches_per_step = k_launches / args.steps
