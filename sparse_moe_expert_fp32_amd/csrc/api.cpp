@@ -529,7 +529,8 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   int *ntiles = at<int>(ws, L.ntiles);
   const int BM = moe::simple_tile_rows();
   const int mt = (int)max_tiles(dims, BM);
-  moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
+  // (the float32 kernels' tile list; the matrix-core path builds its own)
+  if (!use_mfma(dims)) moe::launch_build_tiles(offsets, E, BM, tiles, ntiles, st);
 
   moe::ProjArgs P{};
   P.a = x; P.lda = d; P.gather = true; P.perm_src = perm_src; P.kk = k;
