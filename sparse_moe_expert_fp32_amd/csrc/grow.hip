@@ -48,7 +48,8 @@ void launch_grow_copy(const void *src, void *dst, size_t block_bytes, int E, int
 }
 
 // w_out[i][e F + c] = w[i][e] (+ s * z[i][e F + c] for c >= 1, one rounding),
-// b_out[e F + c] = b[e].  One thread per output entry of a row.
+// b_out[e F + c] = b[e].  One thread per output column, block rows striding
+// over the rows of w.
 __global__ __launch_bounds__(256) void grow_router_kernel(const float *__restrict__ w,
                                                           const float *__restrict__ b,
                                                           const float *__restrict__ z, float s,
@@ -57,17 +58,18 @@ __global__ __launch_bounds__(256) void grow_router_kernel(const float *__restric
                                                           float *__restrict__ b_out) {
   const int EF = E * F;
   const int j = blockIdx.x * 256 + threadIdx.x;
-  const int i = blockIdx.y;
   if (j >= EF) return;
   const int e = j / F, c = j - e * F;
-  const float v = w[(size_t)i * E + e];
-  w_out[(size_t)i * EF + j] = (c > 0 && z) ? fmaf(s, z[(size_t)i * EF + j], v) : v;
-  if (i == 0 && b) b_out[j] = b[e];
+  for (int i = blockIdx.y; i < d; i += gridDim.y) {   // rows of w
+    const float v = w[(size_t)i * E + e];
+    w_out[(size_t)i * EF + j] = (c > 0 && z) ? fmaf(s, z[(size_t)i * EF + j], v) : v;
+  }
+  if (blockIdx.y == 0 && b) b_out[j] = b[e];
 }
 
 void launch_grow_router(const float *w, const float *b, const float *z, float s, int d, int E,
                         int F, float *w_out, float *b_out, hipStream_t st) {
-  dim3 grid((E * F + 255) / 256, d);
+  dim3 grid((E * F + 255) / 256, std::min(d, 4096));
   grow_router_kernel<<<grid, 256, 0, st>>>(w, b, z, s, d, E, F, w_out, b_out);
 }
 
