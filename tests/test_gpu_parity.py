@@ -261,3 +261,29 @@ def test_expert_growth(cuda_ok):
     show("growth", {"y_grown": e1, "y_orig": e0, "y_perturbed_vs_orig": e3,
                     "max_over_mean_before": st0["max_over_mean"],
                     "max_over_mean_after": st3["max_over_mean"], "empty_after": st3["empty"]})
+
+
+def test_grow_copy_and_couple_scalar_paths(cuda_ok):
+    """The byte-wise path of moe_grow_copy (blocks not a multiple of 16
+    bytes) and the element-wise path of moe_rev_couple (pointers not 16-byte
+    aligned, float32 activations), against numpy."""
+    import torch
+    from sparse_moe_expert_fp32_amd import binding as B
+    rng = np.random.default_rng(13)
+    src_np = rng.integers(0, 256, size=(5, 7), dtype=np.uint8)
+    src = torch.from_numpy(src_np).to("cuda:0")
+    dst = torch.empty((15, 7), dtype=torch.uint8, device="cuda:0")
+    B.moe_grow_copy(src, dst, 7, 5, 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), np.repeat(src_np, 3, axis=0))
+    cfg = cfg_of(act="f32", T=3, d=64, E=4, k=1, f=128, r=4, group=32, cfg_id=291)
+    dm = B.dims_of(cfg)
+    x_np = rng.standard_normal(cfg.T * cfg.d + 1).astype(np.float32)
+    m_np = rng.standard_normal(cfg.T * cfg.d + 1).astype(np.float32)
+    x = torch.from_numpy(x_np).to("cuda:0")[1:]     # 4-byte aligned views
+    m = torch.from_numpy(m_np).to("cuda:0")[1:]
+    out = torch.empty(cfg.T * cfg.d + 1, dtype=torch.float32, device="cuda:0")[1:]
+    B.moe_rev_couple(dm, x, m, out, -1)
+    torch.cuda.synchronize()
+    want = (x_np[1:].astype(np.float64) - m_np[1:].astype(np.float64)).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy(), want)
