@@ -8,12 +8,16 @@ setting of "Reversible Foundations: Training a 120B Sparse MoE through
 State-Preserving Scaling", abstract; hidden sizes are this library's).
 
 Prints one JSON line.  `value` is tokens/s of the timed steps with every input
-already resident in device memory.  `roofline` reports the gate/up expert GEMM
-(the dominant kernel; one launch per tile class, timed together) against the
-bf16 matrix-core peak, timed with HIP events on its own launch stream; `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload on this host's cores.
+already resident in device memory.  `roofline` reports the longest of the four
+int4 expert-GEMM stages per step (each stage is four launches, one per tile
+class, timed as one span with HIP events on the launch stream) against the
+bf16 matrix-core peak; `stages` lists all four.  `decode` measures the
+T=64 forward (the weight-streaming shape) against HBM bandwidth, with the
+device caches scrubbed before every timed forward.  `cpu_baseline` times the
+fp64 oracle on a bounded sample of the workload on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-extras]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-extras] [--no-decode]
 """
 from __future__ import annotations
 
@@ -41,12 +45,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gateup_flops(cfg) -> float:
-    """Algorithmic FLOPs of the gate/up stage per step: for every routed slot,
-    the int4-base product of both matrices (2*d*2f) and the adapter product
-    (X A) B's second factor (2*r*2f); X A itself runs in its own kernel."""
-    S = cfg.T * cfg.k
-    return 2.0 * S * 2 * cfg.f * (cfg.d + cfg.r)
+# The four int4 expert-GEMM stages: (timer tag, name, algorithmic FLOPs per
+# routed slot).  The adapter term's second factor is counted where it is
+# fused (the rank-r product into the same accumulator); the adapter
+# projections X A^T and the adapter gradients run in their own kernels.
+def gemm_stages(cfg, train: bool):
+    d, f, r = cfg.d, cfg.f, cfg.r
+    st = [("gateup", "gate/up expert GEMM + SwiGLU (grouped_gemm_kernel<0,...>)", 4.0 * f * (d + r)),
+          ("down", "down expert GEMM (grouped_gemm_kernel<1,...>)", 2.0 * d * (f + r))]
+    if train:
+        st += [("bwd_down", "backward dH + SwiGLU backward (grouped_gemm_t_kernel<0,...>)",
+                2.0 * f * (d + r)),
+               ("bwd_gateup", "backward dX_perm (grouped_gemm_t_kernel<1,...>)", 4.0 * d * (f + r))]
+    return st
 
 
 def layer_flops(cfg, train: bool) -> float:
@@ -77,33 +88,110 @@ def measured_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, target_s: float):
-    """The fp64 oracle (as it stands) on the first Ts tokens of the workload:
-    whole-layer forward and, for a training step, the adapter backward."""
+def cpu_baseline(cfg, inp, target_s: float, gpu_idx=None):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload,
+    extrapolated to the whole step: the routing of every token (timed whole),
+    the expert work (dequantisation, forward and, for a training step, the
+    adapter backward) of whole experts in a seeded random order until about
+    target_s seconds, scaled by all slots over the slots done, and the
+    combine and gate path of 1024 tokens, scaled by T / 1024.  Whole experts
+    keep the per-expert dequantisation amortised over that expert's real
+    load, as in the full step.  Also reports the routing check: near-tie
+    tokens of the fp64 logits, and tokens where the GPU's selection differs
+    outside them."""
     import oracle
     from threadpoolctl import threadpool_limits
     cores = len(os.sched_getaffinity(0))
-    lam = cfg.lora_scale
-
-    def run(Ts):
-        sub = dict(inp)
-        sub["x"], sub["dy"] = inp["x"][:Ts], inp["dy"][:Ts]
-        t0 = time.perf_counter()
-        fwd = oracle.forward(sub, cfg.k, cfg.group, lam, keep=cfg.train)
-        if cfg.train:
-            oracle.backward(sub, fwd, cfg.k, cfg.group, lam)
-        return time.perf_counter() - t0
-
+    lam, k = cfg.lora_scale, cfg.k
     with threadpool_limits(cores):
-        Ts = 8
-        dt = run(Ts)
-        # grow the sample until it takes a few seconds, stay inside the budget
-        while dt < target_s / 4 and Ts < cfg.T:
-            Ts = min(cfg.T, Ts * 4)
-            dt = run(Ts)
-    return {"value": Ts / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {Ts} of {cfg.T} tokens, fp64 whole-layer forward"
-                      f"{' + adapter backward' if cfg.train else ''} in {dt:.1f} s"}
+        t0 = time.perf_counter()
+        R = oracle.route(inp, k)
+        t_route = time.perf_counter() - t0
+        order = np.random.default_rng(0).permutation(cfg.E)
+        done_slots, n_exp, t_exp = 0, 0, 0.0
+        for e in order:
+            if R["counts"][e] == 0:
+                continue
+            t0 = time.perf_counter()
+            oracle.expert_rows(inp, R, int(e), k, cfg.group, lam, backward=cfg.train)
+            t_exp += time.perf_counter() - t0
+            done_slots += int(R["counts"][e])
+            n_exp += 1
+            if t_exp >= target_s:
+                break
+        Tc = min(cfg.T, 1024)
+        O = np.zeros((Tc * k, cfg.d))
+        sp = np.arange(Tc * k, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.combine(R["gates"][:Tc], O, sp)
+        if cfg.train:
+            oracle.gate_backward(inp["dy"][:Tc], O, R["gates"][:Tc], R["topk_idx"][:Tc], sp,
+                                 inp["w_router"])
+        t_tok = (time.perf_counter() - t0) * cfg.T / Tc
+    S = cfg.T * k
+    total = t_route + t_exp * S / done_slots + t_tok
+    rec = {"value": cfg.T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"fp64 oracle, {'forward + adapter backward' if cfg.train else 'forward'}: "
+                     f"routing of all {cfg.T} tokens {t_route:.1f} s; all slots of {n_exp} of "
+                     f"{cfg.E} experts ({done_slots} of {S} slots) {t_exp:.1f} s, scaled by "
+                     f"{S / done_slots:.1f}; combine/gate path of {Tc} tokens scaled by "
+                     f"{cfg.T / Tc:.0f}; whole step {total:.0f} s extrapolated"}
+    b, o = oracle.near_ties(R["logits"], k)
+    routing = {"near_ties": int((b | o).sum())}
+    if gpu_idx is not None:
+        diff = ~np.all(gpu_idx == R["topk_idx"], axis=1)
+        routing["gpu_differs"] = int(diff.sum())
+        routing["gpu_differs_outside_near_ties"] = int((diff & ~(b | o)).sum())
+    return rec, routing
+
+
+def decode_hbm(args, B, DeviceLayer, to_numpy):
+    """The T=64 decode shape (E=460, top-12, unbiased router): forward only,
+    each timed forward preceded (outside its events) by a write of 1 GiB,
+    four times the 256 MB last-level cache, so the expert weights stream from
+    HBM.  Bytes are algorithmic: the int4 base, bf16 group scales and
+    adapters of the experts the seeded routing touches, plus the router, x
+    and y."""
+    import torch
+    cfg = configs.C4
+    inp = inputs.generate(cfg, args.seed)
+    L = DeviceLayer(cfg, inp, device="cuda:0", with_backward=False)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        L.forward()
+    torch.cuda.synchronize()
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    n = max(10, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        scrub.fill_(1)
+        a.record(stream)
+        L.forward()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold = sorted(a.elapsed_time(b) for a, b in ev)
+    a, b = ev[0]
+    a.record(stream)
+    for _ in range(n):
+        L.forward()
+    b.record(stream)
+    torch.cuda.synchronize()
+    warm = a.elapsed_time(b) / n
+    counts = to_numpy(L.counts)
+    touched = int((counts > 0).sum())
+    d, f, r, g = cfg.d, cfg.f, cfg.r, cfg.group
+    per_expert = 3 * d * f // 2 + 3 * (d * f // g) * 2 + 3 * r * (d + f) * 2
+    nbytes = touched * per_expert + d * cfg.E * 4 + 2 * cfg.T * d * 2
+    med = cold[len(cold) // 2]
+    del scrub, L
+    return {"workload": f"{cfg.name} forward (T={cfg.T}, E={cfg.E}, top-{cfg.k}, "
+                        "unbiased router)",
+            "ms": med, "ms_p10": cold[len(cold) // 10], "ms_p90": cold[(9 * len(cold)) // 10],
+            "ms_warm_cache": warm, "tokens_per_s": cfg.T / (med / 1e3),
+            "experts_touched": touched, "bytes": nbytes, "bytes_per_expert": per_expert,
+            "GB_s": nbytes / (med / 1e3) / 1e9, "frac_hbm": nbytes / (med / 1e3) / PEAK_HBM,
+            "scrub": "1 GiB written before each timed forward, outside its events"}
 
 
 def main():
@@ -116,7 +204,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the reversible-replay and growth measurements (kernel "
                          "profiles of the layer step alone)")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the T=64 decode-shape HBM measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a kernel of "
@@ -143,9 +233,7 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
 
-    # timed region: K steps between two events; the gate/up GEMM's launches
-    # are bracketed by their own events on the same stream
-    B.moe_timer_start("gateup")
+    # timed region: K steps between two events on the launch stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -154,11 +242,26 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    k_ms, k_launches = B.moe_timer_stop()
     ms = total_ms / args.steps
     tokens_per_s = cfg.T / (ms / 1e3)
-    log(f"{ms:.3f} ms/step, {tokens_per_s:.4g} tokens/s; gate/up {k_ms / max(1, k_launches):.3f} "
-        f"ms x {k_launches / args.steps:.0f}/step")
+    log(f"{ms:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
+
+    # each int4 expert-GEMM stage timed on its own pass over K more steps:
+    # the library brackets the stage (its four tile-class launches, back to
+    # back on the launch stream) with a pair of HIP events
+    stages = []
+    for tag, name, flops_slot in gemm_stages(cfg, cfg.train):
+        B.moe_timer_start(tag)
+        for _ in range(args.steps):
+            step()
+        k_ms, n = B.moe_timer_stop()
+        per = k_ms / max(1, n)
+        flops = flops_slot * cfg.T * cfg.k
+        stages.append({"stage": tag, "kernel": name, "ms": per, "flops": flops,
+                       "tflops": flops / (per / 1e3) / 1e12,
+                       "frac": flops / (per / 1e3) / PEAK_BF16, "spans_per_step": n / args.steps})
+        log(f"stage {tag}: {per:.3f} ms, {stages[-1]['frac']:.3f} of bf16 peak")
+    dom = max(stages, key=lambda x: x["ms"])
 
     # forward-only rate of the same inputs (context)
     ev0.record(stream)
@@ -230,12 +333,15 @@ def main():
             f"{growth['forward_rel_l2_vs_original']:.2e}")
         del L2, g2
 
-    per_launch_ms = k_ms / max(1, k_launches)
-    launches_per_step = k_launches / args.steps
-    flops_launch = gateup_flops(cfg) / launches_per_step
-    achieved = flops_launch / (per_launch_ms / 1e3)
-    traffic = measured_traffic("gateup")
+    traffic = measured_traffic(dom["stage"])
     counts = to_numpy(L.counts)
+    gpu_idx = to_numpy(L.topk_idx)
+    decode = None
+    if not args.no_decode:
+        t0 = time.perf_counter()
+        decode = decode_hbm(args, B, DeviceLayer, to_numpy)
+        log(f"decode T=64: {decode['ms']:.3f} ms, {decode['GB_s']:.0f} GB/s = "
+            f"{decode['frac_hbm']:.3f} of HBM ({time.perf_counter() - t0:.1f} s)")
     rec = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -254,12 +360,15 @@ def main():
                    "T": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "d_ff": cfg.f, "rank": cfg.r, "group": cfg.group, "act": cfg.act,
                    "router_bias_var": cfg.router_bias_var},
-        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
-                     "traffic": traffic,
-                     "kernel": "gate/up expert GEMM (one launch per tile class: 128/96/64/32 rows)",
-                     "kernel_ms": per_launch_ms, "launches_per_step": launches_per_step,
-                     "flops_per_launch": flops_launch},
+        "roofline": {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": dom["frac"], "traffic": traffic,
+                     "kernel": dom["kernel"] + ", the longest stage per step",
+                     "kernel_ms": dom["ms"], "launches_per_step": 4,
+                     "timed_as": "one event pair around the stage's four tile-class launches "
+                                 "(128/96/64/32-row tiles), once per step",
+                     "flops_per_launch": dom["flops"]},
+        "stages": stages,
+        "decode": decode,
         "layer_tflops": layer_flops(cfg, cfg.train) / (ms / 1e3) / 1e12,
         "layer_frac_of_bf16_peak": layer_flops(cfg, cfg.train) / (ms / 1e3) / PEAK_BF16,
         "forward_ms": fwd_ms,
@@ -286,7 +395,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        rec["cpu_baseline"], rec["routing"] = cpu_baseline(cfg, inp, args.cpu_seconds, gpu_idx)
         log(f"cpu baseline took {time.perf_counter() - t0:.1f} s")
     else:
         rec["cpu_baseline"] = None

@@ -32,7 +32,9 @@
  *   - Launch failures are reported as MOE_ERR_HIP.
  *   - Outputs are overwritten, never accumulated into.  Every output element
  *     is written, including zero gradients of experts that received no token.
- *   - The library keeps no state between calls; calls are re-entrant.
+ *   - The layer calls keep no state between calls and are re-entrant.  The
+ *     one exception is the instrumentation pair moe_timer_start/stop, which
+ *     holds thread-local HIP events between its start and stop calls.
  *   - Results are bitwise reproducible for identical inputs: integer
  *     histograms, scan-ordered placement, fixed-order reductions, no float
  *     atomics.
@@ -116,11 +118,31 @@ typedef enum {
   MOE_CALL_ADAPTER_BWD = 4
 } moe_call;
 
-/* Router, softmax and top-k.  logits[t][e] = sum_c x[t][c] w_router[c][e]
+/* Flags OR-ed into the call id of moe_workspace_size: what the caller will
+ * supply, so that the workspace needs no room for it.  A call checks ws_bytes
+ * against the size its own arguments imply, so a workspace sized with a flag
+ * is valid only for calls that do supply that.
+ *   MOE_WS_SAVE_GIVEN    moe_expert_fwd with a non-NULL save buffer (without
+ *                        one, the forward keeps its intermediates in the
+ *                        workspace)
+ *   MOE_WS_PACKED_GIVEN  moe_expert_fwd with qf set on gate, up and down, or
+ *                        moe_adapter_bwd with qt set on all three (without,
+ *                        the call re-lays out the base in the workspace) */
+#define MOE_WS_SAVE_GIVEN 0x100
+#define MOE_WS_PACKED_GIVEN 0x200
+
+/* Router, softmax and top-k ("Reversible Sparse MoE Single Node" skill card,
+ * Architecture Details: top-12 routing over 460 routed experts; Implementation
+ * Considerations, TQP Quantization: the router stays full precision;
+ * Reversibility: routing is a stateless function of the input).  The
+ * selection order and the gate formula are this library's reading; the pages
+ * state neither.  logits[t][e] = sum_c x[t][c] w_router[c][e]
  * + b_router[e] in float32; the k largest logits are selected under the order
  * (logit descending, expert index ascending) and written in that order to
  * topk_idx; gates[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the
  * selected logits (softmax over all experts renormalised to the selected).
+ * A NaN logit takes part as -inf, so topk_idx always holds k distinct
+ * experts in [0, E) (the gates are then NaN where the logits are).
  *   x          act  [T][d]
  *   w_router   f32  [d][E]
  *   b_router   f32  [E] or NULL (no bias)
@@ -134,8 +156,15 @@ moe_status moe_route(const moe_dims *dims, const void *x, const float *w_router,
 
 /* Expert histogram, scan and stable permutation of the S routed slots into
  * expert-contiguous order (expert ascending, token ascending within an
- * expert).  Every topk_idx entry must be in [0, E) and a token's k entries
- * distinct (as moe_route produces); other input is undefined behaviour.
+ * expert), so that each expert's tokens form one segment for the expert
+ * products: the dispatch of each token to its top-k experts ("Reversible
+ * Sparse MoE Single Node" skill card, Architecture Details, top-12 routing;
+ * the pages leave the data movement open).  topk_idx should hold k distinct
+ * entries in [0, E) per token, as moe_route writes them.  Other input is
+ * made valid first, per token in j order (an entry outside [0, E) is clamped,
+ * a repeated one becomes the lowest expert the token does not use yet), so
+ * the placement stays a bijection and every access in bounds; the layer's
+ * result is then that of the corrected routing.
  *   counts    i32 [E]     slots per expert (out)
  *   offsets   i32 [E+1]   exclusive scan of counts, offsets[E] = S (out)
  *   perm_src  i32 [S]     perm_src[p] = t*k + j of the slot at position p (out)
@@ -147,7 +176,16 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
                        int32_t *slot_pos, void *x_perm, void *ws, size_t ws_bytes,
                        void *stream);
 
-/* Expert FFNs over the permuted rows.  For every position p with expert e
+/* Expert FFNs over the permuted rows, each expert a frozen quantized base
+ * plus trained low-rank adapters ("Reversible Sparse MoE Single Node" skill
+ * card, Principle 3 "TQP Optimizer Strategy": base expert weights quantized
+ * and fixed, low-rank adapters on top; Implementation Considerations, TQP
+ * Quantization: "Int8 or Int4" base, full-precision adapters; Related
+ * Methods: LoRA).  The SwiGLU form, the int4 format and the adapter placement
+ * on all three matrices are this library's readings.  The rows are read from
+ * x by token through perm_src (no x_perm argument: x is small enough to stay
+ * in cache, which saves writing and reading the permuted copy).
+ * For every position p with expert e
  * (offsets[e] <= p < offsets[e+1]) and input row X = x[perm_src[p] / k]:
  *   G = X Wg_hat^T + lambda (X A_g^T) B_g^T,  U likewise with the up matrix,
  *   H = silu(G) * U,   silu(z) = z / (1 + exp(-z))
@@ -165,7 +203,11 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
                           moe_qlora down, void *e_out, void *save, void *ws,
                           size_t ws_bytes, void *stream);
 
-/* Gate-weighted combine: y[t] = sum_{j=0..k-1} gates[t][j] e_out[slot_pos[t*k+j]],
+/* Gate-weighted combine of each token's k expert outputs (the routed mixture
+ * of "Reversible Sparse MoE Single Node" skill card, Architecture Details;
+ * the order of the sum is this library's, fixed so that results are
+ * bitwise repeatable):
+ * y[t] = sum_{j=0..k-1} gates[t][j] e_out[slot_pos[t*k+j]],
  * float32 accumulation in ascending j, one rounding to act at the end.
  *   y act [T][d] (out) */
 moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *slot_pos,
@@ -188,7 +230,13 @@ moe_status moe_combine(const moe_dims *dims, const void *e_out, const int32_t *s
 moe_status moe_rev_couple(const moe_dims *dims, const void *x, const void *m, void *out,
                           int32_t sign, void *stream);
 
-/* Adapter-only backward of route -> expert FFNs -> combine for an upstream
+/* Adapter-only backward ("Reversible Sparse MoE Single Node" skill card,
+ * Principle 3 "TQP Optimizer Strategy" and Pattern 3: the quantized base is
+ * fixed and only the low-rank adapters are trained, so no base gradient is
+ * formed; Implementation Considerations, TQP Quantization: the router is full
+ * precision -- here frozen, with the gate path still carried into dx).  Rows
+ * are read from x and dy by token, as in the forward (no x_perm argument).
+ * Backward of route -> expert FFNs -> combine for an upstream
  * gradient dy (loss L = sum_t <dy_t, y_t>).  The selection is held fixed; the
  * router and every base matrix are frozen (no weight gradient), but the gates
  * pass gradient to x through the router:
@@ -244,7 +292,9 @@ moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *
  * (layout [E][K/64][N][32 B], the byte count of q).  The float32 table of
  * group-scale ratios the forward applies follows, [E][K/128][N]: entry g >= 1
  * of column n is s'[n][g-1] / s'[n][g] and entry 0 is s'[n][K/128-1], where
- * s' is the bf16 scale with magnitudes below 2^-100 raised to 2^-100.  The
+ * s' is the bf16 scale with magnitudes below the column's floor raised to
+ * that floor; the floor is 2^-24 times the column's largest |scale|, and at
+ * least 2^-100 (so no ratio exceeds 2^24).  The
  * products are those of moe_expert_fwd (skill card "Reversible Sparse MoE
  * Single Node", Principle 3: the quantized base is fixed, so it is packed
  * once).

@@ -232,79 +232,112 @@ def route(inputs: dict, k: int, topk_idx: np.ndarray | None = None) -> dict:
             "offsets": offsets, "perm_src": perm_src, "slot_pos": slot_pos}
 
 
+def expert_rows(inputs: dict, R: dict, e: int, k: int, group: int, lam: float = 1.0,
+                backward: bool = False, fw: dict | None = None) -> dict:
+    """Expert e over its segment of the permutation R (as from route()): the
+    forward of its rows ("fw", with the outputs "O") and, with backward, the
+    adapter-only backward for the upstream gradient of those rows,
+    dO[p] = gamma[t(p), j(p)] dY[t(p)]: the six adapter gradients and "dX".
+    A saved forward may be passed as fw."""
+    lo, hi = R["offsets"][e], R["offsets"][e + 1]
+    src = R["perm_src"][lo:hi]
+    rows, js = src // k, src % k
+    ex = Expert(inputs, e, group)
+    X = to_f64(inputs["x"][rows])
+    if fw is None:
+        fw = expert_forward(ex, X, lam)
+    out = {"fw": fw, "O": fw["O"]}
+    if backward:
+        dO = R["gates"][rows, js][:, None] * to_f64(inputs["dy"][rows])
+        out.update(expert_backward(ex, X, fw, dO, lam))
+    return out
+
+
+def combine(gam: np.ndarray, O: np.ndarray, slot_pos: np.ndarray) -> np.ndarray:
+    """y[t] = sum_j gamma[t, j] O[slot_pos[t k + j]], j ascending."""
+    T, k = gam.shape
+    slot = np.asarray(slot_pos).reshape(T, k)
+    y = np.zeros((T, O.shape[1]))
+    for j in range(k):
+        y += gam[:, j:j + 1] * O[slot[:, j]]
+    return y
+
+
+def gate_backward(dy, O: np.ndarray, gam: np.ndarray, topk_idx: np.ndarray,
+                  slot_pos: np.ndarray, w_router) -> tuple:
+    """The gate path of the backward with the selection held fixed:
+    dgamma[t, j] = <dY_t, O_(t,j)>, the softmax over the selected logits
+    dl = gamma (dgamma - <gamma, dgamma>), and the router-input gradient
+    dx_r[t] = sum_j dl[t, j] W_r[:, e(t, j)] (the router itself is frozen)."""
+    dy = to_f64(dy)
+    wr = to_f64(w_router)
+    T, k = gam.shape
+    slot = np.asarray(slot_pos).reshape(T, k)
+    dgam = np.einsum("td,tjd->tj", dy, O[slot])
+    dl = gam * (dgam - (gam * dgam).sum(axis=1, keepdims=True))
+    dx_r = np.zeros(dy.shape)
+    for j in range(k):
+        dx_r += dl[:, j:j + 1] * wr[:, topk_idx[:, j]].T
+    return dgam, dl, dx_r
+
+
 def forward(inputs: dict, k: int, group: int, lam: float = 1.0,
             topk_idx: np.ndarray | None = None, keep: bool = False) -> dict:
     """y[t] = sum_j gamma[t, j] * O_{e(t,j)}(x_t), j ascending."""
     R = route(inputs, k, topk_idx)
-    x = to_f64(inputs["x"])
-    T, d = x.shape
+    T, d = inputs["x"].shape
     E = R["logits"].shape[1]
-    S = T * k
-    O = np.zeros((S, d))
+    O = np.zeros((T * k, d))
     saved = {}
     for e in range(E):
         lo, hi = R["offsets"][e], R["offsets"][e + 1]
         if hi == lo:
             continue
-        rows = R["perm_src"][lo:hi] // k
-        ex = Expert(inputs, e, group)
-        fw = expert_forward(ex, x[rows], lam)
-        O[lo:hi] = fw["O"]
+        res = expert_rows(inputs, R, e, k, group, lam)
+        O[lo:hi] = res["O"]
         if keep:
-            saved[e] = fw
-    gam = R["gates"]
-    y = np.zeros((T, d))
-    for j in range(k):
-        y += gam[:, j:j + 1] * O[R["slot_pos"].reshape(T, k)[:, j]]
+            saved[e] = res["fw"]
     out = dict(R)
-    out.update({"e_out": O, "y": y})
+    out.update({"e_out": O, "y": combine(R["gates"], O, R["slot_pos"])})
     if keep:
         out["saved"] = saved
     return out
+
+
+ADAPTER_GRADS = ("dA_gate", "dB_gate", "dA_up", "dB_up", "dA_down", "dB_down")
+
+
+def adapter_grad_shapes(inputs: dict) -> dict:
+    E, f, d = inputs["q_gate"].shape[0], inputs["q_gate"].shape[1], inputs["q_down"].shape[1]
+    r = inputs["A_gate"].shape[1]
+    return {"dA_gate": (E, r, d), "dB_gate": (E, f, r), "dA_up": (E, r, d), "dB_up": (E, f, r),
+            "dA_down": (E, r, f), "dB_down": (E, d, r)}
 
 
 def backward(inputs: dict, fwd: dict, k: int, group: int, lam: float = 1.0) -> dict:
     """Gradients of L = sum_t <dY_t, y_t> with the top-k choice held fixed:
     dX (through the experts and through the gates into the router input) and
     the six adapter gradients per expert.  The router and base are frozen."""
-    x = to_f64(inputs["x"])
-    dy = to_f64(inputs["dy"])
-    wr = to_f64(inputs["w_router"])
-    T, d = x.shape
-    E = wr.shape[1]
-    idx, gam = fwd["topk_idx"], fwd["gates"]
+    T, d = inputs["x"].shape
+    E = inputs["w_router"].shape[1]
     slot = fwd["slot_pos"].reshape(T, k)
-    O = fwd["e_out"]
-    # gate path: dgamma, softmax over the selected logits, router input grad
-    dgam = np.einsum("td,tjd->tj", dy, O[slot])
-    dl = gam * (dgam - (gam * dgam).sum(axis=1, keepdims=True))
-    dx = np.zeros((T, d))
-    for j in range(k):
-        dx += dl[:, j:j + 1] * wr[:, idx[:, j]].T
-    # expert path
-    f = inputs["q_gate"].shape[1]
-    r = inputs["A_gate"].shape[1]
-    grads = {"dA_gate": np.zeros((E, r, d)), "dB_gate": np.zeros((E, f, r)),
-             "dA_up": np.zeros((E, r, d)), "dB_up": np.zeros((E, f, r)),
-             "dA_down": np.zeros((E, r, f)), "dB_down": np.zeros((E, d, r))}
+    dgam, dl, dx_r = gate_backward(inputs["dy"], fwd["e_out"], fwd["gates"], fwd["topk_idx"],
+                                   fwd["slot_pos"], inputs["w_router"])
+    grads = {n: np.zeros(shape) for n, shape in adapter_grad_shapes(inputs).items()}
     dXp = np.zeros((T * k, d))
     for e in range(E):
         lo, hi = fwd["offsets"][e], fwd["offsets"][e + 1]
         if hi == lo:
             continue
-        src = fwd["perm_src"][lo:hi]
-        rows, js = src // k, src % k
-        ex = Expert(inputs, e, group)
-        fw = fwd["saved"][e] if "saved" in fwd else expert_forward(ex, x[rows], lam)
-        dO = gam[rows, js][:, None] * dy[rows]
-        g = expert_backward(ex, x[rows], fw, dO, lam)
+        res = expert_rows(inputs, fwd, e, k, group, lam, backward=True,
+                          fw=fwd.get("saved", {}).get(e))
         for name in grads:
-            grads[name][e] = g[name]
-        dXp[lo:hi] = g["dX"]
+            grads[name][e] = res[name]
+        dXp[lo:hi] = res["dX"]
+    dx = dx_r.copy()
     for j in range(k):
         dx += dXp[slot[:, j]]
-    out = {"dx": dx, "dx_router": dx - sum(dXp[slot[:, j]] for j in range(k)),
-           "dgates": dgam, "dlogits_sel": dl}
+    out = {"dx": dx, "dx_router": dx_r, "dgates": dgam, "dlogits_sel": dl}
     out.update(grads)
     return out
 
@@ -362,16 +395,9 @@ def backward_tokens(inputs: dict, tokens, k: int, group: int, lam: float = 1.0,
 
 
 def expert_grads(inputs: dict, R: dict, e: int, k: int, group: int, lam: float = 1.0) -> dict:
-    """The six adapter gradients of expert e given the full routing R (as
-    returned by route())."""
-    lo, hi = R["offsets"][e], R["offsets"][e + 1]
-    src = R["perm_src"][lo:hi]
-    rows, js = src // k, src % k
-    ex = Expert(inputs, e, group)
-    X = to_f64(inputs["x"][rows])
-    fw = expert_forward(ex, X, lam)
-    dO = R["gates"][rows, js][:, None] * to_f64(inputs["dy"][rows])
-    return expert_backward(ex, X, fw, dO, lam)
+    """The six adapter gradients (and dX rows) of expert e given the full
+    routing R (as returned by route())."""
+    return expert_rows(inputs, R, e, k, group, lam, backward=True)
 
 
 # --------------------------------------------------- adapter optimizer step --

@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_tqp.
 
 MOE_F32, MOE_BF16 = 0, 1
 CALL_ROUTE, CALL_PERMUTE, CALL_EXPERT_FWD, CALL_COMBINE, CALL_ADAPTER_BWD = range(5)
+# workspace flags OR-ed into a call id of moe_workspace_size
+WS_SAVE_GIVEN, WS_PACKED_GIVEN = 0x100, 0x200
 MAT_GATE_UP, MAT_DOWN = 0, 1
 
 

@@ -100,16 +100,23 @@ bool use_mfma(const moe_dims *d) {
   return d->act == MOE_BF16 && d->group == 128 && d->d_model % 128 == 0 && d->d_ff % 128 == 0;
 }
 
+// Workspace flags of a call (the bits above the call id in
+// moe_workspace_size): what the caller supplies, so that the call needs no
+// room for it.
+bool ws_save_given(int flags) { return (flags & MOE_WS_SAVE_GIVEN) != 0; }
+bool ws_packed_given(int flags) { return (flags & MOE_WS_PACKED_GIVEN) != 0; }
+
 // ---- expert forward workspace
 struct FwdLayout {
   size_t tiles, ntiles, save, G32, U32, tiles_m, ntiles_m, tiles_p, ntiles_p, rs_x, rs_h, rt_g,
       rt_u, rt_d, total;
-  explicit FwdLayout(const moe_dims *d) {
+  FwdLayout(const moe_dims *d, int flags) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, E = d->n_experts;
     Carve c;
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
-    save = c.take(SaveLayout(d).total);  // used when the caller passes no save buffer
+    // Z, G, U, H when the caller passes no save buffer
+    save = ws_save_given(flags) ? 0 : c.take(SaveLayout(d).total);
     if (use_mfma(d)) {
       G32 = U32 = 0;
       tiles_m = c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2));
@@ -118,10 +125,12 @@ struct FwdLayout {
       ntiles_p = c.take(sizeof(int));
       rs_x = c.take((size_t)d->T * (dm / 128) * 4);
       rs_h = c.take(S * (f / 128) * 4);
-      // scale ratios of the three base matrices, [E][N][K/128] f32
-      rt_g = c.take(E * f * (dm / 128) * 4);
-      rt_u = c.take(E * f * (dm / 128) * 4);
-      rt_d = c.take(E * dm * (f / 128) * 4);
+      // scale ratios of the three base matrices, [E][N][K/128] f32 (the
+      // forward-packed bases carry their own)
+      const bool pk = ws_packed_given(flags);
+      rt_g = pk ? 0 : c.take(E * f * (dm / 128) * 4);
+      rt_u = pk ? 0 : c.take(E * f * (dm / 128) * 4);
+      rt_d = pk ? 0 : c.take(E * dm * (f / 128) * 4);
     } else {
       G32 = c.take(S * f * 4);
       U32 = c.take(S * f * 4);
@@ -152,7 +161,7 @@ size_t qt_slot_bytes(const moe_dims *d) {
 struct BwdLayout {
   size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, bt, lt, wt,
       wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
-  explicit BwdLayout(const moe_dims *d) {
+  BwdLayout(const moe_dims *d, int flags) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
     const bool mf = use_mfma(d);
     Carve c;
@@ -172,8 +181,9 @@ struct BwdLayout {
     bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
     // A of down, gate, up transposed to [E][N][r] (bf16), for rank 16
     lt = mf && d->rank == 16 ? c.take((size_t)d->n_experts * d->rank * (f + 2 * dm) * 2) : 0;
-    // transposed int4 base + scales, two slots: down, then gate and up
-    wt = mf ? c.take(2 * qt_slot_bytes(d)) : 0;
+    // transposed int4 base + scales, two slots (down, then gate; up), unless
+    // the caller passes every matrix transposed-packed
+    wt = mf && !ws_packed_given(flags) ? c.take(2 * qt_slot_bytes(d)) : 0;
     wr_t = c.take((size_t)d->n_experts * dm * 4);
     dx_r = c.take((size_t)d->T * dm * 4);
     dO = mf ? 0 : c.take(S * dm * ab);   // the matrix-core path reads dy by token instead
@@ -186,15 +196,25 @@ struct BwdLayout {
   }
 };
 
+// call: a moe_call id, optionally OR-ed with MOE_WS_* flags
 size_t ws_bytes_for(const moe_dims *d, int call) {
-  switch (call) {
+  const int flags = call & ~0xff;
+  switch (call & 0xff) {
     case MOE_CALL_ROUTE: return moe::route_ws_bytes(d->T, d->d_model, d->n_experts);
     case MOE_CALL_PERMUTE: return moe::permute_ws_bytes(d->T, d->n_experts, d->top_k);
-    case MOE_CALL_EXPERT_FWD: return FwdLayout(d).total;
+    case MOE_CALL_EXPERT_FWD: return FwdLayout(d, flags).total;
     case MOE_CALL_COMBINE: return 0;
-    case MOE_CALL_ADAPTER_BWD: return BwdLayout(d).total;
+    case MOE_CALL_ADAPTER_BWD: return BwdLayout(d, flags).total;
     default: return (size_t)-1;
   }
+}
+
+// the flags a call's own arguments imply
+int fwd_flags(const void *save, const moe_qlora &g, const moe_qlora &u, const moe_qlora &dn) {
+  return (save ? MOE_WS_SAVE_GIVEN : 0) | (g.qf && u.qf && dn.qf ? MOE_WS_PACKED_GIVEN : 0);
+}
+int bwd_flags(const moe_qlora &g, const moe_qlora &u, const moe_qlora &dn) {
+  return g.qt && u.qt && dn.qt ? MOE_WS_PACKED_GIVEN : 0;
 }
 
 moe_status check_ws(const moe_dims *d, int call, const void *ws, size_t ws_bytes) {
@@ -302,8 +322,11 @@ moe_status moe_timer_stop(float *total_ms, int32_t *launches) {
 moe_status moe_workspace_size(const moe_dims *dims, int32_t call, size_t *bytes) {
   TRY(check_dims(dims));
   if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
-  if (call < MOE_CALL_ROUTE || call > MOE_CALL_ADAPTER_BWD)
+  const int id = call & 0xff, flags = call & ~0xff;
+  if (id < MOE_CALL_ROUTE || id > MOE_CALL_ADAPTER_BWD)
     return fail(MOE_ERR_INVALID, "unknown call id");
+  if (flags & ~(MOE_WS_SAVE_GIVEN | MOE_WS_PACKED_GIVEN))
+    return fail(MOE_ERR_INVALID, "unknown workspace flag");
   *bytes = ws_bytes_for(dims, call);
   return MOE_OK;
 }
@@ -513,14 +536,14 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   TRY(check_qlora(gate, "gate"));
   TRY(check_qlora(up, "up"));
   TRY(check_qlora(down, "down"));
-  TRY(check_ws(dims, MOE_CALL_EXPERT_FWD, ws, ws_bytes));
+  TRY(check_ws(dims, MOE_CALL_EXPERT_FWD | fwd_flags(save, gate, up, down), ws, ws_bytes));
   hipStream_t st = (hipStream_t)stream;
   const bool bf = dims->act == MOE_BF16;
   const int T = dims->T, d = dims->d_model, E = dims->n_experts, k = dims->top_k, f = dims->d_ff,
             r = dims->rank, g = dims->group;
   const size_t S = (size_t)T * k;
   const float lam = dims->lora_scale;
-  FwdLayout L(dims);
+  FwdLayout L(dims, fwd_flags(save, gate, up, down));
   void *sv = save ? save : at<char>(ws, L.save);
   SaveLayout SL(dims);
   float *Z = at<float>(sv, SL.Z);
@@ -646,14 +669,14 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   TRY(check_qlora(gate, "gate"));
   TRY(check_qlora(up, "up"));
   TRY(check_qlora(down, "down"));
-  TRY(check_ws(dims, MOE_CALL_ADAPTER_BWD, ws, ws_bytes));
+  TRY(check_ws(dims, MOE_CALL_ADAPTER_BWD | bwd_flags(gate, up, down), ws, ws_bytes));
   hipStream_t st = (hipStream_t)stream;
   const bool bf = dims->act == MOE_BF16;
   const int T = dims->T, d = dims->d_model, E = dims->n_experts, k = dims->top_k, f = dims->d_ff,
             r = dims->rank, g = dims->group;
   const size_t S = (size_t)T * k;
   const float lam = dims->lora_scale;
-  BwdLayout L(dims);
+  BwdLayout L(dims, bwd_flags(gate, up, down));
   SaveLayout SL(dims);
   const float *Z = at<const float>((void *)save, SL.Z);
   const void *Gs = at<const char>((void *)save, SL.G), *Us = at<const char>((void *)save, SL.U),
@@ -673,7 +696,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   moe::launch_transpose_f32(w_router, d, E, wr_t, st);
   if (!use_mfma(dims))
     TIMED(MOE_KT_GATE_GRAD, st,
-          moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r,
+          moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, E, dx_r,
                                 dO, st));
 
   if (use_mfma(dims)) {
@@ -787,9 +810,9 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
     // gate gradient and the per-token sum of dX_perm, one pass per token
     TIMED(MOE_KT_GATE_GRAD, st, {
-      if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, dx,
+      if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, E, dx,
                                  st)) {
-        moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, dx_r,
+        moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, E, dx_r,
                               nullptr, st);
         moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);
       }

@@ -118,7 +118,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void gate_grad_kernel(
     const T *__restrict__ dy, const T *__restrict__ e_out, const int32_t *__restrict__ topk_idx,
     const float *__restrict__ gates, const int32_t *__restrict__ slot_pos,
-    const float *__restrict__ wr_t, int d, int k, float *__restrict__ dx_r, T *__restrict__ dO) {
+    const float *__restrict__ wr_t, int d, int k, int E, float *__restrict__ dx_r,
+    T *__restrict__ dO) {
   constexpr int V = Vec16<T>::N;
   __shared__ float red[4 * 32];
   __shared__ int sp[32], se[32];
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
     sp[threadIdx.x] = slot_pos[(size_t)t * k + threadIdx.x];
-    se[threadIdx.x] = topk_idx[(size_t)t * k + threadIdx.x];
+    // (clamped: a caller-supplied index outside [0, E) must not read past W_r)
+    se[threadIdx.x] = min(max(topk_idx[(size_t)t * k + threadIdx.x], 0), E - 1);
     sg[threadIdx.x] = gates[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
     const bf16_t *__restrict__ dy, const bf16_t *__restrict__ e_out,
     const int32_t *__restrict__ topk_idx, const float *__restrict__ gates,
     const int32_t *__restrict__ slot_pos, const float *__restrict__ wr_t,
-    const bf16_t *__restrict__ dxp, int T, int d, int k, bf16_t *__restrict__ dx) {
+    const bf16_t *__restrict__ dxp, int T, int d, int k, int E, bf16_t *__restrict__ dx) {
   constexpr int KM = 4 * KB;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= T) return;
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
   for (int j = 0; j < KM; ++j) {
     const int jc = j < k ? j : k - 1;
     p[j] = slot_pos[(size_t)t * k + jc];
-    e[j] = topk_idx[(size_t)t * k + jc];
+    e[j] = min(max(topk_idx[(size_t)t * k + jc], 0), E - 1);   // in range (see gate_grad_kernel)
     g[j] = gates[(size_t)t * k + jc];
     part[j] = 0.f;
   }
@@ -348,25 +350,25 @@ void launch_transpose_f32(const float *in, int rows, int cols, float *out, hipSt
 
 void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_t *topk_idx,
                       const float *gates, const int32_t *slot_pos, const float *wr_t, int Tn,
-                      int d, int k, float *dx_r, void *dO, hipStream_t st) {
+                      int d, int k, int E, float *dx_r, void *dO, hipStream_t st) {
   if (bf16)
     gate_grad_kernel<bf16_t><<<Tn, 256, 0, st>>>((const bf16_t *)dy, (const bf16_t *)e_out,
-                                                 topk_idx, gates, slot_pos, wr_t, d, k, dx_r,
+                                                 topk_idx, gates, slot_pos, wr_t, d, k, E, dx_r,
                                                  (bf16_t *)dO);
   else
     gate_grad_kernel<float><<<Tn, 256, 0, st>>>((const float *)dy, (const float *)e_out,
-                                                topk_idx, gates, slot_pos, wr_t, d, k, dx_r,
+                                                topk_idx, gates, slot_pos, wr_t, d, k, E, dx_r,
                                                 (float *)dO);
 }
 
 bool launch_token_bwd(const void *dy, const void *e_out, const int32_t *topk_idx,
                       const float *gates, const int32_t *slot_pos, const float *wr_t,
-                      const void *dxp, int Tn, int d, int k, void *dx, hipStream_t st) {
+                      const void *dxp, int Tn, int d, int k, int E, void *dx, hipStream_t st) {
   if (d % 8 != 0 || k > 16) return false;
   const int wgrid = (Tn + 3) / 4;
   const bf16_t *a = (const bf16_t *)dy, *b = (const bf16_t *)e_out, *c = (const bf16_t *)dxp;
   bf16_t *o = (bf16_t *)dx;
-#define MOE_TB(KB) token_bwd_wave_kernel<KB><<<wgrid, 256, 0, st>>>(a, b, topk_idx, gates, slot_pos, wr_t, c, Tn, d, k, o)
+#define MOE_TB(KB) token_bwd_wave_kernel<KB><<<wgrid, 256, 0, st>>>(a, b, topk_idx, gates, slot_pos, wr_t, c, Tn, d, k, E, o)
   switch ((k + 3) / 4) {
     case 1: MOE_TB(1); break;
     case 2: MOE_TB(2); break;

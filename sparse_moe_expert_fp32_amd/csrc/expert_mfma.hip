@@ -88,16 +88,24 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 // ------------------------------------------------------------ scale ratios --
 // Per column c of a quantized matrix [E][N] with ng groups, group-major:
 // rt[e][g][c] = s'[g-1] / s'[g] for g >= 1 and rt[e][0][c] = s'[ng-1] (the
-// final multiplier), where s' is the bf16 scale with magnitudes below 2^-100
-// raised to 2^-100 (so a zero scale leaves a contribution of at most 2^-100
-// times its partial sum).  One thread per column: its ng scales are one
+// final multiplier).  s' is the bf16 scale s with every magnitude below the
+// column's floor m 2^-24 (m = the column's largest |s|, and the floor at
+// least 2^-100) raised to that floor.  So no ratio exceeds 2^24 and the
+// telescoped accumulator stays within 2^24 times the sum of the partial
+// products, far from the float32 range, however zero or widely spread the
+// scales are; a raised group contributes at most floor * |its partial sum|
+// instead of s times it, i.e. an error of one float32 rounding of the
+// column's largest group.  One thread per column: its ng scales are one
 // contiguous run, and each group's writes are contiguous across the wave.
 __global__ __launch_bounds__(256) void scale_ratio_kernel(const uint16_t *__restrict__ s, int E,
                                                           int N, int ng, float *__restrict__ rt) {
   const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
   if (c >= N) return;
-  auto guard = [](float v) { return fabsf(v) < 0x1p-100f ? 0x1p-100f : v; };
   const uint16_t *sc = s + ((size_t)e * N + c) * ng;
+  float m = 0.f;
+  for (int g = 0; g < ng; ++g) m = fmaxf(m, fabsf(bf2f(sc[g])));
+  const float floor_v = fmaxf(m * 0x1p-24f, 0x1p-100f);
+  auto guard = [&](float v) { return fabsf(v) < floor_v ? floor_v : v; };
   float *out = rt + (size_t)e * ng * N + c;
   float prev = guard(bf2f(sc[0]));
   for (int g = 1; g < ng; ++g) {
@@ -515,7 +523,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
           for (int i = 0; i < 4; ++i)
             bv[nf][i] = (short)(Bm[rowb + min(j0 + 4 * lg2 + i, A.r - 1)] & kmask[i]);
         }
-        const int jz = min(j0 + 4 * lg2, A.r - 1);
+        // Z side: rank positions j0 + 4 lg2 + i past r are zeroed like the B
+        // side (the 16-byte load starts at most at r - 4, so it stays inside
+        // the row's r values; what it reads past the rank is never used)
+        const int jz = min(j0 + 4 * lg2, A.r - 4);
 #pragma unroll
         for (int src = 0; src < NSRC; ++src) {
           const float *Zp = src ? A.Z1 : A.Z0;
@@ -529,6 +540,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
 #pragma unroll
               for (int i = 0; i < 4; ++i) z[i] = zr[min(j0 + 4 * lg2 + i, A.r - 1)];
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = kmask[i] ? z[i] : 0.f;
             const short4_t av = zbf(z);
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf) {

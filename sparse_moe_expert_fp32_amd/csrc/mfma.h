@@ -114,20 +114,19 @@ DEV const void *uniform_ptr(const void *p) {
   return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 // lds: wave-uniform LDS byte address where lane i's data lands (+ size * i).
-// Each transfer sets M0 itself; M0 is a reserved register that the compiler
-// initialises right before every instruction of its own that reads it, so no
-// value of the compiler's lives in M0 across these statements.
+// Each transfer sets M0 itself and declares it clobbered, so the compiler
+// keeps none of its own values in M0 across these statements.
 DEV void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 DEV void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 DEV void dma2(const void *sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt

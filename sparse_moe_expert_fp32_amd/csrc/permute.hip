@@ -19,22 +19,46 @@ namespace moe {
 
 constexpr int PB = 256;  // tokens per histogram block
 
+// Caller-supplied indices may be out of range or repeat within a token
+// (the router always writes k distinct valid ones).  Each token's entries are
+// first made canonical, in j order: an index outside [0, E) is clamped into
+// range and an index a lower j already took is replaced by the lowest expert
+// the token does not use yet (k <= E, so one exists).  Valid input passes
+// through unchanged; invalid input still yields a bijective placement with
+// every access inside the buffers.  canon[t k + j] holds the result.
 __global__ __launch_bounds__(PB) void perm_hist_kernel(const int32_t *__restrict__ idx, int Tn,
                                                        int E, int k,
                                                        int32_t *__restrict__ block_counts,
-                                                       int32_t *__restrict__ rank) {
+                                                       int32_t *__restrict__ rank,
+                                                       int32_t *__restrict__ canon) {
   extern __shared__ unsigned long long masks[];  // [4][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x * PB + tid;
   for (int i = tid; i < 4 * E; i += PB) masks[i] = 0ull;
+  if (t < Tn) {
+    int32_t *ct = canon + (size_t)t * k;
+    auto used = [&](int e, int j) {
+      for (int i = 0; i < j; ++i)
+        if (ct[i] == e) return true;
+      return false;
+    };
+    for (int j = 0; j < k; ++j) {
+      int e = min(max(idx[(size_t)t * k + j], 0), E - 1);
+      if (used(e, j)) {
+        e = 0;
+        while (used(e, j)) ++e;
+      }
+      ct[j] = e;
+    }
+  }
   __syncthreads();
   if (t < Tn)
-    for (int j = 0; j < k; ++j) atomicOr(&masks[wave * E + idx[(size_t)t * k + j]], 1ull << lane);
+    for (int j = 0; j < k; ++j) atomicOr(&masks[wave * E + canon[(size_t)t * k + j]], 1ull << lane);
   __syncthreads();
   if (t < Tn) {
     const unsigned long long lower = (1ull << lane) - 1ull;
     for (int j = 0; j < k; ++j) {
-      int e = idx[(size_t)t * k + j];
+      int e = canon[(size_t)t * k + j];
       int r = __popcll(masks[wave * E + e] & lower);
       for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
       rank[(size_t)t * k + j] = r;
@@ -77,14 +101,14 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
   if (e == E - 1) offsets[E] = sc[e];
 }
 
-__global__ void perm_scatter_kernel(const int32_t *__restrict__ idx, int S, int E, int k,
+__global__ void perm_scatter_kernel(const int32_t *__restrict__ canon, int S, int E, int k,
                                     const int32_t *__restrict__ block_off,
                                     const int32_t *__restrict__ offsets,
                                     const int32_t *__restrict__ rank,
                                     int32_t *__restrict__ perm_src, int32_t *__restrict__ slot_pos) {
   int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= S) return;
-  int t = s / k, b = t / PB, e = idx[s];
+  int t = s / k, b = t / PB, e = canon[s];
   int p = offsets[e] + block_off[(size_t)b * E + e] + rank[s];
   perm_src[p] = s;
   slot_pos[s] = p;
@@ -101,9 +125,12 @@ __global__ void perm_copy_kernel(const uint4 *__restrict__ x, const int32_t *__r
   for (int v = threadIdx.x & 63; v < vec_per_row; v += 64) dst[v] = src[v];
 }
 
+// workspace: block counts [nb][E] | rank [S] | canonical indices [S], each
+// 256-byte aligned
 size_t permute_ws_bytes(int T, int E, int k) {
-  size_t nb = (T + PB - 1) / PB;
-  return nb * E * sizeof(int32_t) + (size_t)T * k * sizeof(int32_t) + 256;
+  const size_t nb = (T + PB - 1) / PB, S = (size_t)T * k;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  return al(nb * E * sizeof(int32_t)) + al(S * sizeof(int32_t)) + al(S * sizeof(int32_t));
 }
 
 void launch_permute(const int32_t *idx, int Tn, int E, int k, int32_t *counts, int32_t *offsets,
@@ -112,11 +139,13 @@ void launch_permute(const int32_t *idx, int Tn, int E, int k, int32_t *counts, i
   int nb = (Tn + PB - 1) / PB;
   int S = Tn * k;
   int32_t *block_counts = (int32_t *)ws;
-  int32_t *rank = (int32_t *)((char *)ws + (((size_t)nb * E * 4 + 255) & ~(size_t)255));
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  int32_t *rank = (int32_t *)((char *)ws + al((size_t)nb * E * 4));
+  int32_t *canon = (int32_t *)((char *)rank + al((size_t)S * 4));
   perm_hist_kernel<<<nb, PB, 4 * E * sizeof(unsigned long long), st>>>(idx, Tn, E, k,
-                                                                       block_counts, rank);
+                                                                       block_counts, rank, canon);
   perm_scan_kernel<<<1, 1024, 0, st>>>(block_counts, nb, E, counts, offsets);
-  perm_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(idx, S, E, k, block_counts, offsets, rank,
+  perm_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(canon, S, E, k, block_counts, offsets, rank,
                                                        perm_src, slot_pos);
   if (x_perm)
     perm_copy_kernel<<<(S + 3) / 4, 256, 0, st>>>((const uint4 *)x, perm_src, S, k,

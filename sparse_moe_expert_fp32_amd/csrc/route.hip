@@ -180,6 +180,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
       for (int s = 0; s < splits; ++s) v += partial[((size_t)s * Tn + t) * E + e];
       if (bias) v += bias[e];
       if (logits_out) logits_out[(size_t)t * E + e] = v;
+      // a NaN logit (from non-finite x, W_r or bias) competes as -inf, so the
+      // selection always takes k distinct experts in [0, E): the order would
+      // otherwise never pick it and could run out of candidates
+      if (v != v) v = -INFINITY;
     } else {
       taken |= 1u << n;  // padding never wins
     }

@@ -58,14 +58,20 @@ class DeviceLayer:
         bwd = cfg.train if with_backward is None else with_backward
         self.save = (torch.empty(B.moe_save_size(self.dm), dtype=torch.uint8, device=self.dev)
                      if bwd else None)
-        calls = (B.CALL_ROUTE, B.CALL_PERMUTE, B.CALL_EXPERT_FWD, B.CALL_COMBINE) + \
-            ((B.CALL_ADAPTER_BWD,) if bwd else ())
-        self.ws = {c: torch.empty(max(1, B.moe_workspace_size(self.dm, c)), dtype=torch.uint8,
-                                  device=self.dev) for c in calls}
         # the frozen base re-laid out once (matrix-core path): stage-major for
         # the forward, transposed for the backward
         self.packed, self.packed_f = {}, {}
-        if pack_base and B.pack_base_supported(self.dm):
+        packing = pack_base and B.pack_base_supported(self.dm)
+        # workspaces sized for what this layer supplies (a save buffer when
+        # it trains, the packed bases when it packs)
+        flags = {B.CALL_EXPERT_FWD: (B.WS_SAVE_GIVEN if bwd else 0) |
+                 (B.WS_PACKED_GIVEN if packing else 0),
+                 B.CALL_ADAPTER_BWD: B.WS_PACKED_GIVEN if packing else 0}
+        calls = (B.CALL_ROUTE, B.CALL_PERMUTE, B.CALL_EXPERT_FWD, B.CALL_COMBINE) + \
+            ((B.CALL_ADAPTER_BWD,) if bwd else ())
+        self.ws = {c: torch.empty(max(1, B.moe_workspace_size(self.dm, c | flags.get(c, 0))),
+                                  dtype=torch.uint8, device=self.dev) for c in calls}
+        if packing:
             nbf = B.moe_pack_base_f_size(self.dm)
             nbt = B.moe_pack_base_t_size(self.dm) if bwd else 0
             for m in MATS:

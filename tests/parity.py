@@ -79,6 +79,53 @@ def run_gpu(cfg, inp, backward=True, want_logits=True):
     return out, L
 
 
+def per_row_rel(got, ref) -> np.ndarray:
+    """Relative L2 error of every row (leading index) of got against ref."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    g = got.reshape(got.shape[0], -1)
+    r = ref.reshape(ref.shape[0], -1)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def compare_layer(cfg, gpu: dict, ref: dict, backward: bool, report: dict, seed_note=""):
+    """Whole-tensor relative L2 of y, dX and the six adapter gradients, plus
+    the per-unit rules: every token's y and dX row and every expert's block
+    of each adapter gradient within the same tolerance of its own norm, and
+    experts with no rows exactly zero.  The per-expert maximum is reported."""
+    t = tol(cfg)
+    report["y"] = rel_l2(f64(gpu["y"]), ref["y"])
+    assert report["y"] <= t, f"y rel L2 {report['y']:.3e} > {t} {seed_note}"
+    ey = per_row_rel(f64(gpu["y"]), ref["y"])
+    report["y_token_max"] = float(ey.max())
+    assert ey.max() <= t, f"y of token {int(ey.argmax())}: rel L2 {ey.max():.3e} {seed_note}"
+    if not backward:
+        return report
+    report["dx"] = rel_l2(f64(gpu["dx"]), ref["dx"])
+    assert report["dx"] <= t, f"dx rel L2 {report['dx']:.3e}"
+    ex = per_row_rel(f64(gpu["dx"]), ref["dx"])
+    report["dx_token_max"] = float(ex.max())
+    assert ex.max() <= t, f"dx of token {int(ex.argmax())}: rel L2 {ex.max():.3e}"
+    counts = np.diff(np.asarray(ref["offsets"]))
+    empty = counts == 0
+    worst = (0.0, None, None)
+    for n in ADAPTERS:
+        report[n] = rel_l2(gpu[n], ref[n])
+        assert report[n] <= t, f"{n} rel L2 {report[n]:.3e}"
+        assert np.all(gpu[n][empty] == 0.0), f"{n} of an empty expert is not zero"
+        ee = per_row_rel(gpu[n][~empty], ref[n][~empty])
+        if ee.size and ee.max() > worst[0]:
+            worst = (float(ee.max()), n, int(np.nonzero(~empty)[0][ee.argmax()]))
+        assert ee.size == 0 or ee.max() <= t, \
+            f"{n} of expert {int(np.nonzero(~empty)[0][ee.argmax()])}: rel L2 {ee.max():.3e}"
+    report["expert_max"] = worst[0]
+    report["expert_max_at"] = f"{worst[1]}[{worst[2]}] ({int(counts[worst[2]])} rows)" \
+        if worst[1] else "-"
+    return report
+
+
 def full_parity(cfg, inp, backward=True, seed_note=""):
     """Whole-layer comparison for shapes the oracle finishes in seconds."""
     gpu, _ = run_gpu(cfg, inp, backward)
@@ -87,16 +134,8 @@ def full_parity(cfg, inp, backward=True, seed_note=""):
     lam = cfg.lora_scale
     fwd = oracle.forward(inp, cfg.k, cfg.group, lam, topk_idx=R["topk_idx"], keep=backward)
     report = {"near_ties": R["near_ties"], "gates": R["gates_err"]}
-    t = tol(cfg)
-    report["y"] = rel_l2(f64(gpu["y"]), fwd["y"])
-    assert report["y"] <= t, f"y rel L2 {report['y']:.3e} > {t} {seed_note}"
+    ref = dict(fwd)
     if backward:
-        bwd = oracle.backward(inp, fwd, cfg.k, cfg.group, lam)
-        report["dx"] = rel_l2(f64(gpu["dx"]), bwd["dx"])
-        assert report["dx"] <= t, f"dx rel L2 {report['dx']:.3e}"
-        for n in ADAPTERS:
-            report[n] = rel_l2(gpu[n], bwd[n])
-            assert report[n] <= t, f"{n} rel L2 {report[n]:.3e}"
-            empty = fwd["counts"] == 0
-            assert np.all(gpu[n][empty] == 0.0), f"{n} of an empty expert is not zero"
+        ref.update(oracle.backward(inp, fwd, cfg.k, cfg.group, lam))
+    compare_layer(cfg, gpu, ref, backward, report, seed_note)
     return report, gpu

@@ -52,6 +52,27 @@ def test_workspace_and_save_sizes(B):
     assert B.moe_save_size(big) >= 8192 * 12 * 768 * 2 * 3
 
 
+def test_workspace_flags_shrink_and_validate(B):
+    """A caller that supplies the save buffer and the packed bases needs less
+    workspace (the 8K shape: without the save region and the ratio tables in
+    the forward, without the transposed-base slots in the backward); unknown
+    flag bits are rejected."""
+    big = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16")
+    fw = B.moe_workspace_size(big, B.CALL_EXPERT_FWD)
+    fw_s = B.moe_workspace_size(big, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN)
+    fw_sp = B.moe_workspace_size(big, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN | B.WS_PACKED_GIVEN)
+    assert fw - fw_s >= B.moe_save_size(big)
+    assert fw_s - fw_sp >= 3 * 460 * 768 * 16 * 4
+    assert fw_sp < 16 << 20
+    bw = B.moe_workspace_size(big, B.CALL_ADAPTER_BWD)
+    bw_p = B.moe_workspace_size(big, B.CALL_ADAPTER_BWD | B.WS_PACKED_GIVEN)
+    assert bw - bw_p >= 2 * (460 * 2048 * 768 // 2)
+    out = ctypes.c_size_t(7)
+    assert B.LIB.moe_workspace_size(ctypes.byref(big), B.CALL_EXPERT_FWD | 0x400,
+                                    ctypes.byref(out)) == -1
+    assert out.value == 7
+
+
 BAD = [
     (dict(T=0), -1), (dict(E=0), -1), (dict(E=1025), -1), (dict(k=0), -1), (dict(k=9), -1),
     (dict(E=64, k=33), -1), (dict(r=0), -1), (dict(r=33), -1), (dict(group=16), -2),

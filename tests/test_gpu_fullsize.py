@@ -3,16 +3,20 @@ benchmark times (the same entry points, workspaces and persistent grids).
 
 * bf16 E=64 top-6 (T=4096) and the decode shape E=460 top-12 T=64: whole
   layer against the oracle, forward and adapter backward.
-* E=460 top-12 T=8192 (one 8K sequence, biased router): routing, counts and
-  the permutation for every token; y and dX on sampled tokens; the six adapter
-  gradients of sampled experts (largest, smallest non-empty, median, empty);
-  all computed one by one by the oracle.
+* E=460 top-12 T=8192 (one 8K sequence, biased router), forward and adapter
+  backward: routing, counts and the permutation for every token; then the
+  whole layer against the oracle (every token's y and dX, every expert's six
+  adapter gradients, with the per-token and per-expert rules), the oracle's
+  per-expert work spread over worker processes (tests/oracle_parallel.py).
+  The sampled comparisons (a few tokens, three experts, each computed one by
+  one by the oracle) stay as a fast first tier.
 """
 import numpy as np
 import pytest
 
 import oracle
-from parity import ADAPTERS, check_routing, f64, full_parity, rel_l2, run_gpu
+import oracle_parallel
+from parity import ADAPTERS, check_routing, compare_layer, f64, full_parity, rel_l2, run_gpu
 from sparse_moe_expert_fp32_amd import configs, inputs
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +102,20 @@ def test_e460_t8192_adapter_grads_sampled(cuda_ok, big):
             assert np.all(gpu[n][e] == 0.0)
     show("E460 T8192 adapter grads", {"experts": len(experts), "worst": worst,
                                       "rows": [int(counts[e]) for e in experts]})
+
+
+def test_e460_t8192_whole_layer(cuda_ok, big):
+    """Every token and every expert at the 8K training shape: y, dX, e_out
+    and the six adapter gradients against the fp64 oracle, evaluated on the
+    GPU's routing (identical to the oracle's except on near-tie tokens)."""
+    cfg, inp, gpu, L, R, _ = big
+    ref = oracle_parallel.layer(inp, cfg, topk_idx=R["topk_idx"], backward=True,
+                                log=lambda m: print(f"[fullsize] {m}", flush=True))
+    report = {"near_ties": R["near_ties"], "substituted": R["substituted"]}
+    report["e_out"] = rel_l2(f64(gpu["e_out"]), ref["e_out"])
+    assert report["e_out"] <= 1e-2
+    compare_layer(cfg, gpu, ref, True, report)
+    show("E460 T8192 whole layer", report)
 
 
 def test_e460_t8192_bitwise_repeatable(cuda_ok, big):

@@ -54,6 +54,8 @@ def test_small_f32_ragged(cuda_ok):
     dict(E=130, k=12, T=64, cfg_id=234, router_bias_var=0.0),  # many empty experts
     dict(E=40, k=13, T=45, cfg_id=235),                  # k not a multiple of 4
     dict(E=48, k=20, T=40, cfg_id=236),                  # k > 16: block-per-token kernels
+    dict(d=384, cfg_id=237),                             # d % 256 != 0: partial column tile
+    dict(d=640, f=256, T=150, cfg_id=238),               # (down output and dX_perm)
 ])
 def test_edge_shapes(cuda_ok, kw):
     cfg = cfg_of(**kw)
@@ -167,6 +169,10 @@ def test_packed_base_matches_plain_layout(cuda_ok, kw):
             # to the plain layout (both or neither), down stays packed
             L.w["up"] = B.qlora(L.t["q_up"], L.t["s_up"], L.t["A_up"], L.t["B_up"],
                                 L.packed["up"], None)
+            # (the forward now re-derives the ratio tables: a workspace with room)
+            L.ws[B.CALL_EXPERT_FWD] = torch.empty(
+                B.moe_workspace_size(L.dm, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN),
+                dtype=torch.uint8, device="cuda:0")
         L.train_step()
         torch.cuda.synchronize()
         out.append({"y": to_numpy(L.y), "e_out": to_numpy(L.e_out), "dx": to_numpy(L.dx),
@@ -287,3 +293,117 @@ def test_grow_copy_and_couple_scalar_paths(cuda_ok):
     torch.cuda.synchronize()
     want = (x_np[1:].astype(np.float64) - m_np[1:].astype(np.float64)).astype(np.float32)
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("r", [4, 8, 32])
+def test_matrix_core_ranks(cuda_ok, r):
+    """Adapter ranks other than 16 on the matrix-core path (their epilogues
+    read Z and the adapter factors from global memory, masked to the rank;
+    rank 32 takes two K steps), forward and backward against the oracle."""
+    cfg = cfg_of(r=r, cfg_id=300 + r)
+    rep, _ = full_parity(cfg, inputs.generate(cfg, 0))
+    show(f"rank {r}", rep)
+
+
+def _bf16_pow2(bits: np.ndarray, e: int) -> np.ndarray:
+    """bf16 bit patterns times 2^e (exact: exponent field moved by e)."""
+    b = bits.astype(np.int32)
+    nz = (b & 0x7F80) != 0
+    return np.where(nz, b + (e << 7), b).astype(np.uint16)
+
+
+def test_group_scales_zero_and_spread(cuda_ok):
+    """Group scales on the matrix-core path: columns with an all-zero group
+    (q = 0, s = 0) and columns whose group scales span 2^48 (one group's
+    scale times 2^24, the next zero, the next times 2^-24), in the gate and
+    down matrices of every expert.  The forward telescopes group scales
+    through ratios, so this is where a zero scale or a large spread could
+    overflow; the backward scales its activations instead.  Forward and
+    backward against the oracle, y also column by column."""
+    cfg = cfg_of(T=200, E=12, k=3, d=384, f=384, cfg_id=310)
+    inp = inputs.generate(cfg, 0)
+    for m in ("gate", "down"):
+        q, sc = inp[f"q_{m}"].copy(), inp[f"s_{m}"].copy()
+        N = q.shape[1]
+        spread = np.arange(N) % 7 == 0
+        zero = np.arange(N) % 7 == 3
+        sc[:, spread, 0] = _bf16_pow2(sc[:, spread, 0], 24)
+        sc[:, spread, 2] = _bf16_pow2(sc[:, spread, 2], -24)
+        for sel in (spread, zero):
+            sc[:, sel, 1] = 0
+            q[:, sel, 64:128] = 0
+        inp[f"q_{m}"], inp[f"s_{m}"] = q, sc
+    rep, gpu = full_parity(cfg, inp)
+    ref = oracle.forward(inp, cfg.k, cfg.group, cfg.lora_scale, topk_idx=gpu["topk_idx"])
+    ecol = rel_l2_cols = [rel_l2(oracle.to_f64(gpu["y"])[:, c], ref["y"][:, c])
+                          for c in range(cfg.d)]
+    assert np.all(np.isfinite(oracle.to_f64(gpu["y"])))
+    assert max(ecol) <= 1e-2, (int(np.argmax(ecol)), max(ecol))
+    rep["y_column_max"] = float(max(rel_l2_cols))
+    show("group scales", rep)
+
+
+def test_nan_input_row_keeps_routing_valid(cuda_ok):
+    """A NaN in a row of x makes that token's logits NaN: the router still
+    writes k distinct experts in [0, E) for it (NaN competes as -inf), every
+    other token is routed as the oracle routes it, and the permutation stays
+    a bijection."""
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
+    cfg = cfg_of(T=100, E=20, k=6, cfg_id=320, train=False)
+    inp = inputs.generate(cfg, 0)
+    bad = [5, 77]
+    x = inp["x"].copy()
+    x[5, 17] = 0x7FC0                      # bf16 quiet NaN
+    x[77, :] = 0x7FC0
+    inp["x"] = x
+    L = DeviceLayer(cfg, inp, device="cuda:0", want_logits=True, with_backward=False)
+    L.forward()
+    torch.cuda.synchronize()
+    idx = to_numpy(L.topk_idx)
+    assert idx.min() >= 0 and idx.max() < cfg.E
+    for t in range(cfg.T):
+        assert len(set(idx[t].tolist())) == cfg.k, t
+    for t in bad:                          # all logits NaN: lowest indices, in order
+        assert idx[t].tolist() == list(range(cfg.k)), idx[t]
+    good = np.setdiff1d(np.arange(cfg.T), bad)
+    l64 = oracle.router_logits(inp["x"][good], inp["w_router"], inp.get("b_router"))
+    ref = oracle.topk(l64, cfg.k)
+    b, o = oracle.near_ties(l64, cfg.k)
+    assert np.all((idx[good] == ref).all(axis=1) | b | o)
+    ps = to_numpy(L.perm_src)
+    assert np.array_equal(np.sort(ps), np.arange(cfg.S))
+    y = oracle.to_f64(to_numpy(L.y))
+    assert np.all(np.isfinite(y[good]))
+
+
+def test_permute_repairs_invalid_caller_indices(cuda_ok):
+    """moe_permute fed indices outside [0, E) and repeated within a token: each
+    token's entries are made valid in j order (clamped; a repeat becomes the
+    lowest unused expert), and the placement is that of the repaired routing
+    (bit-exact against the oracle's permutation of it)."""
+    import torch
+    from sparse_moe_expert_fp32_amd.layer import DeviceLayer, to_numpy
+    cfg = cfg_of(T=300, E=10, k=4, d=128, f=128, cfg_id=330, train=False)
+    inp = inputs.generate(cfg, 0)
+    rng = np.random.default_rng(3)
+    idx = rng.integers(-3, 14, size=(cfg.T, cfg.k)).astype(np.int32)
+    idx[0] = [2, 2, 2, 2]
+    idx[1] = [-1, -5, 20, 9]
+    L = DeviceLayer(cfg, inp, with_backward=False)
+    L.topk_idx.copy_(torch.from_numpy(idx))
+    L.permute()
+    torch.cuda.synchronize()
+    fixed = np.empty_like(idx)
+    for t in range(cfg.T):
+        used = []
+        for j in range(cfg.k):
+            e = min(max(int(idx[t, j]), 0), cfg.E - 1)
+            if e in used:
+                e = min(set(range(cfg.E)) - set(used))
+            used.append(e)
+        fixed[t] = used
+    assert fixed[0].tolist() == [2, 0, 1, 3] and fixed[1].tolist() == [0, 1, 9, 2]
+    ref = oracle.permutation(fixed, cfg.E)
+    for name, r in zip(("counts", "offsets", "perm_src", "slot_pos"), ref):
+        assert np.array_equal(to_numpy(getattr(L, name)), r), name

@@ -552,3 +552,33 @@ def test_growth_router_noise_moves_only_copies():
     assert np.array_equal(g["w_router"][:, 1::2], want)
     st = oracle.routing_load(oracle.route(g, cfg.k * 2)["topk_idx"], cfg.E * 2)
     assert st["max_over_mean"] >= 1.0 and 0 <= st["empty"] <= cfg.E * 2
+
+
+def test_routing_load_hand_counted_fixture():
+    """The routing-collapse statistic against hand-counted loads
+    (tests/golden/routing_load.json): empty experts, including the
+    highest-index one, and a maximum shared by two experts."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "routing_load.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        st = oracle.routing_load(np.array(c["topk_idx"], np.int32), c["E"])
+        assert st["empty"] == c["empty"], c["note"]
+        assert st["max_over_mean"] == c["max_over_mean"], c["note"]
+
+
+def test_parallel_executor_matches_whole_layer():
+    """tests/oracle_parallel.py (the oracle's per-expert function in worker
+    processes, routing, combine and gate path in the caller) reproduces
+    oracle.forward / oracle.backward to float64 rounding, empty experts
+    included."""
+    import oracle_parallel
+    cfg = tiny(T=40, E=9, k=3, cfg_id=140, router_bias_var=0.5)
+    inp = inputs.generate(cfg, 0)
+    fwd = oracle.forward(inp, cfg.k, cfg.group, cfg.lora_scale, keep=True)
+    bwd = oracle.backward(inp, fwd, cfg.k, cfg.group, cfg.lora_scale)
+    par = oracle_parallel.layer(inp, cfg, backward=True, workers=3)
+    assert np.array_equal(par["topk_idx"], fwd["topk_idx"])
+    assert np.array_equal(par["perm_src"], fwd["perm_src"])
+    for key, ref in (("e_out", fwd["e_out"]), ("y", fwd["y"]), ("dx", bwd["dx"]),
+                     *((n, bwd[n]) for n in oracle.ADAPTER_GRADS)):
+        np.testing.assert_allclose(par[key], ref, rtol=1e-12, atol=1e-14, err_msg=key)
