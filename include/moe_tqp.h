@@ -203,6 +203,27 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
                           moe_qlora down, void *e_out, void *save, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* moe_expert_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and validation
+ * as moe_expert_fwd; its scratch is the library's own fixed device array of
+ * 64 MiB, which every GPU the library runs on holds from module load to
+ * process end (one copy per device, its address looked up on the first call
+ * on that device).  The call allocates and frees nothing.
+ *   - The scratch a call needs is what moe_workspace_size(MOE_CALL_EXPERT_FWD
+ *     | flags) gives for the flags its own arguments imply; above 64 MiB the
+ *     call returns MOE_ERR_WORKSPACE before any HIP call.  With save and the
+ *     forward-packed bases (qf) given it stays a few MB at T = 8192, E = 460;
+ *     with save NULL the intermediates need about S (3 d_ff act + 3 r fp32)
+ *     bytes more, and without qf the ratio tables 12 E d f / 128 bytes more.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other threads) race on it and give
+ *     undefined results.  Calls ordered on one stream are safe.  Nothing in
+ *     the array needs to start at any value. */
+moe_status moe_expert_fwd_noalloc(const moe_dims *dims, const void *x, const int32_t *offsets,
+                                  const int32_t *perm_src, moe_qlora gate, moe_qlora up,
+                                  moe_qlora down, void *e_out, void *save, void *stream);
+
 /* Gate-weighted combine of each token's k expert outputs (the routed mixture
  * of "Reversible Sparse MoE Single Node" skill card, Architecture Details;
  * the order of the sum is this library's, fixed so that results are

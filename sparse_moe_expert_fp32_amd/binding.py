@@ -55,6 +55,7 @@ def _load():
         "moe_route": [DP, P, P, P, P, P, P, P, SZ, P],
         "moe_permute": [DP, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_fwd": [DP, P, P, P, QLora, QLora, QLora, P, P, P, SZ, P],
+        "moe_expert_fwd_noalloc": [DP, P, P, P, QLora, QLora, QLora, P, P, P],
         "moe_combine": [DP, P, P, P, P, P, SZ, P],
         "moe_adapter_bwd": [DP, P, P, P, P, P, P, P, P, QLora, QLora, QLora, P, P, P,
                             P, P, P, P, P, P, P, SZ, P],
@@ -84,7 +85,8 @@ def _load():
 
 
 LIB = _load()
-EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_combine", "moe_adapter_bwd",
+EXPORTS = ("moe_route", "moe_permute", "moe_expert_fwd", "moe_expert_fwd_noalloc", "moe_combine",
+           "moe_adapter_bwd",
            "moe_workspace_size", "moe_save_size", "moe_status_string", "moe_last_error",
            "moe_abi_version", "moe_timer_start", "moe_timer_stop", "moe_adamw_step",
            "moe_pack_base_t_size", "moe_pack_base_t", "moe_pack_base_f_size", "moe_pack_base_f",
@@ -173,6 +175,12 @@ def moe_expert_fwd(dm, x, offsets, perm_src, gate, up, down, e_out, save, ws, st
     _check(LIB.moe_expert_fwd(ctypes.byref(dm), _p(x), _p(offsets), _p(perm_src), gate, up, down,
                               _p(e_out), _p(save), _p(ws), ws.numel() if ws is not None else 0,
                               _stream(stream)), "moe_expert_fwd")
+
+
+def moe_expert_fwd_noalloc(dm, x, offsets, perm_src, gate, up, down, e_out, save, stream=None):
+    _check(LIB.moe_expert_fwd_noalloc(ctypes.byref(dm), _p(x), _p(offsets), _p(perm_src), gate,
+                                      up, down, _p(e_out), _p(save), _stream(stream)),
+           "moe_expert_fwd_noalloc")
 
 
 def moe_combine(dm, e_out, slot_pos, gates, y, ws=None, stream=None):

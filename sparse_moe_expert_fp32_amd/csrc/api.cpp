@@ -528,15 +528,26 @@ moe_status moe_rev_couple(const moe_dims *dims, const void *x, const void *m, vo
   return hip_status("moe_rev_couple");
 }
 
-moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
-                          const int32_t *perm_src, moe_qlora gate, moe_qlora up, moe_qlora down,
-                          void *e_out, void *save, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status check_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
+                            const int32_t *perm_src, const moe_qlora &gate, const moe_qlora &up,
+                            const moe_qlora &down, const void *e_out) {
   TRY(check_dims(dims));
   REQUIRE(x && offsets && perm_src && e_out, "moe_expert_fwd: x, offsets, perm_src, e_out required");
   TRY(check_qlora(gate, "gate"));
   TRY(check_qlora(up, "up"));
   TRY(check_qlora(down, "down"));
-  TRY(check_ws(dims, MOE_CALL_EXPERT_FWD | fwd_flags(save, gate, up, down), ws, ws_bytes));
+  return MOE_OK;
+}
+
+// The kernel sequence of moe_expert_fwd on a validated call; ws holds at
+// least FwdLayout(dims, fwd_flags(...)).total bytes.
+moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *offsets,
+                          const int32_t *perm_src, moe_qlora gate, moe_qlora up, moe_qlora down,
+                          void *e_out, void *save, void *ws, void *stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool bf = dims->act == MOE_BF16;
   const int T = dims->T, d = dims->d_model, E = dims->n_experts, k = dims->top_k, f = dims->d_ff,
@@ -651,6 +662,38 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
   A.out = e_out; A.ldo = d;
   TIMED(MOE_KT_DOWN, st, moe::launch_lin_simple(bf, false, A, st));
   return hip_status("moe_expert_fwd");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
+                          const int32_t *perm_src, moe_qlora gate, moe_qlora up, moe_qlora down,
+                          void *e_out, void *save, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_expert_fwd(dims, x, offsets, perm_src, gate, up, down, e_out));
+  TRY(check_ws(dims, MOE_CALL_EXPERT_FWD | fwd_flags(save, gate, up, down), ws, ws_bytes));
+  return expert_fwd_run(dims, x, offsets, perm_src, gate, up, down, e_out, save, ws, stream);
+}
+
+moe_status moe_expert_fwd_noalloc(const moe_dims *dims, const void *x, const int32_t *offsets,
+                                  const int32_t *perm_src, moe_qlora gate, moe_qlora up,
+                                  moe_qlora down, void *e_out, void *save, void *stream) {
+  TRY(check_expert_fwd(dims, x, offsets, perm_src, gate, up, down, e_out));
+  const size_t need = ws_bytes_for(dims, MOE_CALL_EXPERT_FWD | fwd_flags(save, gate, up, down));
+  if (need > moe::kStaticScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_expert_fwd_noalloc: this call needs " + std::to_string(need) +
+                    " bytes of scratch, more than the fixed " +
+                    std::to_string(moe::kStaticScratchBytes) +
+                    " bytes (pass save and the packed bases, or call moe_expert_fwd with a "
+                    "workspace)");
+  void *ws = nullptr;
+  const hipError_t e = moe::static_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, std::string("moe_expert_fwd_noalloc: hipGetSymbolAddress: ") +
+                                 hipGetErrorString(e));
+  return expert_fwd_run(dims, x, offsets, perm_src, gate, up, down, e_out, save, ws, stream);
 }
 
 moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,

@@ -177,6 +177,12 @@ void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStre
 void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
                            hipStream_t st);
 
+// ---- fixed device scratch (scratch.hip): the per-device address of the
+// library's static scratch array (kStaticScratchBytes), looked up once per
+// device with that device current
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void **ptr);
+
 // ---- adapter optimizer step (adamw.hip)
 struct AdamWArgs {
   size_t n;

@@ -73,6 +73,23 @@ def test_workspace_flags_shrink_and_validate(B):
     assert out.value == 7
 
 
+def test_noalloc_forward_rejects_before_any_hip_call(B):
+    """moe_expert_fwd_noalloc validates like moe_expert_fwd and refuses,
+    with MOE_ERR_WORKSPACE and before touching the GPU, a call whose scratch
+    would exceed its fixed 64 MiB (the 8K shape without a save buffer)."""
+    big = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16")
+    P = 0x10000
+    q = B.QLora(P, P, P, P, None, None)
+    f = B.LIB.moe_expert_fwd_noalloc
+    assert f(ctypes.byref(big), P, P, P, q, q, q, P, None, None) == -3
+    assert "64" in B.LIB.moe_last_error().decode() or "67108864" in B.LIB.moe_last_error().decode()
+    assert f(ctypes.byref(big), None, P, P, q, q, q, P, P, None) == -1
+    bad = B.QLora(P, None, P, P, None, None)
+    assert f(ctypes.byref(big), P, P, P, bad, q, q, P, P, None) == -1
+    need = B.moe_workspace_size(big, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN | B.WS_PACKED_GIVEN)
+    assert need < 64 << 20
+
+
 BAD = [
     (dict(T=0), -1), (dict(E=0), -1), (dict(E=1025), -1), (dict(k=0), -1), (dict(k=9), -1),
     (dict(E=64, k=33), -1), (dict(r=0), -1), (dict(r=33), -1), (dict(group=16), -2),
