@@ -77,6 +77,8 @@ struct Carve {
 size_t act_bytes(const moe_dims *d) { return d->act == MOE_BF16 ? 2 : 4; }
 
 // ---- save buffer: Z [S][3r] f32 | G [S][f] act | U [S][f] act | H [S][f] act
+// (the matrix-core path keeps the SwiGLU backward's multipliers in the G and U
+// regions: U s (1 + G (1 - s)) and G s with s = sigmoid(G), rounded to bf16)
 struct SaveLayout {
   size_t Z, G, U, H, total;
   explicit SaveLayout(const moe_dims *d) {
@@ -577,7 +579,7 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     float *rs_x = at<float>(ws, L.rs_x), *rs_h = at<float>(ws, L.rs_h);
     float *rt_g = at<float>(ws, L.rt_g), *rt_u = at<float>(ws, L.rt_u), *rt_d = at<float>(ws, L.rt_d);
-    moe::launch_class_tiles(offsets, E, tiles_m, ntiles_m, st);
+    moe::launch_class_tiles(offsets, E, moe::mfma_tile_rows() / 32, tiles_m, ntiles_m, st);
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     // per-row start values -136 * (row sum per group) and per-column scale ratios
     moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st);
@@ -747,7 +749,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     const int grid = persistent_grid(moe::mfma_t_blocks_per_cu());
     const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
-    moe::launch_class_tiles(offsets, E, tiles_m, ntiles_m, st);
+    moe::launch_class_tiles(offsets, E, moe::mfma_t_tile_rows() / 32, tiles_m, ntiles_m, st);
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     uint16_t *bt_d = at<uint16_t>(ws, L.bt);
     uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
@@ -809,7 +811,8 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A; M.LT0 = lt_d;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
-    TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
+    const int ncls_t = moe::mfma_t_tile_rows() / 32;
+    TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < ncls_t; ++c) moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
@@ -850,7 +853,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
     X.out = (uint16_t *)dXp; X.ldo = d;
-    TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < ncls_t; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
     // gate gradient and the per-token sum of dX_perm, one pass per token
     TIMED(MOE_KT_GATE_GRAD, st, {
       if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, E, dx,

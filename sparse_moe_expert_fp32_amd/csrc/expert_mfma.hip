@@ -558,7 +558,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
     // consecutive columns ocol[nf] .. + 3; each becomes one 8-byte store.
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // trailing (clamped) stage loads
     if (MODE == 0) {
-      // H = silu(G) U (and G, U when saved); the row sums of H over this
+      // H = silu(G) U (and, when saved, the SwiGLU backward's multipliers
+      // U s (1 + G (1 - s)) and G s, s = sigmoid(G)); the row sums of H over this
       // item's 128 columns (one quantization group of the down product) are
       // reduced over lane groups by shuffles and over the waves through LDS,
       // and stored as the down product's start values -136 * sum.
@@ -571,20 +572,30 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
 #pragma unroll
         for (int nf = 0; nf < NF / 2; ++nf) {
           const f32x4_t g = acc[m][nf], u = acc[m][nf + NF / 2];
+          float sg[4], sl[4];   // sigmoid(G), silu(G)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sg[i] = sigmoid_rcp(g[i]);
+            sl[i] = g[i] * sg[i];
+          }
           u32x2_t h;
-          h.x = cvt_pk_bf16(silu_rcp(g[0]) * u[0], silu_rcp(g[1]) * u[1]);
-          h.y = cvt_pk_bf16(silu_rcp(g[2]) * u[2], silu_rcp(g[3]) * u[3]);
+          h.x = cvt_pk_bf16(sl[0] * u[0], sl[1] * u[1]);
+          h.y = cvt_pk_bf16(sl[2] * u[2], sl[3] * u[3]);
           hs += (__uint_as_float(h.x << 16) + __uint_as_float(h.x & 0xFFFF0000u)) +
                 (__uint_as_float(h.y << 16) + __uint_as_float(h.y & 0xFFFF0000u));
           if (r < rows) {
             const size_t o = (size_t)(p0 + r) * A.ldo + ocol[nf];
             *reinterpret_cast<u32x2_t *>(&A.out[o]) = h;
-            if (A.saveG)
+            if (A.saveG) {
+              // the SwiGLU backward's multipliers: dG = dH mG, dU = dH mU
+              float mg[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mg[i] = u[i] * sg[i] * __builtin_fmaf(g[i], 1.f - sg[i], 1.f);
               *reinterpret_cast<u32x2_t *>(&A.saveG[o]) =
-                  u32x2_t{cvt_pk_bf16(g[0], g[1]), cvt_pk_bf16(g[2], g[3])};
-            if (A.saveU)
+                  u32x2_t{cvt_pk_bf16(mg[0], mg[1]), cvt_pk_bf16(mg[2], mg[3])};
               *reinterpret_cast<u32x2_t *>(&A.saveU[o]) =
-                  u32x2_t{cvt_pk_bf16(u[0], u[1]), cvt_pk_bf16(u[2], u[3])};
+                  u32x2_t{cvt_pk_bf16(sl[0], sl[1]), cvt_pk_bf16(sl[2], sl[3])};
+            }
           }
         }
         hs += __shfl_xor(hs, 16);
@@ -639,23 +650,25 @@ void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStre
 }
 
 // ------------------------------------------------------------ tile classes --
-// The work list of the grouped GEMMs: each expert's rows in tiles of 128,
-// the last (partial) one rounded up to 32, 64, 96 or 128 rows.  tiles holds
-// the 128-row class first, then 96, 64, 32 (each in expert order); cnt[c] and
-// cnt[4 + c] are the count and first index of class c (c = 0: 128 rows ..
-// c = 3: 32 rows).  One 1024-thread block (E <= 1024).
+// The work list of the grouped GEMMs: each expert's rows in tiles of 32 NC
+// rows, the last (partial) one rounded up to a multiple of 32.  Class c
+// (0 .. NC-1) holds the tiles of 32 (NC - c) rows: tiles lists class 0 first,
+// then 1, ... (each in expert order); cnt[c] and cnt[4 + c] are the count and
+// first index of class c (NC <= 4).  One 1024-thread block (E <= 1024).
 __global__ __launch_bounds__(1024) void build_class_tiles_kernel(const int32_t *__restrict__ offsets,
-                                                                 int E, int2 *__restrict__ tiles,
+                                                                 int E, int NC,
+                                                                 int2 *__restrict__ tiles,
                                                                  int *__restrict__ cnt) {
   __shared__ int sc[4][1024];
   const int e = threadIdx.x;
+  const int BM = 32 * NC;
   int lo = 0, n = 0;
   if (e < E) {
     lo = offsets[e];
     n = offsets[e + 1] - lo;
   }
-  const int nfull = n >> 7, tail = n & 127;
-  const int tcls = tail == 0 ? -1 : 3 - ((tail - 1) >> 5);   // 97..127 -> 0, 1..32 -> 3
+  const int nfull = n / BM, tail = n - nfull * BM;
+  const int tcls = tail == 0 ? -1 : NC - 1 - ((tail - 1) >> 5);   // 1..32 rows -> NC - 1
   int c[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) c[k] = (k == 0 ? nfull : 0) + (tcls == k ? 1 : 0);
@@ -677,12 +690,12 @@ __global__ __launch_bounds__(1024) void build_class_tiles_kernel(const int32_t *
     start[k] = s;
     s += sc[k][1023];
   }
-  // class 0: the full tiles, then a 97..127-row tail
+  // class 0: the full tiles, then a tail of the full class's size
   int pos = start[0] + sc[0][e] - c[0];
-  for (int i = 0; i < c[0]; ++i) tiles[pos + i] = make_int2(e, lo + 128 * i);
+  for (int i = 0; i < c[0]; ++i) tiles[pos + i] = make_int2(e, lo + BM * i);
 #pragma unroll
   for (int k = 1; k < 4; ++k)
-    if (c[k]) tiles[start[k] + sc[k][e] - 1] = make_int2(e, lo + 128 * nfull);
+    if (c[k]) tiles[start[k] + sc[k][e] - 1] = make_int2(e, lo + BM * nfull);
   if (e == 0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -707,8 +720,9 @@ void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipS
   scale_ratio_kernel<<<grid, 256, 0, st>>>(s, E, N, ng, rt);
 }
 
-void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st) {
-  build_class_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, tiles, cnt);
+void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, int *cnt,
+                        hipStream_t st) {
+  build_class_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, nclass, tiles, cnt);
 }
 
 // The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32); cnt as

@@ -6,6 +6,8 @@
 // transpose):
 //   mode 0:  dH = dO W_d + dZ_d A_d, then the SwiGLU backward
 //            dG = dH U s (1 + G (1 - s)), dU = dH G s, s = sigmoid(G)
+//            (the two multipliers of dH come from the forward, which has
+//            s at hand: the epilogue is two products per element)
 //   mode 1:  dX_perm = dG W_g + dU W_u + dZ_g A_g + dZ_u A_u
 // (dZ = lam dOut B of the same matrix, computed beforehand).  The output
 // gradient of a permuted row p is its gate times the upstream gradient of its
@@ -173,12 +175,15 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
       const int arow = tokrows ? A.perm_src[p] / A.kk : p;
       aoff[i] = (uint32_t)arow * (uint32_t)(A.lda * 2) + c * 16;
     }
-    // int4 staging: wave w, load i covers columns 32 (2w + i) .. +31, 32 bytes each
+    // int4 staging: wave w, load i covers columns 32 (2w + i) .. +31, 32 bytes
+    // each; the two 16-byte halves of a column trade places when bit 3 of its
+    // block column (bit 4 of the lane) is set, so that the 8-byte reads of 16
+    // consecutive columns by half a wave touch every bank once
     uint32_t boff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int col = min(c0 + 32 * (2 * w + i) + (lane >> 1), N - 1);
-      boff[i] = (uint32_t)col * 32 + 16 * (lane & 1);
+      boff[i] = (uint32_t)col * 32 + 16 * ((lane & 1) ^ ((lane >> 4) & 1));
     }
     // scale staging: wave w, lanes < 32: column group (w >> 1), k 32 (w & 1) + lane
     const int sg = min(c0 / 128 + (w >> 1), G - 1);
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
     // per-lane LDS read bases (bytes); the rest of every read address is a
     // compile-time constant
     const uint32_t offA0 = opaque(ldsA + (16 * NMH * wm + lr) * 128 + (((2 * lg) ^ row_swz(lr)) << 4)),
-                   offB = opaque(ldsB + (128 * wn + lr) * 32 + 8 * lg),
+                   offB = opaque(ldsB + (128 * wn + lr) * 32 + 16 * ((lg >> 1) ^ (lr >> 3)) + 8 * (lg & 1)),
                    offS = opaque(ldsS + (wn * GT_KS + 16 * lg) * 4);
 
     // the row gates (mode 0, rows of dy by token), fetched now for the epilogue
@@ -224,30 +229,43 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int col = min(c0 + 32 * (2 * w + i) + (lane >> 1), N - 1);
-        dma16(lb16, (uint32_t)col * 32u + 16 * (lane & 1), sb + slot * TS_B + i * 1024);
+        dma16(lb16, (uint32_t)col * 32u + 16 * ((lane & 1) ^ ((lane >> 4) & 1)), sb + slot * TS_B + i * 1024);
       }
     };
+    // The epilogue stages (EPL) are issued whole at the start of their step.
     auto stage = [&](int jr, int slot) {
       if (EPL && jr >= NK) {
         if (jr == NK) stage_ep(0, slot);
         else if (MODE == 1 && jr == NK + 1) stage_ep(1, slot);
-        return;
       }
-      const int j = min(jr, NK - 1);   // past the end: a harmless copy of the last step
+    };
+    // A reduction stage j (< NK) is NOPS single transfers (the A rows, the
+    // int4 words, the scales), which the step computing the stage two before
+    // it issues one at a time between its matrix instructions, so that a
+    // wave never stalls on a full load queue with its matrix work waiting.
+    constexpr int NOPS = AOPS + 3;
+    static_assert(NOPS <= 8, "one transfer per column fragment of a substep");
+    struct StageSrc {
+      const char *a;
+      const uint8_t *q;
+      const float *s;
+    };
+    auto stage_src = [&](int j) {
       const bool second = MODE == 1 && j >= NKh;
       const int kj = second ? j - NKh : j;
-      const char *abase = reinterpret_cast<const char *>(second ? A.a1 : A.a0);
-      const uint32_t koff = (uint32_t)kj * GT_KS * 2;
-      // destinations re-derived per stage (scalar adds) rather than held
+      StageSrc r;
+      r.a = reinterpret_cast<const char *>(second ? A.a1 : A.a0) + (size_t)kj * GT_KS * 2;
+      r.q = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
+      r.s = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
+      return r;
+    };
+    auto stage_op = [&](int op, const StageSrc &src, int slot) {
+      // destinations re-derived per transfer (scalar adds) rather than held
       uint32_t sa = la, sb = lb, ss = ls;
       asm volatile("" : "+s"(sa), "+s"(sb), "+s"(ss));
-#pragma unroll
-      for (int i = 0; i < AOPS; ++i) dma16(abase + koff, aoff[i], sa + slot * TS_A + i * 1024);
-      const uint8_t *qb = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(qb, boff[i], sb + slot * TS_B + i * 1024);
-      const float *sp = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
-      if (lane < 32) dma4(sp, soff, ss + slot * TS_S);
+      if (op < AOPS) dma16(src.a, aoff[op], sa + slot * TS_A + op * 1024);
+      else if (op < AOPS + 2) dma16(src.q, boff[op - AOPS], sb + slot * TS_B + (op - AOPS) * 1024);
+      else if (lane < 32) dma4(src.s, soff, ss + slot * TS_S);
     };
 
     f32x4_t acc[NMH][8], corr[NMH];
@@ -261,8 +279,10 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
     // one 64-deep step: 2 k-substeps x NMH row fragments x (8 + 1) MFMAs.
     // Lane group lg takes k = 16 lg + 8 s .. + 7 in substep s (A chunk
     // 2 lg + s, int4 word 2 lg + s), the same permutation on both operands.
-    auto compute = [&](int slot) {
+    auto compute = [&](int slot, int jl, int nslot) {   // jl: the stage to load into nslot, or -1
       __builtin_amdgcn_sched_barrier(0);
+      const bool ld = jl >= 0;
+      const StageSrc src = stage_src(ld ? jl : 0);
       u32x2_t bw[8];
 #pragma unroll
       for (int nf = 0; nf < 8; ++nf) bw[nf] = lds_ld<u32x2_t>(offB + slot * TS_B + nf * 16 * 32);
@@ -294,30 +314,39 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
           bu.w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
 #pragma unroll
           for (int m = 0; m < NMH; ++m) acc[m][nf] = mfma32(bu, av[m], acc[m][nf]);
+          if (s == 0 && nf < NOPS && ld) stage_op(nf, src, nslot);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // 3-deep ring: step j computes from slot j % 3 while the loads of step
-    // j + 2 (issued at the start of the step) are in flight; at the end of the
-    // step every wave waits for all of its loads and the block syncs.  The
-    // loop runs in groups of three steps; steps past the end compute nothing
-    // (uniform branch) but still issue their loads, clamped to the last real
-    // step.
+    // 3-deep ring: step j computes from slot j % 3 and, between its matrix
+    // instructions, issues the loads of stage j + 2 into slot (j + 2) % 3; at
+    // the end of the step every wave waits for all of its loads and the block
+    // syncs.  The loop runs in groups of three steps; steps past the end
+    // compute nothing and load nothing (uniform branches).
     __syncthreads();  // LDS of the previous item is free
-    stage(0, 0);
-    stage(1, 1);
+    {
+      const StageSrc s0 = stage_src(0), s1 = stage_src(min(1, NK - 1));
+#pragma unroll
+      for (int op = 0; op < NOPS; ++op) stage_op(op, s0, 0);
+      if (NK > 1) {
+#pragma unroll
+        for (int op = 0; op < NOPS; ++op) stage_op(op, s1, 1);
+      } else {
+        stage(1, 1);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     block_barrier();
     for (int j = 0; j < NK; j += 3) {
-#define MOE_T_STEP(JJ, CUR, NXT)                 \
-  {                                              \
-    const int jj = (JJ);                         \
-    stage(jj + 2, NXT);                          \
-    if (jj < NK) compute(CUR);                   \
-    __builtin_amdgcn_s_waitcnt(kWaitVm); \
-    block_barrier();                             \
+#define MOE_T_STEP(JJ, CUR, NXT)                             \
+  {                                                          \
+    const int jj = (JJ), jl = jj + 2;                        \
+    stage(jl, NXT);                                          \
+    if (jj < NK) compute(CUR, jl < NK ? jl : -1, NXT);       \
+    __builtin_amdgcn_s_waitcnt(kWaitVm);                     \
+    block_barrier();                                         \
   }
       MOE_T_STEP(j, 0, 2)
       MOE_T_STEP(j + 1, 1, 0)
@@ -355,7 +384,8 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
         short4_t lv[8];
 #pragma unroll
         for (int nf = 0; nf < 8; ++nf)
-          lv[nf] = lds_ld<short4_t>(ldsB + ls * TS_B + (128 * wn2 + 16 * nf + lr2) * 32 + 8 * lg2);
+          lv[nf] = lds_ld<short4_t>(ldsB + ls * TS_B + (128 * wn2 + 16 * nf + lr2) * 32 +
+                                    16 * ((lg2 >> 1) ^ (lr2 >> 3)) + 8 * (lg2 & 1));
 #pragma unroll
         for (int m = 0; m < NMH; ++m) {
           const int r = rbase + 16 * m;
@@ -410,19 +440,20 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
         const int c = ocol + 16 * nf;
         const f32x4_t a = acc[m][nf];
         if (MODE == 0) {
+          // the forward saved the SwiGLU backward's multipliers
+          // mG = U s (1 + G (1 - s)) and mU = G s
           const size_t o = p * N + c;
           const u32x2_t gw = *reinterpret_cast<const u32x2_t *>(&A.G[o]);
           const u32x2_t uw = *reinterpret_cast<const u32x2_t *>(&A.U[o]);
-          const float gv[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
+          const float mg[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
                                __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xffff0000u)};
-          const float uv[4] = {__uint_as_float(uw.x << 16), __uint_as_float(uw.x & 0xffff0000u),
+          const float mu[4] = {__uint_as_float(uw.x << 16), __uint_as_float(uw.x & 0xffff0000u),
                                __uint_as_float(uw.y << 16), __uint_as_float(uw.y & 0xffff0000u)};
           float dg[4], du[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float sgm = sigmoid_rcp(gv[i]);
-            dg[i] = a[i] * uv[i] * sgm * (1.f + gv[i] * (1.f - sgm));
-            du[i] = a[i] * gv[i] * sgm;
+            dg[i] = a[i] * mg[i];
+            du[i] = a[i] * mu[i];
           }
           *reinterpret_cast<u32x2_t *>(&A.dG[o]) = u32x2_t{cvt_pk_bf16(dg[0], dg[1]), cvt_pk_bf16(dg[2], dg[3])};
           *reinterpret_cast<u32x2_t *>(&A.dU[o]) = u32x2_t{cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};

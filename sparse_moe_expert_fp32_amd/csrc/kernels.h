@@ -99,7 +99,7 @@ struct MfmaGemmArgs {
   // mode 0, whose 128-row kernel needs more registers with it)
   const uint8_t *qp0, *qp1;
   uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
-  uint16_t *saveG, *saveU;                // mode 0, optional
+  uint16_t *saveG, *saveU;                // mode 0, optional: U s (1 + G (1 - s)), G s (s = sigmoid G)
   float *rsum_out; int ld_rsum_out;       // mode 0: -136 * group sums of H rows
 };
 int mfma_tile_rows();
@@ -109,10 +109,12 @@ void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, flo
 // scale ratios of a quantized matrix ([E][N][ng] bf16 -> [E][ng][N] f32):
 // rt[e][g][c] = s[e][c][g-1] / s[e][c][g] for g >= 1, rt[e][0][c] = s[e][c][ng-1]
 void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st);
-// expert tiles of 128 rows, the partial last one of each expert rounded up to
-// 32, 64, 96 or 128 rows, grouped by that class; cnt[8]: count and first
-// index of each class (128-row class first)
-void launch_class_tiles(const int32_t *offsets, int E, int2 *tiles, int *cnt, hipStream_t st);
+// expert tiles of 32 nclass rows (nclass <= 4), the partial last one of each
+// expert rounded up to a multiple of 32, grouped by that class (class c:
+// 32 (nclass - c) rows); cnt[8]: count and first index of each class
+// (the full-size class first)
+void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, int *cnt,
+                        hipStream_t st);
 // int4 [E][N][K/2] -> stage-major [E][K/64][N][32 B] (K a multiple of 64)
 void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st);
 // the launch of tile class cls (0: 128-row tiles .. 3: 32-row tiles)
@@ -132,10 +134,10 @@ struct MfmaGemmTArgs {
   const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
   const uint16_t *L0, *L1;                // adapter A of the matrix, [E][r][N]
   const uint16_t *LT0, *LT1;              // the same transposed, [E][N][r] (rank 16; or null)
-  const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: SwiGLU backward, [S][N]
+  const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: dG = dH G, dU = dH U ([S][N]; G, U the saved multipliers)
   uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
 };
-int mfma_t_tile_rows();
+int mfma_t_tile_rows();         // rows of a full tile (a multiple of 32)
 int mfma_t_tile_cols();
 int mfma_t_blocks_per_cu();   // resident blocks per CU the kernel is built for
 // int4 [E][R][C/2] + scales [E][R][C/128] -> transposed int4 [E][C][R/2] + scales

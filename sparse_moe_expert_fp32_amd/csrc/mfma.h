@@ -114,8 +114,13 @@ DEV const void *uniform_ptr(const void *p) {
   return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 // lds: wave-uniform LDS byte address where lane i's data lands (+ size * i).
-// Each transfer sets M0 itself and declares it clobbered, so the compiler
-// keeps none of its own values in M0 across these statements.
+// Each transfer sets M0 itself and declares it clobbered: the statement is
+// then recorded as defining M0, so the compiler re-initialises M0 before any
+// later instruction of its own that reads it.  (The compiler warns that a
+// reserved register in a clobber list is not saved and restored around the
+// statement; nothing here needs it restored, so that warning is silenced.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 DEV void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
@@ -128,6 +133,7 @@ DEV void dma2(const void *sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8).  vmcnt_imm(n): at most n vector memory operations
