@@ -13,7 +13,8 @@ int4 expert-GEMM stages per step (each stage is four launches, one per tile
 class, timed as one span with HIP events on the launch stream) against the
 bf16 matrix-core peak; `stages` lists all four.  `decode` measures the
 T=64 forward (the weight-streaming shape) against HBM bandwidth, with the
-device caches scrubbed before every timed forward.  `cpu_baseline` times the
+device caches scrubbed before every timed forward; `decode_int8` the same
+with an int8 base (twice the weight bytes).  `cpu_baseline` times the
 fp64 oracle on a bounded sample of the workload on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -145,15 +146,15 @@ def cpu_baseline(cfg, inp, target_s: float, gpu_idx=None):
     return rec, routing
 
 
-def decode_hbm(args, B, DeviceLayer, to_numpy):
+def decode_hbm(args, B, DeviceLayer, to_numpy, bits=4):
     """The T=64 decode shape (E=460, top-12, unbiased router): forward only,
     each timed forward preceded (outside its events) by a write of 1 GiB,
     four times the 256 MB last-level cache, so the expert weights stream from
-    HBM.  Bytes are algorithmic: the int4 base, bf16 group scales and
-    adapters of the experts the seeded routing touches, plus the router, x
-    and y."""
+    HBM.  Bytes are algorithmic: the int4 (or int8) base, bf16 group scales
+    and adapters of the experts the seeded routing touches, plus the router,
+    x and y."""
     import torch
-    cfg = configs.C4
+    cfg = configs.C4 if bits == 4 else configs.C4.with_(name=configs.C4.name + "_int8", bits=8)
     inp = inputs.generate(cfg, args.seed)
     L = DeviceLayer(cfg, inp, device="cuda:0", with_backward=False)
     stream = torch.cuda.current_stream()
@@ -181,12 +182,12 @@ def decode_hbm(args, B, DeviceLayer, to_numpy):
     counts = to_numpy(L.counts)
     touched = int((counts > 0).sum())
     d, f, r, g = cfg.d, cfg.f, cfg.r, cfg.group
-    per_expert = 3 * d * f // 2 + 3 * (d * f // g) * 2 + 3 * r * (d + f) * 2
+    per_expert = 3 * d * f * bits // 8 + 3 * (d * f // g) * 2 + 3 * r * (d + f) * 2
     nbytes = touched * per_expert + d * cfg.E * 4 + 2 * cfg.T * d * 2
     med = cold[len(cold) // 2]
     del scrub, L
     return {"workload": f"{cfg.name} forward (T={cfg.T}, E={cfg.E}, top-{cfg.k}, "
-                        "unbiased router)",
+                        f"unbiased router, int{bits} base)",
             "ms": med, "ms_p10": cold[len(cold) // 10], "ms_p90": cold[(9 * len(cold)) // 10],
             "ms_warm_cache": warm, "tokens_per_s": cfg.T / (med / 1e3),
             "experts_touched": touched, "bytes": nbytes, "bytes_per_expert": per_expert,
@@ -336,12 +337,17 @@ def main():
     traffic = measured_traffic(dom["stage"])
     counts = to_numpy(L.counts)
     gpu_idx = to_numpy(L.topk_idx)
-    decode = None
+    decode = decode8 = None
     if not args.no_decode:
-        t0 = time.perf_counter()
-        decode = decode_hbm(args, B, DeviceLayer, to_numpy)
-        log(f"decode T=64: {decode['ms']:.3f} ms, {decode['GB_s']:.0f} GB/s = "
-            f"{decode['frac_hbm']:.3f} of HBM ({time.perf_counter() - t0:.1f} s)")
+        for bits in (4, 8):
+            t0 = time.perf_counter()
+            dec = decode_hbm(args, B, DeviceLayer, to_numpy, bits)
+            log(f"decode T=64 int{bits}: {dec['ms']:.3f} ms, {dec['GB_s']:.0f} GB/s = "
+                f"{dec['frac_hbm']:.3f} of HBM ({time.perf_counter() - t0:.1f} s)")
+            if bits == 4:
+                decode = dec
+            else:
+                decode8 = dec
     rec = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -369,6 +375,7 @@ def main():
                      "flops_per_launch": dom["flops"]},
         "stages": stages,
         "decode": decode,
+        "decode_int8": decode8,
         "layer_tflops": layer_flops(cfg, cfg.train) / (ms / 1e3) / 1e12,
         "layer_frac_of_bf16_peak": layer_flops(cfg, cfg.train) / (ms / 1e3) / PEAK_BF16,
         "forward_ms": fwd_ms,

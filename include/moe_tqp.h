@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -69,19 +69,26 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Layer dimensions.  Limits: T >= 1, 1 <= k <= min(E, 32), E <= 1024,
  * group in {32, 64, 128}, d % group == 0, f % group == 0, 1 <= r <= 32,
- * S = T*k <= 2^26, d, f <= 65536. */
+ * S = T*k <= 2^26, d, f <= 65536, base_bits in {0, 4, 8}. */
 typedef struct {
   int32_t T, d_model, n_experts, top_k, d_ff, rank, group;
   int32_t act;        /* moe_dtype */
   float lora_scale;   /* lambda in W_eff = W_hat + lambda * A B; finite */
+  int32_t base_bits;  /* storage of the frozen base: 4 (int4; 0 also means 4)
+                         or 8 (int8), the "Int8 or Int4" of the skill card
+                         "Reversible Sparse MoE Single Node", Implementation
+                         Considerations, TQP Quantization */
 } moe_dims;
 
-/* One expert matrix W[N][K] (out x in) for all E experts, frozen int4 base
- * plus adapter.  For gate and up N = f, K = d; for down N = d, K = f.
- *   q     uint8 [E][N][K/2]: symmetric int4, two's-complement nibbles.  Each
- *         aligned little-endian 32-bit word holds one 8-wide block k0..k7 of
- *         K; nibble slot j (bits 4j..4j+3) holds k_{2j} for j < 4 and
- *         k_{2(j-4)+1} for j >= 4.
+/* One expert matrix W[N][K] (out x in) for all E experts, frozen int4 (or
+ * int8) base plus adapter.  For gate and up N = f, K = d; for down N = d,
+ * K = f.
+ *   q     base_bits 4: uint8 [E][N][K/2], symmetric int4, two's-complement
+ *         nibbles.  Each aligned little-endian 32-bit word holds one 8-wide
+ *         block k0..k7 of K; nibble slot j (bits 4j..4j+3) holds k_{2j} for
+ *         j < 4 and k_{2(j-4)+1} for j >= 4.
+ *         base_bits 8: uint8 [E][N][K], one two's-complement byte per value
+ *         in k order.
  *   scale bf16  [E][N][K/g]: W_hat[n][c] = scale[n][c/g] * q[n][c].
  *   A     act   [E][r][K]   (out x in, like the base)
  *   B     act   [E][N][r]
@@ -181,8 +188,8 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
  * card, Principle 3 "TQP Optimizer Strategy": base expert weights quantized
  * and fixed, low-rank adapters on top; Implementation Considerations, TQP
  * Quantization: "Int8 or Int4" base, full-precision adapters; Related
- * Methods: LoRA).  The SwiGLU form, the int4 format and the adapter placement
- * on all three matrices are this library's readings.  The rows are read from
+ * Methods: LoRA).  The SwiGLU form, the int4 and int8 formats and the
+ * adapter placement on all three matrices are this library's readings.  The rows are read from
  * x by token through perm_src (no x_perm argument: x is small enough to stay
  * in cache, which saves writing and reading the permuted copy).
  * For every position p with expert e
@@ -197,7 +204,7 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
  *   offsets, perm_src as written by moe_permute (device)
  *   e_out    act [S][d] in permuted order (out)
  *   save     NULL, or moe_save_size() bytes that moe_adapter_bwd consumes
- *            (opaque: pre-activations and adapter projections) (out) */
+ *            (opaque: the intermediates the backward needs) (out) */
 moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
                           const int32_t *perm_src, moe_qlora gate, moe_qlora up,
                           moe_qlora down, void *e_out, void *save, void *ws,
@@ -290,7 +297,10 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
  * rows N of the base, so their int4 operand must be packed along N: for
  * every expert e, block of 64 storage rows n0 and column c, 32 bytes hold
  * q[e][n0 .. n0+63][c] in the word order of the forward layout, and the
- * scales follow as float32 [E][K/128][N] (K of the matrix).  The backward
+ * scales follow as float32 [E][K/128][N] (K of the matrix).  An int8 base
+ * (q = 16 h + l, h = q >> 4, l = q & 15) is packed as two int4 planes
+ * stacked along N: 2N rows, the first N holding h with scales 16 s, the next
+ * N holding l - 8 with scales s (twice the int4 size).  The backward
  * products are those of moe_adapter_bwd (skill card "Reversible Sparse MoE
  * Single Node", Principle 3: the base is frozen, only the adapters train).
  *   matrix  MOE_MAT_GATE_UP (q [E][f][d/2], scale [E][f][d/128]) or
@@ -310,7 +320,10 @@ moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *
  * each step reading 32 bytes of every output column; packed, one step of
  * one expert is a contiguous run: for every expert e, block of 64 columns of
  * K k0 and storage row n, 32 bytes hold q[e][n][k0/2 .. k0/2+31] unchanged
- * (layout [E][K/64][N][32 B], the byte count of q).  The float32 table of
+ * (layout [E][K/64][N][32 B], the byte count of q).  An int8 base is packed
+ * as two int4 planes along K (2K columns: h = q >> 4, then l - 8 with
+ * l = q & 15, in the int4 word order), with the plane scales 16 s and s in
+ * the ratio table below (2 K/128 groups); the byte count of q again.  The float32 table of
  * group-scale ratios the forward applies follows, [E][K/128][N]: entry g >= 1
  * of column n is s'[n][g-1] / s'[n][g] and entry 0 is s'[n][K/128-1], where
  * s' is the bf16 scale with magnitudes below the column's floor raised to

@@ -22,7 +22,7 @@ What is computed (cited by page title and section):
   * Same card, Related Methods: LoRA, i.e. the adapter product of a row with
     two low-rank factors; stored out x in here (A [r, K], B [N, r]).
 Readings where the pages are silent (each is listed with its reason in the
-design notes of the repository): symmetric int4 with bf16 group scales; top-k
+design notes of the repository): symmetric int4 (or int8) with bf16 group scales; top-k
 over the logits with ties to the lower expert index; gates = softmax over the
 selected logits (= softmax over all experts renormalised over the selected);
 dropless routing; SwiGLU experts without biases, silu(z) = z / (1 + e^-z);
@@ -31,8 +31,8 @@ held constant in the backward and the router receives no weight gradient but
 does pass gradient to x through the gates.
 
 Everything is evaluated in float64 from the exact stored inputs: bf16 bit
-patterns and float32 values convert to float64 exactly, int4 nibbles become
-integers and bf16 scales become float64.  Parity pins for every function are
+patterns and float32 values convert to float64 exactly, int4 nibbles and
+int8 bytes become integers and bf16 scales become float64.  Parity pins for every function are
 in tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -72,9 +72,26 @@ def unpack_int4(q_packed: np.ndarray) -> np.ndarray:
     return out.reshape(lead + (word.shape[-1] * 8,))
 
 
+def unpack_int8(q_bytes: np.ndarray) -> np.ndarray:
+    """uint8 [..., K] -> int64 [..., K]: each byte is one two's-complement
+    value, in k order."""
+    return np.ascontiguousarray(q_bytes, dtype=np.uint8).view(np.int8).astype(np.int64)
+
+
 def dequantize(q_packed: np.ndarray, scale_bits: np.ndarray, group: int) -> np.ndarray:
-    """W_hat[n, c] = s[n, c // group] * q[n, c]  (float64, exact)."""
-    q = unpack_int4(q_packed)
+    """W_hat[n, c] = s[n, c // group] * q[n, c]  (float64, exact).
+
+    The storage width follows from the shapes: with K = (scale columns) *
+    group, q holds K bytes per row for int8 and K/2 for int4 ("Int8 or Int4",
+    skill card "Reversible Sparse MoE Single Node", Implementation
+    Considerations, TQP Quantization)."""
+    K = scale_bits.shape[-1] * group
+    if q_packed.shape[-1] == K:
+        q = unpack_int8(q_packed)
+    elif 2 * q_packed.shape[-1] == K:
+        q = unpack_int4(q_packed)
+    else:
+        raise ValueError("q holds neither K int8 nor K/2 int4 bytes per row")
     s = to_f64(scale_bits)
     return q * np.repeat(s, group, axis=-1)
 

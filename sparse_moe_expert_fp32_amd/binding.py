@@ -29,7 +29,7 @@ class Dims(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("lora_scale", ctypes.c_float)]
+                ("lora_scale", ctypes.c_float), ("base_bits", ctypes.c_int32)]
 
 
 class QLora(ctypes.Structure):
@@ -119,14 +119,14 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def dims(T, d, E, k, f, r, group, act, lora_scale=1.0) -> Dims:
+def dims(T, d, E, k, f, r, group, act, lora_scale=1.0, bits=4) -> Dims:
     a = {"f32": MOE_F32, "bf16": MOE_BF16}.get(act, act)
-    return Dims(T, d, E, k, f, r, group, a, lora_scale)
+    return Dims(T, d, E, k, f, r, group, a, lora_scale, bits)
 
 
 def dims_of(cfg, T: int | None = None) -> Dims:
     return dims(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.r, cfg.group,
-                cfg.act, cfg.lora_scale)
+                cfg.act, cfg.lora_scale, getattr(cfg, "bits", 4))
 
 
 def qlora(q, scale, A, B, qt=None, qf=None) -> QLora:

@@ -25,6 +25,7 @@ class LayerConfig:
     router_bias_var: float = 0.0   # 0 => no router bias
     lora_scale: float = 1.0
     train: bool = False  # forward + adapter-only backward
+    bits: int = 4        # base storage: 4 (int4) or 8 (int8)
 
     @property
     def S(self) -> int:

@@ -43,8 +43,16 @@ moe_status check_dims(const moe_dims *d) {
     return fail(MOE_ERR_UNSUPPORTED, "group must be 32, 64 or 128");
   REQUIRE(d->d_model % d->group == 0, "d_model must be a multiple of group");
   REQUIRE(d->d_ff % d->group == 0, "d_ff must be a multiple of group");
+  if (d->base_bits != 0 && d->base_bits != 4 && d->base_bits != 8)
+    return fail(MOE_ERR_UNSUPPORTED, "base_bits must be 4 or 8 (0 means 4)");
   return MOE_OK;
 }
+
+// storage width of the frozen base: 4 (int4) or 8 (int8)
+int base_bits(const moe_dims *d) { return d->base_bits == 8 ? 8 : 4; }
+// the matrix-core path treats an int8 base as two int4 planes: twice the
+// reduction of an int4 base (forward: along K; backward: along N)
+int plane_mult(const moe_dims *d) { return base_bits(d) / 4; }
 
 moe_status check_qlora(const moe_qlora &m, const char *name) {
   if (!m.q || !m.scale || !m.A || !m.B)
@@ -108,6 +116,16 @@ bool use_mfma(const moe_dims *d) {
 bool ws_save_given(int flags) { return (flags & MOE_WS_SAVE_GIVEN) != 0; }
 bool ws_packed_given(int flags) { return (flags & MOE_WS_PACKED_GIVEN) != 0; }
 
+// one transposed int4 matrix with its f32 scales (d x f or f x d: the same
+// size; an int8 base is two such planes)
+size_t qt_q_bytes(const moe_dims *d) {
+  return (size_t)plane_mult(d) * d->n_experts * d->d_model * d->d_ff / 2;
+}
+size_t qt_slot_bytes(const moe_dims *d) {
+  return qt_q_bytes(d) + (size_t)plane_mult(d) * d->n_experts * d->d_model * d->d_ff / 128 * 4;
+}
+size_t qf_bytes(const moe_dims *d) { return qt_slot_bytes(d); }
+
 // ---- expert forward workspace
 struct FwdLayout {
   size_t tiles, ntiles, save, G32, U32, tiles_m, ntiles_m, tiles_p, ntiles_p, rs_x, rs_h, rt_g,
@@ -125,14 +143,16 @@ struct FwdLayout {
       ntiles_m = c.take(8 * sizeof(int));
       tiles_p = c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2));
       ntiles_p = c.take(sizeof(int));
-      rs_x = c.take((size_t)d->T * (dm / 128) * 4);
-      rs_h = c.take(S * (f / 128) * 4);
+      const size_t pm = plane_mult(d);
+      rs_x = c.take((size_t)d->T * (dm / 128) * 4 * pm);
+      rs_h = c.take(S * (f / 128) * 4 * pm);
       // scale ratios of the three base matrices, [E][N][K/128] f32 (the
-      // forward-packed bases carry their own)
-      const bool pk = ws_packed_given(flags);
-      rt_g = pk ? 0 : c.take(E * f * (dm / 128) * 4);
-      rt_u = pk ? 0 : c.take(E * f * (dm / 128) * 4);
-      rt_d = pk ? 0 : c.take(E * dm * (f / 128) * 4);
+      // forward-packed bases carry their own); an int8 base runs only from
+      // its packed planes, so without the caller's they are packed here
+      const bool pk = ws_packed_given(flags), i8 = base_bits(d) == 8;
+      rt_g = pk ? 0 : c.take(i8 ? qf_bytes(d) : E * f * (dm / 128) * 4);
+      rt_u = pk ? 0 : c.take(i8 ? qf_bytes(d) : E * f * (dm / 128) * 4);
+      rt_d = pk ? 0 : c.take(i8 ? qf_bytes(d) : E * dm * (f / 128) * 4);
     } else {
       G32 = c.take(S * f * 4);
       U32 = c.take(S * f * 4);
@@ -151,12 +171,6 @@ int persistent_grid(int blocks_per_cu = 1) {
       cus < 8)
     cus = 256;
   return (cus * blocks_per_cu) & ~7;
-}
-
-// one transposed int4 matrix with its f32 scales (d x f or f x d: the same size)
-size_t qt_slot_bytes(const moe_dims *d) {
-  const size_t e = d->n_experts, df = (size_t)d->d_model * d->d_ff;
-  return e * df / 2 + e * df / 128 * 4;
 }
 
 // ---- adapter backward workspace
@@ -398,19 +412,19 @@ moe_status moe_pack_base_t(const moe_dims *dims, int32_t matrix, const uint8_t *
   const int E = dims->n_experts, d = dims->d_model, f = dims->d_ff;
   const int R = matrix == MOE_MAT_GATE_UP ? f : d, C = matrix == MOE_MAT_GATE_UP ? d : f;
   uint8_t *qt = (uint8_t *)packed;
-  float *st = reinterpret_cast<float *>(qt + (size_t)E * d * f / 2);
-  moe::launch_transpose_q(q, scale, nullptr, E, R, C, qt, st, (hipStream_t)stream);
+  float *st = reinterpret_cast<float *>(qt + qt_q_bytes(dims));
+  if (base_bits(dims) == 8)
+    moe::launch_transpose_q_int8(q, scale, nullptr, E, R, C, qt, st, (hipStream_t)stream);
+  else
+    moe::launch_transpose_q(q, scale, nullptr, E, R, C, qt, st, (hipStream_t)stream);
   return hip_status("moe_pack_base_t");
 }
 
 // the forward-packed base: int4 words [E][K/64][N][32 B], then the scale
-// ratios [E][K/128][N] f32 (the same sizes for gate/up and down)
-size_t qf_bytes(const moe_dims *d) {
-  const size_t e = d->n_experts, df = (size_t)d->d_model * d->d_ff;
-  return e * df / 2 + e * df / 128 * 4;
-}
+// ratios [E][K/128][N] f32 (the same sizes for gate/up and down; an int8 base
+// is packed as its two int4 planes along K, twice both sizes)
 float *qf_ratios(const moe_dims *d, const void *qf) {
-  return reinterpret_cast<float *>((char *)qf + (size_t)d->n_experts * d->d_model * d->d_ff / 2);
+  return reinterpret_cast<float *>((char *)qf + qt_q_bytes(d));
 }
 
 moe_status moe_pack_base_f_size(const moe_dims *dims, size_t *bytes) {
@@ -439,13 +453,17 @@ moe_status moe_pack_base_f(const moe_dims *dims, int32_t matrix, const uint8_t *
                                        std::to_string(need) + " bytes, got " +
                                        std::to_string(packed_bytes));
   const uintptr_t q0 = (uintptr_t)q, p0 = (uintptr_t)packed;
-  const size_t qsz = (size_t)dims->n_experts * dims->d_model * dims->d_ff / 2;
+  const size_t qsz = (size_t)dims->n_experts * dims->d_model * dims->d_ff * base_bits(dims) / 8;
   REQUIRE(p0 + need <= q0 || q0 + qsz <= p0, "moe_pack_base_f: packed must not overlap q");
   const int d = dims->d_model, f = dims->d_ff;
   const int N = matrix == MOE_MAT_GATE_UP ? f : d, K = matrix == MOE_MAT_GATE_UP ? d : f;
   const int E = dims->n_experts;
-  moe::launch_pack_fwd(q, E, N, K, (uint8_t *)packed, (hipStream_t)stream);
-  moe::launch_scale_ratio(scale, E, N, K / 128, qf_ratios(dims, packed), (hipStream_t)stream);
+  const bool i8 = base_bits(dims) == 8;
+  if (i8)
+    moe::launch_pack_fwd_int8(q, E, N, K, (uint8_t *)packed, (hipStream_t)stream);
+  else
+    moe::launch_pack_fwd(q, E, N, K, (uint8_t *)packed, (hipStream_t)stream);
+  moe::launch_scale_ratio(scale, E, N, K / 128, qf_ratios(dims, packed), (hipStream_t)stream, i8);
   return hip_status("moe_pack_base_f");
 }
 
@@ -581,19 +599,35 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     float *rt_g = at<float>(ws, L.rt_g), *rt_u = at<float>(ws, L.rt_u), *rt_d = at<float>(ws, L.rt_d);
     moe::launch_class_tiles(offsets, E, moe::mfma_tile_rows() / 32, tiles_m, ntiles_m, st);
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
+    // An int8 base runs as its two int4 planes along K (packed here unless the
+    // caller packed it): twice the reduction, the rows read twice, and start
+    // values -136 (first plane) and -128 (second) times the group sums.
+    const bool i8 = base_bits(dims) == 8;
+    const int pm = plane_mult(dims);
     // per-row start values -136 * (row sum per group) and per-column scale ratios
-    moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st);
+    moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st, i8, -128.f);
+    const void *qf_g = gate.qf, *qf_u = up.qf, *qf_d = down.qf;
+    if (i8) {
+      auto pack = [&](const moe_qlora &m, int N, int K, float *buf) {
+        moe::launch_pack_fwd_int8(m.q, E, N, K, (uint8_t *)buf, st);
+        moe::launch_scale_ratio(m.scale, E, N, K / 128, qf_ratios(dims, buf), st, true);
+        return (const void *)buf;
+      };
+      if (!qf_g) qf_g = pack(gate, f, d, rt_g);
+      if (!qf_u) qf_u = pack(up, f, d, rt_u);
+      if (!qf_d) qf_d = pack(down, d, f, rt_d);
+    }
     // (the packed bases carry their ratio tables)
-    const bool pk_gu = gate.qf && up.qf;
+    const bool pk_gu = qf_g && qf_u;
     if (pk_gu) {
-      rt_g = qf_ratios(dims, gate.qf);
-      rt_u = qf_ratios(dims, up.qf);
+      rt_g = qf_ratios(dims, qf_g);
+      rt_u = qf_ratios(dims, qf_u);
     } else {
       moe::launch_scale_ratio(gate.scale, E, f, d / 128, rt_g, st);
       moe::launch_scale_ratio(up.scale, E, f, d / 128, rt_u, st);
     }
-    if (down.qf)
-      rt_d = qf_ratios(dims, down.qf);
+    if (qf_d)
+      rt_d = qf_ratios(dims, qf_d);
     else
       moe::launch_scale_ratio(down.scale, E, d, f / 128, rt_d, st);
     // Z_g = X A_g^T, Z_u = X A_u^T (rows gathered from x)
@@ -605,30 +639,31 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     moe::launch_proj_mfma(Q, mtp, true, st);
     const int grid = persistent_grid(moe::mfma_blocks_per_cu());
     moe::MfmaGemmArgs M{};
-    M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128;
+    M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128 * pm;
     M.tiles = tiles_m; M.offsets = offsets;
-    M.K = d; M.N = f; M.NT = (f + 127) / 128;
-    // the stage-major packed base where both matrices have one
-    M.q0 = gate.q; M.rt0 = rt_g; M.B0 = (const uint16_t *)gate.B;
-    M.q1 = up.q; M.rt1 = rt_u; M.B1 = (const uint16_t *)up.B;
-    M.qp0 = pk_gu ? (const uint8_t *)gate.qf : nullptr;
-    M.qp1 = pk_gu ? (const uint8_t *)up.qf : nullptr;
+    M.K = d * pm; M.ka = d; M.N = f; M.NT = (f + 127) / 128;
+    // the stage-major packed base where both matrices have one (an int8 base
+    // has no plain int4 layout)
+    M.q0 = i8 ? nullptr : gate.q; M.rt0 = rt_g; M.B0 = (const uint16_t *)gate.B;
+    M.q1 = i8 ? nullptr : up.q; M.rt1 = rt_u; M.B1 = (const uint16_t *)up.B;
+    M.qp0 = pk_gu ? (const uint8_t *)qf_g : nullptr;
+    M.qp1 = pk_gu ? (const uint8_t *)qf_u : nullptr;
     M.Z0 = Z; M.Z1 = Z + r; M.ldz = 3 * r; M.r = r; M.lam = lam;
     M.out = (uint16_t *)H; M.ldo = f;
     M.saveG = save ? (uint16_t *)Gs : nullptr;
     M.saveU = save ? (uint16_t *)Us : nullptr;
-    M.rsum_out = rs_h; M.ld_rsum_out = f / 128;
+    M.rsum_out = rs_h; M.ld_rsum_out = f / 128 * pm; M.rsum_split = i8;
     TIMED(MOE_KT_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(0, M, ntiles_m, c, grid, st));
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
     Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
     moe::launch_proj_mfma(Q, mtp, false, st);
     moe::MfmaGemmArgs D{};
-    D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128;
+    D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128 * pm;
     D.tiles = tiles_m; D.offsets = offsets;
-    D.K = f; D.N = d; D.NT = (d + 255) / 256;
-    D.q0 = down.q; D.rt0 = rt_d; D.B0 = (const uint16_t *)down.B;
-    D.qp0 = (const uint8_t *)down.qf;
+    D.K = f * pm; D.ka = f; D.N = d; D.NT = (d + 255) / 256;
+    D.q0 = i8 ? nullptr : down.q; D.rt0 = rt_d; D.B0 = (const uint16_t *)down.B;
+    D.qp0 = (const uint8_t *)qf_d;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
     TIMED(MOE_KT_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));
@@ -646,7 +681,7 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
   moe::LinArgs A{};
   A.a = x; A.lda = d; A.gather = true; A.perm_src = perm_src; A.kk = k;
   A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
-  A.N = f; A.K = d; A.g = g; A.trans = false; A.ldz = 3 * r;
+  A.N = f; A.K = d; A.g = g; A.trans = false; A.bits = base_bits(dims); A.ldz = 3 * r;
   A.l_es = (size_t)f * r; A.l_js = 1; A.l_ns = r; A.r = r; A.lam = lam; A.ldo = f;
   A.acc_out = false;
   A.q = gate.q; A.scale = gate.scale; A.Z = Z; A.lmat = gate.B; A.out = G32;
@@ -767,7 +802,15 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
       moe::launch_transpose_rn(gate.A, E, r, d, lt_g, st);
       moe::launch_transpose_rn(up.A, E, r, d, lt_u, st);
     }
-    const size_t qsz = (size_t)E * d * f / 2, slot = qt_slot_bytes(dims);
+    // An int8 base runs as its two int4 planes stacked along N: twice the
+    // reduction, the rows read twice (transposed here unless the caller packed it)
+    const bool i8 = base_bits(dims) == 8;
+    const int pm = plane_mult(dims);
+    auto transpose = [&](const moe_qlora &m, int R, int C, uint8_t *qt, float *stt) {
+      if (i8) moe::launch_transpose_q_int8(m.q, m.scale, offsets, E, R, C, qt, stt, st);
+      else moe::launch_transpose_q(m.q, m.scale, offsets, E, R, C, qt, stt, st);
+    };
+    const size_t qsz = qt_q_bytes(dims), slot = qt_slot_bytes(dims);
     uint8_t *qt0 = at<uint8_t>(ws, L.wt), *qt1 = qt0 + slot;
     float *st0 = reinterpret_cast<float *>(qt0 + qsz), *st1 = reinterpret_cast<float *>(qt1 + qsz);
     const uint16_t *H16 = (const uint16_t *)H;
@@ -805,9 +848,9 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
       qd = (const uint8_t *)down.qt;
       sd = reinterpret_cast<const float *>(qd + qsz);
     } else {
-      moe::launch_transpose_q(down.q, down.scale, offsets, E, d, f, qt0, st0, st);
+      transpose(down, d, f, qt0, st0);
     }
-    M.K = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qd; M.st0 = sd;
+    M.K = d * pm; M.kr = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qd; M.st0 = sd;
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A; M.LT0 = lt_d;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
@@ -836,19 +879,19 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // dX_perm = dG W_g + dZ_g A_g + dU W_u + dZ_u A_u
     moe::MfmaGemmTArgs X{};
     X.a0 = dG; X.a1 = dU; X.lda = f; X.tiles = tiles_m;
-    X.offsets = offsets; X.K = f; X.N = d; X.NT = (d + 255) / 256;
+    X.offsets = offsets; X.K = f * pm; X.kr = f; X.N = d; X.NT = (d + 255) / 256;
     X.qt0 = qt0; X.st0 = st0; X.qt1 = qt1; X.st1 = st1;
     if (gate.qt) {
       X.qt0 = (const uint8_t *)gate.qt;
       X.st0 = reinterpret_cast<const float *>(X.qt0 + qsz);
     } else {
-      moe::launch_transpose_q(gate.q, gate.scale, offsets, E, f, d, qt0, st0, st);
+      transpose(gate, f, d, qt0, st0);
     }
     if (up.qt) {
       X.qt1 = (const uint8_t *)up.qt;
       X.st1 = reinterpret_cast<const float *>(X.qt1 + qsz);
     } else {
-      moe::launch_transpose_q(up.q, up.scale, offsets, E, f, d, qt1, st1, st);
+      transpose(up, f, d, qt1, st1);
     }
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
@@ -888,6 +931,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
   A.a = dO; A.lda = d; A.gather = false; A.perm_src = perm_src; A.kk = k;
   A.tiles = tiles; A.ntiles = ntiles; A.max_tiles = mt; A.offsets = offsets;
   A.q = down.q; A.scale = down.scale; A.N = f; A.K = d; A.g = g; A.trans = true;
+  A.bits = base_bits(dims);
   A.Z = dZ + 2 * r; A.ldz = 3 * r; A.lmat = down.A; A.l_es = (size_t)r * f; A.l_js = f;
   A.l_ns = 1; A.r = r; A.lam = 1.f; A.out = dH32; A.ldo = f; A.acc_out = false;
   TIMED(MOE_KT_BWD_DOWN, st, moe::launch_lin_simple(bf, true, A, st));

@@ -63,9 +63,11 @@ constexpr int ST_B = 256 * GM_KS / 2, ST_X = 512 * 4;   // (the A stage holds th
 
 // ---------------------------------------------------------------- row sums --
 // out[row][g] = scale * (sum of a[row][g*G .. g*G+G), bf16 values, float32 sum
-// in k order)
+// in k order); with split the row of out has 2 K/G entries and
+// out[row][K/G + g] = scale2 * the same sum
 __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int K, int G,
-                                    float scale, float *__restrict__ out) {
+                                    float scale, float *__restrict__ out, bool split,
+                                    float scale2) {
   const int ng = K / G;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)rows * ng) return;
@@ -82,7 +84,12 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
       s += __uint_as_float(w[j] & 0xFFFF0000u);
     }
   }
-  out[i] = scale * s;
+  if (split) {
+    out[row * 2 * ng + g] = scale * s;
+    out[row * 2 * ng + ng + g] = scale2 * s;
+  } else {
+    out[i] = scale * s;
+  }
 }
 
 // ------------------------------------------------------------ scale ratios --
@@ -97,19 +104,24 @@ __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int 
 // instead of s times it, i.e. an error of one float32 rounding of the
 // column's largest group.  One thread per column: its ng scales are one
 // contiguous run, and each group's writes are contiguous across the wave.
+// With split the column's scale sequence is that of the two int4 planes of
+// an int8 base, 16 s[0 .. ng) then s[0 .. ng) (2 ng groups; 16 s is exact).
 __global__ __launch_bounds__(256) void scale_ratio_kernel(const uint16_t *__restrict__ s, int E,
-                                                          int N, int ng, float *__restrict__ rt) {
+                                                          int N, int ng, float *__restrict__ rt,
+                                                          bool split) {
   const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
   if (c >= N) return;
   const uint16_t *sc = s + ((size_t)e * N + c) * ng;
+  const int ngo = split ? 2 * ng : ng;
+  auto sv = [&](int g) { return g < ng ? (split ? 16.f : 1.f) * bf2f(sc[g]) : bf2f(sc[g - ng]); };
   float m = 0.f;
-  for (int g = 0; g < ng; ++g) m = fmaxf(m, fabsf(bf2f(sc[g])));
+  for (int g = 0; g < ngo; ++g) m = fmaxf(m, fabsf(sv(g)));
   const float floor_v = fmaxf(m * 0x1p-24f, 0x1p-100f);
   auto guard = [&](float v) { return fabsf(v) < floor_v ? floor_v : v; };
-  float *out = rt + (size_t)e * ng * N + c;
-  float prev = guard(bf2f(sc[0]));
-  for (int g = 1; g < ng; ++g) {
-    const float cur = guard(bf2f(sc[g]));
+  float *out = rt + (size_t)e * ngo * N + c;
+  float prev = guard(sv(0));
+  for (int g = 1; g < ngo; ++g) {
+    const float cur = guard(sv(g));
     out[(size_t)g * N] = prev / cur;
     prev = cur;
   }
@@ -182,6 +194,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
   __shared__ int tok_lds[GM_BM];
 
   const int K = A.K, N = A.N, NG = K / GM_KG, NS = 2 * NG;   // NS: half-group stages
+  const int NSA = A.ka / GM_KS;   // stages of the A rows (NS, or NS / 2 for an int8 base)
   const int BNO = MODE == 0 ? 128 : 256;   // output columns per item (per matrix)
   const int total = cls_count[0] * A.NT, tbase = cls_start[0];
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
@@ -315,12 +328,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
         return;
       }
       const int j = jr, g = j >> 1;
+      const int ja = j < NSA ? j : j - NSA;   // (an int8 base's second plane reads the rows again)
       // destinations re-derived per stage (scalar adds) rather than held
       uint32_t sa = la, sb = lb;
       asm volatile("" : "+s"(sa), "+s"(sb));
 #pragma unroll
       for (int i = 0; i < AOPS; ++i)
-        dma16(abase + (size_t)j * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
+        dma16(abase + (size_t)ja * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
       // stage step of the int4 words: 32 bytes (plain), a whole stage of
       // the expert's columns, 32 N bytes (packed)
 #pragma unroll
@@ -608,6 +622,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
 #pragma unroll
         for (int q = 0; q < WAVES; ++q) v += red[q * GM_BM + tid2];
         A.rsum_out[(size_t)(p0 + tid2) * A.ld_rsum_out + nt] = -136.f * v;
+        if (A.rsum_split) A.rsum_out[(size_t)(p0 + tid2) * A.ld_rsum_out + A.NT + nt] = -128.f * v;
       }
     } else {
 #pragma unroll
@@ -647,6 +662,55 @@ void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStre
   const size_t n16 = (size_t)E * N * K / 32;
   pack_fwd_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(
       reinterpret_cast<const uint4 *>(q), N, K, n16, reinterpret_cast<uint4 *>(qf));
+}
+
+// An int8 base as two int4 planes along K: q = 16 h + l with h = q >> 4
+// (-8 .. 7) and l = q & 15 (0 .. 15); plane 1 holds h and plane 2 l - 8, as
+// two's-complement nibbles.  With the plane scales 16 s and s, and the
+// matrix cores' offset of 136 removed as 136 on plane 1 and 128 on plane 2,
+// the products sum 16 s h + s l = s q exactly.  [E][N][K] bytes ->
+// [E][2K/64][N][32 B] (stage j < K/64: plane 1, K-step j; then plane 2),
+// every 8 values of K one word in the nibble order of the int4 layout (slot
+// i holds value 2i for i < 4 and value 2(i-4)+1 for i >= 4).  One thread per
+// 16 output bytes (32 values), in output order.
+DEV uint32_t int8_plane_word(uint2 v, bool low) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = ((i < 4 ? v.x : v.y) >> (8 * (i & 3))) & 0xFFu;
+    const uint32_t nib = low ? ((b & 15u) ^ 8u) : (b >> 4);
+    const int slot = (i & 1) ? 4 + (i >> 1) : (i >> 1);
+    w |= nib << (4 * slot);
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(256) void pack_fwd_int8_kernel(const uint8_t *__restrict__ q, int N,
+                                                            int K, size_t n16,
+                                                            uint4 *__restrict__ qf) {
+  const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= n16) return;
+  const size_t per_e = (size_t)N * K / 16;   // 16-byte output units per expert (2K values)
+  const size_t e = o / per_e, r = o - e * per_e;
+  const size_t j = r / ((size_t)N * 2), cr = r - j * N * 2;   // stage, 2 c + half
+  const size_t c = cr >> 1, h = cr & 1;
+  const size_t nk = (size_t)K / 64;
+  const bool low = j >= nk;
+  const size_t k0 = (low ? j - nk : j) * 64 + 32 * h;
+  const uint4 *src = reinterpret_cast<const uint4 *>(q + (e * N + c) * K + k0);
+  const uint4 a = src[0], b = src[1];
+  uint4 out;
+  out.x = int8_plane_word(make_uint2(a.x, a.y), low);
+  out.y = int8_plane_word(make_uint2(a.z, a.w), low);
+  out.z = int8_plane_word(make_uint2(b.x, b.y), low);
+  out.w = int8_plane_word(make_uint2(b.z, b.w), low);
+  qf[o] = out;
+}
+
+void launch_pack_fwd_int8(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st) {
+  const size_t n16 = (size_t)E * N * K / 16;
+  pack_fwd_int8_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(
+      q, N, K, n16, reinterpret_cast<uint4 *>(qf));
 }
 
 // ------------------------------------------------------------ tile classes --
@@ -709,15 +773,16 @@ int mfma_tile_rows() { return GM_BM; }
 int mfma_blocks_per_cu() { return GM_BPC; }
 
 void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, float *out,
-                         hipStream_t st) {
+                         hipStream_t st, bool split, float scale2) {
   size_t n = (size_t)rows * (K / G);
   group_rowsum_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((const bf16_t *)a, rows, K, G,
-                                                                   scale, out);
+                                                                   scale, out, split, scale2);
 }
 
-void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st) {
+void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st,
+                        bool split) {
   dim3 grid((N + 255) / 256, E);
-  scale_ratio_kernel<<<grid, 256, 0, st>>>(s, E, N, ng, rt);
+  scale_ratio_kernel<<<grid, 256, 0, st>>>(s, E, N, ng, rt, split);
 }
 
 void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, int *cnt,
@@ -736,7 +801,8 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cl
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
   // the packed base where given and used (P.q0 null: plain layout)
   MfmaGemmArgs P = A;
-  const bool use_p = A.qp0 && (mode == 1 || (A.qp1 && cls != 0));
+  // (an int8 base has only the packed layout: q0 null)
+  const bool use_p = A.qp0 && (mode == 1 || (A.qp1 && (cls != 0 || !A.q0)));
   P.q0 = use_p ? A.qp0 : nullptr;
   P.q1 = use_p ? A.qp1 : nullptr;
 #define MOE_GG2(MODE, NM, QP)                                                        \

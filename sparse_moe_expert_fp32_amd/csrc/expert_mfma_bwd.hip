@@ -96,6 +96,48 @@ __global__ __launch_bounds__(256) void transpose_q_kernel(const uint8_t *__restr
   }
 }
 
+// An int8 base [E][R][C] (bytes in c order) + scales [E][R][C/128] as two
+// int4 planes stacked along R, q = 16 h + l: rows 0 .. R-1 hold h = q >> 4
+// with scales 16 s, rows R .. 2R-1 hold l - 8 (l = q & 15) with scales s,
+// each in the transposed layout above ([E][2R/64][C][32 B], scales
+// [E][C/128][2R] f32).  Summed with the matrix cores' 136 offset removed as
+// 136 on the first plane and 128 on the second, the planes give s q exactly.
+// One thread per output word (8 stacked rows of one column); consecutive
+// threads take consecutive words of a column, then consecutive columns.
+__global__ __launch_bounds__(256) void transpose_q_int8_kernel(const uint8_t *__restrict__ q,
+                                                               const uint16_t *__restrict__ s,
+                                                               const int32_t *__restrict__ offsets,
+                                                               int R, int C, uint8_t *__restrict__ qt,
+                                                               float *__restrict__ st) {
+  const int e = blockIdx.z;
+  if (offsets && offsets[e + 1] == offsets[e]) return;
+  const int blk = blockIdx.y;                     // block of 64 stacked rows
+  const int t = blockIdx.x * 256 + threadIdx.x;   // (column, word) of the block
+  const int c = t >> 3, wd = t & 7;
+  if (c >= C) return;
+  const int n0 = blk * 64 + 8 * wd;               // first stacked row of the word
+  const bool low = n0 >= R;
+  const int r0 = low ? n0 - R : n0;
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = q[((size_t)e * R + r0 + i) * C + c];
+    const uint32_t nib = low ? ((b & 15u) ^ 8u) : (b >> 4);
+    w |= nib << (4 * nib_slot(i));
+  }
+  reinterpret_cast<uint32_t *>(qt)[(((size_t)e * (2 * R / 64) + blk) * C + c) * 8 + wd] = w;
+  // the scales of the block's 64 rows for this column's group (one word's
+  // thread per 8 rows writes them)
+  if ((c & 127) == 0) {
+    const int G = C / 128, g = c >> 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sv = bf2f(s[((size_t)e * R + r0 + i) * G + g]);
+      st[((size_t)e * G + g) * 2 * R + n0 + i] = low ? sv : 16.f * sv;
+    }
+  }
+}
+
 // One pipeline stage in LDS, one array per kind (each read is a per-lane base
 // register plus a compile-time offset): A rows (128 x 64 bf16, 16-byte chunks
 // XOR-swizzled by row), int4 words (256 columns x 32 bytes), the scales of the
@@ -138,11 +180,13 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
   const int Kh = A.K, N = A.N, G = N / 128;
   const int NKh = Kh / GT_KS;
   const int NK = MODE == 1 ? 2 * NKh : NKh;   // mode 1 reduces over [dG | dU]
+  const int NKr = A.kr / GT_KS;   // steps of the A rows per source (NKh, or NKh / 2 for int8)
   const int total = cls_count[0] * A.NT, tbase = cls_start[0];
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int wbeg = (int)(((long long)total * xcd) >> 3);
   const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
   const uint4 c136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136
+  const uint4 c128 = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};   // bf16 128
   // int4 unpack: each bf16 pair of 136 + q is one shift and one three-input
   // logic op, ((w >> 4i) & 0x000F000F) ^ 0x43084308 (constants in registers)
   const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
@@ -253,8 +297,9 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
     auto stage_src = [&](int j) {
       const bool second = MODE == 1 && j >= NKh;
       const int kj = second ? j - NKh : j;
+      const int ka = kj < NKr ? kj : kj - NKr;   // (an int8 base's second plane: the rows again)
       StageSrc r;
-      r.a = reinterpret_cast<const char *>(second ? A.a1 : A.a0) + (size_t)kj * GT_KS * 2;
+      r.a = reinterpret_cast<const char *>(second ? A.a1 : A.a0) + (size_t)ka * GT_KS * 2;
       r.q = (second ? A.qt1 : A.qt0) + ((size_t)e * NKh + kj) * N * 32;
       r.s = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
       return r;
@@ -279,8 +324,11 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
     // one 64-deep step: 2 k-substeps x NMH row fragments x (8 + 1) MFMAs.
     // Lane group lg takes k = 16 lg + 8 s .. + 7 in substep s (A chunk
     // 2 lg + s, int4 word 2 lg + s), the same permutation on both operands.
-    auto compute = [&](int slot, int jl, int nslot) {   // jl: the stage to load into nslot, or -1
+    auto compute = [&](int slot, int jc, int jl, int nslot) {   // jc: this stage; jl: the stage to load into nslot, or -1
       __builtin_amdgcn_sched_barrier(0);
+      // the offset the correction removes: 136, or 128 on an int8 base's second plane
+      const int kc = MODE == 1 && jc >= NKh ? jc - NKh : jc;
+      const uint4 coff = kc < NKr ? c136 : c128;
       const bool ld = jl >= 0;
       const StageSrc src = stage_src(ld ? jl : 0);
       u32x2_t bw[8];
@@ -302,7 +350,7 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
         for (int m = 0; m < NMH; ++m) {
           const u32x4_t a4 = lds_ld<u32x4_t>((s ? offA1 : offA0) + slot * TS_A + m * 2048);
           av[m] = scale_frag(make_uint4(a4.x, a4.y, a4.z, a4.w), sc);
-          corr[m] = mfma32(c136, av[m], corr[m]);
+          corr[m] = mfma32(coff, av[m], corr[m]);
         }
 #pragma unroll
         for (int nf = 0; nf < 8; ++nf) {
@@ -344,7 +392,7 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
   {                                                          \
     const int jj = (JJ), jl = jj + 2;                        \
     stage(jl, NXT);                                          \
-    if (jj < NK) compute(CUR, jl < NK ? jl : -1, NXT);       \
+    if (jj < NK) compute(CUR, jj, jl < NK ? jl : -1, NXT);   \
     __builtin_amdgcn_s_waitcnt(kWaitVm);                     \
     block_barrier();                                         \
   }
@@ -495,6 +543,12 @@ void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offs
                         int C, uint8_t *qt, float *st, hipStream_t stream) {
   dim3 grid((C + 255) / 256, R / 64, E);
   transpose_q_kernel<<<grid, 256, 0, stream>>>(q, s, offsets, R, C, qt, st);
+}
+
+void launch_transpose_q_int8(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E,
+                             int R, int C, uint8_t *qt, float *st, hipStream_t stream) {
+  dim3 grid((C * 8 + 255) / 256, 2 * R / 64, E);
+  transpose_q_int8_kernel<<<grid, 256, 0, stream>>>(q, s, offsets, R, C, qt, st);
 }
 
 

@@ -64,6 +64,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
 // A(p, c): GATHER ? a[perm_src[p] / kk][c] : a[p][c].
 // W: !TRANS: q [E][N][K/2], scale [E][N][K/g]  (W(e,n,c) = stored[n][c])
 //     TRANS: q [E][K][N/2], scale [E][K][N/g]  (W(e,n,c) = stored[c][n])
+//     (bits = 8: q holds one two's-complement byte per value, rows of K or N bytes)
 // L(e, j, n) = lmat[e * l_es + j * l_js + n * l_ns] (act dtype), Z float32.
 constexpr int SB_M = 16, SB_N = 64, SB_K = 32;
 
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(256) void lin_simple_kernel(
     const TA *__restrict__ a, int lda, const int32_t *__restrict__ perm_src, int kk,
     const int2 *__restrict__ tiles, const int *__restrict__ ntiles,
     const int32_t *__restrict__ offsets, const uint8_t *__restrict__ q,
-    const uint16_t *__restrict__ scale, int N, int K, int g, const float *__restrict__ Z, int ldz,
+    const uint16_t *__restrict__ scale, int N, int K, int g, int bits, const float *__restrict__ Z,
+    int ldz,
     const TA *__restrict__ lmat, size_t l_es, int l_js, int l_ns, int r, float lam,
     TO *__restrict__ out, int ldo, bool acc_out) {
   __shared__ float As[SB_M][SB_K + 1];
@@ -98,13 +100,11 @@ __global__ __launch_bounds__(256) void lin_simple_kernel(
       int nn = i / SB_K, cc = i % SB_K, n = n0 + nn, c = c0 + cc;
       float w = 0.f;
       if (n < N && c < K) {
-        if (!TRANS) {
-          size_t rowi = (size_t)e * N + n;
-          w = (float)int4_at(q + rowi * (K / 2), c) * bf2f(scale[rowi * (K / g) + c / g]);
-        } else {
-          size_t rowi = (size_t)e * K + c;
-          w = (float)int4_at(q + rowi * (N / 2), n) * bf2f(scale[rowi * (N / g) + n / g]);
-        }
+        // the stored row and the position in it
+        const size_t rowi = TRANS ? (size_t)e * K + c : (size_t)e * N + n;
+        const int L = TRANS ? N : K, at = TRANS ? n : c;
+        const int qv = bits == 8 ? (int)(int8_t)q[rowi * L + at] : int4_at(q + rowi * (L / 2), at);
+        w = (float)qv * bf2f(scale[rowi * (L / g) + at / g]);
       }
       Ws[nn][cc] = w;
     }
@@ -260,7 +260,7 @@ static void lin_dispatch(const LinArgs &L, hipStream_t st) {
 #define LIN_CALL(G, TR)                                                                        \
   lin_simple_kernel<TA, TO, G, TR><<<grid, 256, 0, st>>>(                                      \
       (const TA *)L.a, L.lda, L.perm_src, L.kk, L.tiles, L.ntiles, L.offsets, L.q, L.scale,    \
-      L.N, L.K, L.g, L.Z, L.ldz, (const TA *)L.lmat, L.l_es, L.l_js, L.l_ns, L.r, L.lam,       \
+      L.N, L.K, L.g, L.bits, L.Z, L.ldz, (const TA *)L.lmat, L.l_es, L.l_js, L.l_ns, L.r, L.lam, \
       (TO *)L.out, L.ldo, L.acc_out)
   if (L.gather) {
     if (L.trans) LIN_CALL(true, true); else LIN_CALL(true, false);

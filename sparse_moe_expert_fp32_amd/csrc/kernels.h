@@ -58,6 +58,7 @@ struct LinArgs {
   const void *a; int lda; bool gather; const int32_t *perm_src; int kk;
   const int2 *tiles; const int *ntiles; int max_tiles; const int32_t *offsets;
   const uint8_t *q; const uint16_t *scale; int N, K, g; bool trans;
+  int bits;                               // base storage: 4 (int4) or 8 (int8)
   const float *Z; int ldz; const void *lmat; size_t l_es; int l_js, l_ns, r; float lam;
   void *out; int ldo; bool acc_out;
 };
@@ -90,6 +91,10 @@ struct MfmaGemmArgs {
   const float *rsum; int ld_rsum;         // per A row, per group of 128: -136 * sum of the row
   const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
   int K, N, NT;                           // reduction, columns per matrix, N-tiles per M-tile
+  // ka: the A rows' length.  K for an int4 base; K / 2 for an int8 base split
+  // into two int4 planes along K (launch_pack_fwd_int8): the rows are read
+  // twice, and the start values of the second plane's groups follow the first's
+  int ka;
   // rt: scale ratios [E][K/128][N] of launch_scale_ratio
   const uint8_t *q0; const float *rt0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
   const uint8_t *q1; const float *rt1; const uint16_t *B1;   // up (mode 0)
@@ -101,14 +106,20 @@ struct MfmaGemmArgs {
   uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
   uint16_t *saveG, *saveU;                // mode 0, optional: U s (1 + G (1 - s)), G s (s = sigmoid G)
   float *rsum_out; int ld_rsum_out;       // mode 0: -136 * group sums of H rows
+  int rsum_split;                         // mode 0: also -128 * the sums, at + NT (int8 down)
 };
 int mfma_tile_rows();
 int mfma_blocks_per_cu();      // resident blocks per CU the kernel is built for
+// out[row][g] = scale * (sum of group g of the bf16 row), K / G groups; with
+// split, out has 2 K / G entries per row and out[row][K / G + g] = scale2 * sum
 void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, float *out,
-                         hipStream_t st);
-// scale ratios of a quantized matrix ([E][N][ng] bf16 -> [E][ng][N] f32):
-// rt[e][g][c] = s[e][c][g-1] / s[e][c][g] for g >= 1, rt[e][0][c] = s[e][c][ng-1]
-void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st);
+                         hipStream_t st, bool split = false, float scale2 = 0.f);
+// scale ratios of a quantized matrix ([E][N][ng] bf16 -> [E][ng'][N] f32):
+// rt[e][g][c] = s'[e][c][g-1] / s'[e][c][g] for g >= 1, rt[e][0][c] = s'[e][c][ng'-1],
+// s' the scales (ng' = ng), or with split those of the two int4 planes of an
+// int8 base, 16 s then s (ng' = 2 ng)
+void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st,
+                        bool split = false);
 // expert tiles of 32 nclass rows (nclass <= 4), the partial last one of each
 // expert rounded up to a multiple of 32, grouped by that class (class c:
 // 32 (nclass - c) rows); cnt[8]: count and first index of each class
@@ -117,6 +128,10 @@ void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, 
                         hipStream_t st);
 // int4 [E][N][K/2] -> stage-major [E][K/64][N][32 B] (K a multiple of 64)
 void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st);
+// int8 [E][N][K] -> the stage-major int4 layout of its two planes along K
+// ([E][2K/64][N][32 B]): q = 16 h + l, plane 1 holds h = q >> 4, plane 2
+// l - 8 (l = q & 15), each as a two's-complement nibble
+void launch_pack_fwd_int8(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st);
 // the launch of tile class cls (0: 128-row tiles .. 3: 32-row tiles)
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
                          hipStream_t st);
@@ -129,6 +144,10 @@ struct MfmaGemmTArgs {
   const int32_t *perm_src; int kk; const float *gsc;
   const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
   int K, N, NT;                           // reduction per source, output columns, ceil(N / 256)
+  // kr: the A rows' length per source.  K for an int4 base; K / 2 for an int8
+  // base split into two stacked int4 planes (launch_transpose_q_int8): the rows
+  // are read twice, the second plane's offset correction is 128 instead of 136
+  int kr;
   const uint8_t *qt0, *qt1;               // int4 base transposed, [E][N][K/2] (qt1: mode 1, up)
   const float *st0, *st1;                 // its scales per column group, [E][N/128][K]
   const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
@@ -145,6 +164,11 @@ int mfma_t_blocks_per_cu();   // resident blocks per CU the kernel is built for
 // null); R, C multiples of 128
 void launch_transpose_q(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E, int R,
                         int C, uint8_t *qt, float *st, hipStream_t stream);
+// int8 [E][R][C] + scales [E][R][C/128] -> the transposed int4 layout of its
+// two planes stacked along R (2R rows: h = q >> 4 with scale 16 s, then
+// l - 8 with scale s, l = q & 15): [E][2R/64][C][32 B] + [E][C/128][2R] f32
+void launch_transpose_q_int8(const uint8_t *q, const uint16_t *s, const int32_t *offsets, int E,
+                             int R, int C, uint8_t *qt, float *st, hipStream_t stream);
 
 // ---- rank-r adapter products on the matrix cores (lowrank.hip)
 struct ProjMArgs {                        // Z_s = scale * A M_s^T over each expert's rows

@@ -29,6 +29,9 @@ Storage formats (these are the library's input formats):
     (bits 4j..4j+3) holds k_{2j} for j < 4 and k_{2(j-4)+1} for j >= 4, so a
     word unpacks into the bf16 pairs (k0,k1), (k2,k3), (k4,k5), (k6,k7) with
     one shift and one mask per pair.
+  * int8 base matrix (bits = 8) -> q: uint8 [N, K] holding the two's-complement
+    bytes in k order, scale: bf16 [N, K/group]; s = bf16(max|w| / 127),
+    q = clamp(round_half_even(w / s), -128, 127), q = 0 when s = 0.
 """
 from __future__ import annotations
 
@@ -104,6 +107,32 @@ def quantize_int4(w: np.ndarray, group: int):
     return pack_int4(q), s_bits
 
 
+def quantize_int8(w: np.ndarray, group: int):
+    """w float32 [N, K] -> (q uint8 [N, K] two's-complement bytes,
+    scale bf16 bits [N, K/group])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    wg = w.reshape(N, K // group, group)
+    amax = np.abs(wg).max(axis=2)
+    s_bits = bf16_bits(amax / np.float32(127.0))
+    s = bf16_to_f32(s_bits)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = wg / s[:, :, None]
+    ratio = np.where(s[:, :, None] == 0, np.float32(0), ratio)
+    q = np.clip(np.rint(ratio), -128, 127).astype(np.int8).reshape(N, K)
+    return np.ascontiguousarray(q.view(np.uint8)), s_bits
+
+
+def quantize(w: np.ndarray, group: int, bits: int):
+    if bits == 4:
+        return quantize_int4(w, group)
+    if bits == 8:
+        return quantize_int8(w, group)
+    raise ValueError(f"unsupported base width {bits}")
+
+
 # ------------------------------------------------------------ generator --
 
 def _normal(ss: np.random.SeedSequence, shape, var: float) -> np.ndarray:
@@ -121,7 +150,7 @@ def _expert(cfg: LayerConfig, ss: np.random.SeedSequence):
     wd = _normal(s[2], (d, f), 1.0 / f)
     out = {}
     for name, w in (("gate", wg), ("up", wu), ("down", wd)):
-        out[name] = quantize_int4(w, g)
+        out[name] = quantize(w, g, cfg.bits)
     out["A_gate"] = to_storage(_normal(s[3], (r, d), 1.0 / d), cfg.act)
     out["B_gate"] = to_storage(_normal(s[4], (f, r), 0.02), cfg.act)
     out["A_up"] = to_storage(_normal(s[5], (r, d), 1.0 / d), cfg.act)
@@ -143,7 +172,7 @@ def generate(cfg: LayerConfig, seed: int = 0, threads: int | None = None) -> dic
     """All inputs of one layer call as numpy arrays (see module docstring).
 
     Keys: x [T,d], dy [T,d] (act storage); w_router [d,E] f32; b_router [E]
-    f32 or None; for m in gate/up/down: q_m [E,N,K/2] u8, s_m [E,N,K/g] u16,
+    f32 or None; for m in gate/up/down: q_m [E,N,K/2] u8 (int4; [E,N,K] for int8), s_m [E,N,K/g] u16,
     A_m [E,r,K], B_m [E,N,r] (act storage; out x in like the base).
     N,K = (f,d) for gate/up and (d,f) for down.
     """
@@ -160,7 +189,7 @@ def generate(cfg: LayerConfig, seed: int = 0, threads: int | None = None) -> dic
     adt = np.float32 if cfg.act == "f32" else np.uint16
     shapes = {"gate": (f, d), "up": (f, d), "down": (d, f)}
     for m, (N, K) in shapes.items():
-        out[f"q_{m}"] = np.empty((E, N, K // 2), np.uint8)
+        out[f"q_{m}"] = np.empty((E, N, K * cfg.bits // 8), np.uint8)
         out[f"s_{m}"] = np.empty((E, N, K // g), np.uint16)
         out[f"A_{m}"] = np.empty((E, r, K), adt)
         out[f"B_{m}"] = np.empty((E, N, r), adt)

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(B):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(declared_functions()) == set(B.EXPORTS)
-    assert B.moe_abi_version() == 3
+    assert B.moe_abi_version() == 4
 
 
 def good(B, **kw):
@@ -71,6 +71,27 @@ def test_workspace_flags_shrink_and_validate(B):
     assert B.LIB.moe_workspace_size(ctypes.byref(big), B.CALL_EXPERT_FWD | 0x400,
                                     ctypes.byref(out)) == -1
     assert out.value == 7
+
+
+def test_int8_base_sizes_and_validation(B):
+    """An int8 base ("Int8 or Int4") doubles the packed base sizes (its two
+    int4 planes), the forward workspace holds the planes when the caller does
+    not pack them, and a base width other than 4 or 8 is unsupported."""
+    i4 = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16")
+    i8 = B.dims(8192, 2048, 460, 12, 768, 16, 128, "bf16", bits=8)
+    assert B.moe_pack_base_f_size(i8) == 2 * B.moe_pack_base_f_size(i4)
+    assert B.moe_pack_base_t_size(i8) == 2 * B.moe_pack_base_t_size(i4)
+    f8 = B.moe_workspace_size(i8, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN)
+    assert f8 >= 3 * B.moe_pack_base_f_size(i8)
+    f8p = B.moe_workspace_size(i8, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN | B.WS_PACKED_GIVEN)
+    f4p = B.moe_workspace_size(i4, B.CALL_EXPERT_FWD | B.WS_SAVE_GIVEN | B.WS_PACKED_GIVEN)
+    assert f8p > f4p and f8p < 16 << 20     # only the doubled start-value tables
+    for bad in (1, 5, 16, -4):
+        dm = B.dims(64, 128, 8, 2, 256, 4, 32, "f32", bits=bad)
+        out = ctypes.c_size_t(7)
+        assert B.LIB.moe_workspace_size(ctypes.byref(dm), 0, ctypes.byref(out)) == -2
+        assert out.value == 7
+    assert B.moe_workspace_size(B.dims(64, 128, 8, 2, 256, 4, 32, "f32", bits=0), 0) >= 0
 
 
 def test_noalloc_forward_rejects_before_any_hip_call(B):

@@ -65,6 +65,73 @@ def test_quantize_error_bound_and_exact_dequant(group):
     assert np.all(qa[sf > 0] == 7)
 
 
+# ------------------------------------------------------------- int8 base --
+
+def test_int8_layout_and_quantizer_golden():
+    """The int8 storage ("Int8 or Int4", TQP Quantization): bytes, decoding,
+    dequantisation and one hand-worked quantisation."""
+    g = json.load(open(os.path.join(GOLD, "int8_layout.json")))
+    for case in g["cases"]:
+        back = oracle.unpack_int8(np.array(case["bytes"], np.uint8)[None, :])
+        assert back[0].tolist() == case["values"]
+    sc = g["scaled"]
+    q = np.array(sc["values"], np.int8).view(np.uint8)[None, :]
+    w = oracle.dequantize(q, np.array([[sc["scale_bits"]]], np.uint16), 8)
+    assert w[0].tolist() == sc["dequant"]
+    qz = g["quantize"]
+    q8, s8 = inputs.quantize_int8(np.array([qz["w"]], np.float32), qz["group"])
+    assert s8.tolist() == [[qz["scale_bits"]]]
+    assert q8.view(np.int8)[0].tolist() == qz["q"]
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_quantize_int8_error_bound_and_exact_dequant(group):
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((32, 256)) * rng.uniform(0.01, 3, (32, 1))).astype(np.float32)
+    w[5, group:2 * group] = 0.0             # an all-zero group
+    q, s = inputs.quantize_int8(w, group)
+    assert q.shape == (32, 256)
+    wh = oracle.dequantize(q, s, group)
+    sf = oracle.to_f64(s)
+    bound = np.repeat(sf, group, axis=1) / 2
+    assert np.all(np.abs(w.astype(np.float64) - wh) <= bound * (1 + 1e-12))
+    assert np.all(wh[5, group:2 * group] == 0.0) and sf[5, 1] == 0.0
+    qi = oracle.unpack_int8(q)
+    assert qi.min() >= -128 and qi.max() <= 127
+    # the largest magnitude of every non-zero group quantises to +-127, and
+    # -128 is never produced
+    qa = np.abs(qi).reshape(32, -1, group).max(axis=2)
+    assert np.all(qa[sf > 0] == 127) and qi.min() >= -127
+
+
+def test_int8_and_int4_layers_agree_on_shared_values():
+    """Values in [-7, 7] stored as int8 and as int4 with the same scales give
+    the same dequantised experts, so the oracle's layer must be identical for
+    both storage widths (a wrong int8 decoding -- unsigned bytes, a wrong
+    group repeat -- changes it)."""
+    cfg = tiny(act="f32")
+    inp4 = inputs.generate(cfg, 3)
+    inp8 = dict(inp4)
+    rng = np.random.default_rng(11)
+    for m in ("gate", "up", "down"):
+        E, N, _ = inp4[f"q_{m}"].shape
+        K = inp4[f"s_{m}"].shape[-1] * cfg.group
+        vals = rng.integers(-7, 8, size=(E, N, K)).astype(np.int8)
+        inp4[f"q_{m}"] = inputs.pack_int4(vals)
+        inp8[f"q_{m}"] = np.ascontiguousarray(vals.view(np.uint8))
+    f4 = oracle.forward(inp4, cfg.k, cfg.group)
+    f8 = oracle.forward(inp8, cfg.k, cfg.group)
+    assert np.array_equal(f4["y"], f8["y"])
+    b4 = oracle.backward(inp4, f4, cfg.k, cfg.group)
+    b8 = oracle.backward(inp8, f8, cfg.k, cfg.group)
+    for key in b4:
+        assert np.array_equal(b4[key], b8[key]), key
+    # and a value outside the int4 range changes the int8 layer
+    inp8["q_down"] = inp8["q_down"].copy()
+    inp8["q_down"][0, 0, 0] = np.uint8(100)
+    assert not np.array_equal(oracle.forward(inp8, cfg.k, cfg.group)["y"], f8["y"])
+
+
 # ---------------------------------------------------------------- router --
 
 def test_router_logits_dyadic_exact():
