@@ -162,6 +162,13 @@ struct FwdLayout {
   }
 };
 
+// Whether tile class c (of nc; tiles of 32 (nc - c) rows, the partial last
+// tile of an expert rounded up to a multiple of 32) can hold any tile: every
+// token is routed to k distinct experts, so no expert has more than T rows,
+// and class c needs an expert with more than 32 (nc - 1 - c).  Short batches
+// (decode) skip the launches of the tall classes.
+bool class_possible(int T, int nc, int c) { return T > 32 * (nc - 1 - c); }
+
 // Persistent grids: blocks_per_cu resident blocks on every compute unit
 // (rounded to a multiple of the 8 XCDs).
 int persistent_grid(int blocks_per_cu = 1) {
@@ -653,7 +660,9 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     M.saveG = save ? (uint16_t *)Gs : nullptr;
     M.saveU = save ? (uint16_t *)Us : nullptr;
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128 * pm; M.rsum_split = i8;
-    TIMED(MOE_KT_GATEUP, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(0, M, ntiles_m, c, grid, st));
+    const int ncls = moe::mfma_tile_rows() / 32;
+    TIMED(MOE_KT_GATEUP, st, for (int c = 0; c < ncls; ++c) if (class_possible(T, ncls, c))
+                                 moe::launch_grouped_gemm(0, M, ntiles_m, c, grid, st));
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
     Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
@@ -666,7 +675,8 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     D.qp0 = (const uint8_t *)qf_d;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
-    TIMED(MOE_KT_DOWN, st, for (int c = 0; c < 4; ++c) moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_DOWN, st, for (int c = 0; c < ncls; ++c) if (class_possible(T, ncls, c))
+                               moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));
     return hip_status("moe_expert_fwd");
   }
 
@@ -855,7 +865,8 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
     const int ncls_t = moe::mfma_t_tile_rows() / 32;
-    TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < ncls_t; ++c) moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < ncls_t; ++c) if (class_possible(T, ncls_t, c))
+                                   moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
@@ -896,7 +907,8 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
     X.out = (uint16_t *)dXp; X.ldo = d;
-    TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < ncls_t; ++c) moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < ncls_t; ++c) if (class_possible(T, ncls_t, c))
+                                     moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
     // gate gradient and the per-token sum of dX_perm, one pass per token
     TIMED(MOE_KT_GATE_GRAD, st, {
       if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, E, dx,

@@ -35,30 +35,47 @@ __global__ __launch_bounds__(PB) void perm_hist_kernel(const int32_t *__restrict
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x * PB + tid;
   for (int i = tid; i < 4 * E; i += PB) masks[i] = 0ull;
+  // the token's canonical experts, held in registers (k <= 32: the loops
+  // over j are unrolled, so every index into ce is a constant)
+  int ce[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) ce[j] = 0;
   if (t < Tn) {
-    int32_t *ct = canon + (size_t)t * k;
-    auto used = [&](int e, int j) {
-      for (int i = 0; i < j; ++i)
-        if (ct[i] == e) return true;
-      return false;
-    };
-    for (int j = 0; j < k; ++j) {
-      int e = min(max(idx[(size_t)t * k + j], 0), E - 1);
-      if (used(e, j)) {
-        e = 0;
-        while (used(e, j)) ++e;
+    const int32_t *it = idx + (size_t)t * k;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j >= k) break;
+      int e = min(max(it[j], 0), E - 1);
+      bool dup = false;
+#pragma unroll
+      for (int i = 0; i < j; ++i) dup |= ce[i] == e;
+      if (dup) {   // (never for the router's output)
+        for (e = 0;; ++e) {
+          bool u = false;
+#pragma unroll
+          for (int i = 0; i < j; ++i) u |= ce[i] == e;
+          if (!u) break;
+        }
       }
-      ct[j] = e;
+      ce[j] = e;
+      canon[(size_t)t * k + j] = e;
     }
   }
   __syncthreads();
-  if (t < Tn)
-    for (int j = 0; j < k; ++j) atomicOr(&masks[wave * E + canon[(size_t)t * k + j]], 1ull << lane);
+  if (t < Tn) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j >= k) break;
+      atomicOr(&masks[wave * E + ce[j]], 1ull << lane);
+    }
+  }
   __syncthreads();
   if (t < Tn) {
     const unsigned long long lower = (1ull << lane) - 1ull;
-    for (int j = 0; j < k; ++j) {
-      int e = canon[(size_t)t * k + j];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j >= k) break;
+      const int e = ce[j];
       int r = __popcll(masks[wave * E + e] & lower);
       for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
       rank[(size_t)t * k + j] = r;

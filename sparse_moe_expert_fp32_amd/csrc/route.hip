@@ -171,13 +171,29 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const int NE = (E + 63) >> 6;
   float l[16];
   uint32_t taken = 0;
+  // the split-K partial sums, added in split order; all of one split's loads
+  // are issued together (one wait per split, not one per value)
+  float acc[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float *ps = partial + ((size_t)s * Tn + t) * E;
+    float pv[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int e = lane + 64 * n;
+      pv[n] = n < NE && e < E ? ps[e] : 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) acc[n] += pv[n];
+  }
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     int e = lane + 64 * n;
     float v = -INFINITY;
     if (n < NE && e < E) {
-      v = 0.f;
-      for (int s = 0; s < splits; ++s) v += partial[((size_t)s * Tn + t) * E + e];
+      v = acc[n];
       if (bias) v += bias[e];
       if (logits_out) logits_out[(size_t)t * E + e] = v;
       // a NaN logit (from non-finite x, W_r or bias) competes as -inf, so the
@@ -225,6 +241,7 @@ int route_splits(int T, int d, int E) {
   const int max_splits = d / RT_KS;   // d is a multiple of the quantization group (>= 32)
   int s = (512 + blocks - 1) / blocks;
   if (s > max_splits) s = max_splits;
+  if (s > 16) s = 16;   // (the top-k pass adds the splits of every logit)
   if (s < 1) s = 1;
   return s;
 }
