@@ -191,7 +191,8 @@ struct BwdLayout {
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
     tiles_m = mf ? c.take(max_tiles(d, moe::mfma_t_tile_rows()) * sizeof(int2)) : 0;
-    ntiles_m = mf ? c.take(8 * sizeof(int)) : 0;
+    // tile count, then eight work counters for each of the two products
+    ntiles_m = mf ? c.take(32 * sizeof(int)) : 0;
     tiles_p = mf ? c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2)) : 0;
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
@@ -794,7 +795,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     const int grid = persistent_grid(moe::mfma_t_blocks_per_cu());
     const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
-    moe::launch_class_tiles(offsets, E, moe::mfma_t_tile_rows() / 32, tiles_m, ntiles_m, st);
+    moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st, nullptr, 32);
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     uint16_t *bt_d = at<uint16_t>(ws, L.bt);
     uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
@@ -864,9 +865,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A; M.LT0 = lt_d;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
-    const int ncls_t = moe::mfma_t_tile_rows() / 32;
-    TIMED(MOE_KT_BWD_DOWN, st, for (int c = 0; c < ncls_t; ++c) if (class_possible(T, ncls_t, c))
-                                   moe::launch_grouped_gemm_t(0, M, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, ntiles_m + 8, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
@@ -907,8 +906,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
     X.out = (uint16_t *)dXp; X.ldo = d;
-    TIMED(MOE_KT_BWD_GATEUP, st, for (int c = 0; c < ncls_t; ++c) if (class_possible(T, ncls_t, c))
-                                     moe::launch_grouped_gemm_t(1, X, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, ntiles_m, ntiles_m + 16, grid, st));
     // gate gradient and the per-token sum of dX_perm, one pass per token
     TIMED(MOE_KT_GATE_GRAD, st, {
       if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, E, dx,

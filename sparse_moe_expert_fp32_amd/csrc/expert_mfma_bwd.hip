@@ -142,10 +142,7 @@ __global__ __launch_bounds__(256) void transpose_q_int8_kernel(const uint8_t *__
 // register plus a compile-time offset): A rows (128 x 64 bf16, 16-byte chunks
 // XOR-swizzled by row), int4 words (256 columns x 32 bytes), the scales of the
 // stage's 64 reduction steps for the block's two column groups.
-constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage holds the class's rows)
-// blocks per CU of tile class NMH, as LDS (the A ring holds 32 NMH rows) and
-// registers allow: 32-row tiles four, 64-row tiles three, the others two
-constexpr int gt_bpc(int NMH) { return NMH <= 1 ? 4 : NMH == 2 ? 3 : GT_BPC; }
+constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage holds the item's rows)
 
 // ------------------------------------------------------------------ GEMM --
 // A bf16x8 fragment times 8 per-k scales, rounded back to bf16.
@@ -158,53 +155,36 @@ DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
   return r;
 }
 
-// NMH: row fragments of 16 per wave; the item's tile class has 32 NMH rows
-// (128, 96, 64, 32), each class its own launch.  Waves 2 x 2: wave (wm, wn)
-// takes rows 16 NMH wm .. + 16 NMH and the 128 columns of column group wn.
+// Per-launch values every work item uses.
+struct GtCtx {
+  int Kh, N, G, NKh, NK, NKr;
+  uint32_t ldsA, ldsB, ldsS;   // LDS byte addresses of the ring arrays
+  uint32_t kMask, kMagic;      // int4 unpack constants (held in registers)
+};
+
+// One work item: the rows p0 .. p0 + rows - 1 of expert e (rows <= 32 NMH)
+// times the 256 output columns from c0.  NMH: row fragments of 16 per wave;
+// the item runs as a tile of 32 NMH rows.  Waves 2 x 2: wave (wm, wn) takes
+// rows 16 NMH wm .. + 16 NMH and the 128 columns of column group wn.
 // Products are formed transposed (D^T = W^T A^T: the unpacked weights are the
 // first MFMA operand) so a lane holds one row and four consecutive columns and
-// the epilogue reads G, U and writes its results 8 bytes at a time.
+// the epilogue reads its multipliers and writes its results 8 bytes at a time.
 template <int MODE, int NMH, bool EPL>
-__global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
-    const MfmaGemmTArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
-  // a 3-deep ring of stages (filled by LDS-DMA issued from inline asm, with
-  // explicit waits)
-  // (ringA 32-byte aligned: the second substep's chunk is the first's
-  // address with bit 4 flipped)
-  constexpr int TS_A = 32 * NMH * GT_KS * 2;   // A stage: the class's rows x 64 K
-  __shared__ __attribute__((aligned(32))) uint4 ringA[3][TS_A / 16];
-  __shared__ uint4 ringB[3][TS_B / 16];
-  __shared__ float ringS[3][TS_S / 4];
+DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows, int c0) {
+  // the ring (3 stages, filled by LDS-DMA issued from inline asm, with
+  // explicit waits) holds the item's rows: its A stages are 32 NMH rows apart
+  constexpr int TS_A = 32 * NMH * GT_KS * 2;   // A stage: the tile's rows x 64 K
   constexpr int AOPS = NMH;   // 8-row A loads per wave and stage
-
-  const int Kh = A.K, N = A.N, G = N / 128;
-  const int NKh = Kh / GT_KS;
-  const int NK = MODE == 1 ? 2 * NKh : NKh;   // mode 1 reduces over [dG | dU]
-  const int NKr = A.kr / GT_KS;   // steps of the A rows per source (NKh, or NKh / 2 for int8)
-  const int total = cls_count[0] * A.NT, tbase = cls_start[0];
-  const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
-  const int wbeg = (int)(((long long)total * xcd) >> 3);
-  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
+  const int Kh = X.Kh, N = X.N, G = X.G, NKh = X.NKh, NK = X.NK, NKr = X.NKr;
+  const uint32_t ldsA = X.ldsA, ldsB = X.ldsB, ldsS = X.ldsS, kMask = X.kMask, kMagic = X.kMagic;
   const uint4 c136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136
   const uint4 c128 = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};   // bf16 128
-  // int4 unpack: each bf16 pair of 136 + q is one shift and one three-input
-  // logic op, ((w >> 4i) & 0x000F000F) ^ 0x43084308 (constants in registers)
-  const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
-  uint32_t kMagic;
-  asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(kMagic));
-  const uint32_t ldsA = lds_addr(ringA), ldsB = lds_addr(ringB), ldsS = lds_addr(ringS);
-
-  for (int wi = wbeg + bi; wi < wend; wi += nper) {
+  {
     int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));   // keep tid-only arithmetic inside the loop
+    asm volatile("" : "+v"(tid));   // keep tid-only arithmetic inside the item
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int wm = w & 1, wn = w >> 1;
-    const int ti = wi / A.NT, nt = wi - ti * A.NT;
-    const int2 tile = A.tiles[tbase + ti];
-    const int e = tile.x, p0 = tile.y;
-    const int rows = min(32 * NMH, A.offsets[e + 1] - p0);
-    const int c0 = nt * GT_BN;
 
     // A staging: wave w, load i covers rows 8 (AOPS w + i) .. +7 (8 chunks of
     // 16 B each); chunk c of row r lives at c ^ row_swz(r)
@@ -514,27 +494,83 @@ __global__ __launch_bounds__(256, gt_bpc(NMH)) void grouped_gemm_t_kernel(
   }
 }
 
+// All items of the product in one launch: the tiles of launch_build_tiles
+// (each expert's rows in tiles of 128, in expert order) times the column
+// tiles, in that order, as a persistent work list split into eight
+// contiguous ranges, one per XCD, so that the tiles of one expert, including
+// its short last one, run close together in time on one XCD and share its
+// weights in that L2.  Within its range a block takes the next item from a
+// counter of the XCD (ctr[xcd], zero at launch), so blocks that drew short
+// items take more of them.  Each item runs as the shortest tile class that
+// holds its rows (32, 64, 96 or 128; a wave-uniform branch).  Two blocks per
+// CU, so that one block's VALU work (scaling, unpacking) overlaps the other's
+// matrix work.
+template <int MODE, bool EPL>
+__global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaGemmTArgs A,
+                                                                     const int *__restrict__ ntiles,
+                                                                     int *__restrict__ ctr) {
+  // (ringA 32-byte aligned: the second substep's chunk is the first's
+  // address with bit 4 flipped)
+  __shared__ __attribute__((aligned(32))) uint4 ringA[3][GT_BM * GT_KS * 2 / 16];
+  __shared__ uint4 ringB[3][TS_B / 16];
+  __shared__ float ringS[3][TS_S / 4];
+  GtCtx X;
+  X.Kh = A.K;
+  X.N = A.N;
+  X.G = A.N / 128;
+  X.NKh = A.K / GT_KS;
+  X.NK = MODE == 1 ? 2 * X.NKh : X.NKh;   // mode 1 reduces over [dG | dU]
+  X.NKr = A.kr / GT_KS;   // steps of the A rows per source (NKh, or NKh / 2 for int8)
+  X.ldsA = lds_addr(ringA);
+  X.ldsB = lds_addr(ringB);
+  X.ldsS = lds_addr(ringS);
+  // int4 unpack: each bf16 pair of 136 + q is one shift and one three-input
+  // logic op, ((w >> 4i) & 0x000F000F) ^ 0x43084308 (constants in registers)
+  X.kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(X.kMagic));
+  __shared__ int next_item;
+  const int total = ntiles[0] * A.NT;
+  const int xcd = blockIdx.x & 7;
+  const int wbeg = (int)(((long long)total * xcd) >> 3);
+  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
+  if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+  __syncthreads();
+  for (int wi = next_item; wi < wend; wi = next_item) {
+    // every thread has read next_item; the next draw overlaps this item (its
+    // value is visible after the item's first barrier)
+    __syncthreads();
+    if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+    const int ti = wi / A.NT, nt = wi - ti * A.NT;
+    const int2 tile = A.tiles[ti];
+    const int e = tile.x, p0 = tile.y;
+    const int rows = min(GT_BM, A.offsets[e + 1] - p0);
+    const int c0 = nt * GT_BN;
+    const int nmh = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
+    if (nmh >= 4) gt_item<MODE, 4, EPL>(A, X, e, p0, rows, c0);
+    else if (nmh == 3) gt_item<MODE, 3, EPL>(A, X, e, p0, rows, c0);
+    else if (nmh == 2) gt_item<MODE, 2, EPL>(A, X, e, p0, rows, c0);
+    else gt_item<MODE, 1, EPL>(A, X, e, p0, rows, c0);
+  }
+}
+
 int mfma_t_tile_rows() { return GT_BM; }
 int mfma_t_tile_cols() { return GT_BN; }
 int mfma_t_blocks_per_cu() { return GT_BPC; }
 
-// The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32); cnt as
-// written by launch_class_tiles.
-void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
+// One launch over the tile list of launch_build_tiles (tiles of 128 rows);
+// ctr: eight zeroed counters.
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *ntiles, int *ctr, int grid,
                            hipStream_t st) {
-  const int *c = cnt + cls, *s = cnt + 4 + cls;
-  // grid: GT_BPC blocks per CU; the 64- and 32-row classes run more
-  if (cls >= 2) grid = (grid / GT_BPC * gt_bpc(cls == 2 ? 2 : 1)) & ~7;
   // operands of the epilogue through the LDS ring: rank 16, dZ rows 16-byte
   // aligned, transposed adapter A given
   const bool epl = A.r == 16 && (A.ldz & 3) == 0 && A.LT0 && (mode == 0 || A.LT1);
-#define MOE_GT(MODE, NMH)                                                           \
-  if (epl) grouped_gemm_t_kernel<MODE, NMH, true><<<grid, 256, 0, st>>>(A, c, s);   \
-  else grouped_gemm_t_kernel<MODE, NMH, false><<<grid, 256, 0, st>>>(A, c, s)
+#define MOE_GT(MODE)                                                           \
+  if (epl) grouped_gemm_t_kernel<MODE, true><<<grid, 256, 0, st>>>(A, ntiles, ctr);   \
+  else grouped_gemm_t_kernel<MODE, false><<<grid, 256, 0, st>>>(A, ntiles, ctr)
   if (mode == 0) {
-    if (cls == 0) MOE_GT(0, 4); else if (cls == 1) MOE_GT(0, 3); else if (cls == 2) MOE_GT(0, 2); else MOE_GT(0, 1);
+    MOE_GT(0);
   } else {
-    if (cls == 0) MOE_GT(1, 4); else if (cls == 1) MOE_GT(1, 3); else if (cls == 2) MOE_GT(1, 2); else MOE_GT(1, 1);
+    MOE_GT(1);
   }
 #undef MOE_GT
 }

@@ -17,13 +17,15 @@ namespace moe {
 // ------------------------------------------------------------ tile list --
 // One entry per (expert, BM-row block); entries ordered by expert.  tiles[i]
 // = (e, first row); ntiles[0] = count; first (when given) [e] = index of the
-// expert's first entry.  Launched with one 1024-thread block.
+// expert's first entry; ntiles[1 .. nzero-1] = 0 (counters of the kernels
+// that consume the list).  Launched with one 1024-thread block.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ offsets,
                                                            int E, int BM, int2 *__restrict__ tiles,
                                                            int *__restrict__ ntiles,
-                                                           int *__restrict__ first_out) {
+                                                           int *__restrict__ first_out, int nzero) {
   __shared__ int sc[1024];
   const int e = threadIdx.x;
+  if (e >= 1 && e < nzero) ntiles[e] = 0;
   int c = 0, lo = 0;
   if (e < E) {
     lo = offsets[e];
@@ -248,8 +250,8 @@ __global__ void swiglu_bwd_kernel(const float *__restrict__ dH, const T *__restr
 // ------------------------------------------------------------- launchers --
 
 void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles,
-                        hipStream_t st, int *first) {
-  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, BM, tiles, ntiles, first);
+                        hipStream_t st, int *first, int nzero) {
+  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, BM, tiles, ntiles, first, nzero);
 }
 
 int simple_tile_rows() { return SB_M; }

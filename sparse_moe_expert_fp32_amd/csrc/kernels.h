@@ -50,8 +50,9 @@ void launch_grow_router(const float *w, const float *b, const float *z, float s,
 // ---- float32 expert kernels (expert_simple.hip)
 // first (optional, 2E + 1 ints): index of each expert's first tile, then the
 // number of experts with no tile or more than one, then those experts
+// nzero: ntiles[1 .. nzero-1] are set to zero as well (work counters)
 void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles,
-                        hipStream_t st, int *first = nullptr);
+                        hipStream_t st, int *first = nullptr, int nzero = 0);
 int simple_tile_rows();
 
 struct LinArgs {
@@ -199,8 +200,10 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
 // bf16 [E][r][N] -> [E][N][r]
 void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st);
-// the launch of tile class cls of launch_class_tiles (cnt: counts and starts)
-void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *cnt, int cls, int grid,
+// one launch over the tiles of launch_build_tiles (mfma_t_tile_rows() rows,
+// in expert order), each item as the shortest tile class holding its rows
+// (ctr: eight counters, zero at launch, one per XCD)
+void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *ntiles, int *ctr, int grid,
                            hipStream_t st);
 
 // ---- fixed device scratch (scratch.hip): the per-device address of the
