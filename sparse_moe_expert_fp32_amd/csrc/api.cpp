@@ -140,7 +140,9 @@ struct FwdLayout {
     if (use_mfma(d)) {
       G32 = U32 = 0;
       tiles_m = c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2));
-      ntiles_m = c.take(8 * sizeof(int));
+      // (class counts and starts, or the tile count and eight work counters
+      // for each of the two products)
+      ntiles_m = c.take(32 * sizeof(int));
       tiles_p = c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2));
       ntiles_p = c.take(sizeof(int));
       const size_t pm = plane_mult(d);
@@ -168,6 +170,12 @@ struct FwdLayout {
 // and class c needs an expert with more than 32 (nc - 1 - c).  Short batches
 // (decode) skip the launches of the tall classes.
 bool class_possible(int T, int nc, int c) { return T > 32 * (nc - 1 - c); }
+
+// The forward products run one launch per tile class for short batches
+// (decode: a few rows per expert, where the short classes' extra resident
+// blocks keep more weight loads in flight) and one launch over all tiles
+// otherwise.
+constexpr int kFwdClassLaunchBelowT = 128;
 
 // Persistent grids: blocks_per_cu resident blocks on every compute unit
 // (rounded to a multiple of the 8 XCDs).
@@ -605,7 +613,11 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     float *rs_x = at<float>(ws, L.rs_x), *rs_h = at<float>(ws, L.rs_h);
     float *rt_g = at<float>(ws, L.rt_g), *rt_u = at<float>(ws, L.rt_u), *rt_d = at<float>(ws, L.rt_d);
-    moe::launch_class_tiles(offsets, E, moe::mfma_tile_rows() / 32, tiles_m, ntiles_m, st);
+    const bool by_class = T < kFwdClassLaunchBelowT;
+    if (by_class)
+      moe::launch_class_tiles(offsets, E, moe::mfma_tile_rows() / 32, tiles_m, ntiles_m, st);
+    else
+      moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st, nullptr, 32);
     moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     // An int8 base runs as its two int4 planes along K (packed here unless the
     // caller packed it): twice the reduction, the rows read twice, and start
@@ -662,8 +674,12 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     M.saveU = save ? (uint16_t *)Us : nullptr;
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128 * pm; M.rsum_split = i8;
     const int ncls = moe::mfma_tile_rows() / 32;
-    TIMED(MOE_KT_GATEUP, st, for (int c = 0; c < ncls; ++c) if (class_possible(T, ncls, c))
-                                 moe::launch_grouped_gemm(0, M, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_GATEUP, st, {
+      if (!by_class) moe::launch_grouped_gemm(0, M, ntiles_m, ntiles_m + 8, grid, st);
+      else
+        for (int c = 0; c < ncls; ++c)
+          if (class_possible(T, ncls, c)) moe::launch_grouped_gemm_cls(0, M, ntiles_m, c, grid, st);
+    });
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
     Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
@@ -676,8 +692,12 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     D.qp0 = (const uint8_t *)qf_d;
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
-    TIMED(MOE_KT_DOWN, st, for (int c = 0; c < ncls; ++c) if (class_possible(T, ncls, c))
-                               moe::launch_grouped_gemm(1, D, ntiles_m, c, grid, st));
+    TIMED(MOE_KT_DOWN, st, {
+      if (!by_class) moe::launch_grouped_gemm(1, D, ntiles_m, ntiles_m + 16, grid, st);
+      else
+        for (int c = 0; c < ncls; ++c)
+          if (class_possible(T, ncls, c)) moe::launch_grouped_gemm_cls(1, D, ntiles_m, c, grid, st);
+    });
     return hip_status("moe_expert_fwd");
   }
 

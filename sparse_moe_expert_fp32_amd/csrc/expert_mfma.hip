@@ -164,13 +164,19 @@ DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
 // 130 VGPRs) runs three, the others two
 constexpr int gm_bpc(int NM) { return NM <= 2 ? 3 : GM_BPC; }
 
-// QP: q0, q1 in the stage-major packed layout (launch_pack_fwd)
+// Per-launch values every work item uses.
+struct GmCtx {
+  uint32_t ldsA, ldsB, ldsX;   // LDS byte addresses of the ring arrays
+  uint32_t kMask, kMagic;      // int4 unpack constants (held in registers)
+  int *tok;                    // [GM_BM] LDS: the A row of each tile row
+  float *red;                  // [WAVES][GM_BM] LDS (inside the A ring): row sums
+};
+
+// One work item: rows p0 .. p0 + rows - 1 of expert e (rows <= 16 NM) times
+// column tile nt.  QP: the base in the stage-major packed layout
+// (launch_pack_fwd, A.qp0 / A.qp1), else the storage layout (A.q0 / A.q1).
 template <int MODE, int WAVES, int NM, bool EPL, bool QP>
-__global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_gemm_kernel(
-    const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
-  // (hip-clang passes the second launch bound through as the minimum number
-  // of waves per SIMD: b blocks per CU are b WAVES / 4 waves per SIMD, i.e.
-  // at most 256 VGPRs for two blocks of four waves, 168 for three.)
+DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows, int nt) {
   constexpr int NF = 16 / WAVES;                 // column fragments per wave
   constexpr int BOPS = 8 / WAVES;                // int4-word loads per wave and stage
   constexpr int NT_ = 64 * WAVES;                // threads
@@ -182,32 +188,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
   constexpr auto nfc = [](int nf) {
     return MODE == 0 ? (nf / (NF / 2)) * 128 + (nf % (NF / 2)) * 16 : nf * 16;
   };
-  // a 3-deep ring of half-group stages; after the K loop the first 2 KB of
-  // the A ring hold the cross-wave row sums of H.
-  // (ringA 32-byte aligned: the second substep's chunk is the first's
-  // address with bit 4 flipped)
-  constexpr int ST_A = 16 * NM * GM_KS * 2;     // A stage: the class's rows x 64 K
+  // a 3-deep ring of half-group stages, its A stages 16 NM rows apart; after
+  // the K loop the first 2 KB of the A ring hold the cross-wave row sums of H.
+  constexpr int ST_A = 16 * NM * GM_KS * 2;     // A stage: the tile's rows x 64 K
   static_assert(3 * ST_A >= WAVES * GM_BM * 4, "the row-sum exchange lives in the A ring");
-  __shared__ __attribute__((aligned(32))) uint4 ringA[3][ST_A / 16];
-  __shared__ uint4 ringB[3][ST_B / 16];
-  __shared__ float ringX[3][ST_X / 4];
-  __shared__ int tok_lds[GM_BM];
-
   const int K = A.K, N = A.N, NG = K / GM_KG, NS = 2 * NG;   // NS: half-group stages
   const int NSA = A.ka / GM_KS;   // stages of the A rows (NS, or NS / 2 for an int8 base)
   const int BNO = MODE == 0 ? 128 : 256;   // output columns per item (per matrix)
-  const int total = cls_count[0] * A.NT, tbase = cls_start[0];
-  const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
-  const int wbeg = (int)(((long long)total * xcd) >> 3);
-  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
-  // unpack constants held in registers: each bf16 pair is one shift and one
-  // three-input logic op, ((w >> 4i) & 0x000F000F) ^ 0x43084308
-  const uint32_t kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
-  uint32_t kMagic;
-  asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(kMagic));
-  const uint32_t ldsA = lds_addr(ringA), ldsB = lds_addr(ringB), ldsX = lds_addr(ringX);
-
-  for (int wi = wbeg + bi; wi < wend; wi += nper) {
+  const uint32_t kMask = X.kMask, kMagic = X.kMagic;
+  const uint32_t ldsA = X.ldsA, ldsB = X.ldsB, ldsX = X.ldsX;
+  int *tok_lds = X.tok;
+  {
     // thread indices are re-derived per item through an opaque copy so that
     // the compiler does not keep tid-only address arithmetic live across the
     // whole persistent loop
@@ -215,10 +206,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int ti = wi / A.NT, nt = wi - ti * A.NT;
-    const int2 tile = A.tiles[tbase + ti];
-    const int e = tile.x, p0 = tile.y;
-    const int rows = min(16 * NM, A.offsets[e + 1] - p0);
     const int c0 = nt * BNO;
     __syncthreads();  // LDS of the previous item is free
     for (int t = tid; t < GM_BM; t += NT_) {
@@ -242,8 +229,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
     // BOPS w .. BOPS w + BOPS - 1 (each all gate or all up)
     // (all of a wave's word loads are of one matrix: gate for waves 0-1,
     // up for waves 2-3 in mode 0)
+    const uint8_t *q0 = QP ? A.qp0 : A.q0, *q1 = QP ? A.qp1 : A.q1;
     const uint8_t *qbase =
-        (const uint8_t *)uniform_ptr((MODE == 0 && w >= 2 ? A.q1 : A.q0) + (size_t)e * N * (K / 2));
+        (const uint8_t *)uniform_ptr((MODE == 0 && w >= 2 ? q1 : q0) + (size_t)e * N * (K / 2));
     uint32_t qoff[BOPS];
 #pragma unroll
     for (int i = 0; i < BOPS; ++i) {
@@ -578,7 +566,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
       // reduced over lane groups by shuffles and over the waves through LDS,
       // and stored as the down product's start values -136 * sum.
       __syncthreads();                          // every wave is done with the ring
-      float *red = reinterpret_cast<float *>(ringA);   // [WAVES][128 rows]
+      float *red = X.red;   // [WAVES][128 rows]
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const int r = 16 * m + lr2;
@@ -641,6 +629,87 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 4 * gm_bpc(NM)) void grouped_ge
     }
   }
 }
+
+#define MOE_GM_CTX(ringA, ringB, ringX, tokarr)                     \
+  GmCtx X;                                                          \
+  X.ldsA = lds_addr(ringA);                                         \
+  X.ldsB = lds_addr(ringB);                                         \
+  X.ldsX = lds_addr(ringX);                                         \
+  X.kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);            \
+  asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(X.kMagic));       \
+  X.tok = tokarr;                                                   \
+  X.red = reinterpret_cast<float *>(ringA)
+
+// All items of one product in one launch: the tiles of launch_build_tiles
+// (each expert's rows in tiles of 128, in expert order) times the column
+// tiles, split into eight contiguous ranges, one per XCD, so that an expert's
+// tiles, its short last one included, run close together on one XCD and
+// share its weights in that L2.  Within its range a block draws its next item
+// from a counter of the XCD (ctr[xcd], zero at launch).  Each item runs as the
+// shortest tile class that holds its rows (32, 64, 96 or 128; a wave-uniform
+// branch); the 128-row class reads the storage layout of the base unless P8,
+// the shorter ones the packed layout when PT.  Two blocks of four waves per CU.
+template <int MODE, bool EPL, bool P8, bool PT>
+__global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGemmArgs A,
+                                                                   const int *__restrict__ ntiles,
+                                                                   int *__restrict__ ctr) {
+  // (ringA 32-byte aligned: the second substep's chunk is the first's
+  // address with bit 4 flipped)
+  __shared__ __attribute__((aligned(32))) uint4 ringA[3][GM_BM * GM_KS * 2 / 16];
+  __shared__ uint4 ringB[3][ST_B / 16];
+  __shared__ float ringX[3][ST_X / 4];
+  __shared__ int tok_lds[GM_BM];
+  __shared__ int next_item;
+  MOE_GM_CTX(ringA, ringB, ringX, tok_lds);
+  const int total = ntiles[0] * A.NT;
+  const int xcd = blockIdx.x & 7;
+  const int wbeg = (int)(((long long)total * xcd) >> 3);
+  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
+  if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+  __syncthreads();
+  for (int wi = next_item; wi < wend; wi = next_item) {
+    // every thread has read next_item; the next draw overlaps this item (its
+    // value is visible after the item's first barrier)
+    __syncthreads();
+    if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+    const int ti = wi / A.NT, nt = wi - ti * A.NT;
+    const int2 tile = A.tiles[ti];
+    const int e = tile.x, p0 = tile.y;
+    const int rows = min(GM_BM, A.offsets[e + 1] - p0);
+    const int cls = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);   // 32-row units
+    if (cls >= 4) gm_item<MODE, 4, 8, EPL, P8>(A, X, e, p0, rows, nt);
+    else if (cls == 3) gm_item<MODE, 4, 6, EPL, PT>(A, X, e, p0, rows, nt);
+    else if (cls == 2) gm_item<MODE, 4, 4, EPL, PT>(A, X, e, p0, rows, nt);
+    else gm_item<MODE, 4, 2, EPL, PT>(A, X, e, p0, rows, nt);
+  }
+}
+
+// One tile class per launch (tiles of launch_class_tiles), for short
+// batches: the ring holds only the class's rows, so the short classes run
+// more blocks per CU (gm_bpc), which keeps more weight loads in flight where
+// the products stream the weights of many experts for a few rows each.
+template <int MODE, int NM, bool EPL, bool QP>
+__global__ __launch_bounds__(256, gm_bpc(NM)) void grouped_gemm_cls_kernel(
+    const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
+  constexpr int ST_A = 16 * NM * GM_KS * 2;
+  __shared__ __attribute__((aligned(32))) uint4 ringA[3][ST_A / 16];
+  __shared__ uint4 ringB[3][ST_B / 16];
+  __shared__ float ringX[3][ST_X / 4];
+  __shared__ int tok_lds[GM_BM];
+  MOE_GM_CTX(ringA, ringB, ringX, tok_lds);
+  const int total = cls_count[0] * A.NT, tbase = cls_start[0];
+  const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int wbeg = (int)(((long long)total * xcd) >> 3);
+  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
+  for (int wi = wbeg + bi; wi < wend; wi += nper) {
+    const int ti = wi / A.NT, nt = wi - ti * A.NT;
+    const int2 tile = A.tiles[tbase + ti];
+    const int e = tile.x, p0 = tile.y;
+    const int rows = min(16 * NM, A.offsets[e + 1] - p0);
+    gm_item<MODE, 4, NM, EPL, QP>(A, X, e, p0, rows, nt);
+  }
+}
+#undef MOE_GM_CTX
 
 // ------------------------------------------------------ forward packing --
 // q [E][N][K/2] -> [E][K/64][N][32 B]: each 32-byte K block of a storage row
@@ -790,27 +859,48 @@ void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, 
   build_class_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, nclass, tiles, cnt);
 }
 
-// The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32); cnt as
-// written by launch_class_tiles.
-void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
+// One launch per product over the tiles of launch_build_tiles (ctr: eight
+// zeroed counters).  Mode 1 and the short tiles of mode 0 read the packed
+// base where it is given; the 128-row tiles of mode 0 read the storage layout
+// (the packed reads need more registers there) unless the base has none (an
+// int8 base: q0 null).
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int *ctr, int grid,
                          hipStream_t st) {
+  // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
+  const bool epl = A.r == 16 && (A.ldz & 3) == 0;
+  const bool pt = A.qp0 && (mode == 1 || A.qp1);
+  const bool p8 = pt && (mode == 1 || !A.q0);
+#define MOE_GG3(MODE, EPL)                                                                   \
+  do {                                                                                       \
+    if (p8) grouped_gemm_kernel<MODE, EPL, true, true><<<grid, 256, 0, st>>>(A, ntiles, ctr);   \
+    else if (pt) grouped_gemm_kernel<MODE, EPL, false, true><<<grid, 256, 0, st>>>(A, ntiles, ctr); \
+    else grouped_gemm_kernel<MODE, EPL, false, false><<<grid, 256, 0, st>>>(A, ntiles, ctr);  \
+  } while (0)
+  if (mode == 0) {
+    if (epl) MOE_GG3(0, true); else MOE_GG3(0, false);
+  } else {
+    if (epl) MOE_GG3(1, true); else MOE_GG3(1, false);
+  }
+#undef MOE_GG3
+}
+
+// The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32) of
+// launch_class_tiles (cnt: counts and first indices).
+void launch_grouped_gemm_cls(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
+                             hipStream_t st) {
   const int *c = cnt + cls, *s = cnt + 4 + cls;
   // grid: GM_BPC blocks per CU; the 32-row class runs gm_bpc(2) per CU
   if (cls == 3) grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
-  // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
-  // the packed base where given and used (P.q0 null: plain layout)
-  MfmaGemmArgs P = A;
-  // (an int8 base has only the packed layout: q0 null)
-  const bool use_p = A.qp0 && (mode == 1 || (A.qp1 && (cls != 0 || !A.q0)));
-  P.q0 = use_p ? A.qp0 : nullptr;
-  P.q1 = use_p ? A.qp1 : nullptr;
-#define MOE_GG2(MODE, NM, QP)                                                        \
-  if (epl) grouped_gemm_kernel<MODE, 4, NM, true, QP><<<grid, 256, 0, st>>>(QP ? P : A, c, s);  \
-  else grouped_gemm_kernel<MODE, 4, NM, false, QP><<<grid, 256, 0, st>>>(QP ? P : A, c, s)
+  // the packed base where given and used (an int8 base has only the packed
+  // layout: q0 null)
+  const bool qp = A.qp0 && (mode == 1 || (A.qp1 && (cls != 0 || !A.q0)));
+#define MOE_GG2(MODE, NM, QP)                                                                 \
+  if (epl) grouped_gemm_cls_kernel<MODE, NM, true, QP><<<grid, 256, 0, st>>>(A, c, s);         \
+  else grouped_gemm_cls_kernel<MODE, NM, false, QP><<<grid, 256, 0, st>>>(A, c, s)
 #define MOE_GG(MODE, NM)                                                \
   do {                                                                  \
-    if (P.q0) { MOE_GG2(MODE, NM, true); } else { MOE_GG2(MODE, NM, false); } \
+    if (qp) { MOE_GG2(MODE, NM, true); } else { MOE_GG2(MODE, NM, false); } \
   } while (0)
   if (mode == 0) {
     if (cls == 0) MOE_GG(0, 8); else if (cls == 1) MOE_GG(0, 6); else if (cls == 2) MOE_GG(0, 4); else MOE_GG(0, 2);

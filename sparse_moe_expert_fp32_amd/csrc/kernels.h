@@ -133,9 +133,15 @@ void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStre
 // ([E][2K/64][N][32 B]): q = 16 h + l, plane 1 holds h = q >> 4, plane 2
 // l - 8 (l = q & 15), each as a two's-complement nibble
 void launch_pack_fwd_int8(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st);
-// the launch of tile class cls (0: 128-row tiles .. 3: 32-row tiles)
-void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
+// one launch over the tiles of launch_build_tiles (mfma_tile_rows() rows, in
+// expert order), each item as the shortest tile class holding its rows (ctr:
+// eight counters, zero at launch)
+void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int *ctr, int grid,
                          hipStream_t st);
+// the launch of tile class cls of launch_class_tiles (0: 128-row tiles ..
+// 3: 32-row tiles; cnt: counts and first indices), for short batches
+void launch_grouped_gemm_cls(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
+                             hipStream_t st);
 
 // transposed-base products of the backward (expert_mfma_bwd.hip)
 struct MfmaGemmTArgs {
