@@ -647,9 +647,9 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
 // share its weights in that L2.  Within its range a block draws its next item
 // from a counter of the XCD (ctr[xcd], zero at launch).  Each item runs as the
 // shortest tile class that holds its rows (32, 64, 96 or 128; a wave-uniform
-// branch); the 128-row class reads the storage layout of the base unless P8,
-// the shorter ones the packed layout when PT.  Two blocks of four waves per CU.
-template <int MODE, bool EPL, bool P8, bool PT>
+// branch).  QP: the base in the packed layout.  Two blocks of four waves per
+// CU.
+template <int MODE, bool EPL, bool QP>
 __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGemmArgs A,
                                                                    const int *__restrict__ ntiles,
                                                                    int *__restrict__ ctr) {
@@ -677,10 +677,10 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
     const int e = tile.x, p0 = tile.y;
     const int rows = min(GM_BM, A.offsets[e + 1] - p0);
     const int cls = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);   // 32-row units
-    if (cls >= 4) gm_item<MODE, 4, 8, EPL, P8>(A, X, e, p0, rows, nt);
-    else if (cls == 3) gm_item<MODE, 4, 6, EPL, PT>(A, X, e, p0, rows, nt);
-    else if (cls == 2) gm_item<MODE, 4, 4, EPL, PT>(A, X, e, p0, rows, nt);
-    else gm_item<MODE, 4, 2, EPL, PT>(A, X, e, p0, rows, nt);
+    if (cls >= 4) gm_item<MODE, 4, 8, EPL, QP>(A, X, e, p0, rows, nt);
+    else if (cls == 3) gm_item<MODE, 4, 6, EPL, QP>(A, X, e, p0, rows, nt);
+    else if (cls == 2) gm_item<MODE, 4, 4, EPL, QP>(A, X, e, p0, rows, nt);
+    else gm_item<MODE, 4, 2, EPL, QP>(A, X, e, p0, rows, nt);
   }
 }
 
@@ -860,21 +860,17 @@ void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, 
 }
 
 // One launch per product over the tiles of launch_build_tiles (ctr: eight
-// zeroed counters).  Mode 1 and the short tiles of mode 0 read the packed
-// base where it is given; the 128-row tiles of mode 0 read the storage layout
-// (the packed reads need more registers there) unless the base has none (an
-// int8 base: q0 null).
+// zeroed counters), reading the packed base where it is given (both matrices
+// of gate/up, or down).
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int *ctr, int grid,
                          hipStream_t st) {
   // operands of the epilogue through the LDS ring: rank 16, Z rows 16-byte aligned
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
-  const bool pt = A.qp0 && (mode == 1 || A.qp1);
-  const bool p8 = pt && (mode == 1 || !A.q0);
-#define MOE_GG3(MODE, EPL)                                                                   \
-  do {                                                                                       \
-    if (p8) grouped_gemm_kernel<MODE, EPL, true, true><<<grid, 256, 0, st>>>(A, ntiles, ctr);   \
-    else if (pt) grouped_gemm_kernel<MODE, EPL, false, true><<<grid, 256, 0, st>>>(A, ntiles, ctr); \
-    else grouped_gemm_kernel<MODE, EPL, false, false><<<grid, 256, 0, st>>>(A, ntiles, ctr);  \
+  const bool qp = A.qp0 && (mode == 1 || A.qp1);
+#define MOE_GG3(MODE, EPL)                                                                 \
+  do {                                                                                     \
+    if (qp) grouped_gemm_kernel<MODE, EPL, true><<<grid, 256, 0, st>>>(A, ntiles, ctr);      \
+    else grouped_gemm_kernel<MODE, EPL, false><<<grid, 256, 0, st>>>(A, ntiles, ctr);        \
   } while (0)
   if (mode == 0) {
     if (epl) MOE_GG3(0, true); else MOE_GG3(0, false);
@@ -892,9 +888,8 @@ void launch_grouped_gemm_cls(int mode, const MfmaGemmArgs &A, const int *cnt, in
   // grid: GM_BPC blocks per CU; the 32-row class runs gm_bpc(2) per CU
   if (cls == 3) grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
-  // the packed base where given and used (an int8 base has only the packed
-  // layout: q0 null)
-  const bool qp = A.qp0 && (mode == 1 || (A.qp1 && (cls != 0 || !A.q0)));
+  // the packed base where given
+  const bool qp = A.qp0 && (mode == 1 || A.qp1);
 #define MOE_GG2(MODE, NM, QP)                                                                 \
   if (epl) grouped_gemm_cls_kernel<MODE, NM, true, QP><<<grid, 256, 0, st>>>(A, c, s);         \
   else grouped_gemm_cls_kernel<MODE, NM, false, QP><<<grid, 256, 0, st>>>(A, c, s)

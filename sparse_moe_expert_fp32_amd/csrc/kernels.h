@@ -100,9 +100,8 @@ struct MfmaGemmArgs {
   const uint8_t *q0; const float *rt0; const uint16_t *B0;   // gate (mode 0) / down (mode 1)
   const uint8_t *q1; const float *rt1; const uint16_t *B1;   // up (mode 0)
   const float *Z0, *Z1; int ldz; int r; float lam;             // X A^T projections (float32)
-  // q0, q1 in the stage-major layout of launch_pack_fwd (or null): used by
-  // the launches the layout speeds up (mode 1, and the short tile classes of
-  // mode 0, whose 128-row kernel needs more registers with it)
+  // q0, q1 in the stage-major layout of launch_pack_fwd (or null; mode 0
+  // reads it only when both matrices have it)
   const uint8_t *qp0, *qp1;
   uint16_t *out; int ldo;                 // H [S][f] (mode 0) or e_out [S][d] (mode 1)
   uint16_t *saveG, *saveU;                // mode 0, optional: U s (1 + G (1 - s)), G s (s = sigmoid G)
