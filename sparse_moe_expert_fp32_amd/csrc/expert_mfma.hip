@@ -12,7 +12,7 @@
 //  * Work items (M-tile, N-tile) are processed by a persistent grid.  Each of
 //    the 8 XCDs takes a contiguous eighth of the item list, so the rows and
 //    weights of neighbouring tiles stay in that XCD's L2.
-//  * K streams through a 3-deep LDS ring in half-group stages (64 of K): the
+//  * K streams through a 2-slot LDS ring in half-group stages (64 of K): the
 //    A rows (x gathered by token, or H), the int4 words of the block's 256
 //    columns and, per group, the per-row start values and per-column scale
 //    ratios, all by LDS-DMA (global_load_lds_*).  The stage after the last
@@ -160,9 +160,10 @@ DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
 // from LDS feeds four matrix instructions).  NM (2, 4, 6, 8) is the number of
 // 16-row fragments of the item's tile class: each class of tiles (32, 64, 96,
 // 128 rows) is its own launch, so a short tail tile costs only its rows.
-// blocks per CU of tile class NM: the 32-row class (A ring of 12 KB, about
-// 130 VGPRs) runs three, the others two
-constexpr int gm_bpc(int NM) { return NM <= 2 ? 3 : GM_BPC; }
+// blocks per CU of the class launches of tile class NM, as the registers
+// allow: the 32-row class (2-slot ring of 28 KB, at most 128 VGPRs) four,
+// the others two
+constexpr int gm_bpc(int NM) { return NM <= 2 ? 4 : GM_BPC; }
 
 // Per-launch values every work item uses.
 struct GmCtx {
@@ -188,10 +189,10 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
   constexpr auto nfc = [](int nf) {
     return MODE == 0 ? (nf / (NF / 2)) * 128 + (nf % (NF / 2)) * 16 : nf * 16;
   };
-  // a 3-deep ring of half-group stages, its A stages 16 NM rows apart; after
+  // a 2-slot ring of half-group stages, its A stages 16 NM rows apart; after
   // the K loop the first 2 KB of the A ring hold the cross-wave row sums of H.
   constexpr int ST_A = 16 * NM * GM_KS * 2;     // A stage: the tile's rows x 64 K
-  static_assert(3 * ST_A >= WAVES * GM_BM * 4, "the row-sum exchange lives in the A ring");
+  static_assert(2 * ST_A >= WAVES * GM_BM * 4, "the row-sum exchange lives in the A ring");
   const int K = A.K, N = A.N, NG = K / GM_KG, NS = 2 * NG;   // NS: half-group stages
   const int NSA = A.ka / GM_KS;   // stages of the A rows (NS, or NS / 2 for an int8 base)
   const int BNO = MODE == 0 ? 128 : 256;   // output columns per item (per matrix)
@@ -412,36 +413,31 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // 3-deep ring: step j computes from slot j % 3 while the loads of stage
-    // j + 2 (issued at the start of the step) are in flight; at the end of
-    // the step every wave waits for all of its loads and the block syncs, so
-    // stage j + 1 is in LDS when step j + 1 starts and slot j % 3 is free for
-    // stage j + 3.  The loop runs in groups of six stages (three ring slots,
-    // two parities); stages past the end compute nothing (uniform branch)
-    // but still issue their (clamped) loads.
+    // Two-slot ring: step j computes stage j from slot j % 2 while the loads
+    // of stage j + 1 (issued at the start of the step) fill the other slot;
+    // at the end of the step every wave waits for all of its loads and the
+    // block syncs, so stage j + 1 is in LDS when step j + 1 starts.  (A
+    // deeper ring would not let loads run longer: the end-of-step wait
+    // covers everything issued in the step.)  Stages come in pairs (NS is
+    // even), the even one a group's first; the step after the last loads the
+    // epilogue's operands (rank 16).
     using even_t = std::integral_constant<bool, false>;
     using odd_t = std::integral_constant<bool, true>;
     using ev_t = std::integral_constant<bool, true>;
     using od_t = std::integral_constant<bool, false>;
     stage(ev_t(), 0, 0);
-    stage(od_t(), 1, 1);
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     block_barrier();
-    for (int j = 0; j < NS; j += 6) {
+    for (int j = 0; j < NS; j += 2) {
 #define MOE_F_STEP(JJ, PAR, LD, CUR, NXT)       \
   {                                             \
-    const int jj = (JJ);                        \
-    stage(LD(), jj + 2, NXT);                   \
-    if (jj < NS) compute(PAR(), CUR);           \
-    __builtin_amdgcn_s_waitcnt(kWaitVm); \
+    stage(LD(), (JJ) + 1, NXT);                 \
+    compute(PAR(), CUR);                        \
+    __builtin_amdgcn_s_waitcnt(kWaitVm);        \
     block_barrier();                            \
   }
-      MOE_F_STEP(j, even_t, ev_t, 0, 2)
-      MOE_F_STEP(j + 1, odd_t, od_t, 1, 0)
-      MOE_F_STEP(j + 2, even_t, ev_t, 2, 1)
-      MOE_F_STEP(j + 3, odd_t, od_t, 0, 2)
-      MOE_F_STEP(j + 4, even_t, ev_t, 1, 0)
-      MOE_F_STEP(j + 5, odd_t, od_t, 2, 1)
+      MOE_F_STEP(j, even_t, od_t, 0, 1)
+      MOE_F_STEP(j + 1, odd_t, ev_t, 1, 0)
 #undef MOE_F_STEP
     }
 
@@ -464,7 +460,7 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
     // ---- the last group's scale (group 0's ratio) and the adapter term
     // acc += (lam Z) B^T, K = rank in steps of 16 (mode 0: gate fragments
     // take Z_g and B_g, up fragments Z_u and B_u).  Rank 16: all operands
-    // from the epilogue stage in ring slot NS % 3, one row fragment at a
+    // from the epilogue stage in ring slot NS % 2, one row fragment at a
     // time; otherwise from global memory.
     constexpr int NSRC = MODE == 0 ? 2 : 1;
     auto zbf = [&](f32x4_t z) {   // lam z rounded to bf16 (nearest even)
@@ -473,7 +469,7 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       return __builtin_bit_cast(short4_t, u32x2_t{lo, hi});
     };
     if constexpr (ep_lds) {
-      const int es = NS % 3;
+      const int es = NS % 2;
       const int wc = w2 * WCOLS;   // the wave's first block column slot
       short4_t bv[NF];
 #pragma unroll
@@ -655,9 +651,9 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
                                                                    int *__restrict__ ctr) {
   // (ringA 32-byte aligned: the second substep's chunk is the first's
   // address with bit 4 flipped)
-  __shared__ __attribute__((aligned(32))) uint4 ringA[3][GM_BM * GM_KS * 2 / 16];
-  __shared__ uint4 ringB[3][ST_B / 16];
-  __shared__ float ringX[3][ST_X / 4];
+  __shared__ __attribute__((aligned(32))) uint4 ringA[2][GM_BM * GM_KS * 2 / 16];
+  __shared__ uint4 ringB[2][ST_B / 16];
+  __shared__ float ringX[2][ST_X / 4];
   __shared__ int tok_lds[GM_BM];
   __shared__ int next_item;
   MOE_GM_CTX(ringA, ringB, ringX, tok_lds);
@@ -692,9 +688,9 @@ template <int MODE, int NM, bool EPL, bool QP>
 __global__ __launch_bounds__(256, gm_bpc(NM)) void grouped_gemm_cls_kernel(
     const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
   constexpr int ST_A = 16 * NM * GM_KS * 2;
-  __shared__ __attribute__((aligned(32))) uint4 ringA[3][ST_A / 16];
-  __shared__ uint4 ringB[3][ST_B / 16];
-  __shared__ float ringX[3][ST_X / 4];
+  __shared__ __attribute__((aligned(32))) uint4 ringA[2][ST_A / 16];
+  __shared__ uint4 ringB[2][ST_B / 16];
+  __shared__ float ringX[2][ST_X / 4];
   __shared__ int tok_lds[GM_BM];
   MOE_GM_CTX(ringA, ringB, ringX, tok_lds);
   const int total = cls_count[0] * A.NT, tbase = cls_start[0];
