@@ -9,9 +9,10 @@ State-Preserving Scaling", abstract; hidden sizes are this library's).
 
 Prints one JSON line.  `value` is tokens/s of the timed steps with every input
 already resident in device memory.  `roofline` reports the longest of the four
-int4 expert-GEMM stages per step (each stage is four launches, one per tile
-class, timed as one span with HIP events on the launch stream) against the
-bf16 matrix-core peak; `stages` lists all four.  `decode` measures the
+int4 expert-GEMM stages per step (each stage is one launch at this batch size,
+timed with HIP events on the launch stream) against the bf16 matrix-core
+peak; `stages` lists all four, and `traffic` comes from the committed
+FETCH_SIZE/WRITE_SIZE summary of that stage while the kernel sources match.  `decode` measures the
 T=64 forward (the weight-streaming shape) against HBM bandwidth, with the
 device caches scrubbed before every timed forward; `decode_int8` the same
 with an int8 base (twice the weight bytes).  `cpu_baseline` times the
@@ -248,8 +249,9 @@ def main():
     log(f"{ms:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
 
     # each int4 expert-GEMM stage timed on its own pass over K more steps:
-    # the library brackets the stage (its four tile-class launches, back to
-    # back on the launch stream) with a pair of HIP events
+    # the library brackets the stage (one launch; for short batches its
+    # tile-class launches, back to back on the launch stream) with a pair of
+    # HIP events
     stages = []
     for tag, name, flops_slot in gemm_stages(cfg, cfg.train):
         B.moe_timer_start(tag)
@@ -369,9 +371,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": dom["frac"], "traffic": traffic,
                      "kernel": dom["kernel"] + ", the longest stage per step",
-                     "kernel_ms": dom["ms"], "launches_per_step": 4,
-                     "timed_as": "one event pair around the stage's four tile-class launches "
-                                 "(128/96/64/32-row tiles), once per step",
+                     "kernel_ms": dom["ms"],
+                     # one launch per stage from 128 tokens; below, one per
+                     # tile class that can hold a tile (no expert has more than T rows)
+                     "launches_per_step": 1 if cfg.T >= 128 else
+                     sum(1 for c in range(4) if cfg.T > 32 * (3 - c)),
+                     "timed_as": "one HIP event pair on the launch stream around the stage's "
+                                 "launch, once per step, averaged over the steps",
                      "flops_per_launch": dom["flops"]},
         "stages": stages,
         "decode": decode,
