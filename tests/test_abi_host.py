@@ -35,6 +35,8 @@ def test_library_exports_every_declared_symbol(B):
         assert hasattr(lib, name), name
     assert set(declared_functions()) == set(B.EXPORTS)
     assert B.moe_abi_version() == 4
+    import __graft_entry__
+    assert __graft_entry__.header_abi_version() == B.moe_abi_version()
 
 
 def good(B, **kw):
