@@ -249,9 +249,7 @@ def main():
     log(f"{ms:.3f} ms/step, {tokens_per_s:.4g} tokens/s")
 
     # each int4 expert-GEMM stage timed on its own pass over K more steps:
-    # the library brackets the stage (one launch; for short batches its
-    # tile-class launches, back to back on the launch stream) with a pair of
-    # HIP events
+    # the library brackets the stage (one launch) with a pair of HIP events
     stages = []
     for tag, name, flops_slot in gemm_stages(cfg, cfg.train):
         B.moe_timer_start(tag)
@@ -372,10 +370,7 @@ def main():
                      "unit": "TFLOP/s", "frac": dom["frac"], "traffic": traffic,
                      "kernel": dom["kernel"] + ", the longest stage per step",
                      "kernel_ms": dom["ms"],
-                     # one launch per stage from 128 tokens; below, one per
-                     # tile class that can hold a tile (no expert has more than T rows)
-                     "launches_per_step": 1 if cfg.T >= 128 else
-                     sum(1 for c in range(4) if cfg.T > 32 * (3 - c)),
+                     "launches_per_step": 1,
                      "timed_as": "one HIP event pair on the launch stream around the stage's "
                                  "launch, once per step, averaged over the steps",
                      "flops_per_launch": dom["flops"]},

@@ -126,6 +126,16 @@ size_t qt_slot_bytes(const moe_dims *d) {
 }
 size_t qf_bytes(const moe_dims *d) { return qt_slot_bytes(d); }
 
+// The forward products of short batches (decode: a few rows per expert) run
+// every expert's rows in tiles of 32 in a kernel that holds only 32 rows, so
+// more of its blocks are resident and keep more weight loads in flight; from
+// 128 tokens they run tiles of 128, each as the shortest class that holds its
+// rows.  Either way one launch per product.
+constexpr int kFwdShortBelowT = 128;
+int fwd_tile_rows(const moe_dims *d) {
+  return d->T < kFwdShortBelowT ? 32 : moe::mfma_tile_rows();
+}
+
 // ---- expert forward workspace
 struct FwdLayout {
   size_t tiles, ntiles, save, G32, U32, tiles_m, ntiles_m, tiles_p, ntiles_p, rs_x, rs_h, rt_g,
@@ -139,11 +149,10 @@ struct FwdLayout {
     save = ws_save_given(flags) ? 0 : c.take(SaveLayout(d).total);
     if (use_mfma(d)) {
       G32 = U32 = 0;
-      tiles_m = c.take(max_tiles(d, moe::mfma_tile_rows()) * sizeof(int2));
-      // (class counts and starts, or the tile count and eight work counters
-      // for each of the two products)
+      tiles_m = c.take(max_tiles(d, fwd_tile_rows(d)) * sizeof(int2));
+      // (the tile count and eight work counters for each of the two products)
       ntiles_m = c.take(32 * sizeof(int));
-      tiles_p = c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2));
+      tiles_p = c.take(max_tiles(d, moe::proj_tile_rows(d->T < kFwdShortBelowT)) * sizeof(int2));
       ntiles_p = c.take(sizeof(int));
       const size_t pm = plane_mult(d);
       rs_x = c.take((size_t)d->T * (dm / 128) * 4 * pm);
@@ -163,19 +172,6 @@ struct FwdLayout {
     total = c.off;
   }
 };
-
-// Whether tile class c (of nc; tiles of 32 (nc - c) rows, the partial last
-// tile of an expert rounded up to a multiple of 32) can hold any tile: every
-// token is routed to k distinct experts, so no expert has more than T rows,
-// and class c needs an expert with more than 32 (nc - 1 - c).  Short batches
-// (decode) skip the launches of the tall classes.
-bool class_possible(int T, int nc, int c) { return T > 32 * (nc - 1 - c); }
-
-// The forward products run one launch per tile class for short batches
-// (decode: a few rows per expert, where the short classes' extra resident
-// blocks keep more weight loads in flight) and one launch over all tiles
-// otherwise.
-constexpr int kFwdClassLaunchBelowT = 128;
 
 // Persistent grids: blocks_per_cu resident blocks on every compute unit
 // (rounded to a multiple of the 8 XCDs).
@@ -608,24 +604,25 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
   P.m_es = (size_t)r * d; P.m_cs = 1; P.m_js = d; P.K = d; P.r = r; P.s = 1.f; P.ldz = 3 * r;
 
   if (use_mfma(dims)) {
+    const bool short_t = T < kFwdShortBelowT;
     int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
-    const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
+    const int mtp = (int)max_tiles(dims, moe::proj_tile_rows(short_t));
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
     float *rs_x = at<float>(ws, L.rs_x), *rs_h = at<float>(ws, L.rs_h);
     float *rt_g = at<float>(ws, L.rt_g), *rt_u = at<float>(ws, L.rt_u), *rt_d = at<float>(ws, L.rt_d);
-    const bool by_class = T < kFwdClassLaunchBelowT;
-    if (by_class)
-      moe::launch_class_tiles(offsets, E, moe::mfma_tile_rows() / 32, tiles_m, ntiles_m, st);
-    else
-      moe::launch_build_tiles(offsets, E, moe::mfma_tile_rows(), tiles_m, ntiles_m, st, nullptr, 32);
-    moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
     // An int8 base runs as its two int4 planes along K (packed here unless the
     // caller packed it): twice the reduction, the rows read twice, and start
     // values -136 (first plane) and -128 (second) times the group sums.
     const bool i8 = base_bits(dims) == 8;
     const int pm = plane_mult(dims);
-    // per-row start values -136 * (row sum per group) and per-column scale ratios
-    moe::launch_group_rowsum(x, T, d, 128, -136.f, rs_x, st, i8, -128.f);
+    // set-up in one launch: the products' tile list (zeroing their work
+    // counters), the projections' tile list, and the per-row start values
+    // -136 * (row sum per group)
+    moe::PrepBatch pb;
+    pb.tiles(offsets, E, fwd_tile_rows(dims), tiles_m, ntiles_m, nullptr, 32);
+    pb.tiles(offsets, E, moe::proj_tile_rows(short_t), tiles_p, ntiles_p);
+    pb.rowsum(x, T, d, 128, -136.f, rs_x, i8, -128.f);
+    moe::launch_prep(pb, st);
     const void *qf_g = gate.qf, *qf_u = up.qf, *qf_d = down.qf;
     if (i8) {
       auto pack = [&](const moe_qlora &m, int N, int K, float *buf) {
@@ -656,7 +653,7 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 2;
     Q.m0 = (const uint16_t *)gate.A; Q.m1 = (const uint16_t *)up.A; Q.scale = 1.f;
     Q.Z0 = Z; Q.Z1 = Z + r; Q.ldz = 3 * r;
-    moe::launch_proj_mfma(Q, mtp, true, st);
+    moe::launch_proj_mfma(Q, mtp, true, st, short_t);
     const int grid = persistent_grid(moe::mfma_blocks_per_cu());
     moe::MfmaGemmArgs M{};
     M.a = x; M.lda = d; M.perm_src = perm_src; M.kk = k; M.rsum = rs_x; M.ld_rsum = d / 128 * pm;
@@ -673,17 +670,14 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     M.saveG = save ? (uint16_t *)Gs : nullptr;
     M.saveU = save ? (uint16_t *)Us : nullptr;
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128 * pm; M.rsum_split = i8;
-    const int ncls = moe::mfma_tile_rows() / 32;
     TIMED(MOE_KT_GATEUP, st, {
-      if (!by_class) moe::launch_grouped_gemm(0, M, ntiles_m, ntiles_m + 8, grid, st);
-      else
-        for (int c = 0; c < ncls; ++c)
-          if (class_possible(T, ncls, c)) moe::launch_grouped_gemm_cls(0, M, ntiles_m, c, grid, st);
+      if (short_t) moe::launch_grouped_gemm_short(0, M, ntiles_m, grid, st);
+      else moe::launch_grouped_gemm(0, M, ntiles_m, ntiles_m + 8, grid, st);
     });
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
     Q.m1 = nullptr; Q.Z0 = Z + 2 * r; Q.Z1 = nullptr;
-    moe::launch_proj_mfma(Q, mtp, false, st);
+    moe::launch_proj_mfma(Q, mtp, false, st, short_t);
     moe::MfmaGemmArgs D{};
     D.a = H; D.lda = f; D.rsum = rs_h; D.ld_rsum = f / 128 * pm;
     D.tiles = tiles_m; D.offsets = offsets;
@@ -693,10 +687,8 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     D.Z0 = Z + 2 * r; D.ldz = 3 * r; D.r = r; D.lam = lam;
     D.out = (uint16_t *)e_out; D.ldo = d;
     TIMED(MOE_KT_DOWN, st, {
-      if (!by_class) moe::launch_grouped_gemm(1, D, ntiles_m, ntiles_m + 16, grid, st);
-      else
-        for (int c = 0; c < ncls; ++c)
-          if (class_possible(T, ncls, c)) moe::launch_grouped_gemm_cls(1, D, ntiles_m, c, grid, st);
+      if (short_t) moe::launch_grouped_gemm_short(1, D, ntiles_m, grid, st);
+      else moe::launch_grouped_gemm(1, D, ntiles_m, ntiles_m + 16, grid, st);
     });
     return hip_status("moe_expert_fwd");
   }
@@ -804,35 +796,46 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
 
   // gate path: W_r^T for the router-input gradient; the float32 kernels also
   // take dO from this pass, the matrix-core path runs it last (below)
-  moe::launch_transpose_f32(w_router, d, E, wr_t, st);
-  if (!use_mfma(dims))
+  if (!use_mfma(dims)) {
+    moe::launch_transpose_f32(w_router, d, E, wr_t, st);
     TIMED(MOE_KT_GATE_GRAD, st,
           moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, E, dx_r,
                                 dO, st));
+  }
 
   if (use_mfma(dims)) {
     int2 *tiles_m = at<int2>(ws, L.tiles_m), *tiles_p = at<int2>(ws, L.tiles_p);
     int *ntiles_m = at<int>(ws, L.ntiles_m), *ntiles_p = at<int>(ws, L.ntiles_p);
+    int2 *tiles_w = at<int2>(ws, L.tiles_w);
+    int *ntiles_w = at<int>(ws, L.ntiles_w);
     const int grid = persistent_grid(moe::mfma_t_blocks_per_cu());
     const int mtp = (int)max_tiles(dims, moe::proj_tile_rows());
-    moe::launch_build_tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, st, nullptr, 32);
-    moe::launch_build_tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p, st);
+    const int mtw = (int)max_tiles(dims, moe::wgrad_tile_rows());
     uint16_t *bt_d = at<uint16_t>(ws, L.bt);
     uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
-    moe::launch_transpose_nr(down.B, E, d, r, bt_d, st);
-    moe::launch_transpose_nr(gate.B, E, f, r, bt_g, st);
-    moe::launch_transpose_nr(up.B, E, f, r, bt_u, st);
-    // A of each matrix as [E][N][r] for the epilogue stages of the
-    // input-gradient products (rank 16)
     uint16_t *lt_d = nullptr, *lt_g = nullptr, *lt_u = nullptr;
+    // set-up in one launch: W_r^T; the tile lists of the input-gradient
+    // products (zeroing their work counters), of the projections and of the
+    // adapter-gradient reductions (with the experts they split); B of each
+    // matrix as [E][r][N]; A of each matrix as [E][N][r] for the epilogue
+    // stages of the input-gradient products (rank 16)
+    moe::PrepBatch pb;
+    pb.transpose_f32(w_router, d, E, wr_t);
+    pb.tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, nullptr, 32);
+    pb.tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p);
+    pb.tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, ntiles_w + 1);
+    pb.transpose_nr(down.B, E, d, r, bt_d, st);
+    pb.transpose_nr(gate.B, E, f, r, bt_g, st);
+    pb.transpose_nr(up.B, E, f, r, bt_u, st);
     if (r == 16) {
       lt_d = at<uint16_t>(ws, L.lt);
       lt_g = lt_d + (size_t)E * r * f;
       lt_u = lt_g + (size_t)E * r * d;
-      moe::launch_transpose_rn(down.A, E, r, f, lt_d, st);
-      moe::launch_transpose_rn(gate.A, E, r, d, lt_g, st);
-      moe::launch_transpose_rn(up.A, E, r, d, lt_u, st);
+      pb.transpose_rn(down.A, E, r, f, lt_d, st);
+      pb.transpose_rn(gate.A, E, r, d, lt_g, st);
+      pb.transpose_rn(up.A, E, r, d, lt_u, st);
     }
+    moe::launch_prep(pb, st);
     // An int8 base runs as its two int4 planes stacked along N: twice the
     // reduction, the rows read twice (transposed here unless the caller packed it)
     const bool i8 = base_bits(dims) == 8;
@@ -854,10 +857,6 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     moe::launch_proj_mfma(Q, mtp, true, st);
     Q.gsc = nullptr;
     // dB_d [d][r] = lam sum_p dO[p][n] Z_d[p][j]
-    int2 *tiles_w = at<int2>(ws, L.tiles_w);
-    int *ntiles_w = at<int>(ws, L.ntiles_w);
-    const int mtw = (int)max_tiles(dims, moe::wgrad_tile_rows());
-    moe::launch_build_tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, st, ntiles_w + 1);
     moe::WgradMArgs W{};
     W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r; W.nsrc = 1;
     W.tiles = tiles_w; W.ntiles = ntiles_w; W.tfirst = ntiles_w + 1; W.multi = ntiles_w + 1 + E;

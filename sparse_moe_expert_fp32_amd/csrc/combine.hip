@@ -13,6 +13,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "prep.h"
 
 namespace moe {
 
@@ -75,18 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ e_ou
 // columns are read with unit stride)
 __global__ void transpose_f32_kernel(const float *__restrict__ in, int rows, int cols,
                                      float *__restrict__ out) {
-  __shared__ float tile[32][33];
-  int bx = blockIdx.x * 32, by = blockIdx.y * 32;
-  int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
-  for (int i = ty; i < 32; i += 8) {
-    int r = by + i, c = bx + tx;
-    tile[i][tx] = (r < rows && c < cols) ? in[(size_t)r * cols + c] : 0.f;
-  }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    int r = bx + i, c = by + tx;  // out row = input column
-    if (r < cols && c < rows) out[(size_t)r * rows + c] = tile[tx][i];
-  }
+  transpose_f32_tile(in, rows, cols, out, blockIdx.x * 32, blockIdx.y * 32);
 }
 
 // Block-wide sum of KMAX-wide partial vectors in a fixed tree order.

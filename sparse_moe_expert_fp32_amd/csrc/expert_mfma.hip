@@ -44,6 +44,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "prep.h"
 #include "mfma.h"
 
 namespace moe {
@@ -68,28 +69,8 @@ constexpr int ST_B = 256 * GM_KS / 2, ST_X = 512 * 4;   // (the A stage holds th
 __global__ void group_rowsum_kernel(const bf16_t *__restrict__ a, int rows, int K, int G,
                                     float scale, float *__restrict__ out, bool split,
                                     float scale2) {
-  const int ng = K / G;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)rows * ng) return;
-  size_t row = i / ng;
-  int g = (int)(i % ng);
-  const uint4 *p = reinterpret_cast<const uint4 *>(a + row * K + (size_t)g * G);
-  float s = 0.f;
-  for (int v = 0; v < G / 8; ++v) {
-    uint4 u = p[v];
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s += __uint_as_float(w[j] << 16);
-      s += __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  }
-  if (split) {
-    out[row * 2 * ng + g] = scale * s;
-    out[row * 2 * ng + ng + g] = scale2 * s;
-  } else {
-    out[i] = scale * s;
-  }
+  group_rowsum_elem((size_t)blockIdx.x * blockDim.x + threadIdx.x, a, rows, K, G, scale, out,
+                    split, scale2);
 }
 
 // ------------------------------------------------------------ scale ratios --
@@ -153,16 +134,14 @@ DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
 // MODE 0: gate/up with SwiGLU epilogue (A = x rows gathered by token); a work
 //         item covers up to 128 rows x 128 columns of both gate and up.
 // MODE 1: down (A = H rows in permuted order); up to 128 rows x 256 columns.
-// WAVES waves per block, each with all rows of the item and NF column
-// fragments of 16 (mode 0: half gate, half up, so SwiGLU pairs up in a lane).
-// Gate/up runs 8 waves x 2 fragments (four waves per SIMD, 128 VGPRs);
-// down runs 4 waves x 4 fragments (two waves per SIMD: each A fragment read
-// from LDS feeds four matrix instructions).  NM (2, 4, 6, 8) is the number of
-// 16-row fragments of the item's tile class: each class of tiles (32, 64, 96,
-// 128 rows) is its own launch, so a short tail tile costs only its rows.
-// blocks per CU of the class launches of tile class NM, as the registers
-// allow: the 32-row class (2-slot ring of 28 KB, at most 128 VGPRs) four,
-// the others two
+// WAVES (4) waves per block, each with all rows of the item and NF column
+// fragments of 16 (mode 0: half gate, half up, so SwiGLU pairs up in a lane),
+// so each unpacked weight fragment feeds NM matrix instructions.  NM (2, 4,
+// 6, 8) is the number of 16-row fragments of the item: a tile runs as the
+// shortest class that holds its rows, so a short tail tile costs only its
+// rows.  Resident blocks per CU as the registers allow: the 32-row kernel of
+// short batches (2-slot ring of 28 KB, at most 128 VGPRs) four, the others
+// two.
 constexpr int gm_bpc(int NM) { return NM <= 2 ? 4 : GM_BPC; }
 
 // Per-launch values every work item uses.
@@ -680,26 +659,29 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
   }
 }
 
-// One tile class per launch (tiles of launch_class_tiles), for short
-// batches: the ring holds only the class's rows, so the short classes run
-// more blocks per CU (gm_bpc), which keeps more weight loads in flight where
-// the products stream the weights of many experts for a few rows each.
-template <int MODE, int NM, bool EPL, bool QP>
-__global__ __launch_bounds__(256, gm_bpc(NM)) void grouped_gemm_cls_kernel(
-    const MfmaGemmArgs A, const int *__restrict__ cls_count, const int *__restrict__ cls_start) {
+// Short batches (decode): every expert's rows in tiles of 32 (a list of
+// launch_build_tiles), all of them 32-row items.  The ring holds only 32
+// rows, so more blocks are resident per CU (gm_bpc(2)), which keeps more
+// weight loads in flight where the products stream the weights of many
+// experts for a few rows each.  The items are split into eight contiguous
+// ranges, one per XCD, dealt round-robin to the XCD's blocks.
+template <int MODE, bool EPL, bool QP>
+__global__ __launch_bounds__(256, gm_bpc(2)) void grouped_gemm_short_kernel(
+    const MfmaGemmArgs A, const int *__restrict__ ntiles) {
+  constexpr int NM = 2;
   constexpr int ST_A = 16 * NM * GM_KS * 2;
   __shared__ __attribute__((aligned(32))) uint4 ringA[2][ST_A / 16];
   __shared__ uint4 ringB[2][ST_B / 16];
   __shared__ float ringX[2][ST_X / 4];
   __shared__ int tok_lds[GM_BM];
   MOE_GM_CTX(ringA, ringB, ringX, tok_lds);
-  const int total = cls_count[0] * A.NT, tbase = cls_start[0];
+  const int total = ntiles[0] * A.NT;
   const int nper = gridDim.x >> 3, xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
   const int wbeg = (int)(((long long)total * xcd) >> 3);
   const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
   for (int wi = wbeg + bi; wi < wend; wi += nper) {
     const int ti = wi / A.NT, nt = wi - ti * A.NT;
-    const int2 tile = A.tiles[tbase + ti];
+    const int2 tile = A.tiles[ti];
     const int e = tile.x, p0 = tile.y;
     const int rows = min(16 * NM, A.offsets[e + 1] - p0);
     gm_item<MODE, 4, NM, EPL, QP>(A, X, e, p0, rows, nt);
@@ -778,62 +760,6 @@ void launch_pack_fwd_int8(const uint8_t *q, int E, int N, int K, uint8_t *qf, hi
       q, N, K, n16, reinterpret_cast<uint4 *>(qf));
 }
 
-// ------------------------------------------------------------ tile classes --
-// The work list of the grouped GEMMs: each expert's rows in tiles of 32 NC
-// rows, the last (partial) one rounded up to a multiple of 32.  Class c
-// (0 .. NC-1) holds the tiles of 32 (NC - c) rows: tiles lists class 0 first,
-// then 1, ... (each in expert order); cnt[c] and cnt[4 + c] are the count and
-// first index of class c (NC <= 4).  One 1024-thread block (E <= 1024).
-__global__ __launch_bounds__(1024) void build_class_tiles_kernel(const int32_t *__restrict__ offsets,
-                                                                 int E, int NC,
-                                                                 int2 *__restrict__ tiles,
-                                                                 int *__restrict__ cnt) {
-  __shared__ int sc[4][1024];
-  const int e = threadIdx.x;
-  const int BM = 32 * NC;
-  int lo = 0, n = 0;
-  if (e < E) {
-    lo = offsets[e];
-    n = offsets[e + 1] - lo;
-  }
-  const int nfull = n / BM, tail = n - nfull * BM;
-  const int tcls = tail == 0 ? -1 : NC - 1 - ((tail - 1) >> 5);   // 1..32 rows -> NC - 1
-  int c[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) c[k] = (k == 0 ? nfull : 0) + (tcls == k ? 1 : 0);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) sc[k][e] = c[k];
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = e >= off ? sc[k][e - off] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sc[k][e] += v[k];
-    __syncthreads();
-  }
-  int start[4], s = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    start[k] = s;
-    s += sc[k][1023];
-  }
-  // class 0: the full tiles, then a tail of the full class's size
-  int pos = start[0] + sc[0][e] - c[0];
-  for (int i = 0; i < c[0]; ++i) tiles[pos + i] = make_int2(e, lo + BM * i);
-#pragma unroll
-  for (int k = 1; k < 4; ++k)
-    if (c[k]) tiles[start[k] + sc[k][e] - 1] = make_int2(e, lo + BM * nfull);
-  if (e == 0) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      cnt[k] = sc[k][1023];
-      cnt[4 + k] = start[k];
-    }
-  }
-}
-
 int mfma_tile_rows() { return GM_BM; }
 int mfma_blocks_per_cu() { return GM_BPC; }
 
@@ -848,11 +774,6 @@ void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipS
                         bool split) {
   dim3 grid((N + 255) / 256, E);
   scale_ratio_kernel<<<grid, 256, 0, st>>>(s, E, N, ng, rt, split);
-}
-
-void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, int *cnt,
-                        hipStream_t st) {
-  build_class_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, nclass, tiles, cnt);
 }
 
 // One launch per product over the tiles of launch_build_tiles (ctr: eight
@@ -876,30 +797,27 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int
 #undef MOE_GG3
 }
 
-// The launch of tile class cls (0: 128 rows, 1: 96, 2: 64, 3: 32) of
-// launch_class_tiles (cnt: counts and first indices).
-void launch_grouped_gemm_cls(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
-                             hipStream_t st) {
-  const int *c = cnt + cls, *s = cnt + 4 + cls;
-  // grid: GM_BPC blocks per CU; the 32-row class runs gm_bpc(2) per CU
-  if (cls == 3) grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
+// The short-batch launch over 32-row tiles (ntiles: the count of the list);
+// grid: GM_BPC blocks per CU, scaled to gm_bpc(2)
+void launch_grouped_gemm_short(int mode, const MfmaGemmArgs &A, const int *ntiles, int grid,
+                               hipStream_t st) {
+  grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
   // the packed base where given
   const bool qp = A.qp0 && (mode == 1 || A.qp1);
-#define MOE_GG2(MODE, NM, QP)                                                                 \
-  if (epl) grouped_gemm_cls_kernel<MODE, NM, true, QP><<<grid, 256, 0, st>>>(A, c, s);         \
-  else grouped_gemm_cls_kernel<MODE, NM, false, QP><<<grid, 256, 0, st>>>(A, c, s)
-#define MOE_GG(MODE, NM)                                                \
-  do {                                                                  \
-    if (qp) { MOE_GG2(MODE, NM, true); } else { MOE_GG2(MODE, NM, false); } \
+#define MOE_GS(MODE, EPL, QP) grouped_gemm_short_kernel<MODE, EPL, QP><<<grid, 256, 0, st>>>(A, ntiles)
+#define MOE_GS2(MODE, EPL)                     \
+  do {                                         \
+    if (qp) MOE_GS(MODE, EPL, true);           \
+    else MOE_GS(MODE, EPL, false);             \
   } while (0)
   if (mode == 0) {
-    if (cls == 0) MOE_GG(0, 8); else if (cls == 1) MOE_GG(0, 6); else if (cls == 2) MOE_GG(0, 4); else MOE_GG(0, 2);
+    if (epl) MOE_GS2(0, true); else MOE_GS2(0, false);
   } else {
-    if (cls == 0) MOE_GG(1, 8); else if (cls == 1) MOE_GG(1, 6); else if (cls == 2) MOE_GG(1, 4); else MOE_GG(1, 2);
+    if (epl) MOE_GS2(1, true); else MOE_GS2(1, false);
   }
-#undef MOE_GG
-#undef MOE_GG2
+#undef MOE_GS2
+#undef MOE_GS
 }
 
 }  // namespace moe

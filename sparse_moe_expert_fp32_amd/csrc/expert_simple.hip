@@ -11,6 +11,7 @@
 // reading; the pages do not name the FFN.
 #include "common.h"
 #include "kernels.h"
+#include "prep.h"
 
 namespace moe {
 
@@ -23,41 +24,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
                                                            int E, int BM, int2 *__restrict__ tiles,
                                                            int *__restrict__ ntiles,
                                                            int *__restrict__ first_out, int nzero) {
-  __shared__ int sc[1024];
-  const int e = threadIdx.x;
-  if (e >= 1 && e < nzero) ntiles[e] = 0;
-  int c = 0, lo = 0;
-  if (e < E) {
-    lo = offsets[e];
-    c = (offsets[e + 1] - lo + BM - 1) / BM;
-  }
-  sc[e] = c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = e >= off ? sc[e - off] : 0;
-    __syncthreads();
-    sc[e] += v;
-    __syncthreads();
-  }
-  int first = sc[e] - c;
-  for (int i = 0; i < c; ++i) tiles[first + i] = make_int2(e, lo + i * BM);
-  if (first_out && e < E) first_out[e] = first;
-  if (e == 1023) ntiles[0] = sc[e];
-  if (!first_out) return;
-  // after the first tiles: the number of experts not covered by exactly one
-  // tile (empty or split), then those experts in ascending order
-  __syncthreads();
-  const int f = e < E && c != 1 ? 1 : 0;
-  sc[e] = f;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = e >= off ? sc[e - off] : 0;
-    __syncthreads();
-    sc[e] += v;
-    __syncthreads();
-  }
-  if (f) first_out[E + sc[e]] = e;   // position 1 + (exclusive prefix)
-  if (e == 1023) first_out[E] = sc[e];
+  build_tiles_body(offsets, E, BM, tiles, ntiles, first_out, nzero);
 }
 
 // ------------------------------------------------------ int4 expert GEMM --

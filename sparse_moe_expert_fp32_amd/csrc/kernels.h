@@ -55,6 +55,37 @@ void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int 
                         hipStream_t st, int *first = nullptr, int nzero = 0);
 int simple_tile_rows();
 
+// ---- batched set-up (prep.hip): independent small jobs of one call (tile
+// lists, group row sums, rank-16 adapter transposes) in one launch of
+// 1024-thread blocks; each job takes a contiguous range of the blocks
+struct PrepBatch {
+  enum Kind { kTiles = 1, kRowsum, kTransposeRN16, kTransposeNR16, kTransposeF32 };
+  struct Job {
+    int kind, nblocks;
+    const int32_t *offsets; int E, BM; int2 *tiles; int *ntiles; int *first; int nzero;
+    const void *src; void *dst; int rows, K, G, N; float scale, scale2; int split;
+  };
+  static constexpr int kMax = 12;
+  Job job[kMax];
+  int n = 0;
+  // launch_build_tiles as a job
+  void tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int *ntiles, int *first = nullptr,
+             int nzero = 0);
+  // launch_group_rowsum as a job
+  void rowsum(const void *a, int rows, int K, int G, float scale, float *out, bool split = false,
+              float scale2 = 0.f);
+  // launch_transpose_rn / launch_transpose_nr as a job where the rank-16
+  // kernel applies (else launched on its own now, on st)
+  void transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st);
+  void transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
+  // launch_transpose_f32 as a job
+  void transpose_f32(const float *in, int rows, int cols, float *out);
+
+ private:
+  Job &next();   // the next free job (aborts past kMax: a fixed number per call)
+};
+void launch_prep(const PrepBatch &b, hipStream_t st);
+
 struct LinArgs {
   const void *a; int lda; bool gather; const int32_t *perm_src; int kk;
   const int2 *tiles; const int *ntiles; int max_tiles; const int32_t *offsets;
@@ -90,7 +121,7 @@ struct MfmaGemmArgs {
   const void *a; int lda;                 // A rows: x [T][d] (mode 0) or H [S][f] (mode 1)
   const int32_t *perm_src; int kk;        // mode 0: token of a permuted row
   const float *rsum; int ld_rsum;         // per A row, per group of 128: -136 * sum of the row
-  const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
+  const int2 *tiles; const int32_t *offsets;   // tile list of launch_build_tiles
   int K, N, NT;                           // reduction, columns per matrix, N-tiles per M-tile
   // ka: the A rows' length.  K for an int4 base; K / 2 for an int8 base split
   // into two int4 planes along K (launch_pack_fwd_int8): the rows are read
@@ -120,12 +151,6 @@ void launch_group_rowsum(const void *a, int rows, int K, int G, float scale, flo
 // int8 base, 16 s then s (ng' = 2 ng)
 void launch_scale_ratio(const uint16_t *s, int E, int N, int ng, float *rt, hipStream_t st,
                         bool split = false);
-// expert tiles of 32 nclass rows (nclass <= 4), the partial last one of each
-// expert rounded up to a multiple of 32, grouped by that class (class c:
-// 32 (nclass - c) rows); cnt[8]: count and first index of each class
-// (the full-size class first)
-void launch_class_tiles(const int32_t *offsets, int E, int nclass, int2 *tiles, int *cnt,
-                        hipStream_t st);
 // int4 [E][N][K/2] -> stage-major [E][K/64][N][32 B] (K a multiple of 64)
 void launch_pack_fwd(const uint8_t *q, int E, int N, int K, uint8_t *qf, hipStream_t st);
 // int8 [E][N][K] -> the stage-major int4 layout of its two planes along K
@@ -137,10 +162,10 @@ void launch_pack_fwd_int8(const uint8_t *q, int E, int N, int K, uint8_t *qf, hi
 // eight counters, zero at launch)
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int *ctr, int grid,
                          hipStream_t st);
-// the launch of tile class cls of launch_class_tiles (0: 128-row tiles ..
-// 3: 32-row tiles; cnt: counts and first indices), for short batches
-void launch_grouped_gemm_cls(int mode, const MfmaGemmArgs &A, const int *cnt, int cls, int grid,
-                             hipStream_t st);
+// short batches: one launch over 32-row tiles of launch_build_tiles
+// (ntiles: their count), every item a 32-row item
+void launch_grouped_gemm_short(int mode, const MfmaGemmArgs &A, const int *ntiles, int grid,
+                               hipStream_t st);
 
 // transposed-base products of the backward (expert_mfma_bwd.hip)
 struct MfmaGemmTArgs {
@@ -148,7 +173,7 @@ struct MfmaGemmTArgs {
   // mode 0 with gsc set: A row p is a0[perm_src[p] / kk] (dy by token) and the
   // product row is scaled by gsc[perm_src[p]] (the gate) before the adapter term
   const int32_t *perm_src; int kk; const float *gsc;
-  const int2 *tiles; const int32_t *offsets;   // tile list of launch_class_tiles
+  const int2 *tiles; const int32_t *offsets;   // tile list of launch_build_tiles
   int K, N, NT;                           // reduction per source, output columns, ceil(N / 256)
   // kr: the A rows' length per source.  K for an int4 base; K / 2 for an int8
   // base split into two stacked int4 planes (launch_transpose_q_int8): the rows
@@ -179,14 +204,17 @@ void launch_transpose_q_int8(const uint8_t *q, const uint16_t *s, const int32_t 
 // ---- rank-r adapter products on the matrix cores (lowrank.hip)
 struct ProjMArgs {                        // Z_s = scale * A M_s^T over each expert's rows
   const uint16_t *a; int lda; const int32_t *perm_src; int kk;
-  const int2 *tiles; const int *ntiles; const int32_t *offsets;   // 64-row tiles
+  const int2 *tiles; const int *ntiles; const int32_t *offsets;   // proj_tile_rows() tiles
   int K, r, nsrc;
   const uint16_t *m0, *m1;                // [E][r][K]
   float scale; float *Z0, *Z1; int ldz;
   const float *gsc;                       // GATHER: row p also scaled by gsc[perm_src[p]] (or null)
 };
-void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st);
-int proj_tile_rows();
+// short_rows: 16-row tiles with the reduction split over 8 waves (short
+// batches: a few rows per expert), else 64-row tiles over 4 waves
+void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st,
+                      bool short_rows = false);
+int proj_tile_rows(bool short_rows = false);
 struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p][a] R_s[p][b]
   const uint16_t *w; int ldw; const int32_t *perm_src; int kk;
   const float *rr; int ldr;               // R of source 0

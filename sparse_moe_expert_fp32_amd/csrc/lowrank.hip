@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "prep.h"
 #include "mfma.h"
 
 namespace moe {
@@ -22,19 +23,23 @@ namespace moe {
 // Z_s[p][j] = scale * g_p * sum_k A(p, k) M_s[e][j][k] for sources s < nsrc,
 // j < r.  A(p, k) = a[(GATHER ? perm_src[p] / kk : p) * lda + k]; M_s is
 // [E][r][K]; g_p = gsc[perm_src[p]] when gsc is given (GATHER), else 1.
-// NF = nsrc * ceil(r / 16) 16-column fragments.  One block per 64-row tile;
-// the tiles are spread so that each XCD takes a contiguous run of the list
-// (the tiles of one expert share that XCD's L2 copy of M).  The reduction is
-// split over the four waves (wave w takes the 64-wide k-chunks w, w + 4, ...)
-// and every wave keeps the next chunk's loads in flight while it multiplies
-// the current one; the wave partials are summed through LDS in wave order.
+// NF = nsrc * ceil(r / 16) 16-column fragments.  One block per tile of 64
+// rows (16 for short batches); the tiles are spread so that each XCD takes a
+// contiguous run of the list (the tiles of one expert share that XCD's L2
+// copy of M).  The reduction is split over the NW waves (wave w takes the
+// 64-wide k-chunks w, w + NW, ...) and every wave keeps the next chunk's
+// loads in flight while it multiplies the current one; the wave partials are
+// summed through LDS in wave order.
 // Columns j >= r of a fragment read a valid row of M (row r - 1): column j of
 // the product depends only on column j of M, and those columns are not stored.
 constexpr int PJ_KC = 64;
 
-template <bool GATHER, int NF>
-__global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const ProjMArgs P) {
-  __shared__ float red[3][4 * NF * 4 * 64];   // partials of waves 1..3: [m*NF+f][i][lane]
+// NMR: 16-row fragments per tile (4: 64-row tiles; 1: 16-row tiles for short
+// batches, with NW = 8 waves splitting the reduction so that each wave has
+// fewer chunks to wait for).
+template <bool GATHER, int NF, int NMR, int NW>
+__global__ __launch_bounds__(64 * NW, NF == 4 ? 1 : 2) void proj_mfma_kernel(const ProjMArgs P) {
+  __shared__ float red[NW - 1][NMR * NF * 4 * 64];   // partials of waves 1..NW-1: [m*NF+f][i][lane]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int nt = P.ntiles[0], per = (nt + 7) >> 3;
@@ -45,9 +50,9 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
   const int p_end = P.offsets[e + 1];
   const int nj = (P.r + 15) >> 4;           // 16-column fragments per source
   // rows: fragment m covers rows p0 + 16 m .. +15 (clamped to the expert)
-  const uint16_t *ap[4];
+  const uint16_t *ap[NMR];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < NMR; ++m) {
     const int prow = min(p0 + 16 * m + lr, p_end - 1);
     const size_t arow = GATHER ? (size_t)(P.perm_src[prow] / P.kk) : (size_t)prow;
     ap[m] = P.a + arow * P.lda + 8 * lg;
@@ -59,18 +64,18 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
     const int src = f / nj, j = 16 * (f - src * nj) + lr;
     mp[f] = (src ? P.m1 : P.m0) + ((size_t)e * P.r + min(j, P.r - 1)) * P.K + 8 * lg;
   }
-  f32x4_t acc[4][NF];
+  f32x4_t acc[NMR][NF];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < NMR; ++m)
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  using Av = uint4[4][2];
+  using Av = uint4[NMR][2];
   using Bv = uint4[2][NF];
   auto load = [&](Av &av, Bv &bv, int k0) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) av[m][s] = *reinterpret_cast<const uint4 *>(ap[m] + k0 + 32 * s);
+      for (int m = 0; m < NMR; ++m) av[m][s] = *reinterpret_cast<const uint4 *>(ap[m] + k0 + 32 * s);
 #pragma unroll
       for (int f = 0; f < NF; ++f) bv[s][f] = *reinterpret_cast<const uint4 *>(mp[f] + k0 + 32 * s);
     }
@@ -81,37 +86,37 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m][f] = mfma32(av[m][s], bv[s][f], acc[m][f]);
+        for (int m = 0; m < NMR; ++m) acc[m][f] = mfma32(av[m][s], bv[s][f], acc[m][f]);
   };
-  // chunks w, w + 4, ... of K (K is a multiple of 64; with K < 256 some
+  // chunks w, w + NW, ... of K (K is a multiple of 64; with K < 64 NW some
   // waves have none); two register sets.  Each branch issues the next
   // chunk's loads before multiplying the current one, so the wait before the
   // multiplication leaves the new loads in flight.
-  const int nk = (P.K / PJ_KC - w + 3) >> 2;
+  const int nk = (P.K / PJ_KC - w + NW - 1) / NW;
   if (nk > 0) {
     Av a0, a1;
     Bv b0, b1;
     int k0 = w * PJ_KC;
     load(a0, b0, k0);
-    for (int c = 1;; c += 2, k0 += 8 * PJ_KC) {
+    for (int c = 1;; c += 2, k0 += 2 * NW * PJ_KC) {
       if (c >= nk) {
         comp(a0, b0);
         break;
       }
-      load(a1, b1, k0 + 4 * PJ_KC);
+      load(a1, b1, k0 + NW * PJ_KC);
       comp(a0, b0);
       if (c + 1 >= nk) {
         comp(a1, b1);
         break;
       }
-      load(a0, b0, k0 + 8 * PJ_KC);
+      load(a0, b0, k0 + 2 * NW * PJ_KC);
       comp(a1, b1);
     }
   }
-  // partial sums of waves 1..3 to LDS, summed by wave 0 in wave order
+  // partial sums of waves 1..NW-1 to LDS, summed by wave 0 in wave order
   if (w > 0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < NMR; ++m)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -119,9 +124,9 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
   }
   __syncthreads();
   if (w > 0) return;
-  float gs[4][4];
+  float gs[NMR][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < NMR; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = min(p0 + 16 * m + 4 * lg + i, p_end - 1);
@@ -132,11 +137,13 @@ __global__ __launch_bounds__(256, NF == 4 ? 1 : 2) void proj_mfma_kernel(const P
     const int src = f / nj, j = 16 * (f - src * nj) + lr;
     float *Z = src ? P.Z1 : P.Z0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < NMR; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = ((m * NF + f) * 4 + i) * 64 + lane;
-        const float v = ((acc[m][f][i] + red[0][o]) + red[1][o]) + red[2][o];
+        float v = acc[m][f][i];
+#pragma unroll
+        for (int q = 0; q < NW - 1; ++q) v += red[q][o];
         const int p = p0 + 16 * m + 4 * lg + i;
         if (j < P.r && p < p_end) Z[(size_t)p * P.ldz + j] = gs[m][i] * v;
       }
@@ -345,14 +352,21 @@ __global__ __launch_bounds__(256) void transpose_nr_kernel(const uint16_t *__res
   }
 }
 
-int proj_tile_rows() { return 64; }
+int proj_tile_rows(bool short_rows) { return short_rows ? 16 : 64; }
 
-void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st) {
+void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_t st,
+                      bool short_rows) {
   const int nf = P.nsrc * ((P.r + 15) / 16);
   const unsigned grid = (unsigned)((max_tiles + 7) / 8 * 8);   // every XCD the same share
-#define MOE_PROJ(NF)                                                    \
-  if (gather) proj_mfma_kernel<true, NF><<<grid, 256, 0, st>>>(P);      \
-  else proj_mfma_kernel<false, NF><<<grid, 256, 0, st>>>(P);
+#define MOE_PROJ2(NF, NMR, NW)                                                  \
+  if (gather) proj_mfma_kernel<true, NF, NMR, NW><<<grid, 64 * NW, 0, st>>>(P);  \
+  else proj_mfma_kernel<false, NF, NMR, NW><<<grid, 64 * NW, 0, st>>>(P);
+#define MOE_PROJ(NF)            \
+  if (short_rows) {             \
+    MOE_PROJ2(NF, 1, 8)         \
+  } else {                      \
+    MOE_PROJ2(NF, 4, 4)         \
+  }
   if (nf == 1) {
     MOE_PROJ(1)
   } else if (nf == 2) {
@@ -361,6 +375,7 @@ void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_
     MOE_PROJ(4)
   }
 #undef MOE_PROJ
+#undef MOE_PROJ2
 }
 
 void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st) {
@@ -409,29 +424,11 @@ __global__ __launch_bounds__(256) void transpose_rn_kernel(const uint16_t *__res
 // accesses across the wave.
 __global__ __launch_bounds__(256) void transpose_rn16_kernel(const uint16_t *__restrict__ in, int N,
                                                              uint16_t *__restrict__ out) {
-  const int e = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  const uint16_t *src = in + (size_t)e * 16 * N + n;
-  uint32_t v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (uint32_t)src[(2 * j) * (size_t)N] | ((uint32_t)src[(2 * j + 1) * (size_t)N] << 16);
-  uint4 *dst = reinterpret_cast<uint4 *>(out + ((size_t)e * N + n) * 16);
-  dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
-  dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
+  transpose_rn16_elem(in, N, blockIdx.y, blockIdx.x * 256 + threadIdx.x, out);
 }
 __global__ __launch_bounds__(256) void transpose_nr16_kernel(const uint16_t *__restrict__ in, int N,
                                                              uint16_t *__restrict__ out) {
-  const int e = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  const uint4 *src = reinterpret_cast<const uint4 *>(in + ((size_t)e * N + n) * 16);
-  const uint4 a = src[0], b = src[1];
-  const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint16_t *dst = out + (size_t)e * 16 * N + n;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    dst[(2 * j) * (size_t)N] = (uint16_t)(v[j] & 0xFFFFu);
-    dst[(2 * j + 1) * (size_t)N] = (uint16_t)(v[j] >> 16);
-  }
+  transpose_nr16_elem(in, N, blockIdx.y, blockIdx.x * 256 + threadIdx.x, out);
 }
 
 void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st) {

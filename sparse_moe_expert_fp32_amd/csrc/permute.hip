@@ -26,11 +26,20 @@ constexpr int PB = 256;  // tokens per histogram block
 // the token does not use yet (k <= E, so one exists).  Valid input passes
 // through unchanged; invalid input still yields a bijective placement with
 // every access inside the buffers.  canon[t k + j] holds the result.
+//
+// SINGLE (T <= 256, one block): the block also does what perm_scan_kernel and
+// perm_scatter_kernel do for several blocks -- counts, offsets and the
+// placement -- so a short batch is permuted in one launch.
+template <bool SINGLE>
 __global__ __launch_bounds__(PB) void perm_hist_kernel(const int32_t *__restrict__ idx, int Tn,
                                                        int E, int k,
                                                        int32_t *__restrict__ block_counts,
                                                        int32_t *__restrict__ rank,
-                                                       int32_t *__restrict__ canon) {
+                                                       int32_t *__restrict__ canon,
+                                                       int32_t *__restrict__ counts,
+                                                       int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ perm_src,
+                                                       int32_t *__restrict__ slot_pos) {
   extern __shared__ unsigned long long masks[];  // [4][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x * PB + tid;
@@ -70,6 +79,7 @@ __global__ __launch_bounds__(PB) void perm_hist_kernel(const int32_t *__restrict
     }
   }
   __syncthreads();
+  int rk[32];   // (SINGLE: the ranks stay in registers)
   if (t < Tn) {
     const unsigned long long lower = (1ull << lane) - 1ull;
 #pragma unroll
@@ -78,13 +88,61 @@ __global__ __launch_bounds__(PB) void perm_hist_kernel(const int32_t *__restrict
       const int e = ce[j];
       int r = __popcll(masks[wave * E + e] & lower);
       for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
-      rank[(size_t)t * k + j] = r;
+      if (SINGLE) rk[j] = r;
+      else rank[(size_t)t * k + j] = r;
     }
   }
-  for (int e = tid; e < E; e += PB) {
+  if (!SINGLE) {
+    for (int e = tid; e < E; e += PB) {
+      int c = 0;
+      for (int w = 0; w < 4; ++w) c += __popcll(masks[w * E + e]);
+      block_counts[(size_t)blockIdx.x * E + e] = c;
+    }
+    return;
+  }
+  // counts and their exclusive scan: thread tid takes experts 4 tid .. 4 tid + 3
+  // (E <= 4 PB), then a scan of the per-thread sums
+  __shared__ int tot[PB];
+  __shared__ int off_lds[4 * PB];
+  int c4[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * tid + q;
     int c = 0;
-    for (int w = 0; w < 4; ++w) c += __popcll(masks[w * E + e]);
-    block_counts[(size_t)blockIdx.x * E + e] = c;
+    if (e < E)
+      for (int w = 0; w < 4; ++w) c += __popcll(masks[w * E + e]);
+    c4[q] = c;
+    sum += c;
+  }
+  tot[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < PB; off <<= 1) {   // Hillis-Steele inclusive scan
+    const int v = tid >= off ? tot[tid - off] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  int run = tot[tid] - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * tid + q;
+    if (e < E) {
+      counts[e] = c4[q];
+      offsets[e] = run;
+      off_lds[e] = run;
+    }
+    run += c4[q];
+  }
+  if (tid == PB - 1) offsets[E] = tot[PB - 1];
+  __syncthreads();
+  if (t < Tn) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j >= k) break;
+      const int s = t * k + j, p = off_lds[ce[j]] + rk[j];
+      perm_src[p] = s;
+      slot_pos[s] = p;
+    }
   }
 }
 
@@ -159,11 +217,17 @@ void launch_permute(const int32_t *idx, int Tn, int E, int k, int32_t *counts, i
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   int32_t *rank = (int32_t *)((char *)ws + al((size_t)nb * E * 4));
   int32_t *canon = (int32_t *)((char *)rank + al((size_t)S * 4));
-  perm_hist_kernel<<<nb, PB, 4 * E * sizeof(unsigned long long), st>>>(idx, Tn, E, k,
-                                                                       block_counts, rank, canon);
-  perm_scan_kernel<<<1, 1024, 0, st>>>(block_counts, nb, E, counts, offsets);
-  perm_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(canon, S, E, k, block_counts, offsets, rank,
-                                                       perm_src, slot_pos);
+  const size_t lds = 4 * E * sizeof(unsigned long long);
+  if (nb == 1) {
+    perm_hist_kernel<true><<<1, PB, lds, st>>>(idx, Tn, E, k, block_counts, rank, canon, counts,
+                                               offsets, perm_src, slot_pos);
+  } else {
+    perm_hist_kernel<false><<<nb, PB, lds, st>>>(idx, Tn, E, k, block_counts, rank, canon,
+                                                 nullptr, nullptr, nullptr, nullptr);
+    perm_scan_kernel<<<1, 1024, 0, st>>>(block_counts, nb, E, counts, offsets);
+    perm_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(canon, S, E, k, block_counts, offsets,
+                                                         rank, perm_src, slot_pos);
+  }
   if (x_perm)
     perm_copy_kernel<<<(S + 3) / 4, 256, 0, st>>>((const uint4 *)x, perm_src, S, k,
                                                   row_bytes / 16, (uint4 *)x_perm);

@@ -14,8 +14,9 @@
 //                  tile per 256-thread block fed by an LDS-DMA ring, d
 //                  optionally split across blocks so that small token counts
 //                  still fill the chip; each split writes its own partial.
-//   router_topk    one wave per token: sums the partials in split order, adds
-//                  the bias, then k rounds of a wave-wide argmax on the key
+//   router_topk    one wave per token (four when a short batch has many
+//                  splits): sums the partials in a fixed order, adds the
+//                  bias, then k rounds of a wave-wide argmax on the key
 //                  (logit desc, index asc) and the softmax of the k winners.
 #include "common.h"
 #include "kernels.h"
@@ -161,38 +162,91 @@ __global__ __launch_bounds__(256, 2) void router_logits_kernel(
 // (v, e) beats (v2, e2): larger logit, or equal logit and lower index.
 DEV bool beats(float v, int e, float v2, int e2) { return v > v2 || (v == v2 && e < e2); }
 
+// The wave's best (v, e) by that order, in every lane (all 64 lanes active):
+// DPP exchanges inside each row of 16 lanes (pairs, quads, halves, rows),
+// then the four row winners read as scalars.  Every candidate index is
+// distinct, so the order is total and the result does not depend on the
+// exchange pattern.
+template <int CTRL>
+DEV void argmax_dpp(float &bv, int &be) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  if (beats(ov, oe, bv, be)) { bv = ov; be = oe; }
+}
+DEV void wave_argmax(float &bv, int &be) {
+  argmax_dpp<0xB1>(bv, be);    // quad_perm [1, 0, 3, 2]
+  argmax_dpp<0x4E>(bv, be);    // quad_perm [2, 3, 0, 1]
+  argmax_dpp<0x141>(bv, be);   // row_half_mirror
+  argmax_dpp<0x140>(bv, be);   // row_mirror
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int e = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+    const int oe = __builtin_amdgcn_readlane(be, 16 * r);
+    if (beats(ov, oe, v, e)) { v = ov; e = oe; }
+  }
+  bv = v;
+  be = e;
+}
+
+// WPT waves per token: 1, or 4 for short batches with many splits (wave w
+// adds splits w, w + 4, ..., and wave 0 adds the four sums in wave order).
+// NEM: logit slots per lane (expert e = lane + 64 n, n < NEM; E <= 64 NEM).
+// The partial loads go in batches of NS splits with clamped, unconditional
+// addresses, so a batch is one round trip to memory; the sums skip the
+// clamped repeats and keep split order.
+template <int WPT, int NEM>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float *__restrict__ partial, int splits, const float *__restrict__ bias,
     int Tn, int E, int k, int32_t *__restrict__ topk_idx, float *__restrict__ gates,
     float *__restrict__ logits_out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int NS = WPT == 1 ? 4 : 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = WPT == 1 ? blockIdx.x * 4 + w : blockIdx.x;
   if (t >= Tn) return;
-  const int NE = (E + 63) >> 6;
-  float l[16];
-  uint32_t taken = 0;
-  // the split-K partial sums, added in split order; all of one split's loads
-  // are issued together (one wait per split, not one per value)
-  float acc[16];
+  float acc[NEM];
 #pragma unroll
-  for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < splits; ++s) {
-    const float *ps = partial + ((size_t)s * Tn + t) * E;
-    float pv[16];
+  for (int n = 0; n < NEM; ++n) acc[n] = 0.f;
+  int eoff[NEM];   // clamped expert of each slot
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      const int e = lane + 64 * n;
-      pv[n] = n < NE && e < E ? ps[e] : 0.f;
+  for (int n = 0; n < NEM; ++n) eoff[n] = min(lane + 64 * n, E - 1);
+  for (int s0 = WPT == 1 ? 0 : w; s0 < splits; s0 += NS * WPT) {
+    float pv[NS][NEM];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int s = min(s0 + i * WPT, splits - 1);
+      const float *ps = partial + ((size_t)s * Tn + t) * E;
+#pragma unroll
+      for (int n = 0; n < NEM; ++n) pv[i][n] = ps[eoff[n]];
     }
 #pragma unroll
-    for (int n = 0; n < 16; ++n) acc[n] += pv[n];
-  }
+    for (int i = 0; i < NS; ++i)
+      if (s0 + i * WPT < splits) {
 #pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    int e = lane + 64 * n;
+        for (int n = 0; n < NEM; ++n) acc[n] += pv[i][n];
+      }
+  }
+  if constexpr (WPT > 1) {
+    __shared__ float red[WPT - 1][NEM][64];
+    if (w > 0) {
+#pragma unroll
+      for (int n = 0; n < NEM; ++n) red[w - 1][n][lane] = acc[n];
+    }
+    __syncthreads();
+    if (w > 0) return;
+#pragma unroll
+    for (int n = 0; n < NEM; ++n)
+#pragma unroll
+      for (int i = 0; i < WPT - 1; ++i) acc[n] += red[i][n][lane];
+  }
+  float l[NEM];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int n = 0; n < NEM; ++n) {
+    const int e = lane + 64 * n;
     float v = -INFINITY;
-    if (n < NE && e < E) {
+    if (e < E) {
       v = acc[n];
       if (bias) v += bias[e];
       if (logits_out) logits_out[(size_t)t * E + e] = v;
@@ -211,16 +265,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      int e = lane + 64 * n;
+    for (int n = 0; n < NEM; ++n) {
+      const int e = lane + 64 * n;
       if (!((taken >> n) & 1u) && beats(l[n], e, bv, be)) { bv = l[n]; be = e; }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oe = __shfl_xor(be, off);
-      if (beats(ov, oe, bv, be)) { bv = ov; be = oe; }
-    }
+    wave_argmax(bv, be);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (lane == j) { sel_v = bv; sel_e = be; }
   }
@@ -241,7 +290,7 @@ int route_splits(int T, int d, int E) {
   const int max_splits = d / RT_KS;   // d is a multiple of the quantization group (>= 32)
   int s = (512 + blocks - 1) / blocks;
   if (s > max_splits) s = max_splits;
-  if (s > 16) s = 16;   // (the top-k pass adds the splits of every logit)
+  if (s > 32) s = 32;   // (the top-k pass adds the splits of every logit)
   if (s < 1) s = 1;
   return s;
 }
@@ -269,8 +318,15 @@ void launch_router_logits(bool bf16, const void *x, const float *wr, int Tn, int
 
 void launch_router_topk(const void *ws, int splits, const float *bias, int Tn, int E, int k,
                         int32_t *topk_idx, float *gates, float *logits, hipStream_t st) {
-  router_topk_kernel<<<(Tn + 3) / 4, 256, 0, st>>>((const float *)ws, splits, bias, Tn, E, k,
-                                                   topk_idx, gates, logits);
+  const float *p = (const float *)ws;
+#define MOE_TK(WPT, NEM, GRID) \
+  router_topk_kernel<WPT, NEM><<<GRID, 256, 0, st>>>(p, splits, bias, Tn, E, k, topk_idx, gates, logits)
+  if (splits > 4) {
+    if (E <= 512) MOE_TK(4, 8, Tn); else MOE_TK(4, 16, Tn);
+  } else {
+    if (E <= 512) MOE_TK(1, 8, (Tn + 3) / 4); else MOE_TK(1, 16, (Tn + 3) / 4);
+  }
+#undef MOE_TK
 }
 
 }  // namespace moe

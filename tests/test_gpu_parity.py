@@ -56,6 +56,7 @@ def test_small_f32_ragged(cuda_ok):
     dict(E=48, k=20, T=40, cfg_id=236),                  # k > 16: block-per-token kernels
     dict(d=384, cfg_id=237),                             # d % 256 != 0: partial column tile
     dict(d=640, f=256, T=150, cfg_id=238),               # (down output and dX_perm)
+    dict(T=127, cfg_id=239, router_bias_var=4.0),        # short batch, experts of 33+ rows
 ])
 def test_edge_shapes(cuda_ok, kw):
     cfg = cfg_of(**kw)
