@@ -849,24 +849,38 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     float *st0 = reinterpret_cast<float *>(qt0 + qsz), *st1 = reinterpret_cast<float *>(qt1 + qsz);
     const uint16_t *H16 = (const uint16_t *)H;
 
-    // dZ_d = lam dO B_d = lam g_p (dy[t(p)] B_d)
+    // The projections dZ = lam dOut B ride along the passes that form dB over
+    // the same rows (rank 16, widths multiples of 256): each writes per
+    // 256-column partials, which launch_zpart_reduce adds.  The partials live
+    // in the dX_perm buffer, which is written only at the end.
+    float *zpart = reinterpret_cast<float *>(dXp);
+    const size_t dxp_bytes = (size_t)S * d * 2;
     moe::ProjMArgs Q{};
-    Q.a = (const uint16_t *)dy; Q.lda = d; Q.perm_src = perm_src; Q.kk = k; Q.gsc = gates;
-    Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets; Q.K = d; Q.r = r; Q.nsrc = 1;
-    Q.m0 = bt_d; Q.scale = lam; Q.Z0 = dZ + 2 * r; Q.ldz = 3 * r;
-    moe::launch_proj_mfma(Q, mtp, true, st);
-    Q.gsc = nullptr;
-    // dB_d [d][r] = lam sum_p dO[p][n] Z_d[p][j]
+    Q.perm_src = perm_src; Q.kk = k; Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets;
+    Q.r = r; Q.nsrc = 1; Q.scale = lam; Q.ldz = 3 * r;
     moe::WgradMArgs W{};
     W.perm_src = perm_src; W.kk = k; W.offsets = offsets; W.E = E; W.r = r; W.nsrc = 1;
     W.tiles = tiles_w; W.ntiles = ntiles_w; W.tfirst = ntiles_w + 1; W.multi = ntiles_w + 1 + E;
     W.part = at<float>(ws, L.part);
-    // (= lam sum_p dy[t(p)][n] g_p Z_d[p][j])
+    W.S = (int)S;
+    // dB_d [d][r] = lam sum_p dO[p][n] Z_d[p][j] (= lam sum_p dy[t(p)][n] g_p Z_d[p][j])
+    // and dZ_d = lam dO B_d = lam g_p (dy[t(p)] B_d)
     W.w = (const uint16_t *)dy; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
     W.gsc = gates;
     W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
-    moe::launch_wgrad_mfma(W, mtw, true, st);
-    W.gsc = nullptr;
+    if (moe::wgrad_can_project(W) && (size_t)(d / 256) * S * 64 <= dxp_bytes) {
+      W.pm = bt_d; W.zpart = zpart;
+      moe::launch_wgrad_mfma(W, mtw, true, st);
+      moe::launch_zpart_reduce(zpart, nullptr, d / 256, (int)S, perm_src, gates, lam, dZ + 2 * r,
+                               nullptr, 3 * r, st);
+    } else {
+      Q.a = (const uint16_t *)dy; Q.lda = d; Q.gsc = gates; Q.K = d; Q.m0 = bt_d;
+      Q.Z0 = dZ + 2 * r;
+      moe::launch_proj_mfma(Q, mtp, true, st);
+      moe::launch_wgrad_mfma(W, mtw, true, st);
+    }
+    W.gsc = nullptr; W.pm = nullptr; W.zpart = nullptr;
+    Q.gsc = nullptr;
     // dH = dO W_d + dZ_d A_d with the SwiGLU backward in the epilogue
     moe::MfmaGemmTArgs M{};
     M.a0 = dy; M.lda = d; M.perm_src = perm_src; M.kk = k; M.gsc = gates;
@@ -889,17 +903,27 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
     W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
     moe::launch_wgrad_mfma(W, mtw, false, st);
-    // dZ_g = lam dG B_g, dZ_u = lam dU B_u
-    Q.a = (const uint16_t *)dG; Q.lda = f; Q.K = f; Q.m0 = bt_g; Q.Z0 = dZ;
-    moe::launch_proj_mfma(Q, mtp, false, st);
-    Q.a = (const uint16_t *)dU; Q.m0 = bt_u; Q.Z0 = dZ + r;
-    moe::launch_proj_mfma(Q, mtp, false, st);
-    // dB [f][r] = lam sum_p dG[p][n] Z[p][j]
+    // dB [f][r] = lam sum_p dG[p][n] Z[p][j] and dZ_g = lam dG B_g (up: dU, Z_u, B_u)
     W.w = (const uint16_t *)dG; W.ldw = f; W.rr = Z; W.wide = f; W.scale = lam; W.out = dB_gate;
     W.oe = (size_t)f * r; W.oa = r; W.ob = 1;
-    moe::launch_wgrad_mfma(W, mtw, false, st);
-    W.w = (const uint16_t *)dU; W.rr = Z + r; W.out = dB_up;
-    moe::launch_wgrad_mfma(W, mtw, false, st);
+    const size_t zq = (size_t)(f / 256) * S * 16;   // floats of one matrix's partials
+    if (moe::wgrad_can_project(W) && 2 * zq * 4 <= dxp_bytes) {
+      W.pm = bt_g; W.zpart = zpart;
+      moe::launch_wgrad_mfma(W, mtw, false, st);
+      W.w = (const uint16_t *)dU; W.rr = Z + r; W.out = dB_up; W.pm = bt_u; W.zpart = zpart + zq;
+      moe::launch_wgrad_mfma(W, mtw, false, st);
+      moe::launch_zpart_reduce(zpart, zpart + zq, f / 256, (int)S, nullptr, nullptr, lam, dZ,
+                               dZ + r, 3 * r, st);
+      W.pm = nullptr; W.zpart = nullptr;
+    } else {
+      Q.a = (const uint16_t *)dG; Q.lda = f; Q.K = f; Q.m0 = bt_g; Q.Z0 = dZ;
+      moe::launch_proj_mfma(Q, mtp, false, st);
+      Q.a = (const uint16_t *)dU; Q.m0 = bt_u; Q.Z0 = dZ + r;
+      moe::launch_proj_mfma(Q, mtp, false, st);
+      moe::launch_wgrad_mfma(W, mtw, false, st);
+      W.w = (const uint16_t *)dU; W.rr = Z + r; W.out = dB_up;
+      moe::launch_wgrad_mfma(W, mtw, false, st);
+    }
     // dA [r][d] = sum_p dZ[p][j] X[token(p)][c], gate and up in one pass over X
     W.w = (const uint16_t *)x; W.ldw = d; W.rr = dZ; W.wide = d; W.scale = 1.f; W.out = dA_gate;
     W.oe = (size_t)r * d; W.oa = 1; W.ob = d;

@@ -171,6 +171,14 @@ __global__ __launch_bounds__(64 * NW, NF == 4 ? 1 : 2) void proj_mfma_kernel(con
 // so the next chunk's loads are issued right then and stay in flight across
 // the barriers and matrix work of the current one (barriers wait for LDS
 // operations only).
+//
+// PROJ (one source of rank 16, wide a multiple of 256): the same pass also
+// forms the projection of the rows onto M = [E][16][wide] (the adapter B of
+// the matrix, transposed), Z'_q[p][j] = sum over the block's 256 columns
+// (column range q) of W(p, a) M[e][j][a], as partials zpart[q][p][j];
+// launch_zpart_reduce adds the ranges.  The staged chunk is also stored as
+// it came (rows of 16-byte pieces, piece index XOR-swizzled by row), and
+// each wave multiplies 16 of its rows by M, also staged in LDS.
 constexpr int WG_COLS = 256, WG_ROWS = 64, WG_TILE = 512;
 
 DEV int wg_sw(int c) { return c ^ ((c >> 3) & 7); }
@@ -182,9 +190,14 @@ DEV void lds_barrier() {
   block_barrier();
 }
 
-template <bool GATHER, int NM>
+template <bool GATHER, int NM, bool PROJ>
 __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) {
+  static_assert(!PROJ || NM == 1, "the projection takes one source of rank 16");
   __shared__ uint4 wl[WG_ROWS / 8][WG_COLS];                          // 32 KB
+  // PROJ: M of the block's columns, rows padded by 16 bytes (conflict-free
+  // reads), and the chunk's rows as loaded (32 KB)
+  __shared__ __attribute__((aligned(16))) uint16_t ml[PROJ ? 16 : 1][PROJ ? WG_COLS + 8 : 8];
+  __shared__ uint4 wrow[PROJ ? WG_ROWS : 1][PROJ ? WG_COLS / 8 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t rl[16 * NM][WG_ROWS + 8];
   __shared__ int srow[WG_TILE];                                       // source row per tile row
   __shared__ float sgam[WG_TILE];                                     // its R scale
@@ -200,14 +213,22 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
   const int nj = (G.r + 15) >> 4;   // R fragments per source (NM = nj * nsrc)
   constexpr int RC = 16 * NM;       // staged R columns (all sources)
   constexpr int RPER = RC / 4;      // R values per thread and chunk
+  if constexpr (PROJ) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u, row = idx >> 5, c8 = 8 * (idx & 31);
+      *reinterpret_cast<uint4 *>(&ml[row][c8]) =
+          *reinterpret_cast<const uint4 *>(G.pm + ((size_t)e * 16 + row) * G.wide + a0 + c8);
+    }
+  }
   if (GATHER) {
     for (int t = tid; t < hi - p0; t += 256) {
       const int ps = G.perm_src[p0 + t];
       srow[t] = ps / G.kk;
       sgam[t] = G.gsc ? G.gsc[ps] : 1.f;
     }
-    __syncthreads();
   }
+  if (GATHER || PROJ) __syncthreads();
   f32x4_t acc[NM][4];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
@@ -246,6 +267,10 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
       const int b = cc - (cc / (nj * 16)) * nj * 16;
       rl[cc][pp] = f2bf(pc + pp < hi && b < G.r ? rv[u] : 0.f);
     }
+    if constexpr (PROJ) {   // (piece cg of row r at cg ^ (r & 15))
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wrow[8 * oct + i][cg ^ ((8 * oct + i) & 15)] = in[i];
+    }
     // 8 x 8 transpose of 16-bit elements: column j gets rows 0..7
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -263,6 +288,19 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
     }
     if (pc + WG_ROWS < hi) load(pc + WG_ROWS);
     lds_barrier();
+    if constexpr (PROJ) {
+      // D[j][p] = sum_a M[j][a] W(p, a): lane (lr, lg) ends with rank
+      // columns 4 lg .. 4 lg + 3 of row 16 w + lr
+      f32x4_t zp = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int rr = 16 * w + lr;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        zp = mfma32(*reinterpret_cast<const uint4 *>(&ml[lr][32 * ks + 8 * lg]),
+                    wrow[rr][(4 * ks + lg) ^ (rr & 15)], zp);
+      const int p = pc + rr;
+      if (p < hi)
+        *reinterpret_cast<f32x4_t *>(G.zpart + ((size_t)blockIdx.x * G.S + p) * 16 + 4 * lg) = zp;
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       uint4 bw[4];
@@ -381,10 +419,14 @@ void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_
 void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st) {
   const int nm = G.nsrc * ((G.r + 15) / 16);
   dim3 grid((G.wide + WG_COLS - 1) / WG_COLS, max_tiles);
-#define MOE_WG(NM)                                                      \
-  if (gather) wgrad_mfma_kernel<true, NM><<<grid, 256, 0, st>>>(G);     \
-  else wgrad_mfma_kernel<false, NM><<<grid, 256, 0, st>>>(G);
-  if (nm == 1) {
+  const bool proj = G.pm != nullptr;
+#define MOE_WG(NM)                                                             \
+  if (gather) wgrad_mfma_kernel<true, NM, false><<<grid, 256, 0, st>>>(G);     \
+  else wgrad_mfma_kernel<false, NM, false><<<grid, 256, 0, st>>>(G);
+  if (proj) {
+    if (gather) wgrad_mfma_kernel<true, 1, true><<<grid, 256, 0, st>>>(G);
+    else wgrad_mfma_kernel<false, 1, true><<<grid, 256, 0, st>>>(G);
+  } else if (nm == 1) {
     MOE_WG(1)
   } else if (nm == 2) {
     MOE_WG(2)
@@ -395,6 +437,40 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
   dim3 rgrid((unsigned)(((size_t)G.wide * G.r * G.nsrc + 256 * WR_PER - 1) / (256 * WR_PER)),
              (unsigned)std::min(G.E, 64));
   wgrad_reduce_kernel<<<rgrid, 256, 0, st>>>(G);
+}
+
+bool wgrad_can_project(const WgradMArgs &G) {
+  return G.nsrc == 1 && G.r == 16 && G.wide % WG_COLS == 0;
+}
+
+// dZ_s[p * ldz + j] = scale * g_p * sum_q zpart_s[q][p][j] (q ascending, q <
+// nq), j < 16, for one or two sources (blockIdx.y); g_p = gsc[perm_src[p]]
+// when gsc is given, else 1.  Four rank columns per thread.
+__global__ __launch_bounds__(256) void zpart_reduce_kernel(const float *__restrict__ zp0,
+                                                           const float *__restrict__ zp1, int nq,
+                                                           int S, const int32_t *__restrict__ perm_src,
+                                                           const float *__restrict__ gsc, float scale,
+                                                           float *__restrict__ z0, float *__restrict__ z1,
+                                                           int ldz) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)S * 4) return;
+  const int p = (int)(i >> 2), j = 4 * (int)(i & 3);
+  const float *zp = blockIdx.y ? zp1 : zp0;
+  f32x4_t v = *reinterpret_cast<const f32x4_t *>(zp + (size_t)p * 16 + j);
+  for (int q = 1; q < nq; ++q) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t *>(zp + ((size_t)q * S + p) * 16 + j);
+    v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+  }
+  const float g = scale * (gsc ? gsc[perm_src[p]] : 1.f);
+  float *z = (blockIdx.y ? z1 : z0) + (size_t)p * ldz + j;
+  z[0] = g * v[0]; z[1] = g * v[1]; z[2] = g * v[2]; z[3] = g * v[3];
+}
+
+void launch_zpart_reduce(const float *zp0, const float *zp1, int nq, int S,
+                         const int32_t *perm_src, const float *gsc, float scale, float *z0,
+                         float *z1, int ldz, hipStream_t st) {
+  dim3 grid((unsigned)(((size_t)S * 4 + 255) / 256), zp1 ? 2 : 1);
+  zpart_reduce_kernel<<<grid, 256, 0, st>>>(zp0, zp1, nq, S, perm_src, gsc, scale, z0, z1, ldz);
 }
 
 int wgrad_tile_rows() { return WG_TILE; }
