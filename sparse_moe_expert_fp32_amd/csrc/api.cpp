@@ -898,6 +898,12 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A; M.LT0 = lt_d;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
+    // the gate gradient's dots <dy, e_out[p]> come from this product: per row
+    // and 128 columns, dH . H = g_p times their share (in the router-gradient
+    // buffer, which the per-token pass leaves unused)
+    const int nq = 2 * ((f + 255) / 256);
+    float *dgp = moe::token_bwd_covers(d, k) && (size_t)nq * S <= (size_t)T * d ? dx_r : nullptr;
+    M.H = H16; M.dgp = dgp; M.S = (int)S;
     TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, ntiles_m + 8, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
@@ -953,7 +959,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // gate gradient and the per-token sum of dX_perm, one pass per token
     TIMED(MOE_KT_GATE_GRAD, st, {
       if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, E, dx,
-                                 st)) {
+                                 st, dgp, nq)) {
         moe::launch_gate_grad(bf, dy, e_out, topk_idx, gates, slot_pos, wr_t, T, d, k, E, dx_r,
                               nullptr, st);
         moe::launch_unpermute_sum(bf, false, dx_r, dXp, slot_pos, T, d, k, dx, st);

@@ -178,12 +178,18 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(
 //   dx[t]    = sum_j dl_j * W_r[:, e_j] + sum_j dX_perm[p_j]   (j ascending, float32)
 // The same sums as gate_grad_kernel followed by unpermute_sum_kernel, without
 // the float32 router-gradient rows between them.
+//
+// With dgp (the dH product's per-slot partials of g_p <dy_t, e_out[p]>, nq
+// of them in column order) dgamma_j is their sum divided by gamma_j, and the
+// pass over e_out is made only for a token with a gate below 1e-30 (where
+// that division would lose precision).
 template <int KB>
 __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
     const bf16_t *__restrict__ dy, const bf16_t *__restrict__ e_out,
     const int32_t *__restrict__ topk_idx, const float *__restrict__ gates,
     const int32_t *__restrict__ slot_pos, const float *__restrict__ wr_t,
-    const bf16_t *__restrict__ dxp, int T, int d, int k, int E, bf16_t *__restrict__ dx) {
+    const bf16_t *__restrict__ dxp, int T, int d, int k, int E, bf16_t *__restrict__ dx,
+    const float *__restrict__ dgp, int nq) {
   constexpr int KM = 4 * KB;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= T) return;
@@ -198,6 +204,33 @@ __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
     g[j] = gates[(size_t)t * k + jc];
     part[j] = 0.f;
   }
+  bool direct = dgp == nullptr;
+  if (!direct) {
+    // the partials in q order, eight at a time (clamped addresses, so that a
+    // batch's loads issue together; the repeats are not added)
+    const size_t S = (size_t)T * k;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < k) {
+        float s = 0.f;
+        for (int q0 = 0; q0 < nq; q0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = dgp[(size_t)min(q0 + i, nq - 1) * S + p[j]];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (q0 + i < nq) s += v[i];
+        }
+        part[j] = s / g[j];
+        direct |= !(g[j] >= 1e-30f);
+      }
+    }
+    if (direct) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) part[j] = 0.f;
+    }
+  }
+  if (direct)
   for (int c = lane * 8; c < d; c += 512) {
     float gy[8], v[KM][8];
     Vec16<bf16_t>::ld(dy + (size_t)t * d + c, gy);
@@ -215,8 +248,10 @@ __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     float s = part[j];
+    if (direct) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    }
     part[j] = s;
     if (j < k) mean = fmaf(g[j], s, mean);
   }
@@ -351,14 +386,17 @@ void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_
                                                 (float *)dO);
 }
 
+bool token_bwd_covers(int d, int k) { return d % 8 == 0 && k <= 16; }
+
 bool launch_token_bwd(const void *dy, const void *e_out, const int32_t *topk_idx,
                       const float *gates, const int32_t *slot_pos, const float *wr_t,
-                      const void *dxp, int Tn, int d, int k, int E, void *dx, hipStream_t st) {
-  if (d % 8 != 0 || k > 16) return false;
+                      const void *dxp, int Tn, int d, int k, int E, void *dx, hipStream_t st,
+                      const float *dgp, int nq) {
+  if (!token_bwd_covers(d, k)) return false;
   const int wgrid = (Tn + 3) / 4;
   const bf16_t *a = (const bf16_t *)dy, *b = (const bf16_t *)e_out, *c = (const bf16_t *)dxp;
   bf16_t *o = (bf16_t *)dx;
-#define MOE_TB(KB) token_bwd_wave_kernel<KB><<<wgrid, 256, 0, st>>>(a, b, topk_idx, gates, slot_pos, wr_t, c, Tn, d, k, E, o)
+#define MOE_TB(KB) token_bwd_wave_kernel<KB><<<wgrid, 256, 0, st>>>(a, b, topk_idx, gates, slot_pos, wr_t, c, Tn, d, k, E, o, dgp, nq)
   switch ((k + 3) / 4) {
     case 1: MOE_TB(1); break;
     case 2: MOE_TB(2); break;

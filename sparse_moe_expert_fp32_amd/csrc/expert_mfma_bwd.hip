@@ -458,37 +458,56 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
 
     // epilogue: 8-byte loads of G, U and 8-byte stores of the results
     const bool cols_ok = c0 + 128 * wn2 < N;   // N is a multiple of 128
+    // mode 0 with dgp: the row's dot of dH and H over the wave's 128 columns
+    // (H read along with G and U)
+    const bool want_dg = MODE == 0 && A.dgp != nullptr;
 #pragma unroll
     for (int m = 0; m < NMH; ++m) {
       const int r = rbase + 16 * m;
-      if (!cols_ok || r >= rows) continue;
-      const size_t p = (size_t)(p0 + r);
+      float hdot = 0.f;
+      if (cols_ok && r < rows) {
+        const size_t p = (size_t)(p0 + r);
 #pragma unroll
-      for (int nf = 0; nf < 8; ++nf) {
-        const int c = ocol + 16 * nf;
-        const f32x4_t a = acc[m][nf];
-        if (MODE == 0) {
-          // the forward saved the SwiGLU backward's multipliers
-          // mG = U s (1 + G (1 - s)) and mU = G s
-          const size_t o = p * N + c;
-          const u32x2_t gw = *reinterpret_cast<const u32x2_t *>(&A.G[o]);
-          const u32x2_t uw = *reinterpret_cast<const u32x2_t *>(&A.U[o]);
-          const float mg[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
-                               __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xffff0000u)};
-          const float mu[4] = {__uint_as_float(uw.x << 16), __uint_as_float(uw.x & 0xffff0000u),
-                               __uint_as_float(uw.y << 16), __uint_as_float(uw.y & 0xffff0000u)};
-          float dg[4], du[4];
+        for (int nf = 0; nf < 8; ++nf) {
+          const int c = ocol + 16 * nf;
+          const f32x4_t a = acc[m][nf];
+          if (MODE == 0) {
+            // the forward saved the SwiGLU backward's multipliers
+            // mG = U s (1 + G (1 - s)) and mU = G s
+            const size_t o = p * N + c;
+            const u32x2_t gw = *reinterpret_cast<const u32x2_t *>(&A.G[o]);
+            const u32x2_t uw = *reinterpret_cast<const u32x2_t *>(&A.U[o]);
+            const float mg[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
+                                 __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xffff0000u)};
+            const float mu[4] = {__uint_as_float(uw.x << 16), __uint_as_float(uw.x & 0xffff0000u),
+                                 __uint_as_float(uw.y << 16), __uint_as_float(uw.y & 0xffff0000u)};
+            float dg[4], du[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dg[i] = a[i] * mg[i];
-            du[i] = a[i] * mu[i];
+            for (int i = 0; i < 4; ++i) {
+              dg[i] = a[i] * mg[i];
+              du[i] = a[i] * mu[i];
+            }
+            *reinterpret_cast<u32x2_t *>(&A.dG[o]) = u32x2_t{cvt_pk_bf16(dg[0], dg[1]), cvt_pk_bf16(dg[2], dg[3])};
+            *reinterpret_cast<u32x2_t *>(&A.dU[o]) = u32x2_t{cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
+            if (want_dg) {
+              const u32x2_t hw = *reinterpret_cast<const u32x2_t *>(&A.H[o]);
+              hdot = fmaf(a[0], __uint_as_float(hw.x << 16), hdot);
+              hdot = fmaf(a[1], __uint_as_float(hw.x & 0xffff0000u), hdot);
+              hdot = fmaf(a[2], __uint_as_float(hw.y << 16), hdot);
+              hdot = fmaf(a[3], __uint_as_float(hw.y & 0xffff0000u), hdot);
+            }
+          } else {
+            *reinterpret_cast<u32x2_t *>(&A.out[p * A.ldo + c]) =
+                u32x2_t{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3])};
           }
-          *reinterpret_cast<u32x2_t *>(&A.dG[o]) = u32x2_t{cvt_pk_bf16(dg[0], dg[1]), cvt_pk_bf16(dg[2], dg[3])};
-          *reinterpret_cast<u32x2_t *>(&A.dU[o]) = u32x2_t{cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
-        } else {
-          *reinterpret_cast<u32x2_t *>(&A.out[p * A.ldo + c]) =
-              u32x2_t{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3])};
         }
+      }
+      if (want_dg) {
+        // the four lanes of the row (lane groups), in a fixed order
+        hdot += __shfl_xor(hdot, 16);
+        hdot += __shfl_xor(hdot, 32);
+        if (lg2 == 0 && r < rows)
+          A.dgp[(size_t)(2 * (c0 / 256) + wn2) * A.S + p0 + r] = hdot;
       }
     }
   }

@@ -29,9 +29,13 @@ void launch_gate_grad(bool bf16, const void *dy, const void *e_out, const int32_
 // matrix-core path (bf16, no dO): the gate gradient and the gather of dX in
 // one pass per token, dx[t] = sum_j dl_j W_r[:, e_j] + sum_j dxp[p_j]; returns
 // false (nothing launched) when the shape is not covered (d % 8, k > 16)
+bool token_bwd_covers(int d, int k);   // the shapes launch_token_bwd takes
+// dgp (optional): the partials of the dH product (nq per slot, [nq][S]),
+// from which dgamma = sum / g replaces the pass over e_out where g >= 1e-30
 bool launch_token_bwd(const void *dy, const void *e_out, const int32_t *topk_idx,
                       const float *gates, const int32_t *slot_pos, const float *wr_t,
-                      const void *dxp, int T, int d, int k, int E, void *dx, hipStream_t st);
+                      const void *dxp, int T, int d, int k, int E, void *dx, hipStream_t st,
+                      const float *dgp = nullptr, int nq = 0);
 void launch_unpermute_sum(bool bf16, bool dxp_f32, const float *dx_r, const void *dxp,
                           const int32_t *slot_pos, int T, int d, int k, void *dx,
                           hipStream_t st);
@@ -186,6 +190,10 @@ struct MfmaGemmTArgs {
   const uint16_t *LT0, *LT1;              // the same transposed, [E][N][r] (rank 16; or null)
   const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: dG = dH G, dU = dH U ([S][N]; G, U the saved multipliers)
   uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
+  // mode 0, optional: dgp[q][p] = sum over the q-th 128 columns c of dH[p][c]
+  // H[p][c] (H [S][N] the forward's SwiGLU output; q < 2 NT; S rows); with
+  // the gate applied to the rows this is g_p times <dy, e_out[p]>
+  const uint16_t *H; float *dgp; int S;
 };
 int mfma_t_tile_rows();         // rows of a full tile (a multiple of 32)
 int mfma_t_tile_cols();

@@ -77,6 +77,20 @@ def test_routing_collapse_to_one_expert(cuda_ok):
     show("collapse", rep)
 
 
+def test_vanishing_gate_takes_the_direct_gate_gradient(cuda_ok):
+    """One expert's router bias 200 above the rest: every token's second gate
+    underflows to 0 in float32, so the per-token pass cannot divide the dH
+    partials by it and takes the dots with e_out instead."""
+    cfg = cfg_of(T=96, E=8, k=2, cfg_id=241, router_bias_var=0.0)
+    inp = inputs.generate(cfg, 0)
+    b = np.zeros(cfg.E, np.float32)
+    b[5] = 200.0
+    inp["b_router"] = b
+    rep, gpu = full_parity(cfg, inp)
+    assert gpu["counts"][5] == cfg.T
+    show("vanishing gate", rep)
+
+
 def test_router_dyadic_bit_exact(cuda_ok):
     """x in {i/16}, W_r in {j/64}: every fp32 partial sum is exact, so the GPU
     logits equal the oracle's bit for bit and routing needs no tie exemption."""
