@@ -184,10 +184,15 @@ int persistent_grid(int blocks_per_cu = 1) {
   return (cus * blocks_per_cu) & ~7;
 }
 
+// floats of two [tiles][d_ff][r] adapter-gradient partial buffers
+size_t part2_floats(const moe_dims *d) {
+  return 2 * max_tiles(d, moe::wgrad_tile_rows()) * (size_t)d->d_ff * d->rank;
+}
+
 // ---- adapter backward workspace
 struct BwdLayout {
-  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, bt, lt, wt,
-      wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
+  size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, part2, bt,
+      lt, wt, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
   BwdLayout(const moe_dims *d, int flags) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
     const bool mf = use_mfma(d);
@@ -205,6 +210,8 @@ struct BwdLayout {
     ntiles_w = mf ? c.take((2 + 2 * (size_t)d->n_experts) * sizeof(int)) : 0;
     part = mf ? c.take(max_tiles(d, moe::wgrad_tile_rows()) * 2 * std::max(dm, f) * d->rank * 4)
               : 0;
+    // the partials of the gate and up dB passes, reduced together with dA_d's
+    part2 = mf ? c.take(part2_floats(d) * 4) : 0;
     // B of down, gate, up transposed to [E][r][N] (bf16)
     bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
     // A of down, gate, up transposed to [E][N][r] (bf16), for rank 16
@@ -851,8 +858,9 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
 
     // The projections dZ = lam dOut B ride along the passes that form dB over
     // the same rows (rank 16, widths multiples of 256): each writes per
-    // 256-column partials, which launch_zpart_reduce adds.  The partials live
-    // in the dX_perm buffer, which is written only at the end.
+    // 256-column partials, which launch_lowrank_reduce adds (together with
+    // the adapter-gradient partials of the passes before it).  The dZ
+    // partials live in the dX_perm buffer, which is written only at the end.
     float *zpart = reinterpret_cast<float *>(dXp);
     const size_t dxp_bytes = (size_t)S * d * 2;
     moe::ProjMArgs Q{};
@@ -870,9 +878,10 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
     if (moe::wgrad_can_project(W) && (size_t)(d / 256) * S * 64 <= dxp_bytes) {
       W.pm = bt_d; W.zpart = zpart;
-      moe::launch_wgrad_mfma(W, mtw, true, st);
-      moe::launch_zpart_reduce(zpart, nullptr, d / 256, (int)S, perm_src, gates, lam, dZ + 2 * r,
-                               nullptr, 3 * r, st);
+      moe::launch_wgrad_mfma(W, mtw, true, st, false);
+      const moe::ZpartJob zj{zpart, nullptr, d / 256, (int)S, perm_src, gates, lam, dZ + 2 * r,
+                             nullptr, 3 * r};
+      moe::launch_lowrank_reduce(&W, 1, &zj, st);
     } else {
       Q.a = (const uint16_t *)dy; Q.lda = d; Q.gsc = gates; Q.K = d; Q.m0 = bt_d;
       Q.Z0 = dZ + 2 * r;
@@ -906,22 +915,29 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     M.H = H16; M.dgp = dgp; M.S = (int)S;
     TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, ntiles_m + 8, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
-    W.w = H16; W.ldw = f; W.rr = dZ + 2 * r; W.wide = f; W.scale = 1.f; W.out = dA_down;
-    W.oe = (size_t)r * f; W.oa = 1; W.ob = f;
-    moe::launch_wgrad_mfma(W, mtw, false, st);
+    moe::WgradMArgs Wd = W;
+    Wd.w = H16; Wd.ldw = f; Wd.rr = dZ + 2 * r; Wd.wide = f; Wd.scale = 1.f; Wd.out = dA_down;
+    Wd.oe = (size_t)r * f; Wd.oa = 1; Wd.ob = f;
     // dB [f][r] = lam sum_p dG[p][n] Z[p][j] and dZ_g = lam dG B_g (up: dU, Z_u, B_u)
     W.w = (const uint16_t *)dG; W.ldw = f; W.rr = Z; W.wide = f; W.scale = lam; W.out = dB_gate;
     W.oe = (size_t)f * r; W.oa = r; W.ob = 1;
     const size_t zq = (size_t)(f / 256) * S * 16;   // floats of one matrix's partials
     if (moe::wgrad_can_project(W) && 2 * zq * 4 <= dxp_bytes) {
-      W.pm = bt_g; W.zpart = zpart;
-      moe::launch_wgrad_mfma(W, mtw, false, st);
-      W.w = (const uint16_t *)dU; W.rr = Z + r; W.out = dB_up; W.pm = bt_u; W.zpart = zpart + zq;
-      moe::launch_wgrad_mfma(W, mtw, false, st);
-      moe::launch_zpart_reduce(zpart, zpart + zq, f / 256, (int)S, nullptr, nullptr, lam, dZ,
-                               dZ + r, 3 * r, st);
-      W.pm = nullptr; W.zpart = nullptr;
+      // dA_d, dB_g and dB_u keep their partials apart (dA_d in the shared
+      // buffer, dB_g and dB_u in their own), reduced in one launch with dZ
+      moe::launch_wgrad_mfma(Wd, mtw, false, st, false);
+      moe::WgradMArgs Wg = W, Wu = W;
+      Wg.pm = bt_g; Wg.zpart = zpart; Wg.part = at<float>(ws, L.part2);
+      Wu.w = (const uint16_t *)dU; Wu.rr = Z + r; Wu.out = dB_up; Wu.pm = bt_u;
+      Wu.zpart = zpart + zq; Wu.part = Wg.part + part2_floats(dims) / 2;
+      moe::launch_wgrad_mfma(Wg, mtw, false, st, false);
+      moe::launch_wgrad_mfma(Wu, mtw, false, st, false);
+      const moe::WgradMArgs three[3] = {Wd, Wg, Wu};
+      const moe::ZpartJob zj{zpart, zpart + zq, f / 256, (int)S, nullptr, nullptr, lam, dZ,
+                             dZ + r, 3 * r};
+      moe::launch_lowrank_reduce(three, 3, &zj, st);
     } else {
+      moe::launch_wgrad_mfma(Wd, mtw, false, st);
       Q.a = (const uint16_t *)dG; Q.lda = f; Q.K = f; Q.m0 = bt_g; Q.Z0 = dZ;
       moe::launch_proj_mfma(Q, mtp, false, st);
       Q.a = (const uint16_t *)dU; Q.m0 = bt_u; Q.Z0 = dZ + r;

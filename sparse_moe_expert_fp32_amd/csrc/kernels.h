@@ -241,14 +241,22 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
   const uint16_t *pm; float *zpart; int S;
 };
 int wgrad_tile_rows();
-void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st);
+// reduce = false: the per-tile partials are left for launch_lowrank_reduce
+void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st,
+                       bool reduce = true);
 bool wgrad_can_project(const WgradMArgs &G);
 // z_s[p * ldz + j] = scale * g_p * (sum over the nq ranges of zp_s[q][p][j]),
 // j < 16, for z0 (from zp0) and, when zp1 is given, z1 (from zp1); g_p =
 // gsc[perm_src[p]] when gsc is given, else 1
-void launch_zpart_reduce(const float *zp0, const float *zp1, int nq, int S,
-                         const int32_t *perm_src, const float *gsc, float scale, float *z0,
-                         float *z1, int ldz, hipStream_t st);
+struct ZpartJob {
+  const float *zp0, *zp1; int nq, S;
+  const int32_t *perm_src; const float *gsc; float scale;
+  float *z0, *z1; int ldz;
+};
+// the reductions of up to three adapter-gradient passes launched with
+// reduce = false (each with its own partial buffer) and, optionally, of one
+// set of projection partials, in one launch
+void launch_lowrank_reduce(const WgradMArgs *w, int nw, const ZpartJob *z, hipStream_t st);
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
 // bf16 [E][r][N] -> [E][N][r]
 void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st);

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(64 * NW, NF == 4 ? 1 : 2) void proj_mfma_kernel(con
 // forms the projection of the rows onto M = [E][16][wide] (the adapter B of
 // the matrix, transposed), Z'_q[p][j] = sum over the block's 256 columns
 // (column range q) of W(p, a) M[e][j][a], as partials zpart[q][p][j];
-// launch_zpart_reduce adds the ranges.  The staged chunk is also stored as
+// launch_lowrank_reduce adds the ranges.  The staged chunk is also stored as
 // it came (rows of 16-byte pieces, piece index XOR-swizzled by row), and
 // each wave multiplies 16 of its rows by M, also staged in LDS.
 constexpr int WG_COLS = 256, WG_ROWS = 64, WG_TILE = 512;
@@ -341,13 +341,13 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
 constexpr int WR_PER = 4;
 
 // Only the experts on the list (empty ones, which get zeros, and split ones);
-// block row y takes list entries y, y + gridDim.y, ...
-__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const WgradMArgs G) {
+// block row by (of ny) takes list entries by, by + ny, ...
+DEV void wgrad_reduce_body(const WgradMArgs &G, int bx, int by, int ny) {
   const int tid = threadIdx.x;
   const size_t per = (size_t)G.wide * G.r;
-  const size_t i0 = ((size_t)blockIdx.x * 256 + tid) * WR_PER;
+  const size_t i0 = ((size_t)bx * 256 + tid) * WR_PER;
   const int nl = G.multi[0];
-  for (int q = blockIdx.y; q < nl; q += gridDim.y) {
+  for (int q = by; q < nl; q += ny) {
     const int e = G.multi[1 + q];
     const int count = G.offsets[e + 1] - G.offsets[e];
     const int t0 = count > 0 ? G.tfirst[e] : 0;
@@ -366,6 +366,16 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const WgradMArgs G) {
     }
   }
 }
+
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const WgradMArgs G) {
+  wgrad_reduce_body(G, blockIdx.x, blockIdx.y, gridDim.y);
+}
+
+// blocks of the reduction of one pass: (wide r nsrc / 1024) x min(E, 64)
+__host__ __device__ inline int wgrad_reduce_cols(const WgradMArgs &G) {
+  return (int)(((size_t)G.wide * G.r * G.nsrc + 256 * WR_PER - 1) / (256 * WR_PER));
+}
+__host__ __device__ inline int wgrad_reduce_rows(const WgradMArgs &G) { return G.E < 64 ? G.E : 64; }
 
 // out[e][j][n] = in[e][n][j] for bf16 [E][N][r] -> [E][r][N].  One block per
 // (256 values of n, expert): the block's input is one contiguous run of
@@ -416,7 +426,8 @@ void launch_proj_mfma(const ProjMArgs &P, int max_tiles, bool gather, hipStream_
 #undef MOE_PROJ2
 }
 
-void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st) {
+void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStream_t st,
+                       bool reduce) {
   const int nm = G.nsrc * ((G.r + 15) / 16);
   dim3 grid((G.wide + WG_COLS - 1) / WG_COLS, max_tiles);
   const bool proj = G.pm != nullptr;
@@ -434,8 +445,8 @@ void launch_wgrad_mfma(const WgradMArgs &G, int max_tiles, bool gather, hipStrea
     MOE_WG(4)
   }
 #undef MOE_WG
-  dim3 rgrid((unsigned)(((size_t)G.wide * G.r * G.nsrc + 256 * WR_PER - 1) / (256 * WR_PER)),
-             (unsigned)std::min(G.E, 64));
+  if (!reduce) return;
+  dim3 rgrid((unsigned)wgrad_reduce_cols(G), (unsigned)wgrad_reduce_rows(G));
   wgrad_reduce_kernel<<<rgrid, 256, 0, st>>>(G);
 }
 
@@ -444,33 +455,66 @@ bool wgrad_can_project(const WgradMArgs &G) {
 }
 
 // dZ_s[p * ldz + j] = scale * g_p * sum_q zpart_s[q][p][j] (q ascending, q <
-// nq), j < 16, for one or two sources (blockIdx.y); g_p = gsc[perm_src[p]]
-// when gsc is given, else 1.  Four rank columns per thread.
-__global__ __launch_bounds__(256) void zpart_reduce_kernel(const float *__restrict__ zp0,
-                                                           const float *__restrict__ zp1, int nq,
-                                                           int S, const int32_t *__restrict__ perm_src,
-                                                           const float *__restrict__ gsc, float scale,
-                                                           float *__restrict__ z0, float *__restrict__ z1,
-                                                           int ldz) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)S * 4) return;
+// nq), j < 16, for source src; g_p = gsc[perm_src[p]] when gsc is given,
+// else 1.  Element i: row i / 4, rank columns 4 (i % 4) .. + 3.
+DEV void zpart_reduce_elem(const ZpartJob &Z, size_t i, int src) {
+  if (i >= (size_t)Z.S * 4) return;
   const int p = (int)(i >> 2), j = 4 * (int)(i & 3);
-  const float *zp = blockIdx.y ? zp1 : zp0;
+  const float *zp = src ? Z.zp1 : Z.zp0;
   f32x4_t v = *reinterpret_cast<const f32x4_t *>(zp + (size_t)p * 16 + j);
-  for (int q = 1; q < nq; ++q) {
-    const f32x4_t u = *reinterpret_cast<const f32x4_t *>(zp + ((size_t)q * S + p) * 16 + j);
+  for (int q = 1; q < Z.nq; ++q) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t *>(zp + ((size_t)q * Z.S + p) * 16 + j);
     v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
   }
-  const float g = scale * (gsc ? gsc[perm_src[p]] : 1.f);
-  float *z = (blockIdx.y ? z1 : z0) + (size_t)p * ldz + j;
+  const float g = Z.scale * (Z.gsc ? Z.gsc[Z.perm_src[p]] : 1.f);
+  float *z = (src ? Z.z1 : Z.z0) + (size_t)p * Z.ldz + j;
   z[0] = g * v[0]; z[1] = g * v[1]; z[2] = g * v[2]; z[3] = g * v[3];
 }
 
-void launch_zpart_reduce(const float *zp0, const float *zp1, int nq, int S,
-                         const int32_t *perm_src, const float *gsc, float scale, float *z0,
-                         float *z1, int ldz, hipStream_t st) {
-  dim3 grid((unsigned)(((size_t)S * 4 + 255) / 256), zp1 ? 2 : 1);
-  zpart_reduce_kernel<<<grid, 256, 0, st>>>(zp0, zp1, nq, S, perm_src, gsc, scale, z0, z1, ldz);
+// The deferred reductions of up to three adapter-gradient passes and one set
+// of projection partials in one launch: pass i takes the first cols_i rows_i
+// blocks after the passes before it, then the projection partials (S * 4 /
+// 256 blocks per source).
+struct LowrankReduceArgs {
+  WgradMArgs w[3];
+  int nw;
+  ZpartJob z;
+  int has_z;
+};
+
+__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const LowrankReduceArgs R) {
+  int b = (int)blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (i < R.nw) {
+      const int cols = wgrad_reduce_cols(R.w[i]), rows = wgrad_reduce_rows(R.w[i]);
+      if (b < cols * rows) {
+        wgrad_reduce_body(R.w[i], b % cols, b / cols, rows);
+        return;
+      }
+      b -= cols * rows;
+    }
+  }
+  if (R.has_z) {
+    const int zb = (int)(((size_t)R.z.S * 4 + 255) / 256);
+    zpart_reduce_elem(R.z, (size_t)(b % zb) * 256 + threadIdx.x, b / zb);
+  }
+}
+
+void launch_lowrank_reduce(const WgradMArgs *w, int nw, const ZpartJob *z, hipStream_t st) {
+  LowrankReduceArgs R{};
+  int blocks = 0;
+  R.nw = std::min(nw, 3);
+  for (int i = 0; i < R.nw; ++i) {
+    R.w[i] = w[i];
+    blocks += wgrad_reduce_cols(w[i]) * wgrad_reduce_rows(w[i]);
+  }
+  if (z) {
+    R.z = *z;
+    R.has_z = 1;
+    blocks += (int)(((size_t)z->S * 4 + 255) / 256) * (z->zp1 ? 2 : 1);
+  }
+  if (blocks > 0) lowrank_reduce_kernel<<<blocks, 256, 0, st>>>(R);
 }
 
 int wgrad_tile_rows() { return WG_TILE; }
