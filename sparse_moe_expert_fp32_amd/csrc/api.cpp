@@ -127,13 +127,13 @@ size_t qt_slot_bytes(const moe_dims *d) {
 size_t qf_bytes(const moe_dims *d) { return qt_slot_bytes(d); }
 
 // The forward products of short batches (decode: a few rows per expert) run
-// every expert's rows in tiles of 32 in a kernel that holds only 32 rows, so
+// every expert's rows in tiles of 16 in a kernel that holds only 16 rows, so
 // more of its blocks are resident and keep more weight loads in flight; from
 // 128 tokens they run tiles of 128, each as the shortest class that holds its
 // rows.  Either way one launch per product.
 constexpr int kFwdShortBelowT = 128;
 int fwd_tile_rows(const moe_dims *d) {
-  return d->T < kFwdShortBelowT ? 32 : moe::mfma_tile_rows();
+  return d->T < kFwdShortBelowT ? 16 : moe::mfma_tile_rows();
 }
 
 // ---- expert forward workspace

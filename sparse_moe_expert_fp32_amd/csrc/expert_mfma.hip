@@ -139,10 +139,11 @@ DEV void fwd_stage_sched(std::integer_sequence<int, I...>) {
 // so each unpacked weight fragment feeds NM matrix instructions.  NM (2, 4,
 // 6, 8) is the number of 16-row fragments of the item: a tile runs as the
 // shortest class that holds its rows, so a short tail tile costs only its
-// rows.  Resident blocks per CU as the registers allow: the 32-row kernel of
-// short batches (2-slot ring of 28 KB, at most 128 VGPRs) four, the others
-// two.
+// rows.  Two resident blocks per CU (the 16-row kernel of short batches:
+// short_bpc).
 constexpr int gm_bpc(int NM) { return NM <= 2 ? 4 : GM_BPC; }
+// resident blocks per CU of the short-batch kernel (16-row items)
+constexpr int short_bpc(int MODE) { return MODE == 0 ? 5 : 4; }
 
 // Per-launch values every work item uses.
 struct GmCtx {
@@ -271,6 +272,7 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       const char *zb = reinterpret_cast<const char *>(uniform_ptr(A.Z0));
 #pragma unroll
       for (int i = 0; i < AOPS; ++i) {
+        if (AOPS * wu + i >= 2 * NM) continue;   // (16-row items: waves 0-1 only)
         const int r = min(8 * (AOPS * w + i) + (lane >> 3), GM_BM - 1);
         const int c = ((lane & 7) ^ row_swz(r)) & (MODE == 0 ? 7 : 3);   // Z_d: 4 chunks
         const uint32_t zo = (uint32_t)(p0 + min(r, rows - 1)) * (uint32_t)(A.ldz * 4) + c * 16;
@@ -302,7 +304,8 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       asm volatile("" : "+s"(sa), "+s"(sb));
 #pragma unroll
       for (int i = 0; i < AOPS; ++i)
-        dma16(abase + (size_t)ja * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
+        if (AOPS * wu + i < 2 * NM)   // (16-row items: waves 0-1 only)
+          dma16(abase + (size_t)ja * GM_KS * 2, src_off[i], sa + slot * ST_A + i * 1024);
       // stage step of the int4 words: 32 bytes (plain), a whole stage of
       // the expert's columns, 32 N bytes (packed)
 #pragma unroll
@@ -335,7 +338,7 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
     // matrix instructions.  The scheduling-group barriers at the end pin that
     // order (the scheduler would otherwise cluster every read right before
     // its use to save registers, exposing the LDS latency).
-    constexpr int PD = NM >= 8 ? 2 : 3;   // A read distance, in fragments
+    constexpr int PD = NM >= 8 ? 2 : (2 * NM < 3 ? 2 * NM : 3);   // A read distance, in fragments
     auto compute = [&](auto odd, int slot) {   // odd: compile-time stage parity
       constexpr bool EVEN = !decltype(odd)::value;
       __builtin_amdgcn_sched_barrier(0);
@@ -659,16 +662,18 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
   }
 }
 
-// Short batches (decode): every expert's rows in tiles of 32 (a list of
-// launch_build_tiles), all of them 32-row items.  The ring holds only 32
-// rows, so more blocks are resident per CU (gm_bpc(2)), which keeps more
-// weight loads in flight where the products stream the weights of many
-// experts for a few rows each.  The items are split into eight contiguous
-// ranges, one per XCD, dealt round-robin to the XCD's blocks.
+// Short batches (decode): every expert's rows in tiles of 16 (a list of
+// launch_build_tiles), all of them 16-row items.  The ring holds only 16
+// rows, so more blocks are resident per CU (short_bpc: five for gate/up, whose
+// six column tiles per expert then fill two rounds instead of leaving most of
+// a third empty at decode sizes; four for down), which keeps more weight loads
+// in flight where the products stream the weights of many experts for a few
+// rows each.  The items are split into eight contiguous ranges, one per XCD,
+// dealt round-robin to the XCD's blocks.
 template <int MODE, bool EPL, bool QP>
-__global__ __launch_bounds__(256, gm_bpc(2)) void grouped_gemm_short_kernel(
+__global__ __launch_bounds__(256, short_bpc(MODE)) void grouped_gemm_short_kernel(
     const MfmaGemmArgs A, const int *__restrict__ ntiles) {
-  constexpr int NM = 2;
+  constexpr int NM = 1;
   constexpr int ST_A = 16 * NM * GM_KS * 2;
   __shared__ __attribute__((aligned(32))) uint4 ringA[2][ST_A / 16];
   __shared__ uint4 ringB[2][ST_B / 16];
@@ -797,11 +802,11 @@ void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int
 #undef MOE_GG3
 }
 
-// The short-batch launch over 32-row tiles (ntiles: the count of the list);
-// grid: GM_BPC blocks per CU, scaled to gm_bpc(2)
+// The short-batch launch over 16-row tiles (ntiles: the count of the list);
+// grid: GM_BPC blocks per CU, scaled to short_bpc(mode)
 void launch_grouped_gemm_short(int mode, const MfmaGemmArgs &A, const int *ntiles, int grid,
                                hipStream_t st) {
-  grid = (grid / GM_BPC * gm_bpc(2)) & ~7;
+  grid = (grid / GM_BPC * short_bpc(mode)) & ~7;
   const bool epl = A.r == 16 && (A.ldz & 3) == 0;
   // the packed base where given
   const bool qp = A.qp0 && (mode == 1 || A.qp1);

@@ -166,8 +166,8 @@ void launch_pack_fwd_int8(const uint8_t *q, int E, int N, int K, uint8_t *qf, hi
 // eight counters, zero at launch)
 void launch_grouped_gemm(int mode, const MfmaGemmArgs &A, const int *ntiles, int *ctr, int grid,
                          hipStream_t st);
-// short batches: one launch over 32-row tiles of launch_build_tiles
-// (ntiles: their count), every item a 32-row item
+// short batches: one launch over 16-row tiles of launch_build_tiles
+// (ntiles: their count), every item a 16-row item
 void launch_grouped_gemm_short(int mode, const MfmaGemmArgs &A, const int *ntiles, int grid,
                                hipStream_t st);
 
