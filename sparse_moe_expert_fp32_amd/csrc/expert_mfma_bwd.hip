@@ -144,6 +144,18 @@ __global__ __launch_bounds__(256) void transpose_q_int8_kernel(const uint8_t *__
 // stage's 64 reduction steps for the block's two column groups.
 constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage holds the item's rows)
 
+// Output columns of a wave's 128: fragment nf (of 8) and matrix-instruction
+// row j (0..15) hold column 32 (nf >> 1) + 8 (j >> 2) + 4 (nf & 1) + (j & 3),
+// so that a lane's values of fragments 2t and 2t + 1 are 8 adjacent columns
+// (16-byte accesses in the epilogue).  In LDS, column c of the item's 256 (the
+// int4 words of a stage, and the transposed adapter rows) sits at position
+// c ^ (4 bit3(c)) with its 16-byte halves swapped when bit 4 of c is set:
+// the 16 columns one fragment reads then touch every bank once per half
+// wave.
+DEV int gt_col(int nf, int j) { return 32 * (nf >> 1) + 8 * (j >> 2) + 4 * (nf & 1) + (j & 3); }
+DEV int gt_pos(int c) { return c ^ (4 * ((c >> 3) & 1)); }
+DEV int gt_half(int c) { return (c >> 4) & 1; }
+
 // ------------------------------------------------------------------ GEMM --
 // A bf16x8 fragment times 8 per-k scales, rounded back to bf16.
 DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
@@ -199,15 +211,14 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       const int arow = tokrows ? A.perm_src[p] / A.kk : p;
       aoff[i] = (uint32_t)arow * (uint32_t)(A.lda * 2) + c * 16;
     }
-    // int4 staging: wave w, load i covers columns 32 (2w + i) .. +31, 32 bytes
-    // each; the two 16-byte halves of a column trade places when bit 3 of its
-    // block column (bit 4 of the lane) is set, so that the 8-byte reads of 16
-    // consecutive columns by half a wave touch every bank once
+    // int4 staging: wave w, load i fills LDS positions 32 (2w + i) .. +31, 32
+    // bytes each, lane L half L & 1 of position (L >> 1) (gt_pos, gt_half)
     uint32_t boff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int col = min(c0 + 32 * (2 * w + i) + (lane >> 1), N - 1);
-      boff[i] = (uint32_t)col * 32 + 16 * ((lane & 1) ^ ((lane >> 4) & 1));
+      const int c = gt_pos(32 * (2 * w + i) + (lane >> 1));
+      const int col = min(c0 + c, N - 1);
+      boff[i] = (uint32_t)col * 32 + 16 * ((lane & 1) ^ gt_half(c));
     }
     // scale staging: wave w, lanes < 32: column group (w >> 1), k 32 (w & 1) + lane
     const int sg = min(c0 / 128 + (w >> 1), G - 1);
@@ -219,8 +230,13 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
                    ls = ldsS + ((wu >> 1) * GT_KS + 32 * (wu & 1)) * 4;
     // per-lane LDS read bases (bytes); the rest of every read address is a
     // compile-time constant
+    // (fragment nf reads column 128 wn + gt_col(nf, lr): its LDS position is
+    // that of fragment nf & 1 plus 32 (nf >> 1) columns)
     const uint32_t offA0 = opaque(ldsA + (16 * NMH * wm + lr) * 128 + (((2 * lg) ^ row_swz(lr)) << 4)),
-                   offB = opaque(ldsB + (128 * wn + lr) * 32 + 16 * ((lg >> 1) ^ (lr >> 3)) + 8 * (lg & 1)),
+                   offB0 = opaque(ldsB + (128 * wn + gt_pos(gt_col(0, lr))) * 32 +
+                                  16 * ((lg >> 1) ^ gt_half(gt_col(0, lr))) + 8 * (lg & 1)),
+                   offB1 = opaque(ldsB + (128 * wn + gt_pos(gt_col(1, lr))) * 32 +
+                                  16 * ((lg >> 1) ^ gt_half(gt_col(1, lr))) + 8 * (lg & 1)),
                    offS = opaque(ldsS + (wn * GT_KS + 16 * lg) * 4);
 
     // the row gates (mode 0, rows of dy by token), fetched now for the epilogue
@@ -252,8 +268,9 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       const char *lb16 = reinterpret_cast<const char *>(uniform_ptr((part ? A.LT1 : A.LT0) + (size_t)e * N * 16));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int col = min(c0 + 32 * (2 * w + i) + (lane >> 1), N - 1);
-        dma16(lb16, (uint32_t)col * 32u + 16 * ((lane & 1) ^ ((lane >> 4) & 1)), sb + slot * TS_B + i * 1024);
+        const int c = gt_pos(32 * (2 * w + i) + (lane >> 1));
+        const int col = min(c0 + c, N - 1);
+        dma16(lb16, (uint32_t)col * 32u + 16 * ((lane & 1) ^ gt_half(c)), sb + slot * TS_B + i * 1024);
       }
     };
     // The epilogue stages (EPL) are issued whole at the start of their step.
@@ -313,7 +330,8 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       const StageSrc src = stage_src(ld ? jl : 0);
       u32x2_t bw[8];
 #pragma unroll
-      for (int nf = 0; nf < 8; ++nf) bw[nf] = lds_ld<u32x2_t>(offB + slot * TS_B + nf * 16 * 32);
+      for (int nf = 0; nf < 8; ++nf)
+        bw[nf] = lds_ld<u32x2_t>((nf & 1 ? offB1 : offB0) + slot * TS_B + (nf >> 1) * 32 * 32);
       // substep 1 reads chunk 2 lg + 1, the neighbouring swizzled chunk
       const uint32_t offA1 = offA0 ^ 16u;
 #pragma unroll
@@ -386,13 +404,14 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
 
     // ---- epilogue indices, re-derived from an opaque copy of the thread
     // index: the lane's row in fragment m is rbase + 16 m; its output columns
-    // are ocol + 16 nf .. + 3; col is the column of the A-of-the-matrix
-    // operand lane lr feeds into the adapter product
+    // in fragments 2t and 2t + 1 are ocol + 32 t .. + 7 (gt_col); the
+    // A-of-the-matrix operand lane lr feeds into the adapter product of
+    // fragment nf is column wcol + gt_col(nf, lr)
     int tid2 = threadIdx.x;
     asm volatile("" : "+v"(tid2));
     const int lr2 = tid2 & 15, lg2 = (tid2 >> 4) & 3, wm2 = (tid2 >> 6) & 1, wn2 = tid2 >> 7;
     const int rbase = 16 * NMH * wm2 + lr2;
-    const int ocol = c0 + 128 * wn2 + 4 * lg2, lcol = c0 + 128 * wn2 + lr2;
+    const int wcol = c0 + 128 * wn2, ocol = wcol + 8 * lg2;
 
     // remove the 136 offset of the int4 operand (and apply the row's gate
     // when the rows are dy by token)
@@ -411,9 +430,11 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
         const int ls = src ? (es == 2 ? 0 : es + 1) : es;
         short4_t lv[8];
 #pragma unroll
-        for (int nf = 0; nf < 8; ++nf)
-          lv[nf] = lds_ld<short4_t>(ldsB + ls * TS_B + (128 * wn2 + 16 * nf + lr2) * 32 +
-                                    16 * ((lg2 >> 1) ^ (lr2 >> 3)) + 8 * (lg2 & 1));
+        for (int nf = 0; nf < 8; ++nf) {
+          const int c = gt_col(nf, lr2);
+          lv[nf] = lds_ld<short4_t>(ldsB + ls * TS_B + (128 * wn2 + gt_pos(c)) * 32 +
+                                    16 * ((lg2 >> 1) ^ gt_half(c)) + 8 * (lg2 & 1));
+        }
 #pragma unroll
         for (int m = 0; m < NMH; ++m) {
           const int r = rbase + 16 * m;
@@ -436,7 +457,7 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
           short4_t lv[8];
 #pragma unroll
           for (int nf = 0; nf < 8; ++nf) {
-            const int c = min(lcol + 16 * nf, N - 1);
+            const int c = min(wcol + gt_col(nf, lr2), N - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               lv[nf][i] = (short)(Lm[((size_t)e * A.r + min(j0 + 4 * lg2 + i, A.r - 1)) * N + c] &
@@ -456,11 +477,13 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       }
     }
 
-    // epilogue: 8-byte loads of G, U and 8-byte stores of the results
+    // epilogue: per pair of fragments (2t, 2t + 1) a lane holds 8 adjacent
+    // columns of its row: 16-byte loads of G, U (and H) and 16-byte stores
     const bool cols_ok = c0 + 128 * wn2 < N;   // N is a multiple of 128
     // mode 0 with dgp: the row's dot of dH and H over the wave's 128 columns
-    // (H read along with G and U)
     const bool want_dg = MODE == 0 && A.dgp != nullptr;
+    auto lo = [](uint32_t v) { return __uint_as_float(v << 16); };
+    auto hi = [](uint32_t v) { return __uint_as_float(v & 0xffff0000u); };
 #pragma unroll
     for (int m = 0; m < NMH; ++m) {
       const int r = rbase + 16 * m;
@@ -468,37 +491,38 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       if (cols_ok && r < rows) {
         const size_t p = (size_t)(p0 + r);
 #pragma unroll
-        for (int nf = 0; nf < 8; ++nf) {
-          const int c = ocol + 16 * nf;
-          const f32x4_t a = acc[m][nf];
+        for (int t = 0; t < 4; ++t) {
+          const f32x4_t a0 = acc[m][2 * t], a1 = acc[m][2 * t + 1];
+          const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          const int c = ocol + 32 * t;
           if (MODE == 0) {
             // the forward saved the SwiGLU backward's multipliers
             // mG = U s (1 + G (1 - s)) and mU = G s
             const size_t o = p * N + c;
-            const u32x2_t gw = *reinterpret_cast<const u32x2_t *>(&A.G[o]);
-            const u32x2_t uw = *reinterpret_cast<const u32x2_t *>(&A.U[o]);
-            const float mg[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
-                                 __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xffff0000u)};
-            const float mu[4] = {__uint_as_float(uw.x << 16), __uint_as_float(uw.x & 0xffff0000u),
-                                 __uint_as_float(uw.y << 16), __uint_as_float(uw.y & 0xffff0000u)};
-            float dg[4], du[4];
+            const uint4 gw = *reinterpret_cast<const uint4 *>(&A.G[o]);
+            const uint4 uw = *reinterpret_cast<const uint4 *>(&A.U[o]);
+            const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w}, u4[4] = {uw.x, uw.y, uw.z, uw.w};
+            uint32_t dg[4], du[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              dg[i] = a[i] * mg[i];
-              du[i] = a[i] * mu[i];
+              dg[i] = cvt_pk_bf16(a[2 * i] * lo(g4[i]), a[2 * i + 1] * hi(g4[i]));
+              du[i] = cvt_pk_bf16(a[2 * i] * lo(u4[i]), a[2 * i + 1] * hi(u4[i]));
             }
-            *reinterpret_cast<u32x2_t *>(&A.dG[o]) = u32x2_t{cvt_pk_bf16(dg[0], dg[1]), cvt_pk_bf16(dg[2], dg[3])};
-            *reinterpret_cast<u32x2_t *>(&A.dU[o]) = u32x2_t{cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
+            *reinterpret_cast<uint4 *>(&A.dG[o]) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+            *reinterpret_cast<uint4 *>(&A.dU[o]) = make_uint4(du[0], du[1], du[2], du[3]);
             if (want_dg) {
-              const u32x2_t hw = *reinterpret_cast<const u32x2_t *>(&A.H[o]);
-              hdot = fmaf(a[0], __uint_as_float(hw.x << 16), hdot);
-              hdot = fmaf(a[1], __uint_as_float(hw.x & 0xffff0000u), hdot);
-              hdot = fmaf(a[2], __uint_as_float(hw.y << 16), hdot);
-              hdot = fmaf(a[3], __uint_as_float(hw.y & 0xffff0000u), hdot);
+              const uint4 hw = *reinterpret_cast<const uint4 *>(&A.H[o]);
+              const uint32_t h4[4] = {hw.x, hw.y, hw.z, hw.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                hdot = fmaf(a[2 * i], lo(h4[i]), hdot);
+                hdot = fmaf(a[2 * i + 1], hi(h4[i]), hdot);
+              }
             }
           } else {
-            *reinterpret_cast<u32x2_t *>(&A.out[p * A.ldo + c]) =
-                u32x2_t{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3])};
+            *reinterpret_cast<uint4 *>(&A.out[p * A.ldo + c]) =
+                make_uint4(cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]),
+                           cvt_pk_bf16(a[4], a[5]), cvt_pk_bf16(a[6], a[7]));
           }
         }
       }
