@@ -204,7 +204,8 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
  *   offsets, perm_src as written by moe_permute (device)
  *   e_out    act [S][d] in permuted order (out)
  *   save     NULL, or moe_save_size() bytes that moe_adapter_bwd consumes
- *            (opaque: the intermediates the backward needs) (out) */
+ *            (opaque: the intermediates the backward needs) (out)
+ * x, e_out and save must be 16-byte aligned (MOE_ERR_INVALID otherwise). */
 moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
                           const int32_t *perm_src, moe_qlora gate, moe_qlora up,
                           moe_qlora down, void *e_out, void *save, void *ws,

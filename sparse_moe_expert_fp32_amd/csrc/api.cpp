@@ -573,9 +573,11 @@ namespace {
 
 moe_status check_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
                             const int32_t *perm_src, const moe_qlora &gate, const moe_qlora &up,
-                            const moe_qlora &down, const void *e_out) {
+                            const moe_qlora &down, const void *e_out, const void *save) {
   TRY(check_dims(dims));
   REQUIRE(x && offsets && perm_src && e_out, "moe_expert_fwd: x, offsets, perm_src, e_out required");
+  REQUIRE((((uintptr_t)x | (uintptr_t)e_out | (uintptr_t)save) & 15) == 0,
+          "moe_expert_fwd: x, e_out and save must be 16-byte aligned");
   TRY(check_qlora(gate, "gate"));
   TRY(check_qlora(up, "up"));
   TRY(check_qlora(down, "down"));
@@ -738,7 +740,7 @@ extern "C" {
 moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *offsets,
                           const int32_t *perm_src, moe_qlora gate, moe_qlora up, moe_qlora down,
                           void *e_out, void *save, void *ws, size_t ws_bytes, void *stream) {
-  TRY(check_expert_fwd(dims, x, offsets, perm_src, gate, up, down, e_out));
+  TRY(check_expert_fwd(dims, x, offsets, perm_src, gate, up, down, e_out, save));
   TRY(check_ws(dims, MOE_CALL_EXPERT_FWD | fwd_flags(save, gate, up, down), ws, ws_bytes));
   return expert_fwd_run(dims, x, offsets, perm_src, gate, up, down, e_out, save, ws, stream);
 }
@@ -746,7 +748,7 @@ moe_status moe_expert_fwd(const moe_dims *dims, const void *x, const int32_t *of
 moe_status moe_expert_fwd_noalloc(const moe_dims *dims, const void *x, const int32_t *offsets,
                                   const int32_t *perm_src, moe_qlora gate, moe_qlora up,
                                   moe_qlora down, void *e_out, void *save, void *stream) {
-  TRY(check_expert_fwd(dims, x, offsets, perm_src, gate, up, down, e_out));
+  TRY(check_expert_fwd(dims, x, offsets, perm_src, gate, up, down, e_out, save));
   const size_t need = ws_bytes_for(dims, MOE_CALL_EXPERT_FWD | fwd_flags(save, gate, up, down));
   if (need > moe::kStaticScratchBytes)
     return fail(MOE_ERR_WORKSPACE,

@@ -164,11 +164,12 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
   constexpr int WCOLS = (MODE == 0 ? 128 : 256) / WAVES;   // block column slots per wave (per matrix in mode 0)
   constexpr int AOPS = (2 * NM + WAVES - 1) / WAVES;       // 8-row A loads per wave and stage
   constexpr int XOPS = 8 / WAVES;                // group-data loads per wave (even stages)
-  // first block column slot of fragment nf relative to the wave's columns:
-  // mode 0 gate slots 0..127 then up 128..255, mode 1 0..255
-  constexpr auto nfc = [](int nf) {
-    return MODE == 0 ? (nf / (NF / 2)) * 128 + (nf % (NF / 2)) * 16 : nf * 16;
-  };
+  // Block column slots (mode 0: gate 0..127, then up 128..255; mode 1:
+  // 0..255).  Matrix-instruction row j of fragment nf is slot w WCOLS +
+  // fpair(nf) + gt_col(nf & 1, j): fragments 0-1 (mode 0: gate) and 2-3 (up)
+  // are pairs whose lanes hold 8 adjacent columns each.
+  static_assert(NF == 4, "the column permutation pairs fragments 0-1 and 2-3");
+  constexpr auto fpair = [](int nf) { return MODE == 0 ? (nf >> 1) * 128 : (nf >> 1) * 32; };
   // a 2-slot ring of half-group stages, its A stages 16 NM rows apart; after
   // the K loop the first 2 KB of the A ring hold the cross-wave row sums of H.
   constexpr int ST_A = 16 * NM * GM_KS * 2;     // A stage: the tile's rows x 64 K
@@ -216,10 +217,12 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
     uint32_t qoff[BOPS];
 #pragma unroll
     for (int i = 0; i < BOPS; ++i) {
-      const int bc = 32 * (BOPS * w + i) + (lane >> 1);
+      // lane L fills half L & 1 of LDS position 32 (BOPS w + i) + L / 2,
+      // which holds block column slot gt_pos of it (halves by gt_half)
+      const int bc = gt_pos(32 * (BOPS * w + i) + (lane >> 1));
       const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
       // (packed base: column c of a stage at 32 c; plain: at c K/2)
-      qoff[i] = (uint32_t)c * (QP ? 32u : (uint32_t)(K / 2)) + 16 * (lane & 1);
+      qoff[i] = (uint32_t)c * (QP ? 32u : (uint32_t)(K / 2)) + 16 * ((lane & 1) ^ gt_half(bc));
     }
     // group data, 8 loads of 64 floats: loads 0-3 the ratios of block
     // columns 64 q + lane (group g at + g N), loads 4-5 the start values of
@@ -251,11 +254,17 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
                    lx = ldsX + wu * XOPS * 256;
     // per-lane LDS read bases (bytes); the rest of every read address is a
     // compile-time constant.  The int4 word lane lr feeds into the first MFMA
-    // operand is block column slot w * WCOLS + nfc + lr; the lane's
-    // accumulator holds the four output columns from slot w * WCOLS + nfc + 4 lg.
+    // operand of fragment nf is block column slot w WCOLS + fpair(nf) +
+    // gt_col(nf & 1, lr) (offB0 / offB1 by the parity of nf); the lane's
+    // accumulator holds the four output columns from slot w WCOLS + fpair(nf)
+    // + 8 lg + 4 (nf & 1).
+    const int bcol0 = gt_col(0, lr), bcol1 = gt_col(1, lr);
     const uint32_t offA0 = opaque(ldsA + lr * 128 + (((2 * lg) ^ row_swz(lr)) << 4)),
-                   offB = opaque(ldsB + (w * WCOLS + lr) * 32 + 8 * lg),
-                   offR = opaque(ldsX + (w * WCOLS + 4 * lg) * 4),
+                   offB0 = opaque(ldsB + (w * WCOLS + gt_pos(bcol0)) * 32 +
+                                  16 * ((lg >> 1) ^ gt_half(bcol0)) + 8 * (lg & 1)),
+                   offB1 = opaque(ldsB + (w * WCOLS + gt_pos(bcol1)) * 32 +
+                                  16 * ((lg >> 1) ^ gt_half(bcol1)) + 8 * (lg & 1)),
+                   offR = opaque(ldsX + (w * WCOLS + 8 * lg) * 4),
                    offC = opaque(ldsX + 1024 + lr * 32);
 
     // The epilogue's operands go through the ring too, as the stage after
@@ -279,12 +288,12 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
         dma16(zb, zo, sa + slot * ST_A + i * 1024);
       }
 #pragma unroll
-      for (int i = 0; i < BOPS; ++i) {
-        const int bc = 32 * (BOPS * w + i) + (lane >> 1);
+      for (int i = 0; i < BOPS; ++i) {   // (the int4 words' placement)
+        const int bc = gt_pos(32 * (BOPS * w + i) + (lane >> 1));
         const bool up = MODE == 0 && bc >= 128;
         const int c = min(c0 + (MODE == 0 ? (bc & 127) : bc), N - 1);
         const char *bb = reinterpret_cast<const char *>(uniform_ptr((up ? A.B1 : A.B0) + (size_t)e * N * 16));
-        dma16(bb, (uint32_t)c * 32u + 16 * (lane & 1), sb + slot * ST_B + i * 1024);
+        dma16(bb, (uint32_t)c * 32u + 16 * ((lane & 1) ^ gt_half(bc)), sb + slot * ST_B + i * 1024);
       }
 #pragma unroll
       for (int i = 0; i < XOPS; ++i) dma4(xbase, xoff[i], sx + slot * ST_X + i * 256);
@@ -344,11 +353,13 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       __builtin_amdgcn_sched_barrier(0);
       u32x2_t bq[NF];
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf) bq[nf] = lds_ld<u32x2_t>(offB + slot * ST_B + nfc(nf) * 32);
+      for (int nf = 0; nf < NF; ++nf)
+        bq[nf] = lds_ld<u32x2_t>((nf & 1 ? offB1 : offB0) + slot * ST_B + fpair(nf) * 32);
       f32x4_t rv[NF], nv4[2];
       if (EVEN) {
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) rv[nf] = lds_ld<f32x4_t>(offR + slot * ST_X + nfc(nf) * 4);
+        for (int nf = 0; nf < NF; ++nf)
+          rv[nf] = lds_ld<f32x4_t>(offR + slot * ST_X + (fpair(nf) + 4 * (nf & 1)) * 4);
         nv4[0] = lds_ld<f32x4_t>(offC + slot * ST_X);
         if (NM > 4) nv4[1] = lds_ld<f32x4_t>(offC + slot * ST_X + 16);
       }
@@ -425,16 +436,17 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
 
     // ---- epilogue columns (in the matrix's own column space), re-derived
     // from an opaque copy of the thread index: col = the B-operand column of
-    // lane lr, ocol = the first of the lane's four output columns
+    // lane lr, ocol = the first of the lane's four output columns (those of
+    // fragment 2t + 1 follow those of 2t)
     int tid2 = threadIdx.x;
     asm volatile("" : "+v"(tid2));
     const int lr2 = tid2 & 15, lg2 = (tid2 >> 4) & 3, w2 = tid2 >> 6;
     int col[NF], ocol[NF];
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) {
-      const int mc = c0 + w2 * WCOLS + (MODE == 0 ? nfc(nf) & 127 : nfc(nf));
-      col[nf] = mc + lr2;
-      ocol[nf] = mc + 4 * lg2;
+      const int mc = c0 + w2 * WCOLS + (fpair(nf) & (MODE == 0 ? 127 : 255));
+      col[nf] = mc + gt_col(nf & 1, lr2);
+      ocol[nf] = mc + 8 * lg2 + 4 * (nf & 1);
     }
     // mode 0: fragment nf belongs to the up matrix when nf >= NF / 2
     auto is_up = [](int nf) { return MODE == 0 && nf >= NF / 2; };
@@ -456,12 +468,15 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       short4_t bv[NF];
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
-        const f32x4_t sl = lds_ld<f32x4_t>(ldsX + es * ST_X + (wc + nfc(nf) + 4 * lg2) * 4);
+        const f32x4_t sl =
+            lds_ld<f32x4_t>(ldsX + es * ST_X + (wc + fpair(nf) + 8 * lg2 + 4 * (nf & 1)) * 4);
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[m][nf][i] *= sl[i];
-        bv[nf] = lds_ld<short4_t>(ldsB + es * ST_B + (wc + nfc(nf) + lr2) * 32 + 8 * lg2);
+        const int bc = gt_col(nf & 1, lr2);   // (placed like the int4 words)
+        bv[nf] = lds_ld<short4_t>(ldsB + es * ST_B + (wc + fpair(nf) + gt_pos(bc)) * 32 +
+                                  16 * ((lg2 >> 1) ^ gt_half(bc)) + 8 * (lg2 & 1));
       }
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -534,8 +549,9 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       }
     }
 
-    // ---- epilogue: lane (lr, lg) holds, for row 16 m + lr, the four
-    // consecutive columns ocol[nf] .. + 3; each becomes one 8-byte store.
+    // ---- epilogue: lane (lr, lg) holds, for row 16 m + lr, the eight
+    // consecutive columns ocol[2t] .. + 7 in fragments 2t and 2t + 1; each
+    // such pair becomes one 16-byte store.
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // trailing (clamped) stage loads
     if (MODE == 0) {
       // H = silu(G) U (and, when saved, the SwiGLU backward's multipliers
@@ -549,33 +565,41 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
       for (int m = 0; m < NM; ++m) {
         const int r = 16 * m + lr2;
         float hs = 0.f;
+        // gate fragments 0-1 with up fragments 2-3: columns ocol[0] .. + 7
+        float sg[8], sl[8];   // sigmoid(G), silu(G)
+        uint32_t hw[4];
 #pragma unroll
-        for (int nf = 0; nf < NF / 2; ++nf) {
-          const f32x4_t g = acc[m][nf], u = acc[m][nf + NF / 2];
-          float sg[4], sl[4];   // sigmoid(G), silu(G)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f32x4_t g = acc[m][h2], u = acc[m][h2 + 2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            sg[i] = sigmoid_rcp(g[i]);
-            sl[i] = g[i] * sg[i];
+            sg[4 * h2 + i] = sigmoid_rcp(g[i]);
+            sl[4 * h2 + i] = g[i] * sg[4 * h2 + i];
           }
-          u32x2_t h;
-          h.x = cvt_pk_bf16(sl[0] * u[0], sl[1] * u[1]);
-          h.y = cvt_pk_bf16(sl[2] * u[2], sl[3] * u[3]);
-          hs += (__uint_as_float(h.x << 16) + __uint_as_float(h.x & 0xFFFF0000u)) +
-                (__uint_as_float(h.y << 16) + __uint_as_float(h.y & 0xFFFF0000u));
-          if (r < rows) {
-            const size_t o = (size_t)(p0 + r) * A.ldo + ocol[nf];
-            *reinterpret_cast<u32x2_t *>(&A.out[o]) = h;
-            if (A.saveG) {
-              // the SwiGLU backward's multipliers: dG = dH mG, dU = dH mU
-              float mg[4];
+          const uint32_t h0 = cvt_pk_bf16(sl[4 * h2] * u[0], sl[4 * h2 + 1] * u[1]);
+          const uint32_t h1 = cvt_pk_bf16(sl[4 * h2 + 2] * u[2], sl[4 * h2 + 3] * u[3]);
+          hw[2 * h2] = h0;
+          hw[2 * h2 + 1] = h1;
+          hs += (__uint_as_float(h0 << 16) + __uint_as_float(h0 & 0xFFFF0000u)) +
+                (__uint_as_float(h1 << 16) + __uint_as_float(h1 & 0xFFFF0000u));
+        }
+        if (r < rows) {
+          const size_t o = (size_t)(p0 + r) * A.ldo + ocol[0];
+          *reinterpret_cast<uint4 *>(&A.out[o]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          if (A.saveG) {
+            // the SwiGLU backward's multipliers: dG = dH mG, dU = dH mU
+            float mg[8];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) mg[i] = u[i] * sg[i] * __builtin_fmaf(g[i], 1.f - sg[i], 1.f);
-              *reinterpret_cast<u32x2_t *>(&A.saveG[o]) =
-                  u32x2_t{cvt_pk_bf16(mg[0], mg[1]), cvt_pk_bf16(mg[2], mg[3])};
-              *reinterpret_cast<u32x2_t *>(&A.saveU[o]) =
-                  u32x2_t{cvt_pk_bf16(sl[0], sl[1]), cvt_pk_bf16(sl[2], sl[3])};
+            for (int v = 0; v < 8; ++v) {
+              const float g = acc[m][v >> 2][v & 3], u = acc[m][2 + (v >> 2)][v & 3];
+              mg[v] = u * sg[v] * __builtin_fmaf(g, 1.f - sg[v], 1.f);
             }
+            *reinterpret_cast<uint4 *>(&A.saveG[o]) =
+                make_uint4(cvt_pk_bf16(mg[0], mg[1]), cvt_pk_bf16(mg[2], mg[3]),
+                           cvt_pk_bf16(mg[4], mg[5]), cvt_pk_bf16(mg[6], mg[7]));
+            *reinterpret_cast<uint4 *>(&A.saveU[o]) =
+                make_uint4(cvt_pk_bf16(sl[0], sl[1]), cvt_pk_bf16(sl[2], sl[3]),
+                           cvt_pk_bf16(sl[4], sl[5]), cvt_pk_bf16(sl[6], sl[7]));
           }
         }
         hs += __shfl_xor(hs, 16);
@@ -596,11 +620,13 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
         const int r = 16 * m + lr2;
         if (r < rows) {
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            if (ocol[nf] < N)
-              *reinterpret_cast<u32x2_t *>(&A.out[(size_t)(p0 + r) * A.ldo + ocol[nf]]) =
-                  u32x2_t{cvt_pk_bf16(acc[m][nf][0], acc[m][nf][1]),
-                          cvt_pk_bf16(acc[m][nf][2], acc[m][nf][3])};
+          for (int t = 0; t < NF / 2; ++t) {
+            if (ocol[2 * t] < N)
+              *reinterpret_cast<uint4 *>(&A.out[(size_t)(p0 + r) * A.ldo + ocol[2 * t]]) =
+                  make_uint4(cvt_pk_bf16(acc[m][2 * t][0], acc[m][2 * t][1]),
+                             cvt_pk_bf16(acc[m][2 * t][2], acc[m][2 * t][3]),
+                             cvt_pk_bf16(acc[m][2 * t + 1][0], acc[m][2 * t + 1][1]),
+                             cvt_pk_bf16(acc[m][2 * t + 1][2], acc[m][2 * t + 1][3]));
           }
         }
       }

@@ -145,16 +145,10 @@ __global__ __launch_bounds__(256) void transpose_q_int8_kernel(const uint8_t *__
 constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage holds the item's rows)
 
 // Output columns of a wave's 128: fragment nf (of 8) and matrix-instruction
-// row j (0..15) hold column 32 (nf >> 1) + 8 (j >> 2) + 4 (nf & 1) + (j & 3),
-// so that a lane's values of fragments 2t and 2t + 1 are 8 adjacent columns
-// (16-byte accesses in the epilogue).  In LDS, column c of the item's 256 (the
-// int4 words of a stage, and the transposed adapter rows) sits at position
-// c ^ (4 bit3(c)) with its 16-byte halves swapped when bit 4 of c is set:
-// the 16 columns one fragment reads then touch every bank once per half
-// wave.
-DEV int gt_col(int nf, int j) { return 32 * (nf >> 1) + 8 * (j >> 2) + 4 * (nf & 1) + (j & 3); }
-DEV int gt_pos(int c) { return c ^ (4 * ((c >> 3) & 1)); }
-DEV int gt_half(int c) { return (c >> 4) & 1; }
+// row j hold column gt_col(nf, j) (8 adjacent columns per lane and fragment
+// pair, 16-byte accesses in the epilogue); in LDS, column c of the item's 256
+// (the int4 words of a stage, and the transposed adapter rows) sits at
+// gt_pos(c), halves swapped by gt_half(c).
 
 // ------------------------------------------------------------------ GEMM --
 // A bf16x8 fragment times 8 per-k scales, rounded back to bf16.

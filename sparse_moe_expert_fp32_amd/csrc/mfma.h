@@ -52,6 +52,18 @@ DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 // of 256 bytes once: rows r and r + 8 share a bank group under r & 7 alone.
 DEV int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// Output-column permutation of the int4 products: matrix-instruction row j
+// (0..15) of column fragment nf holds column 32 (nf >> 1) + 8 (j >> 2) +
+// 4 (nf & 1) + (j & 3) of the fragments' span, so that a lane's four values
+// of fragment 2t and four of 2t + 1 are 8 adjacent columns (16-byte accesses
+// in an epilogue).  Rows of 32 bytes per column in LDS (the int4 words of a
+// stage, adapter rows) then sit at position gt_pos(c) = c ^ (4 bit3(c)), the
+// two 16-byte halves swapped when bit 4 of c is set (gt_half): the 16 columns
+// one fragment reads, 8 bytes a lane, touch every bank once per half wave.
+DEV constexpr int gt_col(int nf, int j) { return 32 * (nf >> 1) + 8 * (j >> 2) + 4 * (nf & 1) + (j & 3); }
+DEV constexpr int gt_pos(int c) { return c ^ (4 * ((c >> 3) & 1)); }
+DEV constexpr int gt_half(int c) { return (c >> 4) & 1; }
+
 // D = A(16x32) B(32x16) + C.  Lane l holds A row l%16 / B column l%16 with 8
 // consecutive K values of lane group l/16; D lane l holds column l%16, rows
 // 4*(l/16) .. 4*(l/16)+3.
