@@ -157,6 +157,21 @@ def test_null_pointers_rejected_before_launch(B):
     assert L.moe_route(None, P, P, None, P, P, None, P, 1 << 30, None) == -1
 
 
+def test_unaligned_expert_fwd_buffers_rejected(B):
+    """x, e_out and save are read and written in 16-byte pieces: a pointer
+    off a 16-byte boundary is refused on the host, before any launch."""
+    dm = good(B)
+    L = B.LIB
+    P = FAKE
+    q = B.QLora(P, P, P, P)
+    for x, e_out, save in ((P + 8, P, None), (P, P + 2, None), (P, P, P + 4)):
+        assert L.moe_expert_fwd(ctypes.byref(dm), x, P, P, q, q, q, e_out, save, P, 1 << 30,
+                                None) == -1
+        assert "16-byte" in L.moe_last_error().decode()
+        assert L.moe_expert_fwd_noalloc(ctypes.byref(dm), x, P, P, q, q, q, e_out, save,
+                                        None) == -1
+
+
 def test_small_workspace_rejected(B):
     dm = good(B)
     L = B.LIB
