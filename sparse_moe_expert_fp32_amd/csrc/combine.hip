@@ -180,9 +180,10 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(
 // the float32 router-gradient rows between them.
 //
 // With dgp (the dH product's per-slot partials of g_p <dy_t, e_out[p]>, nq
-// of them in column order) dgamma_j is their sum divided by gamma_j, and the
-// pass over e_out is made only for a token with a gate below 1e-30 (where
-// that division would lose precision).
+// of them in column order) dgamma_j is their sum divided by gamma_j (the sum
+// in a fixed lane order: lane groups of every fourth partial, then the groups
+// pairwise), and the pass over e_out is made only for a token with a gate
+// below 1e-30 (where that division would lose precision).
 template <int KB>
 __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
     const bf16_t *__restrict__ dy, const bf16_t *__restrict__ e_out,
@@ -206,22 +207,22 @@ __global__ __launch_bounds__(256) void token_bwd_wave_kernel(
   }
   bool direct = dgp == nullptr;
   if (!direct) {
-    // the partials in q order, eight at a time (clamped addresses, so that a
-    // batch's loads issue together; the repeats are not added)
+    // the partials on the lanes, all loads in one round trip: lane l takes
+    // slot j = l % 16 and the partials q = l / 16, l / 16 + 4, ... in order;
+    // the four lane groups are then added by shuffles (a fixed order)
     const size_t S = (size_t)T * k;
+    const int jl = lane & 15;
+    float s = 0.f;
+    if (jl < k) {
+      const int pj = slot_pos[(size_t)t * k + jl];
+      for (int q = lane >> 4; q < nq; q += 4) s += dgp[(size_t)q * S + pj];
+    }
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j < k) {
-        float s = 0.f;
-        for (int q0 = 0; q0 < nq; q0 += 8) {
-          float v[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = dgp[(size_t)min(q0 + i, nq - 1) * S + p[j]];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (q0 + i < nq) s += v[i];
-        }
-        part[j] = s / g[j];
+        part[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j)) / g[j];
         direct |= !(g[j] >= 1e-30f);
       }
     }
