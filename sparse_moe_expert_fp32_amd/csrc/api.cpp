@@ -192,7 +192,7 @@ size_t part2_floats(const moe_dims *d) {
 // ---- adapter backward workspace
 struct BwdLayout {
   size_t tiles, ntiles, tiles_m, ntiles_m, tiles_p, ntiles_p, tiles_w, ntiles_w, part, part2, bt,
-      lt, wt, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
+      wt, wr_t, dx_r, dO, dZ, dH32, dG, dU, dXp, total;
   BwdLayout(const moe_dims *d, int flags) {
     size_t S = (size_t)d->T * d->top_k, f = d->d_ff, dm = d->d_model, ab = act_bytes(d);
     const bool mf = use_mfma(d);
@@ -212,10 +212,9 @@ struct BwdLayout {
               : 0;
     // the partials of the gate and up dB passes, reduced together with dA_d's
     part2 = mf ? c.take(part2_floats(d) * 4) : 0;
-    // B of down, gate, up transposed to [E][r][N] (bf16)
+    // B of down, gate, up transposed to [E][r][N] (bf16), for projections
+    // that do not ride along the dB passes
     bt = mf ? c.take((size_t)d->n_experts * d->rank * (dm + 2 * f) * 2) : 0;
-    // A of down, gate, up transposed to [E][N][r] (bf16), for rank 16
-    lt = mf && d->rank == 16 ? c.take((size_t)d->n_experts * d->rank * (f + 2 * dm) * 2) : 0;
     // transposed int4 base + scales, two slots (down, then gate; up), unless
     // the caller passes every matrix transposed-packed
     wt = mf && !ws_packed_given(flags) ? c.take(2 * qt_slot_bytes(d)) : 0;
@@ -822,27 +821,26 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     const int mtw = (int)max_tiles(dims, moe::wgrad_tile_rows());
     uint16_t *bt_d = at<uint16_t>(ws, L.bt);
     uint16_t *bt_g = bt_d + (size_t)E * r * d, *bt_u = bt_g + (size_t)E * r * f;
-    uint16_t *lt_d = nullptr, *lt_g = nullptr, *lt_u = nullptr;
+    // The projections dZ = lam dO B ride along the dB reductions (rank 16,
+    // 256-column ranges, partials in the dX_perm buffer) and read B as
+    // stored; otherwise they run on their own over B as [E][r][N].
+    const size_t dxp_bytes = (size_t)S * d * 2;
+    const size_t zq = (size_t)(f / 256) * S * 16;   // floats of one matrix's partials
+    const bool fuse_d = r == 16 && d % 256 == 0 && (size_t)(d / 256) * S * 64 <= dxp_bytes;
+    const bool fuse_gu = r == 16 && f % 256 == 0 && 2 * zq * 4 <= dxp_bytes;
     // set-up in one launch: W_r^T; the tile lists of the input-gradient
     // products (zeroing their work counters), of the projections and of the
     // adapter-gradient reductions (with the experts they split); B of each
-    // matrix as [E][r][N]; A of each matrix as [E][N][r] for the epilogue
-    // stages of the input-gradient products (rank 16)
+    // matrix as [E][r][N] where its projection runs on its own
     moe::PrepBatch pb;
     pb.transpose_f32(w_router, d, E, wr_t);
     pb.tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, nullptr, 32);
     pb.tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p);
     pb.tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, ntiles_w + 1);
-    pb.transpose_nr(down.B, E, d, r, bt_d, st);
-    pb.transpose_nr(gate.B, E, f, r, bt_g, st);
-    pb.transpose_nr(up.B, E, f, r, bt_u, st);
-    if (r == 16) {
-      lt_d = at<uint16_t>(ws, L.lt);
-      lt_g = lt_d + (size_t)E * r * f;
-      lt_u = lt_g + (size_t)E * r * d;
-      pb.transpose_rn(down.A, E, r, f, lt_d, st);
-      pb.transpose_rn(gate.A, E, r, d, lt_g, st);
-      pb.transpose_rn(up.A, E, r, d, lt_u, st);
+    if (!fuse_d) pb.transpose_nr(down.B, E, d, r, bt_d, st);
+    if (!fuse_gu) {
+      pb.transpose_nr(gate.B, E, f, r, bt_g, st);
+      pb.transpose_nr(up.B, E, f, r, bt_u, st);
     }
     moe::launch_prep(pb, st);
     // An int8 base runs as its two int4 planes stacked along N: twice the
@@ -864,7 +862,6 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // the adapter-gradient partials of the passes before it).  The dZ
     // partials live in the dX_perm buffer, which is written only at the end.
     float *zpart = reinterpret_cast<float *>(dXp);
-    const size_t dxp_bytes = (size_t)S * d * 2;
     moe::ProjMArgs Q{};
     Q.perm_src = perm_src; Q.kk = k; Q.tiles = tiles_p; Q.ntiles = ntiles_p; Q.offsets = offsets;
     Q.r = r; Q.nsrc = 1; Q.scale = lam; Q.ldz = 3 * r;
@@ -878,8 +875,8 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     W.w = (const uint16_t *)dy; W.ldw = d; W.rr = Z + 2 * r; W.ldr = 3 * r; W.wide = d;
     W.gsc = gates;
     W.scale = lam; W.out = dB_down; W.oe = (size_t)d * r; W.oa = r; W.ob = 1;
-    if (moe::wgrad_can_project(W) && (size_t)(d / 256) * S * 64 <= dxp_bytes) {
-      W.pm = bt_d; W.zpart = zpart;
+    if (fuse_d) {
+      W.pm = (const uint16_t *)down.B; W.zpart = zpart;
       moe::launch_wgrad_mfma(W, mtw, true, st, false);
       const moe::ZpartJob zj{zpart, nullptr, d / 256, (int)S, perm_src, gates, lam, dZ + 2 * r,
                              nullptr, 3 * r};
@@ -906,7 +903,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
       transpose(down, d, f, qt0, st0);
     }
     M.K = d * pm; M.kr = d; M.N = f; M.NT = (f + 255) / 256; M.qt0 = qd; M.st0 = sd;
-    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A; M.LT0 = lt_d;
+    M.Z0 = dZ + 2 * r; M.ldz = 3 * r; M.r = r; M.L0 = (const uint16_t *)down.A;
     M.G = (const uint16_t *)Gs; M.U = (const uint16_t *)Us;
     M.dG = (uint16_t *)dG; M.dU = (uint16_t *)dU;
     // the gate gradient's dots <dy, e_out[p]> come from this product: per row
@@ -923,14 +920,13 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // dB [f][r] = lam sum_p dG[p][n] Z[p][j] and dZ_g = lam dG B_g (up: dU, Z_u, B_u)
     W.w = (const uint16_t *)dG; W.ldw = f; W.rr = Z; W.wide = f; W.scale = lam; W.out = dB_gate;
     W.oe = (size_t)f * r; W.oa = r; W.ob = 1;
-    const size_t zq = (size_t)(f / 256) * S * 16;   // floats of one matrix's partials
-    if (moe::wgrad_can_project(W) && 2 * zq * 4 <= dxp_bytes) {
+    if (fuse_gu) {
       // dA_d, dB_g and dB_u keep their partials apart (dA_d in the shared
       // buffer, dB_g and dB_u in their own), reduced in one launch with dZ
       moe::launch_wgrad_mfma(Wd, mtw, false, st, false);
       moe::WgradMArgs Wg = W, Wu = W;
-      Wg.pm = bt_g; Wg.zpart = zpart; Wg.part = at<float>(ws, L.part2);
-      Wu.w = (const uint16_t *)dU; Wu.rr = Z + r; Wu.out = dB_up; Wu.pm = bt_u;
+      Wg.pm = (const uint16_t *)gate.B; Wg.zpart = zpart; Wg.part = at<float>(ws, L.part2);
+      Wu.w = (const uint16_t *)dU; Wu.rr = Z + r; Wu.out = dB_up; Wu.pm = (const uint16_t *)up.B;
       Wu.zpart = zpart + zq; Wu.part = Wg.part + part2_floats(dims) / 2;
       moe::launch_wgrad_mfma(Wg, mtw, false, st, false);
       moe::launch_wgrad_mfma(Wu, mtw, false, st, false);
@@ -971,7 +967,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
       transpose(up, f, d, qt1, st1);
     }
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
-    X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A; X.LT0 = lt_g; X.LT1 = lt_u;
+    X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A;
     X.out = (uint16_t *)dXp; X.ldo = d;
     TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, ntiles_m, ntiles_m + 16, grid, st));
     // gate gradient and the per-token sum of dX_perm, one pass per token

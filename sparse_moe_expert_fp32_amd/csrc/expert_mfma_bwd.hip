@@ -259,12 +259,16 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
           dma16(zb, zo, sa + slot * TS_A + i * 1024);
         }
       }
-      const char *lb16 = reinterpret_cast<const char *>(uniform_ptr((part ? A.LT1 : A.LT0) + (size_t)e * N * 16));
+      // the adapter A of the matrix as stored ([E][16][N]): rank row j of
+      // the item's 256 columns at j * 512 bytes (wave w, load i: rows
+      // 2 (2 w + i) and + 1, 8 columns a lane; a partial tile repeats its
+      // last 8 columns)
+      const char *lb16 = reinterpret_cast<const char *>(uniform_ptr((part ? A.L1 : A.L0) + (size_t)e * 16 * N));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int c = gt_pos(32 * (2 * w + i) + (lane >> 1));
-        const int col = min(c0 + c, N - 1);
-        dma16(lb16, (uint32_t)col * 32u + 16 * ((lane & 1) ^ gt_half(c)), sb + slot * TS_B + i * 1024);
+        const int j = 2 * (2 * w + i) + (lane >> 5);
+        const int col = min(c0 + 8 * (lane & 31), N - 8);
+        dma16(lb16, ((uint32_t)j * (uint32_t)N + (uint32_t)col) * 2u, sb + slot * TS_B + i * 1024);
       }
     };
     // The epilogue stages (EPL) are issued whole at the start of their step.
@@ -418,16 +422,18 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
     const int nsrc = MODE == 1 ? 2 : 1;
     if constexpr (EPL) {
       // from the epilogue stages: dZ rows in the A array of ring slot NK % 3,
-      // L^T rows in the word arrays of slots NK % 3 and (mode 1) NK % 3 + 1
+      // the rank rows of L in the word arrays of slots NK % 3 and (mode 1)
+      // NK % 3 + 1 (rank values 4 lg .. 4 lg + 3 of a column: four 16-bit
+      // reads 512 bytes apart)
       const int es = NK % 3;
       for (int src = 0; src < nsrc; ++src) {
         const int ls = src ? (es == 2 ? 0 : es + 1) : es;
         short4_t lv[8];
 #pragma unroll
         for (int nf = 0; nf < 8; ++nf) {
-          const int c = gt_col(nf, lr2);
-          lv[nf] = lds_ld<short4_t>(ldsB + ls * TS_B + (128 * wn2 + gt_pos(c)) * 32 +
-                                    16 * ((lg2 >> 1) ^ gt_half(c)) + 8 * (lg2 & 1));
+          const uint32_t la16 = ldsB + ls * TS_B + (128 * wn2 + gt_col(nf, lr2)) * 2 + 4 * lg2 * 512;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lv[nf][i] = lds_ld<short>(la16 + i * 512);
         }
 #pragma unroll
         for (int m = 0; m < NMH; ++m) {
@@ -600,7 +606,9 @@ void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *ntiles, 
                            hipStream_t st) {
   // operands of the epilogue through the LDS ring: rank 16, dZ rows 16-byte
   // aligned, transposed adapter A given
-  const bool epl = A.r == 16 && (A.ldz & 3) == 0 && A.LT0 && (mode == 0 || A.LT1);
+  // (the epilogue stages load A's rank rows in 16-byte pieces)
+  const bool epl = A.r == 16 && (A.ldz & 3) == 0 &&
+                   (((uintptr_t)A.L0 | (uintptr_t)(mode == 1 ? A.L1 : A.L0)) & 15) == 0;
 #define MOE_GT(MODE)                                                           \
   if (epl) grouped_gemm_t_kernel<MODE, true><<<grid, 256, 0, st>>>(A, ntiles, ctr);   \
   else grouped_gemm_t_kernel<MODE, false><<<grid, 256, 0, st>>>(A, ntiles, ctr)

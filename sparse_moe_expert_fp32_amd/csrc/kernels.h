@@ -60,10 +60,10 @@ void launch_build_tiles(const int32_t *offsets, int E, int BM, int2 *tiles, int 
 int simple_tile_rows();
 
 // ---- batched set-up (prep.hip): independent small jobs of one call (tile
-// lists, group row sums, rank-16 adapter transposes) in one launch of
+// lists, group row sums, rank-16 adapter-B transposes, W_r^T) in one launch of
 // 1024-thread blocks; each job takes a contiguous range of the blocks
 struct PrepBatch {
-  enum Kind { kTiles = 1, kRowsum, kTransposeRN16, kTransposeNR16, kTransposeF32 };
+  enum Kind { kTiles = 1, kRowsum, kTransposeNR16, kTransposeF32 };
   struct Job {
     int kind, nblocks;
     const int32_t *offsets; int E, BM; int2 *tiles; int *ntiles; int *first; int nzero;
@@ -78,9 +78,8 @@ struct PrepBatch {
   // launch_group_rowsum as a job
   void rowsum(const void *a, int rows, int K, int G, float scale, float *out, bool split = false,
               float scale2 = 0.f);
-  // launch_transpose_rn / launch_transpose_nr as a job where the rank-16
-  // kernel applies (else launched on its own now, on st)
-  void transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st);
+  // launch_transpose_nr as a job where the rank-16 kernel applies (else
+  // launched on its own now, on st)
   void transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
   // launch_transpose_f32 as a job
   void transpose_f32(const float *in, int rows, int cols, float *out);
@@ -187,7 +186,6 @@ struct MfmaGemmTArgs {
   const float *st0, *st1;                 // its scales per column group, [E][N/128][K]
   const float *Z0, *Z1; int ldz; int r;   // dZ = lam dOut B (float32)
   const uint16_t *L0, *L1;                // adapter A of the matrix, [E][r][N]
-  const uint16_t *LT0, *LT1;              // the same transposed, [E][N][r] (rank 16; or null)
   const uint16_t *G, *U; uint16_t *dG, *dU;   // mode 0: dG = dH G, dU = dH U ([S][N]; G, U the saved multipliers)
   uint16_t *out; int ldo;                 // mode 1: dX_perm [S][N]
   // mode 0, optional: dgp[q][p] = sum over the q-th 128 columns c of dH[p][c]
@@ -236,8 +234,9 @@ struct WgradMArgs {                       // out_s[e][a][b] = scale * sum_p W[p]
   const int *multi;                       // count, then the experts not written by one tile
   float *part;                            // partials: [tiles][nsrc][wide][r]
   // optional (wgrad_can_project): the projection of the same rows onto pm
-  // [E][16][wide] (bf16), as partials zpart [wide / 256][S][16] (f32) over the
-  // 256-column ranges, for launch_zpart_reduce
+  // [E][wide][16] (bf16, the adapter B as stored), as partials zpart
+  // [wide / 256][S][16] (f32) over the 256-column ranges, for
+  // launch_lowrank_reduce
   const uint16_t *pm; float *zpart; int S;
 };
 int wgrad_tile_rows();
@@ -259,7 +258,6 @@ struct ZpartJob {
 void launch_lowrank_reduce(const WgradMArgs *w, int nw, const ZpartJob *z, hipStream_t st);
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st);
 // bf16 [E][r][N] -> [E][N][r]
-void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st);
 // one launch over the tiles of launch_build_tiles (mfma_t_tile_rows() rows,
 // in expert order), each item as the shortest tile class holding its rows
 // (ctr: eight counters, zero at launch, one per XCD)

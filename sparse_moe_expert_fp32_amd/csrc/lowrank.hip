@@ -173,12 +173,13 @@ __global__ __launch_bounds__(64 * NW, NF == 4 ? 1 : 2) void proj_mfma_kernel(con
 // operations only).
 //
 // PROJ (one source of rank 16, wide a multiple of 256): the same pass also
-// forms the projection of the rows onto M = [E][16][wide] (the adapter B of
-// the matrix, transposed), Z'_q[p][j] = sum over the block's 256 columns
-// (column range q) of W(p, a) M[e][j][a], as partials zpart[q][p][j];
-// launch_lowrank_reduce adds the ranges.  The staged chunk is also stored as
-// it came (rows of 16-byte pieces, piece index XOR-swizzled by row), and
-// each wave multiplies 16 of its rows by M, also staged in LDS.
+// forms the projection of the rows onto the adapter B = [E][wide][16] of the
+// matrix, Z'_q[p][j] = sum over the block's 256 columns (column range q) of
+// W(p, a) B[e][a][j], as partials zpart[q][p][j]; launch_lowrank_reduce adds
+// the ranges.  The staged chunk is also stored as it came (rows of 16-byte
+// pieces, piece index XOR-swizzled by row), and each wave multiplies 16 of
+// its rows by B, staged in LDS transposed (ml[j][a], from its rows of 16
+// rank values as stored).
 constexpr int WG_COLS = 256, WG_ROWS = 64, WG_TILE = 512;
 
 DEV int wg_sw(int c) { return c ^ ((c >> 3) & 7); }
@@ -213,12 +214,17 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const WgradMArgs G) 
   const int nj = (G.r + 15) >> 4;   // R fragments per source (NM = nj * nsrc)
   constexpr int RC = 16 * NM;       // staged R columns (all sources)
   constexpr int RPER = RC / 4;      // R values per thread and chunk
-  if constexpr (PROJ) {
+  if constexpr (PROJ) {   // B[e][a0 + a][jh .. jh + 7] -> ml[jh ..][a]
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 256 * u, row = idx >> 5, c8 = 8 * (idx & 31);
-      *reinterpret_cast<uint4 *>(&ml[row][c8]) =
-          *reinterpret_cast<const uint4 *>(G.pm + ((size_t)e * 16 + row) * G.wide + a0 + c8);
+      const int idx = tid + 256 * u, a = idx >> 1, jh = 8 * (idx & 1);
+      const uint4 v = *reinterpret_cast<const uint4 *>(G.pm + ((size_t)e * G.wide + a0 + a) * 16 + jh);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ml[jh + 2 * i][a] = (uint16_t)(wv[i] & 0xFFFFu);
+        ml[jh + 2 * i + 1][a] = (uint16_t)(wv[i] >> 16);
+      }
     }
   }
   if (GATHER) {
@@ -519,44 +525,12 @@ void launch_lowrank_reduce(const WgradMArgs *w, int nw, const ZpartJob *z, hipSt
 
 int wgrad_tile_rows() { return WG_TILE; }
 
-// out[e][n][j] = in[e][j][n] for bf16 [E][r][N] -> [E][N][r]: one block per
-// (256 values of n, expert), read as r row segments of 512 bytes, written
-// as one contiguous run of 256 r values, through LDS.
-__global__ __launch_bounds__(256) void transpose_rn_kernel(const uint16_t *__restrict__ in, int r,
-                                                           int N, uint16_t *__restrict__ out) {
-  __shared__ uint16_t t[TN_N * 33];   // [n][j], j < r <= 32, padded
-  const int e = blockIdx.y, n0 = blockIdx.x * TN_N, tid = threadIdx.x;
-  const int nn = min(TN_N, N - n0);
-  for (int i = tid; i < nn * r; i += 256) {
-    const int j = i / nn, n = i - j * nn;
-    t[n * 33 + j] = in[((size_t)e * r + j) * N + n0 + n];
-  }
-  __syncthreads();
-  uint16_t *dst = out + ((size_t)e * N + n0) * r;
-  for (int i = tid; i < nn * r; i += 256) {
-    const int n = i / r, j = i - n * r;
-    dst[i] = t[n * 33 + j];
-  }
-}
-
 // Rank 16: one thread per n, 16 values of 2 bytes each way; the column
 // side moves as two 16-byte accesses, the row side as coalesced 2-byte
 // accesses across the wave.
-__global__ __launch_bounds__(256) void transpose_rn16_kernel(const uint16_t *__restrict__ in, int N,
-                                                             uint16_t *__restrict__ out) {
-  transpose_rn16_elem(in, N, blockIdx.y, blockIdx.x * 256 + threadIdx.x, out);
-}
 __global__ __launch_bounds__(256) void transpose_nr16_kernel(const uint16_t *__restrict__ in, int N,
                                                              uint16_t *__restrict__ out) {
   transpose_nr16_elem(in, N, blockIdx.y, blockIdx.x * 256 + threadIdx.x, out);
-}
-
-void launch_transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st) {
-  dim3 grid((N + TN_N - 1) / TN_N, E);
-  if (r == 16 && ((uintptr_t)out & 15) == 0)   // (16-byte stores)
-    transpose_rn16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, N, (uint16_t *)out);
-  else
-    transpose_rn_kernel<<<grid, 256, 0, st>>>((const uint16_t *)in, r, N, (uint16_t *)out);
 }
 
 void launch_transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st) {

@@ -86,21 +86,9 @@ DEV void group_rowsum_elem(size_t i, const bf16_t *__restrict__ a, int rows, int
   }
 }
 
-// Rank-16 adapter transposes of bf16 matrices, one column n of expert e per
-// thread (16-byte accesses on the [E][N][16] side, which must be 16-byte
-// aligned): rn16 [E][16][N] -> [E][N][16], nr16 [E][N][16] -> [E][16][N].
-DEV void transpose_rn16_elem(const uint16_t *__restrict__ in, int N, int e, int n,
-                             uint16_t *__restrict__ out) {
-  if (n >= N) return;
-  const uint16_t *src = in + (size_t)e * 16 * N + n;
-  uint32_t v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    v[j] = (uint32_t)src[(2 * j) * (size_t)N] | ((uint32_t)src[(2 * j + 1) * (size_t)N] << 16);
-  uint4 *dst = reinterpret_cast<uint4 *>(out + ((size_t)e * N + n) * 16);
-  dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
-  dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
-}
+// Rank-16 adapter transpose of a bf16 matrix, one column n of expert e per
+// thread (16-byte loads on the [E][N][16] side, which must be 16-byte
+// aligned): nr16 [E][N][16] -> [E][16][N].
 DEV void transpose_nr16_elem(const uint16_t *__restrict__ in, int N, int e, int n,
                              uint16_t *__restrict__ out) {
   if (n >= N) return;

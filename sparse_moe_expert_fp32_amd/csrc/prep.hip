@@ -34,17 +34,13 @@ __global__ __launch_bounds__(1024) void prep_kernel(const PrepBatch B) {
       group_rowsum_elem((size_t)lb * 1024 + tid, (const bf16_t *)J.src, J.rows, J.K, J.G, J.scale,
                         (float *)J.dst, J.split != 0, J.scale2);
       break;
-    case PrepBatch::kTransposeRN16:
     case PrepBatch::kTransposeNR16: {
       // four units of (256 columns, expert) per block
       const int units = (J.N + 255) / 256;
       const int u = lb * 4 + (tid >> 8);
       const int e = u / units, n = (u - e * units) * 256 + (tid & 255);
       if (e >= J.E) break;
-      if (J.kind == PrepBatch::kTransposeRN16)
-        transpose_rn16_elem((const uint16_t *)J.src, J.N, e, n, (uint16_t *)J.dst);
-      else
-        transpose_nr16_elem((const uint16_t *)J.src, J.N, e, n, (uint16_t *)J.dst);
+      transpose_nr16_elem((const uint16_t *)J.src, J.N, e, n, (uint16_t *)J.dst);
       break;
     }
     case PrepBatch::kTransposeF32: {
@@ -83,16 +79,6 @@ void PrepBatch::rowsum(const void *a, int rows, int K, int G, float scale, float
   J.kind = kRowsum; J.nblocks = (int)((elems + 1023) / 1024);
   J.src = a; J.dst = out; J.rows = rows; J.K = K; J.G = G; J.scale = scale; J.scale2 = scale2;
   J.split = split;
-}
-
-void PrepBatch::transpose_rn(const void *in, int E, int r, int N, void *out, hipStream_t st) {
-  if (r != 16 || ((uintptr_t)out & 15) != 0) {   // (16-byte stores)
-    launch_transpose_rn(in, E, r, N, out, st);
-    return;
-  }
-  Job &J = next();
-  J.kind = kTransposeRN16; J.nblocks = (E * ((N + 255) / 256) + 3) / 4;
-  J.src = in; J.dst = out; J.E = E; J.N = N;
 }
 
 void PrepBatch::transpose_nr(const void *in, int E, int N, int r, void *out, hipStream_t st) {
