@@ -105,6 +105,7 @@ typedef struct {
  *         this q and scale.  Same contract as qt: pack once, results
  *         identical with NULL; read only by the matrix-core path; 16-byte
  *         aligned.
+ * q, A and B must be 16-byte aligned (MOE_ERR_INVALID otherwise).
  * Effective matrix: W_eff = W_hat + lambda * B A, i.e. for a row x,
  * x W_eff^T = x W_hat^T + lambda (x A^T) B^T. */
 typedef struct {

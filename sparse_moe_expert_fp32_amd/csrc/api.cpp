@@ -57,6 +57,9 @@ int plane_mult(const moe_dims *d) { return base_bits(d) / 4; }
 moe_status check_qlora(const moe_qlora &m, const char *name) {
   if (!m.q || !m.scale || !m.A || !m.B)
     return fail(MOE_ERR_INVALID, std::string(name) + ": q, scale, A and B must be non-NULL");
+  // (the products stream q, A and B in 16-byte pieces)
+  if ((((uintptr_t)m.q | (uintptr_t)m.A | (uintptr_t)m.B) & 15) != 0)
+    return fail(MOE_ERR_INVALID, std::string(name) + ": q, A and B must be 16-byte aligned");
   if (((uintptr_t)m.qt & 15) != 0)
     return fail(MOE_ERR_INVALID, std::string(name) + ": qt must be 16-byte aligned");
   if (((uintptr_t)m.qf & 15) != 0)
@@ -826,8 +829,11 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // stored; otherwise they run on their own over B as [E][r][N].
     const size_t dxp_bytes = (size_t)S * d * 2;
     const size_t zq = (size_t)(f / 256) * S * 16;   // floats of one matrix's partials
-    const bool fuse_d = r == 16 && d % 256 == 0 && (size_t)(d / 256) * S * 64 <= dxp_bytes;
-    const bool fuse_gu = r == 16 && f % 256 == 0 && 2 * zq * 4 <= dxp_bytes;
+    // (B is read there in 16-byte pieces)
+    const bool fuse_d = r == 16 && d % 256 == 0 && (size_t)(d / 256) * S * 64 <= dxp_bytes &&
+                        ((uintptr_t)down.B & 15) == 0;
+    const bool fuse_gu = r == 16 && f % 256 == 0 && 2 * zq * 4 <= dxp_bytes &&
+                         (((uintptr_t)gate.B | (uintptr_t)up.B) & 15) == 0;
     // set-up in one launch: W_r^T; the tile lists of the input-gradient
     // products (zeroing their work counters), of the projections and of the
     // adapter-gradient reductions (with the experts they split); B of each

@@ -172,6 +172,22 @@ def test_unaligned_expert_fwd_buffers_rejected(B):
                                         None) == -1
 
 
+def test_unaligned_adapter_or_base_rejected(B):
+    """q, A and B are streamed in 16-byte pieces: each must be 16-byte
+    aligned, in the forward and in the backward."""
+    dm = good(B)
+    L = B.LIB
+    P = FAKE
+    q = B.QLora(P, P, P, P)
+    for bad in (B.QLora(P + 4, P, P, P), B.QLora(P, P, P + 2, P), B.QLora(P, P, P, P + 8)):
+        assert L.moe_expert_fwd(ctypes.byref(dm), P, P, P, q, bad, q, P, None, P, 1 << 30,
+                                None) == -1
+        assert "16-byte" in L.moe_last_error().decode()
+        assert L.moe_adapter_bwd(ctypes.byref(dm), P, P, P, P, P, P, P, P, q, q, bad, P, P, P,
+                                 P, P, P, P, P, P, P, 1 << 30, None) == -1
+        assert "16-byte" in L.moe_last_error().decode()
+
+
 def test_small_workspace_rejected(B):
     dm = good(B)
     L = B.LIB
