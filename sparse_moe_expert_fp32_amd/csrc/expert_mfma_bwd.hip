@@ -21,10 +21,12 @@
 //   sum_n A[p][n] s[n][g] q[n][c] = sum_n A'_g[p][n] q[n][c],
 //   A'_g[p][n] = bf16(A[p][n] s[n][g]),   g = c / 128,
 // and the int4 operand stays int4 all the way to the matrix cores, unpacked
-// exactly as 136 + q (nibble in the mantissa of 128.0).  The offset is taken
-// out by one more MFMA per row fragment against a constant 136 operand, which
-// accumulates 136 sum_n A'_g[p][n] from exactly the values the main products
-// used.
+// exactly as 136 + q (nibble in the mantissa of 128.0).  The scaled operand
+// is itself formed on the matrix cores, as a product of a diagonal matrix of
+// the scales with the fragment (exact in float32, then rounded once to bf16).
+// The offset is taken out by one more MFMA per row fragment against a
+// constant 136 operand, which accumulates 136 sum_n A'_g[p][n] from exactly
+// the values the main products used.
 //
 // A pre-pass transposes the int4 nibbles so that each output column holds its
 // reduction run as packed words (the same 8-per-word order as the forward
@@ -34,7 +36,7 @@
 // scales stream through a 3-deep LDS ring (LDS-DMA, A XOR-swizzled) in steps
 // of 64; v_mfma_f32_16x16x32_bf16 into float32 accumulators; persistent
 // XCD-partitioned work list; two blocks per CU, so that one block's VALU work
-// (scaling, unpacking) overlaps the other's matrix work.
+// (unpacking) overlaps the other's matrix work.
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
@@ -141,8 +143,11 @@ __global__ __launch_bounds__(256) void transpose_q_int8_kernel(const uint8_t *__
 // One pipeline stage in LDS, one array per kind (each read is a per-lane base
 // register plus a compile-time offset): A rows (128 x 64 bf16, 16-byte chunks
 // XOR-swizzled by row), int4 words (256 columns x 32 bytes), the scales of the
-// stage's 64 reduction steps for the block's two column groups.
-constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage holds the item's rows)
+// stage's 64 reduction steps for the block's two column groups (wave w loads
+// the 32 of group w / 2 from k = 32 (w % 2) into its own 256-byte region;
+// its upper 32 lanes repeat the lower lanes' sources into the region's upper
+// half, which nothing reads, so the transfer needs no lane mask).
+constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 4 * 64 * 4;   // (the A stage holds the item's rows)
 
 // Output columns of a wave's 128: fragment nf (of 8) and matrix-instruction
 // row j hold column gt_col(nf, j) (8 adjacent columns per lane and fragment
@@ -151,20 +156,31 @@ constexpr int TS_B = GT_BN * GT_KS / 2, TS_S = 2 * GT_KS * 4;   // (the A stage 
 // gt_pos(c), halves swapped by gt_half(c).
 
 // ------------------------------------------------------------------ GEMM --
-// A bf16x8 fragment times 8 per-k scales, rounded back to bf16.
-DEV uint4 scale_frag(uint4 a, const float (&sc)[8]) {
-  uint4 r;
-  r.x = cvt_pk_bf16(__uint_as_float(a.x << 16) * sc[0], __uint_as_float(a.x & 0xffff0000u) * sc[1]);
-  r.y = cvt_pk_bf16(__uint_as_float(a.y << 16) * sc[2], __uint_as_float(a.y & 0xffff0000u) * sc[3]);
-  r.z = cvt_pk_bf16(__uint_as_float(a.z << 16) * sc[4], __uint_as_float(a.z & 0xffff0000u) * sc[5]);
-  r.w = cvt_pk_bf16(__uint_as_float(a.w << 16) * sc[6], __uint_as_float(a.w & 0xffff0000u) * sc[7]);
-  return r;
+// A bf16x8 fragment (lane: row l % 16, 8 consecutive k of lane group l / 16)
+// times its 8 per-k scales, rounded back to bf16, with the products formed on
+// the matrix cores: two 16x16x16 products of a diagonal matrix of scales by
+// the fragment's two 4-wide halves.  The diagonal operand d_t of lane
+// (i, b) holds the scale of k = 16 (i / 4) + 8 s + 4 t + i % 4 at element
+// i % 4 when b = i / 4 and zeros elsewhere, so output element u of lane
+// (row, b) is that row's value at k = 16 b + 8 s + 4 t + u times its scale:
+// the lane's own eight k in order.  A bf16 times a bf16 is exact in float32,
+// and the other terms are zeros, so each product is exact and the
+// conversion rounds it once, as a vector multiply would; a row holding an
+// infinity or NaN turns its neighbours in the same 16 k into NaN (its
+// products are non-finite either way).
+DEV uint4 scale_frag_mfma(const u32x4_t a, short4_t d0, short4_t d1) {
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  const f32x4_t p0 = mfma16(d0, __builtin_bit_cast(short4_t, u32x2_t{a.x, a.y}), z);
+  const f32x4_t p1 = mfma16(d1, __builtin_bit_cast(short4_t, u32x2_t{a.z, a.w}), z);
+  return make_uint4(cvt_pk_bf16(p0[0], p0[1]), cvt_pk_bf16(p0[2], p0[3]), cvt_pk_bf16(p1[0], p1[1]),
+                    cvt_pk_bf16(p1[2], p1[3]));
 }
 
 // Per-launch values every work item uses.
 struct GtCtx {
   int Kh, N, G, NKh, NK, NKr;
   uint32_t ldsA, ldsB, ldsS;   // LDS byte addresses of the ring arrays
+  uint32_t ldsD;               // 1 KB of LDS that transfers with nothing to load land in
   uint32_t kMask, kMagic;      // int4 unpack constants (held in registers)
 };
 
@@ -216,22 +232,38 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
     }
     // scale staging: wave w, lanes < 32: column group (w >> 1), k 32 (w & 1) + lane
     const int sg = min(c0 / 128 + (w >> 1), G - 1);
-    const int sk = 32 * (w & 1) + lane;
+    const int sk = 32 * (w & 1) + (lane & 31);
     const uint32_t soff = (uint32_t)(sg * Kh + sk) * 4u;
     // this wave's LDS-DMA destinations within a stage (wave-uniform)
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);
     const uint32_t la = ldsA + wu * AOPS * 1024, lb = ldsB + wu * 2 * 1024,
-                   ls = ldsS + ((wu >> 1) * GT_KS + 32 * (wu & 1)) * 4;
+                   ls = ldsS + wu * 256;
     // per-lane LDS read bases (bytes); the rest of every read address is a
     // compile-time constant
     // (fragment nf reads column 128 wn + gt_col(nf, lr): its LDS position is
     // that of fragment nf & 1 plus 32 (nf >> 1) columns)
+    // (offD: the scale that lane lr places on the diagonal of the scaling
+    // products, k = 16 (lr / 4) + (lr % 4) + a compile-time 8 s + 4 t, in the
+    // region of the wave that loaded group wn's k / 32)
     const uint32_t offA0 = opaque(ldsA + (16 * NMH * wm + lr) * 128 + (((2 * lg) ^ row_swz(lr)) << 4)),
                    offB0 = opaque(ldsB + (128 * wn + gt_pos(gt_col(0, lr))) * 32 +
                                   16 * ((lg >> 1) ^ gt_half(gt_col(0, lr))) + 8 * (lg & 1)),
                    offB1 = opaque(ldsB + (128 * wn + gt_pos(gt_col(1, lr))) * 32 +
                                   16 * ((lg >> 1) ^ gt_half(gt_col(1, lr))) + 8 * (lg & 1)),
-                   offS = opaque(ldsS + (wn * GT_KS + 16 * lg) * 4);
+                   offD = opaque(ldsS + (2 * wn + (lr >> 3)) * 256 + (16 * ((lr >> 2) & 1) + (lr & 3)) * 4);
+    // byte selectors that place the bf16 scale (the upper half of its float32
+    // word) at element lr % 4 of the lane's 4-element diagonal operand, in
+    // the lanes whose lane group is lr / 4, and zeros everywhere else
+    // (selector byte 0x0c gives a zero byte)
+    uint32_t selLo, selHi;
+    {
+      const bool on = (lr >> 2) == lg;
+      const uint32_t put = (lr & 1) ? 0x03020c0cu : 0x0c0c0302u;
+      selLo = on && (lr & 2) == 0 ? put : 0x0c0c0c0cu;
+      selHi = on && (lr & 2) != 0 ? put : 0x0c0c0c0cu;
+      selLo = opaque(selLo);
+      selHi = opaque(selHi);
+    }
 
     // the row gates (mode 0, rows of dy by token), fetched now for the epilogue
     float gm[NMH];
@@ -299,13 +331,15 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       r.s = (second ? A.st1 : A.st0) + (size_t)e * G * Kh + kj * GT_KS;
       return r;
     };
-    auto stage_op = [&](int op, const StageSrc &src, int slot) {
+    // (live = false: the transfer lands in the unread LDS area instead)
+    auto stage_op = [&](int op, const StageSrc &src, int slot, bool live = true) {
       // destinations re-derived per transfer (scalar adds) rather than held
       uint32_t sa = la, sb = lb, ss = ls;
       asm volatile("" : "+s"(sa), "+s"(sb), "+s"(ss));
-      if (op < AOPS) dma16(src.a, aoff[op], sa + slot * TS_A + op * 1024);
-      else if (op < AOPS + 2) dma16(src.q, boff[op - AOPS], sb + slot * TS_B + (op - AOPS) * 1024);
-      else if (lane < 32) dma4(src.s, soff, ss + slot * TS_S);
+      if (op < AOPS) dma16(src.a, aoff[op], live ? sa + slot * TS_A + op * 1024 : X.ldsD);
+      else if (op < AOPS + 2)
+        dma16(src.q, boff[op - AOPS], live ? sb + slot * TS_B + (op - AOPS) * 1024 : X.ldsD);
+      else dma4(src.s, soff, live ? ss + slot * TS_S : X.ldsD);
     };
 
     f32x4_t acc[NMH][8], corr[NMH];
@@ -319,33 +353,41 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
     // one 64-deep step: 2 k-substeps x NMH row fragments x (8 + 1) MFMAs.
     // Lane group lg takes k = 16 lg + 8 s .. + 7 in substep s (A chunk
     // 2 lg + s, int4 word 2 lg + s), the same permutation on both operands.
-    auto compute = [&](int slot, int jc, int jl, int nslot) {   // jc: this stage; jl: the stage to load into nslot, or -1
+    // (a step with no stage left to load issues its transfers anyway, from
+    // the last stage into the LDS area nothing reads: the step stays one
+    // branch-free block that the compiler schedules as a whole)
+    auto compute = [&](int slot, int jc, int jl, int nslot) {   // jc: this stage; jl: the stage to load into nslot
       __builtin_amdgcn_sched_barrier(0);
       // the offset the correction removes: 136, or 128 on an int8 base's second plane
       const int kc = MODE == 1 && jc >= NKh ? jc - NKh : jc;
       const uint4 coff = kc < NKr ? c136 : c128;
-      const bool ld = jl >= 0;
-      const StageSrc src = stage_src(ld ? jl : 0);
+      const bool ld = jl < NK;
+      const StageSrc src = stage_src(ld ? jl : NK - 1);
       u32x2_t bw[8];
 #pragma unroll
       for (int nf = 0; nf < 8; ++nf)
         bw[nf] = lds_ld<u32x2_t>((nf & 1 ? offB1 : offB0) + slot * TS_B + (nf >> 1) * 32 * 32);
       // substep 1 reads chunk 2 lg + 1, the neighbouring swizzled chunk
       const uint32_t offA1 = offA0 ^ 16u;
+      // the scaling products' diagonal operands, dg[s][t] for k = 16 b + 8 s
+      // + 4 t + (0 .. 3) in lane group b
+      short4_t dg[2][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t f = lds_ld<uint32_t>(offD + slot * TS_S + (8 * s + 4 * t) * 4);
+          dg[s][t] = __builtin_bit_cast(short4_t, u32x2_t{__builtin_amdgcn_perm(f, f, selLo),
+                                                          __builtin_amdgcn_perm(f, f, selHi)});
+        }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        float sc[8];
-        {
-          const f32x4_t s0 = lds_ld<f32x4_t>(offS + slot * TS_S + 32 * s);
-          const f32x4_t s1 = lds_ld<f32x4_t>(offS + slot * TS_S + 32 * s + 16);
-          sc[0] = s0[0]; sc[1] = s0[1]; sc[2] = s0[2]; sc[3] = s0[3];
-          sc[4] = s1[0]; sc[5] = s1[1]; sc[6] = s1[2]; sc[7] = s1[3];
-        }
+        __builtin_amdgcn_sched_barrier(0);
         uint4 av[NMH];
 #pragma unroll
         for (int m = 0; m < NMH; ++m) {
           const u32x4_t a4 = lds_ld<u32x4_t>((s ? offA1 : offA0) + slot * TS_A + m * 2048);
-          av[m] = scale_frag(make_uint4(a4.x, a4.y, a4.z, a4.w), sc);
+          av[m] = scale_frag_mfma(a4, dg[s][0], dg[s][1]);
           corr[m] = mfma32(coff, av[m], corr[m]);
         }
 #pragma unroll
@@ -358,7 +400,7 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
           bu.w = __builtin_amdgcn_bitop3_b32(x >> 12, kMask, kMagic, 0x6A);
 #pragma unroll
           for (int m = 0; m < NMH; ++m) acc[m][nf] = mfma32(bu, av[m], acc[m][nf]);
-          if (s == 0 && nf < NOPS && ld) stage_op(nf, src, nslot);
+          if (s == 0 && nf < NOPS) stage_op(nf, src, nslot, ld);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -384,13 +426,13 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     block_barrier();
     for (int j = 0; j < NK; j += 3) {
-#define MOE_T_STEP(JJ, CUR, NXT)                             \
-  {                                                          \
-    const int jj = (JJ), jl = jj + 2;                        \
-    stage(jl, NXT);                                          \
-    if (jj < NK) compute(CUR, jj, jl < NK ? jl : -1, NXT);   \
-    __builtin_amdgcn_s_waitcnt(kWaitVm);                     \
-    block_barrier();                                         \
+#define MOE_T_STEP(JJ, CUR, NXT)                                    \
+  {                                                                 \
+    const int jj = (JJ), jl = jj + 2;                               \
+    stage(jl, NXT);                                                 \
+    if (jj < NK) compute(CUR, jj, jl, NXT);                          \
+    __builtin_amdgcn_s_waitcnt(kWaitVm);                            \
+    block_barrier();                                                \
   }
       MOE_T_STEP(j, 0, 2)
       MOE_T_STEP(j + 1, 1, 0)
@@ -546,7 +588,7 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
 // counter of the XCD (ctr[xcd], zero at launch), so blocks that drew short
 // items take more of them.  Each item runs as the shortest tile class that
 // holds its rows (32, 64, 96 or 128; a wave-uniform branch).  Two blocks per
-// CU, so that one block's VALU work (scaling, unpacking) overlaps the other's
+// CU, so that one block's VALU work (unpacking) overlaps the other's
 // matrix work.
 template <int MODE, bool EPL>
 __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaGemmTArgs A,
@@ -557,6 +599,7 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
   __shared__ __attribute__((aligned(32))) uint4 ringA[3][GT_BM * GT_KS * 2 / 16];
   __shared__ uint4 ringB[3][TS_B / 16];
   __shared__ float ringS[3][TS_S / 4];
+  __shared__ uint4 ringD[64];
   GtCtx X;
   X.Kh = A.K;
   X.N = A.N;
@@ -567,6 +610,7 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
   X.ldsA = lds_addr(ringA);
   X.ldsB = lds_addr(ringB);
   X.ldsS = lds_addr(ringS);
+  X.ldsD = __builtin_amdgcn_readfirstlane(lds_addr(ringD));
   // int4 unpack: each bf16 pair of 136 + q is one shift and one three-input
   // logic op, ((w >> 4i) & 0x000F000F) ^ 0x43084308 (constants in registers)
   X.kMask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
