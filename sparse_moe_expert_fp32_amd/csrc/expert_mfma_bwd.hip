@@ -532,6 +532,20 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
       float hdot = 0.f;
       if (cols_ok && r < rows) {
         const size_t p = (size_t)(p0 + r);
+        // mode 0: every operand of the row fragment is loaded before any of
+        // its stores (a load written after a store would wait for it: the
+        // compiler cannot tell that they do not overlap), one round trip
+        // per fragment
+        uint4 gw[4], uw[4], hw[4];
+        if (MODE == 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const size_t o = p * N + ocol + 32 * t;
+            gw[t] = *reinterpret_cast<const uint4 *>(&A.G[o]);
+            uw[t] = *reinterpret_cast<const uint4 *>(&A.U[o]);
+            if (want_dg) hw[t] = *reinterpret_cast<const uint4 *>(&A.H[o]);
+          }
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const f32x4_t a0 = acc[m][2 * t], a1 = acc[m][2 * t + 1];
@@ -541,9 +555,8 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
             // the forward saved the SwiGLU backward's multipliers
             // mG = U s (1 + G (1 - s)) and mU = G s
             const size_t o = p * N + c;
-            const uint4 gw = *reinterpret_cast<const uint4 *>(&A.G[o]);
-            const uint4 uw = *reinterpret_cast<const uint4 *>(&A.U[o]);
-            const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w}, u4[4] = {uw.x, uw.y, uw.z, uw.w};
+            const uint32_t g4[4] = {gw[t].x, gw[t].y, gw[t].z, gw[t].w},
+                           u4[4] = {uw[t].x, uw[t].y, uw[t].z, uw[t].w};
             uint32_t dg[4], du[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -553,8 +566,7 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
             *reinterpret_cast<uint4 *>(&A.dG[o]) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
             *reinterpret_cast<uint4 *>(&A.dU[o]) = make_uint4(du[0], du[1], du[2], du[3]);
             if (want_dg) {
-              const uint4 hw = *reinterpret_cast<const uint4 *>(&A.H[o]);
-              const uint32_t h4[4] = {hw.x, hw.y, hw.z, hw.w};
+              const uint32_t h4[4] = {hw[t].x, hw[t].y, hw[t].z, hw[t].w};
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 hdot = fmaf(a[2 * i], lo(h4[i]), hdot);
