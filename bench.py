@@ -153,7 +153,9 @@ def decode_hbm(args, B, DeviceLayer, to_numpy, bits=4):
     times the 256 MB last-level cache, so the expert weights stream from HBM.
     (A write of the same size leaves the cache full of dirty lines that the
     forward's first reads must write back, 256 MB of traffic that is not the
-    forward's; that time is reported beside it.)  Bytes are algorithmic: the
+    forward's; that time is reported beside it, and so is the int4 forward
+    run over three weight sets in turn with no scrub at all.)  Bytes are
+    algorithmic: the
     int4 (or int8) base, bf16 group scales and adapters of the experts the
     seeded routing touches, plus the router, x and y."""
     import torch
@@ -184,6 +186,29 @@ def decode_hbm(args, B, DeviceLayer, to_numpy, bits=4):
 
     cold, ev = timed(False)
     cold_w, _ = timed(True)
+    # (int4) the same routing over three sets of expert weights in turn, no
+    # scrub: each forward reads weights the other two sets have evicted
+    rotated = None
+    if bits == 4:
+        sets = [L]
+        for i in (1, 2):
+            other = inputs.generate(cfg, args.seed + 1000 + i)
+            mixed = {key: (other[key] if key.split("_")[0] in ("q", "s", "A", "B") else v)
+                     for key, v in inp.items()}
+            sets.append(DeviceLayer(cfg, mixed, device="cuda:0", with_backward=False))
+        for S_ in sets:
+            S_.forward()
+        torch.cuda.synchronize()
+        evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(3 * n)]
+        for i, (a, b) in enumerate(evr):
+            a.record(stream)
+            sets[i % 3].forward()
+            b.record(stream)
+        torch.cuda.synchronize()
+        rt = sorted(a.elapsed_time(b) for a, b in evr)
+        rotated = rt[len(rt) // 2]
+        del sets
     a, b = ev[0]
     a.record(stream)
     for _ in range(n):
@@ -202,6 +227,7 @@ def decode_hbm(args, B, DeviceLayer, to_numpy, bits=4):
                         f"unbiased router, int{bits} base)",
             "ms": med, "ms_p10": cold[len(cold) // 10], "ms_p90": cold[(9 * len(cold)) // 10],
             "ms_warm_cache": warm, "ms_after_write_scrub": cold_w[len(cold_w) // 2],
+            "ms_three_weight_sets_in_turn": rotated,
             "tokens_per_s": cfg.T / (med / 1e3),
             "experts_touched": touched, "bytes": nbytes, "bytes_per_expert": per_expert,
             "GB_s": nbytes / (med / 1e3) / 1e9, "frac_hbm": nbytes / (med / 1e3) / PEAK_HBM,
