@@ -649,7 +649,9 @@ DEV void gm_item(const MfmaGemmArgs &A, const GmCtx &X, int e, int p0, int rows,
 // tiles, split into eight contiguous ranges, one per XCD, so that an expert's
 // tiles, its short last one included, run close together on one XCD and
 // share its weights in that L2.  Within its range a block draws its next item
-// from a counter of the XCD (ctr[xcd], zero at launch).  Each item runs as the
+// from a counter of the XCD (ctr[xcd], zero at launch); in the gate/up
+// product, once its range is used up, it draws from the other XCDs' ranges
+// (draw_item).  Each item runs as the
 // shortest tile class that holds its rows (32, 64, 96 or 128; a wave-uniform
 // branch).  QP: the base in the packed layout.  Two blocks of four waves per
 // CU.
@@ -667,15 +669,17 @@ __global__ __launch_bounds__(256, GM_BPC) void grouped_gemm_kernel(const MfmaGem
   MOE_GM_CTX(ringA, ringB, ringX, tok_lds);
   const int total = ntiles[0] * A.NT;
   const int xcd = blockIdx.x & 7;
-  const int wbeg = (int)(((long long)total * xcd) >> 3);
-  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
-  if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+  // (the down product's items are short, and items taken from other XCDs'
+  // ranges cost it more than the balance gains: measured 4 % slower)
+  constexpr bool steal = MODE == 0;
+  int rng = xcd;
+  if (threadIdx.x == 0) next_item = draw_item(ctr, total, rng, xcd, steal);
   __syncthreads();
-  for (int wi = next_item; wi < wend; wi = next_item) {
+  for (int wi = next_item; wi >= 0; wi = next_item) {
     // every thread has read next_item; the next draw overlaps this item (its
     // value is visible after the item's first barrier)
     __syncthreads();
-    if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+    if (threadIdx.x == 0) next_item = draw_item(ctr, total, rng, xcd, steal);
     const int ti = wi / A.NT, nt = wi - ti * A.NT;
     const int2 tile = A.tiles[ti];
     const int e = tile.x, p0 = tile.y;

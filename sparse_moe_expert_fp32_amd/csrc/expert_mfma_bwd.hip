@@ -598,7 +598,8 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
 // its short last one, run close together in time on one XCD and share its
 // weights in that L2.  Within its range a block takes the next item from a
 // counter of the XCD (ctr[xcd], zero at launch), so blocks that drew short
-// items take more of them.  Each item runs as the shortest tile class that
+// items take more of them, and once its range is used up from the other
+// XCDs' ranges (draw_item).  Each item runs as the shortest tile class that
 // holds its rows (32, 64, 96 or 128; a wave-uniform branch).  Two blocks per
 // CU, so that one block's VALU work (unpacking) overlaps the other's
 // matrix work.
@@ -630,15 +631,14 @@ __global__ __launch_bounds__(256, GT_BPC) void grouped_gemm_t_kernel(const MfmaG
   __shared__ int next_item;
   const int total = ntiles[0] * A.NT;
   const int xcd = blockIdx.x & 7;
-  const int wbeg = (int)(((long long)total * xcd) >> 3);
-  const int wend = (int)(((long long)total * (xcd + 1)) >> 3);
-  if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+  int rng = xcd;
+  if (threadIdx.x == 0) next_item = draw_item(ctr, total, rng, xcd);
   __syncthreads();
-  for (int wi = next_item; wi < wend; wi = next_item) {
+  for (int wi = next_item; wi >= 0; wi = next_item) {
     // every thread has read next_item; the next draw overlaps this item (its
     // value is visible after the item's first barrier)
     __syncthreads();
-    if (threadIdx.x == 0) next_item = wbeg + atomicAdd(&ctr[xcd], 1);
+    if (threadIdx.x == 0) next_item = draw_item(ctr, total, rng, xcd);
     const int ti = wi / A.NT, nt = wi - ti * A.NT;
     const int2 tile = A.tiles[ti];
     const int e = tile.x, p0 = tile.y;

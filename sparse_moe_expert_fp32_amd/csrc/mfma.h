@@ -160,6 +160,23 @@ constexpr int kWaitAll = 0x0070;
 // landed), and waiting for all of them costs nothing measurable here.
 constexpr int kWaitVm = vmcnt_imm(0);
 
+// Next item of a persistent launch whose `total` items are split into eight
+// contiguous ranges, one per XCD, each with a zeroed counter ctr[r]: a block
+// draws from range *rng (its own XCD's first) and, once that range is used
+// up, from the following ranges in turn, so that no XCD idles while another
+// still has items (the ranges hold equal numbers of items, not equal work).
+// -1 when every range is used up.  One thread calls it; the counters only
+// choose which block computes an item.  (steal = false: the own range only.)
+DEV int draw_item(int *ctr, int total, int &rng, int xcd, bool steal = true) {
+  for (; rng < xcd + (steal ? 8 : 1); ++rng) {
+    const int r = rng & 7;
+    const int end = (int)(((long long)total * (r + 1)) >> 3);
+    const int w = (int)(((long long)total * r) >> 3) + atomicAdd(&ctr[r], 1);
+    if (w < end) return w;
+  }
+  return -1;
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would make the compiler drain every outstanding load, including LDS-DMA
 // that is deliberately left in flight.  Callers wait (s_waitcnt) for the
