@@ -153,8 +153,9 @@ struct FwdLayout {
     if (use_mfma(d)) {
       G32 = U32 = 0;
       tiles_m = c.take(max_tiles(d, fwd_tile_rows(d)) * sizeof(int2));
-      // (the tile count and eight work counters for each of the two products)
-      ntiles_m = c.take(32 * sizeof(int));
+      // (the tile count and eight work counters for each of the two products,
+      // one 128-byte line per counter)
+      ntiles_m = c.take(moe::kWorkListInts * sizeof(int));
       tiles_p = c.take(max_tiles(d, moe::proj_tile_rows(d->T < kFwdShortBelowT)) * sizeof(int2));
       ntiles_p = c.take(sizeof(int));
       const size_t pm = plane_mult(d);
@@ -203,8 +204,9 @@ struct BwdLayout {
     tiles = c.take(max_tiles(d, moe::simple_tile_rows()) * sizeof(int2));
     ntiles = c.take(sizeof(int));
     tiles_m = mf ? c.take(max_tiles(d, moe::mfma_t_tile_rows()) * sizeof(int2)) : 0;
-    // tile count, then eight work counters for each of the two products
-    ntiles_m = mf ? c.take(32 * sizeof(int)) : 0;
+    // tile count, then eight work counters for each of the two products (one
+    // 128-byte line per counter)
+    ntiles_m = mf ? c.take(moe::kWorkListInts * sizeof(int)) : 0;
     tiles_p = mf ? c.take(max_tiles(d, moe::proj_tile_rows()) * sizeof(int2)) : 0;
     ntiles_p = mf ? c.take(sizeof(int)) : 0;
     // adapter-gradient work items and their partial sums ([tiles][2][wide][r] f32)
@@ -630,7 +632,7 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     // counters), the projections' tile list, and the per-row start values
     // -136 * (row sum per group)
     moe::PrepBatch pb;
-    pb.tiles(offsets, E, fwd_tile_rows(dims), tiles_m, ntiles_m, nullptr, 32);
+    pb.tiles(offsets, E, fwd_tile_rows(dims), tiles_m, ntiles_m, nullptr, moe::kWorkListInts);
     pb.tiles(offsets, E, moe::proj_tile_rows(short_t), tiles_p, ntiles_p);
     pb.rowsum(x, T, d, 128, -136.f, rs_x, i8, -128.f);
     moe::launch_prep(pb, st);
@@ -683,7 +685,7 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     M.rsum_out = rs_h; M.ld_rsum_out = f / 128 * pm; M.rsum_split = i8;
     TIMED(MOE_KT_GATEUP, st, {
       if (short_t) moe::launch_grouped_gemm_short(0, M, ntiles_m, grid, st);
-      else moe::launch_grouped_gemm(0, M, ntiles_m, ntiles_m + 8, grid, st);
+      else moe::launch_grouped_gemm(0, M, ntiles_m, ntiles_m + moe::kCtrSet0, grid, st);
     });
     // Z_d = H A_d^T
     Q.a = (const uint16_t *)H; Q.lda = f; Q.K = f; Q.nsrc = 1; Q.m0 = (const uint16_t *)down.A;
@@ -699,7 +701,7 @@ moe_status expert_fwd_run(const moe_dims *dims, const void *x, const int32_t *of
     D.out = (uint16_t *)e_out; D.ldo = d;
     TIMED(MOE_KT_DOWN, st, {
       if (short_t) moe::launch_grouped_gemm_short(1, D, ntiles_m, grid, st);
-      else moe::launch_grouped_gemm(1, D, ntiles_m, ntiles_m + 16, grid, st);
+      else moe::launch_grouped_gemm(1, D, ntiles_m, ntiles_m + moe::kCtrSet1, grid, st);
     });
     return hip_status("moe_expert_fwd");
   }
@@ -840,7 +842,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     // matrix as [E][r][N] where its projection runs on its own
     moe::PrepBatch pb;
     pb.transpose_f32(w_router, d, E, wr_t);
-    pb.tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, nullptr, 32);
+    pb.tiles(offsets, E, moe::mfma_t_tile_rows(), tiles_m, ntiles_m, nullptr, moe::kWorkListInts);
     pb.tiles(offsets, E, moe::proj_tile_rows(), tiles_p, ntiles_p);
     pb.tiles(offsets, E, moe::wgrad_tile_rows(), tiles_w, ntiles_w, ntiles_w + 1);
     if (!fuse_d) pb.transpose_nr(down.B, E, d, r, bt_d, st);
@@ -918,7 +920,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     const int nq = 2 * ((f + 255) / 256);
     float *dgp = moe::token_bwd_covers(d, k) && (size_t)nq * S <= (size_t)T * d ? dx_r : nullptr;
     M.H = H16; M.dgp = dgp; M.S = (int)S;
-    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, ntiles_m + 8, grid, st));
+    TIMED(MOE_KT_BWD_DOWN, st, moe::launch_grouped_gemm_t(0, M, ntiles_m, ntiles_m + moe::kCtrSet0, grid, st));
     // dA_d [r][f] = sum_p dZ_d[p][j] H[p][c]
     moe::WgradMArgs Wd = W;
     Wd.w = H16; Wd.ldw = f; Wd.rr = dZ + 2 * r; Wd.wide = f; Wd.scale = 1.f; Wd.out = dA_down;
@@ -975,7 +977,7 @@ moe_status moe_adapter_bwd(const moe_dims *dims, const void *dy, const void *x,
     X.Z0 = dZ; X.Z1 = dZ + r; X.ldz = 3 * r; X.r = r;
     X.L0 = (const uint16_t *)gate.A; X.L1 = (const uint16_t *)up.A;
     X.out = (uint16_t *)dXp; X.ldo = d;
-    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, ntiles_m, ntiles_m + 16, grid, st));
+    TIMED(MOE_KT_BWD_GATEUP, st, moe::launch_grouped_gemm_t(1, X, ntiles_m, ntiles_m + moe::kCtrSet1, grid, st));
     // gate gradient and the per-token sum of dX_perm, one pass per token
     TIMED(MOE_KT_GATE_GRAD, st, {
       if (!moe::launch_token_bwd(dy, e_out, topk_idx, gates, slot_pos, wr_t, dXp, T, d, k, E, dx,

@@ -268,6 +268,15 @@ void launch_grouped_gemm_t(int mode, const MfmaGemmTArgs &A, const int *ntiles, 
 // library's static scratch array (kStaticScratchBytes), looked up once per
 // device with that device current
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+
+// Work-list block of the persistent products (tile list of 128-row tiles):
+// the tile count, then for each of the two products of a call eight work
+// counters, one per XCD, each on a 128-byte line of its own, so that the
+// atomics of different XCDs do not contend for one line.  The list builder
+// zeroes the block (nzero = kWorkListInts).
+constexpr int kCtrStride = 32;                               // ints between counters
+constexpr int kCtrSet0 = 32, kCtrSet1 = 32 + 8 * kCtrStride;  // first counter of each product
+constexpr int kWorkListInts = 32 + 16 * kCtrStride;
 hipError_t static_scratch(void **ptr);
 
 // ---- adapter optimizer step (adamw.hip)

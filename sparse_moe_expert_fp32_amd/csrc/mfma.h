@@ -2,6 +2,7 @@
 // int4 unpacking and direct global->LDS loads.
 #pragma once
 #include "common.h"
+#include "kernels.h"
 
 namespace moe {
 
@@ -161,7 +162,7 @@ constexpr int kWaitAll = 0x0070;
 constexpr int kWaitVm = vmcnt_imm(0);
 
 // Next item of a persistent launch whose `total` items are split into eight
-// contiguous ranges, one per XCD, each with a zeroed counter ctr[r]: a block
+// contiguous ranges, one per XCD, each with a zeroed counter ctr[r kCtrStride]: a block
 // draws from range *rng (its own XCD's first) and, once that range is used
 // up, from the following ranges in turn, so that no XCD idles while another
 // still has items (the ranges hold equal numbers of items, not equal work).
@@ -171,7 +172,7 @@ DEV int draw_item(int *ctr, int total, int &rng, int xcd, bool steal = true) {
   for (; rng < xcd + (steal ? 8 : 1); ++rng) {
     const int r = rng & 7;
     const int end = (int)(((long long)total * (r + 1)) >> 3);
-    const int w = (int)(((long long)total * r) >> 3) + atomicAdd(&ctr[r], 1);
+    const int w = (int)(((long long)total * r) >> 3) + atomicAdd(&ctr[r * kCtrStride], 1);
     if (w < end) return w;
   }
   return -1;
