@@ -430,7 +430,7 @@ DEV void gt_item(const MfmaGemmTArgs &A, const GtCtx &X, int e, int p0, int rows
   {                                                                 \
     const int jj = (JJ), jl = jj + 2;                               \
     stage(jl, NXT);                                                 \
-    if (jj < NK) compute(CUR, jj, jl, NXT);                          \
+    if (jj < NK) compute(CUR, jj, jl, NXT);                         \
     __builtin_amdgcn_s_waitcnt(kWaitVm);                            \
     block_barrier();                                                \
   }

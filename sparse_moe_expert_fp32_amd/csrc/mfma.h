@@ -162,10 +162,11 @@ constexpr int kWaitAll = 0x0070;
 constexpr int kWaitVm = vmcnt_imm(0);
 
 // Next item of a persistent launch whose `total` items are split into eight
-// contiguous ranges, one per XCD, each with a zeroed counter ctr[r kCtrStride]: a block
-// draws from range *rng (its own XCD's first) and, once that range is used
-// up, from the following ranges in turn, so that no XCD idles while another
-// still has items (the ranges hold equal numbers of items, not equal work).
+// contiguous ranges, one per XCD, range r with the zeroed counter
+// ctr[r * kCtrStride]: a block draws from range *rng (its own XCD's first)
+// and, once that range is used up, from the following ranges in turn, so
+// that no XCD idles while another still has items (the ranges hold equal
+// numbers of items, not equal work).
 // -1 when every range is used up.  One thread calls it; the counters only
 // choose which block computes an item.  (steal = false: the own range only.)
 DEV int draw_item(int *ctr, int total, int &rng, int xcd, bool steal = true) {
